@@ -1,0 +1,390 @@
+// Exact attention over the tokens a decode step selected (sparse mode) or over
+// every cached token (dense mode), as a split-K flash decode with an online
+// softmax in fp32, followed by a combine of the split partials.
+//
+// Sparse mode attends, for each query head, over the raw keys of the level-1
+// chunks it kept, token 0 (the attention sink) and the raw tail [c*n_1, N)
+// (page rit.work "zha-tree-indexer-long-context", section "Дерево сокращает
+// сам поиск нужных ключей": exact attention over the raw keys of the reached
+// leaves; page "ZHA 用树形稀疏注意力改造现有大模型", section
+// 稀疏注意力为什么还会被索引拖慢: the first token is always kept).  The KV
+// bytes of a chunk are read once per KV group: a per-chunk bit mask says
+// which of the group's query heads selected it.
+//
+// Slot space of a group (32-slot tiles):
+//   [0, nk*c)           kept chunks in ascending order; token 0 is masked here
+//   [nk*c]              token 0 for every head (when chunk 0 is complete)
+//   [..., total)        the tail tokens, every head
+//
+// bf16 path: QK^T and PV run on v_mfma_f32_16x16x32_bf16 with the group's
+// heads as the 16 MFMA rows.  V stays in its row-major layout: a lane loads 16
+// bytes of one token row and the contraction index of the PV product is
+// permuted so that each lane's eight B-operand values come from eight such
+// loads.  P is split into bf16 hi + lo parts (two MFMAs), so the PV product
+// keeps ~16 bits of P.  fp32 path: the same tiling on v_mfma_f32_16x16x4_f32.
+#include "zha_common.h"
+#include "zha_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileSlots = 32;
+constexpr int kMinTilesPerBlock = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ uint32_t pick_half(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xFFFFu); }
+
+__device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+struct Slots {
+    int64_t nk, total, tail_start;
+    int sink;
+};
+
+template <bool DENSE>
+__device__ __forceinline__ Slots slot_space(const ZhaAttnArgs& a, int g, int c) {
+    Slots s;
+    if (DENSE) {
+        s.nk = 0;
+        s.sink = 0;
+        s.tail_start = 0;
+        s.total = a.n_tokens;
+    } else {
+        s.nk = a.klist ? (int64_t)a.nkept[g] : 0;
+        const int64_t n1 = a.n_tokens / c;
+        s.tail_start = (int64_t)c * n1;
+        s.sink = n1 > 0 ? 1 : 0;
+        s.total = s.nk * c + s.sink + (a.n_tokens - s.tail_start);
+    }
+    return s;
+}
+
+template <bool DENSE>
+__device__ __forceinline__ void slot_to_token(const ZhaAttnArgs& a, const Slots& s, int g, int c, uint32_t allg,
+                                              int64_t slot, int32_t* tok, uint32_t* msk) {
+    if (slot >= s.total) {
+        *tok = 0;
+        *msk = 0u;
+        return;
+    }
+    if (DENSE) {
+        *tok = (int32_t)slot;
+        *msk = allg;
+        return;
+    }
+    const int64_t kc = s.nk * c;
+    if (slot < kc) {
+        const int64_t e = slot / c;
+        const int64_t t = (int64_t)a.klist[(size_t)g * a.cap1 + e] * c + (slot - e * c);
+        *tok = (int32_t)t;
+        *msk = t == 0 ? 0u : a.kmask[(size_t)g * a.cap1 + e];
+        return;
+    }
+    const int64_t r = slot - kc;
+    if (s.sink && r == 0) {
+        *tok = 0;
+        *msk = allg;
+        return;
+    }
+    *tok = (int32_t)(s.tail_start + r - s.sink);
+    *msk = allg;
+}
+
+__device__ __forceinline__ int active_blocks(int64_t tiles, int Bg) {
+    int64_t n = (tiles + kMinTilesPerBlock - 1) / kMinTilesPerBlock;
+    if (n < 1) n = 1;
+    if (n > Bg) n = Bg;
+    return (int)n;
+}
+
+// grid (Bg, H_kv), 256 threads.
+template <bool BF16, bool DENSE>
+__global__ __launch_bounds__(kThreads) void zha_attn_kernel(ZhaAttnArgs a, int G, int c, float tau, int Bg) {
+    __shared__ int32_t s_tok[kWaves][kTileSlots];
+    __shared__ uint32_t s_msk[kWaves][kTileSlots];
+    __shared__ float s_buf[kWaves * 16 * ZHA_D];          // P tiles during the loop, partial O after it
+    __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+
+    const int g = blockIdx.y, b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, q4 = lane >> 4;
+    const uint32_t allg = (G >= 32) ? 0xFFFFFFFFu : ((1u << G) - 1u);
+    const Slots sp = slot_space<DENSE>(a, g, c);
+    const int64_t tiles = (sp.total + kTileSlots - 1) / kTileSlots;
+    const int nact = active_blocks(tiles, Bg);
+    if (b == 0 && threadIdx.x == 0) a.nact[g] = nact;
+    if (b >= nact) return;
+    const int64_t t0 = tiles * b / nact, t1 = tiles * (b + 1) / nact;
+    const float scale = tau * kLog2e;                     // logits in log2 units
+    float* s_p = s_buf + wave * 16 * 33;                  // [16 heads][33]
+
+    const size_t head_row0 = (size_t)g * (size_t)a.cap_tok;
+
+    // Q as the A operand: row = head j (zero beyond G)
+    uint4 qa16[4];
+    float qa32[32];
+    if (BF16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (j < G)
+                qa16[s] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                                          ((size_t)g * G + j) * ZHA_D + 32 * s + 8 * q4);
+            else
+                qa16[s] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                qa32[4 * m + e] = (j < G) ? static_cast<const float*>(a.q)[((size_t)g * G + j) * ZHA_D + 16 * m + 4 * q4 + e] : 0.f;
+    }
+
+    float m_run[4], l_run[4];
+    zha_f32x4 O[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = zha_neg_inf(); l_run[i] = 0.f; }
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) O[c8] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+        if (lane < kTileSlots) {
+            int32_t tok;
+            uint32_t msk;
+            slot_to_token<DENSE>(a, sp, g, c, allg, t * kTileSlots + lane, &tok, &msk);
+            s_tok[wave][lane] = tok;
+            s_msk[wave][lane] = msk;
+        }
+        zha_wave_lds_sync();
+
+        zha_f32x4 S[2];
+        uint4 vr[8];
+        float4 vf[8][2];
+        if (BF16) {
+            const uint16_t* K = static_cast<const uint16_t*>(a.K);
+            const uint16_t* V = static_cast<const uint16_t*>(a.V);
+            uint4 kr[2][4];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const uint16_t* row = K + (head_row0 + (size_t)s_tok[wave][16 * bb + j]) * ZHA_D + 8 * q4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) kr[bb][s] = *reinterpret_cast<const uint4*>(row + 32 * s);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                vr[i] = *reinterpret_cast<const uint4*>(V + (head_row0 + (size_t)s_tok[wave][4 * i + q4]) * ZHA_D + 8 * j);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                zha_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zha_as_bf16x8(qa16[s]), zha_as_bf16x8(kr[bb][s]), acc, 0, 0, 0);
+                S[bb] = acc;
+            }
+        } else {
+            const float* K = static_cast<const float*>(a.K);
+            const float* V = static_cast<const float*>(a.V);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const float4* row = reinterpret_cast<const float4*>(K + (head_row0 + (size_t)s_tok[wave][16 * bb + j]) * ZHA_D);
+                zha_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const float4 kf = row[4 * m + q4];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa32[4 * m + 0], kf.x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa32[4 * m + 1], kf.y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa32[4 * m + 2], kf.z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa32[4 * m + 3], kf.w, acc, 0, 0, 0);
+                }
+                S[bb] = acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4* row = reinterpret_cast<const float4*>(V + (head_row0 + (size_t)s_tok[wave][4 * i + q4]) * ZHA_D + 8 * j);
+                vf[i][0] = row[0];
+                vf[i][1] = row[1];
+            }
+        }
+
+        // S[bb][i]: head 4*q4+i against slot 16*bb+j.  Mask, scale, online softmax.
+        const uint32_t mk0 = s_msk[wave][j], mk1 = s_msk[wave][16 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * q4 + i;
+            const float x0 = ((mk0 >> h) & 1u) ? S[0][i] * scale : zha_neg_inf();
+            const float x1 = ((mk1 >> h) & 1u) ? S[1][i] * scale : zha_neg_inf();
+            float mx = fmaxf(x0, x1);
+            for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+            const float mn = fmaxf(m_run[i], mx);
+            float alpha, p0, p1;
+            if (mn == zha_neg_inf()) {
+                alpha = 1.f; p0 = 0.f; p1 = 0.f;
+            } else {
+                alpha = exp2f(m_run[i] - mn);
+                p0 = exp2f(x0 - mn);
+                p1 = exp2f(x1 - mn);
+            }
+            float rs = p0 + p1;
+            for (int o = 8; o > 0; o >>= 1) rs += __shfl_xor(rs, o, 16);
+            l_run[i] = l_run[i] * alpha + rs;
+            m_run[i] = mn;
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) O[c8][i] *= alpha;
+            s_p[h * 33 + j] = p0;
+            s_p[h * 33 + 16 + j] = p1;
+        }
+        zha_wave_lds_sync();
+
+        if (BF16) {
+            // A operand: row head j, contraction slots 4e + q4, e = 0..7, as bf16 hi + lo
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float pa = s_p[j * 33 + 4 * (2 * e2) + q4];
+                const float pb = s_p[j * 33 + 4 * (2 * e2 + 1) + q4];
+                const uint32_t ha = zha_f32_to_bf16_rne(pa), hb = zha_f32_to_bf16_rne(pb);
+                const uint32_t la = zha_f32_to_bf16_rne(pa - zha_bf16_to_f32(ha));
+                const uint32_t lb = zha_f32_to_bf16_rne(pb - zha_bf16_to_f32(hb));
+                hi[e2] = ha | (hb << 16);
+                lo[e2] = la | (lb << 16);
+            }
+            const zha_bf16x8 Ahi = zha_as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            const zha_bf16x8 Alo = zha_as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) {
+                const int w = c8 >> 1, odd = c8 & 1;
+                uint32_t bw[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2)
+                    bw[e2] = pick_half(comp(vr[2 * e2], w), odd) | (pick_half(comp(vr[2 * e2 + 1], w), odd) << 16);
+                const zha_bf16x8 Bv = zha_as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
+                O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bv, O[c8], 0, 0, 0);
+                O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bv, O[c8], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float pa = s_p[j * 33 + 4 * i + q4];
+                const float v8[8] = {vf[i][0].x, vf[i][0].y, vf[i][0].z, vf[i][0].w,
+                                     vf[i][1].x, vf[i][1].y, vf[i][1].z, vf[i][1].w};
+#pragma unroll
+                for (int c8 = 0; c8 < 8; ++c8) O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, v8[c8], O[c8], 0, 0, 0);
+            }
+        }
+        zha_wave_lds_sync();
+    }
+
+    // ---- combine the block's waves; O[c8][i] is head 4*q4+i, column d = 8*j + c8
+    __syncthreads();
+    if (j == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s_m[wave][4 * q4 + i] = m_run[i];
+            s_l[wave][4 * q4 + i] = l_run[i];
+        }
+    float* so = s_buf + wave * 16 * ZHA_D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) so[(4 * q4 + i) * ZHA_D + 8 * j + c8] = O[c8][i];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * ZHA_D; idx += kThreads) {
+        const int h = idx >> 7, d = idx & (ZHA_D - 1);
+        float M = zha_neg_inf();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        float L = 0.f, acc = 0.f;
+        if (M != zha_neg_inf()) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float f = exp2f(s_m[w][h] - M);
+                L = fmaf(s_l[w][h], f, L);
+                acc = fmaf(s_buf[(w * 16 + h) * ZHA_D + d], f, acc);
+            }
+        }
+        const size_t ph = ((size_t)g * Bg + b) * G + h;
+        if (d == 0) {
+            a.pm[ph] = M;
+            a.pl[ph] = L;
+        }
+        a.po[ph * ZHA_D + d] = acc;
+    }
+}
+
+// grid (H_q, 128 / 32), 256 threads = 8 partial lanes x 32 columns:
+// out[h][d] = sum_b O_b[d] 2^(m_b - M) / sum_b l_b 2^(m_b - M).
+constexpr int kCombThreads = 256;
+__global__ __launch_bounds__(kCombThreads) void zha_combine_kernel(ZhaAttnArgs a, int G, int Bg,
+                                                                   float* __restrict__ out) {
+    __shared__ float f[ZHA_ATTN_MAXB];
+    __shared__ float red[kCombThreads];
+    const int h = blockIdx.x, g = h / G, hl = h - g * G, tid = threadIdx.x;
+    const int n = a.nact[g];
+    const size_t base = (size_t)g * Bg * G + hl;          // partial b of head h at base + b*G
+    float m = zha_neg_inf();
+    for (int b = tid; b < n; b += kCombThreads) m = fmaxf(m, a.pm[base + (size_t)b * G]);
+    red[tid] = m;
+    __syncthreads();
+    for (int o = kCombThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+        __syncthreads();
+    }
+    const float M = red[0];
+    __syncthreads();
+    float l = 0.f;
+    for (int b = tid; b < n; b += kCombThreads) {
+        const float mb = a.pm[base + (size_t)b * G];
+        const float fb = mb == zha_neg_inf() ? 0.f : exp2f(mb - M);
+        f[b] = fb;
+        l = fmaf(a.pl[base + (size_t)b * G], fb, l);
+    }
+    red[tid] = l;
+    __syncthreads();
+    for (int o = kCombThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) red[tid] += red[tid + o];
+        __syncthreads();
+    }
+    const float L = red[0];
+    __syncthreads();
+    const int dd = tid & 31, bl = tid >> 5;
+    const int d = blockIdx.y * 32 + dd;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int b = bl; b < n; b += kCombThreads / 32) acc = fmaf(a.po[(base + (size_t)b * G) * ZHA_D + d], f[b], acc);
+    red[tid] = acc;
+    __syncthreads();
+    if (bl == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int k = 0; k < kCombThreads / 32; ++k) t += red[k * 32 + dd];
+        out[(size_t)h * ZHA_D + d] = t / L;
+    }
+}
+
+}  // namespace
+
+hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, int H_kv, int G, int c, float tau,
+                                int Bg, hipStream_t stream) {
+    dim3 grid((unsigned)Bg, (unsigned)H_kv);
+    if (kv_dtype == 0) {
+        if (dense)
+            hipLaunchKernelGGL((zha_attn_kernel<true, true>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+        else
+            hipLaunchKernelGGL((zha_attn_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+    } else {
+        if (dense)
+            hipLaunchKernelGGL((zha_attn_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+        else
+            hipLaunchKernelGGL((zha_attn_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+    }
+    return hipGetLastError();
+}
+
+hipError_t zha_launch_combine(const ZhaAttnArgs& a, int H_kv, int G, int Bg, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(zha_combine_kernel, dim3((unsigned)(H_kv * G), ZHA_D / 32), dim3(kCombThreads), 0, stream, a, G,
+                       Bg, out);
+    return hipGetLastError();
+}

@@ -171,7 +171,8 @@ def generate(w: Workload, device="cpu", seed: int | None = None) -> dict:
     elif w.generator == "clusters":
         # 64 unit cluster directions per head; each cluster is 8 contiguous tokens at a
         # non-overlapping start in [1, N-8) whose keys have cosine 0.5..0.9 with it.
-        n_cl, span = 64, 8
+        span = 8
+        n_cl = max(1, min(64, (N - 1) // (2 * span)))   # fewer clusters only when N is tiny
         for g in range(H):
             u = _unit(_randn((n_cl, d), base, dev, "cl_dir", g))
             # slot i spans [1 + 2*span*i, 1 + 2*span*(i+1)); an offset < span keeps clusters disjoint
@@ -205,11 +206,12 @@ def generate(w: Workload, device="cpu", seed: int | None = None) -> dict:
             qn = _randn((w.steps, G, d), base, dev, "topic_qnoise", g)
             qg = mu[topic[tseg]][:, None, :] + 0.5 * qn
             q[:, g * G:(g + 1) * G] = qg
-            n_slots = (N - 1 - 16) // 16
-            slots = torch.randperm(n_slots, generator=_gen(base, "cpu", "needle_slot", g))[:w.steps]
+            n_slots = max(0, (N - 1 - 16) // 16)
+            n_nd = min(w.steps, n_slots)                              # one needle per step while they fit
+            slots = torch.randperm(n_slots, generator=_gen(base, "cpu", "needle_slot", g))[:n_nd]
             qbar = qg.mean(dim=1)                                     # [steps, d]
             eps = _randn((w.steps, 16, d), base, dev, "needle_eps", g)
-            needles = qbar[:, None, :] + 0.1 * eps
+            needles = (qbar[:, None, :] + 0.1 * eps)[:n_nd]
             idx = (1 + slots[:, None] * 16 + torch.arange(16)[None, :]).reshape(-1).to(dev)
             k[g, idx] = needles.reshape(-1, d).to(dt)
     else:

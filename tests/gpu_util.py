@@ -1,0 +1,193 @@
+"""Shared helpers of the GPU tests: device inputs, host copies for the oracle, comparisons."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from hierarchical_tree_indexed_zha_amd import binding as B
+from hierarchical_tree_indexed_zha_amd import workloads as W
+from hierarchical_tree_indexed_zha_amd.runtime import ZhaLayer
+
+# Tolerances.  Selection: leaf sets identical unless a level's cut margin is
+# below MARGIN (then either side of the cut is correct).  Attention: max-abs
+# ATOL against the oracle on the same selected set (bf16 inputs, fp32
+# accumulation).
+MARGIN = 1e-4
+ATOL = 2e-2
+# Routing checks on the GPU's own candidate sets: scores (relative to 1 + |sigma|),
+# cumulative mass, and the ordering of kept vs dropped probabilities.  fp32 scores
+# and sums carry ~1e-6 relative error.
+SCORE_RTOL = 1e-4
+MASS_TOL = 1e-5
+ORDER_RTOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Exact host copy for the oracle: bf16 as raw uint16 bits, fp32 as float32."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def make_layer(w: W.Workload, device="cuda", seed=None, top_p=None, capacity=None):
+    x = W.generate(w, device=device, seed=seed)
+    cfg = B.config_of(w, capacity=capacity if capacity is not None else w.capacity)
+    if top_p is not None:
+        cfg.top_p = top_p
+    layer = ZhaLayer(cfg, x["k"], x["v"], x["ref_q"])
+    return layer, x
+
+
+def oracle_tree(layer: ZhaLayer, n_tokens: int, keys_host=None):
+    kh = to_host(layer.k) if keys_host is None else keys_host
+    return kh, O.SummaryTree(kh, to_host(layer.ref_q), n_tokens, layer.cfg.chunk, layer.cfg.levels)
+
+
+def _kept_by_head(route, g, G):
+    nk = int(route["n_kept"][g])
+    nodes = route["kept"][g, :nk].numpy().astype(np.int64)
+    masks = route["mask"][g, :nk].numpy().astype(np.int64)
+    return [nodes[(masks >> hl) & 1 == 1] for hl in range(G)]
+
+
+def check_routing(layer: ZhaLayer, qh, n_tokens: int, tree: O.SummaryTree, p: float, label: str = ""):
+    """Level by level, check the GPU's routing against the oracle's arithmetic on the GPU's own
+    candidate sets: candidate sets follow the expansion rule, scores match, stats are exact,
+    and each head's kept set is a valid minimal top-p cut of the oracle's probabilities
+    (mass reaches p, dropping its lightest node falls below p, no dropped node outweighs a
+    kept one), all within rounding tolerances.  Returns (worst score error, per-level kept sets)."""
+    cfg = layer.cfg
+    c, L, H = cfg.chunk, cfg.levels, cfg.n_kv_heads
+    G = cfg.n_q_heads // H
+    top = max([lv for lv in range(1, L + 1) if n_tokens // c ** lv > 0], default=0)
+    routes = {lv: layer.route_level(lv) for lv in range(1, top + 1)}
+    worst = 0.0
+    kept_all = {lv: [None] * cfg.n_q_heads for lv in routes}
+    for g in range(H):
+        prev_kept = None
+        for lv in range(top, 0, -1):
+            r = routes[lv]
+            n_here = n_tokens // c ** lv
+            if lv == top:
+                nodes = np.arange(n_here, dtype=np.int64)
+            else:
+                rp = routes[lv + 1]
+                nk = int(rp["n_kept"][g])
+                parents = rp["kept"][g, :nk].numpy().astype(np.int64)
+                nodes = np.concatenate([(parents[:, None] * c + np.arange(c)[None, :]).ravel(),
+                                        np.arange(c * (n_tokens // c ** (lv + 1)), n_here, dtype=np.int64)])
+            assert int(r["n_cand"][g]) == len(nodes), f"{label} level {lv} group {g}: candidate count"
+            sig = r["sigma"][g, :, :len(nodes)].numpy().astype(np.float64)
+            kept_h = _kept_by_head(r, g, G)
+            s_all, b_all, _ = tree.get(lv, g, nodes) if len(nodes) else (None, None, None)
+            for hl in range(G):
+                h = g * G + hl
+                is_c = sig[hl] > -np.inf
+                cand = nodes[is_c]
+                if lv == top:
+                    expect = nodes
+                else:
+                    up = n_tokens // c ** (lv + 1)
+                    expect = np.sort(np.concatenate([(prev_kept[hl][:, None] * c + np.arange(c)[None, :]).ravel(),
+                                                     np.arange(c * up, n_here, dtype=np.int64)]))
+                assert cand.tolist() == expect.tolist(), f"{label} level {lv} head {h}: candidate set"
+                kept = kept_h[hl]
+                assert int(r["stats"][h, 0]) == len(cand) and int(r["stats"][h, 1]) == len(kept), \
+                    f"{label} level {lv} head {h}: stats"
+                if len(cand) == 0:
+                    assert len(kept) == 0
+                    continue
+                so = O.plane_scores(qh[h], s_all[is_c], b_all[is_c], tree.tau)
+                err = float((np.abs(sig[hl][is_c] - so) / (1.0 + np.abs(so))).max())
+                worst = max(worst, err)
+                assert err <= SCORE_RTOL, f"{label} level {lv} head {h}: score error {err:.3g}"
+                e = np.exp(so - so.max())
+                pi = e / e.sum()
+                inkept = np.isin(cand, kept)
+                assert set(kept.tolist()) <= set(cand.tolist())
+                if p >= 1.0:
+                    assert inkept.all(), f"{label} level {lv} head {h}: p=1 must keep all"
+                    continue
+                assert len(kept) >= 1
+                mass = pi[inkept].sum()
+                lightest = pi[inkept].min()
+                assert mass >= p - MASS_TOL, f"{label} level {lv} head {h}: kept mass {mass:.6f} < p"
+                assert mass - lightest < p + MASS_TOL, f"{label} level {lv} head {h}: cut not minimal"
+                if (~inkept).any():
+                    heaviest_dropped = pi[~inkept].max()
+                    assert heaviest_dropped <= lightest * (1 + ORDER_RTOL) + 1e-15, \
+                        f"{label} level {lv} head {h}: dropped {heaviest_dropped:.3g} > kept {lightest:.3g}"
+            prev_kept = kept_h
+            for hl in range(G):
+                kept_all[lv][g * G + hl] = kept_h[hl].tolist()
+    return worst, kept_all
+
+
+def compare_decode(layer: ZhaLayer, x_q: torch.Tensor, n_tokens: int, tree: O.SummaryTree, kh, vh,
+                   p: float, label: str = "", check_outputs_vs_oracle: bool = True, heads=None):
+    """Decode on the GPU and compare with the oracle.
+
+    Every head: routing checked level by level (check_routing) and attention checked on
+    the GPU's own selection.  Heads whose oracle cut margins are all >= MARGIN: per-level
+    node sets identical to the oracle's own routing and output within ATOL of it.
+    Returns (n_exempt, max attention error, worst score error)."""
+    out = layer.decode(x_q).clone()
+    torch.cuda.synchronize()
+    out_h = out.cpu().numpy().astype(np.float64)
+    qh = to_host(x_q)
+    worst_sig, gk = check_routing(layer, qh, n_tokens, tree, p, label)
+    G = layer.cfg.n_q_heads // layer.cfg.n_kv_heads
+    c = layer.cfg.chunk
+    n_exempt, max_err = 0, 0.0
+    for h in (range(layer.cfg.n_q_heads) if heads is None else heads):
+        r = O.route_head(qh[h], tree, h // G, p)
+        exempt = r.min_margin < MARGIN
+        n_exempt += exempt
+        if not exempt:
+            for lv in r.levels:
+                got_h = gk[lv.level][h] if lv.level in gk else []
+                assert got_h == lv.kept.tolist(), (
+                    f"{label} head {h} level {lv.level}: GPU kept {got_h[:20]}... ({len(got_h)}) vs oracle "
+                    f"{lv.kept.tolist()[:20]}... ({len(lv.kept)}), margin {lv.margin:.3g}")
+        leaves = gk[1][h] if 1 in gk else []
+        toks = O.final_token_set(np.array(leaves, dtype=np.int64), n_tokens, c)
+        ref = O.attend(qh[h], kh[h // G], vh[h // G], toks, tree.tau)
+        err = float(np.abs(out_h[h] - ref).max())
+        max_err = max(max_err, err)
+        assert err <= ATOL, f"{label} head {h}: attention error {err:.3g} on the GPU's selected set"
+        if check_outputs_vs_oracle and not exempt:
+            o_ref = O.attend(qh[h], kh[h // G], vh[h // G], r.tokens, tree.tau)
+            err2 = float(np.abs(out_h[h] - o_ref).max())
+            assert err2 <= ATOL, f"{label} head {h}: output error {err2:.3g} vs oracle decode"
+    return n_exempt, max_err, worst_sig
+
+
+def compare_tree(layer: ZhaLayer, tree: O.SummaryTree, n_tokens: int, sample: int | None = None, seed: int = 0,
+                 rtol: float = 2e-5):
+    """Summary planes of the GPU tree against the oracle's (all nodes, or a sample per level)."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for lv in range(1, layer.cfg.levels + 1):
+        n = n_tokens // layer.cfg.chunk ** lv
+        if n == 0:
+            continue
+        s_g, b_g, l_g = (t.cpu().numpy() for t in layer.tree_level(lv))
+        for g in range(layer.cfg.n_kv_heads):
+            nodes = np.arange(n) if sample is None or n <= sample else np.sort(rng.choice(n, sample, replace=False))
+            s_o, b_o, l_o = tree.get(lv, g, nodes)
+            for name, a, b in (("lse", l_g[g, nodes], l_o), ("b", b_g[g, nodes], b_o), ("s", s_g[g, nodes], s_o)):
+                err = np.abs(a - b) / (1.0 + np.abs(b))
+                e = float(err.max())
+                worst = max(worst, e)
+                assert e <= rtol, f"level {lv} head {g} {name}: max rel err {e:.3g}"
+    return worst

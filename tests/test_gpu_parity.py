@@ -1,0 +1,201 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on seeded inputs.
+
+Bars: leaf and per-level node sets identical per query head unless some level's
+cut margin is below 1e-4; attention within 2e-2 max-abs of the oracle on the
+same selected set; summaries within 2e-5 relative; integer outputs exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hierarchical_tree_indexed_zha_amd import binding as B
+from hierarchical_tree_indexed_zha_amd import workloads as W
+from tests.gpu_util import (ATOL, compare_decode, compare_tree, make_layer, oracle_tree, say, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(name, n, levels=None, steps=4, **kw):
+    return W.scaled(W.get(name), n, steps=steps, levels=levels, **kw)
+
+
+# Small-to-medium cases: several tiles, ragged tails, every generator, both dtypes, R = 1 and 16.
+CASES = [
+    ("tiny", W.get("tiny")),                                 # fp32, R=16, c=4, L=6, N=16384 (full size)
+    ("light@32768", _w("light", 32768)),                     # bf16, R=1, c=8, L=3
+    ("light@30001", _w("light", 30001, levels=4)),           # ragged: tail, orphans, empty top level
+    ("deep@16384", _w("deep", 16384, levels=6)),             # R=16, c=4, 4 top nodes
+    ("deep@20003", _w("deep", 20003, levels=6)),             # ragged deep tree
+    ("wide@16384", _w("wide", 16384)),                       # c=256, L=1, flat
+    ("wide@16500", _w("wide", 16500)),                       # ragged flat
+    ("ultra@65536", _w("ultra", 65536, levels=5)),           # light router on topic data
+]
+
+
+@pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
+def test_tree_summaries_match_oracle(name, w):
+    say(f"[tree] {name}")
+    layer, x = make_layer(w)
+    layer.build(w.n_tokens)
+    torch.cuda.synchronize()
+    kh, tree = oracle_tree(layer, w.n_tokens)
+    worst = compare_tree(layer, tree, w.n_tokens, sample=512)
+    say(f"[tree] {name}: worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
+def test_decode_matches_oracle(name, w):
+    say(f"[decode] {name}")
+    layer, x = make_layer(w)
+    layer.build(w.n_tokens)
+    kh, tree = oracle_tree(layer, w.n_tokens)
+    vh = to_host(layer.v)
+    tot_ex, worst, wsig = 0, 0.0, 0.0
+    for t in range(min(3, w.steps)):
+        ex, err, es = compare_decode(layer, x["q"][t], w.n_tokens, tree, kh, vh, w.top_p, label=f"{name} step {t}")
+        tot_ex += ex
+        worst = max(worst, err)
+        wsig = max(wsig, es)
+    say(f"[decode] {name}: heads exempt from exact identity {tot_ex}/{3 * w.n_q_heads}, "
+        f"max attention err {worst:.2e}, max score err {wsig:.2e}")
+
+
+@pytest.mark.parametrize("name,w", CASES[:4], ids=[c[0] for c in CASES[:4]])
+def test_p_one_equals_dense(name, w):
+    """p = 1 keeps every node, so the decode reproduces dense attention."""
+    say(f"[p=1] {name}")
+    layer, x = make_layer(w, top_p=1.0)
+    layer.build(w.n_tokens)
+    out = layer.decode(x["q"][0]).clone()
+    dense = layer.dense(x["q"][0]).clone()
+    torch.cuda.synchronize()
+    for lv in range(1, w.levels + 1):
+        n = w.n_tokens // w.chunk ** lv
+        if n:
+            st = layer.route_level(lv)["stats"]
+            assert torch.equal(st[:, 0], st[:, 1])         # every candidate kept
+    ref = O.dense_decode(to_host(x["q"][0]), to_host(layer.k), to_host(layer.v), w.n_tokens)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= ATOL
+    assert float((out - dense).abs().max()) <= 1e-4
+
+
+DENSE = [
+    ("tiny", W.get("tiny"), 16384),
+    ("light@8192", _w("light", 8192), 8192),
+    ("light@777", _w("light", 777), 777),
+    ("deep@50000", _w("deep", 50000), 50000),
+    ("light@1", _w("light", 64), 1),
+    ("light@31", _w("light", 64), 31),
+]
+
+
+@pytest.mark.parametrize("name,w,n", DENSE, ids=[d[0] for d in DENSE])
+def test_dense_matches_oracle(name, w, n):
+    say(f"[dense] {name} n={n}")
+    layer, x = make_layer(w)
+    layer.n_tokens = n
+    out = layer.dense(x["q"][0]).clone()
+    torch.cuda.synchronize()
+    ref = O.dense_decode(to_host(x["q"][0]), to_host(layer.k), to_host(layer.v), n)
+    err = float(np.abs(out.cpu().numpy() - ref).max())
+    say(f"[dense] {name}: max err {err:.2e}")
+    assert err <= ATOL
+
+
+EDGE = [
+    # (label, workload, n_tokens): no complete chunk, one chunk, exact powers, just past them
+    ("N=1", _w("deep", 1024, levels=3), 1),
+    ("N=3<c", _w("deep", 1024, levels=3), 3),
+    ("N=c", _w("deep", 1024, levels=3), 4),
+    ("N=c^L", _w("deep", 1024, levels=3), 64),
+    ("N=c^L+1", _w("deep", 1024, levels=3), 65),
+    ("N=c^L-1", _w("deep", 1024, levels=3), 63),
+    ("N=1000", _w("deep", 1024, levels=3), 1000),
+    ("c8,N=520", _w("light", 1024, levels=3), 520),
+    ("wide,N=255", _w("wide", 1024), 255),
+    ("wide,N=257", _w("wide", 1024), 257),
+]
+
+
+@pytest.mark.parametrize("label,w,n", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_sizes(label, w, n):
+    say(f"[edge] {label}")
+    layer, x = make_layer(w)
+    layer.build(n)
+    kh, tree = oracle_tree(layer, n)
+    vh = to_host(layer.v)
+    compare_tree(layer, tree, n)
+    compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label=label)
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 8, 16, 32])
+def test_reference_query_counts(R):
+    w = _w("deep", 8192, levels=4, n_ref=R)
+    say(f"[R] R={R}")
+    layer, x = make_layer(w)
+    layer.build(w.n_tokens)
+    kh, tree = oracle_tree(layer, w.n_tokens)
+    compare_tree(layer, tree, w.n_tokens, sample=256)
+    compare_decode(layer, x["q"][0], w.n_tokens, tree, kh, to_host(layer.v), w.top_p, label=f"R={R}")
+
+
+@pytest.mark.parametrize("heads", [(1, 1), (2, 4), (1, 16), (3, 12)])
+def test_group_shapes(heads):
+    hkv, hq = heads
+    w = _w("light", 4096, levels=2, n_kv_heads=hkv, n_q_heads=hq)
+    say(f"[group] H_kv={hkv} H_q={hq}")
+    layer, x = make_layer(w)
+    layer.build(w.n_tokens)
+    kh, tree = oracle_tree(layer, w.n_tokens)
+    compare_decode(layer, x["q"][0], w.n_tokens, tree, kh, to_host(layer.v), w.top_p, label=f"{heads}")
+
+
+@pytest.mark.parametrize("name,w,m", [("light@4000", _w("light", 4000, levels=3, steps=100), 100),
+                                      ("deep@1000", _w("deep", 1000, levels=4, steps=70, append=True), 70),
+                                      ("ultra@4090", _w("ultra", 4090, levels=3, steps=80), 80)])
+def test_append_matches_oracle(name, w, m):
+    """Tree after m appends equals the oracle tree over all n+m tokens; decode after appends matches."""
+    say(f"[append] {name}")
+    layer, x = make_layer(w, capacity=w.n_tokens + m)
+    layer.build(w.n_tokens)
+    for t in range(m):
+        layer.append(x["k_app"][t], x["v_app"][t])
+    torch.cuda.synchronize()
+    n = w.n_tokens + m
+    k_all = layer.k.clone()
+    assert torch.equal(k_all[:, w.n_tokens:n], x["k_app"][:m].transpose(0, 1))
+    kh, tree = oracle_tree(layer, n)
+    compare_tree(layer, tree, n)
+    compare_decode(layer, x["q"][0], n, tree, kh, to_host(layer.v), w.top_p, label=f"{name} after append")
+
+
+def test_decode_is_deterministic():
+    w = _w("light", 65536)
+    say("[determinism]")
+    layer, x = make_layer(w)
+    layer.build(w.n_tokens)
+    a = layer.decode(x["q"][0]).clone()
+    ra = layer.route_level(1)
+    b = layer.decode(x["q"][0]).clone()
+    rb = layer.route_level(1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for k in ra:
+        assert torch.equal(ra[k], rb[k]), k
+
+
+def test_abi_rejects_bad_arguments_on_device():
+    w = _w("light", 1024)
+    layer, x = make_layer(w)
+    with pytest.raises(B.ZhaError) as e:
+        B.zha_decode_step(layer.cfg, layer.bufs, w.capacity + 1, x["q"][0], layer.out)
+    assert e.value.code == B.ZHA_ERR_CAPACITY
+    with pytest.raises(B.ZhaError) as e:
+        B.zha_decode_step(layer.cfg, layer.bufs, 0, x["q"][0], layer.out)
+    assert e.value.code == B.ZHA_ERR_ARG
+    with pytest.raises(B.ZhaError) as e:
+        B.zha_append_token(layer.cfg, layer.bufs, w.capacity, x["k"][:, 0], x["v"][:, 0])
+    assert e.value.code == B.ZHA_ERR_CAPACITY

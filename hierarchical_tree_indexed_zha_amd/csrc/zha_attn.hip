@@ -21,7 +21,7 @@
 // bytes of one token row and the contraction index of the PV product is
 // permuted so that each lane's eight B-operand values come from eight such
 // loads.  P is split into bf16 hi + lo parts (two MFMAs), so the PV product
-// keeps ~16 bits of P.  fp32 path: the same tiling on v_mfma_f32_16x16x4_f32.
+// keeps 16 significant bits of P.  fp32 path: the same tiling on v_mfma_f32_16x16x4_f32.
 #include "zha_common.h"
 #include "zha_internal.h"
 
@@ -33,7 +33,12 @@ constexpr int kTileSlots = 32;
 constexpr int kMinTilesPerBlock = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ uint32_t pick_half(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xFFFFu); }
+// Byte permute: bytes of (hi_src:lo_src) picked by `sel` (v_perm_b32).
+__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+constexpr uint32_t kLowHalves = 0x05040100u;    // (lo half of lo_src) | (lo half of hi_src) << 16
+constexpr uint32_t kHighHalves = 0x07060302u;   // (hi half of lo_src) | (hi half of hi_src) << 16
 
 __device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -102,7 +107,7 @@ __device__ __forceinline__ int active_blocks(int64_t tiles, int Bg) {
 
 // grid (Bg, H_kv), 256 threads.
 template <bool BF16, bool DENSE>
-__global__ __launch_bounds__(kThreads) void zha_attn_kernel(ZhaAttnArgs a, int G, int c, float tau, int Bg) {
+__global__ __launch_bounds__(kThreads, 3) void zha_attn_kernel(ZhaAttnArgs a, int G, int c, float tau, int Bg) {
     __shared__ int32_t s_tok[kWaves][kTileSlots];
     __shared__ uint32_t s_msk[kWaves][kTileSlots];
     __shared__ float s_buf[kWaves * 16 * ZHA_D];          // P tiles during the loop, partial O after it
@@ -150,13 +155,17 @@ __global__ __launch_bounds__(kThreads) void zha_attn_kernel(ZhaAttnArgs a, int G
 #pragma unroll
     for (int c8 = 0; c8 < 8; ++c8) O[c8] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // the slot -> token map of the next tile is fetched while this tile computes
+    int32_t nx_tok = 0;
+    uint32_t nx_msk = 0;
+    if (lane < kTileSlots && t0 + wave < t1)
+        slot_to_token<DENSE>(a, sp, g, c, allg, (t0 + wave) * kTileSlots + lane, &nx_tok, &nx_msk);
     for (int64_t t = t0 + wave; t < t1; t += kWaves) {
         if (lane < kTileSlots) {
-            int32_t tok;
-            uint32_t msk;
-            slot_to_token<DENSE>(a, sp, g, c, allg, t * kTileSlots + lane, &tok, &msk);
-            s_tok[wave][lane] = tok;
-            s_msk[wave][lane] = msk;
+            s_tok[wave][lane] = nx_tok;
+            s_msk[wave][lane] = nx_msk;
+            if (t + kWaves < t1)
+                slot_to_token<DENSE>(a, sp, g, c, allg, (t + kWaves) * kTileSlots + lane, &nx_tok, &nx_msk);
         }
         zha_wave_lds_sync();
 
@@ -216,8 +225,7 @@ __global__ __launch_bounds__(kThreads) void zha_attn_kernel(ZhaAttnArgs a, int G
             const int h = 4 * q4 + i;
             const float x0 = ((mk0 >> h) & 1u) ? S[0][i] * scale : zha_neg_inf();
             const float x1 = ((mk1 >> h) & 1u) ? S[1][i] * scale : zha_neg_inf();
-            float mx = fmaxf(x0, x1);
-            for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+            const float mx = zha_row16_max(fmaxf(x0, x1));
             const float mn = fmaxf(m_run[i], mx);
             float alpha, p0, p1;
             if (mn == zha_neg_inf()) {
@@ -227,8 +235,7 @@ __global__ __launch_bounds__(kThreads) void zha_attn_kernel(ZhaAttnArgs a, int G
                 p0 = exp2f(x0 - mn);
                 p1 = exp2f(x1 - mn);
             }
-            float rs = p0 + p1;
-            for (int o = 8; o > 0; o >>= 1) rs += __shfl_xor(rs, o, 16);
+            const float rs = zha_row16_sum(p0 + p1);
             l_run[i] = l_run[i] * alpha + rs;
             m_run[i] = mn;
 #pragma unroll
@@ -240,26 +247,28 @@ __global__ __launch_bounds__(kThreads) void zha_attn_kernel(ZhaAttnArgs a, int G
 
         if (BF16) {
             // A operand: row head j, contraction slots 4e + q4, e = 0..7, as bf16 hi + lo
+            // parts: hi = P truncated to bf16, lo = the residual truncated to bf16, so
+            // hi + lo keeps 16 significant bits of P.
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 const float pa = s_p[j * 33 + 4 * (2 * e2) + q4];
                 const float pb = s_p[j * 33 + 4 * (2 * e2 + 1) + q4];
-                const uint32_t ha = zha_f32_to_bf16_rne(pa), hb = zha_f32_to_bf16_rne(pb);
-                const uint32_t la = zha_f32_to_bf16_rne(pa - zha_bf16_to_f32(ha));
-                const uint32_t lb = zha_f32_to_bf16_rne(pb - zha_bf16_to_f32(hb));
-                hi[e2] = ha | (hb << 16);
-                lo[e2] = la | (lb << 16);
+                const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb);
+                hi[e2] = perm(ub, ua, kHighHalves);
+                const float ra = pa - __uint_as_float(ua & 0xFFFF0000u);
+                const float rb = pb - __uint_as_float(ub & 0xFFFF0000u);
+                lo[e2] = perm(__float_as_uint(rb), __float_as_uint(ra), kHighHalves);
             }
             const zha_bf16x8 Ahi = zha_as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
             const zha_bf16x8 Alo = zha_as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
 #pragma unroll
             for (int c8 = 0; c8 < 8; ++c8) {
-                const int w = c8 >> 1, odd = c8 & 1;
+                const int w = c8 >> 1;
+                const uint32_t sel = (c8 & 1) ? kHighHalves : kLowHalves;
                 uint32_t bw[4];
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2)
-                    bw[e2] = pick_half(comp(vr[2 * e2], w), odd) | (pick_half(comp(vr[2 * e2 + 1], w), odd) << 16);
+                for (int e2 = 0; e2 < 4; ++e2) bw[e2] = perm(comp(vr[2 * e2 + 1], w), comp(vr[2 * e2], w), sel);
                 const zha_bf16x8 Bv = zha_as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
                 O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bv, O[c8], 0, 0, 0);
                 O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bv, O[c8], 0, 0, 0);

@@ -89,6 +89,25 @@ __device__ __forceinline__ float zha_wave_max(float v) {
     return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)x, 63));
 }
 
+// Reductions over each row of 16 lanes (DPP row_ror); every lane of the row
+// receives its row's result.
+__device__ __forceinline__ float zha_row16_max(float v) {
+    uint32_t x = __float_as_uint(v);
+    x = __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(zha_dpp<0x128, 0xF>(x, x))));
+    x = __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(zha_dpp<0x124, 0xF>(x, x))));
+    x = __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(zha_dpp<0x122, 0xF>(x, x))));
+    x = __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(zha_dpp<0x121, 0xF>(x, x))));
+    return __uint_as_float(x);
+}
+
+__device__ __forceinline__ float zha_row16_sum(float v) {
+    v += __uint_as_float(zha_dpp<0x128, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    v += __uint_as_float(zha_dpp<0x124, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    v += __uint_as_float(zha_dpp<0x122, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    v += __uint_as_float(zha_dpp<0x121, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    return v;
+}
+
 __device__ __forceinline__ float zha_wave_sum(float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;

@@ -145,9 +145,14 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
             for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], fmaf(tau, acc[i], bv));
         }
         // max over the planes of one candidate (adjacent columns)
-        for (int o = span >> 1; o > 0; o >>= 1)
+        if (span == 16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], __shfl_xor(best[i], o, 16));
+            for (int i = 0; i < 4; ++i) best[i] = zha_row16_max(best[i]);
+        } else {
+            for (int o = span >> 1; o > 0; o >>= 1)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], __shfl_xor(best[i], o, 16));
+        }
         if (valid && (j % span) == 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -223,15 +228,120 @@ __device__ __forceinline__ uint64_t mass_of(uint32_t key) {
     return (uint64_t)(exp2f(-(float)key * (1.4426950408889634f / kKeyScale)) * kFix);
 }
 
+constexpr int kSmallN = 1024;   // groups with at most this many candidates select in one workgroup
+constexpr int kSmallK = kSmallN / 64;
+static_assert(ZHA_MAX_GROUP * kSmallN <= 16384, "small-path scores must fit the key buffer");
+static_assert(ZHA_MAX_GROUP * 256 <= 2 * 2048, "small-path histograms must fit the histogram buffers");
+
+// One wave selects for query head (g, hl) among n <= kSmallN candidates whose
+// scores are in LDS (sg); position lane + 64k sits in register slot k.  8-bit
+// digits, wave-local histograms (hist: 256 u64, cntb: 256 u32), no workgroup
+// barrier.  The kept bitmap words go to kw[0 .. nk).
+__device__ void select_head_wave(const float* sg, int64_t n, float top_p, uint64_t* hist, uint32_t* cntb,
+                                 uint64_t* kw, uint32_t* n_cand_out, uint32_t* n_kept_out) {
+    constexpr int K = kSmallK;
+    const int lane = threadIdx.x & 63;
+    const int nk = (int)((n + 63) / 64);
+    float sv[K];
+    float m = zha_neg_inf();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t pos = lane + 64 * k;
+        sv[k] = (pos < n) ? sg[pos] : zha_neg_inf();
+        m = fmaxf(m, sv[k]);
+    }
+    m = zha_wave_max(m);
+    uint32_t key[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) key[k] = key_of(sv[k], m);
+    const bool none = m == zha_neg_inf();
+    const bool keep_all = !none && top_p >= 1.0f;
+    uint32_t ustar = 0, ties = 0;
+    uint64_t need = 0;
+    if (!none && !keep_all) {
+        uint32_t prefix = 0;
+#pragma unroll 1
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { hist[lane * 4 + i] = 0; cntb[lane * 4 + i] = 0; }
+            zha_wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (k < nk && key[k] < kNoMass && (pass == 0 || (key[k] >> (shift + 8)) == prefix)) {
+                    const uint32_t b = (key[k] >> shift) & 255u;
+                    atomicAdd((unsigned long long*)&hist[b], (unsigned long long)mass_of(key[k]));
+                    atomicAdd(&cntb[b], 1u);
+                }
+            }
+            zha_wave_lds_sync();
+            uint64_t hb[4], mine = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { hb[i] = hist[lane * 4 + i]; mine += hb[i]; }
+            uint64_t total;
+            uint64_t before = wave_excl_scan_u64(mine, &total);
+            if (pass == 0) {
+                uint64_t T = (uint64_t)ceil((double)top_p * (double)total);
+                need = T < 1 ? 1 : (T > total ? total : T);
+            }
+            int my_bin = -1;
+            uint64_t my_before = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (before < need && before + hb[i] >= need && my_bin < 0) { my_bin = lane * 4 + i; my_before = before; }
+                before += hb[i];
+            }
+            const uint64_t found = __ballot(my_bin >= 0);
+            const int src = __ffsll((long long)found) - 1;
+            const uint32_t bin = (uint32_t)__shfl(my_bin, src, 64);
+            need -= zha_readlane_u64(my_before, src);
+            prefix = (prefix << 8) | bin;
+            if (pass == 3) { ustar = prefix; ties = cntb[bin]; }
+            zha_wave_lds_sync();
+        }
+    }
+    uint32_t n_cand = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const bool cand = k < nk && key[k] != kNotCand;
+        const bool kept = !none && (keep_all ? cand : (cand && key[k] < kNoMass && (key[k] < ustar || (key[k] == ustar && ties == 1))));
+        const uint64_t wk = __ballot(kept);
+        n_cand += __popcll(__ballot(cand));
+        if (lane == 0 && k < nk) kw[k] = wk;
+    }
+    zha_wave_lds_sync();
+    if (!none && !keep_all && ties > 1) {
+        // several candidates share the cut key: take them in ascending position order
+        uint64_t run = 0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint64_t w = (k < nk && key[k] == ustar) ? mass_of(key[k]) : 0ull;
+            uint64_t tot;
+            const uint64_t ex = wave_excl_scan_u64(w, &tot);
+            const uint64_t extra = __ballot(w > 0 && run + ex < need);
+            if (lane == 0 && k < nk) kw[k] |= extra;
+            run += tot;
+        }
+        zha_wave_lds_sync();
+    }
+    uint32_t n_kept = 0;
+#pragma unroll 1
+    for (int k = 0; k < nk; ++k) n_kept += __popcll(kw[k]);
+    *n_cand_out = n_cand;
+    *n_kept_out = n_kept;
+}
+
 // grid (H_q), 1024 threads: one query head per workgroup; the last head of a
 // group to finish writes the group's kept list and the next level's candidates.
 // Keys sit in LDS (kLdsKeys candidates) or are recomputed from the scores on
 // every pass for larger frontiers; all passes are rolled loops.
 __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelArgs a, int G, int c,
                                                                        float top_p) {
-    __shared__ uint32_t keys[kLdsKeys];
-    __shared__ uint64_t histbuf[2][2048];
-    __shared__ uint32_t cntbuf[2][2048];
+    __shared__ uint32_t keys[kLdsKeys];                 // also: small-path scores [G][kSmallN]
+    __shared__ uint64_t histbuf[2][2048];               // also: small-path histograms [G][256]
+    __shared__ uint32_t cntbuf[2][2048];                // also: small-path counts [G][256]
+    __shared__ int32_t s_nid[kSmallN];
+    __shared__ uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
     __shared__ float swf[kSelWaves];
     __shared__ int s_bin;
     __shared__ uint64_t s_before, s_need, s_run;
@@ -240,7 +350,82 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
 
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n = a.top ? a.n_top : (int64_t)a.ncand[g];
+    const size_t lrow = (size_t)g * a.cap;
+    // Small frontiers: the group's first workgroup selects for all G heads (one wave
+    // each) and merges from LDS.  Scores and node ids of the first kSmallN positions
+    // are fetched together with the candidate count.
+    float* s_sig = reinterpret_cast<float*>(keys);                        // [G][kSmallN]
+    int64_t n;
+    if (a.top) {
+        n = a.n_top;
+    } else {
+        const int32_t nc = a.ncand[g];
+        const int32_t nd = tid < a.cap ? a.cand_node[lrow + tid] : 0;
+        n = nc;
+        if (n <= kSmallN && hl == 0) s_nid[tid] = nd;
+    }
+    if (n <= kSmallN) {
+        if (hl != 0) return;                       // the same decision for every head of the group
+        for (int i = tid; i < G * kSmallN; i += kSelThreads) {
+            const int hh = i / kSmallN, pos = i - hh * kSmallN;
+            s_sig[i] = pos < n ? a.sig[((size_t)g * G + hh) * a.cap + pos] : zha_neg_inf();
+        }
+        __syncthreads();
+        uint64_t* kw = s_kw;                                              // [G][kSmallK]
+        if (wave < G) {
+            uint32_t nc_h, nk_h;
+            select_head_wave(s_sig + wave * kSmallN, n, top_p, &histbuf[0][0] + wave * 256,
+                             &cntbuf[0][0] + wave * 256, kw + wave * kSmallK, &nc_h, &nk_h);
+            if (lane == 0) {
+                a.stats[2 * (g * G + wave) + 0] = (int32_t)nc_h;
+                a.stats[2 * (g * G + wave) + 1] = (int32_t)nk_h;
+            }
+            for (int k = lane; k < (int)((n + 63) / 64); k += 64)
+                a.kbm[((size_t)g * G + wave) * a.wcap + k] = kw[wave * kSmallK + k];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        // merge the heads' kept words: kept list and the next level's candidates
+        const int nk = (int)((n + 63) / 64);
+        const size_t nrow = (size_t)g * a.next_cap;
+        const uint64_t lt = (1ull << lane) - 1ull;
+        uint64_t run = 0;
+#pragma unroll 1
+        for (int k = 0; k < nk; ++k) {
+            uint64_t u = 0;
+#pragma unroll 1
+            for (int hh = 0; hh < G; ++hh) u |= kw[hh * kSmallK + k];
+            if ((u >> lane) & 1ull) {
+                const uint64_t rank = run + __popcll(u & lt);
+                uint32_t msk = 0;
+#pragma unroll 1
+                for (int hh = 0; hh < G; ++hh) msk |= (uint32_t)((kw[hh * kSmallK + k] >> lane) & 1ull) << hh;
+                const int64_t pos = lane + 64 * k;
+                const int32_t node = a.top ? (int32_t)pos : s_nid[pos];
+                a.klist[lrow + rank] = node;
+                a.kmask[lrow + rank] = msk;
+                if (a.next_node) {
+#pragma unroll 1
+                    for (int i = 0; i < c; ++i) {
+                        a.next_node[nrow + rank * c + i] = node * c + i;
+                        a.next_mask[nrow + rank * c + i] = msk;
+                    }
+                }
+            }
+            run += __popcll(u);
+        }
+        if (a.next_node) {
+            const uint32_t allg = all_heads(G);
+            const int64_t n_orph = a.orph_hi - a.orph_lo;
+            for (int64_t o = lane; o < n_orph; o += 64) {
+                a.next_node[nrow + run * c + o] = (int32_t)(a.orph_lo + o);
+                a.next_mask[nrow + run * c + o] = allg;
+            }
+            if (lane == 0) a.next_ncand[g] = (int32_t)(run * c + n_orph);
+        }
+        if (lane == 0) a.nkept[g] = (int32_t)run;
+        return;
+    }
     const float* sg = a.sig + ((size_t)g * G + hl) * a.cap;
     uint64_t* bm = a.kbm + ((size_t)g * G + hl) * a.wcap;
     const int64_t nwords = (n + 63) / 64;
@@ -365,7 +550,6 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
     if (!s_last) return;
     __threadfence();
     const uint64_t* gbm = a.kbm + (size_t)g * G * a.wcap;
-    const size_t lrow = (size_t)g * a.cap;
     const size_t nrow = (size_t)g * a.next_cap;
     // Merge in steps of mw bitmap words (16384 positions).  LDS is reused: node ids
     // of the step's positions in `keys`, the G head words in histbuf, the union in

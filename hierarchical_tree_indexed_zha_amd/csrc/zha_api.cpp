@@ -86,7 +86,7 @@ struct Layout {
     std::vector<size_t> t_s, t_b, t_l;
     size_t tree_bytes = 0;
     // decode scratch
-    std::vector<size_t> sig, kbm, cnode, cmask, klist, kmask, ncand, nkept, done, stats;
+    std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, done, stats;
     std::vector<int64_t> wcap;            // bitmap words per head per level
     size_t pm = 0, pl = 0, po = 0, nact = 0;
     size_t scratch_bytes = 0;
@@ -121,7 +121,7 @@ Layout make_layout(const zha_config* cfg) {
     y.tree_bytes = off;
 
     off = 0;
-    for (auto* v : {&y.sig, &y.kbm, &y.cnode, &y.cmask, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.done, &y.stats})
+    for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.done, &y.stats})
         v->assign(y.L + 1, 0);
     y.wcap.assign(y.L + 1, 0);
     for (int l = 1; l <= y.L; ++l) {
@@ -129,8 +129,6 @@ Layout make_layout(const zha_config* cfg) {
         y.wcap[l] = (int64_t)((n + 63) / 64);
         y.sig[l] = off;   off = align_up(off + sizeof(float) * H * G * n);
         y.kbm[l] = off;   off = align_up(off + sizeof(uint64_t) * H * G * (size_t)y.wcap[l]);
-        y.cnode[l] = off; off = align_up(off + sizeof(int32_t) * H * n);
-        y.cmask[l] = off; off = align_up(off + sizeof(uint32_t) * H * n);
         y.klist[l] = off; off = align_up(off + sizeof(int32_t) * H * n);
         y.kmask[l] = off; off = align_up(off + sizeof(uint32_t) * H * n);
         y.ncand[l] = off; off = align_up(off + sizeof(int32_t) * H);
@@ -316,8 +314,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.cap = y.cap[l];
         a.top = l == top ? 1 : 0;
         a.n_top = n_nodes(cfg, n_tokens, l);
-        a.cand_node = (const int32_t*)(X + y.cnode[l]);
-        a.cand_mask = (const uint32_t*)(X + y.cmask[l]);
+        a.dc = zha_make_div((uint32_t)c);
         a.ncand = (int32_t*)(X + y.ncand[l]);
         a.sig = (float*)(X + y.sig[l]);
         a.kbm = (uint64_t*)(X + y.kbm[l]);
@@ -327,18 +324,18 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.klist = (int32_t*)(X + y.klist[l]);
         a.kmask = (uint32_t*)(X + y.kmask[l]);
         a.nkept = (int32_t*)(X + y.nkept[l]);
-        if (l > 1) {
-            a.next_node = (int32_t*)(X + y.cnode[l - 1]);
-            a.next_mask = (uint32_t*)(X + y.cmask[l - 1]);
-            a.next_ncand = (int32_t*)(X + y.ncand[l - 1]);
-            a.next_cap = y.cap[l - 1];
-            a.orph_lo = (int64_t)c * n_nodes(cfg, n_tokens, l);
-            a.orph_hi = n_nodes(cfg, n_tokens, l - 1);
+        if (l < top) {
+            a.pklist = (const int32_t*)(X + y.klist[l + 1]);
+            a.pkmask = (const uint32_t*)(X + y.kmask[l + 1]);
+            a.pnkept = (const int32_t*)(X + y.nkept[l + 1]);
+            a.pcap = y.cap[l + 1];
+            a.orph_lo = (int64_t)c * n_nodes(cfg, n_tokens, l + 1);
+            a.orph_hi = n_nodes(cfg, n_tokens, l);
         } else {
-            a.next_node = nullptr;
-            a.next_mask = nullptr;
-            a.next_ncand = nullptr;
-            a.next_cap = 0;
+            a.pklist = nullptr;
+            a.pkmask = nullptr;
+            a.pnkept = nullptr;
+            a.pcap = 0;
             a.orph_lo = a.orph_hi = 0;
         }
         const int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);

@@ -18,19 +18,49 @@ hipError_t zha_launch_kv_write(int kv_dtype, void* K, void* V, const void* kn, c
                                int64_t cap_tok, int64_t row, hipStream_t stream);
 
 // ---- per-level routing (zha_route.hip)
+// Unsigned 32-bit division by a divisor fixed per launch (the chunk size),
+// by multiplication with a precomputed reciprocal: the round-up method of
+// Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication" (PLDI 1994), section 4.  With l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0)
+// where t = mulhi(m, n), exact for every 32-bit n and 1 <= d < 2^31.
+struct ZhaDiv {
+    uint32_t d, m, s1, s2;
+};
+inline ZhaDiv zha_make_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    ZhaDiv r;
+    r.d = d;
+    r.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    r.s1 = l < 1 ? l : 1;
+    r.s2 = l > 1 ? l - 1 : 0;
+    return r;
+}
+__device__ __forceinline__ uint32_t zha_div(uint32_t n, const ZhaDiv& v) {
+    const uint32_t t = __umulhi(n, v.m);
+    return (t + ((n - t) >> v.s1)) >> v.s2;
+}
+
 // Level l's candidates sit at positions 0..n-1 in ascending node order: at the
-// first routed level they are nodes 0..n_top-1 seen by every head; below it,
-// cand_node/cand_mask/ncand were written by the level above (children of its
-// kept nodes, then the orphans of this level).
+// first routed level they are nodes 0..n_top-1 seen by every head; below it they
+// are the children of the level above's kept nodes (its kept list, ascending,
+// with the heads that kept each) followed by this level's orphans, nodes
+// [orph_lo, orph_hi) seen by every head.
 struct ZhaLevelArgs {
     const float* S;            // level planes [H_kv][cap][R][128]
     const float* B;            // [H_kv][cap][R]
     int64_t cap;               // node slots per head at this level
     int top;                   // 1 at the first routed level
     int64_t n_top;             // candidates at the first routed level (all its nodes)
-    const int32_t* cand_node;  // [H_kv][cap] (unused when top)
-    const uint32_t* cand_mask; // [H_kv][cap]
-    int32_t* ncand;            // [H_kv] (written when top, read otherwise)
+    // the level above (unused when top): its kept nodes are this level's parents
+    const int32_t* pklist;     // [H_kv][pcap]
+    const uint32_t* pkmask;    // [H_kv][pcap]
+    const int32_t* pnkept;     // [H_kv]
+    int64_t pcap;
+    int64_t orph_lo, orph_hi;  // this level's orphans
+    ZhaDiv dc;                 // division by the chunk size
+    int32_t* ncand;            // out [H_kv]: candidates at this level
     float* sig;                // [H_kv][G][cap]
     uint64_t* kbm;             // per-head kept bitmaps [H_kv][G][wcap]
     int64_t wcap;              // bitmap words per head
@@ -39,12 +69,6 @@ struct ZhaLevelArgs {
     int32_t* klist;            // out: kept nodes [H_kv][cap], ascending
     uint32_t* kmask;           // out: their head masks
     int32_t* nkept;            // out [H_kv]
-    // candidates of the level below (not written at level 1)
-    int32_t* next_node;        // [H_kv][next_cap]
-    uint32_t* next_mask;
-    int32_t* next_ncand;       // [H_kv]
-    int64_t next_cap;
-    int64_t orph_lo, orph_hi;  // orphan nodes of the level below
 };
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream);

@@ -14,18 +14,22 @@
 // 16x16x4 fp32 tile holds 16 heads (G real) against 16 planes, and the planes
 // stream from HBM once per group whatever the number of heads that see them.
 //
-// Selection runs one 1024-thread workgroup per query head.  Probabilities are
-// handled as 2^40-scaled integers e_i = exp(sigma_i - max) so that every sum
-// is exact and order-free (bitwise-reproducible).  Candidates are ranked by
-// delta_i = max - sigma_i quantised to 2^-27 (monotone in sigma), located by a
-// three-pass mass-weighted radix select (11 + 11 + 10 bits); candidates whose
-// quantised delta equals the cut's are taken in ascending position (= node)
-// order until the cumulative mass reaches ceil(p * sum e).  Each head writes
-// its kept flags as a bitmap (one wave ballot per 64 positions, no atomics);
-// the last head of the group to finish ORs the group's bitmaps into the kept
-// list and writes the next level's candidates (children of kept nodes, then
-// that level's orphans), so the next score kernel reaches its planes in one
-// dependent load.
+// Selection keeps, per query head, the shortest prefix of candidates in
+// descending-probability order whose mass reaches p.  Probabilities are handled
+// as 2^40-scaled integers e_i = exp(sigma_i - max) so that every sum is exact and
+// order-free (bitwise-reproducible).  Candidates are ranked by delta_i = max -
+// sigma_i quantised to 2^-27 (monotone in sigma) and the cut is found by a
+// mass-weighted radix select; candidates whose quantised delta equals the cut's
+// are taken in ascending position (= node) order until the cumulative mass
+// reaches ceil(p * sum e).  Small frontiers (<= 1024 candidates per group) are
+// selected by one workgroup, one wave per head, with 8-bit digits; larger ones
+// by one 1024-thread workgroup per head with 11/11/10-bit digits, whose kept
+// flags go to a bitmap that the last head of the group to finish merges.
+//
+// The candidates of a level are never written out: they are the children of the
+// level above's kept nodes (kept list and head masks, ascending) followed by the
+// level's orphans, so a candidate's node id and head mask come from one read of
+// its parent's kept-list entry.
 #include "zha_common.h"
 #include "zha_internal.h"
 
@@ -42,6 +46,7 @@ __device__ __forceinline__ uint32_t all_heads(int G) { return G >= 32 ? 0xFFFFFF
 
 // grid (blocks, H_kv), 256 threads.  Each wave scores items of U = 16/R
 // candidates (R <= 16) or one candidate over R/16 column blocks (R > 16).
+// Candidate positions and node ids fit in 32 bits (capacity < 2^31).
 template <bool BF16>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const void* __restrict__ q,
                                                                         ZhaLevelArgs a, int G, int c, int R,
@@ -55,21 +60,26 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     const int cl = R <= 16 ? j / R : 0;
     const uint32_t allg = all_heads(G);
     const size_t lrow = (size_t)g * a.cap;
+    const size_t prow = (size_t)g * a.pcap;
+    const int stride = gridDim.x * 4;
+    const int pcap = (int)a.pcap;
 
-    // first item's candidate fetched together with the candidate count
-    int64_t it = (int64_t)blockIdx.x * 4 + wave;
-    int32_t node0 = 0;
-    uint32_t mask0 = allg;
+    // The first item's parent entry is read together with the parent count: its
+    // index is bounded by the parent level's capacity, not by the count.
+    int it = blockIdx.x * 4 + wave;
+    int32_t pk = 0;
+    uint32_t pm = allg;
     if (!a.top) {
-        const int64_t p0 = it * U + cl;
-        if (p0 < a.cap) {
-            node0 = a.cand_node[lrow + p0];
-            mask0 = a.cand_mask[lrow + p0];
+        const int pi = (int)zha_div((uint32_t)(it * U + cl), a.dc);
+        if (pi < pcap) {
+            pk = a.pklist[prow + pi];
+            pm = a.pkmask[prow + pi];
         }
     }
-    const int64_t n_cand = a.top ? a.n_top : (int64_t)a.ncand[g];
+    const int pn = a.top ? 0 : a.pnkept[g];
+    const int n_cand = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (a.top) a.ncand[g] = (int32_t)n_cand;
+        a.ncand[g] = n_cand;
         a.done[g] = 0;
     }
     // A operand: row = query head j of the group, contraction index d = 16m + 4kq + e.
@@ -98,40 +108,47 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
         for (int k = 0; k < 32; ++k) qa[k] = 0.f;
     }
 
-    const int64_t items = (n_cand + U - 1) / U;
-    bool first = true;
-    for (; it < items; it += (int64_t)gridDim.x * 4) {
-        const int64_t pos = it * U + cl;
+    const int items = (n_cand + U - 1) / U;
+    for (; it < items; it += stride) {
+        const int pos = it * U + cl;
         const bool valid = pos < n_cand;
-        int64_t node = 0;
+        int32_t node = 0;
         uint32_t cm = 0;
         if (valid) {
             if (a.top) {
                 node = pos;
                 cm = allg;
-            } else if (first) {
-                node = node0;
-                cm = mask0;
+            } else if (pos < pn * c) {
+                // child pos % c of the kept parent at index pos / c
+                node = pk * c + (pos - (int)zha_div((uint32_t)pos, a.dc) * c);
+                cm = pm;
             } else {
-                node = a.cand_node[lrow + pos];
-                cm = a.cand_mask[lrow + pos];
+                node = (int32_t)a.orph_lo + (pos - pn * c);
+                cm = allg;
             }
         }
-        first = false;
+        if (!a.top) {
+            // parent entry of this wave's next item, in flight with this item's planes
+            const int npi = (int)zha_div((uint32_t)((it + stride) * U + cl), a.dc);
+            if (it + stride < items && npi < pn) {
+                pk = a.pklist[prow + npi];
+                pm = a.pkmask[prow + npi];
+            }
+        }
         float best[4] = {zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf()};
         for (int cb = 0; cb < CB; ++cb) {
             const int r = R <= 16 ? (j % R) : (cb * 16 + j);
-            const size_t prow = (lrow + (size_t)node) * R + r;
+            const size_t prw = (lrow + (size_t)node) * R + r;
             float4 sv[8];
             if (valid) {
-                const float4* plane = reinterpret_cast<const float4*>(a.S + prow * ZHA_D);
+                const float4* plane = reinterpret_cast<const float4*>(a.S + prw * ZHA_D);
 #pragma unroll
                 for (int m = 0; m < 8; ++m) sv[m] = plane[4 * m + kq];
             } else {
 #pragma unroll
                 for (int m = 0; m < 8; ++m) sv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            const float bv = valid ? a.B[prow] : zha_neg_inf();
+            const float bv = valid ? a.B[prw] : zha_neg_inf();
             zha_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -163,7 +180,7 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     }
 }
 
-// ---- selection helpers (kSelThreads threads, one wave does the scans)
+// ---- selection helpers
 
 // Exclusive prefix sum across one wave (all lanes active); *total gets the wave sum.
 __device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v, uint64_t* total) {
@@ -172,82 +189,109 @@ __device__ __forceinline__ uint64_t wave_excl_scan_u64(uint64_t v, uint64_t* tot
     return x - v;
 }
 
+// Selection keys: the quantised delta of a candidate that carries mass, or one
+// of two sentinels.  A candidate's fixed-point mass is a function of its key
+// alone, so every pass sees exactly the same masses.
+constexpr uint32_t kNotCand = 0xFFFFFFFFu;    // not this head's candidate
+constexpr uint32_t kNoMass = 0xFFFFFFFEu;     // candidate with delta >= kDeltaMax (mass 0)
+constexpr float kDeltaBelowMax = 31.999998092651367f;   // largest float below kDeltaMax
+
+__device__ __forceinline__ uint32_t key_of(float s, float m) {
+    const float dl = m - s;                   // NaN or +inf only for s = -inf
+    const uint32_t k = (uint32_t)(fminf(dl, kDeltaBelowMax) * kKeyScale);
+    return s == zha_neg_inf() ? kNotCand : (dl < kDeltaMax ? k : kNoMass);
+}
+
+__device__ __forceinline__ uint64_t mass_of(uint32_t key) {
+    // e^{-delta} with delta = key * 2^-27, as 2^40-scaled fixed point truncated to
+    // an integer.  x <= 2^40 has 24 significant bits, so x = hi * 2^32 + lo with
+    // both parts exact.
+    const float x = exp2f(-(float)key * (1.4426950408889634f / kKeyScale)) * kFix;
+    const float hi = floorf(x * 0x1p-32f);
+    const float lo = fmaf(hi, -0x1p32f, x);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Large frontiers: 2048-bin histograms of key digits 31..21, 20..10 and 9..0.
+// Bin b sits at b + b / 32 so that one lane's 32 consecutive bins are read
+// without LDS bank conflicts.
+constexpr int kHistBins = 2048;
+constexpr int kHistPadded = kHistBins + kHistBins / 32;
+__device__ __forceinline__ int hpad(uint32_t b) { return (int)(b + (b >> 5)); }
+
 // Run by one whole wave: the bin b with before(b) < need <= before(b) + hist[b]
-// (before(b) = sum of bins < b) goes to *out_bin / *out_before.  When `need`
-// is 0 it is first set to ceil(p * total) (clamped to [1, total]).
-template <int NBINS>
+// (before(b) = mass of the bins below b) goes to *out_bin / *out_before.  When
+// `need` is 0 it is first set to ceil(p * total) (clamped to [1, total]).  Two
+// scans: over the 64 lanes' 32-bin sums, then over the 32 bins of the lane
+// whose range holds the crossing.
 __device__ void wave_find_cross(const uint64_t* hist, uint64_t need, float top_p, int* out_bin,
                                 uint64_t* out_before, uint64_t* out_need) {
-    constexpr int per = NBINS / 64;
     const int lane = threadIdx.x & 63;
-    const int b0 = lane * per;
+    const uint64_t* row = hist + lane * 33;
     uint64_t mine = 0;
 #pragma unroll 8
-    for (int i = 0; i < per; ++i) mine += hist[b0 + i];
+    for (int i = 0; i < 32; ++i) mine += row[i];
     uint64_t total;
-    uint64_t before = wave_excl_scan_u64(mine, &total);
+    const uint64_t before = wave_excl_scan_u64(mine, &total);
     if (need == 0) {
         uint64_t T = (uint64_t)ceil((double)top_p * (double)total);
         if (T < 1) T = 1;
         if (T > total) T = total;
         need = T;
     }
-    if (before < need && before + mine >= need) {          // the crossing bin is one of this lane's
-#pragma unroll 1
-        for (int i = 0; i < per; ++i) {
-            const uint64_t hb = hist[b0 + i];
-            if (before + hb >= need) {
-                *out_bin = b0 + i;
-                *out_before = before;
-                *out_need = need;
-                break;
-            }
-            before += hb;
-        }
+    const uint64_t hit = __ballot(before < need && before + mine >= need);
+    const int L = hit ? __ffsll((long long)hit) - 1 : 63;
+    const uint64_t base = zha_readlane_u64(before, L);
+    const uint64_t x = lane < 32 ? hist[L * 33 + lane] : 0ull;
+    uint64_t t2;
+    const uint64_t ex = wave_excl_scan_u64(x, &t2);
+    const uint64_t hit2 = __ballot(lane < 32 && base + ex < need && base + ex + x >= need);
+    const int jb = hit2 ? __ffsll((long long)hit2) - 1 : 31;
+    const uint64_t ex_j = zha_readlane_u64(ex, jb);
+    if (lane == 0) {
+        *out_bin = L * 32 + jb;
+        *out_before = base + ex_j;
+        *out_need = need;
     }
 }
 
-__device__ __forceinline__ uint64_t fixed_mass(float delta) { return (uint64_t)(__expf(-delta) * kFix); }
-__device__ __forceinline__ uint32_t delta_key(float delta) { return (uint32_t)(delta * kKeyScale); }
-
-// Selection keys: the quantised delta of a candidate that carries mass, or one
-// of two sentinels.  A candidate's fixed-point mass is a function of its key
-// alone, so every pass sees exactly the same masses.
-constexpr uint32_t kNotCand = 0xFFFFFFFFu;    // not this head's candidate
-constexpr uint32_t kNoMass = 0xFFFFFFFEu;     // candidate with delta >= kDeltaMax (mass 0)
-constexpr int kLdsKeys = 16384;               // heads with at most this many candidates stage keys in LDS
-
-__device__ __forceinline__ uint32_t key_of(float s, float m) {
-    if (s == zha_neg_inf()) return kNotCand;
-    const float dl = m - s;
-    return dl < kDeltaMax ? delta_key(dl) : kNoMass;
-}
-
-__device__ __forceinline__ uint64_t mass_of(uint32_t key) {
-    // e^{-delta} with delta = key * 2^-27, as 2^40-scaled fixed point
-    return (uint64_t)(exp2f(-(float)key * (1.4426950408889634f / kKeyScale)) * kFix);
-}
-
-constexpr int kSmallN = 1024;   // groups with at most this many candidates select in one workgroup
+constexpr int kLdsKeys = 32768;               // heads with at most this many candidates keep their keys in LDS
+constexpr int kSlots = kLdsKeys / kSelThreads;   // positions tid + 1024 k held in registers while staging
+constexpr int kMergeW = kLdsKeys / 64;        // bitmap words merged per step
+constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup
 constexpr int kSmallK = kSmallN / 64;
-static_assert(ZHA_MAX_GROUP * kSmallN <= 16384, "small-path scores must fit the key buffer");
-static_assert(ZHA_MAX_GROUP * 256 <= 2 * 2048, "small-path histograms must fit the histogram buffers");
+static_assert(kSelThreads == kSmallN, "small path: one position per thread");
+static_assert(ZHA_MAX_GROUP * kSmallN + ZHA_MAX_GROUP * 256 * 3 <= kLdsKeys,
+              "small-path scores, histograms and counts must fit the key buffer");
+static_assert(2 * ZHA_MAX_GROUP * kMergeW + kMergeW * 32 <= kLdsKeys,
+              "merge: head words and parent ids must fit the key buffer");
+static_assert(kMergeW + kMergeW / 2 <= kHistPadded, "merge: union words and prefixes must fit the histogram");
+static_assert(kMergeW <= kSelThreads, "merge: one thread per word of a step");
 
-// One wave selects for query head (g, hl) among n <= kSmallN candidates whose
-// scores are in LDS (sg); position lane + 64k sits in register slot k.  8-bit
-// digits, wave-local histograms (hist: 256 u64, cntb: 256 u32), no workgroup
-// barrier.  The kept bitmap words go to kw[0 .. nk).
-__device__ void select_head_wave(const float* sg, int64_t n, float top_p, uint64_t* hist, uint32_t* cntb,
+// Bit `lane` of a 64-bit word, and the number of set bits below it.
+__device__ __forceinline__ uint32_t lane_bit(uint64_t w, int lane) {
+    const uint32_t h = lane < 32 ? (uint32_t)w : (uint32_t)(w >> 32);
+    return (h >> (lane & 31)) & 1u;
+}
+__device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
+}
+
+// One wave selects for one query head among n <= 64 K candidates whose scores
+// are in LDS (sg); position lane + 64k sits in register slot k.  8-bit digits,
+// wave-local histograms (hist: 256 u64, cntb: 256 u32), no workgroup barrier.
+// The kept bitmap words go to kw[0 .. nk).
+template <int K>
+__device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* hist, uint32_t* cntb,
                                  uint64_t* kw, uint32_t* n_cand_out, uint32_t* n_kept_out) {
-    constexpr int K = kSmallK;
     const int lane = threadIdx.x & 63;
-    const int nk = (int)((n + 63) / 64);
+    const int nk = (n + 63) >> 6;
     float sv[K];
     float m = zha_neg_inf();
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int64_t pos = lane + 64 * k;
-        sv[k] = (pos < n) ? sg[pos] : zha_neg_inf();
+        const int pos = lane + 64 * k;
+        sv[k] = pos < n ? sg[pos] : zha_neg_inf();
         m = fmaxf(m, sv[k]);
     }
     m = zha_wave_max(m);
@@ -263,50 +307,61 @@ __device__ void select_head_wave(const float* sg, int64_t n, float top_p, uint64
 #pragma unroll 1
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { hist[lane * 4 + i] = 0; cntb[lane * 4 + i] = 0; }
+            reinterpret_cast<uint4*>(hist)[2 * lane] = make_uint4(0u, 0u, 0u, 0u);
+            reinterpret_cast<uint4*>(hist)[2 * lane + 1] = make_uint4(0u, 0u, 0u, 0u);
+            reinterpret_cast<uint4*>(cntb)[lane] = make_uint4(0u, 0u, 0u, 0u);
             zha_wave_lds_sync();
+            // keys whose digits above this pass's match the prefix found so far
+            const uint32_t hs = pass == 0 ? 31u : (uint32_t)(shift + 8);
+            const uint32_t want = pass == 0 ? 0u : prefix;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                if (k < nk && key[k] < kNoMass && (pass == 0 || (key[k] >> (shift + 8)) == prefix)) {
-                    const uint32_t b = (key[k] >> shift) & 255u;
-                    atomicAdd((unsigned long long*)&hist[b], (unsigned long long)mass_of(key[k]));
+                const uint32_t kk = key[k];
+                const uint32_t top = pass == 0 ? 0u : (kk >> hs);
+                if (kk < kNoMass && top == want) {
+                    const uint32_t b = (kk >> shift) & 255u;
+                    atomicAdd((unsigned long long*)&hist[b], (unsigned long long)mass_of(kk));
                     atomicAdd(&cntb[b], 1u);
                 }
             }
             zha_wave_lds_sync();
-            uint64_t hb[4], mine = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { hb[i] = hist[lane * 4 + i]; mine += hb[i]; }
+            const uint4 h01 = reinterpret_cast<const uint4*>(hist)[2 * lane];
+            const uint4 h23 = reinterpret_cast<const uint4*>(hist)[2 * lane + 1];
+            const uint64_t hb[4] = {((uint64_t)h01.y << 32) | h01.x, ((uint64_t)h01.w << 32) | h01.z,
+                                    ((uint64_t)h23.y << 32) | h23.x, ((uint64_t)h23.w << 32) | h23.z};
+            const uint64_t mine = hb[0] + hb[1] + hb[2] + hb[3];
             uint64_t total;
             uint64_t before = wave_excl_scan_u64(mine, &total);
             if (pass == 0) {
-                uint64_t T = (uint64_t)ceil((double)top_p * (double)total);
+                const uint64_t T = (uint64_t)ceil((double)top_p * (double)total);
                 need = T < 1 ? 1 : (T > total ? total : T);
             }
             int my_bin = -1;
             uint64_t my_before = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (before < need && before + hb[i] >= need && my_bin < 0) { my_bin = lane * 4 + i; my_before = before; }
+                const bool cross = before < need && before + hb[i] >= need && my_bin < 0;
+                my_bin = cross ? lane * 4 + i : my_bin;
+                my_before = cross ? before : my_before;
                 before += hb[i];
             }
             const uint64_t found = __ballot(my_bin >= 0);
-            const int src = __ffsll((long long)found) - 1;
-            const uint32_t bin = (uint32_t)__shfl(my_bin, src, 64);
+            const int src = found ? __ffsll((long long)found) - 1 : 0;
+            const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(my_bin, src);
             need -= zha_readlane_u64(my_before, src);
             prefix = (prefix << 8) | bin;
             if (pass == 3) { ustar = prefix; ties = cntb[bin]; }
             zha_wave_lds_sync();
         }
     }
-    uint32_t n_cand = 0;
+    uint32_t n_cand = 0, n_kept = 0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const bool cand = k < nk && key[k] != kNotCand;
         const bool kept = !none && (keep_all ? cand : (cand && key[k] < kNoMass && (key[k] < ustar || (key[k] == ustar && ties == 1))));
         const uint64_t wk = __ballot(kept);
         n_cand += __popcll(__ballot(cand));
+        n_kept += __popcll(wk);
         if (lane == 0 && k < nk) kw[k] = wk;
     }
     zha_wave_lds_sync();
@@ -319,134 +374,180 @@ __device__ void select_head_wave(const float* sg, int64_t n, float top_p, uint64
             uint64_t tot;
             const uint64_t ex = wave_excl_scan_u64(w, &tot);
             const uint64_t extra = __ballot(w > 0 && run + ex < need);
+            n_kept += __popcll(extra);
             if (lane == 0 && k < nk) kw[k] |= extra;
             run += tot;
         }
         zha_wave_lds_sync();
     }
-    uint32_t n_kept = 0;
-#pragma unroll 1
-    for (int k = 0; k < nk; ++k) n_kept += __popcll(kw[k]);
     *n_cand_out = n_cand;
     *n_kept_out = n_kept;
 }
 
+// Scores of all G heads at position tid (< cap) into LDS, and the node id of
+// that position; every global read is issued before any result is used.  `pn`
+// (kept parents) is only needed for the node id.
+__device__ __forceinline__ void stage_small(const ZhaLevelArgs& a, int g, int G, int c, int tid, int pn,
+                                            float* s_sig, int32_t* s_nid) {
+    const bool in = tid < a.cap;
+    float v[ZHA_MAX_GROUP];
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        v[hh] = (hh < G && in) ? a.sig[((size_t)g * G + hh) * a.cap + tid] : zha_neg_inf();
+    const int pi = (int)zha_div((uint32_t)tid, a.dc);
+    int32_t pk = 0;
+    if (!a.top && pi < a.pcap) pk = a.pklist[(size_t)g * a.pcap + pi];
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        if (hh < G) s_sig[hh * kSmallN + tid] = v[hh];
+    int32_t node = tid;
+    if (!a.top) node = tid < pn * c ? pk * c + (tid - pi * c) : (int32_t)a.orph_lo + (tid - pn * c);
+    s_nid[tid] = node;
+}
+
 // grid (H_q), 1024 threads: one query head per workgroup; the last head of a
-// group to finish writes the group's kept list and the next level's candidates.
-// Keys sit in LDS (kLdsKeys candidates) or are recomputed from the scores on
-// every pass for larger frontiers; all passes are rolled loops.
+// group to finish writes the group's kept list.  Keys sit in LDS (up to
+// kLdsKeys candidates) or are recomputed from the scores on every pass for
+// larger frontiers.
 __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelArgs a, int G, int c,
                                                                        float top_p) {
-    __shared__ uint32_t keys[kLdsKeys];                 // also: small-path scores [G][kSmallN]
-    __shared__ uint64_t histbuf[2][2048];               // also: small-path histograms [G][256]
-    __shared__ uint32_t cntbuf[2][2048];                // also: small-path counts [G][256]
+    // keys: per-candidate keys; small path: scores [G][kSmallN], then histograms
+    // [G][256] (u64) and counts [G][256]; merge: head words [kMergeW][G] (u64),
+    // then the step's parent node ids.
+    __shared__ __align__(16) uint32_t keys[kLdsKeys];
+    __shared__ __align__(16) uint64_t hist[kHistPadded];   // merge: union words, then popcount prefixes
+    __shared__ uint32_t cntb[kHistBins];
     __shared__ int32_t s_nid[kSmallN];
     __shared__ uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
+    __shared__ uint64_t s_wt[kSelWaves];
     __shared__ float swf[kSelWaves];
-    __shared__ int s_bin;
+    __shared__ int s_bin, s_last;
     __shared__ uint64_t s_before, s_need, s_run;
     __shared__ uint32_t s_cnt[2];
-    __shared__ int s_last;
 
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t lrow = (size_t)g * a.cap;
-    // Small frontiers: the group's first workgroup selects for all G heads (one wave
-    // each) and merges from LDS.  Scores and node ids of the first kSmallN positions
-    // are fetched together with the candidate count.
-    float* s_sig = reinterpret_cast<float*>(keys);                        // [G][kSmallN]
-    int64_t n;
-    if (a.top) {
-        n = a.n_top;
+    const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
+    float* s_sig = reinterpret_cast<float*>(keys);
+
+    // Every global read below is issued before the candidate count is known:
+    // reads stay inside the level's arrays (positions < cap) and positions >= n
+    // are ignored afterwards, so the count, the scores and the node ids cost one
+    // memory round trip together.
+    float sv[kSlots];                          // own head's scores, positions tid + 1024 k
+    int pn, n;
+    if (a.cap <= kSmallN) {
+        if (hl != 0) return;                   // n <= cap: the small path for sure
+        pn = a.top ? 0 : a.pnkept[g];
+        stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
+        n = a.top ? (int)a.n_top : pn * c + n_orph;
     } else {
-        const int32_t nc = a.ncand[g];
-        const int32_t nd = tid < a.cap ? a.cand_node[lrow + tid] : 0;
-        n = nc;
-        if (n <= kSmallN && hl == 0) s_nid[tid] = nd;
-    }
-    if (n <= kSmallN) {
-        if (hl != 0) return;                       // the same decision for every head of the group
-        for (int i = tid; i < G * kSmallN; i += kSelThreads) {
-            const int hh = i / kSmallN, pos = i - hh * kSmallN;
-            s_sig[i] = pos < n ? a.sig[((size_t)g * G + hh) * a.cap + pos] : zha_neg_inf();
+        const int pnk = a.top ? 0 : a.pnkept[g];
+        const float* sg0 = a.sig + ((size_t)g * G + hl) * a.cap;
+        const int lim = (int)min(a.cap, (int64_t)kLdsKeys);
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            const int pos = tid + k * kSelThreads;
+            sv[k] = pos < lim ? sg0[pos] : zha_neg_inf();
         }
+        pn = pnk;
+        n = a.top ? (int)a.n_top : pn * c + n_orph;
+        if (n <= kSmallN) {
+            if (hl != 0) return;               // the same decision for every head of the group
+            stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
+        }
+    }
+
+    if (n <= kSmallN) {
+        // ---- small frontier: the group's first workgroup selects for all G heads
+        // (one wave each) and merges from LDS
         __syncthreads();
-        uint64_t* kw = s_kw;                                              // [G][kSmallK]
+        uint64_t* shist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);      // [G][256]
+        uint32_t* scnt = keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256;           // [G][256]
+        uint64_t* kw = s_kw;                                                               // [G][kSmallK]
+        const int nk = (n + 63) >> 6;
         if (wave < G) {
             uint32_t nc_h, nk_h;
-            select_head_wave(s_sig + wave * kSmallN, n, top_p, &histbuf[0][0] + wave * 256,
-                             &cntbuf[0][0] + wave * 256, kw + wave * kSmallK, &nc_h, &nk_h);
+            const float* sg = s_sig + wave * kSmallN;
+            uint64_t* hh_ = shist + wave * 256;
+            uint32_t* cc_ = scnt + wave * 256;
+            uint64_t* kk_ = kw + wave * kSmallK;
+            if (nk <= 1) select_head_wave<1>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+            else if (nk <= 2) select_head_wave<2>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+            else if (nk <= 4) select_head_wave<4>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+            else if (nk <= 8) select_head_wave<8>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+            else select_head_wave<16>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
             if (lane == 0) {
                 a.stats[2 * (g * G + wave) + 0] = (int32_t)nc_h;
                 a.stats[2 * (g * G + wave) + 1] = (int32_t)nk_h;
             }
-            for (int k = lane; k < (int)((n + 63) / 64); k += 64)
-                a.kbm[((size_t)g * G + wave) * a.wcap + k] = kw[wave * kSmallK + k];
+            if (lane < nk) a.kbm[((size_t)g * G + wave) * a.wcap + lane] = kk_[lane];
         }
         __syncthreads();
-        if (wave != 0) return;
-        // merge the heads' kept words: kept list and the next level's candidates
-        const int nk = (int)((n + 63) / 64);
-        const size_t nrow = (size_t)g * a.next_cap;
-        const uint64_t lt = (1ull << lane) - 1ull;
-        uint64_t run = 0;
-#pragma unroll 1
-        for (int k = 0; k < nk; ++k) {
-            uint64_t u = 0;
-#pragma unroll 1
-            for (int hh = 0; hh < G; ++hh) u |= kw[hh * kSmallK + k];
-            if ((u >> lane) & 1ull) {
-                const uint64_t rank = run + __popcll(u & lt);
-                uint32_t msk = 0;
-#pragma unroll 1
-                for (int hh = 0; hh < G; ++hh) msk |= (uint32_t)((kw[hh * kSmallK + k] >> lane) & 1ull) << hh;
-                const int64_t pos = lane + 64 * k;
-                const int32_t node = a.top ? (int32_t)pos : s_nid[pos];
-                a.klist[lrow + rank] = node;
-                a.kmask[lrow + rank] = msk;
-                if (a.next_node) {
-#pragma unroll 1
-                    for (int i = 0; i < c; ++i) {
-                        a.next_node[nrow + rank * c + i] = node * c + i;
-                        a.next_mask[nrow + rank * c + i] = msk;
-                    }
-                }
-            }
-            run += __popcll(u);
+        // union of the heads' kept words -> kept list (ascending node) and head masks:
+        // wave w < nk handles word w; its rank offset is the popcount of the words below
+        if (nk == 0) {
+            if (tid == 0) a.nkept[g] = 0;
+            return;
         }
-        if (a.next_node) {
-            const uint32_t allg = all_heads(G);
-            const int64_t n_orph = a.orph_hi - a.orph_lo;
-            for (int64_t o = lane; o < n_orph; o += 64) {
-                a.next_node[nrow + run * c + o] = (int32_t)(a.orph_lo + o);
-                a.next_mask[nrow + run * c + o] = allg;
-            }
-            if (lane == 0) a.next_ncand[g] = (int32_t)(run * c + n_orph);
+        if (wave >= nk) return;
+        uint64_t u = 0;
+        uint32_t below = 0;
+#pragma unroll 1
+        for (int hh = 0; hh < G; ++hh) u |= kw[hh * kSmallK + wave];
+        // words below this one: lane k < wave contributes the union of word k
+        uint64_t uk = 0;
+        if (lane < wave) {
+#pragma unroll 1
+            for (int hh = 0; hh < G; ++hh) uk |= kw[hh * kSmallK + lane];
         }
-        if (lane == 0) a.nkept[g] = (int32_t)run;
+        below = (uint32_t)__popcll(uk);
+        for (int o = 32; o > 0; o >>= 1) below += __shfl_xor(below, o, 64);
+        if (lane_bit(u, lane)) {
+            const uint32_t rank = below + bits_below_lane(u);
+            uint32_t msk = 0;
+#pragma unroll 1
+            for (int hh = 0; hh < G; ++hh) msk |= lane_bit(kw[hh * kSmallK + wave], lane) << hh;
+            a.klist[lrow + rank] = s_nid[lane + 64 * wave];
+            a.kmask[lrow + rank] = msk;
+        }
+        if (wave == nk - 1 && lane == 0) a.nkept[g] = (int32_t)(below + (uint32_t)__popcll(u));
         return;
     }
+
+    // ---- large frontier: one workgroup per head
     const float* sg = a.sig + ((size_t)g * G + hl) * a.cap;
     uint64_t* bm = a.kbm + ((size_t)g * G + hl) * a.wcap;
-    const int64_t nwords = (n + 63) / 64;
+    const int nwords = (n + 63) >> 6;
+    const int nslot = (n + kSelThreads - 1) / kSelThreads;   // positions per thread
     const bool staged = n <= kLdsKeys;
 
     if (tid < 2) s_cnt[tid] = 0;
     float m = zha_neg_inf();
-#pragma unroll 4
-    for (int64_t pos = tid; pos < n; pos += kSelThreads) {
-        const float s = sg[pos];
-        m = fmaxf(m, s);
-        if (staged) keys[pos] = __float_as_uint(s);        // raw score until the max is known
+    if (staged) {
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            if (k < nslot) {
+                if (tid + k * kSelThreads >= n) sv[k] = zha_neg_inf();
+                m = fmaxf(m, sv[k]);
+            }
+        }
+    } else {
+        for (int pos = tid; pos < n; pos += kSelThreads) m = fmaxf(m, sg[pos]);
     }
     m = zha_wave_max(m);
     if (lane == 0) swf[wave] = m;
     __syncthreads();
     m = swf[0];
+#pragma unroll
     for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, swf[w]);
     if (staged) {
-#pragma unroll 2
-        for (int64_t pos = tid; pos < n; pos += kSelThreads) keys[pos] = key_of(__uint_as_float(keys[pos]), m);
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            const int pos = tid + k * kSelThreads;
+            if (k < nslot && pos < n) keys[pos] = key_of(sv[k], m);
+        }
     }
 
     // Kept rule: keep_all, or key < ustar, or key == ustar when that key is unique.
@@ -455,47 +556,55 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
     uint32_t ustar = 0, ties = 0;
     uint64_t need = 0;
     if (!none && !keep_all) {
-        // digits of the key: bits 31..21, 20..10, 9..0; pass p counts into buffer p & 1
-        // while the other buffer is cleared for pass p + 1
-        uint32_t mshift = 32, mval = 0, bshift = 21, bmask = 2047;
-        for (int i = tid; i < 2048; i += kSelThreads) { histbuf[0][i] = 0; cntbuf[0][i] = 0; }
+        uint32_t mshift = 31, mval = 0, bshift = 21, bmask = 2047;
+        for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
+        for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
         __syncthreads();
 #pragma unroll 1
         for (int pass = 0; pass < 3; ++pass) {
-            uint64_t* hist = histbuf[pass & 1];
-            uint32_t* cntb = cntbuf[pass & 1];
-            for (int i = tid; i < 2048; i += kSelThreads) { histbuf[(pass + 1) & 1][i] = 0; cntbuf[(pass + 1) & 1][i] = 0; }
-#pragma unroll 2
-            for (int64_t pos = tid; pos < n; pos += kSelThreads) {
-                const uint32_t key = staged ? keys[pos] : key_of(sg[pos], m);
-                if (key < kNoMass && (uint32_t)((uint64_t)key >> mshift) == mval) {
-                    const uint32_t b = (key >> bshift) & bmask;
-                    atomicAdd((unsigned long long*)&hist[b], (unsigned long long)mass_of(key));
-                    atomicAdd(&cntb[b], 1u);
+            // pass 0 counts every key that carries mass; later passes only the keys
+            // whose higher digits equal the bins found so far
+#pragma unroll 1
+            for (int k = 0; k < nslot; ++k) {
+                const int pos = tid + k * kSelThreads;
+                if (pos < n) {
+                    const uint32_t key = staged ? keys[pos] : key_of(sg[pos], m);
+                    const bool match = pass == 0 ? true : (key >> mshift) == mval;
+                    if (key < kNoMass && match) {
+                        const uint32_t b = (key >> bshift) & bmask;
+                        atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
+                        atomicAdd(&cntb[b], 1u);
+                    }
                 }
             }
             __syncthreads();
-            if (wave == 0) wave_find_cross<2048>(hist, need, top_p, &s_bin, &s_before, &s_need);
+            if (wave == 0) wave_find_cross(hist, need, top_p, &s_bin, &s_before, &s_need);
             __syncthreads();
             const uint32_t bin = (uint32_t)s_bin;
             need = s_need - s_before;            // mass still needed inside this bin
             if (pass == 0) { mshift = 21; mval = bin; bshift = 10; bmask = 2047; }
             else if (pass == 1) { mshift = 10; mval = (mval << 11) | bin; bshift = 0; bmask = 1023; }
             else { ustar = (mval << 10) | bin; ties = cntb[bin]; }
+            if (pass < 2) {
+                __syncthreads();                 // every thread has read this pass's result
+                for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
+                for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
+                __syncthreads();
+            }
         }
     }
     const uint64_t need_tie = need;
 
-    // kept flags -> this head's bitmap, one ballot per 64 positions
+    // kept flags -> this head's bitmap: slot k of wave w is word 16 k + w
     uint32_t my_cand = 0, my_kept = 0;
-#pragma unroll 2
-    for (int64_t base = 0; base < n; base += kSelThreads) {
-        const int64_t pos = base + tid;
+#pragma unroll 1
+    for (int k = 0; k < nslot; ++k) {
+        const int pos = tid + k * kSelThreads;
         const uint32_t key = pos < n ? (staged ? keys[pos] : key_of(sg[pos], m)) : kNotCand;
         const bool cand = key != kNotCand;
         const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
         const uint64_t word = __ballot(kept);
-        const int64_t wi = base / 64 + wave;
+        const int wi = k * kSelWaves + wave;
         if (lane == 0 && wi < nwords) bm[wi] = word;
         my_cand += cand;
         my_kept += kept;
@@ -506,19 +615,19 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
         __threadfence();
         if (tid == 0) s_run = 0;
 #pragma unroll 1
-        for (int64_t base = 0; base < n; base += kSelThreads) {
-            const int64_t pos = base + tid;
+        for (int base = 0; base < n; base += kSelThreads) {
+            const int pos = base + tid;
             const uint32_t key = pos < n ? (staged ? keys[pos] : key_of(sg[pos], m)) : kNotCand;
             const uint64_t w = key == ustar ? mass_of(key) : 0ull;
             uint64_t wt;
             const uint64_t ex = wave_excl_scan_u64(w, &wt);
             __syncthreads();
-            if (lane == 0) histbuf[1][wave] = wt;
+            if (lane == 0) s_wt[wave] = wt;
             __syncthreads();
             uint64_t before = s_run;
-            for (int ww = 0; ww < wave; ++ww) before += histbuf[1][ww];
+            for (int ww = 0; ww < wave; ++ww) before += s_wt[ww];
             uint64_t tot = 0;
-            for (int ww = 0; ww < kSelWaves; ++ww) tot += histbuf[1][ww];
+            for (int ww = 0; ww < kSelWaves; ++ww) tot += s_wt[ww];
             if (w > 0 && before + ex < need_tie) {
                 atomicOr((unsigned long long*)&bm[pos >> 6], 1ull << (pos & 63));
                 ++my_kept;
@@ -550,87 +659,104 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
     if (!s_last) return;
     __threadfence();
     const uint64_t* gbm = a.kbm + (size_t)g * G * a.wcap;
-    const size_t nrow = (size_t)g * a.next_cap;
-    // Merge in steps of mw bitmap words (16384 positions).  LDS is reused: node ids
-    // of the step's positions in `keys`, the G head words in histbuf, the union in
-    // cntbuf[0] (as 64-bit words) and its exclusive popcount prefix in cntbuf[1].
-    constexpr int mw = kLdsKeys / 64;                       // 256 words
-    int32_t* nid = reinterpret_cast<int32_t*>(keys);        // [mw * 64]
-    uint64_t* hw = &histbuf[0][0];                          // [G][mw], G * mw <= 4096
-    uint64_t* s_union = reinterpret_cast<uint64_t*>(cntbuf[0]);
-    uint32_t* s_wpre = cntbuf[1];
+    const size_t prow = (size_t)g * a.pcap;
+    uint64_t* hw = reinterpret_cast<uint64_t*>(keys);                              // [kMergeW][G]
+    int32_t* s_par = reinterpret_cast<int32_t*>(keys) + 2 * ZHA_MAX_GROUP * kMergeW;   // parent node ids
+    uint64_t* s_union = hist;                                                      // [kMergeW]
+    uint32_t* s_wpre = reinterpret_cast<uint32_t*>(hist + kMergeW);                // [kMergeW]
+    const int pnc = pn * c;
     if (tid == 0) s_run = 0;
 #pragma unroll 1
-    for (int64_t wb = 0; wb < nwords; wb += mw) {
-        const int nw = (int)min((int64_t)mw, nwords - wb);
-        const int64_t npos = min((int64_t)nw * 64, n - wb * 64);
-        for (int i = tid; i < G * nw; i += kSelThreads) {
-            const int hh = i / nw, wi = i - hh * nw;
-            hw[hh * mw + wi] = __hip_atomic_load(gbm + (size_t)hh * a.wcap + wb + wi, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (!a.top) {
-#pragma unroll 4
-            for (int64_t p = tid; p < npos; p += kSelThreads) nid[p] = a.cand_node[lrow + wb * 64 + p];
+    for (int wb = 0; wb < nwords; wb += kMergeW) {
+        const int nw = min(kMergeW, nwords - wb);
+        const int p0 = wb * 64;
+        const int npos = min(nw * 64, n - p0);
+        // parents of this step's child positions (at most kMergeW * 32 of them for c >= 2)
+        const int pb0 = (int)zha_div((uint32_t)p0, a.dc);
+        const int pb1 = a.top ? pb0 : min(pn, (int)zha_div((uint32_t)(p0 + npos + c - 1), a.dc));
+        const int npar = max(0, pb1 - pb0);
+        {
+            // the G heads' words (one word per thread) and the parent ids of this
+            // step, all reads in flight together
+            constexpr int kPerP = kMergeW * 32 / kSelThreads;
+            uint64_t hv[ZHA_MAX_GROUP];
+            int32_t pv[kPerP];
+#pragma unroll
+            for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+                hv[hh] = (hh < G && tid < nw) ? __hip_atomic_load(gbm + (size_t)hh * a.wcap + wb + tid,
+                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                              : 0ull;
+#pragma unroll
+            for (int t = 0; t < kPerP; ++t) {
+                const int i = tid + t * kSelThreads;
+                pv[t] = i < npar ? a.pklist[prow + pb0 + i] : 0;
+            }
+            if (tid < nw) {
+                uint64_t u = 0;
+#pragma unroll
+                for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+                    if (hh < G) hw[tid * G + hh] = hv[hh];
+                    u |= hv[hh];
+                }
+                s_union[tid] = u;
+            }
+#pragma unroll
+            for (int t = 0; t < kPerP; ++t) {
+                const int i = tid + t * kSelThreads;
+                if (i < npar) s_par[i] = pv[t];
+            }
         }
         __syncthreads();
         if (wave == 0) {
-            // union words and their exclusive popcount prefix (4 words per lane)
+            // exclusive popcount prefix of the union words (kMergeW / 64 words per lane)
+            constexpr int per = kMergeW / 64;
             uint32_t cnt = 0;
-            for (int q = 0; q < mw / 64; ++q) {
-                const int wi = lane * (mw / 64) + q;
-                uint64_t u = 0;
-                if (wi < nw)
-                    for (int hh = 0; hh < G; ++hh) u |= hw[hh * mw + wi];
-                s_union[wi] = u;
-                cnt += __popcll(u);
+#pragma unroll
+            for (int q = 0; q < per; ++q) {
+                const int wi = lane * per + q;
+                cnt += wi < nw ? __popcll(s_union[wi]) : 0u;
             }
             uint64_t tot;
             uint32_t pre = (uint32_t)wave_excl_scan_u64(cnt, &tot);
-            for (int q = 0; q < mw / 64; ++q) {
-                const int wi = lane * (mw / 64) + q;
+#pragma unroll
+            for (int q = 0; q < per; ++q) {
+                const int wi = lane * per + q;
                 s_wpre[wi] = pre;
-                pre += __popcll(s_union[wi]);
+                pre += wi < nw ? __popcll(s_union[wi]) : 0u;
             }
             if (lane == 0) s_before = tot;
         }
         __syncthreads();
-        const uint64_t run = s_run;
+        const uint32_t run = (uint32_t)s_run;
+        // word wi = 16 k + wave, bit = lane
 #pragma unroll 1
-        for (int64_t p = tid; p < npos; p += kSelThreads) {
-            const int wi = (int)(p >> 6), b = (int)(p & 63);
+        for (int wi = wave; wi < nw; wi += kSelWaves) {
             const uint64_t u = s_union[wi];
-            if (!((u >> b) & 1ull)) continue;
-            const uint64_t rank = run + s_wpre[wi] + __popcll(u & ((1ull << b) - 1ull));
+            if (!lane_bit(u, lane)) continue;
+            const uint32_t rank = run + s_wpre[wi] + bits_below_lane(u);
             uint32_t msk = 0;
-            for (int hh = 0; hh < G; ++hh) msk |= (uint32_t)((hw[hh * mw + wi] >> b) & 1ull) << hh;
-            const int32_t node = a.top ? (int32_t)(wb * 64 + p) : nid[p];
+#pragma unroll
+            for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+                if (hh < G) msk |= lane_bit(hw[wi * G + hh], lane) << hh;
+            const int pos = p0 + wi * 64 + lane;
+            int32_t node;
+            if (a.top) {
+                node = pos;
+            } else if (pos < pnc) {
+                const int pi = (int)zha_div((uint32_t)pos, a.dc);
+                node = s_par[pi - pb0] * c + (pos - pi * c);
+            } else {
+                node = (int32_t)a.orph_lo + (pos - pnc);
+            }
             a.klist[lrow + rank] = node;
             a.kmask[lrow + rank] = msk;
-            if (a.next_node) {
-                for (int i = 0; i < c; ++i) {
-                    a.next_node[nrow + rank * c + i] = node * c + i;
-                    a.next_mask[nrow + rank * c + i] = msk;
-                }
-            }
         }
         __syncthreads();
         if (tid == 0) s_run = run + s_before;
         __syncthreads();
     }
-    const uint64_t total = s_run;
-    if (a.next_node) {
-        const uint32_t allg = all_heads(G);
-        const int64_t n_orph = a.orph_hi - a.orph_lo;
-        for (int64_t o = tid; o < n_orph; o += kSelThreads) {
-            a.next_node[nrow + total * c + o] = (int32_t)(a.orph_lo + o);
-            a.next_mask[nrow + total * c + o] = allg;
-        }
-        if (tid == 0) a.next_ncand[g] = (int32_t)(total * c + n_orph);
-    }
-    if (tid == 0) a.nkept[g] = (int32_t)total;
+    if (tid == 0) a.nkept[g] = (int32_t)s_run;
 }
-
 
 }  // namespace
 

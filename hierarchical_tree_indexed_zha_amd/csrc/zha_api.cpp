@@ -86,7 +86,7 @@ struct Layout {
     std::vector<size_t> t_s, t_b, t_l;
     size_t tree_bytes = 0;
     // decode scratch
-    std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, done, stats;
+    std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, stats;
     std::vector<int64_t> wcap;            // bitmap words per head per level
     size_t pm = 0, pl = 0, po = 0, nact = 0;
     size_t scratch_bytes = 0;
@@ -121,7 +121,7 @@ Layout make_layout(const zha_config* cfg) {
     y.tree_bytes = off;
 
     off = 0;
-    for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.done, &y.stats})
+    for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.stats})
         v->assign(y.L + 1, 0);
     y.wcap.assign(y.L + 1, 0);
     for (int l = 1; l <= y.L; ++l) {
@@ -133,7 +133,6 @@ Layout make_layout(const zha_config* cfg) {
         y.kmask[l] = off; off = align_up(off + sizeof(uint32_t) * H * n);
         y.ncand[l] = off; off = align_up(off + sizeof(int32_t) * H);
         y.nkept[l] = off; off = align_up(off + sizeof(int32_t) * H);
-        y.done[l] = off;  off = align_up(off + sizeof(int32_t) * H);
         y.stats[l] = off; off = align_up(off + sizeof(int32_t) * 2 * H * G);
     }
     attn_partials(cfg, off, y.pm, y.pl, y.po, y.nact);
@@ -319,7 +318,6 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.sig = (float*)(X + y.sig[l]);
         a.kbm = (uint64_t*)(X + y.kbm[l]);
         a.wcap = y.wcap[l];
-        a.done = (int32_t*)(X + y.done[l]);
         a.stats = (int32_t*)(X + y.stats[l]);
         a.klist = (int32_t*)(X + y.klist[l]);
         a.kmask = (uint32_t*)(X + y.kmask[l]);

@@ -64,7 +64,6 @@ struct ZhaLevelArgs {
     float* sig;                // [H_kv][G][cap]
     uint64_t* kbm;             // per-head kept bitmaps [H_kv][G][wcap]
     int64_t wcap;              // bitmap words per head
-    int32_t* done;             // [H_kv]
     int32_t* stats;            // out [H_q][2]
     int32_t* klist;            // out: kept nodes [H_kv][cap], ascending
     uint32_t* kmask;           // out: their head masks

@@ -30,6 +30,8 @@
 // level above's kept nodes (kept list and head masks, ascending) followed by the
 // level's orphans, so a candidate's node id and head mask come from one read of
 // its parent's kept-list entry.
+#include <algorithm>
+
 #include "zha_common.h"
 #include "zha_internal.h"
 
@@ -78,10 +80,7 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     }
     const int pn = a.top ? 0 : a.pnkept[g];
     const int n_cand = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        a.ncand[g] = n_cand;
-        a.done[g] = 0;
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
     // A operand: row = query head j of the group, contraction index d = 16m + 4kq + e.
     float qa[32];
     if (j < G) {
@@ -258,15 +257,18 @@ __device__ void wave_find_cross(const uint64_t* hist, uint64_t need, float top_p
 constexpr int kLdsKeys = 32768;               // heads with at most this many candidates keep their keys in LDS
 constexpr int kSlots = kLdsKeys / kSelThreads;   // positions tid + 1024 k held in registers while staging
 constexpr int kMergeW = kLdsKeys / 64;        // bitmap words merged per step
+constexpr int kBatch = 8;                     // LDS keys read together in a pass
+constexpr int kMergeBlocks = 32;              // merge workgroups per group
+static_assert((kSlots & (kSlots - 1)) == 0 && kSlots % kBatch == 0, "slot batches");
 constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup
 constexpr int kSmallK = kSmallN / 64;
 static_assert(kSelThreads == kSmallN, "small path: one position per thread");
-static_assert(ZHA_MAX_GROUP * kSmallN + ZHA_MAX_GROUP * 256 * 3 <= kLdsKeys,
-              "small-path scores, histograms and counts must fit the key buffer");
 static_assert(2 * ZHA_MAX_GROUP * kMergeW + kMergeW * 32 <= kLdsKeys,
               "merge: head words and parent ids must fit the key buffer");
 static_assert(kMergeW + kMergeW / 2 <= kHistPadded, "merge: union words and prefixes must fit the histogram");
 static_assert(kMergeW <= kSelThreads, "merge: one thread per word of a step");
+static_assert(ZHA_MAX_GROUP * (kSmallN + 3 * 256) + kSmallN <= kLdsKeys, "small path inside the key buffer");
+static_assert(ZHA_MAX_GROUP * kSmallK <= kHistPadded, "small-path kept words inside the histogram");
 
 // Bit `lane` of a 64-bit word, and the number of set bits below it.
 __device__ __forceinline__ uint32_t lane_bit(uint64_t w, int lane) {
@@ -350,8 +352,15 @@ __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* 
             const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(my_bin, src);
             need -= zha_readlane_u64(my_before, src);
             prefix = (prefix << 8) | bin;
-            if (pass == 3) { ustar = prefix; ties = cntb[bin]; }
+            const uint32_t cnt = cntb[bin];
             zha_wave_lds_sync();
+            if (cnt == 1 || pass == 3) {
+                // the crossing bin holds one key (or the keys equal to the cut): the cut
+                // is the largest key with this prefix
+                ustar = (prefix << shift) | ((1u << shift) - 1u);
+                ties = cnt;
+                break;
+            }
         }
     }
     uint32_t n_cand = 0, n_kept = 0;
@@ -405,120 +414,271 @@ __device__ __forceinline__ void stage_small(const ZhaLevelArgs& a, int g, int G,
     s_nid[tid] = node;
 }
 
-// grid (H_q), 1024 threads: one query head per workgroup; the last head of a
-// group to finish writes the group's kept list.  Keys sit in LDS (up to
-// kLdsKeys candidates) or are recomputed from the scores on every pass for
-// larger frontiers.
-__global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelArgs a, int G, int c,
+// One merge step over bitmap words [wb, min(wb + kMergeW, wend)) of a group, run
+// by a whole workgroup: OR the G heads' kept bitmaps, write the kept list entries of the
+// step (ascending position = ascending node) with the mask of heads that kept
+// each node, and return the step's kept count.  `run` is the count of the
+// earlier steps.  LDS: `ws` holds the step's head words [kMergeW][16] (u64,
+// heads >= G zero) and then its parents' node ids; `hs` the union words and
+// their popcount prefixes.
+struct MergeArgs {
+    const uint64_t* gbm;       // the group's head bitmaps [G][wcap]
+    const int32_t* par;        // the parent level's kept list of the group (null at the first routed level)
+    int32_t* kl;               // the group's kept list
+    uint32_t* km;              // and head masks
+    ZhaDiv dc;
+    uint32_t wcap;
+    int c, G, n, pn, orph_lo;
+};
+
+__device__ __forceinline__ uint32_t merge_step(const MergeArgs& ma, int wb, int wend, uint32_t run, uint32_t* ws,
+                                               uint64_t* hs, uint32_t* s_tot_) {
+    uint32_t& s_tot = *s_tot_;
+    // thread index laundered per step: keeps the compiler from holding every
+    // per-thread index of a step in registers across the whole step loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    uint64_t* hw = reinterpret_cast<uint64_t*>(ws);                                  // [kMergeW][16]
+    int32_t* s_par = reinterpret_cast<int32_t*>(ws) + 2 * ZHA_MAX_GROUP * kMergeW;   // parent node ids
+    uint64_t* s_union = hs;                                                          // [kMergeW]
+    uint32_t* s_wpre = reinterpret_cast<uint32_t*>(hs + kMergeW);                    // [kMergeW]
+    const int c = ma.c;
+    const int pnc = ma.pn * c;
+    const int nw = min(kMergeW, wend - wb);
+    const int p0 = wb * 64;
+    const int npos = min(nw * 64, ma.n - p0);
+    // parents of this step's child positions (at most kMergeW * 32 of them for c >= 2)
+    const int pb0 = (int)zha_div((uint32_t)p0, ma.dc);
+    const int pb1 = ma.par ? min(ma.pn, (int)zha_div((uint32_t)(p0 + npos + c - 1), ma.dc)) : pb0;
+    const int npar = max(0, pb1 - pb0);
+    {
+        // the G heads' words and the parent ids of this step, all reads in flight
+        // together: flat index i = 512 hh + wi
+        constexpr int kPerW = ZHA_MAX_GROUP * kMergeW / kSelThreads;
+        constexpr int kPerP = kMergeW * 32 / kSelThreads;
+        uint64_t hv[kPerW];
+        int32_t pv[kPerP];
+        const uint64_t* wbase = ma.gbm + wb;
+        const int32_t* pbase = ma.par + pb0;
+#pragma unroll
+        for (int t = 0; t < kPerW; ++t) {
+            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
+            const uint32_t hh = i / kMergeW, wi = i % kMergeW;
+            hv[t] = (hh < (uint32_t)ma.G && wi < (uint32_t)nw)
+                        ? __hip_atomic_load(wbase + (hh * ma.wcap + wi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : 0ull;
+        }
+#pragma unroll
+        for (int t = 0; t < kPerP; ++t) {
+            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
+            pv[t] = i < (uint32_t)npar ? pbase[i] : 0;
+        }
+#pragma unroll
+        for (int t = 0; t < kPerW; ++t) {
+            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
+            hw[(i % kMergeW) * ZHA_MAX_GROUP + i / kMergeW] = hv[t];
+        }
+#pragma unroll
+        for (int t = 0; t < kPerP; ++t) {
+            const int i = tid + t * kSelThreads;
+            if (i < npar) s_par[i] = pv[t];
+        }
+    }
+    __syncthreads();
+    if (tid < nw) {
+        const uint4* wq = reinterpret_cast<const uint4*>(hw) + tid * (ZHA_MAX_GROUP / 2);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
+            const uint4 v = wq[t];
+            lo |= v.x | v.z;
+            hi |= v.y | v.w;
+        }
+        s_union[tid] = ((uint64_t)hi << 32) | lo;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // exclusive popcount prefix of the union words (kMergeW / 64 words per lane)
+        constexpr int per = kMergeW / 64;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            const int wi = lane * per + q;
+            cnt += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
+        }
+        uint64_t tot;
+        uint32_t pre = (uint32_t)wave_excl_scan_u64(cnt, &tot);
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            const int wi = lane * per + q;
+            s_wpre[wi] = pre;
+            pre += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
+        }
+        if (lane == 0) s_tot = (uint32_t)tot;
+    }
+    __syncthreads();
+    // word wi = 16 k + wave, bit = lane
+    const int sh = lane & 31;
+    const bool hi = lane >= 32;
+#pragma unroll 1
+    for (int wi = wave; wi < nw; wi += kSelWaves) {
+        const uint64_t u = s_union[wi];
+        const uint32_t pre = s_wpre[wi];
+        const uint4* wq = reinterpret_cast<const uint4*>(hw) + wi * (ZHA_MAX_GROUP / 2);
+        uint4 hq[ZHA_MAX_GROUP / 2];
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) hq[t] = wq[t];
+        const int pos = p0 + wi * 64 + lane;
+        const bool child = ma.par && pos < pnc;
+        const int pi = (int)zha_div((uint32_t)pos, ma.dc);
+        const int32_t par = child ? s_par[pi - pb0] : 0;
+        if (!lane_bit(u, lane)) continue;
+        // lane's bit of each head word: low dword for lanes < 32, high dword above
+        uint32_t msk = 0;
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
+            const uint32_t w0 = hi ? hq[t].y : hq[t].x;
+            const uint32_t w1 = hi ? hq[t].w : hq[t].z;
+            msk |= ((w0 >> sh) & 1u) << (2 * t);
+            msk |= ((w1 >> sh) & 1u) << (2 * t + 1);
+        }
+        const uint32_t rank = run + pre + bits_below_lane(u);
+        int32_t node;
+        if (!ma.par) node = pos;
+        else if (child) node = par * c + (pos - pi * c);
+        else node = ma.orph_lo + (pos - pnc);
+        ma.kl[rank] = node;
+        ma.km[rank] = msk;
+    }
+    const uint32_t tot = s_tot;
+    __syncthreads();
+    return tot;
+}
+
+// Small frontiers (n <= kSmallN candidates): one workgroup selects for all G
+// heads of group g (one wave each) from the scores staged in LDS (s_sig
+// [G][kSmallN], s_nid node ids) and writes the kept list.  LDS scratch: s_hist
+// [G][256] (u64), s_cnt [G][256], s_kw [G][kSmallK].
+__device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g, int G, float top_p, int n,
+                                                   const float* s_sig, const int32_t* s_nid, uint64_t* s_hist,
+                                                   uint32_t* s_cnt, uint64_t* s_kw) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t lrow = (size_t)g * a.cap;
+    const int nk = (n + 63) >> 6;
+    if (wave < G) {
+        uint32_t nc_h, nk_h;
+        const float* sg = s_sig + wave * kSmallN;
+        uint64_t* hh_ = s_hist + wave * 256;
+        uint32_t* cc_ = s_cnt + wave * 256;
+        uint64_t* kk_ = s_kw + wave * kSmallK;
+        if (nk <= 1) select_head_wave<1>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+        else if (nk <= 2) select_head_wave<2>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+        else if (nk <= 4) select_head_wave<4>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+        else if (nk <= 8) select_head_wave<8>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+        else select_head_wave<16>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+        if (lane == 0) {
+            a.stats[2 * (g * G + wave) + 0] = (int32_t)nc_h;
+            a.stats[2 * (g * G + wave) + 1] = (int32_t)nk_h;
+        }
+        if (lane < nk) a.kbm[((size_t)g * G + wave) * a.wcap + lane] = kk_[lane];
+    }
+    __syncthreads();
+    // union of the heads' kept words -> kept list (ascending node) and head masks:
+    // wave w < nk handles word w; its rank offset is the popcount of the words below
+    if (nk == 0) {
+        if (tid == 0) a.nkept[g] = 0;
+        return;
+    }
+    if (wave >= nk) return;
+    uint64_t u = 0, uk = 0;
+#pragma unroll 1
+    for (int hh = 0; hh < G; ++hh) u |= s_kw[hh * kSmallK + wave];
+    if (lane < wave) {
+#pragma unroll 1
+        for (int hh = 0; hh < G; ++hh) uk |= s_kw[hh * kSmallK + lane];
+    }
+    uint32_t below = (uint32_t)__popcll(uk);
+    for (int o = 32; o > 0; o >>= 1) below += __shfl_xor(below, o, 64);
+    if (lane_bit(u, lane)) {
+        const uint32_t rank = below + bits_below_lane(u);
+        uint32_t msk = 0;
+#pragma unroll 1
+        for (int hh = 0; hh < G; ++hh) msk |= lane_bit(s_kw[hh * kSmallK + wave], lane) << hh;
+        a.klist[lrow + rank] = s_nid[lane + 64 * wave];
+        a.kmask[lrow + rank] = msk;
+    }
+    if (wave == nk - 1 && lane == 0) a.nkept[g] = (int32_t)(below + (uint32_t)__popcll(u));
+}
+
+// grid (H_kv), 1024 threads: levels with at most kSmallN node slots.  The
+// group's workgroup stages every head's scores with one round trip and selects.
+__global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelArgs a, int G, int c,
                                                                        float top_p) {
-    // keys: per-candidate keys; small path: scores [G][kSmallN], then histograms
-    // [G][256] (u64) and counts [G][256]; merge: head words [kMergeW][G] (u64),
-    // then the step's parent node ids.
+    __shared__ __align__(16) float s_sig[ZHA_MAX_GROUP * kSmallN];
+    __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
+    __shared__ __align__(16) uint32_t s_cnt[ZHA_MAX_GROUP * 256];
+    __shared__ int32_t s_nid[kSmallN];
+    __shared__ uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
+
+    const int g = blockIdx.x;
+    const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
+    const int pn = a.top ? 0 : a.pnkept[g];
+    stage_small(a, g, G, c, threadIdx.x, pn, s_sig, s_nid);
+    const int n = a.top ? (int)a.n_top : pn * c + n_orph;
+    __syncthreads();
+    select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw);
+}
+
+// grid (H_q), 1024 threads: levels with more than kSmallN node slots, one query
+// head per workgroup.  Up to kLdsKeys candidates the keys stay in registers
+// (positions tid + 1024 k); larger frontiers recompute them from the scores on
+// every pass.  The last head of a group to finish writes the group's kept list.
+__global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelArgs a, int G, int c,
+                                                                       float top_p) {
+    // keys: the keys (for the ordered tie pass); merge: head words [kMergeW][16]
+    // (u64), then the step's parent node ids
     __shared__ __align__(16) uint32_t keys[kLdsKeys];
     __shared__ __align__(16) uint64_t hist[kHistPadded];   // merge: union words, then popcount prefixes
     __shared__ uint32_t cntb[kHistBins];
-    __shared__ int32_t s_nid[kSmallN];
-    __shared__ uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
     __shared__ uint64_t s_wt[kSelWaves];
     __shared__ float swf[kSelWaves];
-    __shared__ int s_bin, s_last;
+    __shared__ int s_bin;
     __shared__ uint64_t s_before, s_need, s_run;
     __shared__ uint32_t s_cnt[2];
 
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t lrow = (size_t)g * a.cap;
     const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
-    float* s_sig = reinterpret_cast<float*>(keys);
+    const float* sg = a.sig + ((size_t)g * G + hl) * a.cap;
 
-    // Every global read below is issued before the candidate count is known:
-    // reads stay inside the level's arrays (positions < cap) and positions >= n
-    // are ignored afterwards, so the count, the scores and the node ids cost one
-    // memory round trip together.
-    float sv[kSlots];                          // own head's scores, positions tid + 1024 k
-    int pn, n;
-    if (a.cap <= kSmallN) {
-        if (hl != 0) return;                   // n <= cap: the small path for sure
-        pn = a.top ? 0 : a.pnkept[g];
-        stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
-        n = a.top ? (int)a.n_top : pn * c + n_orph;
-    } else {
-        const int pnk = a.top ? 0 : a.pnkept[g];
-        const float* sg0 = a.sig + ((size_t)g * G + hl) * a.cap;
+    // The count and the scores of positions < min(cap, kLdsKeys) are read
+    // together (one round trip); positions >= n are ignored afterwards.
+    const int pn = a.top ? 0 : a.pnkept[g];
+    uint32_t kr[kSlots];
+    {
         const int lim = (int)min(a.cap, (int64_t)kLdsKeys);
 #pragma unroll
         for (int k = 0; k < kSlots; ++k) {
             const int pos = tid + k * kSelThreads;
-            sv[k] = pos < lim ? sg0[pos] : zha_neg_inf();
-        }
-        pn = pnk;
-        n = a.top ? (int)a.n_top : pn * c + n_orph;
-        if (n <= kSmallN) {
-            if (hl != 0) return;               // the same decision for every head of the group
-            stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
+            kr[k] = __float_as_uint(pos < lim ? sg[pos] : zha_neg_inf());
         }
     }
-
+    const int n = a.top ? (int)a.n_top : pn * c + n_orph;
     if (n <= kSmallN) {
-        // ---- small frontier: the group's first workgroup selects for all G heads
-        // (one wave each) and merges from LDS
+        // a small frontier at a large level: the group's first workgroup selects for
+        // all heads, with the key buffer as its LDS
+        if (hl != 0) return;
+        float* s_sig = reinterpret_cast<float*>(keys);                                   // [G][kSmallN]
+        uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
+        uint32_t* s_cnt = keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256;      // [G][256]
+        int32_t* s_nid = reinterpret_cast<int32_t*>(s_cnt + ZHA_MAX_GROUP * 256);          // [kSmallN]
+        uint64_t* s_kw = hist;                                                           // [G][kSmallK]
+        stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
         __syncthreads();
-        uint64_t* shist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);      // [G][256]
-        uint32_t* scnt = keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256;           // [G][256]
-        uint64_t* kw = s_kw;                                                               // [G][kSmallK]
-        const int nk = (n + 63) >> 6;
-        if (wave < G) {
-            uint32_t nc_h, nk_h;
-            const float* sg = s_sig + wave * kSmallN;
-            uint64_t* hh_ = shist + wave * 256;
-            uint32_t* cc_ = scnt + wave * 256;
-            uint64_t* kk_ = kw + wave * kSmallK;
-            if (nk <= 1) select_head_wave<1>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-            else if (nk <= 2) select_head_wave<2>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-            else if (nk <= 4) select_head_wave<4>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-            else if (nk <= 8) select_head_wave<8>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-            else select_head_wave<16>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-            if (lane == 0) {
-                a.stats[2 * (g * G + wave) + 0] = (int32_t)nc_h;
-                a.stats[2 * (g * G + wave) + 1] = (int32_t)nk_h;
-            }
-            if (lane < nk) a.kbm[((size_t)g * G + wave) * a.wcap + lane] = kk_[lane];
-        }
-        __syncthreads();
-        // union of the heads' kept words -> kept list (ascending node) and head masks:
-        // wave w < nk handles word w; its rank offset is the popcount of the words below
-        if (nk == 0) {
-            if (tid == 0) a.nkept[g] = 0;
-            return;
-        }
-        if (wave >= nk) return;
-        uint64_t u = 0;
-        uint32_t below = 0;
-#pragma unroll 1
-        for (int hh = 0; hh < G; ++hh) u |= kw[hh * kSmallK + wave];
-        // words below this one: lane k < wave contributes the union of word k
-        uint64_t uk = 0;
-        if (lane < wave) {
-#pragma unroll 1
-            for (int hh = 0; hh < G; ++hh) uk |= kw[hh * kSmallK + lane];
-        }
-        below = (uint32_t)__popcll(uk);
-        for (int o = 32; o > 0; o >>= 1) below += __shfl_xor(below, o, 64);
-        if (lane_bit(u, lane)) {
-            const uint32_t rank = below + bits_below_lane(u);
-            uint32_t msk = 0;
-#pragma unroll 1
-            for (int hh = 0; hh < G; ++hh) msk |= lane_bit(kw[hh * kSmallK + wave], lane) << hh;
-            a.klist[lrow + rank] = s_nid[lane + 64 * wave];
-            a.kmask[lrow + rank] = msk;
-        }
-        if (wave == nk - 1 && lane == 0) a.nkept[g] = (int32_t)(below + (uint32_t)__popcll(u));
+        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw);
         return;
     }
-
-    // ---- large frontier: one workgroup per head
-    const float* sg = a.sig + ((size_t)g * G + hl) * a.cap;
-    uint64_t* bm = a.kbm + ((size_t)g * G + hl) * a.wcap;
     const int nwords = (n + 63) >> 6;
     const int nslot = (n + kSelThreads - 1) / kSelThreads;   // positions per thread
     const bool staged = n <= kLdsKeys;
@@ -529,8 +689,8 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
 #pragma unroll
         for (int k = 0; k < kSlots; ++k) {
             if (k < nslot) {
-                if (tid + k * kSelThreads >= n) sv[k] = zha_neg_inf();
-                m = fmaxf(m, sv[k]);
+                if (tid + k * kSelThreads >= n) kr[k] = __float_as_uint(zha_neg_inf());
+                m = fmaxf(m, __uint_as_float(kr[k]));
             }
         }
     } else {
@@ -544,10 +704,8 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
     for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, swf[w]);
     if (staged) {
 #pragma unroll
-        for (int k = 0; k < kSlots; ++k) {
-            const int pos = tid + k * kSelThreads;
-            if (k < nslot && pos < n) keys[pos] = key_of(sv[k], m);
-        }
+        for (int k = 0; k < kSlots; ++k)
+            if (k < nslot) keys[tid + k * kSelThreads] = key_of(__uint_as_float(kr[k]), m);
     }
 
     // Kept rule: keep_all, or key < ustar, or key == ustar when that key is unique.
@@ -564,13 +722,29 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
         for (int pass = 0; pass < 3; ++pass) {
             // pass 0 counts every key that carries mass; later passes only the keys
             // whose higher digits equal the bins found so far
+            const bool all = pass == 0;
+            if (staged) {
+                // keys read from LDS kBatch slots at a time (all reads in flight together)
 #pragma unroll 1
-            for (int k = 0; k < nslot; ++k) {
-                const int pos = tid + k * kSelThreads;
-                if (pos < n) {
-                    const uint32_t key = staged ? keys[pos] : key_of(sg[pos], m);
-                    const bool match = pass == 0 ? true : (key >> mshift) == mval;
-                    if (key < kNoMass && match) {
+                for (int k0 = 0; k0 < nslot; k0 += kBatch) {
+                    uint32_t kk[kBatch];
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j) kk[j] = keys[tid + ((k0 + j) & (kSlots - 1)) * kSelThreads];
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j) {
+                        const uint32_t key = k0 + j < nslot ? kk[j] : kNotCand;
+                        if (key < kNoMass && (all || (key >> mshift) == mval)) {
+                            const uint32_t b = (key >> bshift) & bmask;
+                            atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
+                            atomicAdd(&cntb[b], 1u);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll 4
+                for (int pos = tid; pos < n; pos += kSelThreads) {
+                    const uint32_t key = key_of(sg[pos], m);
+                    if (key < kNoMass && (all || (key >> mshift) == mval)) {
                         const uint32_t b = (key >> bshift) & bmask;
                         atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
                         atomicAdd(&cntb[b], 1u);
@@ -582,32 +756,55 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
             __syncthreads();
             const uint32_t bin = (uint32_t)s_bin;
             need = s_need - s_before;            // mass still needed inside this bin
-            if (pass == 0) { mshift = 21; mval = bin; bshift = 10; bmask = 2047; }
-            else if (pass == 1) { mshift = 10; mval = (mval << 11) | bin; bshift = 0; bmask = 1023; }
-            else { ustar = (mval << 10) | bin; ties = cntb[bin]; }
-            if (pass < 2) {
-                __syncthreads();                 // every thread has read this pass's result
-                for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
-                for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
-                __syncthreads();
+            const uint32_t cnt = cntb[bin];
+            const uint32_t pref = pass == 0 ? bin : (mval << (pass == 1 ? 11 : 10)) | bin;
+            if (cnt == 1 || pass == 2) {
+                // the crossing bin holds one key (or the keys equal to the cut): the cut
+                // is the largest key with this prefix
+                ustar = (pref << bshift) | ((1u << bshift) - 1u);
+                ties = cnt;
+                break;
             }
+            if (pass == 0) { mshift = 21; mval = pref; bshift = 10; bmask = 2047; }
+            else { mshift = 10; mval = pref; bshift = 0; bmask = 1023; }
+            __syncthreads();                     // every thread has read this pass's result
+            for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
+            for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
+            __syncthreads();
         }
     }
     const uint64_t need_tie = need;
 
     // kept flags -> this head's bitmap: slot k of wave w is word 16 k + w
+    uint64_t* bm = a.kbm + ((size_t)g * G + hl) * a.wcap;
     uint32_t my_cand = 0, my_kept = 0;
+    if (staged) {
 #pragma unroll 1
-    for (int k = 0; k < nslot; ++k) {
-        const int pos = tid + k * kSelThreads;
-        const uint32_t key = pos < n ? (staged ? keys[pos] : key_of(sg[pos], m)) : kNotCand;
-        const bool cand = key != kNotCand;
-        const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
-        const uint64_t word = __ballot(kept);
-        const int wi = k * kSelWaves + wave;
-        if (lane == 0 && wi < nwords) bm[wi] = word;
-        my_cand += cand;
-        my_kept += kept;
+        for (int k = 0; k < nslot; ++k) {
+            {
+                const uint32_t key = keys[tid + k * kSelThreads];
+                const bool cand = key != kNotCand;
+                const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
+                const uint64_t word = __ballot(kept);
+                const int wi = k * kSelWaves + wave;
+                if (lane == 0 && wi < nwords) bm[wi] = word;
+                my_cand += cand;
+                my_kept += kept;
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int k = 0; k < nslot; ++k) {
+            const int pos = tid + k * kSelThreads;
+            const uint32_t key = pos < n ? key_of(sg[pos], m) : kNotCand;
+            const bool cand = key != kNotCand;
+            const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
+            const uint64_t word = __ballot(kept);
+            const int wi = k * kSelWaves + wave;
+            if (lane == 0 && wi < nwords) bm[wi] = word;
+            my_cand += cand;
+            my_kept += kept;
+        }
     }
     if (!none && !keep_all && ties > 1) {
         // several candidates share the cut key: take them in ascending position order
@@ -646,116 +843,65 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_select_kernel(ZhaLevelA
         }
     }
 
-    // ---- the last head of the group to finish merges the group's bitmaps
     __syncthreads();
     if (tid == 0) {
         a.stats[2 * h + 0] = (int32_t)s_cnt[0];
         a.stats[2 * h + 1] = (int32_t)s_cnt[1];
-        __threadfence();
-        const int prev = atomicAdd(&a.done[g], 1);
-        s_last = (prev == G - 1);
     }
+}
+
+// grid (kMergeBlocks, H_kv), 1024 threads: the kept list of a level whose heads
+// were selected by zha_select_large_kernel.  Block b handles an equal share of
+// the group's bitmap words (a multiple of 16); its rank offset is the number of
+// kept nodes in the words before its share.
+__global__ __launch_bounds__(kSelThreads) void zha_merge_kernel(ZhaLevelArgs a, int G, int c) {
+    __shared__ __align__(16) uint32_t ws[kLdsKeys];
+    __shared__ __align__(16) uint64_t hs[kMergeW + kMergeW / 2];
+    __shared__ uint32_t s_part[kSelWaves];
+    __shared__ uint32_t s_tot;
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int pn = a.top ? 0 : a.pnkept[g];
+    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (n <= kSmallN) return;                    // selected and merged by the select kernel
+    const int nwords = (n + 63) >> 6;
+    const int share = ((nwords + gridDim.x - 1) / gridDim.x + kSelWaves - 1) / kSelWaves * kSelWaves;
+    const int w0 = blockIdx.x * share;
+    const int w1 = min(nwords, w0 + share);
+    if (w0 >= w1) return;
+    MergeArgs ma;
+    ma.gbm = a.kbm + (size_t)g * G * a.wcap;
+    ma.par = a.top ? nullptr : a.pklist + (size_t)g * a.pcap;
+    ma.kl = a.klist + (size_t)g * a.cap;
+    ma.km = a.kmask + (size_t)g * a.cap;
+    ma.dc = a.dc;
+    ma.wcap = (uint32_t)a.wcap;
+    ma.c = c;
+    ma.G = G;
+    ma.n = n;
+    ma.pn = pn;
+    ma.orph_lo = (int)a.orph_lo;
+    // kept nodes in the words before this block's share
+    uint32_t cnt = 0;
+#pragma unroll 1
+    for (int w = tid; w < w0; w += kSelThreads) {
+        uint64_t hv[ZHA_MAX_GROUP];
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hv[hh] = hh < G ? ma.gbm[(size_t)hh * ma.wcap + w] : 0ull;
+        uint64_t u = 0;
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= hv[hh];
+        cnt += (uint32_t)__popcll(u);
+    }
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    if (lane == 0) s_part[wave] = cnt;
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const uint64_t* gbm = a.kbm + (size_t)g * G * a.wcap;
-    const size_t prow = (size_t)g * a.pcap;
-    uint64_t* hw = reinterpret_cast<uint64_t*>(keys);                              // [kMergeW][G]
-    int32_t* s_par = reinterpret_cast<int32_t*>(keys) + 2 * ZHA_MAX_GROUP * kMergeW;   // parent node ids
-    uint64_t* s_union = hist;                                                      // [kMergeW]
-    uint32_t* s_wpre = reinterpret_cast<uint32_t*>(hist + kMergeW);                // [kMergeW]
-    const int pnc = pn * c;
-    if (tid == 0) s_run = 0;
+    uint32_t run = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) run += s_part[w];
 #pragma unroll 1
-    for (int wb = 0; wb < nwords; wb += kMergeW) {
-        const int nw = min(kMergeW, nwords - wb);
-        const int p0 = wb * 64;
-        const int npos = min(nw * 64, n - p0);
-        // parents of this step's child positions (at most kMergeW * 32 of them for c >= 2)
-        const int pb0 = (int)zha_div((uint32_t)p0, a.dc);
-        const int pb1 = a.top ? pb0 : min(pn, (int)zha_div((uint32_t)(p0 + npos + c - 1), a.dc));
-        const int npar = max(0, pb1 - pb0);
-        {
-            // the G heads' words (one word per thread) and the parent ids of this
-            // step, all reads in flight together
-            constexpr int kPerP = kMergeW * 32 / kSelThreads;
-            uint64_t hv[ZHA_MAX_GROUP];
-            int32_t pv[kPerP];
-#pragma unroll
-            for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-                hv[hh] = (hh < G && tid < nw) ? __hip_atomic_load(gbm + (size_t)hh * a.wcap + wb + tid,
-                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                              : 0ull;
-#pragma unroll
-            for (int t = 0; t < kPerP; ++t) {
-                const int i = tid + t * kSelThreads;
-                pv[t] = i < npar ? a.pklist[prow + pb0 + i] : 0;
-            }
-            if (tid < nw) {
-                uint64_t u = 0;
-#pragma unroll
-                for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
-                    if (hh < G) hw[tid * G + hh] = hv[hh];
-                    u |= hv[hh];
-                }
-                s_union[tid] = u;
-            }
-#pragma unroll
-            for (int t = 0; t < kPerP; ++t) {
-                const int i = tid + t * kSelThreads;
-                if (i < npar) s_par[i] = pv[t];
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // exclusive popcount prefix of the union words (kMergeW / 64 words per lane)
-            constexpr int per = kMergeW / 64;
-            uint32_t cnt = 0;
-#pragma unroll
-            for (int q = 0; q < per; ++q) {
-                const int wi = lane * per + q;
-                cnt += wi < nw ? __popcll(s_union[wi]) : 0u;
-            }
-            uint64_t tot;
-            uint32_t pre = (uint32_t)wave_excl_scan_u64(cnt, &tot);
-#pragma unroll
-            for (int q = 0; q < per; ++q) {
-                const int wi = lane * per + q;
-                s_wpre[wi] = pre;
-                pre += wi < nw ? __popcll(s_union[wi]) : 0u;
-            }
-            if (lane == 0) s_before = tot;
-        }
-        __syncthreads();
-        const uint32_t run = (uint32_t)s_run;
-        // word wi = 16 k + wave, bit = lane
-#pragma unroll 1
-        for (int wi = wave; wi < nw; wi += kSelWaves) {
-            const uint64_t u = s_union[wi];
-            if (!lane_bit(u, lane)) continue;
-            const uint32_t rank = run + s_wpre[wi] + bits_below_lane(u);
-            uint32_t msk = 0;
-#pragma unroll
-            for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-                if (hh < G) msk |= lane_bit(hw[wi * G + hh], lane) << hh;
-            const int pos = p0 + wi * 64 + lane;
-            int32_t node;
-            if (a.top) {
-                node = pos;
-            } else if (pos < pnc) {
-                const int pi = (int)zha_div((uint32_t)pos, a.dc);
-                node = s_par[pi - pb0] * c + (pos - pi * c);
-            } else {
-                node = (int32_t)a.orph_lo + (pos - pnc);
-            }
-            a.klist[lrow + rank] = node;
-            a.kmask[lrow + rank] = msk;
-        }
-        __syncthreads();
-        if (tid == 0) s_run = run + s_before;
-        __syncthreads();
-    }
-    if (tid == 0) a.nkept[g] = (int32_t)s_run;
+    for (int wb = w0; wb < w1; wb += kMergeW) run += merge_step(ma, wb, w1, run, ws, hs, &s_tot);
+    if (w1 == nwords && tid == 0) a.nkept[g] = (int32_t)run;
 }
 
 }  // namespace
@@ -780,7 +926,18 @@ hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArg
 }
 
 hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream) {
-    hipLaunchKernelGGL(zha_route_select_kernel, dim3((unsigned)(H_kv * G)), dim3(kSelThreads), 0, stream, a, G,
+    if (a.cap <= kSmallN) {
+        hipLaunchKernelGGL(zha_select_small_kernel, dim3((unsigned)H_kv), dim3(kSelThreads), 0, stream, a, G, c,
+                           top_p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(zha_select_large_kernel, dim3((unsigned)(H_kv * G)), dim3(kSelThreads), 0, stream, a, G,
                        c, top_p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t wcap = a.wcap;
+    const int blocks = (int)std::min<int64_t>(kMergeBlocks, (wcap + kSelWaves - 1) / kSelWaves);
+    hipLaunchKernelGGL(zha_merge_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(kSelThreads), 0, stream, a,
+                       G, c);
     return hipGetLastError();
 }

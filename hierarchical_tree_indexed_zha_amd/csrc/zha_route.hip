@@ -414,148 +414,6 @@ __device__ __forceinline__ void stage_small(const ZhaLevelArgs& a, int g, int G,
     s_nid[tid] = node;
 }
 
-// One merge step over bitmap words [wb, min(wb + kMergeW, wend)) of a group, run
-// by a whole workgroup: OR the G heads' kept bitmaps, write the kept list entries of the
-// step (ascending position = ascending node) with the mask of heads that kept
-// each node, and return the step's kept count.  `run` is the count of the
-// earlier steps.  LDS: `ws` holds the step's head words [kMergeW][16] (u64,
-// heads >= G zero) and then its parents' node ids; `hs` the union words and
-// their popcount prefixes.
-struct MergeArgs {
-    const uint64_t* gbm;       // the group's head bitmaps [G][wcap]
-    const int32_t* par;        // the parent level's kept list of the group (null at the first routed level)
-    int32_t* kl;               // the group's kept list
-    uint32_t* km;              // and head masks
-    ZhaDiv dc;
-    uint32_t wcap;
-    int c, G, n, pn, orph_lo;
-};
-
-__device__ __forceinline__ uint32_t merge_step(const MergeArgs& ma, int wb, int wend, uint32_t run, uint32_t* ws,
-                                               uint64_t* hs, uint32_t* s_tot_) {
-    uint32_t& s_tot = *s_tot_;
-    // thread index laundered per step: keeps the compiler from holding every
-    // per-thread index of a step in registers across the whole step loop
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, wave = tid >> 6;
-    uint64_t* hw = reinterpret_cast<uint64_t*>(ws);                                  // [kMergeW][16]
-    int32_t* s_par = reinterpret_cast<int32_t*>(ws) + 2 * ZHA_MAX_GROUP * kMergeW;   // parent node ids
-    uint64_t* s_union = hs;                                                          // [kMergeW]
-    uint32_t* s_wpre = reinterpret_cast<uint32_t*>(hs + kMergeW);                    // [kMergeW]
-    const int c = ma.c;
-    const int pnc = ma.pn * c;
-    const int nw = min(kMergeW, wend - wb);
-    const int p0 = wb * 64;
-    const int npos = min(nw * 64, ma.n - p0);
-    // parents of this step's child positions (at most kMergeW * 32 of them for c >= 2)
-    const int pb0 = (int)zha_div((uint32_t)p0, ma.dc);
-    const int pb1 = ma.par ? min(ma.pn, (int)zha_div((uint32_t)(p0 + npos + c - 1), ma.dc)) : pb0;
-    const int npar = max(0, pb1 - pb0);
-    {
-        // the G heads' words and the parent ids of this step, all reads in flight
-        // together: flat index i = 512 hh + wi
-        constexpr int kPerW = ZHA_MAX_GROUP * kMergeW / kSelThreads;
-        constexpr int kPerP = kMergeW * 32 / kSelThreads;
-        uint64_t hv[kPerW];
-        int32_t pv[kPerP];
-        const uint64_t* wbase = ma.gbm + wb;
-        const int32_t* pbase = ma.par + pb0;
-#pragma unroll
-        for (int t = 0; t < kPerW; ++t) {
-            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
-            const uint32_t hh = i / kMergeW, wi = i % kMergeW;
-            hv[t] = (hh < (uint32_t)ma.G && wi < (uint32_t)nw)
-                        ? __hip_atomic_load(wbase + (hh * ma.wcap + wi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : 0ull;
-        }
-#pragma unroll
-        for (int t = 0; t < kPerP; ++t) {
-            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
-            pv[t] = i < (uint32_t)npar ? pbase[i] : 0;
-        }
-#pragma unroll
-        for (int t = 0; t < kPerW; ++t) {
-            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
-            hw[(i % kMergeW) * ZHA_MAX_GROUP + i / kMergeW] = hv[t];
-        }
-#pragma unroll
-        for (int t = 0; t < kPerP; ++t) {
-            const int i = tid + t * kSelThreads;
-            if (i < npar) s_par[i] = pv[t];
-        }
-    }
-    __syncthreads();
-    if (tid < nw) {
-        const uint4* wq = reinterpret_cast<const uint4*>(hw) + tid * (ZHA_MAX_GROUP / 2);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
-            const uint4 v = wq[t];
-            lo |= v.x | v.z;
-            hi |= v.y | v.w;
-        }
-        s_union[tid] = ((uint64_t)hi << 32) | lo;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        // exclusive popcount prefix of the union words (kMergeW / 64 words per lane)
-        constexpr int per = kMergeW / 64;
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int q = 0; q < per; ++q) {
-            const int wi = lane * per + q;
-            cnt += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
-        }
-        uint64_t tot;
-        uint32_t pre = (uint32_t)wave_excl_scan_u64(cnt, &tot);
-#pragma unroll
-        for (int q = 0; q < per; ++q) {
-            const int wi = lane * per + q;
-            s_wpre[wi] = pre;
-            pre += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
-        }
-        if (lane == 0) s_tot = (uint32_t)tot;
-    }
-    __syncthreads();
-    // word wi = 16 k + wave, bit = lane
-    const int sh = lane & 31;
-    const bool hi = lane >= 32;
-#pragma unroll 1
-    for (int wi = wave; wi < nw; wi += kSelWaves) {
-        const uint64_t u = s_union[wi];
-        const uint32_t pre = s_wpre[wi];
-        const uint4* wq = reinterpret_cast<const uint4*>(hw) + wi * (ZHA_MAX_GROUP / 2);
-        uint4 hq[ZHA_MAX_GROUP / 2];
-#pragma unroll
-        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) hq[t] = wq[t];
-        const int pos = p0 + wi * 64 + lane;
-        const bool child = ma.par && pos < pnc;
-        const int pi = (int)zha_div((uint32_t)pos, ma.dc);
-        const int32_t par = child ? s_par[pi - pb0] : 0;
-        if (!lane_bit(u, lane)) continue;
-        // lane's bit of each head word: low dword for lanes < 32, high dword above
-        uint32_t msk = 0;
-#pragma unroll
-        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
-            const uint32_t w0 = hi ? hq[t].y : hq[t].x;
-            const uint32_t w1 = hi ? hq[t].w : hq[t].z;
-            msk |= ((w0 >> sh) & 1u) << (2 * t);
-            msk |= ((w1 >> sh) & 1u) << (2 * t + 1);
-        }
-        const uint32_t rank = run + pre + bits_below_lane(u);
-        int32_t node;
-        if (!ma.par) node = pos;
-        else if (child) node = par * c + (pos - pi * c);
-        else node = ma.orph_lo + (pos - pnc);
-        ma.kl[rank] = node;
-        ma.km[rank] = msk;
-    }
-    const uint32_t tot = s_tot;
-    __syncthreads();
-    return tot;
-}
-
 // Small frontiers (n <= kSmallN candidates): one workgroup selects for all G
 // heads of group g (one wave each) from the scores staged in LDS (s_sig
 // [G][kSmallN], s_nid node ids) and writes the kept list.  LDS scratch: s_hist
@@ -850,58 +708,161 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
     }
 }
 
-// grid (kMergeBlocks, H_kv), 1024 threads: the kept list of a level whose heads
-// were selected by zha_select_large_kernel.  Block b handles an equal share of
-// the group's bitmap words (a multiple of 16); its rank offset is the number of
-// kept nodes in the words before its share.
-__global__ __launch_bounds__(kSelThreads) void zha_merge_kernel(ZhaLevelArgs a, int G, int c) {
-    __shared__ __align__(16) uint32_t ws[kLdsKeys];
-    __shared__ __align__(16) uint64_t hs[kMergeW + kMergeW / 2];
+// grid (blocks, H_kv), 1024 threads: the kept list of a level whose heads were
+// selected by zha_select_large_kernel.  Block b owns bitmap words [b share,
+// (b + 1) share) of its group (share <= kMergeW, a multiple of 16): it ORs the G
+// heads' words, writes the kept list entries of its positions (ascending
+// position = ascending node) with the mask of heads that kept each node, and
+// offsets their ranks by the kept nodes in the words before its share.  The
+// count, the share's words, its parents' node ids and the words before it are
+// all read before the count is known (bounded by the capacities), so they cost
+// one memory round trip together.
+__global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelArgs a, int G, int c, int share) {
+    __shared__ __align__(16) uint64_t hw[kMergeW * ZHA_MAX_GROUP];   // [word][16 heads], heads >= G zero
+    __shared__ int32_t s_par[kMergeW * 32];                            // parents' node ids
+    __shared__ uint64_t s_union[kMergeW];
+    __shared__ uint32_t s_wpre[kMergeW];
     __shared__ uint32_t s_part[kSelWaves];
     __shared__ uint32_t s_tot;
     const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wcap = (int)a.wcap;
+    const int w0 = blockIdx.x * share;
+    const int wend_s = min(w0 + share, wcap);                 // words this block may own
+    const uint64_t* gbm = a.kbm + (size_t)g * G * a.wcap;
+    const int32_t* par = a.top ? nullptr : a.pklist + (size_t)g * a.pcap;
+    const int p0 = w0 * 64;
+    const int pb0 = (int)zha_div((uint32_t)p0, a.dc);
+    const int pb_s = a.top ? pb0 : min((int)a.pcap, (int)zha_div((uint32_t)(wend_s * 64 + c - 1), a.dc));
+    const int npar_s = max(0, pb_s - pb0);
+
+    constexpr int kPerW = ZHA_MAX_GROUP * kMergeW / kSelThreads;
+    constexpr int kPerP = kMergeW * 32 / kSelThreads;
     const int pn = a.top ? 0 : a.pnkept[g];
+    uint64_t hv[kPerW];
+    int32_t pv[kPerP];
+    uint64_t pw[ZHA_MAX_GROUP];
+#pragma unroll
+    for (int t = 0; t < kPerW; ++t) {
+        const uint32_t i = (uint32_t)(tid + t * kSelThreads);
+        const uint32_t hh = i / kMergeW, wi = i % kMergeW;
+        hv[t] = (hh < (uint32_t)G && w0 + (int)wi < wend_s) ? gbm[(size_t)hh * a.wcap + w0 + wi] : 0ull;
+    }
+#pragma unroll
+    for (int t = 0; t < kPerP; ++t) {
+        const int i = tid + t * kSelThreads;
+        pv[t] = i < npar_s ? par[pb0 + i] : 0;
+    }
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        pw[hh] = (hh < G && tid < w0) ? gbm[(size_t)hh * a.wcap + tid] : 0ull;
+
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
     if (n <= kSmallN) return;                    // selected and merged by the select kernel
     const int nwords = (n + 63) >> 6;
-    const int share = ((nwords + gridDim.x - 1) / gridDim.x + kSelWaves - 1) / kSelWaves * kSelWaves;
-    const int w0 = blockIdx.x * share;
-    const int w1 = min(nwords, w0 + share);
-    if (w0 >= w1) return;
-    MergeArgs ma;
-    ma.gbm = a.kbm + (size_t)g * G * a.wcap;
-    ma.par = a.top ? nullptr : a.pklist + (size_t)g * a.pcap;
-    ma.kl = a.klist + (size_t)g * a.cap;
-    ma.km = a.kmask + (size_t)g * a.cap;
-    ma.dc = a.dc;
-    ma.wcap = (uint32_t)a.wcap;
-    ma.c = c;
-    ma.G = G;
-    ma.n = n;
-    ma.pn = pn;
-    ma.orph_lo = (int)a.orph_lo;
-    // kept nodes in the words before this block's share
+    if (w0 >= nwords) return;
+    const int w1 = min(wend_s, nwords);
+    const int nw = w1 - w0;
+    const int pnc = pn * c;
+
+    // rank offset: kept nodes in words [0, w0)
     uint32_t cnt = 0;
-#pragma unroll 1
-    for (int w = tid; w < w0; w += kSelThreads) {
-        uint64_t hv[ZHA_MAX_GROUP];
-#pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hv[hh] = hh < G ? ma.gbm[(size_t)hh * ma.wcap + w] : 0ull;
+    {
         uint64_t u = 0;
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= hv[hh];
-        cnt += (uint32_t)__popcll(u);
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= pw[hh];
+        cnt = (uint32_t)__popcll(u);
+#pragma unroll 1
+        for (int w = tid + kSelThreads; w < w0; w += kSelThreads) {
+            uint64_t v = 0;
+            for (int hh = 0; hh < G; ++hh) v |= gbm[(size_t)hh * a.wcap + w];
+            cnt += (uint32_t)__popcll(v);
+        }
     }
     for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
     if (lane == 0) s_part[wave] = cnt;
+#pragma unroll
+    for (int t = 0; t < kPerW; ++t) {
+        const uint32_t i = (uint32_t)(tid + t * kSelThreads);
+        hw[(i % kMergeW) * ZHA_MAX_GROUP + i / kMergeW] = (int)(i % kMergeW) < nw ? hv[t] : 0ull;
+    }
+#pragma unroll
+    for (int t = 0; t < kPerP; ++t) {
+        const int i = tid + t * kSelThreads;
+        if (i < npar_s) s_par[i] = pv[t];
+    }
     __syncthreads();
     uint32_t run = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) run += s_part[w];
+    if (tid < nw) {
+        const uint4* wq = reinterpret_cast<const uint4*>(hw) + tid * (ZHA_MAX_GROUP / 2);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
+            const uint4 v = wq[t];
+            lo |= v.x | v.z;
+            hi |= v.y | v.w;
+        }
+        s_union[tid] = ((uint64_t)hi << 32) | lo;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // exclusive popcount prefix of the union words (kMergeW / 64 words per lane)
+        constexpr int per = kMergeW / 64;
+        uint32_t c2 = 0;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            const int wi = lane * per + q;
+            c2 += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
+        }
+        uint64_t tot;
+        uint32_t pre = (uint32_t)wave_excl_scan_u64(c2, &tot);
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            const int wi = lane * per + q;
+            s_wpre[wi] = pre;
+            pre += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
+        }
+        if (lane == 0) s_tot = (uint32_t)tot;
+    }
+    __syncthreads();
+    int32_t* kl = a.klist + (size_t)g * a.cap;
+    uint32_t* km = a.kmask + (size_t)g * a.cap;
+    // word wi = 16 k + wave, bit = lane
+    const int sh = lane & 31;
+    const bool hi = lane >= 32;
 #pragma unroll 1
-    for (int wb = w0; wb < w1; wb += kMergeW) run += merge_step(ma, wb, w1, run, ws, hs, &s_tot);
-    if (w1 == nwords && tid == 0) a.nkept[g] = (int32_t)run;
+    for (int wi = wave; wi < nw; wi += kSelWaves) {
+        const uint64_t u = s_union[wi];
+        const uint32_t pre = s_wpre[wi];
+        const uint4* wq = reinterpret_cast<const uint4*>(hw) + wi * (ZHA_MAX_GROUP / 2);
+        uint4 hq[ZHA_MAX_GROUP / 2];
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) hq[t] = wq[t];
+        const int pos = p0 + wi * 64 + lane;
+        const bool child = par && pos < pnc;
+        const int pi = (int)zha_div((uint32_t)pos, a.dc);
+        const int32_t pnode = child ? s_par[pi - pb0] : 0;
+        if (!lane_bit(u, lane)) continue;
+        // lane's bit of each head word: low dword for lanes < 32, high dword above
+        uint32_t msk = 0;
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
+            const uint32_t x0 = hi ? hq[t].y : hq[t].x;
+            const uint32_t x1 = hi ? hq[t].w : hq[t].z;
+            msk |= ((x0 >> sh) & 1u) << (2 * t);
+            msk |= ((x1 >> sh) & 1u) << (2 * t + 1);
+        }
+        const uint32_t rank = run + pre + bits_below_lane(u);
+        int32_t node;
+        if (!par) node = pos;
+        else if (child) node = pnode * c + (pos - pi * c);
+        else node = (int32_t)a.orph_lo + (pos - pnc);
+        kl[rank] = node;
+        km[rank] = msk;
+    }
+    if (w1 == nwords && tid == 0) a.nkept[g] = (int32_t)(run + s_tot);
 }
 
 }  // namespace
@@ -935,9 +896,13 @@ hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c
                        c, top_p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // bitmap words per merge block: a multiple of 16, at most kMergeW, over at
+    // least kMergeBlocks blocks when the level is large enough
     const int64_t wcap = a.wcap;
-    const int blocks = (int)std::min<int64_t>(kMergeBlocks, (wcap + kSelWaves - 1) / kSelWaves);
-    hipLaunchKernelGGL(zha_merge_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(kSelThreads), 0, stream, a,
-                       G, c);
+    int64_t share = (wcap + kMergeBlocks - 1) / kMergeBlocks;
+    share = std::min<int64_t>(kMergeW, (share + kSelWaves - 1) / kSelWaves * kSelWaves);
+    const int64_t blocks = (wcap + share - 1) / share;
+    hipLaunchKernelGGL(zha_route_merge_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(kSelThreads), 0, stream,
+                       a, G, c, (int)share);
     return hipGetLastError();
 }

@@ -42,7 +42,55 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--out", default=None, help="also append the JSON line(s) to this file")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zha_attn_kernel_light_traffic.txt")
+ATTN_SOURCES = [os.path.join(ROOT, "hierarchical_tree_indexed_zha_amd", "csrc", f)
+                for f in ("zha_attn.hip", "zha_common.h", "zha_internal.h")]
+
+
+def attn_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the gather kernel from the committed FETCH_SIZE /
+    WRITE_SIZE counter passes (copy-calibrated), or None when they are missing,
+    were taken on another workload, or the kernel source changed since."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith((" ", "#", "$")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload or kv.get("source_digest") != attn_source_digest():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device-to-device copy of nbytes, reps times: the reference kernel
+    whose FETCH_SIZE / WRITE_SIZE counters calibrate the gather kernel's."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def union_tokens(route1, g, n_tokens, c):
@@ -113,24 +161,38 @@ def bench_workload(args, torch, W, B, ZhaLayer):
     us_dense = t_dense / args.steps * 1e6
     _log(f"[bench] decode-only {us_dec:.1f} us, append-only {us_app} us, dense {us_dense:.1f} us")
 
-    # phase timing with HIP events on the decode stream (same steps, replayed from N)
+    # Phase timing: the timed append+decode steps replayed from N with HIP events
+    # recorded by the library on the decode stream around routing, the gather
+    # kernel and the combine; no host synchronisation inside the replay.
     layer.n_tokens = N
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
     for row in evs:
         for e in row:
-            e.record(stream)
+            e.record(stream)          # creates the underlying HIP events
     torch.cuda.synchronize()
-    gather_bytes = router_bytes = 0
-    keys_read = []
-    route_ms = gather_ms = comb_ms = 0.0
-    R = w.n_ref
     for t in range(args.steps):
         i = t % x["q"].shape[0]
         if w.append:
             layer.append(x["k_app"][i], x["v_app"][i])
         B.zha_decode_step_timed(cfg, layer.bufs, layer.n_tokens, x["q"][i], layer.out,
                                 [e.cuda_event for e in evs[t]])
+    torch.cuda.synchronize()
+    route_ms = sum(r[0].elapsed_time(r[1]) for r in evs)
+    gather_ms = sum(r[1].elapsed_time(r[2]) for r in evs)
+    comb_ms = sum(r[2].elapsed_time(r[3]) for r in evs)
+
+    # Algorithmic bytes of the same steps: replayed once more, reading each step's
+    # kept lists on the host (the selection is deterministic).
+    layer.n_tokens = N
+    gather_bytes = router_bytes = 0
+    keys_read = []
+    R = w.n_ref
+    for t in range(args.steps):
+        i = t % x["q"].shape[0]
+        if w.append:
+            layer.append(x["k_app"][i], x["v_app"][i])
+        layer.decode(x["q"][i])
         torch.cuda.synchronize()
         n = layer.n_tokens
         r1 = layer.route_level(1)
@@ -140,9 +202,7 @@ def bench_workload(args, torch, W, B, ZhaLayer):
         for lv in range(1, w.levels + 1):
             if n // c ** lv:
                 router_bytes += int(layer.route_level(lv)["n_cand"].sum()) * R * (d + 1) * 4
-        route_ms += evs[t][0].elapsed_time(evs[t][1])
-        gather_ms += evs[t][1].elapsed_time(evs[t][2])
-        comb_ms += evs[t][2].elapsed_time(evs[t][3])
+    layer.n_tokens = N
     K = args.steps
     gather_us = gather_ms / K * 1e3
     route_us = route_ms / K * 1e3
@@ -151,6 +211,7 @@ def bench_workload(args, torch, W, B, ZhaLayer):
     dense_bytes = w.n_kv_heads * N * 2 * d * e_kv
     _log(f"[bench] phases: route {route_us:.1f} us ({router_gbs:.0f} GB/s alg), gather {gather_us:.1f} us "
          f"({gather_gbs:.0f} GB/s alg), combine {comb_ms / K * 1e3:.1f} us; keys read {sum(keys_read) / K:.4f}")
+    traffic = read_traffic(w.name)
 
     result = {
         "metric": METRIC,
@@ -179,10 +240,12 @@ def bench_workload(args, torch, W, B, ZhaLayer):
         "router_gbs_alg": round(router_gbs, 1),
         "dense_gbs_alg": round(dense_bytes / (us_dense * 1e-6) / 1e9, 1),
         "build_ms": round(t_build * 1e3, 3),
-        "roofline": {"bound": "hbm", "kernel": "zha_attn_kernel (gather)", "achieved": round(gather_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "bytes_per_launch": int(gather_bytes / K), "avg_launch_us": round(gather_us, 3)},
+        "roofline": {"bound": "hbm", "kernel": "zha_attn_kernel<bf16, sparse> (gather)",
+                     "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "bytes_per_launch": int(gather_bytes / K), "avg_launch_us": round(gather_us, 3),
+                     "traffic_over_alg": None if traffic is None else round(traffic / (gather_bytes / K), 4)},
     }
     return result, layer, x, w
 
@@ -262,6 +325,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 4)
+        return
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from hierarchical_tree_indexed_zha_amd import binding as B
     from hierarchical_tree_indexed_zha_amd import workloads as W

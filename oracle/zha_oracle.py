@@ -215,8 +215,11 @@ def top_p_cut(sigma, node_ids, p: float):
 
     Returns (kept node ids in rank order, pi in candidate order, margin) where
     margin is the distance of this cut from changing under a small
-    perturbation of the probabilities:
-        min(S_K - p,  p - S_{K-1}  (p when K = 1),  pi_(K) - pi_(K+1)  (inf when K = |C|)).
+    perturbation of the scores:
+        min(S_K - p,  p - S_{K-1}  (p when K = 1),  1 - pi_(K+1) / pi_(K)  (inf when K = |C|)).
+    The first two terms are cumulative probability; the last is the relative
+    gap between the last kept and the first dropped candidate (about their
+    score difference), which is what decides their order under score error.
     """
     sigma = np.asarray(sigma, dtype=np.float64)
     node_ids = np.asarray(node_ids, dtype=np.int64)
@@ -234,7 +237,7 @@ def top_p_cut(sigma, node_ids, p: float):
     margin = cum[k - 1] - p
     margin = min(margin, p - (cum[k - 2] if k >= 2 else 0.0))
     if k < n:
-        margin = min(margin, pi[order[k - 1]] - pi[order[k]])
+        margin = min(margin, 1.0 - pi[order[k]] / pi[order[k - 1]])
     return node_ids[order[:k]], pi, float(margin)
 
 

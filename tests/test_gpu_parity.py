@@ -32,6 +32,10 @@ CASES = [
     ("wide@16384", _w("wide", 16384)),                       # c=256, L=1, flat
     ("wide@16500", _w("wide", 16500)),                       # ragged flat
     ("ultra@65536", _w("ultra", 65536, levels=5)),           # light router on topic data
+    # chunk sizes that are not powers of two (parent index and child offset by division)
+    ("light-c6@20001", _w("light", 20001, levels=4, chunk=6)),   # small frontiers only
+    ("deep-c3@9000", _w("deep", 9000, levels=5, chunk=3)),       # R=16, orphans at several levels
+    ("light-c5@50000", _w("light", 50000, levels=4, chunk=5)),   # level 1 takes the large select + merge
 ]
 
 

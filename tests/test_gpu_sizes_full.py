@@ -1,0 +1,49 @@
+"""Parity at the workloads' full sizes, in the configuration bench.py times: the
+whole cache built, one appended token for the append workloads, then one decode
+step through the C ABI.  The oracle computes each checked output on its own
+(summaries node by node, routing and attention per query head); the ultra cache
+(10,485,760 tokens) is checked on one KV group.  Same bars as the small cases."""
+import pytest
+import torch
+
+from hierarchical_tree_indexed_zha_amd import workloads as W
+from tests.gpu_util import compare_decode, compare_tree, make_layer, oracle_tree, say, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _prepare(w):
+    layer, x = make_layer(w)
+    layer.build(w.n_tokens)
+    n = w.n_tokens
+    if w.append:
+        layer.append(x["k_app"][0], x["v_app"][0])
+        n += 1
+    torch.cuda.synchronize()
+    return layer, x, n
+
+
+@pytest.mark.parametrize("name", ["light", "deep", "wide"])
+def test_full_size_decode(name):
+    w = W.get(name)
+    say(f"[full] {name}: N={w.n_tokens} c={w.chunk} L={w.levels} R={w.n_ref}")
+    layer, x, n = _prepare(w)
+    kh, tree = oracle_tree(layer, n)
+    vh = to_host(layer.v)
+    worst_tree = compare_tree(layer, tree, n, sample=48)
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label=f"{name} full")
+    say(f"[full] {name}: tree err {worst_tree:.2e}, exempt heads {ex}/{w.n_q_heads}, "
+        f"attention err {err:.2e}, score err {es:.2e}")
+
+
+def test_full_size_ultra_one_group():
+    w = W.get("ultra")
+    say(f"[full] ultra: N={w.n_tokens} c={w.chunk} L={w.levels}, group 0")
+    layer, x, n = _prepare(w)
+    kh = to_host(layer.k[0:1])
+    vh = to_host(layer.v[0:1])
+    _, tree = oracle_tree(layer, n, keys_host=kh)
+    tree.qref = tree.qref[0:1]
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label="ultra full",
+                                 heads=[0, 5], groups=[0])
+    say(f"[full] ultra: exempt heads {ex}/2, attention err {err:.2e}, score err {es:.2e}")

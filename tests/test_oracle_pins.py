@@ -355,6 +355,21 @@ def test_cut_ties_break_by_ascending_index_and_margin_flags_them():
     assert margin == 0.0          # a tie straddles the cut: either side is correct
 
 
+def test_cut_margin_terms():
+    """The margin is the smallest of the two cumulative distances from p and the
+    relative gap between the last kept and the first dropped probability."""
+    pis = np.array([0.5, 0.25, 0.25 - 5e-5, 5e-5])
+    sigma = np.log(pis)                      # softmax(log pi) = pi (they sum to 1)
+    kept, pi, margin = O.top_p_cut(sigma, np.arange(4), 0.6)
+    assert kept.tolist() == [0, 1]
+    # S_K - p = 0.15, p - S_{K-1} = 0.1, relative tie gap 5e-5 / 0.25 = 2e-4
+    assert abs(margin - 2e-4) < 1e-12
+    kept, pi, margin = O.top_p_cut(sigma, np.arange(4), 0.75 - 5e-5)
+    assert kept.tolist() == [0, 1] and abs(margin - 5e-5) < 1e-12      # S_K - p
+    kept, pi, margin = O.top_p_cut(sigma, np.arange(4), 0.5 + 1e-6)
+    assert kept.tolist() == [0, 1] and abs(margin - 1e-6) < 1e-12      # p - S_{K-1}
+
+
 def test_cut_keeps_at_least_one_and_all_at_p_one():
     sigma = np.array([5.0, -5.0, -6.0])
     assert O.top_p_cut(sigma, np.arange(3), 1e-12)[0].tolist() == [0]

@@ -87,6 +87,8 @@ struct Layout {
     size_t tree_bytes = 0;
     // decode scratch
     std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, stats;
+    std::vector<size_t> hmax, hcut, hdone, hmass, hcnt, tiem, chunk;   // sliced levels only
+    std::vector<int> slices;                               // 0 when the level is not sliced
     std::vector<int64_t> wcap;            // bitmap words per head per level
     size_t pm = 0, pl = 0, po = 0, nact = 0;
     size_t scratch_bytes = 0;
@@ -121,8 +123,10 @@ Layout make_layout(const zha_config* cfg) {
     y.tree_bytes = off;
 
     off = 0;
-    for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.stats})
+    for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.stats, &y.hmax, &y.hcut, &y.hdone, &y.hmass, &y.hcnt,
+                    &y.tiem, &y.chunk})
         v->assign(y.L + 1, 0);
+    y.slices.assign(y.L + 1, 0);
     y.wcap.assign(y.L + 1, 0);
     for (int l = 1; l <= y.L; ++l) {
         const size_t n = (size_t)y.cap[l];
@@ -134,6 +138,19 @@ Layout make_layout(const zha_config* cfg) {
         y.ncand[l] = off; off = align_up(off + sizeof(int32_t) * H);
         y.nkept[l] = off; off = align_up(off + sizeof(int32_t) * H);
         y.stats[l] = off; off = align_up(off + sizeof(int32_t) * 2 * H * G);
+        if (n > (size_t)ZHA_LDS_KEYS) {
+            // levels wider than one workgroup's LDS select over slices of the whole GPU
+            const size_t sl = (n + ZHA_SLICE - 1) / ZHA_SLICE;
+            const size_t nch = ((size_t)y.wcap[l] + 511) / 512;
+            y.slices[l] = (int)sl;
+            y.hmax[l] = off;  off = align_up(off + sizeof(float) * H * G * ZHA_SCORE_MAXB);
+            y.hcut[l] = off;  off = align_up(off + sizeof(HugeCut) * H * G);
+            y.hdone[l] = off; off = align_up(off + sizeof(uint32_t) * 3 * H * G);
+            y.hmass[l] = off; off = align_up(off + sizeof(uint64_t) * 3 * H * G * 2048);
+            y.hcnt[l] = off;  off = align_up(off + sizeof(uint32_t) * 3 * H * G * 2048);
+            y.tiem[l] = off;  off = align_up(off + sizeof(uint64_t) * H * G * sl);
+            y.chunk[l] = off; off = align_up(off + sizeof(uint32_t) * H * nch);
+        }
     }
     attn_partials(cfg, off, y.pm, y.pl, y.po, y.nact);
     y.scratch_bytes = off;
@@ -322,6 +339,25 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.klist = (int32_t*)(X + y.klist[l]);
         a.kmask = (uint32_t*)(X + y.kmask[l]);
         a.nkept = (int32_t*)(X + y.nkept[l]);
+        if (y.slices[l]) {
+            a.hblk = (float*)(X + y.hmax[l]);
+            a.hstate = (HugeCut*)(X + y.hcut[l]);
+            a.hdone = (uint32_t*)(X + y.hdone[l]);
+            a.hmass = (uint64_t*)(X + y.hmass[l]);
+            a.hcnt = (uint32_t*)(X + y.hcnt[l]);
+            a.tiem = (uint64_t*)(X + y.tiem[l]);
+            a.chunk_cnt = (uint32_t*)(X + y.chunk[l]);
+            a.slices = y.slices[l];
+        } else {
+            a.hblk = nullptr;
+            a.hstate = nullptr;
+            a.hdone = nullptr;
+            a.hmass = nullptr;
+            a.hcnt = nullptr;
+            a.tiem = nullptr;
+            a.chunk_cnt = nullptr;
+            a.slices = 0;
+        }
         if (l < top) {
             a.pklist = (const int32_t*)(X + y.klist[l + 1]);
             a.pkmask = (const uint32_t*)(X + y.kmask[l + 1]);
@@ -337,6 +373,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             a.orph_lo = a.orph_hi = 0;
         }
         const int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);
+        a.score_blocks = blocks;
         hipError_t e = zha_launch_route_score(cfg->kv_dtype, q, a, y.H, y.G, c, R, tau, blocks, s);
         if (e != hipSuccess) return hip_fail(e, "route score launch");
         e = zha_launch_route_select(a, y.H, y.G, c, cfg->top_p, s);

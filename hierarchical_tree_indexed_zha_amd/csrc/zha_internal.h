@@ -47,6 +47,17 @@ __device__ __forceinline__ uint32_t zha_div(uint32_t n, const ZhaDiv& v) {
 // are the children of the level above's kept nodes (its kept list, ascending,
 // with the heads that kept each) followed by this level's orphans, nodes
 // [orph_lo, orph_hi) seen by every head.
+// The selection cut of one query head at a sliced level, as far as the digit
+// passes have found it (one per head, written by the last slice of each pass).
+struct HugeCut {
+    uint32_t done;                        // 1 when the cut key is known
+    uint32_t ustar, ties;                 // the cut: largest kept key, keys equal to it
+    uint32_t mshift, mval, bshift, bmask; // the next pass's digit, when not done
+    uint32_t pad;
+    uint64_t need;                        // mass still needed inside the current prefix
+};
+static_assert(sizeof(HugeCut) == 40, "HugeCut layout");
+
 struct ZhaLevelArgs {
     const float* S;            // level planes [H_kv][cap][R][128]
     const float* B;            // [H_kv][cap][R]
@@ -68,7 +79,20 @@ struct ZhaLevelArgs {
     int32_t* klist;            // out: kept nodes [H_kv][cap], ascending
     uint32_t* kmask;           // out: their head masks
     int32_t* nkept;            // out [H_kv]
+    // Levels with more than ZHA_LDS_KEYS node slots select over slices of
+    // ZHA_SLICE positions spread over the whole GPU (null otherwise):
+    float* hblk;               // [H_q][ZHA_SCORE_MAXB] largest score per head in each score block
+    int score_blocks;          // score blocks per group (entries of hblk per head)
+    HugeCut* hstate;           // [H_q] the cut found so far per head
+    uint32_t* hdone;           // [3][H_q] slices done per pass
+    uint64_t* hmass;           // [3][H_q][2048] per-pass digit histograms: fixed-point mass
+    uint32_t* hcnt;            // [3][H_q][2048] and count
+    uint64_t* tiem;            // [H_q][slices] mass of cut-equal keys per slice
+    uint32_t* chunk_cnt;       // [H_kv][wcap / 512] kept nodes per 512-word chunk
+    int slices;                // slices per head
 };
+#define ZHA_LDS_KEYS 32768     // candidates per head selected in one workgroup's LDS
+#define ZHA_SLICE 32768        // positions per slice workgroup of a larger level
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream);
 hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream);

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     }
 
     const int items = (n_cand + U - 1) / U;
+    float hm[4] = {zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf()};   // largest score per head
     for (; it < items; it += stride) {
         const int pos = it * U + cl;
         const bool valid = pos < n_cand;
@@ -175,6 +176,26 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
                 const int h = 4 * kq + i;
                 if (h < G) a.sig[((size_t)g * G + h) * a.cap + (size_t)pos] = ((cm >> h) & 1u) ? best[i] : zha_neg_inf();
             }
+        }
+        if (valid) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if ((cm >> (4 * kq + i)) & 1u) hm[i] = fmaxf(hm[i], best[i]);
+        }
+    }
+    if (a.hblk) {
+        // sliced levels: the largest score of each head over this block
+        __shared__ float s_hm[4][16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = zha_row16_max(hm[i]);
+            if (j == 0) s_hm[wave][4 * kq + i] = x;
+        }
+        __syncthreads();
+        if (threadIdx.x < G) {
+            const int h = threadIdx.x;
+            const float x = fmaxf(fmaxf(s_hm[0][h], s_hm[1][h]), fmaxf(s_hm[2][h], s_hm[3][h]));
+            a.hblk[(size_t)(g * G + h) * ZHA_SCORE_MAXB + blockIdx.x] = x;
         }
     }
 }
@@ -254,7 +275,7 @@ __device__ void wave_find_cross(const uint64_t* hist, uint64_t need, float top_p
     }
 }
 
-constexpr int kLdsKeys = 32768;               // heads with at most this many candidates keep their keys in LDS
+constexpr int kLdsKeys = ZHA_LDS_KEYS;        // heads with at most this many candidates keep their keys in LDS
 constexpr int kSlots = kLdsKeys / kSelThreads;   // positions tid + 1024 k held in registers while staging
 constexpr int kMergeW = kLdsKeys / 64;        // bitmap words merged per step
 constexpr int kBatch = 8;                     // LDS keys read together in a pass
@@ -753,21 +774,37 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
         const int i = tid + t * kSelThreads;
         pv[t] = i < npar_s ? par[pb0 + i] : 0;
     }
+    const bool chunked = a.chunk_cnt != nullptr;   // sliced level: kept counts per 512-word chunk
+    const int nch = (wcap + kMergeW - 1) / kMergeW;
+    uint32_t cc = 0;
+    if (chunked) {
 #pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-        pw[hh] = (hh < G && tid < w0) ? gbm[(size_t)hh * a.wcap + tid] : 0ull;
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) pw[hh] = 0ull;
+        if (tid < w0 / kMergeW) cc = a.chunk_cnt[(size_t)g * nch + tid];
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+            pw[hh] = (hh < G && tid < w0) ? gbm[(size_t)hh * a.wcap + tid] : 0ull;
+    }
 
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (n <= kSmallN) return;                    // selected and merged by the select kernel
+    if (!a.hblk && n <= kSmallN) return;         // selected and merged by the select kernel
     const int nwords = (n + 63) >> 6;
-    if (w0 >= nwords) return;
+    if (w0 >= nwords) {
+        if (blockIdx.x == 0 && nwords == 0 && tid == 0) a.nkept[g] = 0;
+        return;
+    }
     const int w1 = min(wend_s, nwords);
     const int nw = w1 - w0;
     const int pnc = pn * c;
 
     // rank offset: kept nodes in words [0, w0)
     uint32_t cnt = 0;
-    {
+    if (chunked) {
+        cnt = cc;
+#pragma unroll 1
+        for (int i = tid + kSelThreads; i < w0 / kMergeW; i += kSelThreads) cnt += a.chunk_cnt[(size_t)g * nch + i];
+    } else {
         uint64_t u = 0;
 #pragma unroll
         for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= pw[hh];
@@ -865,6 +902,345 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
     if (w1 == nwords && tid == 0) a.nkept[g] = (int32_t)(run + s_tot);
 }
 
+
+// ---- levels with more than kLdsKeys node slots: the candidates of each head are
+// cut into slices of ZHA_SLICE positions, one 256-thread workgroup per (slice,
+// head), so a pass over the keys uses the whole GPU.  Digit histograms are summed
+// per head in global memory with integer atomics (exact and order-free); each
+// pass kernel first replays the crossings of the passes before it from those
+// histograms, so every workgroup reaches the same cut.
+
+constexpr int kHugeThreads = 1024;
+constexpr int kHugeWaves = kHugeThreads / 64;
+constexpr int kHugePer = ZHA_SLICE / kHugeThreads;   // positions per thread
+static_assert(ZHA_SLICE % 64 == 0 && kHugePer * kHugeThreads == ZHA_SLICE, "slice layout");
+static_assert(ZHA_SLICE % (kHugeWaves * 64) == 0, "a slice holds whole words of every wave");
+
+// grid (H_q), 256 threads: clears the level's histograms and counts.
+__global__ __launch_bounds__(kHugeThreads) void zha_huge_init_kernel(ZhaLevelArgs a, int Hq) {
+    const int h = blockIdx.x;
+    for (int i = threadIdx.x; i < 3 * kHistBins; i += kHugeThreads) {
+        const int pass = i / kHistBins, b = i - pass * kHistBins;
+        a.hmass[((size_t)pass * Hq + h) * kHistBins + b] = 0ull;
+        a.hcnt[((size_t)pass * Hq + h) * kHistBins + b] = 0u;
+    }
+    if (threadIdx.x < 3) a.hdone[threadIdx.x * Hq + h] = 0u;
+    if (threadIdx.x == 0) {
+        a.stats[2 * h + 0] = 0;
+        a.stats[2 * h + 1] = 0;
+    }
+}
+
+// The candidate count of the level and the head's largest score (from the score
+// kernel's per-block maxima); called by the whole workgroup.
+struct SliceView {
+    int n, p0;
+    float m;
+};
+__device__ __forceinline__ SliceView slice_view(const ZhaLevelArgs& a, int G, int c, int h, int s, float* red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = h / G;
+    SliceView v;
+    v.p0 = s * ZHA_SLICE;
+    const int pn = a.top ? 0 : a.pnkept[g];
+    float x = tid < a.score_blocks ? a.hblk[(size_t)h * ZHA_SCORE_MAXB + tid] : zha_neg_inf();
+    x = zha_wave_max(x);
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    v.m = red[0];
+#pragma unroll
+    for (int w = 1; w < kHugeWaves; ++w) v.m = fmaxf(v.m, red[w]);
+    v.n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    __syncthreads();
+    return v;
+}
+
+// The slice's keys in registers: position p0 + tid + 256 k in slot k.
+__device__ __forceinline__ void slice_keys(const ZhaLevelArgs& a, int h, const SliceView& v,
+                                           uint32_t (&key)[kHugePer]) {
+    const int tid = threadIdx.x;
+    const float* sg = a.sig + (size_t)h * a.cap;
+    const int lim = min(v.n, v.p0 + ZHA_SLICE);
+    float x[kHugePer];
+#pragma unroll
+    for (int k = 0; k < kHugePer; ++k) {
+        const int pos = v.p0 + tid + k * kHugeThreads;
+        x[k] = pos < lim ? sg[pos] : zha_neg_inf();
+    }
+#pragma unroll
+    for (int k = 0; k < kHugePer; ++k) {
+        const int pos = v.p0 + tid + k * kHugeThreads;
+        key[k] = pos < v.n ? key_of(x[k], v.m) : kNotCand;
+    }
+}
+
+
+// Run by the whole workgroup that finished pass PASS of head h last: read that
+// pass's complete histogram, find the bin where the cumulative mass crosses, and
+// record the head's cut state for the following kernels.
+__device__ void advance_cut(const ZhaLevelArgs& a, int Hq, int h, int pass, float top_p, const HugeCut& prev,
+                            uint64_t* lhist, uint32_t* lcnt, int* s_bin, uint64_t* s_before, uint64_t* s_need) {
+    const int tid = threadIdx.x;
+    const uint64_t* gm = a.hmass + ((size_t)pass * Hq + h) * kHistBins;
+    const uint32_t* gc = a.hcnt + ((size_t)pass * Hq + h) * kHistBins;
+    for (int b = tid; b < kHistBins; b += kHugeThreads) {
+        // the other workgroups' sums, read past this device's caches
+        lhist[hpad((uint32_t)b)] = __hip_atomic_load(gm + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lcnt[b] = __hip_atomic_load(gc + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (tid < 64) wave_find_cross(lhist, pass == 0 ? 0ull : prev.need, top_p, s_bin, s_before, s_need);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t bin = (uint32_t)*s_bin;
+        const uint32_t cnt = lcnt[bin];
+        const uint32_t pref = pass == 0 ? bin : (prev.mval << (pass == 1 ? 11 : 10)) | bin;
+        const uint32_t bshift = pass == 0 ? 21u : pass == 1 ? 10u : 0u;
+        HugeCut nx;
+        nx.need = *s_need - *s_before;
+        nx.pad = 0;
+        if (cnt == 1 || pass == 2) {
+            // the crossing bin holds one key (or the keys equal to the cut): the cut is
+            // the largest key with this prefix
+            nx.done = 1;
+            nx.ustar = (pref << bshift) | ((1u << bshift) - 1u);
+            nx.ties = cnt;
+            nx.mshift = nx.mval = nx.bshift = nx.bmask = 0;
+        } else {
+            nx.done = 0;
+            nx.ustar = nx.ties = 0;
+            nx.mshift = pass == 0 ? 21u : 10u;
+            nx.mval = pref;
+            nx.bshift = pass == 0 ? 10u : 0u;
+            nx.bmask = pass == 0 ? 2047u : 1023u;
+        }
+        a.hstate[h] = nx;
+    }
+}
+
+// grid (slices, H_q): digit histogram of pass PASS over one slice, added into the
+// head's global histogram; the last slice to finish records the head's cut state.
+template <int PASS>
+__global__ __launch_bounds__(kHugeThreads) void zha_huge_pass_kernel(ZhaLevelArgs a, int G, int c, float top_p, int Hq) {
+    __shared__ __align__(16) uint64_t lhist[kHistPadded];
+    __shared__ uint32_t lcnt[kHistBins];
+    __shared__ int s_bin, s_last;
+    __shared__ uint64_t s_before, s_need;
+    __shared__ float red[kHugeWaves];
+    const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+    HugeCut st;
+    if (PASS > 0) st = a.hstate[h];
+    const SliceView v = slice_view(a, G, c, h, s, red);
+    if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
+    if (PASS > 0 && st.done) return;           // an earlier pass already found the cut
+    const uint32_t mshift = PASS > 0 ? st.mshift : 31u, mval = PASS > 0 ? st.mval : 0u;
+    const uint32_t bshift = PASS > 0 ? st.bshift : 21u, bmask = PASS > 0 ? st.bmask : 2047u;
+    uint32_t key[kHugePer];
+    slice_keys(a, h, v, key);
+    for (int i = tid; i < kHistPadded; i += kHugeThreads) lhist[i] = 0ull;
+    for (int i = tid; i < kHistBins; i += kHugeThreads) lcnt[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kHugePer; ++k) {
+        const uint32_t kk = key[k];
+        if (kk < kNoMass && (PASS == 0 || (kk >> mshift) == mval)) {
+            const uint32_t b = (kk >> bshift) & bmask;
+            atomicAdd((unsigned long long*)&lhist[hpad(b)], (unsigned long long)mass_of(kk));
+            atomicAdd(&lcnt[b], 1u);
+        }
+    }
+    __syncthreads();
+    uint64_t* gm = a.hmass + ((size_t)PASS * Hq + h) * kHistBins;
+    uint32_t* gc = a.hcnt + ((size_t)PASS * Hq + h) * kHistBins;
+    for (int b = tid; b < kHistBins; b += kHugeThreads) {
+        const uint32_t cnt = lcnt[b];
+        if (cnt) {
+            atomicAdd((unsigned long long*)&gm[b], (unsigned long long)lhist[hpad((uint32_t)b)]);
+            atomicAdd(&gc[b], cnt);
+        }
+    }
+    // the last of the head's active slices to get here resolves this pass (one fence
+    // per workgroup, by the thread that signals)
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        const int active = (v.n + ZHA_SLICE - 1) / ZHA_SLICE;
+        s_last = atomicAdd(&a.hdone[PASS * Hq + h], 1u) == (uint32_t)(active - 1);
+        if (s_last) __threadfence();
+    }
+    __syncthreads();
+    if (!s_last) return;
+    advance_cut(a, Hq, h, PASS, top_p, st, lhist, lcnt, &s_bin, &s_before, &s_need);
+}
+
+// Block-wide sums over kHugeThreads threads (all threads receive the result).
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t t;
+    wave_excl_scan_u64(v, &t);
+    __syncthreads();
+    if (lane == 0) red[wave] = t;
+    __syncthreads();
+    uint64_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < kHugeWaves; ++w) sum += red[w];
+    return sum;
+}
+
+// grid (slices, H_q), 256 threads: kept flags of one slice into the head's bitmap
+// (words of 64 positions, each written by one lane), candidate and kept counts,
+// and the slice's mass of keys equal to the cut when the cut key is shared.
+__global__ __launch_bounds__(kHugeThreads) void zha_huge_bitmap_kernel(ZhaLevelArgs a, int G, int c, float top_p,
+                                                                      int Hq) {
+    __shared__ uint64_t red[kHugeWaves];
+    __shared__ float redf[kHugeWaves];
+    const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const HugeCut cut = a.hstate[h];
+    const SliceView v = slice_view(a, G, c, h, s, redf);
+    if (v.p0 >= v.n) return;
+    uint32_t key[kHugePer];
+    slice_keys(a, h, v, key);
+    const bool none = v.m == zha_neg_inf();
+    const bool keep_all = !none && top_p >= 1.0f;
+    uint32_t ustar = 0, ties = 0;
+    if (!none && !keep_all) {
+        ustar = cut.ustar;
+        ties = cut.ties;
+    }
+    uint64_t* bm = a.kbm + (size_t)h * a.wcap;
+    const int nwords = (v.n + 63) >> 6;
+    uint32_t my_cand = 0, my_kept = 0;
+    uint64_t my_tie = 0;
+#pragma unroll
+    for (int k = 0; k < kHugePer; ++k) {
+        const uint32_t kk = key[k];
+        const bool cand = kk != kNotCand;
+        const bool kept = !none && (keep_all ? cand : (kk < kNoMass && (kk < ustar || (kk == ustar && ties == 1))));
+        const uint64_t word = __ballot(kept);
+        const int wi = (v.p0 >> 6) + wave + kHugeWaves * k;
+        if (lane == 0 && wi < nwords) bm[wi] = word;
+        my_cand += cand;
+        my_kept += kept;
+        if (ties > 1 && kk == ustar) my_tie += mass_of(kk);
+    }
+    const uint64_t both = block_sum_u64(((uint64_t)my_kept << 32) | my_cand, red);
+    if (tid == 0) {
+        atomicAdd(&a.stats[2 * h + 0], (int32_t)(uint32_t)both);
+        atomicAdd(&a.stats[2 * h + 1], (int32_t)(both >> 32));
+    }
+    if (ties > 1) {
+        const uint64_t t = block_sum_u64(my_tie, red);
+        if (tid == 0) a.tiem[(size_t)h * a.slices + s] = t;
+    }
+}
+
+// grid (slices, H_q): when several keys equal the cut key, take them in ascending
+// position order (slice by slice, then within the slice) until the mass still
+// needed at the cut is reached.  A slice whose equal keys all come before that
+// point takes them all, one that starts after it takes none; only the slice where
+// it falls walks its positions in order.
+__global__ __launch_bounds__(kHugeThreads) void zha_huge_ties_kernel(ZhaLevelArgs a, int G, int c, float top_p,
+                                                                    int Hq) {
+    __shared__ uint64_t red[kHugeWaves];
+    __shared__ float redf[kHugeWaves];
+    __shared__ uint64_t wsum[kHugeWaves][kHugePer];   // equal-key mass per (wave, slot)
+    const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const HugeCut st = a.hstate[h];
+    if (st.ties <= 1u) return;                 // the cut key is unique
+    const SliceView v = slice_view(a, G, c, h, s, redf);
+    if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
+    // equal-key mass of the slices before this one, and of this one
+    uint64_t prev = 0;
+    for (int i = tid; i < s; i += kHugeThreads) prev += a.tiem[(size_t)h * a.slices + i];
+    const uint64_t before_slice = block_sum_u64(prev, red);
+    const uint64_t mine = a.tiem[(size_t)h * a.slices + s];
+    const uint64_t need = st.need;
+    if (before_slice >= need) return;          // the cut was reached in an earlier slice
+    uint32_t key[kHugePer];
+    slice_keys(a, h, v, key);
+    uint64_t* bm = a.kbm + (size_t)h * a.wcap;
+    const int nwords = (v.n + 63) >> 6;
+    uint32_t my_extra = 0;
+    if (before_slice + mine <= need) {
+        // every equal key of this slice precedes the point where the cut is reached
+#pragma unroll
+        for (int k = 0; k < kHugePer; ++k) {
+            const bool take = key[k] == st.ustar;
+            const uint64_t extra = __ballot(take);
+            const int wi = (v.p0 >> 6) + wave + kHugeWaves * k;
+            if (lane == 0 && extra && wi < nwords) atomicOr((unsigned long long*)&bm[wi], (unsigned long long)extra);
+            my_extra += take;
+        }
+    } else {
+        // positions run k-major (slot k covers p0 + 1024 k .. p0 + 1024 k + 1023): the mass
+        // before (slot k, wave w) is every slot < k plus the waves < w of slot k
+#pragma unroll
+        for (int k = 0; k < kHugePer; ++k) {
+            const uint64_t wk = key[k] == st.ustar ? mass_of(key[k]) : 0ull;
+            uint64_t t;
+            wave_excl_scan_u64(wk, &t);
+            if (lane == 0) wsum[wave][k] = t;
+        }
+        __syncthreads();
+        uint64_t run = before_slice;
+#pragma unroll 1
+        for (int k = 0; k < kHugePer; ++k) {
+            uint64_t bw = 0, tot = 0;
+            for (int ww = 0; ww < kHugeWaves; ++ww) {
+                const uint64_t x = wsum[ww][k];
+                bw += ww < wave ? x : 0ull;
+                tot += x;
+            }
+            uint32_t kk = 0;                       // slot k's key, selected without indexing registers
+#pragma unroll
+            for (int q = 0; q < kHugePer; ++q) kk = q == k ? key[q] : kk;
+            const uint64_t wk = kk == st.ustar ? mass_of(kk) : 0ull;
+            uint64_t t;
+            const uint64_t ex = wave_excl_scan_u64(wk, &t);
+            const bool take = wk > 0 && run + bw + ex < need;
+            const uint64_t extra = __ballot(take);
+            const int wi = (v.p0 >> 6) + wave + kHugeWaves * k;
+            if (lane == 0 && extra && wi < nwords) atomicOr((unsigned long long*)&bm[wi], (unsigned long long)extra);
+            my_extra += take;
+            run += tot;
+            if (run >= need) break;                // uniform: every thread holds the same run
+        }
+    }
+    const uint64_t tot = block_sum_u64(my_extra, red);
+    if (tid == 0 && tot) atomicAdd(&a.stats[2 * h + 1], (int32_t)tot);
+}
+
+// grid (chunks, H_kv), 512 threads: kept nodes (union over the group's heads) in
+// each chunk of kMergeW bitmap words, for the merge's rank offsets.
+__global__ __launch_bounds__(kMergeW) void zha_chunk_count_kernel(ZhaLevelArgs a, int G, int c) {
+    __shared__ uint32_t part[kMergeW / 64];
+    const int g = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+    const int nch = (int)((a.wcap + kMergeW - 1) / kMergeW);
+    const int w = ch * kMergeW + tid;
+    uint64_t hv[ZHA_MAX_GROUP];
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        hv[hh] = (hh < G && w < a.wcap) ? a.kbm[((size_t)g * G + hh) * a.wcap + w] : 0ull;
+    const int pn = a.top ? 0 : a.pnkept[g];
+    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    const int nwords = (n + 63) >> 6;
+    uint64_t u = 0;
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= hv[hh];
+    uint32_t cnt = w < nwords ? (uint32_t)__popcll(u) : 0u;
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    if ((tid & 63) == 0) part[tid >> 6] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int i = 0; i < kMergeW / 64; ++i) t += part[i];
+        a.chunk_cnt[(size_t)g * nch + ch] = t;
+    }
+}
+
 }  // namespace
 
 int zha_score_blocks(int64_t max_cand, int R) {
@@ -878,6 +1254,11 @@ int zha_score_blocks(int64_t max_cand, int R) {
 
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream) {
+    if (a.hblk) {
+        hipLaunchKernelGGL(zha_huge_init_kernel, dim3((unsigned)(H_kv * G)), dim3(kHugeThreads), 0, stream, a, H_kv * G);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     dim3 grid((unsigned)blocks, (unsigned)H_kv);
     if (kv_dtype == 0)
         hipLaunchKernelGGL(zha_route_score_kernel<true>, grid, dim3(kScoreThreads), 0, stream, q, a, G, c, R, tau);
@@ -890,6 +1271,22 @@ hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c
     if (a.cap <= kSmallN) {
         hipLaunchKernelGGL(zha_select_small_kernel, dim3((unsigned)H_kv), dim3(kSelThreads), 0, stream, a, G, c,
                            top_p);
+        return hipGetLastError();
+    }
+    if (a.hblk) {
+        // sliced level: three digit passes, the bitmap, the ordered ties, chunk counts, merge
+        const int Hq = H_kv * G;
+        const dim3 sg((unsigned)a.slices, (unsigned)Hq);
+        hipLaunchKernelGGL(zha_huge_pass_kernel<0>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
+        hipLaunchKernelGGL(zha_huge_pass_kernel<1>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
+        hipLaunchKernelGGL(zha_huge_pass_kernel<2>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
+        hipLaunchKernelGGL(zha_huge_bitmap_kernel, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
+        hipLaunchKernelGGL(zha_huge_ties_kernel, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
+        const int64_t nch = (a.wcap + kMergeW - 1) / kMergeW;
+        hipLaunchKernelGGL(zha_chunk_count_kernel, dim3((unsigned)nch, (unsigned)H_kv), dim3(kMergeW), 0, stream, a,
+                           G, c);
+        hipLaunchKernelGGL(zha_route_merge_kernel, dim3((unsigned)nch, (unsigned)H_kv), dim3(kSelThreads), 0, stream,
+                           a, G, c, kMergeW);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(zha_select_large_kernel, dim3((unsigned)(H_kv * G)), dim3(kSelThreads), 0, stream, a, G,

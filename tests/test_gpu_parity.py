@@ -36,6 +36,7 @@ CASES = [
     ("light-c6@20001", _w("light", 20001, levels=4, chunk=6)),   # small frontiers only
     ("deep-c3@9000", _w("deep", 9000, levels=5, chunk=3)),       # R=16, orphans at several levels
     ("light-c5@50000", _w("light", 50000, levels=4, chunk=5)),   # level 1 takes the large select + merge
+    ("light@600000", _w("light", 600000, levels=4)),             # level 1 (75,000 slots) selects over slices
 ]
 
 
@@ -203,3 +204,34 @@ def test_abi_rejects_bad_arguments_on_device():
     with pytest.raises(B.ZhaError) as e:
         B.zha_append_token(layer.cfg, layer.bufs, w.capacity, x["k"][:, 0], x["v"][:, 0])
     assert e.value.code == B.ZHA_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("p", [0.95, 0.999])
+def test_equal_scores_take_lowest_positions(p):
+    """Every key equal: every node of a level has the same score, so each cut is one
+    large tie resolved by ascending node index.  Levels of 136 and 546 slots take the
+    one-workgroup path, 2,187 and 8,750 the per-head path, 35,000 the sliced path; at
+    p = 0.999 its frontier (34,936) spans two slices, the cut falling in the second."""
+    w = _w("deep", 140000, levels=5, steps=2, top_p=p)
+    say(f"[ties] deep@140000, all keys equal, p={p}")
+    layer, x = make_layer(w)
+    layer.k[:, :w.n_tokens] = layer.k[:, :1].clone()
+    layer.build(w.n_tokens)
+    kh, tree = oracle_tree(layer, w.n_tokens)
+    out = layer.decode(x["q"][0]).clone()
+    torch.cuda.synchronize()
+    qh = to_host(x["q"][0])
+    G = w.group
+    for h in range(w.n_q_heads):
+        r = O.route_head(qh[h], tree, h // G, w.top_p)
+        for lv in r.levels:
+            route = layer.route_level(lv.level)
+            g = h // G
+            nk = int(route["n_kept"][g])
+            nodes = route["kept"][g, :nk].numpy()
+            masks = route["mask"][g, :nk].numpy()
+            got = nodes[(masks >> (h % G)) & 1 == 1].tolist()
+            assert got == lv.kept.tolist(), f"head {h} level {lv.level}: {len(got)} kept vs {len(lv.kept)}"
+        toks = O.final_token_set(r.kept_leaves(), w.n_tokens, w.chunk)
+        ref = O.attend(qh[h], kh[h // G], to_host(layer.v)[h // G], toks, tree.tau)
+        assert float(np.abs(out[h].cpu().numpy() - ref).max()) <= ATOL

@@ -138,8 +138,8 @@ Layout make_layout(const zha_config* cfg) {
         y.ncand[l] = off; off = align_up(off + sizeof(int32_t) * H);
         y.nkept[l] = off; off = align_up(off + sizeof(int32_t) * H);
         y.stats[l] = off; off = align_up(off + sizeof(int32_t) * 2 * H * G);
-        if (n > (size_t)ZHA_LDS_KEYS) {
-            // levels wider than one workgroup's LDS select over slices of the whole GPU
+        if (n > (size_t)ZHA_SLICED_MIN_CAP) {
+            // the widest levels select over slices of the whole GPU
             const size_t sl = (n + ZHA_SLICE - 1) / ZHA_SLICE;
             const size_t nch = ((size_t)y.wcap[l] + 511) / 512;
             y.slices[l] = (int)sl;
@@ -163,11 +163,16 @@ Layout make_layout(const zha_config* cfg) {
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
-int attn_blocks(int64_t n_slots) {
+// Attention workgroups per KV group: about 8 tiles of 32 slots each, at most one
+// resident round of the whole device (768 workgroups: 256 CUs x 3 resident) so
+// that no partial second round trails the launch.
+int attn_blocks(int64_t n_slots, int H) {
     const int64_t tiles = (n_slots + 31) / 32;
     int64_t b = (tiles + 7) / 8;
     if (b < 1) b = 1;
     if (b > ZHA_ATTN_MAXB) b = ZHA_ATTN_MAXB;
+    const int64_t round = 768 / H;
+    if (b > round) b = round > 0 ? round : 1;
     return (int)b;
 }
 
@@ -394,7 +399,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     at_.pl = (float*)(X + y.pl);
     at_.po = (float*)(X + y.po);
     at_.nact = (int32_t*)(X + y.nact);
-    const int Bg = attn_blocks(n_tokens + 1);
+    const int Bg = attn_blocks(n_tokens + 1, y.H);
     if ((rc = record(events, 1, s))) return rc;
     hipError_t e = zha_launch_attention(cfg->kv_dtype, false, at_, y.H, y.G, c, tau, Bg, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -445,7 +450,7 @@ int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_
     a.pl = (float*)(X + pl);
     a.po = (float*)(X + po);
     a.nact = (int32_t*)(X + nact);
-    const int Bg = attn_blocks(n_tokens);
+    const int Bg = attn_blocks(n_tokens, H);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = zha_launch_attention(cfg->kv_dtype, true, a, H, G, cfg->chunk, tau_of(cfg), Bg, s);
     if (e != hipSuccess) return hip_fail(e, "dense attention launch");

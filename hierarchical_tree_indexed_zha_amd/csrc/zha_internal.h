@@ -79,7 +79,7 @@ struct ZhaLevelArgs {
     int32_t* klist;            // out: kept nodes [H_kv][cap], ascending
     uint32_t* kmask;           // out: their head masks
     int32_t* nkept;            // out [H_kv]
-    // Levels with more than ZHA_LDS_KEYS node slots select over slices of
+    // Levels with more than ZHA_SLICED_MIN_CAP node slots select over slices of
     // ZHA_SLICE positions spread over the whole GPU (null otherwise):
     float* hblk;               // [H_q][ZHA_SCORE_MAXB] largest score per head in each score block
     int score_blocks;          // score blocks per group (entries of hblk per head)
@@ -92,7 +92,8 @@ struct ZhaLevelArgs {
     int slices;                // slices per head
 };
 #define ZHA_LDS_KEYS 32768     // candidates per head selected in one workgroup's LDS
-#define ZHA_SLICE 32768        // positions per slice workgroup of a larger level
+#define ZHA_SLICE 32768        // positions per slice workgroup of a sliced level
+#define ZHA_SLICED_MIN_CAP 262144   // levels with more node slots select over slices
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream);
 hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream);

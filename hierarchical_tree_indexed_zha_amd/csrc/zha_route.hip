@@ -279,6 +279,7 @@ constexpr int kLdsKeys = ZHA_LDS_KEYS;        // heads with at most this many ca
 constexpr int kSlots = kLdsKeys / kSelThreads;   // positions tid + 1024 k held in registers while staging
 constexpr int kMergeW = kLdsKeys / 64;        // bitmap words merged per step
 constexpr int kBatch = 8;                     // LDS keys read together in a pass
+constexpr int kGlobBatch = 16;                // scores re-read together from global memory
 constexpr int kMergeBlocks = 32;              // merge workgroups per group
 static_assert((kSlots & (kSlots - 1)) == 0 && kSlots % kBatch == 0, "slot batches");
 constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup
@@ -573,7 +574,19 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
             }
         }
     } else {
-        for (int pos = tid; pos < n; pos += kSelThreads) m = fmaxf(m, sg[pos]);
+        // frontiers beyond the LDS keys: the scores are re-read (from L2) kGlobBatch
+        // positions per thread at a time, all reads of a batch in flight together
+#pragma unroll 1
+        for (int k0 = 0; k0 < nslot; k0 += kGlobBatch) {
+            float xs[kGlobBatch];
+#pragma unroll
+            for (int j = 0; j < kGlobBatch; ++j) {
+                const int pos = tid + (k0 + j) * kSelThreads;
+                xs[j] = pos < n ? sg[pos] : zha_neg_inf();
+            }
+#pragma unroll
+            for (int j = 0; j < kGlobBatch; ++j) m = fmaxf(m, xs[j]);
+        }
     }
     m = zha_wave_max(m);
     if (lane == 0) swf[wave] = m;
@@ -620,13 +633,22 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
                     }
                 }
             } else {
-#pragma unroll 4
-                for (int pos = tid; pos < n; pos += kSelThreads) {
-                    const uint32_t key = key_of(sg[pos], m);
-                    if (key < kNoMass && (all || (key >> mshift) == mval)) {
-                        const uint32_t b = (key >> bshift) & bmask;
-                        atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
-                        atomicAdd(&cntb[b], 1u);
+#pragma unroll 1
+                for (int k0 = 0; k0 < nslot; k0 += kGlobBatch) {
+                    float xs[kGlobBatch];
+#pragma unroll
+                    for (int j = 0; j < kGlobBatch; ++j) {
+                        const int pos = tid + (k0 + j) * kSelThreads;
+                        xs[j] = pos < n ? sg[pos] : zha_neg_inf();
+                    }
+#pragma unroll
+                    for (int j = 0; j < kGlobBatch; ++j) {
+                        const uint32_t key = key_of(xs[j], m);
+                        if (key < kNoMass && (all || (key >> mshift) == mval)) {
+                            const uint32_t b = (key >> bshift) & bmask;
+                            atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
+                            atomicAdd(&cntb[b], 1u);
+                        }
                     }
                 }
             }
@@ -673,16 +695,27 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         }
     } else {
 #pragma unroll 1
-        for (int k = 0; k < nslot; ++k) {
-            const int pos = tid + k * kSelThreads;
-            const uint32_t key = pos < n ? key_of(sg[pos], m) : kNotCand;
-            const bool cand = key != kNotCand;
-            const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
-            const uint64_t word = __ballot(kept);
-            const int wi = k * kSelWaves + wave;
-            if (lane == 0 && wi < nwords) bm[wi] = word;
-            my_cand += cand;
-            my_kept += kept;
+        for (int k0 = 0; k0 < nslot; k0 += kGlobBatch) {
+            float xs[kGlobBatch];
+#pragma unroll
+            for (int j = 0; j < kGlobBatch; ++j) {
+                const int pos = tid + (k0 + j) * kSelThreads;
+                xs[j] = pos < n ? sg[pos] : zha_neg_inf();
+            }
+#pragma unroll
+            for (int j = 0; j < kGlobBatch; ++j) {
+                const int k = k0 + j;
+                if (k < nslot) {
+                    const uint32_t key = key_of(xs[j], m);
+                    const bool cand = key != kNotCand;
+                    const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
+                    const uint64_t word = __ballot(kept);
+                    const int wi = k * kSelWaves + wave;
+                    if (lane == 0 && wi < nwords) bm[wi] = word;
+                    my_cand += cand;
+                    my_kept += kept;
+                }
+            }
         }
     }
     if (!none && !keep_all && ties > 1) {

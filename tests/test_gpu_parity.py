@@ -206,14 +206,17 @@ def test_abi_rejects_bad_arguments_on_device():
     assert e.value.code == B.ZHA_ERR_CAPACITY
 
 
-@pytest.mark.parametrize("p", [0.95, 0.999])
-def test_equal_scores_take_lowest_positions(p):
+@pytest.mark.parametrize("gen,n,p", [("deep", 140000, 0.95), ("deep", 140000, 0.999), ("light", 1100000, 0.999)],
+                         ids=["140k-p0.95", "140k-p0.999", "1.1M-p0.999"])
+def test_equal_scores_take_lowest_positions(gen, n, p):
     """Every key equal: every node of a level has the same score, so each cut is one
-    large tie resolved by ascending node index.  Levels of 136 and 546 slots take the
-    one-workgroup path, 2,187 and 8,750 the per-head path, 35,000 the sliced path; at
-    p = 0.999 its frontier (34,936) spans two slices, the cut falling in the second."""
-    w = _w("deep", 140000, levels=5, steps=2, top_p=p)
-    say(f"[ties] deep@140000, all keys equal, p={p}")
+    large tie resolved by ascending node index.  At 140,000 tokens (chunk 4) levels of
+    136 and 546 slots take the one-workgroup path, 2,187, 8,750 and 35,000 the per-head
+    path (at p = 0.999 the 34,936-candidate frontier exceeds the LDS keys and is re-read
+    from memory); at 1,100,000 tokens level 1 (275,000 slots) selects over slices and
+    the tie spans nine of them."""
+    w = _w(gen, n, levels=5, steps=2, top_p=p, chunk=4)
+    say(f"[ties] {gen}@{n}, all keys equal, p={p}")
     layer, x = make_layer(w)
     layer.k[:, :w.n_tokens] = layer.k[:, :1].clone()
     layer.build(w.n_tokens)

@@ -162,8 +162,9 @@ def bench_workload(args, torch, W, B, ZhaLayer):
     _log(f"[bench] decode-only {us_dec:.1f} us, append-only {us_app} us, dense {us_dense:.1f} us")
 
     # Phase timing: the timed append+decode steps replayed from N with HIP events
-    # recorded by the library on the decode stream around routing, the gather
-    # kernel and the combine; no host synchronisation inside the replay.
+    # on the decode stream: before routing, at the start and end of the gather
+    # kernel (recorded by its dispatch) and after the combine; no host
+    # synchronisation inside the replay.
     layer.n_tokens = N
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     stream = torch.cuda.current_stream()

@@ -400,10 +400,11 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     at_.po = (float*)(X + y.po);
     at_.nact = (int32_t*)(X + y.nact);
     const int Bg = attn_blocks(n_tokens + 1, y.H);
-    if ((rc = record(events, 1, s))) return rc;
-    hipError_t e = zha_launch_attention(cfg->kv_dtype, false, at_, y.H, y.G, c, tau, Bg, s);
+    // events 1 and 2 bracket the gather kernel's own execution
+    hipError_t e = zha_launch_attention(cfg->kv_dtype, false, at_, y.H, y.G, c, tau, Bg, s,
+                                        events ? static_cast<hipEvent_t>(events[1]) : nullptr,
+                                        events ? static_cast<hipEvent_t>(events[2]) : nullptr);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
-    if ((rc = record(events, 2, s))) return rc;
     e = zha_launch_combine(at_, y.H, y.G, Bg, out, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     if ((rc = record(events, 3, s))) return rc;

@@ -22,6 +22,8 @@
 // permuted so that each lane's eight B-operand values come from eight such
 // loads.  P is split into bf16 hi + lo parts (two MFMAs), so the PV product
 // keeps 16 significant bits of P.  fp32 path: the same tiling on v_mfma_f32_16x16x4_f32.
+#include <hip/hip_ext.h>
+
 #include "zha_common.h"
 #include "zha_internal.h"
 
@@ -376,18 +378,24 @@ __global__ __launch_bounds__(kCombThreads) void zha_combine_kernel(ZhaAttnArgs a
 }  // namespace
 
 hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, int H_kv, int G, int c, float tau,
-                                int Bg, hipStream_t stream) {
-    dim3 grid((unsigned)Bg, (unsigned)H_kv);
+                                int Bg, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    const dim3 grid((unsigned)Bg, (unsigned)H_kv);
+    // start / stop (may be null) are recorded by the dispatch itself: they time
+    // the kernel alone
     if (kv_dtype == 0) {
         if (dense)
-            hipLaunchKernelGGL((zha_attn_kernel<true, true>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+            hipExtLaunchKernelGGL((zha_attn_kernel<true, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, a, G,
+                                  c, tau, Bg);
         else
-            hipLaunchKernelGGL((zha_attn_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+            hipExtLaunchKernelGGL((zha_attn_kernel<true, false>), grid, dim3(kThreads), 0, stream, start, stop, 0, a,
+                                  G, c, tau, Bg);
     } else {
         if (dense)
-            hipLaunchKernelGGL((zha_attn_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+            hipExtLaunchKernelGGL((zha_attn_kernel<false, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, a,
+                                  G, c, tau, Bg);
         else
-            hipLaunchKernelGGL((zha_attn_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, G, c, tau, Bg);
+            hipExtLaunchKernelGGL((zha_attn_kernel<false, false>), grid, dim3(kThreads), 0, stream, start, stop, 0, a,
+                                  G, c, tau, Bg);
     }
     return hipGetLastError();
 }

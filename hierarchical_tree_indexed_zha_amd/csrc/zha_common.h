@@ -36,6 +36,17 @@ __device__ __forceinline__ void zha_wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Wait until this wave's global stores and atomics have completed.  A
+// workgroup barrier does not wait for them, so before one thread of a workgroup
+// publishes the workgroup's results to other workgroups (release fence, then a
+// counter atomic) every wave calls this first.  s_waitcnt immediate for gfx9:
+// vmcnt(0), expcnt and lgkmcnt left at their no-wait maxima.
+__device__ __forceinline__ void zha_wave_mem_wait() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <typename T>
 __device__ __forceinline__ T zha_shfl_xor(T v, int mask, int width = 64) {
     return __shfl_xor(v, mask, width);

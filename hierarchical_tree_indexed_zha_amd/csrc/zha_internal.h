@@ -116,5 +116,6 @@ struct ZhaAttnArgs {
     int32_t* nact;             // [H_kv]
 };
 hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, int H_kv, int G, int c,
-                                float tau, int Bg, hipStream_t stream);
+                                float tau, int Bg, hipStream_t stream, hipEvent_t start = nullptr,
+                                hipEvent_t stop = nullptr);
 hipError_t zha_launch_combine(const ZhaAttnArgs& a, int H_kv, int G, int Bg, float* out, hipStream_t stream);

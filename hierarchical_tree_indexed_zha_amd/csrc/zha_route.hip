@@ -1092,8 +1092,9 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_pass_kernel(ZhaLevelArg
             atomicAdd(&gc[b], cnt);
         }
     }
-    // the last of the head's active slices to get here resolves this pass (one fence
-    // per workgroup, by the thread that signals)
+    // the last of the head's active slices to get here resolves this pass: every
+    // wave's histogram atomics complete, then one release fence and the counter
+    zha_wave_mem_wait();
     __syncthreads();
     if (tid == 0) {
         __threadfence();

@@ -153,11 +153,12 @@ int zha_decode_step(const zha_config* cfg, const zha_buffers* bufs, int64_t n_to
                     const void* q, float* out, void* stream);
 
 /* zha_decode_step, plus HIP events recorded on `stream` around its phases:
- * events[0] before the first routing kernel, events[1] after the last routing
- * kernel (before the gather-attention kernel), events[2] after the gather-
- * attention kernel, events[3] after the combine kernel.  `events` may be NULL
- * and any entry may be NULL (hipEvent_t values created by the caller).  Used to
- * time the phases of a step separately. */
+ * events[0] before the first routing kernel; events[1] and events[2] at the
+ * start and the end of the gather-attention kernel itself (recorded by its
+ * dispatch, so events[1] -> events[2] is that kernel's execution time);
+ * events[3] after the combine kernel.  `events` may be NULL and any entry may be
+ * NULL (hipEvent_t values created by the caller).  Used to time the phases of a
+ * step separately. */
 int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens,
                           const void* q, float* out, void* const* events, void* stream);
 

@@ -166,12 +166,13 @@ char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 // Attention workgroups per KV group: about 8 tiles of 32 slots each, at most one
 // resident round of the whole device (768 workgroups: 256 CUs x 3 resident) so
 // that no partial second round trails the launch.
-int attn_blocks(int64_t n_slots, int H) {
+int attn_blocks(int64_t n_slots, int H, int kv_dtype) {
     const int64_t tiles = (n_slots + 31) / 32;
     int64_t b = (tiles + 7) / 8;
     if (b < 1) b = 1;
     if (b > ZHA_ATTN_MAXB) b = ZHA_ATTN_MAXB;
-    const int64_t round = 768 / H;
+    // one resident round on 256 compute units
+    const int64_t round = 256 * (kv_dtype == ZHA_BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BLOCKS_F32) / H;
     if (b > round) b = round > 0 ? round : 1;
     return (int)b;
 }
@@ -399,7 +400,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     at_.pl = (float*)(X + y.pl);
     at_.po = (float*)(X + y.po);
     at_.nact = (int32_t*)(X + y.nact);
-    const int Bg = attn_blocks(n_tokens + 1, y.H);
+    const int Bg = attn_blocks(n_tokens + 1, y.H, cfg->kv_dtype);
     // events 1 and 2 bracket the gather kernel's own execution
     hipError_t e = zha_launch_attention(cfg->kv_dtype, false, at_, y.H, y.G, c, tau, Bg, s,
                                         events ? static_cast<hipEvent_t>(events[1]) : nullptr,
@@ -451,7 +452,7 @@ int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_
     a.pl = (float*)(X + pl);
     a.po = (float*)(X + po);
     a.nact = (int32_t*)(X + nact);
-    const int Bg = attn_blocks(n_tokens, H);
+    const int Bg = attn_blocks(n_tokens, H, cfg->kv_dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = zha_launch_attention(cfg->kv_dtype, true, a, H, G, cfg->chunk, tau_of(cfg), Bg, s);
     if (e != hipSuccess) return hip_fail(e, "dense attention launch");

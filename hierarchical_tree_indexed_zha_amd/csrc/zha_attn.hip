@@ -107,9 +107,88 @@ __device__ __forceinline__ int active_blocks(int64_t tiles, int Bg) {
     return (int)n;
 }
 
+// The K and V rows of one 32-slot tile (bf16), token ids in LDS: K as the B
+// operand of QK^T (lane j, q4: slot 16 bb + j, columns 32 s + 8 q4), V in row
+// order (lane j, q4: slot 4 i + q4, columns 8 j .. 8 j + 7).
+__device__ __forceinline__ void load_kv_bf16(const uint16_t* K, const uint16_t* V, size_t head_row0,
+                                             const int32_t* tok, int j, int q4, uint4 (&kr)[2][4],
+                                             uint4 (&vr)[8]) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const uint16_t* row = K + (head_row0 + (size_t)tok[16 * bb + j]) * ZHA_D + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kr[bb][s] = *reinterpret_cast<const uint4*>(row + 32 * s);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        vr[i] = *reinterpret_cast<const uint4*>(V + (head_row0 + (size_t)tok[4 * i + q4]) * ZHA_D + 8 * j);
+}
+
+// Masked, scaled logits of one tile folded into the running softmax of the
+// lane's heads 4 q4 + i; the tile's probabilities go to s_p [16 heads][33].
+__device__ __forceinline__ void softmax_tile(const zha_f32x4 (&S)[2], uint32_t mk0, uint32_t mk1, float scale,
+                                             int j, int q4, float (&m_run)[4], float (&l_run)[4],
+                                             zha_f32x4 (&O)[8], float* s_p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * q4 + i;
+        const float x0 = ((mk0 >> h) & 1u) ? S[0][i] * scale : zha_neg_inf();
+        const float x1 = ((mk1 >> h) & 1u) ? S[1][i] * scale : zha_neg_inf();
+        const float mx = zha_row16_max(fmaxf(x0, x1));
+        const float mn = fmaxf(m_run[i], mx);
+        float alpha, p0, p1;
+        if (mn == zha_neg_inf()) {
+            alpha = 1.f; p0 = 0.f; p1 = 0.f;
+        } else {
+            alpha = exp2f(m_run[i] - mn);
+            p0 = exp2f(x0 - mn);
+            p1 = exp2f(x1 - mn);
+        }
+        const float rs = zha_row16_sum(p0 + p1);
+        l_run[i] = l_run[i] * alpha + rs;
+        m_run[i] = mn;
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) O[c8][i] *= alpha;
+        s_p[h * 33 + j] = p0;
+        s_p[h * 33 + 16 + j] = p1;
+    }
+}
+
+// O += P V for one bf16 tile: P (from s_p) as bf16 hi + lo parts, V rows vr.
+__device__ __forceinline__ void pv_tile_bf16(const float* s_p, const uint4 (&vr)[8], int j, int q4,
+                                             zha_f32x4 (&O)[8]) {
+    // A operand: row head j, contraction slots 4e + q4, e = 0..7, as bf16 hi + lo
+    // parts: hi = P truncated to bf16, lo = the residual truncated to bf16, so
+    // hi + lo keeps 16 significant bits of P.
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        const float pa = s_p[j * 33 + 4 * (2 * e2) + q4];
+        const float pb = s_p[j * 33 + 4 * (2 * e2 + 1) + q4];
+        const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb);
+        hi[e2] = perm(ub, ua, kHighHalves);
+        const float ra = pa - __uint_as_float(ua & 0xFFFF0000u);
+        const float rb = pb - __uint_as_float(ub & 0xFFFF0000u);
+        lo[e2] = perm(__float_as_uint(rb), __float_as_uint(ra), kHighHalves);
+    }
+    const zha_bf16x8 Ahi = zha_as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    const zha_bf16x8 Alo = zha_as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) {
+        const int w = c8 >> 1;
+        const uint32_t sel = (c8 & 1) ? kHighHalves : kLowHalves;
+        uint32_t bw[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) bw[e2] = perm(comp(vr[2 * e2 + 1], w), comp(vr[2 * e2], w), sel);
+        const zha_bf16x8 Bv = zha_as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bv, O[c8], 0, 0, 0);
+        O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bv, O[c8], 0, 0, 0);
+    }
+}
+
 // grid (Bg, H_kv), 256 threads.
 template <bool BF16, bool DENSE>
-__global__ __launch_bounds__(kThreads, 3) void zha_attn_kernel(ZhaAttnArgs a, int G, int c, float tau, int Bg) {
+__global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BLOCKS_F32) void zha_attn_kernel(ZhaAttnArgs a, int G, int c, float tau, int Bg) {
     __shared__ int32_t s_tok[kWaves][kTileSlots];
     __shared__ uint32_t s_msk[kWaves][kTileSlots];
     __shared__ float s_buf[kWaves * 16 * ZHA_D];          // P tiles during the loop, partial O after it
@@ -172,21 +251,10 @@ __global__ __launch_bounds__(kThreads, 3) void zha_attn_kernel(ZhaAttnArgs a, in
         zha_wave_lds_sync();
 
         zha_f32x4 S[2];
-        uint4 vr[8];
-        float4 vf[8][2];
-        if (BF16) {
-            const uint16_t* K = static_cast<const uint16_t*>(a.K);
-            const uint16_t* V = static_cast<const uint16_t*>(a.V);
-            uint4 kr[2][4];
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const uint16_t* row = K + (head_row0 + (size_t)s_tok[wave][16 * bb + j]) * ZHA_D + 8 * q4;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) kr[bb][s] = *reinterpret_cast<const uint4*>(row + 32 * s);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                vr[i] = *reinterpret_cast<const uint4*>(V + (head_row0 + (size_t)s_tok[wave][4 * i + q4]) * ZHA_D + 8 * j);
+        if constexpr (BF16) {
+            uint4 kr[2][4], vr[8];
+            load_kv_bf16(static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.V), head_row0,
+                         s_tok[wave], j, q4, kr, vr);
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 zha_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -195,6 +263,10 @@ __global__ __launch_bounds__(kThreads, 3) void zha_attn_kernel(ZhaAttnArgs a, in
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zha_as_bf16x8(qa16[s]), zha_as_bf16x8(kr[bb][s]), acc, 0, 0, 0);
                 S[bb] = acc;
             }
+            // S[bb][i]: head 4*q4+i against slot 16*bb+j.  Mask, scale, online softmax.
+            softmax_tile(S, s_msk[wave][j], s_msk[wave][16 + j], scale, j, q4, m_run, l_run, O, s_p);
+            zha_wave_lds_sync();
+            pv_tile_bf16(s_p, vr, j, q4, O);
         } else {
             const float* K = static_cast<const float*>(a.K);
             const float* V = static_cast<const float*>(a.V);
@@ -212,70 +284,15 @@ __global__ __launch_bounds__(kThreads, 3) void zha_attn_kernel(ZhaAttnArgs a, in
                 }
                 S[bb] = acc;
             }
+            float4 vf[8][2];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float4* row = reinterpret_cast<const float4*>(V + (head_row0 + (size_t)s_tok[wave][4 * i + q4]) * ZHA_D + 8 * j);
                 vf[i][0] = row[0];
                 vf[i][1] = row[1];
             }
-        }
-
-        // S[bb][i]: head 4*q4+i against slot 16*bb+j.  Mask, scale, online softmax.
-        const uint32_t mk0 = s_msk[wave][j], mk1 = s_msk[wave][16 + j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * q4 + i;
-            const float x0 = ((mk0 >> h) & 1u) ? S[0][i] * scale : zha_neg_inf();
-            const float x1 = ((mk1 >> h) & 1u) ? S[1][i] * scale : zha_neg_inf();
-            const float mx = zha_row16_max(fmaxf(x0, x1));
-            const float mn = fmaxf(m_run[i], mx);
-            float alpha, p0, p1;
-            if (mn == zha_neg_inf()) {
-                alpha = 1.f; p0 = 0.f; p1 = 0.f;
-            } else {
-                alpha = exp2f(m_run[i] - mn);
-                p0 = exp2f(x0 - mn);
-                p1 = exp2f(x1 - mn);
-            }
-            const float rs = zha_row16_sum(p0 + p1);
-            l_run[i] = l_run[i] * alpha + rs;
-            m_run[i] = mn;
-#pragma unroll
-            for (int c8 = 0; c8 < 8; ++c8) O[c8][i] *= alpha;
-            s_p[h * 33 + j] = p0;
-            s_p[h * 33 + 16 + j] = p1;
-        }
-        zha_wave_lds_sync();
-
-        if (BF16) {
-            // A operand: row head j, contraction slots 4e + q4, e = 0..7, as bf16 hi + lo
-            // parts: hi = P truncated to bf16, lo = the residual truncated to bf16, so
-            // hi + lo keeps 16 significant bits of P.
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const float pa = s_p[j * 33 + 4 * (2 * e2) + q4];
-                const float pb = s_p[j * 33 + 4 * (2 * e2 + 1) + q4];
-                const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb);
-                hi[e2] = perm(ub, ua, kHighHalves);
-                const float ra = pa - __uint_as_float(ua & 0xFFFF0000u);
-                const float rb = pb - __uint_as_float(ub & 0xFFFF0000u);
-                lo[e2] = perm(__float_as_uint(rb), __float_as_uint(ra), kHighHalves);
-            }
-            const zha_bf16x8 Ahi = zha_as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            const zha_bf16x8 Alo = zha_as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-#pragma unroll
-            for (int c8 = 0; c8 < 8; ++c8) {
-                const int w = c8 >> 1;
-                const uint32_t sel = (c8 & 1) ? kHighHalves : kLowHalves;
-                uint32_t bw[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) bw[e2] = perm(comp(vr[2 * e2 + 1], w), comp(vr[2 * e2], w), sel);
-                const zha_bf16x8 Bv = zha_as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
-                O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bv, O[c8], 0, 0, 0);
-                O[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bv, O[c8], 0, 0, 0);
-            }
-        } else {
+            softmax_tile(S, s_msk[wave][j], s_msk[wave][16 + j], scale, j, q4, m_run, l_run, O, s_p);
+            zha_wave_lds_sync();
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float pa = s_p[j * 33 + 4 * i + q4];

@@ -123,6 +123,18 @@ def check_routing(layer: ZhaLayer, qh, n_tokens: int, tree: O.SummaryTree, p: fl
                     assert inkept.all(), f"{label} level {lv} head {h}: p=1 must keep all"
                     continue
                 assert len(kept) >= 1
+                # The GPU's own order, exactly: keys formed from its fp32 scores as the
+                # kernels form them (delta to the head's maximum in 2^-27 steps).  Every
+                # candidate below the largest kept key is kept, and among the candidates
+                # equal to it the kept ones are the lowest positions.
+                s32 = r["sigma"][g, hl, :len(nodes)].numpy()[is_c]
+                dl = (np.float32(s32.max()) - s32).astype(np.float32)
+                kq = (np.minimum(dl, np.float32(31.999998092651367)) * np.float32(134217728.0)).astype(np.uint32)
+                keys = np.where(dl < np.float32(32.0), kq, np.uint32(0xFFFFFFFE))
+                kcut = keys[inkept].max()
+                assert inkept[keys < kcut].all(), f"{label} level {lv} head {h}: a key below the cut dropped"
+                at = inkept[keys == kcut]
+                assert at[:int(at.sum())].all(), f"{label} level {lv} head {h}: ties not taken in position order"
                 mass = pi[inkept].sum()
                 lightest = pi[inkept].min()
                 assert mass >= p - MASS_TOL, f"{label} level {lv} head {h}: kept mass {mass:.6f} < p"

@@ -238,3 +238,22 @@ def test_equal_scores_take_lowest_positions(gen, n, p):
         toks = O.final_token_set(r.kept_leaves(), w.n_tokens, w.chunk)
         ref = O.attend(qh[h], kh[h // G], to_host(layer.v)[h // G], toks, tree.tau)
         assert float(np.abs(out[h].cpu().numpy() - ref).max()) <= ATOL
+
+
+def test_repeated_keys_tie_in_position_order():
+    """The key sequence repeats eight times with a period of 17,408 tokens (17 nodes of
+    the fifth level), so every node has seven exact copies and each head's cut falls
+    among equal scores.  The routing check orders each head's candidates by the keys
+    formed from the GPU's own scores and requires the kept ones among equal keys to be
+    the lowest positions: on the per-head path (levels of 34,816 slots, beyond the LDS
+    keys, 8,704 and 2,176) and on the one-workgroup path (544 and 136)."""
+    n = 139264
+    w = _w("deep", n, levels=5, steps=2, chunk=4)
+    say(f"[repeated keys] deep@{n}, period {n // 8}")
+    layer, x = make_layer(w)
+    layer.k[:, :n] = layer.k[:, :n // 8].repeat(1, 8, 1)
+    layer.build(n)
+    kh, tree = oracle_tree(layer, n)
+    vh = to_host(layer.v)
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label="repeated keys")
+    say(f"[repeated keys] heads exempt {ex}/{w.n_q_heads}, max attention err {err:.2e}, max score err {es:.2e}")

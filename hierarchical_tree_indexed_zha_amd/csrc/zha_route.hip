@@ -970,6 +970,11 @@ struct SliceView {
     int n, p0;
     float m;
 };
+// Candidates of head h at this level (a uniform scalar read: idle slices leave on it).
+__device__ __forceinline__ int head_n(const ZhaLevelArgs& a, int G, int c, int h) {
+    const int pn = a.top ? 0 : a.pnkept[h / G];
+    return a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+}
 __device__ __forceinline__ SliceView slice_view(const ZhaLevelArgs& a, int G, int c, int h, int s, float* red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = h / G;
@@ -1062,10 +1067,13 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_pass_kernel(ZhaLevelArg
     __shared__ float red[kHugeWaves];
     const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
     HugeCut st;
-    if (PASS > 0) st = a.hstate[h];
+    if (PASS > 0) {
+        st = a.hstate[h];
+        if (st.done) return;                   // an earlier pass already found the cut
+    }
+    if (s * ZHA_SLICE >= head_n(a, G, c, h)) return;
     const SliceView v = slice_view(a, G, c, h, s, red);
     if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
-    if (PASS > 0 && st.done) return;           // an earlier pass already found the cut
     const uint32_t mshift = PASS > 0 ? st.mshift : 31u, mval = PASS > 0 ? st.mval : 0u;
     const uint32_t bshift = PASS > 0 ? st.bshift : 21u, bmask = PASS > 0 ? st.bmask : 2047u;
     uint32_t key[kHugePer];
@@ -1130,6 +1138,7 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_bitmap_kernel(ZhaLevelA
     __shared__ float redf[kHugeWaves];
     const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    if (s * ZHA_SLICE >= head_n(a, G, c, h)) return;
     const HugeCut cut = a.hstate[h];
     const SliceView v = slice_view(a, G, c, h, s, redf);
     if (v.p0 >= v.n) return;
@@ -1183,6 +1192,7 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_ties_kernel(ZhaLevelArg
     const int lane = tid & 63, wave = tid >> 6;
     const HugeCut st = a.hstate[h];
     if (st.ties <= 1u) return;                 // the cut key is unique
+    if (s * ZHA_SLICE >= head_n(a, G, c, h)) return;
     const SliceView v = slice_view(a, G, c, h, s, redf);
     if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
     // equal-key mass of the slices before this one, and of this one

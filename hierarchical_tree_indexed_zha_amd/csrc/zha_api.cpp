@@ -372,10 +372,13 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             a.orph_lo = (int64_t)c * n_nodes(cfg, n_tokens, l + 1);
             a.orph_hi = n_nodes(cfg, n_tokens, l);
         } else {
-            a.pklist = nullptr;
-            a.pkmask = nullptr;
-            a.pnkept = nullptr;
-            a.pcap = 0;
+            // the first routed level has no parents: the parent arrays point at this
+            // level's own (readable; their values go unused), so that a kernel may
+            // issue its parent reads before it knows whether the level is the first
+            a.pklist = (const int32_t*)(X + y.klist[l]);
+            a.pkmask = (const uint32_t*)(X + y.kmask[l]);
+            a.pnkept = (const int32_t*)(X + y.nkept[l]);
+            a.pcap = 1;
             a.orph_lo = a.orph_hi = 0;
         }
         const int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);

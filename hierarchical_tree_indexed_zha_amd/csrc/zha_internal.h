@@ -64,7 +64,8 @@ struct ZhaLevelArgs {
     int64_t cap;               // node slots per head at this level
     int top;                   // 1 at the first routed level
     int64_t n_top;             // candidates at the first routed level (all its nodes)
-    // the level above (unused when top): its kept nodes are this level's parents
+    // the level above: its kept nodes are this level's parents (at the first routed
+    // level: readable memory with pcap 1, whose values go unused)
     const int32_t* pklist;     // [H_kv][pcap]
     const uint32_t* pkmask;    // [H_kv][pcap]
     const int32_t* pnkept;     // [H_kv]

@@ -53,6 +53,12 @@ template <bool BF16>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const void* __restrict__ q,
                                                                         ZhaLevelArgs a, int G, int c, int R,
                                                                         float tau) {
+    // every argument the kernel uses, fetched in one batch before any of them is
+    // needed (otherwise the loads come in dependent rounds behind uniform branches)
+    asm volatile("" ::"s"(q), "s"(a.S), "s"(a.B), "s"(a.cap), "s"(a.top), "s"(a.n_top), "s"(a.pklist),
+                 "s"(a.pkmask), "s"(a.pnkept), "s"(a.pcap), "s"(a.orph_lo), "s"(a.orph_hi), "s"(a.dc.m),
+                 "s"(a.dc.s1), "s"(a.dc.s2), "s"(a.ncand), "s"(a.sig), "s"(a.hblk), "s"(G), "s"(c), "s"(R),
+                 "s"(tau));
     const int g = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, kq = lane >> 4;
@@ -66,46 +72,47 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     const int stride = gridDim.x * 4;
     const int pcap = (int)a.pcap;
 
-    // The first item's parent entry is read together with the parent count: its
-    // index is bounded by the parent level's capacity, not by the count.
+    // One round trip before any work: the parent count, the first item's parent
+    // entry (its index clamped to the parent level's capacity, not bounded by the
+    // count) and the query rows are all in flight together.  At the first routed
+    // level the parent arrays point at readable memory whose values go unused.
     int it = blockIdx.x * 4 + wave;
-    int32_t pk = 0;
-    uint32_t pm = allg;
-    if (!a.top) {
-        const int pi = (int)zha_div((uint32_t)(it * U + cl), a.dc);
-        if (pi < pcap) {
-            pk = a.pklist[prow + pi];
-            pm = a.pkmask[prow + pi];
-        }
-    }
-    const int pn = a.top ? 0 : a.pnkept[g];
-    const int n_cand = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
-    // A operand: row = query head j of the group, contraction index d = 16m + 4kq + e.
+    const int pi0 = min((int)zha_div((uint32_t)(it * U + cl), a.dc), pcap - 1);
+    int32_t pk = a.pklist[prow + pi0];
+    uint32_t pm = a.pkmask[prow + pi0];
+    const int pn_raw = a.pnkept[g];
+    // A operand: row = query head j of the group (zero beyond G), contraction index
+    // d = 16m + 4kq + e.
     float qa[32];
-    if (j < G) {
-        if (BF16) {
-            const uint16_t* qr = static_cast<const uint16_t*>(q) + ((size_t)g * G + j) * ZHA_D + 4 * kq;
+    const int jq = j < G ? j : 0;
+    if (BF16) {
+        const uint16_t* qr = static_cast<const uint16_t*>(q) + ((size_t)g * G + jq) * ZHA_D + 4 * kq;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const uint2 v = *reinterpret_cast<const uint2*>(qr + 16 * m);
-                qa[4 * m + 0] = zha_bf16_to_f32(v.x & 0xFFFFu);
-                qa[4 * m + 1] = zha_bf16_to_f32(v.x >> 16);
-                qa[4 * m + 2] = zha_bf16_to_f32(v.y & 0xFFFFu);
-                qa[4 * m + 3] = zha_bf16_to_f32(v.y >> 16);
-            }
-        } else {
-            const float* qr = static_cast<const float*>(q) + ((size_t)g * G + j) * ZHA_D + 4 * kq;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float4 v = *reinterpret_cast<const float4*>(qr + 16 * m);
-                qa[4 * m + 0] = v.x; qa[4 * m + 1] = v.y; qa[4 * m + 2] = v.z; qa[4 * m + 3] = v.w;
-            }
+        for (int m = 0; m < 8; ++m) {
+            const uint2 v = *reinterpret_cast<const uint2*>(qr + 16 * m);
+            qa[4 * m + 0] = zha_bf16_to_f32(v.x & 0xFFFFu);
+            qa[4 * m + 1] = zha_bf16_to_f32(v.x >> 16);
+            qa[4 * m + 2] = zha_bf16_to_f32(v.y & 0xFFFFu);
+            qa[4 * m + 3] = zha_bf16_to_f32(v.y >> 16);
         }
     } else {
+        const float* qr = static_cast<const float*>(q) + ((size_t)g * G + jq) * ZHA_D + 4 * kq;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) qa[k] = 0.f;
+        for (int m = 0; m < 8; ++m) {
+            const float4 v = *reinterpret_cast<const float4*>(qr + 16 * m);
+            qa[4 * m + 0] = v.x; qa[4 * m + 1] = v.y; qa[4 * m + 2] = v.z; qa[4 * m + 3] = v.w;
+        }
     }
+    asm volatile("" ::"v"(pk), "v"(pm), "s"(pn_raw), "v"(qa[0]), "v"(qa[31]));
+#pragma unroll
+    for (int k = 0; k < 32; ++k) qa[k] = j < G ? qa[k] : 0.f;
+    if (a.top) {
+        pk = 0;
+        pm = allg;
+    }
+    const int pn = a.top ? 0 : pn_raw;
+    const int n_cand = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
 
     const int items = (n_cand + U - 1) / U;
     float hm[4] = {zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf()};   // largest score per head

@@ -189,6 +189,7 @@ __device__ __forceinline__ void pv_tile_bf16(const float* s_p, const uint4 (&vr)
 // grid (Bg, H_kv), 256 threads.
 template <bool BF16, bool DENSE>
 __global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BLOCKS_F32) void zha_attn_kernel(ZhaAttnArgs a, int G, int c, float tau, int Bg) {
+    ZHA_ATTN_ARGS_READY(a, "s"(G), "s"(c), "s"(tau), "s"(Bg));
     __shared__ int32_t s_tok[kWaves][kTileSlots];
     __shared__ uint32_t s_msk[kWaves][kTileSlots];
     __shared__ float s_buf[kWaves * 16 * ZHA_D];          // P tiles during the loop, partial O after it
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BL
 constexpr int kCombThreads = 256;
 __global__ __launch_bounds__(kCombThreads) void zha_combine_kernel(ZhaAttnArgs a, int G, int Bg,
                                                                    float* __restrict__ out) {
+    ZHA_ATTN_ARGS_READY(a, "s"(G), "s"(Bg), "s"(out));
     __shared__ float f[ZHA_ATTN_MAXB];
     __shared__ float red[kCombThreads];
     const int h = blockIdx.x, g = h / G, hl = h - g * G, tid = threadIdx.x;

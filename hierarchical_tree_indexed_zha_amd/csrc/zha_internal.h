@@ -92,6 +92,12 @@ struct ZhaLevelArgs {
     uint32_t* chunk_cnt;       // [H_kv][wcap / 512] kept nodes per 512-word chunk
     int slices;                // slices per head
 };
+// One field in each 64-byte line of a level's arguments, and the arguments that
+// follow them, demanded at kernel entry: the argument loads then go out in one
+// batch (the compiler otherwise fetches them in dependent rounds behind uniform
+// branches, each a memory round trip on a cold argument line).
+#define ZHA_LEVEL_ARGS_READY(a, ...) \
+    asm volatile("" ::"s"((a).S), "s"((a).pcap), "s"((a).wcap), "s"((a).hdone), "s"((a).slices), __VA_ARGS__)
 #define ZHA_LDS_KEYS 32768     // candidates per head selected in one workgroup's LDS
 #define ZHA_SLICE 32768        // positions per slice workgroup of a sliced level
 #define ZHA_SLICED_MIN_CAP 262144   // levels with more node slots select over slices
@@ -116,6 +122,7 @@ struct ZhaAttnArgs {
     float* po;                 // [H_kv][Bg][G][128]
     int32_t* nact;             // [H_kv]
 };
+#define ZHA_ATTN_ARGS_READY(a, ...) asm volatile("" ::"s"((a).K), "s"((a).n_tokens), __VA_ARGS__)
 hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, int H_kv, int G, int c,
                                 float tau, int Bg, hipStream_t stream, hipEvent_t start = nullptr,
                                 hipEvent_t stop = nullptr);

@@ -502,6 +502,7 @@ __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g,
 // group's workgroup stages every head's scores with one round trip and selects.
 __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelArgs a, int G, int c,
                                                                        float top_p) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p));
     __shared__ __align__(16) float s_sig[ZHA_MAX_GROUP * kSmallN];
     __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
     __shared__ __align__(16) uint32_t s_cnt[ZHA_MAX_GROUP * 256];
@@ -523,6 +524,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelA
 // every pass.  The last head of a group to finish writes the group's kept list.
 __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelArgs a, int G, int c,
                                                                        float top_p) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p));
     // keys: the keys (for the ordered tie pass); merge: head words [kMergeW][16]
     // (u64), then the step's parent node ids
     __shared__ __align__(16) uint32_t keys[kLdsKeys];
@@ -779,6 +781,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
 // all read before the count is known (bounded by the capacities), so they cost
 // one memory round trip together.
 __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelArgs a, int G, int c, int share) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(share));
     __shared__ __align__(16) uint64_t hw[kMergeW * ZHA_MAX_GROUP];   // [word][16 heads], heads >= G zero
     __shared__ int32_t s_par[kMergeW * 32];                            // parents' node ids
     __shared__ uint64_t s_union[kMergeW];
@@ -958,6 +961,7 @@ static_assert(ZHA_SLICE % (kHugeWaves * 64) == 0, "a slice holds whole words of 
 
 // grid (H_q), 256 threads: clears the level's histograms and counts.
 __global__ __launch_bounds__(kHugeThreads) void zha_huge_init_kernel(ZhaLevelArgs a, int Hq) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(Hq));
     const int h = blockIdx.x;
     for (int i = threadIdx.x; i < 3 * kHistBins; i += kHugeThreads) {
         const int pass = i / kHistBins, b = i - pass * kHistBins;
@@ -1067,6 +1071,7 @@ __device__ void advance_cut(const ZhaLevelArgs& a, int Hq, int h, int pass, floa
 // head's global histogram; the last slice to finish records the head's cut state.
 template <int PASS>
 __global__ __launch_bounds__(kHugeThreads) void zha_huge_pass_kernel(ZhaLevelArgs a, int G, int c, float top_p, int Hq) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(Hq));
     __shared__ __align__(16) uint64_t lhist[kHistPadded];
     __shared__ uint32_t lcnt[kHistBins];
     __shared__ int s_bin, s_last;
@@ -1141,6 +1146,7 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
 // and the slice's mass of keys equal to the cut when the cut key is shared.
 __global__ __launch_bounds__(kHugeThreads) void zha_huge_bitmap_kernel(ZhaLevelArgs a, int G, int c, float top_p,
                                                                       int Hq) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(Hq));
     __shared__ uint64_t red[kHugeWaves];
     __shared__ float redf[kHugeWaves];
     const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
@@ -1192,6 +1198,7 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_bitmap_kernel(ZhaLevelA
 // it falls walks its positions in order.
 __global__ __launch_bounds__(kHugeThreads) void zha_huge_ties_kernel(ZhaLevelArgs a, int G, int c, float top_p,
                                                                     int Hq) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(Hq));
     __shared__ uint64_t red[kHugeWaves];
     __shared__ float redf[kHugeWaves];
     __shared__ uint64_t wsum[kHugeWaves][kHugePer];   // equal-key mass per (wave, slot)
@@ -1266,6 +1273,7 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_ties_kernel(ZhaLevelArg
 // grid (chunks, H_kv), 512 threads: kept nodes (union over the group's heads) in
 // each chunk of kMergeW bitmap words, for the merge's rank offsets.
 __global__ __launch_bounds__(kMergeW) void zha_chunk_count_kernel(ZhaLevelArgs a, int G, int c) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c));
     __shared__ uint32_t part[kMergeW / 64];
     const int g = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int nch = (int)((a.wcap + kMergeW - 1) / kMergeW);

@@ -329,6 +329,21 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         if (n_nodes(cfg, n_tokens, l) > 0) { top = l; break; }
     if ((rc = record(events, 0, s))) return rc;
 
+    // The first routed levels, while small, form one chain: all their nodes scored
+    // in one launch, then selected level after level by one workgroup per group.
+    int nchain = 0;
+    {
+        int64_t planes = 0;
+        for (int l = top; l >= 1 && nchain < ZHA_MAX_CHAIN; --l) {
+            if (y.cap[l] > ZHA_SMALL_SLOTS || y.slices[l]) break;
+            planes += n_nodes(cfg, n_tokens, l) * (int64_t)R;
+            if (planes > ZHA_CHAIN_PLANES) break;
+            ++nchain;
+        }
+        if (nchain < 2) nchain = 0;   // a lone small level gains nothing
+    }
+    ZhaChainArgs chain;
+    chain.n = nchain;
     for (int l = top; l >= 1; --l) {
         ZhaLevelArgs a;
         a.S = (const float*)(T + y.t_s[l]);
@@ -383,6 +398,15 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         }
         const int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);
         a.score_blocks = blocks;
+        if (top - l < nchain) {
+            chain.lv[top - l] = a;
+            chain.blocks[top - l] = blocks;
+            if (top - l == nchain - 1) {
+                hipError_t e = zha_launch_route_chain(cfg->kv_dtype, q, chain, y.H, y.G, c, R, tau, cfg->top_p, s);
+                if (e != hipSuccess) return hip_fail(e, "route chain launch");
+            }
+            continue;
+        }
         hipError_t e = zha_launch_route_score(cfg->kv_dtype, q, a, y.H, y.G, c, R, tau, blocks, s);
         if (e != hipSuccess) return hip_fail(e, "route score launch");
         e = zha_launch_route_select(a, y.H, y.G, c, cfg->top_p, s);

@@ -105,6 +105,19 @@ hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArg
                                   int R, float tau, int blocks, hipStream_t stream);
 hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream);
 int zha_score_blocks(int64_t max_cand, int R);
+// The first routed levels while they are small (node slots <= ZHA_SMALL_SLOTS,
+// together at most ZHA_CHAIN_PLANES planes per group): every node scored by one
+// launch, then the levels selected one after the other by one workgroup per group.
+#define ZHA_SMALL_SLOTS 1024
+#define ZHA_MAX_CHAIN 6
+#define ZHA_CHAIN_PLANES 32768
+struct ZhaChainArgs {
+    ZhaLevelArgs lv[ZHA_MAX_CHAIN];   // lv[0] is the first routed level
+    int blocks[ZHA_MAX_CHAIN];        // score workgroups per group for each level
+    int n;
+};
+hipError_t zha_launch_route_chain(int kv_dtype, const void* q, const ZhaChainArgs& m, int H_kv, int G, int c, int R,
+                                  float tau, float top_p, hipStream_t stream);
 
 // ---- attention (zha_attn.hip)
 struct ZhaAttnArgs {

@@ -44,22 +44,32 @@ constexpr float kFix = 1099511627776.0f;   // 2^40: fixed-point scale of e_i in 
 constexpr float kKeyScale = 134217728.0f;  // 2^27: delta quantum
 constexpr float kDeltaMax = 32.0f;         // e^-32 * 2^40 < 1: heavier deltas carry no mass
 
+// threadIdx.x as a value that the compiler cannot hoist out of a loop: per-lane
+// addresses are recomputed where they are used instead of held in registers
+__device__ __forceinline__ int lane_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 __device__ __forceinline__ uint32_t all_heads(int G) { return G >= 32 ? 0xFFFFFFFFu : ((1u << G) - 1u); }
 
-// grid (blocks, H_kv), 256 threads.  Each wave scores items of U = 16/R
-// candidates (R <= 16) or one candidate over R/16 column blocks (R > 16).
+// Scores one level's candidates for every head of group g, as workgroup blk of
+// nblk (256 threads).  Each wave scores items of U = 16/R candidates (R <= 16)
+// or one candidate over R/16 column blocks (R > 16).  ALL: every node of the
+// level is a candidate of every head (positions are node ids), whatever the
+// level above kept.  hm gets the largest score of the lane's heads 4 kq + i.
 // Candidate positions and node ids fit in 32 bits (capacity < 2^31).
-template <bool BF16>
-__global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const void* __restrict__ q,
-                                                                        ZhaLevelArgs a, int G, int c, int R,
-                                                                        float tau) {
+template <bool BF16, bool ALL>
+__device__ __forceinline__ void score_level(const void* __restrict__ q, const ZhaLevelArgs& a, int G, int c, int R,
+                                            float tau, int g, int blk, int nblk, float (&hm)[4]) {
     // every argument the kernel uses, fetched in one batch before any of them is
     // needed (otherwise the loads come in dependent rounds behind uniform branches)
     asm volatile("" ::"s"(q), "s"(a.S), "s"(a.B), "s"(a.cap), "s"(a.top), "s"(a.n_top), "s"(a.pklist),
                  "s"(a.pkmask), "s"(a.pnkept), "s"(a.pcap), "s"(a.orph_lo), "s"(a.orph_hi), "s"(a.dc.m),
                  "s"(a.dc.s1), "s"(a.dc.s2), "s"(a.ncand), "s"(a.sig), "s"(a.hblk), "s"(G), "s"(c), "s"(R),
                  "s"(tau));
-    const int g = blockIdx.y;
+    const bool top = ALL || a.top;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, kq = lane >> 4;
     const int U = R <= 16 ? 16 / R : 1;
@@ -69,14 +79,14 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     const uint32_t allg = all_heads(G);
     const size_t lrow = (size_t)g * a.cap;
     const size_t prow = (size_t)g * a.pcap;
-    const int stride = gridDim.x * 4;
+    const int stride = nblk * 4;
     const int pcap = (int)a.pcap;
 
     // One round trip before any work: the parent count, the first item's parent
     // entry (its index clamped to the parent level's capacity, not bounded by the
     // count) and the query rows are all in flight together.  At the first routed
     // level the parent arrays point at readable memory whose values go unused.
-    int it = blockIdx.x * 4 + wave;
+    int it = blk * 4 + wave;
     const int pi0 = min((int)zha_div((uint32_t)(it * U + cl), a.dc), pcap - 1);
     int32_t pk = a.pklist[prow + pi0];
     uint32_t pm = a.pkmask[prow + pi0];
@@ -106,23 +116,24 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     asm volatile("" ::"v"(pk), "v"(pm), "s"(pn_raw), "v"(qa[0]), "v"(qa[31]));
 #pragma unroll
     for (int k = 0; k < 32; ++k) qa[k] = j < G ? qa[k] : 0.f;
-    if (a.top) {
+    if (top) {
         pk = 0;
         pm = allg;
     }
-    const int pn = a.top ? 0 : pn_raw;
-    const int n_cand = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
+    const int pn = top ? 0 : pn_raw;
+    const int n_cand = top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (blk == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
 
     const int items = (n_cand + U - 1) / U;
-    float hm[4] = {zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf()};   // largest score per head
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hm[i] = zha_neg_inf();   // largest score per head
     for (; it < items; it += stride) {
         const int pos = it * U + cl;
         const bool valid = pos < n_cand;
         int32_t node = 0;
         uint32_t cm = 0;
         if (valid) {
-            if (a.top) {
+            if (top) {
                 node = pos;
                 cm = allg;
             } else if (pos < pn * c) {
@@ -134,7 +145,7 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
                 cm = allg;
             }
         }
-        if (!a.top) {
+        if (!top) {
             // parent entry of this wave's next item, in flight with this item's planes
             const int npi = (int)zha_div((uint32_t)((it + stride) * U + cl), a.dc);
             if (it + stride < items && npi < pn) {
@@ -190,8 +201,20 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
                 if ((cm >> (4 * kq + i)) & 1u) hm[i] = fmaxf(hm[i], best[i]);
         }
     }
+}
+
+// grid (blocks, H_kv), 256 threads: one level's candidate scores.
+template <bool BF16>
+__global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const void* __restrict__ q,
+                                                                        ZhaLevelArgs a, int G, int c, int R,
+                                                                        float tau) {
+    const int g = blockIdx.y;
+    float hm[4];
+    score_level<BF16, false>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm);
     if (a.hblk) {
         // sliced levels: the largest score of each head over this block
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int j = lane & 15, kq = lane >> 4;
         __shared__ float s_hm[4][16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -205,6 +228,19 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
             a.hblk[(size_t)(g * G + h) * ZHA_SCORE_MAXB + blockIdx.x] = x;
         }
     }
+}
+
+// grid (max blocks, H_kv, levels), 256 threads: every node of each of the first
+// routed levels scored for every head of the group, positions = node ids (the
+// levels' selection then gathers its candidates' scores from these).
+template <bool BF16>
+__global__ __launch_bounds__(kScoreThreads) void zha_route_score_all_kernel(const void* __restrict__ q,
+                                                                            ZhaChainArgs m, int G, int c, int R,
+                                                                            float tau) {
+    const int z = blockIdx.z;
+    if ((int)blockIdx.x >= m.blocks[z]) return;
+    float hm[4];
+    score_level<BF16, true>(q, m.lv[z], G, c, R, tau, blockIdx.y, blockIdx.x, m.blocks[z], hm);
 }
 
 // ---- selection helpers
@@ -290,6 +326,7 @@ constexpr int kGlobBatch = 16;                // scores re-read together from gl
 constexpr int kMergeBlocks = 32;              // merge workgroups per group
 static_assert((kSlots & (kSlots - 1)) == 0 && kSlots % kBatch == 0, "slot batches");
 constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup
+static_assert(kSmallN == ZHA_SMALL_SLOTS, "small levels");
 constexpr int kSmallK = kSmallN / 64;
 static_assert(kSelThreads == kSmallN, "small path: one position per thread");
 static_assert(2 * ZHA_MAX_GROUP * kMergeW + kMergeW * 32 <= kLdsKeys,
@@ -315,7 +352,7 @@ __device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
 template <int K>
 __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* hist, uint32_t* cntb,
                                  uint64_t* kw, uint32_t* n_cand_out, uint32_t* n_kept_out) {
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_tid() & 63;
     const int nk = (n + 63) >> 6;
     float sv[K];
     float m = zha_neg_inf();
@@ -449,8 +486,9 @@ __device__ __forceinline__ void stage_small(const ZhaLevelArgs& a, int g, int G,
 // [G][256] (u64), s_cnt [G][256], s_kw [G][kSmallK].
 __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g, int G, float top_p, int n,
                                                    const float* s_sig, const int32_t* s_nid, uint64_t* s_hist,
-                                                   uint32_t* s_cnt, uint64_t* s_kw) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                   uint32_t* s_cnt, uint64_t* s_kw, int32_t* o_pk = nullptr,
+                                                   uint32_t* o_pm = nullptr, int* o_pn = nullptr) {
+    const int tid = lane_tid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t lrow = (size_t)g * a.cap;
     const int nk = (n + 63) >> 6;
     if (wave < G) {
@@ -473,29 +511,41 @@ __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g,
     __syncthreads();
     // union of the heads' kept words -> kept list (ascending node) and head masks:
     // wave w < nk handles word w; its rank offset is the popcount of the words below
+    // (with o_pk, the kept list, its masks and its length also go to LDS)
     if (nk == 0) {
-        if (tid == 0) a.nkept[g] = 0;
-        return;
-    }
-    if (wave >= nk) return;
-    uint64_t u = 0, uk = 0;
+        if (tid == 0) {
+            a.nkept[g] = 0;
+            if (o_pn) *o_pn = 0;
+        }
+    } else if (wave < nk) {
+        uint64_t u = 0, uk = 0;
 #pragma unroll 1
-    for (int hh = 0; hh < G; ++hh) u |= s_kw[hh * kSmallK + wave];
-    if (lane < wave) {
+        for (int hh = 0; hh < G; ++hh) u |= s_kw[hh * kSmallK + wave];
+        if (lane < wave) {
 #pragma unroll 1
-        for (int hh = 0; hh < G; ++hh) uk |= s_kw[hh * kSmallK + lane];
-    }
-    uint32_t below = (uint32_t)__popcll(uk);
-    for (int o = 32; o > 0; o >>= 1) below += __shfl_xor(below, o, 64);
-    if (lane_bit(u, lane)) {
-        const uint32_t rank = below + bits_below_lane(u);
-        uint32_t msk = 0;
+            for (int hh = 0; hh < G; ++hh) uk |= s_kw[hh * kSmallK + lane];
+        }
+        uint32_t below = (uint32_t)__popcll(uk);
+        for (int o = 32; o > 0; o >>= 1) below += __shfl_xor(below, o, 64);
+        if (lane_bit(u, lane)) {
+            const uint32_t rank = below + bits_below_lane(u);
+            uint32_t msk = 0;
 #pragma unroll 1
-        for (int hh = 0; hh < G; ++hh) msk |= lane_bit(s_kw[hh * kSmallK + wave], lane) << hh;
-        a.klist[lrow + rank] = s_nid[lane + 64 * wave];
-        a.kmask[lrow + rank] = msk;
+            for (int hh = 0; hh < G; ++hh) msk |= lane_bit(s_kw[hh * kSmallK + wave], lane) << hh;
+            const int32_t node = s_nid[lane + 64 * wave];
+            a.klist[lrow + rank] = node;
+            a.kmask[lrow + rank] = msk;
+            if (o_pk) {
+                o_pk[rank] = node;
+                o_pm[rank] = msk;
+            }
+        }
+        if (wave == nk - 1 && lane == 0) {
+            const uint32_t tot = below + (uint32_t)__popcll(u);
+            a.nkept[g] = (int32_t)tot;
+            if (o_pn) *o_pn = (int)tot;
+        }
     }
-    if (wave == nk - 1 && lane == 0) a.nkept[g] = (int32_t)(below + (uint32_t)__popcll(u));
 }
 
 // grid (H_kv), 1024 threads: levels with at most kSmallN node slots.  The
@@ -516,6 +566,71 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelA
     const int n = a.top ? (int)a.n_top : pn * c + n_orph;
     __syncthreads();
     select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw);
+}
+
+// grid (H_kv), 1024 threads: the first routed levels, all small, selected one
+// after the other by one workgroup per group with the kept lists in LDS.  Every
+// node of these levels was scored beforehand (positions = node ids); each level
+// gathers its candidates' scores, writes them back in candidate order, and
+// selects.
+__global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainArgs m, int G, int c, float top_p) {
+    __shared__ __align__(16) float s_sig[ZHA_MAX_GROUP * kSmallN];
+    __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
+    __shared__ __align__(16) uint32_t s_cnt[ZHA_MAX_GROUP * 256];
+    __shared__ int32_t s_nid[kSmallN];
+    __shared__ uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
+    __shared__ int32_t s_pk[kSmallN];
+    __shared__ uint32_t s_pm[kSmallN];
+    __shared__ int s_pn;
+
+    const int g = blockIdx.x;
+    const uint32_t allg = all_heads(G);
+#pragma unroll 1
+    for (int li = 0; li < m.n; ++li) {
+        const ZhaLevelArgs& a = m.lv[li];
+        const int p = lane_tid();                      // candidate position (n <= kSmallN)
+        const int pn = li == 0 ? 0 : s_pn;
+        const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+        int32_t node = 0;
+        uint32_t msk = 0;
+        if (p < n) {
+            if (a.top) {
+                node = p;
+                msk = allg;
+            } else if (p < pn * c) {
+                const int pi = (int)zha_div((uint32_t)p, a.dc);
+                node = s_pk[pi] * c + (p - pi * c);
+                msk = s_pm[pi];
+            } else {
+                node = (int32_t)a.orph_lo + (p - pn * c);
+                msk = allg;
+            }
+        }
+        float v[ZHA_MAX_GROUP];
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+            v[hh] = (hh < G && p < n && ((msk >> hh) & 1u)) ? a.sig[((size_t)g * G + hh) * a.cap + node]
+                                                           : zha_neg_inf();
+        __syncthreads();                               // every gather done before the write-back below
+        // all gathered values in registers at once (otherwise the compiler waits for
+        // each write-back store before the next LDS write)
+        asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+                     "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+            if (hh < G) s_sig[hh * kSmallN + p] = v[hh];
+        s_nid[p] = node;
+        float* sgw = a.sig + (size_t)g * G * a.cap + p;
+        if (p < n) {
+#pragma unroll
+            for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+                if (hh < G) sgw[(size_t)hh * a.cap] = v[hh];
+        }
+        if (p == 0) a.ncand[g] = n;
+        __syncthreads();
+        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw, s_pk, s_pm, &s_pn);
+        __syncthreads();
+    }
 }
 
 // grid (H_q), 1024 threads: levels with more than kSmallN node slots, one query
@@ -1323,6 +1438,25 @@ hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArg
         hipLaunchKernelGGL(zha_route_score_kernel<true>, grid, dim3(kScoreThreads), 0, stream, q, a, G, c, R, tau);
     else
         hipLaunchKernelGGL(zha_route_score_kernel<false>, grid, dim3(kScoreThreads), 0, stream, q, a, G, c, R, tau);
+    return hipGetLastError();
+}
+
+hipError_t zha_launch_route_chain(int kv_dtype, const void* q, const ZhaChainArgs& m, int H_kv, int G, int c, int R,
+                                  float tau, float top_p, hipStream_t stream) {
+    int bmax = 1;
+    for (int i = 0; i < m.n; ++i) {
+        if (m.lv[i].cap > kSmallN) return hipErrorInvalidValue;
+        bmax = std::max(bmax, m.blocks[i]);
+    }
+    const dim3 grid((unsigned)bmax, (unsigned)H_kv, (unsigned)m.n);
+    if (kv_dtype == 0)
+        hipLaunchKernelGGL(zha_route_score_all_kernel<true>, grid, dim3(kScoreThreads), 0, stream, q, m, G, c, R, tau);
+    else
+        hipLaunchKernelGGL(zha_route_score_all_kernel<false>, grid, dim3(kScoreThreads), 0, stream, q, m, G, c, R,
+                           tau);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(zha_select_chain_kernel, dim3((unsigned)H_kv), dim3(kSelThreads), 0, stream, m, G, c, top_p);
     return hipGetLastError();
 }
 

@@ -348,7 +348,7 @@ __device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
 // One wave selects for one query head among n <= 64 K candidates whose scores
 // are in LDS (sg); position lane + 64k sits in register slot k.  8-bit digits,
 // wave-local histograms (hist: 256 u64, cntb: 256 u32), no workgroup barrier.
-// The kept bitmap words go to kw[0 .. nk).
+// The kept bitmap words go to kw[16 k], k < nk.
 template <int K>
 __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* hist, uint32_t* cntb,
                                  uint64_t* kw, uint32_t* n_cand_out, uint32_t* n_kept_out) {
@@ -437,7 +437,7 @@ __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* 
         const uint64_t wk = __ballot(kept);
         n_cand += __popcll(__ballot(cand));
         n_kept += __popcll(wk);
-        if (lane == 0 && k < nk) kw[k] = wk;
+        if (lane == 0 && k < nk) kw[16 * k] = wk;
     }
     zha_wave_lds_sync();
     if (!none && !keep_all && ties > 1) {
@@ -450,7 +450,7 @@ __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* 
             const uint64_t ex = wave_excl_scan_u64(w, &tot);
             const uint64_t extra = __ballot(w > 0 && run + ex < need);
             n_kept += __popcll(extra);
-            if (lane == 0 && k < nk) kw[k] |= extra;
+            if (lane == 0 && k < nk) kw[16 * k] |= extra;
             run += tot;
         }
         zha_wave_lds_sync();
@@ -483,7 +483,8 @@ __device__ __forceinline__ void stage_small(const ZhaLevelArgs& a, int g, int G,
 // Small frontiers (n <= kSmallN candidates): one workgroup selects for all G
 // heads of group g (one wave each) from the scores staged in LDS (s_sig
 // [G][kSmallN], s_nid node ids) and writes the kept list.  LDS scratch: s_hist
-// [G][256] (u64), s_cnt [G][256], s_kw [G][kSmallK].
+// [G][256] (u64), s_cnt [G][256], s_kw [kSmallK][16] (u64, word-major: a word's
+// 16 head words are adjacent; heads >= G hold zero).
 __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g, int G, float top_p, int n,
                                                    const float* s_sig, const int32_t* s_nid, uint64_t* s_hist,
                                                    uint32_t* s_cnt, uint64_t* s_kw, int32_t* o_pk = nullptr,
@@ -496,7 +497,7 @@ __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g,
         const float* sg = s_sig + wave * kSmallN;
         uint64_t* hh_ = s_hist + wave * 256;
         uint32_t* cc_ = s_cnt + wave * 256;
-        uint64_t* kk_ = s_kw + wave * kSmallK;
+        uint64_t* kk_ = s_kw + wave;
         if (nk <= 1) select_head_wave<1>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
         else if (nk <= 2) select_head_wave<2>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
         else if (nk <= 4) select_head_wave<4>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
@@ -506,7 +507,9 @@ __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g,
             a.stats[2 * (g * G + wave) + 0] = (int32_t)nc_h;
             a.stats[2 * (g * G + wave) + 1] = (int32_t)nk_h;
         }
-        if (lane < nk) a.kbm[((size_t)g * G + wave) * a.wcap + lane] = kk_[lane];
+        if (lane < nk) a.kbm[((size_t)g * G + wave) * a.wcap + lane] = kk_[16 * lane];
+    } else if (wave < ZHA_MAX_GROUP && lane < nk) {
+        s_kw[16 * lane + wave] = 0ull;
     }
     __syncthreads();
     // union of the heads' kept words -> kept list (ascending node) and head masks:
@@ -518,20 +521,40 @@ __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g,
             if (o_pn) *o_pn = 0;
         }
     } else if (wave < nk) {
-        uint64_t u = 0, uk = 0;
-#pragma unroll 1
-        for (int hh = 0; hh < G; ++hh) u |= s_kw[hh * kSmallK + wave];
-        if (lane < wave) {
-#pragma unroll 1
-            for (int hh = 0; hh < G; ++hh) uk |= s_kw[hh * kSmallK + lane];
+        // word `wave` of the 16 heads (128 contiguous bytes, read by every lane at
+        // once) and, for the lanes below `wave`, word `lane`: all reads in flight
+        const uint4* wq = reinterpret_cast<const uint4*>(s_kw + 16 * wave);
+        const uint4* lq = reinterpret_cast<const uint4*>(s_kw + 16 * (lane < wave ? lane : 0));
+        uint4 hq[ZHA_MAX_GROUP / 2], lw[ZHA_MAX_GROUP / 2];
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
+            hq[t] = wq[t];
+            lw[t] = lq[t];
         }
-        uint32_t below = (uint32_t)__popcll(uk);
+        uint32_t ulo = 0, uhi = 0, llo = 0, lhi = 0;
+#pragma unroll
+        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
+            ulo |= hq[t].x | hq[t].z;
+            uhi |= hq[t].y | hq[t].w;
+            llo |= lw[t].x | lw[t].z;
+            lhi |= lw[t].y | lw[t].w;
+        }
+        const uint64_t u = ((uint64_t)uhi << 32) | ulo;
+        uint32_t below = lane < wave ? (uint32_t)(__popc(llo) + __popc(lhi)) : 0u;
         for (int o = 32; o > 0; o >>= 1) below += __shfl_xor(below, o, 64);
         if (lane_bit(u, lane)) {
             const uint32_t rank = below + bits_below_lane(u);
+            // lane's bit of each head word: low dword for lanes < 32, high dword above
+            const int sh = lane & 31;
+            const bool hi = lane >= 32;
             uint32_t msk = 0;
-#pragma unroll 1
-            for (int hh = 0; hh < G; ++hh) msk |= lane_bit(s_kw[hh * kSmallK + wave], lane) << hh;
+#pragma unroll
+            for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
+                const uint32_t w0 = hi ? hq[t].y : hq[t].x;
+                const uint32_t w1 = hi ? hq[t].w : hq[t].z;
+                msk |= ((w0 >> sh) & 1u) << (2 * t);
+                msk |= ((w1 >> sh) & 1u) << (2 * t + 1);
+            }
             const int32_t node = s_nid[lane + 64 * wave];
             a.klist[lrow + rank] = node;
             a.kmask[lrow + rank] = msk;
@@ -557,7 +580,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelA
     __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
     __shared__ __align__(16) uint32_t s_cnt[ZHA_MAX_GROUP * 256];
     __shared__ int32_t s_nid[kSmallN];
-    __shared__ uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
+    __shared__ __align__(16) uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
 
     const int g = blockIdx.x;
     const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
@@ -578,7 +601,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainA
     __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
     __shared__ __align__(16) uint32_t s_cnt[ZHA_MAX_GROUP * 256];
     __shared__ int32_t s_nid[kSmallN];
-    __shared__ uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
+    __shared__ __align__(16) uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
     __shared__ int32_t s_pk[kSmallN];
     __shared__ uint32_t s_pm[kSmallN];
     __shared__ int s_pn;
@@ -677,7 +700,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
         uint32_t* s_cnt = keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256;      // [G][256]
         int32_t* s_nid = reinterpret_cast<int32_t*>(s_cnt + ZHA_MAX_GROUP * 256);          // [kSmallN]
-        uint64_t* s_kw = hist;                                                           // [G][kSmallK]
+        uint64_t* s_kw = hist;                                                           // [kSmallK][16]
         stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
         __syncthreads();
         select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw);

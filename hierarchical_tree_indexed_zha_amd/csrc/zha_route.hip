@@ -333,7 +333,7 @@ static_assert(2 * ZHA_MAX_GROUP * kMergeW + kMergeW * 32 <= kLdsKeys,
               "merge: head words and parent ids must fit the key buffer");
 static_assert(kMergeW + kMergeW / 2 <= kHistPadded, "merge: union words and prefixes must fit the histogram");
 static_assert(kMergeW <= kSelThreads, "merge: one thread per word of a step");
-static_assert(ZHA_MAX_GROUP * (kSmallN + 3 * 256) + kSmallN <= kLdsKeys, "small path inside the key buffer");
+static_assert(ZHA_MAX_GROUP * (kSmallN + 2 * 256) + kSmallN <= kLdsKeys, "small path inside the key buffer");
 static_assert(ZHA_MAX_GROUP * kSmallK <= kHistPadded, "small-path kept words inside the histogram");
 
 // Bit `lane` of a 64-bit word, and the number of set bits below it.
@@ -345,13 +345,19 @@ __device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
 }
 
+// Small-path histogram bins pack a key count above a mass sum: at most kSmallN
+// keys of mass <= 2^40 sum below 2^52, so the fields never carry into each other
+// and one 64-bit LDS atomic per key updates both.
+constexpr int kCntShift = 52;
+constexpr uint64_t kMassMask = (1ull << kCntShift) - 1ull;
+
 // One wave selects for one query head among n <= 64 K candidates whose scores
 // are in LDS (sg); position lane + 64k sits in register slot k.  8-bit digits,
-// wave-local histograms (hist: 256 u64, cntb: 256 u32), no workgroup barrier.
+// a wave-local packed histogram (hist: 256 u64), no workgroup barrier.
 // The kept bitmap words go to kw[16 k], k < nk.
 template <int K>
-__device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* hist, uint32_t* cntb,
-                                 uint64_t* kw, uint32_t* n_cand_out, uint32_t* n_kept_out) {
+__device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* hist, uint64_t* kw,
+                                 uint32_t* n_cand_out, uint32_t* n_kept_out) {
     const int lane = lane_tid() & 63;
     const int nk = (n + 63) >> 6;
     float sv[K];
@@ -377,7 +383,6 @@ __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* 
             const int shift = 24 - 8 * pass;
             reinterpret_cast<uint4*>(hist)[2 * lane] = make_uint4(0u, 0u, 0u, 0u);
             reinterpret_cast<uint4*>(hist)[2 * lane + 1] = make_uint4(0u, 0u, 0u, 0u);
-            reinterpret_cast<uint4*>(cntb)[lane] = make_uint4(0u, 0u, 0u, 0u);
             zha_wave_lds_sync();
             // keys whose digits above this pass's match the prefix found so far
             const uint32_t hs = pass == 0 ? 31u : (uint32_t)(shift + 8);
@@ -386,11 +391,9 @@ __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* 
             for (int k = 0; k < K; ++k) {
                 const uint32_t kk = key[k];
                 const uint32_t top = pass == 0 ? 0u : (kk >> hs);
-                if (kk < kNoMass && top == want) {
-                    const uint32_t b = (kk >> shift) & 255u;
-                    atomicAdd((unsigned long long*)&hist[b], (unsigned long long)mass_of(kk));
-                    atomicAdd(&cntb[b], 1u);
-                }
+                if (kk < kNoMass && top == want)
+                    atomicAdd((unsigned long long*)&hist[(kk >> shift) & 255u],
+                              (unsigned long long)(mass_of(kk) | (1ull << kCntShift)));
             }
             zha_wave_lds_sync();
             const uint4 h01 = reinterpret_cast<const uint4*>(hist)[2 * lane];
@@ -399,26 +402,29 @@ __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* 
                                     ((uint64_t)h23.y << 32) | h23.x, ((uint64_t)h23.w << 32) | h23.z};
             const uint64_t mine = hb[0] + hb[1] + hb[2] + hb[3];
             uint64_t total;
-            uint64_t before = wave_excl_scan_u64(mine, &total);
+            uint64_t before = wave_excl_scan_u64(mine, &total) & kMassMask;
             if (pass == 0) {
-                const uint64_t T = (uint64_t)ceil((double)top_p * (double)total);
-                need = T < 1 ? 1 : (T > total ? total : T);
+                const uint64_t tm = total & kMassMask;
+                const uint64_t T = (uint64_t)ceil((double)top_p * (double)tm);
+                need = T < 1 ? 1 : (T > tm ? tm : T);
             }
             int my_bin = -1;
-            uint64_t my_before = 0;
+            uint64_t my_before = 0, my_val = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool cross = before < need && before + hb[i] >= need && my_bin < 0;
+                const uint64_t hm = hb[i] & kMassMask;
+                const bool cross = before < need && before + hm >= need && my_bin < 0;
                 my_bin = cross ? lane * 4 + i : my_bin;
                 my_before = cross ? before : my_before;
-                before += hb[i];
+                my_val = cross ? hb[i] : my_val;
+                before += hm;
             }
             const uint64_t found = __ballot(my_bin >= 0);
             const int src = found ? __ffsll((long long)found) - 1 : 0;
             const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(my_bin, src);
             need -= zha_readlane_u64(my_before, src);
             prefix = (prefix << 8) | bin;
-            const uint32_t cnt = cntb[bin];
+            const uint32_t cnt = (uint32_t)(zha_readlane_u64(my_val, src) >> kCntShift);
             zha_wave_lds_sync();
             if (cnt == 1 || pass == 3) {
                 // the crossing bin holds one key (or the keys equal to the cut): the cut
@@ -483,11 +489,11 @@ __device__ __forceinline__ void stage_small(const ZhaLevelArgs& a, int g, int G,
 // Small frontiers (n <= kSmallN candidates): one workgroup selects for all G
 // heads of group g (one wave each) from the scores staged in LDS (s_sig
 // [G][kSmallN], s_nid node ids) and writes the kept list.  LDS scratch: s_hist
-// [G][256] (u64), s_cnt [G][256], s_kw [kSmallK][16] (u64, word-major: a word's
+// [G][256] (u64), s_kw [kSmallK][16] (u64, word-major: a word's
 // 16 head words are adjacent; heads >= G hold zero).
 __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g, int G, float top_p, int n,
                                                    const float* s_sig, const int32_t* s_nid, uint64_t* s_hist,
-                                                   uint32_t* s_cnt, uint64_t* s_kw, int32_t* o_pk = nullptr,
+                                                   uint64_t* s_kw, int32_t* o_pk = nullptr,
                                                    uint32_t* o_pm = nullptr, int* o_pn = nullptr) {
     const int tid = lane_tid(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t lrow = (size_t)g * a.cap;
@@ -496,13 +502,12 @@ __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g,
         uint32_t nc_h, nk_h;
         const float* sg = s_sig + wave * kSmallN;
         uint64_t* hh_ = s_hist + wave * 256;
-        uint32_t* cc_ = s_cnt + wave * 256;
         uint64_t* kk_ = s_kw + wave;
-        if (nk <= 1) select_head_wave<1>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-        else if (nk <= 2) select_head_wave<2>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-        else if (nk <= 4) select_head_wave<4>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-        else if (nk <= 8) select_head_wave<8>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
-        else select_head_wave<16>(sg, n, top_p, hh_, cc_, kk_, &nc_h, &nk_h);
+        if (nk <= 1) select_head_wave<1>(sg, n, top_p, hh_, kk_, &nc_h, &nk_h);
+        else if (nk <= 2) select_head_wave<2>(sg, n, top_p, hh_, kk_, &nc_h, &nk_h);
+        else if (nk <= 4) select_head_wave<4>(sg, n, top_p, hh_, kk_, &nc_h, &nk_h);
+        else if (nk <= 8) select_head_wave<8>(sg, n, top_p, hh_, kk_, &nc_h, &nk_h);
+        else select_head_wave<16>(sg, n, top_p, hh_, kk_, &nc_h, &nk_h);
         if (lane == 0) {
             a.stats[2 * (g * G + wave) + 0] = (int32_t)nc_h;
             a.stats[2 * (g * G + wave) + 1] = (int32_t)nk_h;
@@ -578,7 +583,6 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelA
     ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p));
     __shared__ __align__(16) float s_sig[ZHA_MAX_GROUP * kSmallN];
     __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
-    __shared__ __align__(16) uint32_t s_cnt[ZHA_MAX_GROUP * 256];
     __shared__ int32_t s_nid[kSmallN];
     __shared__ __align__(16) uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
 
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelA
     stage_small(a, g, G, c, threadIdx.x, pn, s_sig, s_nid);
     const int n = a.top ? (int)a.n_top : pn * c + n_orph;
     __syncthreads();
-    select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw);
+    select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw);
 }
 
 // grid (H_kv), 1024 threads: the first routed levels, all small, selected one
@@ -599,7 +603,6 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelA
 __global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainArgs m, int G, int c, float top_p) {
     __shared__ __align__(16) float s_sig[ZHA_MAX_GROUP * kSmallN];
     __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
-    __shared__ __align__(16) uint32_t s_cnt[ZHA_MAX_GROUP * 256];
     __shared__ int32_t s_nid[kSmallN];
     __shared__ __align__(16) uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
     __shared__ int32_t s_pk[kSmallN];
@@ -651,7 +654,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainA
         }
         if (p == 0) a.ncand[g] = n;
         __syncthreads();
-        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw, s_pk, s_pm, &s_pn);
+        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw, s_pk, s_pm, &s_pn);
         __syncthreads();
     }
 }
@@ -698,12 +701,11 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         if (hl != 0) return;
         float* s_sig = reinterpret_cast<float*>(keys);                                   // [G][kSmallN]
         uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
-        uint32_t* s_cnt = keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256;      // [G][256]
-        int32_t* s_nid = reinterpret_cast<int32_t*>(s_cnt + ZHA_MAX_GROUP * 256);          // [kSmallN]
+        int32_t* s_nid = reinterpret_cast<int32_t*>(keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256);
         uint64_t* s_kw = hist;                                                           // [kSmallK][16]
         stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
         __syncthreads();
-        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_cnt, s_kw);
+        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw);
         return;
     }
     const int nwords = (n + 63) >> 6;

@@ -664,8 +664,8 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainA
 // (positions tid + 1024 k); larger frontiers recompute them from the scores on
 // every pass.  The last head of a group to finish writes the group's kept list.
 __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelArgs a, int G, int c,
-                                                                       float top_p) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p));
+                                                                       float top_p, int small_only) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(small_only));
     // keys: the keys (for the ordered tie pass); merge: head words [kMergeW][16]
     // (u64), then the step's parent node ids
     __shared__ __align__(16) uint32_t keys[kLdsKeys];
@@ -679,6 +679,20 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
 
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (small_only) {
+        // a sliced level: only a frontier of at most kSmallN candidates is selected
+        // here (by the group's first workgroup); the slice kernels take larger ones
+        const int pn0 = a.top ? 0 : a.pnkept[g];
+        const int n0 = a.top ? (int)a.n_top : pn0 * c + (int)(a.orph_hi - a.orph_lo);
+        if (n0 > kSmallN || hl != 0) return;
+        float* s_sig = reinterpret_cast<float*>(keys);                                   // [G][kSmallN]
+        uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
+        int32_t* s_nid = reinterpret_cast<int32_t*>(keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256);
+        stage_small(a, g, G, c, tid, pn0, s_sig, s_nid);
+        __syncthreads();
+        select_small_group(a, g, G, top_p, n0, s_sig, s_nid, s_hist, hist);
+        return;
+    }
     const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
     const float* sg = a.sig + ((size_t)g * G + hl) * a.cap;
 
@@ -971,7 +985,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
     }
 
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (!a.hblk && n <= kSmallN) return;         // selected and merged by the select kernel
+    if (n <= kSmallN) return;                    // selected and merged by the select kernel
     const int nwords = (n + 63) >> 6;
     if (w0 >= nwords) {
         if (blockIdx.x == 0 && nwords == 0 && tid == 0) a.nkept[g] = 0;
@@ -1223,7 +1237,8 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_pass_kernel(ZhaLevelArg
         st = a.hstate[h];
         if (st.done) return;                   // an earlier pass already found the cut
     }
-    if (s * ZHA_SLICE >= head_n(a, G, c, h)) return;
+    const int nh = head_n(a, G, c, h);
+    if (nh <= kSmallN || s * ZHA_SLICE >= nh) return;   // small frontiers: selected whole elsewhere
     const SliceView v = slice_view(a, G, c, h, s, red);
     if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
     const uint32_t mshift = PASS > 0 ? st.mshift : 31u, mval = PASS > 0 ? st.mval : 0u;
@@ -1291,7 +1306,8 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_bitmap_kernel(ZhaLevelA
     __shared__ float redf[kHugeWaves];
     const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    if (s * ZHA_SLICE >= head_n(a, G, c, h)) return;
+    const int nh = head_n(a, G, c, h);
+    if (nh <= kSmallN || s * ZHA_SLICE >= nh) return;   // small frontiers: selected whole elsewhere
     const HugeCut cut = a.hstate[h];
     const SliceView v = slice_view(a, G, c, h, s, redf);
     if (v.p0 >= v.n) return;
@@ -1346,7 +1362,8 @@ __global__ __launch_bounds__(kHugeThreads) void zha_huge_ties_kernel(ZhaLevelArg
     const int lane = tid & 63, wave = tid >> 6;
     const HugeCut st = a.hstate[h];
     if (st.ties <= 1u) return;                 // the cut key is unique
-    if (s * ZHA_SLICE >= head_n(a, G, c, h)) return;
+    const int nh = head_n(a, G, c, h);
+    if (nh <= kSmallN || s * ZHA_SLICE >= nh) return;   // small frontiers: selected whole elsewhere
     const SliceView v = slice_view(a, G, c, h, s, redf);
     if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
     // equal-key mass of the slices before this one, and of this one
@@ -1424,6 +1441,7 @@ __global__ __launch_bounds__(kMergeW) void zha_chunk_count_kernel(ZhaLevelArgs a
         hv[hh] = (hh < G && w < a.wcap) ? a.kbm[((size_t)g * G + hh) * a.wcap + w] : 0ull;
     const int pn = a.top ? 0 : a.pnkept[g];
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (n <= kSmallN) return;                  // selected and merged by the select kernel
     const int nwords = (n + 63) >> 6;
     uint64_t u = 0;
 #pragma unroll
@@ -1492,8 +1510,13 @@ hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c
         return hipGetLastError();
     }
     if (a.hblk) {
-        // sliced level: three digit passes, the bitmap, the ordered ties, chunk counts, merge
+        // sliced level: a frontier of at most kSmallN candidates is selected and merged
+        // by one workgroup per group; larger ones take three digit passes over slices,
+        // the bitmap, the ordered ties, chunk counts and the merge (each of which
+        // leaves at once for a small frontier)
         const int Hq = H_kv * G;
+        hipLaunchKernelGGL(zha_select_large_kernel, dim3((unsigned)Hq), dim3(kSelThreads), 0, stream, a, G, c, top_p,
+                           1);
         const dim3 sg((unsigned)a.slices, (unsigned)Hq);
         hipLaunchKernelGGL(zha_huge_pass_kernel<0>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
         hipLaunchKernelGGL(zha_huge_pass_kernel<1>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
@@ -1508,7 +1531,7 @@ hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c
         return hipGetLastError();
     }
     hipLaunchKernelGGL(zha_select_large_kernel, dim3((unsigned)(H_kv * G)), dim3(kSelThreads), 0, stream, a, G,
-                       c, top_p);
+                       c, top_p, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // bitmap words per merge block: a multiple of 16, at most kMergeW, over at

@@ -93,6 +93,17 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def head_tokens(route1, g, hl, n_tokens, c):
+    """Distinct tokens head hl of group g attends: its kept chunks, the sink if not among them, the tail."""
+    nk = int(route1["n_kept"][g])
+    kept = route1["kept"][g, :nk]
+    mine = ((route1["mask"][g, :nk] >> hl) & 1) == 1
+    n_mine = int(mine.sum())
+    kept0 = n_mine > 0 and bool(mine[0]) and int(kept[0]) == 0
+    n1 = n_tokens // c
+    return n_mine * c + (0 if (kept0 or n1 == 0) else 1) + (n_tokens - c * n1)
+
+
 def union_tokens(route1, g, n_tokens, c):
     """Distinct tokens the gather reads for group g: kept chunks, the sink if not among them, the tail."""
     nk = int(route1["n_kept"][g])
@@ -182,12 +193,15 @@ def bench_workload(args, torch, W, B, ZhaLayer):
     route_ms = sum(r[0].elapsed_time(r[1]) for r in evs)
     gather_ms = sum(r[1].elapsed_time(r[2]) for r in evs)
     comb_ms = sum(r[2].elapsed_time(r[3]) for r in evs)
+    step_us = sorted(r[0].elapsed_time(r[3]) * 1e3 for r in evs)      # each decode between its first and last event
+    dec_med_us = step_us[len(step_us) // 2]
 
     # Algorithmic bytes of the same steps: replayed once more, reading each step's
     # kept lists on the host (the selection is deterministic).
     layer.n_tokens = N
     gather_bytes = router_bytes = 0
     keys_read = []
+    keys_head = []
     R = w.n_ref
     for t in range(args.steps):
         i = t % x["q"].shape[0]
@@ -200,6 +214,9 @@ def bench_workload(args, torch, W, B, ZhaLayer):
         ut = [union_tokens(r1, g, n, c) for g in range(w.n_kv_heads)]
         gather_bytes += sum(ut) * 2 * d * e_kv
         keys_read.append(sum(ut) / (w.n_kv_heads * n))
+        G = w.n_q_heads // w.n_kv_heads
+        keys_head.append(sum(head_tokens(r1, g, hl, n, c) for g in range(w.n_kv_heads) for hl in range(G))
+                         / (w.n_q_heads * n))
         for lv in range(1, w.levels + 1):
             if n // c ** lv:
                 router_bytes += int(layer.route_level(lv)["n_cand"].sum()) * R * (d + 1) * 4
@@ -236,6 +253,8 @@ def bench_workload(args, torch, W, B, ZhaLayer):
         "dense_us": round(us_dense, 3),
         "speedup_vs_dense": round(us_dense / us_dec, 3),
         "keys_read_frac": round(sum(keys_read) / K, 5),
+        "keys_read_frac_head_mean": round(sum(keys_head) / K, 5),
+        "decode_us_events_median": round(dec_med_us, 3),
         "phase_us": {"route": round(route_us, 3), "gather": round(gather_us, 3),
                      "combine": round(comb_ms / K * 1e3, 3)},
         "router_gbs_alg": round(router_gbs, 1),
@@ -285,9 +304,27 @@ def cpu_baseline(args, layer, x, w, torch):
         done += 1
     us = elapsed / done * 1e6
     _log(f"[cpu] oracle {done} steps, {us / 1e3:.1f} ms/step, threads {threads}")
+    # the same steps again on one core (BLAS limited to one thread), a third of the budget
+    us1, done1 = None, 0
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            elapsed1 = 0.0
+            while done1 < done and (elapsed1 < args.cpu_seconds / 3 or done1 < 1):
+                i = done1 % x["q"].shape[0]
+                t0 = time.perf_counter()
+                O.decode_step(conv(x["q"][i]), kh, vh, tree, w.top_p)
+                elapsed1 += time.perf_counter() - t0
+                done1 += 1
+        us1 = elapsed1 / done1 * 1e6
+        _log(f"[cpu] oracle on one core: {done1} decode steps, {us1 / 1e3:.1f} ms/step")
+    except Exception as e:
+        _log(f"[cpu] one-core timing skipped: {e}")
     return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "value_one_core": None if us1 is None else round(us1, 1),
             "sample": f"{done} append+decode steps of {w.name} (N={N}) after an untimed fp64 tree "
-                      f"precompute of {t_pre:.1f} s; host cores available {os.cpu_count()}"}
+                      f"precompute of {t_pre:.1f} s; host cores available {os.cpu_count()}; "
+                      f"value_one_core: {done1} decode steps with BLAS on one thread"}
 
 
 def sweep(args, torch, W, B, ZhaLayer):

@@ -696,19 +696,27 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
     const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
     const float* sg = a.sig + ((size_t)g * G + hl) * a.cap;
 
-    // The count and the scores of positions < min(cap, kLdsKeys) are read
-    // together (one round trip); positions >= n are ignored afterwards.
+    // The count and the scores of the first half of the LDS positions are read
+    // together (one round trip, bounded by the capacity); the second half's reads,
+    // bounded by the count, follow as soon as it arrives.  Positions >= n are
+    // ignored afterwards.
     const int pn = a.top ? 0 : a.pnkept[g];
     uint32_t kr[kSlots];
-    {
-        const int lim = (int)min(a.cap, (int64_t)kLdsKeys);
+    const int lim = (int)min(a.cap, (int64_t)kLdsKeys);
 #pragma unroll
-        for (int k = 0; k < kSlots; ++k) {
-            const int pos = tid + k * kSelThreads;
-            kr[k] = __float_as_uint(pos < lim ? sg[pos] : zha_neg_inf());
-        }
+    for (int k = 0; k < kSlots / 2; ++k) {
+        const int pos = tid + k * kSelThreads;
+        kr[k] = __float_as_uint(pos < lim ? sg[pos] : zha_neg_inf());
     }
     const int n = a.top ? (int)a.n_top : pn * c + n_orph;
+    {
+        const int lim2 = min(lim, n);
+#pragma unroll
+        for (int k = kSlots / 2; k < kSlots; ++k) {
+            const int pos = tid + k * kSelThreads;
+            kr[k] = __float_as_uint(pos < lim2 ? sg[pos] : zha_neg_inf());
+        }
+    }
     if (n <= kSmallN) {
         // a small frontier at a large level: the group's first workgroup selects for
         // all heads, with the key buffer as its LDS
@@ -775,8 +783,8 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         __syncthreads();
 #pragma unroll 1
         for (int pass = 0; pass < 3; ++pass) {
-            // pass 0 counts every key that carries mass; later passes only the keys
-            // whose higher digits equal the bins found so far
+            // pass 0 adds the mass of every key that carries mass; later passes count
+            // and add only the keys whose higher digits equal the bins found so far
             const bool all = pass == 0;
             if (staged) {
                 // keys read from LDS kBatch slots at a time (all reads in flight together)
@@ -791,7 +799,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
                         if (key < kNoMass && (all || (key >> mshift) == mval)) {
                             const uint32_t b = (key >> bshift) & bmask;
                             atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
-                            atomicAdd(&cntb[b], 1u);
+                            if (!all) atomicAdd(&cntb[b], 1u);
                         }
                     }
                 }
@@ -810,7 +818,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
                         if (key < kNoMass && (all || (key >> mshift) == mval)) {
                             const uint32_t b = (key >> bshift) & bmask;
                             atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
-                            atomicAdd(&cntb[b], 1u);
+                            if (!all) atomicAdd(&cntb[b], 1u);
                         }
                     }
                 }
@@ -820,7 +828,9 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
             __syncthreads();
             const uint32_t bin = (uint32_t)s_bin;
             need = s_need - s_before;            // mass still needed inside this bin
-            const uint32_t cnt = cntb[bin];
+            // pass 0 counts no keys (its bins hold many at these sizes): it never ends
+            // the search
+            const uint32_t cnt = pass == 0 ? 0u : cntb[bin];
             const uint32_t pref = pass == 0 ? bin : (mval << (pass == 1 ? 11 : 10)) | bin;
             if (cnt == 1 || pass == 2) {
                 // the crossing bin holds one key (or the keys equal to the cut): the cut

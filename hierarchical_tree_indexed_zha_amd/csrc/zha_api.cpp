@@ -344,6 +344,10 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     }
     ZhaChainArgs chain;
     chain.n = nchain;
+    // a large level above a routed one may leave its merge to the level below's
+    // score kernel
+    ZhaLevelArgs above;
+    bool defer_above = false;
     for (int l = top; l >= 1; --l) {
         ZhaLevelArgs a;
         a.S = (const float*)(T + y.t_s[l]);
@@ -407,10 +411,15 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             }
             continue;
         }
-        hipError_t e = zha_launch_route_score(cfg->kv_dtype, q, a, y.H, y.G, c, R, tau, blocks, s);
+        const bool defer = l >= 2 && y.cap[l] > ZHA_SMALL_SLOTS && !y.slices[l] &&
+                           zha_defer_fits(y.G, y.wcap[l], a.top ? 0 : a.pcap);
+        hipError_t e = zha_launch_route_score(cfg->kv_dtype, q, a, y.H, y.G, c, R, tau, blocks, s,
+                                              defer_above ? &above : nullptr);
         if (e != hipSuccess) return hip_fail(e, "route score launch");
-        e = zha_launch_route_select(a, y.H, y.G, c, cfg->top_p, s);
+        e = zha_launch_route_select(a, y.H, y.G, c, cfg->top_p, s, !defer);
         if (e != hipSuccess) return hip_fail(e, "route select launch");
+        above = a;
+        defer_above = defer;
     }
 
     ZhaAttnArgs at_;

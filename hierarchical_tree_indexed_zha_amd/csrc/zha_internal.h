@@ -101,9 +101,22 @@ struct ZhaLevelArgs {
 #define ZHA_LDS_KEYS 32768     // candidates per head selected in one workgroup's LDS
 #define ZHA_SLICE 32768        // positions per slice workgroup of a sliced level
 #define ZHA_SLICED_MIN_CAP 262144   // levels with more node slots select over slices
+// A large level (more than ZHA_SMALL_SLOTS node slots, not sliced) whose G heads'
+// bitmap words together number at most ZHA_DEFER_WORDS and whose parents at most
+// ZHA_DEFER_PARENTS is selected without a merge launch: the score kernel of the
+// level below (`defer` = the level above's arguments) derives its kept list from
+// the bitmaps in LDS and writes it.
+#define ZHA_DEFER_WORDS 2048
+#define ZHA_DEFER_PARENTS 4096
+bool zha_defer_fits(int G, int64_t wcap, int64_t pcap);
+size_t zha_defer_lds_bytes(int G, int64_t wcap, int64_t pcap);
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
-                                  int R, float tau, int blocks, hipStream_t stream);
-hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream);
+                                  int R, float tau, int blocks, hipStream_t stream,
+                                  const ZhaLevelArgs* defer = nullptr);
+// merge = false leaves a large, unsliced level's kept list to the next level's
+// score kernel (zha_launch_route_score with `defer`)
+hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream,
+                                   bool merge = true);
 int zha_score_blocks(int64_t max_cand, int R);
 // The first routed levels while they are small (node slots <= ZHA_SMALL_SLOTS,
 // together at most ZHA_CHAIN_PLANES planes per group): every node scored by one

@@ -54,15 +54,84 @@ __device__ __forceinline__ int lane_tid() {
 
 __device__ __forceinline__ uint32_t all_heads(int G) { return G >= 32 ? 0xFFFFFFFFu : ((1u << G) - 1u); }
 
+// Bit `lane` of a 64-bit word, and the number of set bits below it.
+__device__ __forceinline__ uint32_t lane_bit(uint64_t w, int lane) {
+    const uint32_t h = lane < 32 ? (uint32_t)w : (uint32_t)(w >> 32);
+    return (h >> (lane & 31)) & 1u;
+}
+__device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
+}
+
+// A level whose merge is left to the level below it: the score workgroups of the
+// level below stage its per-head kept bitmaps (position-indexed, [G][wc] words),
+// their union and its popcount prefix, and the kept list of the level above it
+// (its parents), then read any entry of its kept list from LDS.
+constexpr int kDeferW = ZHA_DEFER_WORDS / kScoreThreads;    // head words per thread
+constexpr int kDeferP = ZHA_DEFER_PARENTS / kScoreThreads;  // parent entries per thread
+static_assert(kDeferW * kScoreThreads == ZHA_DEFER_WORDS && kDeferP * kScoreThreads == ZHA_DEFER_PARENTS,
+              "deferred merge staging");
+
+struct DeferView {
+    const uint64_t* hw;    // [G][wc] head words
+    const uint64_t* u;     // [wc] union of the head words (zero from word nw on)
+    const uint32_t* pre;   // [wc] kept nodes in the words below
+    const int32_t* gk;     // the level's parents (kept list of the level above it)
+    int wc, nw, gn;        // words per head, words holding candidates, parents kept
+};
+
+// Node id and head mask of the level's candidate at position qp.
+__device__ __forceinline__ void defer_node(const ZhaLevelArgs& pa, const DeferView& v, int G, int c, int qp,
+                                           int32_t& node, uint32_t& mask) {
+    const int w = qp >> 6, b = qp & 63;
+    if (pa.top) node = qp;
+    else if (qp < v.gn * c) {
+        const int gi = (int)zha_div((uint32_t)qp, pa.dc);
+        node = v.gk[gi] * c + (qp - gi * c);
+    } else node = (int32_t)pa.orph_lo + (qp - v.gn * c);
+    uint32_t m = 0;
+    for (int hh = 0; hh < G; ++hh) m |= (uint32_t)((v.hw[hh * v.wc + w] >> b) & 1ull) << hh;
+    mask = m;
+}
+
+// Entry r (< the kept count) of the level's kept list: the word holding it (the
+// last whose prefix is <= r), then its bit by halving popcounts.
+__device__ __forceinline__ void defer_entry(const ZhaLevelArgs& pa, const DeferView& v, int G, int c, uint32_t r,
+                                            int32_t& node, uint32_t& mask) {
+    int lo = 0, hi = v.nw - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (v.pre[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    uint64_t x = v.u[lo];
+    uint32_t k = r - v.pre[lo];
+    int b = 0;
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) {
+        const uint32_t cnt = (uint32_t)__popcll(x & ((1ull << sh) - 1ull));
+        if (k >= cnt) {
+            k -= cnt;
+            x >>= sh;
+            b += sh;
+        }
+    }
+    defer_node(pa, v, G, c, lo * 64 + b, node, mask);
+}
+
 // Scores one level's candidates for every head of group g, as workgroup blk of
 // nblk (256 threads).  Each wave scores items of U = 16/R candidates (R <= 16)
 // or one candidate over R/16 column blocks (R > 16).  ALL: every node of the
 // level is a candidate of every head (positions are node ids), whatever the
 // level above kept.  hm gets the largest score of the lane's heads 4 kq + i.
+// DEF: the level above (pa) was selected but not merged; its kept list is
+// derived here from its bitmaps (dynamic LDS), and this workgroup writes its
+// share of it (all of it together with the other workgroups).
 // Candidate positions and node ids fit in 32 bits (capacity < 2^31).
-template <bool BF16, bool ALL>
+template <bool BF16, bool ALL, bool DEF = false>
 __device__ __forceinline__ void score_level(const void* __restrict__ q, const ZhaLevelArgs& a, int G, int c, int R,
-                                            float tau, int g, int blk, int nblk, float (&hm)[4]) {
+                                            float tau, int g, int blk, int nblk, float (&hm)[4],
+                                            const ZhaLevelArgs* pa = nullptr) {
     // every argument the kernel uses, fetched in one batch before any of them is
     // needed (otherwise the loads come in dependent rounds behind uniform branches)
     asm volatile("" ::"s"(q), "s"(a.S), "s"(a.B), "s"(a.cap), "s"(a.top), "s"(a.n_top), "s"(a.pklist),
@@ -87,10 +156,33 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     // count) and the query rows are all in flight together.  At the first routed
     // level the parent arrays point at readable memory whose values go unused.
     int it = blk * 4 + wave;
-    const int pi0 = min((int)zha_div((uint32_t)(it * U + cl), a.dc), pcap - 1);
-    int32_t pk = a.pklist[prow + pi0];
-    uint32_t pm = a.pkmask[prow + pi0];
-    const int pn_raw = a.pnkept[g];
+    int32_t pk = 0;
+    uint32_t pm = 0;
+    int pn_raw = 0;
+    uint64_t dw[DEF ? kDeferW : 1];
+    int32_t dg[DEF ? kDeferP : 1];
+    if (DEF) {
+        // the level above's head words, its parents' node ids and their count
+        const int nall = G * (int)pa->wcap;
+        const uint64_t* kb = pa->kbm + (size_t)g * G * pa->wcap;
+#pragma unroll
+        for (int k = 0; k < kDeferW; ++k) {
+            const int i = (int)threadIdx.x + k * kScoreThreads;
+            dw[k] = i < nall ? kb[i] : 0ull;
+        }
+        const int gcap = pa->top ? 0 : (int)pa->pcap;
+#pragma unroll
+        for (int k = 0; k < kDeferP; ++k) {
+            const int i = (int)threadIdx.x + k * kScoreThreads;
+            dg[k] = i < gcap ? pa->pklist[(size_t)g * pa->pcap + i] : 0;
+        }
+        pn_raw = pa->pnkept[g];
+    } else {
+        const int pi0 = min((int)zha_div((uint32_t)(it * U + cl), a.dc), pcap - 1);
+        pk = a.pklist[prow + pi0];
+        pm = a.pkmask[prow + pi0];
+        pn_raw = a.pnkept[g];
+    }
     // A operand: row = query head j of the group (zero beyond G), contraction index
     // d = 16m + 4kq + e.
     float qa[32];
@@ -116,6 +208,83 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     asm volatile("" ::"v"(pk), "v"(pm), "s"(pn_raw), "v"(qa[0]), "v"(qa[31]));
 #pragma unroll
     for (int k = 0; k < 32; ++k) qa[k] = j < G ? qa[k] : 0.f;
+    DeferView dv{};
+    if constexpr (DEF) {
+        extern __shared__ __align__(16) uint64_t zha_defer_lds[];
+        __shared__ uint32_t s_wsum[kScoreThreads / 64];
+        const int tid = threadIdx.x;
+        const int wc = (int)pa->wcap, nall = G * wc;
+        const int gcap = pa->top ? 0 : (int)pa->pcap;
+        uint64_t* hw = zha_defer_lds;
+        uint64_t* uu = hw + nall;
+        uint32_t* pre = reinterpret_cast<uint32_t*>(uu + wc);
+        int32_t* gk = reinterpret_cast<int32_t*>(pre + wc);
+        const int gn = pa->top ? 0 : pn_raw;
+        const int nl = pa->top ? (int)pa->n_top : gn * c + (int)(pa->orph_hi - pa->orph_lo);
+        const int nwl = (nl + 63) >> 6;
+#pragma unroll
+        for (int k = 0; k < kDeferW; ++k) {
+            const int i = tid + k * kScoreThreads;
+            if (i < nall) hw[i] = dw[k];
+        }
+#pragma unroll
+        for (int k = 0; k < kDeferP; ++k) {
+            const int i = tid + k * kScoreThreads;
+            if (i < gcap) gk[i] = dg[k];
+        }
+        __syncthreads();
+        // union of words [tid P, tid P + P) (words from nwl on hold no candidate),
+        // then the workgroup's exclusive popcount prefix
+        const int P = (wc + kScoreThreads - 1) / kScoreThreads;
+        uint32_t cnt = 0;
+#pragma unroll 1
+        for (int k = 0; k < P; ++k) {
+            const int w = tid * P + k;
+            uint64_t x = 0;
+            if (w < nwl)
+                for (int hh = 0; hh < G; ++hh) x |= hw[hh * wc + w];
+            if (w < wc) uu[w] = x;
+            cnt += (uint32_t)__popcll(x);
+        }
+        const uint32_t inc = (uint32_t)zha_wave_incl_scan_u64(cnt);
+        if (lane == 63) s_wsum[wave] = inc;
+        __syncthreads();
+        uint32_t run = inc - cnt, tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kScoreThreads / 64; ++w2) {
+            const uint32_t x = s_wsum[w2];
+            run += w2 < wave ? x : 0u;
+            tot += x;
+        }
+#pragma unroll 1
+        for (int k = 0; k < P; ++k) {
+            const int w = tid * P + k;
+            if (w < wc) {
+                pre[w] = run;
+                run += (uint32_t)__popcll(uu[w]);
+            }
+        }
+        __syncthreads();
+        dv = DeferView{hw, uu, pre, gk, wc, nwl, gn};
+        // this workgroup's share of the level above's kept list: words 4 blk + wave
+        // + 4 nblk k, one position per lane
+        int32_t* kl = pa->klist + (size_t)g * pa->cap;
+        uint32_t* km = pa->kmask + (size_t)g * pa->cap;
+#pragma unroll 1
+        for (int w = blk * 4 + wave; w < nwl; w += 4 * nblk) {
+            const uint64_t x = uu[w];
+            if (lane_bit(x, lane)) {
+                int32_t node;
+                uint32_t msk;
+                defer_node(*pa, dv, G, c, w * 64 + lane, node, msk);
+                const uint32_t rank = pre[w] + bits_below_lane(x);
+                kl[rank] = node;
+                km[rank] = msk;
+            }
+        }
+        if (blk == 0 && tid == 0) pa->nkept[g] = (int32_t)tot;
+        pn_raw = (int)tot;
+    }
     if (top) {
         pk = 0;
         pm = allg;
@@ -138,14 +307,16 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
                 cm = allg;
             } else if (pos < pn * c) {
                 // child pos % c of the kept parent at index pos / c
-                node = pk * c + (pos - (int)zha_div((uint32_t)pos, a.dc) * c);
+                const int pi = (int)zha_div((uint32_t)pos, a.dc);
+                if (DEF) defer_entry(*pa, dv, G, c, (uint32_t)pi, pk, pm);
+                node = pk * c + (pos - pi * c);
                 cm = pm;
             } else {
                 node = (int32_t)a.orph_lo + (pos - pn * c);
                 cm = allg;
             }
         }
-        if (!top) {
+        if (!DEF && !top) {
             // parent entry of this wave's next item, in flight with this item's planes
             const int npi = (int)zha_div((uint32_t)((it + stride) * U + cl), a.dc);
             if (it + stride < items && npi < pn) {
@@ -203,6 +374,24 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     }
 }
 
+// Sliced levels: the largest score of each head over this workgroup.
+__device__ __forceinline__ void block_head_max(const ZhaLevelArgs& a, int g, int G, const float (&hm)[4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, kq = lane >> 4;
+    __shared__ float s_hm[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x = zha_row16_max(hm[i]);
+        if (j == 0) s_hm[wave][4 * kq + i] = x;
+    }
+    __syncthreads();
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        const float x = fmaxf(fmaxf(s_hm[0][h], s_hm[1][h]), fmaxf(s_hm[2][h], s_hm[3][h]));
+        a.hblk[(size_t)(g * G + h) * ZHA_SCORE_MAXB + blockIdx.x] = x;
+    }
+}
+
 // grid (blocks, H_kv), 256 threads: one level's candidate scores.
 template <bool BF16>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const void* __restrict__ q,
@@ -211,23 +400,21 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
     const int g = blockIdx.y;
     float hm[4];
     score_level<BF16, false>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm);
-    if (a.hblk) {
-        // sliced levels: the largest score of each head over this block
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int j = lane & 15, kq = lane >> 4;
-        __shared__ float s_hm[4][16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x = zha_row16_max(hm[i]);
-            if (j == 0) s_hm[wave][4 * kq + i] = x;
-        }
-        __syncthreads();
-        if (threadIdx.x < G) {
-            const int h = threadIdx.x;
-            const float x = fmaxf(fmaxf(s_hm[0][h], s_hm[1][h]), fmaxf(s_hm[2][h], s_hm[3][h]));
-            a.hblk[(size_t)(g * G + h) * ZHA_SCORE_MAXB + blockIdx.x] = x;
-        }
-    }
+    if (a.hblk) block_head_max(a, g, G, hm);
+}
+
+// As zha_route_score_kernel, for a level whose parent level (pa) was selected but
+// not merged: the workgroups derive and write that level's kept list themselves
+// (dynamic LDS: zha_defer_lds_bytes).
+template <bool BF16>
+__global__ __launch_bounds__(kScoreThreads) void zha_route_score_defer_kernel(const void* __restrict__ q,
+                                                                              ZhaLevelArgs a, ZhaLevelArgs pa,
+                                                                              int G, int c, int R, float tau) {
+    ZHA_LEVEL_ARGS_READY(pa, "s"(G));
+    const int g = blockIdx.y;
+    float hm[4];
+    score_level<BF16, false, true>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm, &pa);
+    if (a.hblk) block_head_max(a, g, G, hm);
 }
 
 // grid (max blocks, H_kv, levels), 256 threads: every node of each of the first
@@ -336,14 +523,6 @@ static_assert(kMergeW <= kSelThreads, "merge: one thread per word of a step");
 static_assert(ZHA_MAX_GROUP * (kSmallN + 2 * 256) + kSmallN <= kLdsKeys, "small path inside the key buffer");
 static_assert(ZHA_MAX_GROUP * kSmallK <= kHistPadded, "small-path kept words inside the histogram");
 
-// Bit `lane` of a 64-bit word, and the number of set bits below it.
-__device__ __forceinline__ uint32_t lane_bit(uint64_t w, int lane) {
-    const uint32_t h = lane < 32 ? (uint32_t)w : (uint32_t)(w >> 32);
-    return (h >> (lane & 31)) & 1u;
-}
-__device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
-}
 
 // Small-path histogram bins pack a key count above a mass sum: at most kSmallN
 // keys of mass <= 2^40 sum below 2^52, so the fields never carry into each other
@@ -1479,14 +1658,35 @@ int zha_score_blocks(int64_t max_cand, int R) {
     return (int)blocks;
 }
 
+bool zha_defer_fits(int G, int64_t wcap, int64_t pcap) {
+    return (int64_t)G * wcap <= ZHA_DEFER_WORDS && pcap <= ZHA_DEFER_PARENTS;
+}
+
+size_t zha_defer_lds_bytes(int G, int64_t wcap, int64_t pcap) {
+    return sizeof(uint64_t) * (size_t)(G + 1) * (size_t)wcap + sizeof(uint32_t) * (size_t)wcap +
+           sizeof(int32_t) * (size_t)pcap;
+}
+
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
-                                  int R, float tau, int blocks, hipStream_t stream) {
+                                  int R, float tau, int blocks, hipStream_t stream, const ZhaLevelArgs* defer) {
     if (a.hblk) {
         hipLaunchKernelGGL(zha_huge_init_kernel, dim3((unsigned)(H_kv * G)), dim3(kHugeThreads), 0, stream, a, H_kv * G);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     dim3 grid((unsigned)blocks, (unsigned)H_kv);
+    if (defer) {
+        const int64_t pcap = defer->top ? 0 : defer->pcap;
+        if (a.top || defer->hblk || !zha_defer_fits(G, defer->wcap, pcap)) return hipErrorInvalidValue;
+        const size_t lds = zha_defer_lds_bytes(G, defer->wcap, pcap);
+        if (kv_dtype == 0)
+            hipLaunchKernelGGL(zha_route_score_defer_kernel<true>, grid, dim3(kScoreThreads), lds, stream, q, a, *defer,
+                               G, c, R, tau);
+        else
+            hipLaunchKernelGGL(zha_route_score_defer_kernel<false>, grid, dim3(kScoreThreads), lds, stream, q, a,
+                               *defer, G, c, R, tau);
+        return hipGetLastError();
+    }
     if (kv_dtype == 0)
         hipLaunchKernelGGL(zha_route_score_kernel<true>, grid, dim3(kScoreThreads), 0, stream, q, a, G, c, R, tau);
     else
@@ -1513,7 +1713,8 @@ hipError_t zha_launch_route_chain(int kv_dtype, const void* q, const ZhaChainArg
     return hipGetLastError();
 }
 
-hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream) {
+hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream,
+                                   bool merge) {
     if (a.cap <= kSmallN) {
         hipLaunchKernelGGL(zha_select_small_kernel, dim3((unsigned)H_kv), dim3(kSelThreads), 0, stream, a, G, c,
                            top_p);
@@ -1543,7 +1744,7 @@ hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c
     hipLaunchKernelGGL(zha_select_large_kernel, dim3((unsigned)(H_kv * G)), dim3(kSelThreads), 0, stream, a, G,
                        c, top_p, 0);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !merge) return e;   // without merge: the next level's score kernel derives the list
     // bitmap words per merge block: a multiple of 16, at most kMergeW, over at
     // least kMergeBlocks blocks when the level is large enough
     const int64_t wcap = a.wcap;

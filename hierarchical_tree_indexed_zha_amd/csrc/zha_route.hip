@@ -266,23 +266,6 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
         }
         __syncthreads();
         dv = DeferView{hw, uu, pre, gk, wc, nwl, gn};
-        // this workgroup's share of the level above's kept list: words 4 blk + wave
-        // + 4 nblk k, one position per lane
-        int32_t* kl = pa->klist + (size_t)g * pa->cap;
-        uint32_t* km = pa->kmask + (size_t)g * pa->cap;
-#pragma unroll 1
-        for (int w = blk * 4 + wave; w < nwl; w += 4 * nblk) {
-            const uint64_t x = uu[w];
-            if (lane_bit(x, lane)) {
-                int32_t node;
-                uint32_t msk;
-                defer_node(*pa, dv, G, c, w * 64 + lane, node, msk);
-                const uint32_t rank = pre[w] + bits_below_lane(x);
-                kl[rank] = node;
-                km[rank] = msk;
-            }
-        }
-        if (blk == 0 && tid == 0) pa->nkept[g] = (int32_t)tot;
         pn_raw = (int)tot;
     }
     if (top) {
@@ -291,7 +274,6 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     }
     const int pn = top ? 0 : pn_raw;
     const int n_cand = top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (blk == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
 
     const int items = (n_cand + U - 1) / U;
 #pragma unroll
@@ -371,6 +353,28 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
             for (int i = 0; i < 4; ++i)
                 if ((cm >> (4 * kq + i)) & 1u) hm[i] = fmaxf(hm[i], best[i]);
         }
+    }
+    // Stores issued before the loop would hold up its first loads (the memory
+    // counter waits are in order), so the counts and the derived kept list go last.
+    if (blk == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
+    if constexpr (DEF) {
+        // this workgroup's share of the level above's kept list: words 4 blk + wave
+        // + 4 nblk k, one position per lane
+        int32_t* kl = pa->klist + (size_t)g * pa->cap;
+        uint32_t* km = pa->kmask + (size_t)g * pa->cap;
+#pragma unroll 1
+        for (int w = blk * 4 + wave; w < dv.nw; w += 4 * nblk) {
+            const uint64_t x = dv.u[w];
+            if (lane_bit(x, lane)) {
+                int32_t node;
+                uint32_t msk;
+                defer_node(*pa, dv, G, c, w * 64 + lane, node, msk);
+                const uint32_t rank = dv.pre[w] + bits_below_lane(x);
+                kl[rank] = node;
+                km[rank] = msk;
+            }
+        }
+        if (blk == 0 && threadIdx.x == 0) pa->nkept[g] = pn;
     }
 }
 
@@ -455,8 +459,10 @@ __device__ __forceinline__ uint32_t key_of(float s, float m) {
 __device__ __forceinline__ uint64_t mass_of(uint32_t key) {
     // e^{-delta} with delta = key * 2^-27, as 2^40-scaled fixed point truncated to
     // an integer.  x <= 2^40 has 24 significant bits, so x = hi * 2^32 + lo with
-    // both parts exact.
-    const float x = exp2f(-(float)key * (1.4426950408889634f / kKeyScale)) * kFix;
+    // both parts exact.  The exponent lies in [-46.2, 0] for every 32-bit key,
+    // where the hardware exp2 is what exp2f returns (exp2f only rescales
+    // arguments below -126).
+    const float x = __builtin_amdgcn_exp2f(-(float)key * (1.4426950408889634f / kKeyScale)) * kFix;
     const float hi = floorf(x * 0x1p-32f);
     const float lo = fmaf(hi, -0x1p32f, x);
     return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
@@ -938,47 +944,75 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
             for (int j = 0; j < kGlobBatch; ++j) m = fmaxf(m, xs[j]);
         }
     }
+    // the first pass's histogram, cleared before the barrier below
+    for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
     m = zha_wave_max(m);
     if (lane == 0) swf[wave] = m;
     __syncthreads();
     m = swf[0];
 #pragma unroll
     for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, swf[w]);
-    if (staged) {
-#pragma unroll
-        for (int k = 0; k < kSlots; ++k)
-            if (k < nslot) keys[tid + k * kSelThreads] = key_of(__uint_as_float(kr[k]), m);
-    }
 
     // Kept rule: keep_all, or key < ustar, or key == ustar when that key is unique.
     const bool none = m == zha_neg_inf();        // this head has no candidate at this level
     const bool keep_all = !none && top_p >= 1.0f;
+    const bool cut = !none && !keep_all;
+    if (staged) {
+        // keys to LDS and, when there is a cut to find, the first digit pass in the
+        // same loop: every key's mass into its top-digit bin, a key without mass
+        // adding zero to its lane's unused padding entry (33 lane + 32, never read)
+        const int dummy = 33 * lane + 32;
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            if (k < nslot) {
+                const uint32_t key = key_of(__uint_as_float(kr[k]), m);
+                keys[tid + k * kSelThreads] = key;
+                if (cut) {
+                    const bool has = key < kNoMass;
+                    const int at = has ? hpad((key >> 21) & 2047u) : dummy;
+                    const uint64_t ms = has ? mass_of(key) : 0ull;
+                    atomicAdd((unsigned long long*)&hist[at], (unsigned long long)ms);
+                }
+            }
+        }
+    }
     uint32_t ustar = 0, ties = 0;
     uint64_t need = 0;
-    if (!none && !keep_all) {
+    if (cut) {
         uint32_t mshift = 31, mval = 0, bshift = 21, bmask = 2047;
-        for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
-        for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
-        __syncthreads();
 #pragma unroll 1
         for (int pass = 0; pass < 3; ++pass) {
             // pass 0 adds the mass of every key that carries mass; later passes count
             // and add only the keys whose higher digits equal the bins found so far
             const bool all = pass == 0;
             if (staged) {
-                // keys read from LDS kBatch slots at a time (all reads in flight together)
+                // pass 0 went with the staging; later passes read the keys from LDS
+                // kBatch slots at a time (all reads in flight together), test a batch
+                // first and touch the histogram only for the few keys that match
 #pragma unroll 1
-                for (int k0 = 0; k0 < nslot; k0 += kBatch) {
+                for (int k0 = 0; k0 < (all ? 0 : nslot); k0 += kBatch) {
                     uint32_t kk[kBatch];
 #pragma unroll
                     for (int j = 0; j < kBatch; ++j) kk[j] = keys[tid + ((k0 + j) & (kSlots - 1)) * kSelThreads];
+                    {
+                        uint32_t hit = 0;
 #pragma unroll
-                    for (int j = 0; j < kBatch; ++j) {
-                        const uint32_t key = k0 + j < nslot ? kk[j] : kNotCand;
-                        if (key < kNoMass && (all || (key >> mshift) == mval)) {
-                            const uint32_t b = (key >> bshift) & bmask;
-                            atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
-                            if (!all) atomicAdd(&cntb[b], 1u);
+                        for (int j = 0; j < kBatch; ++j) {
+                            const uint32_t key = kk[j];
+                            const bool mt = k0 + j < nslot && key < kNoMass && (key >> mshift) == mval;
+                            hit |= (uint32_t)mt << j;
+                        }
+                        if (hit) {
+#pragma unroll
+                            for (int j = 0; j < kBatch; ++j) {
+                                if ((hit >> j) & 1u) {
+                                    const uint32_t key = kk[j];
+                                    const uint32_t b = (key >> bshift) & bmask;
+                                    atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
+                                    atomicAdd(&cntb[b], 1u);
+                                }
+                            }
                         }
                     }
                 }

@@ -54,6 +54,18 @@ __device__ __forceinline__ int lane_tid() {
 
 __device__ __forceinline__ uint32_t all_heads(int G) { return G >= 32 ? 0xFFFFFFFFu : ((1u << G) - 1u); }
 
+// Kept parents of group g (0 at the first routed level, whose parent pointer is
+// readable memory with an unused value), read after every read the caller issued
+// before it so that all of them share one round trip: left alone, the compiler
+// waits for a load whose value it needs in a scalar register right where it
+// issues it, ahead of everything else, and sinks reads used only past an early
+// return below that wait.
+__device__ __forceinline__ int parent_count(const ZhaLevelArgs& a, int g) {
+    int raw = a.pnkept[g];
+    asm volatile("" : "+v"(raw)::"memory");
+    return a.top ? 0 : __builtin_amdgcn_readfirstlane(raw);
+}
+
 // Bit `lane` of a 64-bit word, and the number of set bits below it.
 __device__ __forceinline__ uint32_t lane_bit(uint64_t w, int lane) {
     const uint32_t h = lane < 32 ? (uint32_t)w : (uint32_t)(w >> 32);
@@ -651,24 +663,25 @@ __device__ void select_head_wave(const float* sg, int n, float top_p, uint64_t* 
 }
 
 // Scores of all G heads at position tid (< cap) into LDS, and the node id of
-// that position; every global read is issued before any result is used.  `pn`
-// (kept parents) is only needed for the node id.
-__device__ __forceinline__ void stage_small(const ZhaLevelArgs& a, int g, int G, int c, int tid, int pn,
-                                            float* s_sig, int32_t* s_nid) {
+// that position; every global read, the parent count among them, is issued
+// before any result is used.  Returns the parent count.
+__device__ __forceinline__ int stage_small(const ZhaLevelArgs& a, int g, int G, int c, int tid,
+                                           float* s_sig, int32_t* s_nid) {
     const bool in = tid < a.cap;
     float v[ZHA_MAX_GROUP];
 #pragma unroll
     for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
         v[hh] = (hh < G && in) ? a.sig[((size_t)g * G + hh) * a.cap + tid] : zha_neg_inf();
     const int pi = (int)zha_div((uint32_t)tid, a.dc);
-    int32_t pk = 0;
-    if (!a.top && pi < a.pcap) pk = a.pklist[(size_t)g * a.pcap + pi];
+    const int32_t pk = pi < a.pcap ? a.pklist[(size_t)g * a.pcap + pi] : 0;   // unused at the first level
+    const int pn = parent_count(a, g);
 #pragma unroll
     for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
         if (hh < G) s_sig[hh * kSmallN + tid] = v[hh];
     int32_t node = tid;
     if (!a.top) node = tid < pn * c ? pk * c + (tid - pi * c) : (int32_t)a.orph_lo + (tid - pn * c);
     s_nid[tid] = node;
+    return pn;
 }
 
 // Small frontiers (n <= kSmallN candidates): one workgroup selects for all G
@@ -773,8 +786,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelA
 
     const int g = blockIdx.x;
     const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
-    const int pn = a.top ? 0 : a.pnkept[g];
-    stage_small(a, g, G, c, threadIdx.x, pn, s_sig, s_nid);
+    const int pn = stage_small(a, g, G, c, threadIdx.x, s_sig, s_nid);
     const int n = a.top ? (int)a.n_top : pn * c + n_orph;
     __syncthreads();
     select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw);
@@ -873,7 +885,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         float* s_sig = reinterpret_cast<float*>(keys);                                   // [G][kSmallN]
         uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
         int32_t* s_nid = reinterpret_cast<int32_t*>(keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256);
-        stage_small(a, g, G, c, tid, pn0, s_sig, s_nid);
+        stage_small(a, g, G, c, tid, s_sig, s_nid);
         __syncthreads();
         select_small_group(a, g, G, top_p, n0, s_sig, s_nid, s_hist, hist);
         return;
@@ -885,7 +897,6 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
     // together (one round trip, bounded by the capacity); the second half's reads,
     // bounded by the count, follow as soon as it arrives.  Positions >= n are
     // ignored afterwards.
-    const int pn = a.top ? 0 : a.pnkept[g];
     uint32_t kr[kSlots];
     const int lim = (int)min(a.cap, (int64_t)kLdsKeys);
 #pragma unroll
@@ -893,6 +904,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         const int pos = tid + k * kSelThreads;
         kr[k] = __float_as_uint(pos < lim ? sg[pos] : zha_neg_inf());
     }
+    const int pn = parent_count(a, g);
     const int n = a.top ? (int)a.n_top : pn * c + n_orph;
     {
         const int lim2 = min(lim, n);
@@ -910,7 +922,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
         int32_t* s_nid = reinterpret_cast<int32_t*>(keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256);
         uint64_t* s_kw = hist;                                                           // [kSmallK][16]
-        stage_small(a, g, G, c, tid, pn, s_sig, s_nid);
+        stage_small(a, g, G, c, tid, s_sig, s_nid);
         __syncthreads();
         select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw);
         return;
@@ -1179,7 +1191,6 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
 
     constexpr int kPerW = ZHA_MAX_GROUP * kMergeW / kSelThreads;
     constexpr int kPerP = kMergeW * 32 / kSelThreads;
-    const int pn = a.top ? 0 : a.pnkept[g];
     uint64_t hv[kPerW];
     int32_t pv[kPerP];
     uint64_t pw[ZHA_MAX_GROUP];
@@ -1196,16 +1207,13 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
     }
     const bool chunked = a.chunk_cnt != nullptr;   // sliced level: kept counts per 512-word chunk
     const int nch = (wcap + kMergeW - 1) / kMergeW;
-    uint32_t cc = 0;
-    if (chunked) {
+    // (one straight-line block of reads: a branch here makes the compiler wait for
+    // every read before the two paths join; a sliced level reads its chunk counts
+    // after the early return)
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) pw[hh] = 0ull;
-        if (tid < w0 / kMergeW) cc = a.chunk_cnt[(size_t)g * nch + tid];
-    } else {
-#pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-            pw[hh] = (hh < G && tid < w0) ? gbm[(size_t)hh * a.wcap + tid] : 0ull;
-    }
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        pw[hh] = (!chunked && hh < G && tid < w0) ? gbm[(size_t)hh * a.wcap + tid] : 0ull;
+    const int pn = parent_count(a, g);
 
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
     if (n <= kSmallN) return;                    // selected and merged by the select kernel
@@ -1221,9 +1229,8 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
     // rank offset: kept nodes in words [0, w0)
     uint32_t cnt = 0;
     if (chunked) {
-        cnt = cc;
 #pragma unroll 1
-        for (int i = tid + kSelThreads; i < w0 / kMergeW; i += kSelThreads) cnt += a.chunk_cnt[(size_t)g * nch + i];
+        for (int i = tid; i < w0 / kMergeW; i += kSelThreads) cnt += a.chunk_cnt[(size_t)g * nch + i];
     } else {
         uint64_t u = 0;
 #pragma unroll

@@ -343,53 +343,68 @@ __global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BL
     }
 }
 
-// grid (H_q, 128 / 32), 256 threads = 8 partial lanes x 32 columns:
+// grid (H_q, 128 / 32), NT threads = NT / 32 partial lanes x 32 columns, NT >= Bg
+// (256, or ZHA_ATTN_MAXB for wider splits):
 // out[h][d] = sum_b O_b[d] 2^(m_b - M) / sum_b l_b 2^(m_b - M).
-constexpr int kCombThreads = 256;
-__global__ __launch_bounds__(kCombThreads) void zha_combine_kernel(ZhaAttnArgs a, int G, int Bg,
-                                                                   float* __restrict__ out) {
+// Every read (the partial count, and each partial's m, l and columns, bounded by
+// the launch's Bg and masked by the count afterwards) goes out in one batch: one
+// memory round trip.  Partials at or beyond the count are never combined
+// arithmetically (their memory may hold anything), only selected away.
+template <int NT>
+__global__ __launch_bounds__(NT) void zha_combine_kernel(ZhaAttnArgs a, int G, int Bg, float* __restrict__ out) {
+    constexpr int kWv = NT / 64;
+    constexpr int kLanes = NT / 32;        // partial lanes of the column pass
+    constexpr int kPerO = NT / kLanes;     // columns (partials) per thread: 32
+    static_assert(NT <= ZHA_ATTN_MAXB && kPerO * kLanes == NT, "combine split");
     ZHA_ATTN_ARGS_READY(a, "s"(G), "s"(Bg), "s"(out));
-    __shared__ float f[ZHA_ATTN_MAXB];
-    __shared__ float red[kCombThreads];
+    __shared__ float f[NT];
+    __shared__ float red[NT];
+    __shared__ float wred[2][kWv];
     const int h = blockIdx.x, g = h / G, hl = h - g * G, tid = threadIdx.x;
-    const int n = a.nact[g];
-    const size_t base = (size_t)g * Bg * G + hl;          // partial b of head h at base + b*G
-    float m = zha_neg_inf();
-    for (int b = tid; b < n; b += kCombThreads) m = fmaxf(m, a.pm[base + (size_t)b * G]);
-    red[tid] = m;
-    __syncthreads();
-    for (int o = kCombThreads / 2; o > 0; o >>= 1) {
-        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
-    float l = 0.f;
-    for (int b = tid; b < n; b += kCombThreads) {
-        const float mb = a.pm[base + (size_t)b * G];
-        const float fb = mb == zha_neg_inf() ? 0.f : exp2f(mb - M);
-        f[b] = fb;
-        l = fmaf(a.pl[base + (size_t)b * G], fb, l);
-    }
-    red[tid] = l;
-    __syncthreads();
-    for (int o = kCombThreads / 2; o > 0; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
-    }
-    const float L = red[0];
-    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
     const int dd = tid & 31, bl = tid >> 5;
     const int d = blockIdx.y * 32 + dd;
+    const size_t base = (size_t)g * Bg * G + hl;          // partial b of head h at base + b*G
+    // partial tid's m and l; columns d of partials bl + kLanes j
+    const float mb = tid < Bg ? a.pm[base + (size_t)tid * G] : zha_neg_inf();
+    const float lb = tid < Bg ? a.pl[base + (size_t)tid * G] : 0.f;
+    float ov[kPerO];
+#pragma unroll
+    for (int j = 0; j < kPerO; ++j) {
+        const int b = bl + j * kLanes;
+        ov[j] = b < Bg ? a.po[(base + (size_t)b * G) * ZHA_D + d] : 0.f;
+    }
+    int nraw = a.nact[g];
+    asm volatile("" : "+v"(nraw)::"memory");
+    const int n = __builtin_amdgcn_readfirstlane(nraw);
+
+    const bool live = tid < n && mb != zha_neg_inf();
+    float m = zha_wave_max(live ? mb : zha_neg_inf());
+    if (lane == 0) wred[0][wave] = m;
+    __syncthreads();
+    float M = wred[0][0];
+#pragma unroll
+    for (int w = 1; w < kWv; ++w) M = fmaxf(M, wred[0][w]);
+    const float fb = live ? exp2f(mb - M) : 0.f;
+    f[tid] = fb;
+    const float l = zha_wave_sum(live ? lb * fb : 0.f);
+    if (lane == 0) wred[1][wave] = l;
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWv; ++w) L += wred[1][w];
     float acc = 0.f;
-#pragma unroll 4
-    for (int b = bl; b < n; b += kCombThreads / 32) acc = fmaf(a.po[(base + (size_t)b * G) * ZHA_D + d], f[b], acc);
+#pragma unroll
+    for (int j = 0; j < kPerO; ++j) {
+        const int b = bl + j * kLanes;
+        acc = b < n ? fmaf(ov[j], f[b], acc) : acc;
+    }
     red[tid] = acc;
     __syncthreads();
     if (bl == 0) {
         float t = 0.f;
 #pragma unroll
-        for (int k = 0; k < kCombThreads / 32; ++k) t += red[k * 32 + dd];
+        for (int k = 0; k < kLanes; ++k) t += red[k * 32 + dd];
         out[(size_t)h * ZHA_D + d] = t / L;
     }
 }
@@ -420,7 +435,11 @@ hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, 
 }
 
 hipError_t zha_launch_combine(const ZhaAttnArgs& a, int H_kv, int G, int Bg, float* out, hipStream_t stream) {
-    hipLaunchKernelGGL(zha_combine_kernel, dim3((unsigned)(H_kv * G), ZHA_D / 32), dim3(kCombThreads), 0, stream, a, G,
-                       Bg, out);
+    if (Bg < 1 || Bg > ZHA_ATTN_MAXB) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(H_kv * G), ZHA_D / 32);
+    if (Bg <= 256)
+        hipLaunchKernelGGL(zha_combine_kernel<256>, grid, dim3(256), 0, stream, a, G, Bg, out);
+    else
+        hipLaunchKernelGGL(zha_combine_kernel<ZHA_ATTN_MAXB>, grid, dim3(ZHA_ATTN_MAXB), 0, stream, a, G, Bg, out);
     return hipGetLastError();
 }

@@ -427,10 +427,12 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     at_.V = bufs->v;
     at_.cap_tok = cfg->capacity;
     at_.q = q;
-    at_.klist = top >= 1 ? (const int32_t*)(X + y.klist[1]) : nullptr;
-    at_.kmask = top >= 1 ? (const uint32_t*)(X + y.kmask[1]) : nullptr;
-    at_.nkept = top >= 1 ? (const int32_t*)(X + y.nkept[1]) : nullptr;
-    at_.cap1 = y.cap[1];
+    // the level-1 lists are readable even when no level is routed (cap1 = 0 then
+    // says they hold nothing)
+    at_.klist = (const int32_t*)(X + y.klist[1]);
+    at_.kmask = (const uint32_t*)(X + y.kmask[1]);
+    at_.nkept = (const int32_t*)(X + y.nkept[1]);
+    at_.cap1 = top >= 1 ? y.cap[1] : 0;
     at_.n_tokens = n_tokens;
     at_.pm = (float*)(X + y.pm);
     at_.pl = (float*)(X + y.pl);

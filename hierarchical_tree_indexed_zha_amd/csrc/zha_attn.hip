@@ -12,9 +12,13 @@
 // which of the group's query heads selected it.
 //
 // Slot space of a group (32-slot tiles):
-//   [0, nk*c)           kept chunks in ascending order; token 0 is masked here
-//   [nk*c]              token 0 for every head (when chunk 0 is complete)
-//   [..., total)        the tail tokens, every head
+//   [0]                 token 0 for every head (when chunk 0 is complete)
+//   [sink, lead)        the tail tokens, every head
+//   [lead, total)       kept chunks in ascending order; token 0 is masked here
+// The lead (sink and tail) depends on N alone, so a slot's token is known before
+// the kept count arrives.  Wave w of block b takes tiles 4b + w, then every
+// 4 nact-th tile after it: its first tile's kept-list entries are read together
+// with the count (one memory round trip), and only the later tiles wait for it.
 //
 // bf16 path: QK^T and PV run on v_mfma_f32_16x16x32_bf16 with the group's
 // heads as the 16 MFMA rows.  V stays in its row-major layout: a lane loads 16
@@ -47,57 +51,71 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int i) {
 }
 
 struct Slots {
-    int64_t nk, total, tail_start;
+    int64_t lead, total, tail_start;   // total: known once the kept count is
     int sink;
 };
 
+// The slot space's lead (from N alone); total is set from the kept count later.
 template <bool DENSE>
-__device__ __forceinline__ Slots slot_space(const ZhaAttnArgs& a, int g, int c) {
+__device__ __forceinline__ Slots slot_lead(const ZhaAttnArgs& a, int c) {
     Slots s;
     if (DENSE) {
-        s.nk = 0;
         s.sink = 0;
         s.tail_start = 0;
+        s.lead = 0;
         s.total = a.n_tokens;
     } else {
-        s.nk = a.klist ? (int64_t)a.nkept[g] : 0;
         const int64_t n1 = a.n_tokens / c;
         s.tail_start = (int64_t)c * n1;
         s.sink = n1 > 0 ? 1 : 0;
-        s.total = s.nk * c + s.sink + (a.n_tokens - s.tail_start);
+        s.lead = s.sink + (a.n_tokens - s.tail_start);
+        s.total = s.lead;
     }
     return s;
 }
 
+// Token and head mask of a slot, whatever the kept count (a slot at or beyond
+// the total is masked by the caller).  Branch-free, with both kept-list reads
+// issued together: a kept-chunk slot outside the list's capacity (cap1 = 0 when
+// no level is routed) reads the group's first entry and is masked.
+// In two halves, so that a caller can issue the reads and use them later:
+// slot_fetch reads the kept-list entry, slot_finish forms the token and mask.
+struct SlotRaw {
+    int32_t kn;
+    uint32_t km;
+};
 template <bool DENSE>
-__device__ __forceinline__ void slot_to_token(const ZhaAttnArgs& a, const Slots& s, int g, int c, uint32_t allg,
-                                              int64_t slot, int32_t* tok, uint32_t* msk) {
-    if (slot >= s.total) {
-        *tok = 0;
-        *msk = 0u;
-        return;
+__device__ __forceinline__ SlotRaw slot_fetch(const ZhaAttnArgs& a, const Slots& s, int g, int c, int64_t slot) {
+    SlotRaw r{0, 0u};
+    if (!DENSE) {
+        const bool chunk = slot >= s.lead;
+        const int64_t e = chunk ? (slot - s.lead) / c : 0;
+        const size_t idx = (size_t)g * a.cap1 + (size_t)((chunk && e < a.cap1) ? e : 0);
+        r.kn = a.klist[idx];
+        r.km = a.kmask[idx];
     }
+    return r;
+}
+template <bool DENSE>
+__device__ __forceinline__ void slot_finish(const ZhaAttnArgs& a, const Slots& s, int c, uint32_t allg, int64_t slot,
+                                            const SlotRaw& r, int32_t* tok, uint32_t* msk) {
     if (DENSE) {
         *tok = (int32_t)slot;
         *msk = allg;
         return;
     }
-    const int64_t kc = s.nk * c;
-    if (slot < kc) {
-        const int64_t e = slot / c;
-        const int64_t t = (int64_t)a.klist[(size_t)g * a.cap1 + e] * c + (slot - e * c);
-        *tok = (int32_t)t;
-        *msk = t == 0 ? 0u : a.kmask[(size_t)g * a.cap1 + e];
-        return;
-    }
-    const int64_t r = slot - kc;
-    if (s.sink && r == 0) {
-        *tok = 0;
-        *msk = allg;
-        return;
-    }
-    *tok = (int32_t)(s.tail_start + r - s.sink);
-    *msk = allg;
+    const bool chunk = slot >= s.lead;
+    const int64_t e = chunk ? (slot - s.lead) / c : 0;
+    const bool ok = chunk && e < a.cap1;
+    const int64_t t = (int64_t)r.kn * c + (slot - s.lead - e * c);
+    const int32_t tail_tok = (s.sink && slot == 0) ? 0 : (int32_t)(s.tail_start + slot - s.sink);
+    *tok = chunk ? (ok ? (int32_t)t : 0) : tail_tok;
+    *msk = chunk ? ((ok && t != 0) ? r.km : 0u) : allg;
+}
+template <bool DENSE>
+__device__ __forceinline__ void slot_to_token(const ZhaAttnArgs& a, const Slots& s, int g, int c, uint32_t allg,
+                                              int64_t slot, int32_t* tok, uint32_t* msk) {
+    slot_finish<DENSE>(a, s, c, allg, slot, slot_fetch<DENSE>(a, s, g, c, slot), tok, msk);
 }
 
 __device__ __forceinline__ int active_blocks(int64_t tiles, int Bg) {
@@ -199,12 +217,12 @@ __global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BL
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, q4 = lane >> 4;
     const uint32_t allg = (G >= 32) ? 0xFFFFFFFFu : ((1u << G) - 1u);
-    const Slots sp = slot_space<DENSE>(a, g, c);
-    const int64_t tiles = (sp.total + kTileSlots - 1) / kTileSlots;
-    const int nact = active_blocks(tiles, Bg);
-    if (b == 0 && threadIdx.x == 0) a.nact[g] = nact;
-    if (b >= nact) return;
-    const int64_t t0 = tiles * b / nact, t1 = tiles * (b + 1) / nact;
+    Slots sp = slot_lead<DENSE>(a, c);
+    // this wave's first tile (4 b + wave, whatever the count): its slots' tokens
+    // are requested before the kept count is
+    const int64_t tw0 = (int64_t)b * kWaves + wave;
+    const int64_t slot0 = tw0 * kTileSlots + (lane & (kTileSlots - 1));
+    SlotRaw raw0 = slot_fetch<DENSE>(a, sp, g, c, slot0);
     const float scale = tau * kLog2e;                     // logits in log2 units
     float* s_p = s_buf + wave * 16 * 33;                  // [16 heads][33]
 
@@ -230,6 +248,27 @@ __global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BL
                 qa32[4 * m + e] = (j < G) ? static_cast<const float*>(a.q)[((size_t)g * G + j) * ZHA_D + 16 * m + 4 * q4 + e] : 0.f;
     }
 
+    // the kept count, read after every read above (one round trip for all of them)
+    // (the first tile's entries are used only after this point)
+    if (!DENSE) {
+        int nk_raw = a.nkept[g];
+        asm volatile("" : "+v"(nk_raw), "+v"(raw0.kn), "+v"(raw0.km)::"memory");
+        const int nk = a.cap1 > 0 ? __builtin_amdgcn_readfirstlane(nk_raw) : 0;
+        sp.total = sp.lead + (int64_t)nk * c;
+    }
+    const int64_t tiles = (sp.total + kTileSlots - 1) / kTileSlots;
+    const int nact = active_blocks(tiles, Bg);
+    if (b == 0 && threadIdx.x == 0) a.nact[g] = nact;
+    if (b >= nact) return;
+    const int64_t tstep = (int64_t)nact * kWaves;         // tiles of one round over the active waves
+    int32_t nx_tok = 0;
+    uint32_t nx_msk = 0;
+    slot_finish<DENSE>(a, sp, c, allg, slot0, raw0, &nx_tok, &nx_msk);
+    if (slot0 >= sp.total) {
+        nx_tok = 0;
+        nx_msk = 0u;
+    }
+
     float m_run[4], l_run[4];
     zha_f32x4 O[8];
 #pragma unroll
@@ -238,16 +277,18 @@ __global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BL
     for (int c8 = 0; c8 < 8; ++c8) O[c8] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
 
     // the slot -> token map of the next tile is fetched while this tile computes
-    int32_t nx_tok = 0;
-    uint32_t nx_msk = 0;
-    if (lane < kTileSlots && t0 + wave < t1)
-        slot_to_token<DENSE>(a, sp, g, c, allg, (t0 + wave) * kTileSlots + lane, &nx_tok, &nx_msk);
-    for (int64_t t = t0 + wave; t < t1; t += kWaves) {
+    for (int64_t t = tw0; t < tiles; t += tstep) {
         if (lane < kTileSlots) {
             s_tok[wave][lane] = nx_tok;
             s_msk[wave][lane] = nx_msk;
-            if (t + kWaves < t1)
-                slot_to_token<DENSE>(a, sp, g, c, allg, (t + kWaves) * kTileSlots + lane, &nx_tok, &nx_msk);
+            const int64_t ns = (t + tstep) * kTileSlots + lane;
+            if (t + tstep < tiles) {
+                slot_to_token<DENSE>(a, sp, g, c, allg, ns, &nx_tok, &nx_msk);
+                if (ns >= sp.total) {
+                    nx_tok = 0;
+                    nx_msk = 0u;
+                }
+            }
         }
         zha_wave_lds_sync();
 

@@ -138,10 +138,10 @@ struct ZhaAttnArgs {
     const void* V;
     int64_t cap_tok;
     const void* q;             // [H_q][128]
-    const int32_t* klist;      // kept level-1 chunks [H_kv][cap1] (sparse mode; nullptr = none)
+    const int32_t* klist;      // kept level-1 chunks [H_kv][cap1] (sparse mode: always readable)
     const uint32_t* kmask;
     const int32_t* nkept;      // [H_kv]
-    int64_t cap1;
+    int64_t cap1;              // 0 when no level is routed (the lists then hold nothing)
     int64_t n_tokens;
     float* pm;                 // [H_kv][Bg][G]
     float* pl;                 // [H_kv][Bg][G]

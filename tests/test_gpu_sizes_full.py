@@ -47,3 +47,24 @@ def test_full_size_ultra_one_group():
     ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label="ultra full",
                                  heads=[0, 5], groups=[0])
     say(f"[full] ultra: exempt heads {ex}/2, attention err {err:.2e}, score err {es:.2e}")
+
+
+def test_full_size_one_kv_group():
+    """light's full size with a single KV group of 8 query heads: the gather and
+    dense decode then split over more than 256 workgroups per group (the combine's
+    wide form, 512 partials at most)."""
+    import numpy as np
+    import oracle as O
+    from tests.gpu_util import ATOL
+    w = W.scaled(W.get("light"), W.get("light").n_tokens, steps=4, n_kv_heads=1, n_q_heads=8)
+    say(f"[full] light, one KV group: N={w.n_tokens}")
+    layer, x, n = _prepare(w)
+    kh, tree = oracle_tree(layer, n)
+    vh = to_host(layer.v)
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label="light one group")
+    out = layer.dense(x["q"][0]).clone()
+    torch.cuda.synchronize()
+    ref = O.dense_decode(to_host(x["q"][0]), kh, vh, n)
+    derr = float(np.abs(out.cpu().numpy() - ref).max())
+    say(f"[full] light one group: exempt heads {ex}/8, attention err {err:.2e}, dense err {derr:.2e}")
+    assert derr <= ATOL

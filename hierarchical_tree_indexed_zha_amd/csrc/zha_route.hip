@@ -24,12 +24,14 @@
 // reaches ceil(p * sum e).  Small frontiers (<= 1024 candidates per group) are
 // selected by one workgroup, one wave per head, with 8-bit digits; larger ones
 // by one 1024-thread workgroup per head with 11/11/10-bit digits, whose kept
-// flags go to a bitmap that the last head of the group to finish merges.
+// flags go to per-head bitmaps over the candidate positions.  A merge kernel, or
+// the next level's score kernel, turns the bitmaps into the group's kept list.
 //
 // The candidates of a level are never written out: they are the children of the
 // level above's kept nodes (kept list and head masks, ascending) followed by the
 // level's orphans, so a candidate's node id and head mask come from one read of
-// its parent's kept-list entry.
+// its parent's kept-list entry (or, below an unmerged level, from that level's
+// bitmaps staged in LDS).
 #include <algorithm>
 
 #include "zha_common.h"
@@ -857,9 +859,11 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainA
 }
 
 // grid (H_q), 1024 threads: levels with more than kSmallN node slots, one query
-// head per workgroup.  Up to kLdsKeys candidates the keys stay in registers
-// (positions tid + 1024 k); larger frontiers recompute them from the scores on
-// every pass.  The last head of a group to finish writes the group's kept list.
+// head per workgroup.  Up to kLdsKeys candidates the keys stay in LDS (position
+// tid + 1024 k in slot k); larger frontiers recompute them from the scores on
+// every pass.  Each head writes its kept bitmap; the kept list is formed later.
+// A frontier of at most kSmallN candidates is instead selected for every head,
+// and its kept list written, by the group's first workgroup (the small path).
 __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelArgs a, int G, int c,
                                                                        float top_p, int small_only) {
     ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(small_only));

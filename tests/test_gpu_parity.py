@@ -36,7 +36,8 @@ CASES = [
     ("light-c6@20001", _w("light", 20001, levels=4, chunk=6)),   # small frontiers only
     ("deep-c3@9000", _w("deep", 9000, levels=5, chunk=3)),       # R=16, orphans at several levels
     ("light-c5@50000", _w("light", 50000, levels=4, chunk=5)),   # level 1 takes the large select + merge
-    ("light@600000", _w("light", 600000, levels=4)),             # level 1 (75,000 slots) selects over slices
+    ("light@600000", _w("light", 600000, levels=4)),             # level 1 (75,000 slots): scores re-read per pass
+    ("light@131072-L2", _w("light", 131072, levels=2)),          # a large top level (2,048 nodes) left unmerged
 ]
 
 

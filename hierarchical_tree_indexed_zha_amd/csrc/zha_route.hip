@@ -403,7 +403,7 @@ __device__ __forceinline__ void block_head_max(const ZhaLevelArgs& a, int g, int
         if (j == 0) s_hm[wave][4 * kq + i] = x;
     }
     __syncthreads();
-    if (threadIdx.x < G) {
+    if ((int)threadIdx.x < G) {
         const int h = threadIdx.x;
         const float x = fmaxf(fmaxf(s_hm[0][h], s_hm[1][h]), fmaxf(s_hm[2][h], s_hm[3][h]));
         a.hblk[(size_t)(g * G + h) * ZHA_SCORE_MAXB + blockIdx.x] = x;

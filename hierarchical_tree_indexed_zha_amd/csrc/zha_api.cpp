@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -91,6 +92,7 @@ struct Layout {
     std::vector<int> slices;                               // 0 when the level is not sliced
     std::vector<int64_t> wcap;            // bitmap words per head per level
     size_t pm = 0, pl = 0, po = 0, nact = 0;
+    size_t noparent = 0;                  // readable, never written: the first routed level's parent arrays
     size_t scratch_bytes = 0;
     size_t dense_bytes = 0;
 };
@@ -153,6 +155,7 @@ Layout make_layout(const zha_config* cfg) {
         }
     }
     attn_partials(cfg, off, y.pm, y.pl, y.po, y.nact);
+    y.noparent = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(64, H));   // one entry per group
     y.scratch_bytes = off;
 
     size_t doff = 0, a, b, c, d;
@@ -391,12 +394,13 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             a.orph_lo = (int64_t)c * n_nodes(cfg, n_tokens, l + 1);
             a.orph_hi = n_nodes(cfg, n_tokens, l);
         } else {
-            // the first routed level has no parents: the parent arrays point at this
-            // level's own (readable; their values go unused), so that a kernel may
-            // issue its parent reads before it knows whether the level is the first
-            a.pklist = (const int32_t*)(X + y.klist[l]);
-            a.pkmask = (const uint32_t*)(X + y.kmask[l]);
-            a.pnkept = (const int32_t*)(X + y.nkept[l]);
+            // the first routed level has no parents: the parent arrays point at a
+            // small scratch region that no kernel writes (their values go unused), so
+            // that a kernel may issue its parent reads before it knows whether the
+            // level is the first
+            a.pklist = (const int32_t*)(X + y.noparent);
+            a.pkmask = (const uint32_t*)(X + y.noparent);
+            a.pnkept = (const int32_t*)(X + y.noparent);
             a.pcap = 1;
             a.orph_lo = a.orph_hi = 0;
         }

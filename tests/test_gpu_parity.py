@@ -38,6 +38,7 @@ CASES = [
     ("light-c5@50000", _w("light", 50000, levels=4, chunk=5)),   # level 1 takes the large select + merge
     ("light@600000", _w("light", 600000, levels=4)),             # level 1 (75,000 slots): scores re-read per pass
     ("light@131072-L2", _w("light", 131072, levels=2)),          # a large top level (2,048 nodes) left unmerged
+    ("light-f32@65536", _w("light", 65536, kv_dtype="f32")),     # fp32 cache: the two-per-CU gather at many tiles
 ]
 
 

@@ -181,14 +181,20 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
         const uint64_t* kb = pa->kbm + (size_t)g * G * pa->wcap;
 #pragma unroll
         for (int k = 0; k < kDeferW; ++k) {
-            const int i = (int)threadIdx.x + k * kScoreThreads;
-            dw[k] = i < nall ? kb[i] : 0ull;
+            dw[k] = 0ull;
+            if (k * kScoreThreads < nall) {           // uniform: slots wholly past the end skipped
+                const int i = (int)threadIdx.x + k * kScoreThreads;
+                if (i < nall) dw[k] = kb[i];
+            }
         }
         const int gcap = pa->top ? 0 : (int)pa->pcap;
 #pragma unroll
         for (int k = 0; k < kDeferP; ++k) {
-            const int i = (int)threadIdx.x + k * kScoreThreads;
-            dg[k] = i < gcap ? pa->pklist[(size_t)g * pa->pcap + i] : 0;
+            dg[k] = 0;
+            if (k * kScoreThreads < gcap) {
+                const int i = (int)threadIdx.x + k * kScoreThreads;
+                if (i < gcap) dg[k] = pa->pklist[(size_t)g * pa->pcap + i];
+            }
         }
         pn_raw = pa->pnkept[g];
     } else {
@@ -672,8 +678,10 @@ __device__ __forceinline__ int stage_small(const ZhaLevelArgs& a, int g, int G, 
     const bool in = tid < a.cap;
     float v[ZHA_MAX_GROUP];
 #pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-        v[hh] = (hh < G && in) ? a.sig[((size_t)g * G + hh) * a.cap + tid] : zha_neg_inf();
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+        v[hh] = zha_neg_inf();
+        if (hh < G && in) v[hh] = a.sig[((size_t)g * G + hh) * a.cap + tid];   // hh < G: uniform
+    }
     const int pi = (int)zha_div((uint32_t)tid, a.dc);
     const int32_t pk = pi < a.pcap ? a.pklist[(size_t)g * a.pcap + pi] : 0;   // unused at the first level
     const int pn = parent_count(a, g);
@@ -833,9 +841,10 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainA
         }
         float v[ZHA_MAX_GROUP];
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-            v[hh] = (hh < G && p < n && ((msk >> hh) & 1u)) ? a.sig[((size_t)g * G + hh) * a.cap + node]
-                                                           : zha_neg_inf();
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+            v[hh] = zha_neg_inf();
+            if (hh < G && p < n && ((msk >> hh) & 1u)) v[hh] = a.sig[((size_t)g * G + hh) * a.cap + node];
+        }
         __syncthreads();                               // every gather done before the write-back below
         // all gathered values in registers at once (otherwise the compiler waits for
         // each write-back store before the next LDS write)
@@ -901,12 +910,17 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
     // together (one round trip, bounded by the capacity); the second half's reads,
     // bounded by the count, follow as soon as it arrives.  Positions >= n are
     // ignored afterwards.
+    // (slots that lie wholly past the bound are skipped by a uniform branch: no
+    // per-lane work for them)
     uint32_t kr[kSlots];
     const int lim = (int)min(a.cap, (int64_t)kLdsKeys);
 #pragma unroll
     for (int k = 0; k < kSlots / 2; ++k) {
-        const int pos = tid + k * kSelThreads;
-        kr[k] = __float_as_uint(pos < lim ? sg[pos] : zha_neg_inf());
+        kr[k] = __float_as_uint(zha_neg_inf());
+        if (k * kSelThreads < lim) {
+            const int pos = tid + k * kSelThreads;
+            if (pos < lim) kr[k] = __float_as_uint(sg[pos]);
+        }
     }
     const int pn = parent_count(a, g);
     const int n = a.top ? (int)a.n_top : pn * c + n_orph;
@@ -914,8 +928,11 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
         const int lim2 = min(lim, n);
 #pragma unroll
         for (int k = kSlots / 2; k < kSlots; ++k) {
-            const int pos = tid + k * kSelThreads;
-            kr[k] = __float_as_uint(pos < lim2 ? sg[pos] : zha_neg_inf());
+            kr[k] = __float_as_uint(zha_neg_inf());
+            if (k * kSelThreads < lim2) {
+                const int pos = tid + k * kSelThreads;
+                if (pos < lim2) kr[k] = __float_as_uint(sg[pos]);
+            }
         }
     }
     if (n <= kSmallN) {
@@ -1215,8 +1232,10 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
     // every read before the two paths join; a sliced level reads its chunk counts
     // after the early return)
 #pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-        pw[hh] = (!chunked && hh < G && tid < w0) ? gbm[(size_t)hh * a.wcap + tid] : 0ull;
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+        pw[hh] = 0ull;
+        if (!chunked && hh < G && tid < w0) pw[hh] = gbm[(size_t)hh * a.wcap + tid];
+    }
     const int pn = parent_count(a, g);
 
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);

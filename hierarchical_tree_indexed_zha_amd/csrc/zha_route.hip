@@ -1215,16 +1215,25 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
     uint64_t hv[kPerW];
     int32_t pv[kPerP];
     uint64_t pw[ZHA_MAX_GROUP];
+    // (slots whose heads or parents all lie past their bound are skipped by a
+    // uniform branch)
+    constexpr int kHeadsPerSlot = kSelThreads / kMergeW;
 #pragma unroll
     for (int t = 0; t < kPerW; ++t) {
-        const uint32_t i = (uint32_t)(tid + t * kSelThreads);
-        const uint32_t hh = i / kMergeW, wi = i % kMergeW;
-        hv[t] = (hh < (uint32_t)G && w0 + (int)wi < wend_s) ? gbm[(size_t)hh * a.wcap + w0 + wi] : 0ull;
+        hv[t] = 0ull;
+        if (t * kHeadsPerSlot < G) {
+            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
+            const uint32_t hh = i / kMergeW, wi = i % kMergeW;
+            if (hh < (uint32_t)G && w0 + (int)wi < wend_s) hv[t] = gbm[(size_t)hh * a.wcap + w0 + wi];
+        }
     }
 #pragma unroll
     for (int t = 0; t < kPerP; ++t) {
-        const int i = tid + t * kSelThreads;
-        pv[t] = i < npar_s ? par[pb0 + i] : 0;
+        pv[t] = 0;
+        if (t * kSelThreads < npar_s) {
+            const int i = tid + t * kSelThreads;
+            if (i < npar_s) pv[t] = par[pb0 + i];
+        }
     }
     const bool chunked = a.chunk_cnt != nullptr;   // sliced level: kept counts per 512-word chunk
     const int nch = (wcap + kMergeW - 1) / kMergeW;

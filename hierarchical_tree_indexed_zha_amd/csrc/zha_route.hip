@@ -1192,7 +1192,10 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
 // one memory round trip together.
 __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelArgs a, int G, int c, int share) {
     ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(share));
-    __shared__ __align__(16) uint64_t hw[kMergeW * ZHA_MAX_GROUP];   // [word][16 heads], heads >= G zero
+    // [word][16 heads (+1 padding)], heads >= G zero: a row of 17 words, so that the
+    // threads of a wave (consecutive rows) reach distinct LDS banks
+    constexpr int kRow = ZHA_MAX_GROUP + 1;
+    __shared__ __align__(16) uint64_t hw[kMergeW * kRow];
     __shared__ int32_t s_par[kMergeW * 32];                            // parents' node ids
     __shared__ uint64_t s_union[kMergeW];
     __shared__ uint32_t s_wpre[kMergeW];
@@ -1280,7 +1283,7 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
 #pragma unroll
     for (int t = 0; t < kPerW; ++t) {
         const uint32_t i = (uint32_t)(tid + t * kSelThreads);
-        hw[(i % kMergeW) * ZHA_MAX_GROUP + i / kMergeW] = (int)(i % kMergeW) < nw ? hv[t] : 0ull;
+        hw[(i % kMergeW) * kRow + i / kMergeW] = (int)(i % kMergeW) < nw ? hv[t] : 0ull;
     }
 #pragma unroll
     for (int t = 0; t < kPerP; ++t) {
@@ -1292,15 +1295,10 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) run += s_part[w];
     if (tid < nw) {
-        const uint4* wq = reinterpret_cast<const uint4*>(hw) + tid * (ZHA_MAX_GROUP / 2);
-        uint32_t lo = 0, hi = 0;
+        uint64_t u = 0;
 #pragma unroll
-        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
-            const uint4 v = wq[t];
-            lo |= v.x | v.z;
-            hi |= v.y | v.w;
-        }
-        s_union[tid] = ((uint64_t)hi << 32) | lo;
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= hw[tid * kRow + hh];
+        s_union[tid] = u;
     }
     __syncthreads();
     if (wave == 0) {
@@ -1326,30 +1324,22 @@ __global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelAr
     int32_t* kl = a.klist + (size_t)g * a.cap;
     uint32_t* km = a.kmask + (size_t)g * a.cap;
     // word wi = 16 k + wave, bit = lane
-    const int sh = lane & 31;
-    const bool hi = lane >= 32;
 #pragma unroll 1
     for (int wi = wave; wi < nw; wi += kSelWaves) {
         const uint64_t u = s_union[wi];
         const uint32_t pre = s_wpre[wi];
-        const uint4* wq = reinterpret_cast<const uint4*>(hw) + wi * (ZHA_MAX_GROUP / 2);
-        uint4 hq[ZHA_MAX_GROUP / 2];
+        uint64_t hr[ZHA_MAX_GROUP];                   // the row's head words (one address per read)
 #pragma unroll
-        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) hq[t] = wq[t];
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hr[hh] = hw[wi * kRow + hh];
         const int pos = p0 + wi * 64 + lane;
         const bool child = par && pos < pnc;
         const int pi = (int)zha_div((uint32_t)pos, a.dc);
         const int32_t pnode = child ? s_par[pi - pb0] : 0;
         if (!lane_bit(u, lane)) continue;
-        // lane's bit of each head word: low dword for lanes < 32, high dword above
+        // lane's bit of each head word
         uint32_t msk = 0;
 #pragma unroll
-        for (int t = 0; t < ZHA_MAX_GROUP / 2; ++t) {
-            const uint32_t x0 = hi ? hq[t].y : hq[t].x;
-            const uint32_t x1 = hi ? hq[t].w : hq[t].z;
-            msk |= ((x0 >> sh) & 1u) << (2 * t);
-            msk |= ((x1 >> sh) & 1u) << (2 * t + 1);
-        }
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) msk |= (uint32_t)((hr[hh] >> lane) & 1ull) << hh;
         const uint32_t rank = run + pre + bits_below_lane(u);
         int32_t node;
         if (!par) node = pos;

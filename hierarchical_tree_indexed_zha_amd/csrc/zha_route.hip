@@ -537,6 +537,7 @@ constexpr int kMergeW = kLdsKeys / 64;        // bitmap words merged per step
 constexpr int kBatch = 8;                     // LDS keys read together in a pass
 constexpr int kGlobBatch = 16;                // scores re-read together from global memory
 constexpr int kMergeBlocks = 32;              // merge workgroups per group
+constexpr int kRankMax = 256;                 // crossing-bin keys ranked directly instead of histogrammed
 static_assert((kSlots & (kSlots - 1)) == 0 && kSlots % kBatch == 0, "slot batches");
 constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup
 static_assert(kSmallN == ZHA_SMALL_SLOTS, "small levels");
@@ -555,6 +556,16 @@ static_assert(ZHA_MAX_GROUP * kSmallK <= kHistPadded, "small-path kept words ins
 // and one 64-bit LDS atomic per key updates both.
 constexpr int kCntShift = 52;
 constexpr uint64_t kMassMask = (1ull << kCntShift) - 1ull;
+
+// The cut inside a crossing bin that holds few keys.  Ordered by (key,
+// position), the bin's keys are taken while the mass before them is below
+// `need` (what the bin must still supply); the cut is the key, and the position,
+// whose own mass reaches it.  Entry e = {key, position, mass lo, mass hi}: the mass
+// before entry j is the sum over the entries that precede it in that order.
+__device__ __forceinline__ bool rank_precedes(const uint4& f, const uint4& e) {
+    return f.x < e.x || (f.x == e.x && f.y < e.y);
+}
+__device__ __forceinline__ uint64_t entry_mass(const uint4& e) { return ((uint64_t)e.w << 32) | e.z; }
 
 // One wave selects for one query head among n <= 64 K candidates whose scores
 // are in LDS (sg); position lane + 64k sits in register slot k.  8-bit digits,
@@ -886,6 +897,11 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
     __shared__ int s_bin;
     __shared__ uint64_t s_before, s_need, s_run;
     __shared__ uint32_t s_cnt[2];
+    // the keys of the previous pass's crossing bin {key, position, mass lo, mass hi}
+    // while there are at most kRankMax, their partial ranks, their count, the cut
+    __shared__ __align__(16) uint4 s_ent[kRankMax];
+    __shared__ uint64_t s_rank[kRankMax];
+    __shared__ uint32_t s_nent, s_cut[2];
 
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -987,7 +1003,8 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
 #pragma unroll
     for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, swf[w]);
 
-    // Kept rule: keep_all, or key < ustar, or key == ustar when that key is unique.
+    // Kept rule: keep_all, or key < ustar, or key == ustar when that key is unique
+    // (a ranked cut: key == ustar at a position <= plim).
     const bool none = m == zha_neg_inf();        // this head has no candidate at this level
     const bool keep_all = !none && top_p >= 1.0f;
     const bool cut = !none && !keep_all;
@@ -1010,10 +1027,11 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
             }
         }
     }
-    uint32_t ustar = 0, ties = 0;
+    uint32_t ustar = 0, ties = 0, plim = 0xFFFFFFFFu;
     uint64_t need = 0;
     if (cut) {
         uint32_t mshift = 31, mval = 0, bshift = 21, bmask = 2047;
+        bool rec = false;                        // this pass records the previous crossing bin's keys
 #pragma unroll 1
         for (int pass = 0; pass < 3; ++pass) {
             // pass 0 adds the mass of every key that carries mass; later passes count
@@ -1042,8 +1060,15 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
                                 if ((hit >> j) & 1u) {
                                     const uint32_t key = kk[j];
                                     const uint32_t b = (key >> bshift) & bmask;
-                                    atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
+                                    const uint64_t ms = mass_of(key);
+                                    atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)ms);
                                     atomicAdd(&cntb[b], 1u);
+                                    if (rec) {
+                                        const uint32_t e = atomicAdd(&s_nent, 1u);
+                                        if (e < kRankMax)
+                                            s_ent[e] = make_uint4(key, (uint32_t)(tid + (k0 + j) * kSelThreads),
+                                                                  (uint32_t)ms, (uint32_t)(ms >> 32));
+                                    }
                                 }
                             }
                         }
@@ -1063,13 +1088,58 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
                         const uint32_t key = key_of(xs[j], m);
                         if (key < kNoMass && (all || (key >> mshift) == mval)) {
                             const uint32_t b = (key >> bshift) & bmask;
-                            atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)mass_of(key));
-                            if (!all) atomicAdd(&cntb[b], 1u);
+                            const uint64_t ms = mass_of(key);
+                            atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)ms);
+                            if (!all) {
+                                atomicAdd(&cntb[b], 1u);
+                                if (rec) {
+                                    const uint32_t e = atomicAdd(&s_nent, 1u);
+                                    if (e < kRankMax)
+                                        s_ent[e] = make_uint4(key, (uint32_t)(tid + (k0 + j) * kSelThreads),
+                                                              (uint32_t)ms, (uint32_t)(ms >> 32));
+                                }
+                            }
                         }
                     }
                 }
             }
             __syncthreads();
+            const int nent = rec ? (int)s_nent : 0;
+            if (nent > 0 && nent <= kRankMax) {
+                // the previous crossing bin holds few keys: rank them directly.  Entry j's
+                // mass before it is summed in C chunks of the entries (one chunk per
+                // thread, a wave's threads sharing theirs: broadcast reads), then the entry
+                // whose own mass reaches what the bin must supply is the cut.
+                const int np = (nent + 63) & ~63;
+                const int C = kSelThreads / np;
+                const int j = tid % np, ck = tid / np;
+                const int chunk = (nent + C - 1) / C;
+                if (j < nent && ck < C) {
+                    const uint4 e = s_ent[j];
+                    const int i0 = ck * chunk, i1 = min(nent, i0 + chunk);
+                    uint64_t acc = 0;
+#pragma unroll 4
+                    for (int i = i0; i < i1; ++i) {
+                        const uint4 f = s_ent[i];
+                        acc += rank_precedes(f, e) ? entry_mass(f) : 0ull;
+                    }
+                    if (i1 > i0) atomicAdd((unsigned long long*)&s_rank[j], (unsigned long long)acc);
+                }
+                __syncthreads();
+                if (tid < nent) {
+                    const uint4 e = s_ent[tid];
+                    const uint64_t before = s_rank[tid];
+                    if (before < need && before + entry_mass(e) >= need) {
+                        s_cut[0] = e.x;
+                        s_cut[1] = e.y;
+                    }
+                }
+                __syncthreads();
+                ustar = s_cut[0];
+                plim = s_cut[1];
+                ties = 1;
+                break;
+            }
             if (wave == 0) wave_find_cross(hist, need, top_p, &s_bin, &s_before, &s_need);
             __syncthreads();
             const uint32_t bin = (uint32_t)s_bin;
@@ -1085,11 +1155,23 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
                 ties = cnt;
                 break;
             }
+            {
+                // every key of the crossing bin has at least the mass of its largest key,
+                // so the bin's mass over that bounds how many keys the next pass meets
+                const uint64_t mmin = mass_of((pref << bshift) | ((1u << bshift) - 1u));
+                rec = mmin > 0 && hist[hpad(bin)] <= (uint64_t)kRankMax * mmin;
+            }
             if (pass == 0) { mshift = 21; mval = pref; bshift = 10; bmask = 2047; }
             else { mshift = 10; mval = pref; bshift = 0; bmask = 1023; }
             __syncthreads();                     // every thread has read this pass's result
             for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
             for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
+            for (int i = tid; i < kRankMax; i += kSelThreads) s_rank[i] = 0;
+            if (tid == 0) {
+                s_nent = 0;
+                s_cut[0] = 0;
+                s_cut[1] = 0;
+            }
             __syncthreads();
         }
     }
@@ -1104,7 +1186,10 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
             {
                 const uint32_t key = keys[tid + k * kSelThreads];
                 const bool cand = key != kNotCand;
-                const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
+                const bool kept = !none && (keep_all ? cand
+                                                     : (key < kNoMass &&
+                                                        (key < ustar || (key == ustar && ties == 1 &&
+                                                                         (uint32_t)(tid + k * kSelThreads) <= plim))));
                 const uint64_t word = __ballot(kept);
                 const int wi = k * kSelWaves + wave;
                 if (lane == 0 && wi < nwords) bm[wi] = word;
@@ -1127,7 +1212,10 @@ __global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelA
                 if (k < nslot) {
                     const uint32_t key = key_of(xs[j], m);
                     const bool cand = key != kNotCand;
-                    const bool kept = !none && (keep_all ? cand : (key < kNoMass && (key < ustar || (key == ustar && ties == 1))));
+                    const bool kept = !none && (keep_all ? cand
+                                                         : (key < kNoMass &&
+                                                            (key < ustar || (key == ustar && ties == 1 &&
+                                                                             (uint32_t)(tid + k * kSelThreads) <= plim))));
                     const uint64_t word = __ballot(kept);
                     const int wi = k * kSelWaves + wave;
                     if (lane == 0 && wi < nwords) bm[wi] = word;

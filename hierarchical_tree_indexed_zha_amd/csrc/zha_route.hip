@@ -1803,7 +1803,7 @@ __global__ __launch_bounds__(kMergeW) void zha_chunk_count_kernel(ZhaLevelArgs a
 int zha_score_blocks(int64_t max_cand, int R) {
     const int64_t U = R <= 16 ? 16 / R : 1;
     const int64_t items = (max_cand + U - 1) / U;
-    int64_t blocks = (items + 7) / 8;        // about two items per wave
+    int64_t blocks = (items + 3) / 4;        // one item per wave
     if (blocks < 1) blocks = 1;
     if (blocks > ZHA_SCORE_MAXB) blocks = ZHA_SCORE_MAXB;
     return (int)blocks;

@@ -536,7 +536,7 @@ constexpr int kSlots = kLdsKeys / kSelThreads;   // positions tid + 1024 k held 
 constexpr int kMergeW = kLdsKeys / 64;        // bitmap words merged per step
 constexpr int kBatch = 8;                     // LDS keys read together in a pass
 constexpr int kGlobBatch = 16;                // scores re-read together from global memory
-constexpr int kMergeBlocks = 32;              // merge workgroups per group
+constexpr int kMergeBlocks = 64;              // merge workgroups per group
 constexpr int kRankMax = 128;                 // crossing-bin keys ranked directly instead of histogrammed
 static_assert((kSlots & (kSlots - 1)) == 0 && kSlots % kBatch == 0, "slot batches");
 constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup

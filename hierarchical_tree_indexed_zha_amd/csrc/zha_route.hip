@@ -550,13 +550,6 @@ static_assert(kMergeW <= kSelThreads, "merge: one thread per word of a step");
 static_assert(ZHA_MAX_GROUP * (kSmallN + 2 * 256) + kSmallN <= kLdsKeys, "small path inside the key buffer");
 static_assert(ZHA_MAX_GROUP * kSmallK <= kHistPadded, "small-path kept words inside the histogram");
 
-
-// Small-path histogram bins pack a key count above a mass sum: at most kSmallN
-// keys of mass <= 2^40 sum below 2^52, so the fields never carry into each other
-// and one 64-bit LDS atomic per key updates both.
-constexpr int kCntShift = 52;
-constexpr uint64_t kMassMask = (1ull << kCntShift) - 1ull;
-
 // The cut inside a crossing bin that holds few keys.  Ordered by (key,
 // position), the bin's keys are taken while the mass before them is below
 // `need` (what the bin must still supply); the cut is the key, and the position,
@@ -566,6 +559,12 @@ __device__ __forceinline__ bool rank_precedes(const uint4& f, const uint4& e) {
     return f.x < e.x || (f.x == e.x && f.y < e.y);
 }
 __device__ __forceinline__ uint64_t entry_mass(const uint4& e) { return ((uint64_t)e.w << 32) | e.z; }
+
+// Small-path histogram bins pack a key count above a mass sum: at most kSmallN
+// keys of mass <= 2^40 sum below 2^52, so the fields never carry into each other
+// and one 64-bit LDS atomic per key updates both.
+constexpr int kCntShift = 52;
+constexpr uint64_t kMassMask = (1ull << kCntShift) - 1ull;
 
 // One wave selects for one query head among n <= 64 K candidates whose scores
 // are in LDS (sg); position lane + 64k sits in register slot k.  8-bit digits,

@@ -359,7 +359,7 @@ def sweep(args, torch, W, B, ZhaLayer):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path (one GPU holds the whole cache at these sizes).",
               file=sys.stderr)
         sys.exit(2)
     import torch

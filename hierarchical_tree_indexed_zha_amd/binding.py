@@ -22,10 +22,11 @@ ZHA_BF16 = 0
 ZHA_F32 = 1
 
 EXPORTS = [
-    "zha_check_config", "zha_tree_bytes", "zha_scratch_bytes", "zha_dense_scratch_bytes",
+    "zha_check_config", "zha_tree_bytes", "zha_scratch_bytes", "zha_dense_scratch_bytes", "zha_sel_bytes",
     "zha_tree_level_offsets", "zha_route_level_offsets", "zha_build_tree", "zha_append_token",
     "zha_decode_step", "zha_decode_step_timed", "dense_decode", "zha_last_error",
 ]
+STATS_MAX_LEVELS = 32
 
 
 class ZhaError(RuntimeError):
@@ -45,6 +46,7 @@ class Config(ctypes.Structure):
         ("top_p", ctypes.c_float),
         ("kv_dtype", ctypes.c_int32),
         ("capacity", ctypes.c_int64),
+        ("sink", ctypes.c_int32),
     ]
 
 
@@ -56,6 +58,33 @@ class Buffers(ctypes.Structure):
         ("tree", ctypes.c_void_p),
         ("scratch", ctypes.c_void_p),
     ]
+
+
+class Stats(ctypes.Structure):
+    """zha_stats (include/zha.h): per-level counts and bytes of one decode step."""
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("top_level", ctypes.c_int32),
+        ("levels", ctypes.c_int32),
+        ("cand", ctypes.c_int64 * STATS_MAX_LEVELS),
+        ("kept", ctypes.c_int64 * STATS_MAX_LEVELS),
+        ("group_cand", ctypes.c_int64 * STATS_MAX_LEVELS),
+        ("group_kept", ctypes.c_int64 * STATS_MAX_LEVELS),
+        ("bytes_read", ctypes.c_int64 * STATS_MAX_LEVELS),
+        ("bytes_streamed", ctypes.c_int64 * STATS_MAX_LEVELS),
+        ("gather_tokens", ctypes.c_int64),
+        ("gather_bytes", ctypes.c_int64),
+    ]
+
+
+def stats_from_bytes(raw: bytes) -> dict:
+    """A zha_stats read back from device memory, as a dict of ints and lists (index l-1 = level l)."""
+    st = Stats.from_buffer_copy(raw)
+    out = {}
+    for name, typ in Stats._fields_:
+        v = getattr(st, name)
+        out[name] = list(v) if hasattr(typ, "_length_") else int(v)
+    return out
 
 
 class RouteOffsets(ctypes.Structure):
@@ -78,6 +107,7 @@ def lib() -> ctypes.CDLL:
             "zha_tree_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_scratch_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_dense_scratch_bytes": (ctypes.c_size_t, [cfgp]),
+            "zha_sel_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_tree_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int32, P(ctypes.c_int64), P(ctypes.c_int64),
                                                       P(ctypes.c_int64), P(ctypes.c_int64)]),
             "zha_route_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int32, P(RouteOffsets)]),
@@ -85,9 +115,10 @@ def lib() -> ctypes.CDLL:
             "zha_append_token": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p]),
             "zha_decode_step": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                               ctypes.c_void_p]),
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
             "zha_decode_step_timed": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p,
-                                                     ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_void_p]),
+                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                     P(ctypes.c_void_p), ctypes.c_void_p]),
             "dense_decode": (ctypes.c_int, [cfgp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
             "zha_last_error": (ctypes.c_char_p, []),
@@ -124,10 +155,10 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity) -> Config:
+def make_config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity, sink=1) -> Config:
     if isinstance(kv_dtype, str):
         kv_dtype = ZHA_BF16 if kv_dtype == "bf16" else ZHA_F32
-    return Config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity)
+    return Config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity, sink)
 
 
 def config_of(w, capacity: int | None = None) -> Config:
@@ -161,6 +192,13 @@ def zha_dense_scratch_bytes(cfg: Config) -> int:
     return n
 
 
+def zha_sel_bytes(cfg: Config) -> int:
+    n = lib().zha_sel_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise ZhaError(ZHA_ERR_ARG, last_error())
+    return n
+
+
 def zha_tree_level_offsets(cfg: Config, level: int) -> dict:
     s, b, l, n = (ctypes.c_int64() for _ in range(4))
     _check(lib().zha_tree_level_offsets(ctypes.byref(cfg), level, ctypes.byref(s), ctypes.byref(b), ctypes.byref(l),
@@ -187,16 +225,20 @@ def zha_append_token(cfg: Config, bufs: Buffers, n_before: int, k_new, v_new, st
                                   _stream(stream)))
 
 
-def zha_decode_step(cfg: Config, bufs: Buffers, n_tokens: int, q, out, stream=None) -> None:
-    _check(lib().zha_decode_step(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out),
-                                 _stream(stream)))
+def zha_decode_step(cfg: Config, bufs: Buffers, n_tokens: int, q, out, sel=None, stats=None,
+                    stream=None) -> None:
+    """sel: None or device int32 [H_q][1 + capacity // chunk]; stats: None or a device buffer of
+    ctypes.sizeof(Stats) bytes."""
+    _check(lib().zha_decode_step(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out), _ptr(sel),
+                                 _ptr(stats), _stream(stream)))
 
 
-def zha_decode_step_timed(cfg: Config, bufs: Buffers, n_tokens: int, q, out, events, stream=None) -> None:
+def zha_decode_step_timed(cfg: Config, bufs: Buffers, n_tokens: int, q, out, events, sel=None, stats=None,
+                          stream=None) -> None:
     """events: four raw hipEvent_t handles (ints, or None) recorded around the step's phases."""
     arr = (ctypes.c_void_p * 4)(*[e if e else None for e in events])
-    _check(lib().zha_decode_step_timed(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out), arr,
-                                       _stream(stream)))
+    _check(lib().zha_decode_step_timed(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out),
+                                       _ptr(sel), _ptr(stats), arr, _stream(stream)))
 
 
 def dense_decode(cfg: Config, k, v, n_tokens: int, q, out, scratch, stream=None) -> None:

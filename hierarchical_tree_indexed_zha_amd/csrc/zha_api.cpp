@@ -65,6 +65,8 @@ int validate(const zha_config* cfg) {
     if (cfg->capacity < 1) return fail(ZHA_ERR_ARG, "capacity must be >= 1 (got %lld)", (long long)cfg->capacity);
     if (cfg->capacity >= (int64_t(1) << 31))
         return fail(ZHA_ERR_UNSUPPORTED, "capacity must be < 2^31 (got %lld)", (long long)cfg->capacity);
+    if (cfg->sink == 0) return fail(ZHA_ERR_UNSUPPORTED, "sink = 0 (no attention sink) is not implemented");
+    if (cfg->sink != 1) return fail(ZHA_ERR_ARG, "sink must be 1 (got %d)", cfg->sink);
     return ZHA_OK;
 }
 
@@ -211,6 +213,12 @@ size_t zha_dense_scratch_bytes(const zha_config* cfg) {
     return make_layout(cfg).dense_bytes;
 }
 
+size_t zha_sel_bytes(const zha_config* cfg) {
+    if (validate(cfg) != ZHA_OK) return 0;
+    ok();
+    return sizeof(int32_t) * (size_t)cfg->n_q_heads * (size_t)(cfg->capacity / cfg->chunk + 1);
+}
+
 int zha_tree_level_offsets(const zha_config* cfg, int32_t level, int64_t* s_off, int64_t* b_off, int64_t* lse_off,
                            int64_t* n_cap) {
     int rc = validate(cfg);
@@ -311,7 +319,7 @@ int record(void* const* events, int i, hipStream_t s) {
 }
 
 int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q, float* out,
-                void* const* events, void* stream) {
+                int32_t* sel, zha_stats* stats, void* const* events, void* stream) {
     int rc = validate(cfg);
     if (rc) return rc;
     if (!bufs || !bufs->k || !bufs->v || !bufs->tree || !bufs->scratch || !q || !out)
@@ -451,6 +459,32 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     e = zha_launch_combine(at_, y.H, y.G, Bg, out, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     if ((rc = record(events, 3, s))) return rc;
+    if (sel) {
+        e = zha_launch_sel(at_.klist, at_.kmask, at_.nkept, at_.cap1, y.H, y.G, sel, s);
+        if (e != hipSuccess) return hip_fail(e, "sel launch");
+    }
+    if (stats) {
+        ZhaReportArgs r{};
+        for (int l = 1; l <= y.L; ++l) {
+            r.ncand[l - 1] = (const int32_t*)(X + y.ncand[l]);
+            r.nkept[l - 1] = (const int32_t*)(X + y.nkept[l]);
+            r.hstats[l - 1] = (const int32_t*)(X + y.stats[l]);
+            r.routed[l - 1] = n_nodes(cfg, n_tokens, l) > 0 ? 1 : 0;
+            r.all_nodes[l - 1] = top - l < nchain ? n_nodes(cfg, n_tokens, l) : 0;
+        }
+        r.klist1 = at_.klist;
+        r.cap1 = at_.cap1;
+        r.n_tokens = n_tokens;
+        r.plane_bytes = (int64_t)R * (ZHA_D + 1) * 4;
+        r.kv_row_bytes = 2 * ZHA_D * (cfg->kv_dtype == ZHA_BF16 ? 2 : 4);
+        r.H = y.H;
+        r.G = y.G;
+        r.c = c;
+        r.levels = y.L;
+        r.top = top;
+        e = zha_launch_stats(r, stats, s);
+        if (e != hipSuccess) return hip_fail(e, "stats launch");
+    }
     return ok();
 }
 }  // namespace
@@ -458,13 +492,13 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
 extern "C" {
 
 int zha_decode_step(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q, float* out,
-                    void* stream) {
-    return decode_impl(cfg, bufs, n_tokens, q, out, nullptr, stream);
+                    int32_t* sel, zha_stats* stats, void* stream) {
+    return decode_impl(cfg, bufs, n_tokens, q, out, sel, stats, nullptr, stream);
 }
 
 int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q,
-                          float* out, void* const* events, void* stream) {
-    return decode_impl(cfg, bufs, n_tokens, q, out, events, stream);
+                          float* out, int32_t* sel, zha_stats* stats, void* const* events, void* stream) {
+    return decode_impl(cfg, bufs, n_tokens, q, out, sel, stats, events, stream);
 }
 
 int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_tokens, const void* q, float* out,

@@ -153,3 +153,22 @@ hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, 
                                 float tau, int Bg, hipStream_t stream, hipEvent_t start = nullptr,
                                 hipEvent_t stop = nullptr);
 hipError_t zha_launch_combine(const ZhaAttnArgs& a, int H_kv, int G, int Bg, float* out, hipStream_t stream);
+
+// ---- optional outputs of a decode step (zha_report.hip)
+struct zha_stats;
+struct ZhaReportArgs {
+    const int32_t* ncand[32];    // per level l (index l-1): [H_kv] union candidates
+    const int32_t* nkept[32];    // [H_kv] nodes kept by some head
+    const int32_t* hstats[32];   // [H_q][2] per head: candidates, kept
+    int64_t all_nodes[32];       // > 0: the level's every node was scored (its count per head)
+    int32_t routed[32];          // 1 when the level has a complete node
+    const int32_t* klist1;       // level-1 kept list [H_kv][cap1]
+    int64_t cap1;                // 0 when no level was routed
+    int64_t n_tokens;
+    int64_t plane_bytes;         // R (d + 1) 4: summary bytes of one node
+    int64_t kv_row_bytes;        // 2 d e_kv: K and V bytes of one token
+    int H, G, c, levels, top;
+};
+hipError_t zha_launch_sel(const int32_t* klist, const uint32_t* kmask, const int32_t* nkept, int64_t cap1, int H_kv,
+                          int G, int32_t* sel, hipStream_t stream);
+hipError_t zha_launch_stats(const ZhaReportArgs& r, zha_stats* out, hipStream_t stream);

@@ -1451,8 +1451,9 @@ constexpr int kHugeWaves = kHugeThreads / 64;
 constexpr int kHugePer = ZHA_SLICE / kHugeThreads;   // positions per thread
 static_assert(ZHA_SLICE % 64 == 0 && kHugePer * kHugeThreads == ZHA_SLICE, "slice layout");
 static_assert(ZHA_SLICE % (kHugeWaves * 64) == 0, "a slice holds whole words of every wave");
+static_assert(kHugeWaves * 64 == kHugeThreads, "slot k of wave w is bitmap word (p0 >> 6) + w + kHugeWaves k");
 
-// grid (H_q), 256 threads: clears the level's histograms and counts.
+// grid (H_q), kHugeThreads (1024) threads: clears the level's histograms and counts.
 __global__ __launch_bounds__(kHugeThreads) void zha_huge_init_kernel(ZhaLevelArgs a, int Hq) {
     ZHA_LEVEL_ARGS_READY(a, "s"(Hq));
     const int h = blockIdx.x;
@@ -1497,7 +1498,8 @@ __device__ __forceinline__ SliceView slice_view(const ZhaLevelArgs& a, int G, in
     return v;
 }
 
-// The slice's keys in registers: position p0 + tid + 256 k in slot k.
+// The slice's keys in registers: position p0 + tid + kHugeThreads k (= 1024 k) in slot k,
+// so wave w's lanes of slot k cover bitmap word (p0 >> 6) + w + kHugeWaves k.
 __device__ __forceinline__ void slice_keys(const ZhaLevelArgs& a, int h, const SliceView& v,
                                            uint32_t (&key)[kHugePer]) {
     const int tid = threadIdx.x;
@@ -1635,7 +1637,7 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
     return sum;
 }
 
-// grid (slices, H_q), 256 threads: kept flags of one slice into the head's bitmap
+// grid (slices, H_q), kHugeThreads (1024) threads: kept flags of one slice into the head's bitmap
 // (words of 64 positions, each written by one lane), candidate and kept counts,
 // and the slice's mass of keys equal to the cut when the cut key is shared.
 __global__ __launch_bounds__(kHugeThreads) void zha_huge_bitmap_kernel(ZhaLevelArgs a, int G, int c, float top_p,

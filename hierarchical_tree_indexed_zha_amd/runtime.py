@@ -34,24 +34,79 @@ class ZhaLayer:
         self.out = torch.empty((cfg.n_q_heads, d), dtype=torch.float32, device=dev)
         self.n_tokens = 0
 
+    # -- argument checks: the ABI takes raw pointers, so shape, dtype, device and
+    # layout are checked here before any pointer crosses it
+    def _need(self, name, t, shape, dtype):
+        if not isinstance(t, torch.Tensor) or t.device != self.k.device or t.dtype != dtype \
+                or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            got = (tuple(t.shape), t.dtype, str(t.device), t.is_contiguous()) if isinstance(t, torch.Tensor) else type(t)
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on "
+                             f"{self.k.device}; got {got}")
+
+    @property
+    def kv_torch_dtype(self):
+        return torch.bfloat16 if self.cfg.kv_dtype == B.ZHA_BF16 else torch.float32
+
+    def _check_q_out(self, q, out):
+        d = self.cfg.head_dim
+        self._need("q", q, (self.cfg.n_q_heads, d), self.kv_torch_dtype)
+        self._need("out", out, (self.cfg.n_q_heads, d), torch.float32)
+
     # -- the C ABI entry points
     def build(self, n_tokens: int):
         B.zha_build_tree(self.cfg, self.bufs, n_tokens)
         self.n_tokens = n_tokens
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor):
+        shape = (self.cfg.n_kv_heads, self.cfg.head_dim)
+        self._need("k_new", k_new, shape, self.kv_torch_dtype)
+        self._need("v_new", v_new, shape, self.kv_torch_dtype)
         B.zha_append_token(self.cfg, self.bufs, self.n_tokens, k_new, v_new)
         self.n_tokens += 1
 
-    def decode(self, q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    def decode(self, q: torch.Tensor, out: torch.Tensor | None = None, sel: torch.Tensor | None = None,
+               stats: torch.Tensor | None = None) -> torch.Tensor:
+        """One decode step.  sel: optional int32 [H_q][1 + capacity // chunk] (per-head kept
+        chunk lists); stats: optional uint8 tensor of stats_nbytes() bytes (a zha_stats)."""
         out = self.out if out is None else out
-        B.zha_decode_step(self.cfg, self.bufs, self.n_tokens, q, out)
+        self._check_q_out(q, out)
+        if sel is not None:
+            self._need("sel", sel, self.sel_shape(), torch.int32)
+        if stats is not None:
+            self._need("stats", stats, (self.stats_nbytes(),), torch.uint8)
+        B.zha_decode_step(self.cfg, self.bufs, self.n_tokens, q, out, sel, stats)
         return out
 
     def dense(self, q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         out = self.out if out is None else out
+        self._check_q_out(q, out)
         B.dense_decode(self.cfg, self.k, self.v, self.n_tokens, q, out, self.dense_scratch)
         return out
+
+    # -- optional decode outputs
+    def sel_shape(self):
+        return (self.cfg.n_q_heads, self.cfg.capacity // self.cfg.chunk + 1)
+
+    def new_sel(self) -> torch.Tensor:
+        return torch.zeros(self.sel_shape(), dtype=torch.int32, device=self.k.device)
+
+    @staticmethod
+    def stats_nbytes() -> int:
+        import ctypes
+        return ctypes.sizeof(B.Stats)
+
+    def new_stats(self) -> torch.Tensor:
+        return torch.zeros(self.stats_nbytes(), dtype=torch.uint8, device=self.k.device)
+
+    @staticmethod
+    def read_stats(stats: torch.Tensor) -> dict:
+        return B.stats_from_bytes(bytes(stats.cpu().numpy().tobytes()))
+
+    @staticmethod
+    def read_sel(sel: torch.Tensor) -> list[list[int]]:
+        """Per query head, the ascending kept chunk indices a `sel` output holds."""
+        s = sel.cpu()
+        return [s[h, 1:1 + int(s[h, 0])].tolist() for h in range(s.shape[0])]
 
     # -- views for tests and diagnostics
     def _view(self, buf, off, dtype, shape):

@@ -60,7 +60,7 @@ extern "C" {
 #define ZHA_OK               0
 #define ZHA_ERR_ARG         -1   /* null pointer, bad config value, level out of range */
 #define ZHA_ERR_CAPACITY    -2   /* n_tokens (or n_tokens + 1 on append) exceeds capacity */
-#define ZHA_ERR_UNSUPPORTED -3   /* valid but not implemented: head_dim != 128, group > 16, n_ref not in {1,2,4,8,16,32} */
+#define ZHA_ERR_UNSUPPORTED -3   /* valid but not implemented: head_dim != 128, group > 16, n_ref not in {1,2,4,8,16,32}, sink != 1 */
 #define ZHA_ERR_HIP         -4   /* a HIP launch or runtime call failed */
 
 /* kv_dtype values. */
@@ -77,6 +77,9 @@ typedef struct zha_config {
     float   top_p;       /* p in (0, 1]; p = 1 keeps every node */
     int32_t kv_dtype;    /* ZHA_BF16 or ZHA_F32 (K, V and q) */
     int64_t capacity;    /* rows of K and V per KV head; 1 <= capacity < 2^31 */
+    int32_t sink;        /* 1: token 0 is always attended (the attention sink).  0 (no sink)
+                          * is valid but not implemented (ZHA_ERR_UNSUPPORTED); other values
+                          * are ZHA_ERR_ARG */
 } zha_config;
 
 typedef struct zha_buffers {
@@ -134,23 +137,66 @@ int zha_route_level_offsets(const zha_config* cfg, int32_t level, zha_route_offs
  * leaves from raw keys, higher levels by the exact log-sum-exp merge of their
  * c children (equal to summarising the raw keys, since reference queries are
  * shared across levels).  0 <= n_tokens <= capacity.  Overwrites those tree
- * slots; leaves other slots untouched. */
+ * slots; leaves other slots untouched.
+ * Defined by: page "Zyphra 分层注意力（ZHA）…", section 机制拆解 (chunk
+ * summaries compressed again level by level); page "ZHA 用树形稀疏注意力改造现有大模型",
+ * section 稀疏注意力为什么还会被索引拖慢 (tangent planes at reference queries). */
 int zha_build_tree(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, void* stream);
 
 /* Append one token: write k_new, v_new (device [H_kv][d] of kv_dtype) into row
  * n_before of K and V, then summarise each node the token completes (levels l
  * with (n_before + 1) % c^l == 0).  The caller then holds n_before + 1 tokens.
- * Requires n_before + 1 <= capacity and a tree that is current for n_before. */
+ * Requires n_before + 1 <= capacity and a tree that is current for n_before.
+ * Defined by: page rit.work "zha-tree-indexer-long-context", section "Дерево
+ * сокращает сам поиск нужных ключей" (the tree grows with the context; the
+ * full cache is kept). */
 int zha_append_token(const zha_config* cfg, const zha_buffers* bufs, int64_t n_before,
                      const void* k_new, const void* v_new, void* stream);
+
+/* Per-step statistics a decode step writes to device memory when asked (see
+ * zha_decode_step).  Index l-1 holds level l; levels above levels, and levels the
+ * step did not route, hold zero.  A KV group's candidates at a level are the union
+ * of its query heads' candidates: the nodes whose summary planes the router must
+ * read once for the whole group. */
+#define ZHA_STATS_MAX_LEVELS 32
+typedef struct zha_stats {
+    int64_t n_tokens;                                /* tokens the step attended over */
+    int32_t top_level;                               /* highest level with a complete node (0: none) */
+    int32_t levels;                                  /* cfg->levels */
+    int64_t cand[ZHA_STATS_MAX_LEVELS];              /* candidates, summed over query heads */
+    int64_t kept[ZHA_STATS_MAX_LEVELS];              /* kept nodes, summed over query heads */
+    int64_t group_cand[ZHA_STATS_MAX_LEVELS];        /* union candidates, summed over KV groups */
+    int64_t group_kept[ZHA_STATS_MAX_LEVELS];        /* nodes kept by some head of a group, summed over groups */
+    int64_t bytes_read[ZHA_STATS_MAX_LEVELS];        /* summary bytes the level's routing needs:
+                                                        group_cand * n_ref * (head_dim + 1) * 4 */
+    int64_t bytes_streamed[ZHA_STATS_MAX_LEVELS];    /* summary bytes the kernels streamed for the level:
+                                                        equal to bytes_read, except at the small top levels
+                                                        whose every complete node is scored ahead of their
+                                                        selection (then n_nodes * n_kv_heads * n_ref *
+                                                        (head_dim + 1) * 4) */
+    int64_t gather_tokens;                           /* distinct tokens attended, summed over KV groups */
+    int64_t gather_bytes;                            /* K and V bytes those tokens occupy */
+} zha_stats;
+
+/* Bytes of the `sel` output of zha_decode_step: int32 [n_q_heads][1 + capacity / chunk]. */
+size_t zha_sel_bytes(const zha_config* cfg);
 
 /* One decode step for all query heads over tokens [0, n_tokens) (1 <= n_tokens
  * <= capacity) with a tree current for n_tokens.  Routes every query head
  * independently from the top level down, then attends exactly over its
  * selected raw tokens; writes out [H_q][d] float32.  The routing of each level
- * stays in scratch until the next call (zha_route_level_offsets). */
+ * stays in scratch until the next call (zha_route_level_offsets).
+ *   sel    NULL, or device int32 [H_q][1 + capacity / chunk] (zha_sel_bytes):
+ *          row h receives head h's kept level-1 chunk count k, then the k chunk
+ *          indices in ascending order (chunk j covers tokens [j c, j c + c)).
+ *          Head h attends over those chunks, token 0 and the tail
+ *          [c (n_tokens / c), n_tokens).  Entries past k are left as they were.
+ *   stats  NULL, or a device zha_stats, written by the step's last kernel.
+ * Defined by: page "ZHA 用树形稀疏注意力改造现有大模型", section
+ * 稀疏注意力为什么还会被索引拖慢 (top-level scoring, minimal top-p node set,
+ * expansion down to raw KV entries, token 0 always kept). */
 int zha_decode_step(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens,
-                    const void* q, float* out, void* stream);
+                    const void* q, float* out, int32_t* sel, zha_stats* stats, void* stream);
 
 /* zha_decode_step, plus HIP events recorded on `stream` around its phases:
  * events[0] before the first routing kernel; events[1] and events[2] at the
@@ -158,14 +204,18 @@ int zha_decode_step(const zha_config* cfg, const zha_buffers* bufs, int64_t n_to
  * dispatch, so events[1] -> events[2] is that kernel's execution time);
  * events[3] after the combine kernel.  `events` may be NULL and any entry may be
  * NULL (hipEvent_t values created by the caller).  Used to time the phases of a
- * step separately. */
+ * step separately.  Same definition as zha_decode_step. */
 int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens,
-                          const void* q, float* out, void* const* events, void* stream);
+                          const void* q, float* out, int32_t* sel, zha_stats* stats,
+                          void* const* events, void* stream);
 
 /* Dense baseline: exact softmax attention of every query head over all
  * n_tokens tokens (1 <= n_tokens <= capacity); scratch of
- * zha_dense_scratch_bytes(cfg) bytes.  cfg's tree fields are ignored apart
- * from validation. */
+ * zha_dense_scratch_bytes(cfg) bytes (its split partials: the library
+ * allocates nothing).  cfg's tree fields are ignored apart from validation.
+ * Defined by: page rit.work "zha-tree-indexer-long-context", section "Дерево
+ * сокращает сам поиск нужных ключей" (full attention reads the whole cache for
+ * every new token). */
 int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_tokens,
                  const void* q, float* out, void* scratch, void* stream);
 

@@ -220,3 +220,76 @@ def compare_tree(layer: ZhaLayer, tree: O.SummaryTree, n_tokens: int, sample: in
                 worst = max(worst, e)
                 assert e <= rtol, f"level {lv} head {g} {name}: max rel err {e:.3g}"
     return worst
+
+
+def check_sel_stats(layer: ZhaLayer, sel: torch.Tensor, stats: torch.Tensor, n_tokens: int, tree: O.SummaryTree,
+                    qh, p: float, label: str = "", chained_levels=()):
+    """The decode step's optional outputs against the oracle.
+
+    sel: per head, the kept level-1 chunks; for a head whose oracle cuts all have margin
+    >= MARGIN they must be the oracle's kept leaves, and the attended token set built
+    from them must be the oracle's token set; for every head they must be what the
+    routing in scratch says.  stats: per level, candidate and kept sums over heads, the
+    union candidates per group and the router bytes of the SURVEY's formula
+    sum_g |U_g| * R * (d + 1) * 4, with U_g the union of the group's per-head candidate
+    sets (the oracle's where all of the group's heads are unambiguous); the gathered
+    tokens and bytes."""
+    cfg = layer.cfg
+    c, L, H, R, d = cfg.chunk, cfg.levels, cfg.n_kv_heads, cfg.n_ref, cfg.head_dim
+    G = cfg.n_q_heads // H
+    st = layer.read_stats(stats)
+    got_sel = layer.read_sel(sel)
+    top = max([lv for lv in range(1, L + 1) if n_tokens // c ** lv > 0], default=0)
+    assert st["n_tokens"] == n_tokens and st["top_level"] == top and st["levels"] == L, label
+    if top >= 1:
+        kept1 = layer.kept_sets(1)
+        assert got_sel == kept1, f"{label}: sel differs from the level-1 routing in scratch"
+    else:
+        assert all(len(s) == 0 for s in got_sel), label
+    routes = [O.route_head(qh[h], tree, h // G, p) for h in range(cfg.n_q_heads)]
+    for h, r in enumerate(routes):
+        if r.min_margin >= MARGIN:
+            assert got_sel[h] == r.kept_leaves().tolist(), f"{label} head {h}: sel vs oracle leaves"
+            toks = O.final_token_set(np.array(got_sel[h], dtype=np.int64), n_tokens, c)
+            assert toks.tolist() == r.tokens.tolist(), f"{label} head {h}: token set vs oracle"
+    plane = R * (d + 1) * 4
+    e_kv = 2 if cfg.kv_dtype == B.ZHA_BF16 else 4
+    for lv in range(1, B.STATS_MAX_LEVELS + 1):
+        i = lv - 1
+        if lv > top:
+            for k in ("cand", "kept", "group_cand", "group_kept", "bytes_read", "bytes_streamed"):
+                assert st[k][i] == 0, f"{label} level {lv}: {k} should be 0"
+            continue
+        r = layer.route_level(lv)
+        assert st["cand"][i] == int(r["stats"][:, 0].sum()), f"{label} level {lv}: cand"
+        assert st["kept"][i] == int(r["stats"][:, 1].sum()), f"{label} level {lv}: kept"
+        assert st["group_kept"][i] == int(r["n_kept"].sum()), f"{label} level {lv}: group_kept"
+        union = 0
+        for g in range(H):
+            hs = range(g * G, (g + 1) * G)
+            if all(routes[h].min_margin >= MARGIN for h in hs):
+                u = set()
+                for h in hs:
+                    for lr in routes[h].levels:
+                        if lr.level == lv:
+                            u |= set(lr.candidates.tolist())
+                n_u = len(u)
+            else:
+                n_u = int(r["n_cand"][g])
+            assert int(r["n_cand"][g]) == n_u, f"{label} level {lv} group {g}: union candidates"
+            union += n_u
+        assert st["group_cand"][i] == union, f"{label} level {lv}: group_cand"
+        assert st["bytes_read"][i] == union * plane, f"{label} level {lv}: bytes_read formula"
+        if lv in chained_levels:
+            assert st["bytes_streamed"][i] == (n_tokens // c ** lv) * H * plane, f"{label} level {lv}: streamed"
+        else:
+            assert st["bytes_streamed"][i] >= st["bytes_read"][i]
+    toks = 0
+    for g in range(H):
+        u = set()
+        for h in range(g * G, (g + 1) * G):
+            u |= set(O.final_token_set(np.array(got_sel[h], dtype=np.int64), n_tokens, c).tolist())
+        toks += len(u)
+    assert st["gather_tokens"] == toks, f"{label}: gather tokens {st['gather_tokens']} vs {toks}"
+    assert st["gather_bytes"] == toks * 2 * d * e_kv
+    return st

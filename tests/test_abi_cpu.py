@@ -27,9 +27,13 @@ def test_library_exports_every_declared_symbol():
     assert sorted(B.EXPORTS) == names
 
 
-def _cfg(**kw):
-    base = dict(n_kv_heads=4, n_q_heads=32, head_dim=128, chunk=8, levels=4, n_ref=1, top_p=0.75,
+def _base():
+    return dict(n_kv_heads=4, n_q_heads=32, head_dim=128, chunk=8, levels=4, n_ref=1, top_p=0.75,
                 kv_dtype="bf16", capacity=262144)
+
+
+def _cfg(**kw):
+    base = _base()
     base.update(kw)
     return B.make_config(**base)
 
@@ -52,6 +56,9 @@ def _cfg(**kw):
     (dict(kv_dtype=7), B.ZHA_ERR_ARG),
     (dict(capacity=0), B.ZHA_ERR_ARG),
     (dict(capacity=1 << 31), B.ZHA_ERR_UNSUPPORTED),
+    (dict(sink=0), B.ZHA_ERR_UNSUPPORTED),
+    (dict(sink=2), B.ZHA_ERR_ARG),
+    (dict(sink=-1), B.ZHA_ERR_ARG),
 ])
 def test_config_validation(kw, code):
     with pytest.raises(B.ZhaError) as e:
@@ -74,6 +81,7 @@ def test_valid_configs_pass_and_sizes_match_layout():
                 expect += (nbytes + 255) // 256 * 256
         assert B.zha_tree_bytes(cfg) == expect
         assert B.zha_scratch_bytes(cfg) > 0 and B.zha_dense_scratch_bytes(cfg) > 0
+        assert B.zha_sel_bytes(cfg) == 4 * w.n_q_heads * (w.capacity // w.chunk + 1)
         o = B.zha_tree_level_offsets(cfg, w.levels)
         assert o["n_cap"] == w.capacity // w.chunk ** w.levels
         r = B.zha_route_level_offsets(cfg, 1)
@@ -91,9 +99,12 @@ def test_entry_points_reject_bad_arguments_before_touching_the_device():
         (lambda: B.zha_build_tree(cfg, B.Buffers(None, fake, fake, fake, fake), 10, 0), B.ZHA_ERR_ARG),
         (lambda: B.zha_append_token(cfg, bufs, 1000, fake, fake, 0), B.ZHA_ERR_CAPACITY),
         (lambda: B.zha_append_token(cfg, bufs, 10, None, fake, 0), B.ZHA_ERR_ARG),
-        (lambda: B.zha_decode_step(cfg, bufs, 0, fake, fake, 0), B.ZHA_ERR_ARG),
-        (lambda: B.zha_decode_step(cfg, bufs, 1001, fake, fake, 0), B.ZHA_ERR_CAPACITY),
-        (lambda: B.zha_decode_step(cfg, B.Buffers(fake, fake, fake, fake, None), 10, fake, fake, 0), B.ZHA_ERR_ARG),
+        (lambda: B.zha_decode_step(cfg, bufs, 0, fake, fake, stream=0), B.ZHA_ERR_ARG),
+        (lambda: B.zha_decode_step(cfg, bufs, 1001, fake, fake, fake, fake, stream=0), B.ZHA_ERR_CAPACITY),
+        (lambda: B.zha_decode_step(cfg, B.Buffers(fake, fake, fake, fake, None), 10, fake, fake, stream=0),
+         B.ZHA_ERR_ARG),
+        (lambda: B.zha_decode_step(B.make_config(**{**_base(), "capacity": 1000, "sink": 0}), bufs, 10, fake, fake,
+                                   stream=0), B.ZHA_ERR_UNSUPPORTED),
         (lambda: B.dense_decode(cfg, fake, fake, 1001, fake, fake, fake, 0), B.ZHA_ERR_CAPACITY),
         (lambda: B.dense_decode(cfg, fake, fake, 10, fake, fake, None, 0), B.ZHA_ERR_ARG),
         (lambda: B.zha_tree_level_offsets(cfg, 0), B.ZHA_ERR_ARG),
@@ -110,3 +121,23 @@ def test_null_config_is_rejected():
     assert lib.zha_check_config(None) == B.ZHA_ERR_ARG
     assert lib.zha_tree_bytes(None) == 0
     assert b"NULL" in lib.zha_last_error()
+
+
+def test_stats_struct_layout_matches_header():
+    """The ctypes mirror of zha_stats has the header's field order and size: two leading
+    scalars (8 + 4 + 4 bytes), six per-level int64 arrays, two trailing int64 totals."""
+    import ctypes
+    n = B.STATS_MAX_LEVELS
+    assert ctypes.sizeof(B.Stats) == 16 + 6 * 8 * n + 16
+    src = open(os.path.join(ROOT, "include", "zha.h")).read()
+    body = src[src.index("typedef struct zha_stats"):src.index("} zha_stats;")]
+    names = re.findall(r"^\s*(?:int64_t|int32_t)\s+(\w+)", body, flags=re.M)
+    assert names == [f for f, _ in B.Stats._fields_]
+    assert f"#define ZHA_STATS_MAX_LEVELS {n}" in src
+
+
+def test_config_struct_layout_matches_header():
+    src = open(os.path.join(ROOT, "include", "zha.h")).read()
+    body = src[src.index("typedef struct zha_config"):src.index("} zha_config;")]
+    names = re.findall(r"^\s*(?:int64_t|int32_t|float)\s+(\w+)", body, flags=re.M)
+    assert names == [f for f, _ in B.Config._fields_]

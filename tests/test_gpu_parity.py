@@ -259,3 +259,37 @@ def test_repeated_keys_tie_in_position_order():
     vh = to_host(layer.v)
     ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label="repeated keys")
     say(f"[repeated keys] heads exempt {ex}/{w.n_q_heads}, max attention err {err:.2e}, max score err {es:.2e}")
+
+
+SEL_CASES = [
+    ("tiny", W.get("tiny"), None),
+    ("light@32768", _w("light", 32768), None),
+    ("light@30001", _w("light", 30001, levels=4), None),
+    ("deep@20003", _w("deep", 20003, levels=6), None),
+    ("wide@16500", _w("wide", 16500), None),
+    ("ultra@65536", _w("ultra", 65536, levels=5), None),
+    ("N=3<c", _w("deep", 1024, levels=3), 3),
+    ("N=c^L+1", _w("deep", 1024, levels=3), 65),
+]
+
+
+@pytest.mark.parametrize("name,w,n", SEL_CASES, ids=[c[0] for c in SEL_CASES])
+def test_sel_and_stats_outputs(name, w, n):
+    """zha_decode_step's optional outputs: per-head kept chunk lists (sel) against the
+    oracle's leaves and token sets, and the device-written statistics against the
+    routing and the router-byte formula."""
+    from tests.gpu_util import check_sel_stats
+    n = w.n_tokens if n is None else n
+    say(f"[sel/stats] {name} n={n}")
+    layer, x = make_layer(w)
+    layer.build(n)
+    layer.n_tokens = n
+    kh, tree = oracle_tree(layer, n)
+    sel, stats = layer.new_sel(), layer.new_stats()
+    out = layer.decode(x["q"][0], sel=sel, stats=stats).clone()
+    plain = layer.decode(x["q"][0]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain), "the optional outputs must not change the step"
+    st = check_sel_stats(layer, sel, stats, n, tree, to_host(x["q"][0]), w.top_p, label=name)
+    say(f"[sel/stats] {name}: group_cand {st['group_cand'][:w.levels]}, bytes_read {st['bytes_read'][:w.levels]}, "
+        f"gather tokens {st['gather_tokens']}")

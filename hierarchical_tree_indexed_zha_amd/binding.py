@@ -24,8 +24,9 @@ ZHA_F32 = 1
 EXPORTS = [
     "zha_check_config", "zha_tree_bytes", "zha_scratch_bytes", "zha_dense_scratch_bytes", "zha_sel_bytes",
     "zha_tree_level_offsets", "zha_route_level_offsets", "zha_build_tree", "zha_append_token",
-    "zha_decode_step", "zha_decode_step_timed", "dense_decode", "zha_last_error",
+    "zha_decode_step", "zha_decode_step_timed", "dense_decode", "zha_last_error", "zha_decode_step_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 STATS_MAX_LEVELS = 32
 
 
@@ -122,6 +123,9 @@ def lib() -> ctypes.CDLL:
             "dense_decode": (ctypes.c_int, [cfgp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
             "zha_last_error": (ctypes.c_char_p, []),
+            "zha_decode_step_noalloc": (ctypes.c_int, [cfgp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                       ctypes.c_void_p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -244,3 +248,9 @@ def zha_decode_step_timed(cfg: Config, bufs: Buffers, n_tokens: int, q, out, eve
 def dense_decode(cfg: Config, k, v, n_tokens: int, q, out, scratch, stream=None) -> None:
     _check(lib().dense_decode(ctypes.byref(cfg), _ptr(k), _ptr(v), n_tokens, _ptr(q), _ptr(out), _ptr(scratch),
                               _stream(stream)))
+
+
+def zha_decode_step_noalloc(cfg: Config, k, v, tree, n_tokens: int, q, out, stream=None) -> None:
+    """zha_decode_step on the library's own per-GPU scratch (no caller scratch, nothing allocated)."""
+    _check(lib().zha_decode_step_noalloc(ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(tree), n_tokens, _ptr(q),
+                                         _ptr(out), _stream(stream)))

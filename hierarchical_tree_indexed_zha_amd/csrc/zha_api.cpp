@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <vector>
 
 #include "zha_common.h"
@@ -538,3 +539,57 @@ int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_
 }
 
 }  // extern "C"
+
+// ---- decode without caller scratch, for callers that cannot allocate
+//
+// The step's scratch is a file-scope device array.  Host code never uses the
+// array's name as an address: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept per device.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[ZHA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(ZHA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(ZHA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_noalloc_ptr[dev] = p;
+    }
+    *out = g_noalloc_ptr[dev];
+    return ZHA_OK;
+}
+
+}  // namespace
+
+extern "C" int zha_decode_step_noalloc(const zha_config* cfg, const void* k, const void* v, const void* tree,
+                                       int64_t n_tokens, const void* q, float* out, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!k || !v || !tree || !q || !out) return fail(ZHA_ERR_ARG, "k, v, tree, q and out must be non-NULL");
+    const size_t need = make_layout(cfg).scratch_bytes;
+    if (need > (size_t)ZHA_NOALLOC_SCRATCH_BYTES)
+        return fail(ZHA_ERR_UNSUPPORTED,
+                    "this configuration needs %zu bytes of decode scratch, more than the %zu the no-allocation "
+                    "entry point holds (use zha_decode_step with caller scratch)",
+                    need, (size_t)ZHA_NOALLOC_SCRATCH_BYTES);
+    void* x = nullptr;
+    if ((rc = noalloc_scratch(&x))) return rc;
+    zha_buffers b;
+    b.k = const_cast<void*>(k);
+    b.v = const_cast<void*>(v);
+    b.ref_q = nullptr;
+    b.tree = const_cast<void*>(tree);
+    b.scratch = x;
+    return decode_impl(cfg, &b, n_tokens, q, out, nullptr, nullptr, nullptr, stream);
+}

@@ -219,6 +219,19 @@ int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_
 int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_tokens,
                  const void* q, float* out, void* scratch, void* stream);
 
+/* zha_decode_step without caller scratch, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The step's scratch is a device array inside the
+ * library of ZHA_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the
+ * process ends; configurations whose zha_scratch_bytes() exceeds it are rejected
+ * with ZHA_ERR_UNSUPPORTED before anything is enqueued.  Every call on a GPU
+ * shares that GPU's array and leaves the step's routing in it: calls that
+ * overlap in time on one GPU (several streams or threads) race and must be
+ * serialised by the caller.  Allocates nothing; no sel/stats outputs. */
+#define ZHA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int zha_decode_step_noalloc(const zha_config* cfg, const void* k, const void* v, const void* tree,
+                            int64_t n_tokens, const void* q, float* out, void* stream);
+
 /* Message for the last error returned on this thread ("" if none). */
 const char* zha_last_error(void);
 

@@ -89,7 +89,8 @@ def stats_from_bytes(raw: bytes) -> dict:
 
 
 class RouteOffsets(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int64) for n in ("n_cand", "sigma", "n_kept", "kept", "mask", "stats", "n_cap")]
+    _fields_ = [(n, ctypes.c_int64) for n in ("n_cand", "sigma", "n_kept", "kept", "mask", "stats", "kbm", "n_cap",
+                                              "wcap", "chained", "sig_stride")]
 
 
 _lib = None
@@ -111,7 +112,7 @@ def lib() -> ctypes.CDLL:
             "zha_sel_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_tree_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int32, P(ctypes.c_int64), P(ctypes.c_int64),
                                                       P(ctypes.c_int64), P(ctypes.c_int64)]),
-            "zha_route_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int32, P(RouteOffsets)]),
+            "zha_route_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int64, ctypes.c_int32, P(RouteOffsets)]),
             "zha_build_tree": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p]),
             "zha_append_token": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p]),
@@ -210,9 +211,9 @@ def zha_tree_level_offsets(cfg: Config, level: int) -> dict:
     return {"s": s.value, "b": b.value, "lse": l.value, "n_cap": n.value}
 
 
-def zha_route_level_offsets(cfg: Config, level: int) -> dict:
+def zha_route_level_offsets(cfg: Config, n_tokens: int, level: int) -> dict:
     o = RouteOffsets()
-    _check(lib().zha_route_level_offsets(ctypes.byref(cfg), level, ctypes.byref(o)))
+    _check(lib().zha_route_level_offsets(ctypes.byref(cfg), n_tokens, level, ctypes.byref(o)))
     return {n: getattr(o, n) for n, _ in RouteOffsets._fields_}
 
 

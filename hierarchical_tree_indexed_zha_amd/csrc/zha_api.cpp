@@ -91,9 +91,9 @@ struct Layout {
     size_t tree_bytes = 0;
     // decode scratch
     std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, stats;
-    std::vector<size_t> hmax, hcut, hdone, hmass, hcnt, tiem, chunk;   // sliced levels only
-    std::vector<int> slices;                               // 0 when the level is not sliced
+    std::vector<size_t> hblk, ghist, hdone, hcut, tick, desc;   // selection state of a level below the chain
     std::vector<int64_t> wcap;            // bitmap words per head per level
+    std::vector<int64_t> sstr;            // score row stride per level (slots rounded up to 4)
     size_t pm = 0, pl = 0, po = 0, nact = 0;
     size_t noparent = 0;                  // readable, never written: the first routed level's parent arrays
     size_t scratch_bytes = 0;
@@ -128,34 +128,28 @@ Layout make_layout(const zha_config* cfg) {
     y.tree_bytes = off;
 
     off = 0;
-    for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.stats, &y.hmax, &y.hcut, &y.hdone, &y.hmass, &y.hcnt,
-                    &y.tiem, &y.chunk})
+    for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.stats, &y.hblk, &y.ghist, &y.hdone, &y.hcut,
+                    &y.tick, &y.desc})
         v->assign(y.L + 1, 0);
-    y.slices.assign(y.L + 1, 0);
     y.wcap.assign(y.L + 1, 0);
+    y.sstr.assign(y.L + 1, 0);
     for (int l = 1; l <= y.L; ++l) {
         const size_t n = (size_t)y.cap[l];
         y.wcap[l] = (int64_t)((n + 63) / 64);
-        y.sig[l] = off;   off = align_up(off + sizeof(float) * H * G * n);
+        y.sstr[l] = (int64_t)((n + 3) / 4 * 4);
+        y.sig[l] = off;   off = align_up(off + sizeof(float) * H * G * (size_t)y.sstr[l]);
         y.kbm[l] = off;   off = align_up(off + sizeof(uint64_t) * H * G * (size_t)y.wcap[l]);
         y.klist[l] = off; off = align_up(off + sizeof(int32_t) * H * n);
         y.kmask[l] = off; off = align_up(off + sizeof(uint32_t) * H * n);
         y.ncand[l] = off; off = align_up(off + sizeof(int32_t) * H);
         y.nkept[l] = off; off = align_up(off + sizeof(int32_t) * H);
         y.stats[l] = off; off = align_up(off + sizeof(int32_t) * 2 * H * G);
-        if (n > (size_t)ZHA_SLICED_MIN_CAP) {
-            // the widest levels select over slices of the whole GPU
-            const size_t sl = (n + ZHA_SLICE - 1) / ZHA_SLICE;
-            const size_t nch = ((size_t)y.wcap[l] + 511) / 512;
-            y.slices[l] = (int)sl;
-            y.hmax[l] = off;  off = align_up(off + sizeof(float) * H * G * ZHA_SCORE_MAXB);
-            y.hcut[l] = off;  off = align_up(off + sizeof(HugeCut) * H * G);
-            y.hdone[l] = off; off = align_up(off + sizeof(uint32_t) * 3 * H * G);
-            y.hmass[l] = off; off = align_up(off + sizeof(uint64_t) * 3 * H * G * 2048);
-            y.hcnt[l] = off;  off = align_up(off + sizeof(uint32_t) * 3 * H * G * 2048);
-            y.tiem[l] = off;  off = align_up(off + sizeof(uint64_t) * H * G * sl);
-            y.chunk[l] = off; off = align_up(off + sizeof(uint32_t) * H * nch);
-        }
+        y.hblk[l] = off;  off = align_up(off + sizeof(float) * H * G * ZHA_SCORE_MAXB);
+        y.ghist[l] = off; off = align_up(off + sizeof(uint64_t) * H * G * ZHA_HIST_BINS);
+        y.hdone[l] = off; off = align_up(off + sizeof(uint32_t) * H * G);
+        y.hcut[l] = off;  off = align_up(off + 16 * H * G);
+        y.tick[l] = off;  off = align_up(off + sizeof(uint32_t) * H);
+        y.desc[l] = off;  off = align_up(off + sizeof(uint32_t) * H * (size_t)zha_apply_chunks((int64_t)n));
     }
     attn_partials(cfg, off, y.pm, y.pl, y.po, y.nact);
     y.noparent = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(64, H));   // one entry per group
@@ -184,6 +178,27 @@ int attn_blocks(int64_t n_slots, int H, int kv_dtype) {
 }
 
 float tau_of(const zha_config* cfg) { return 1.0f / std::sqrt((float)cfg->head_dim); }
+
+// Highest level with a complete node over n_tokens tokens (0: none).
+int top_level(const zha_config* cfg, int64_t n_tokens) {
+    for (int l = cfg->levels; l >= 1; --l)
+        if (n_nodes(cfg, n_tokens, l) > 0) return l;
+    return 0;
+}
+
+// Levels of the chain, counted from the top: each at most ZHA_CHAIN_SLOTS complete
+// nodes, together at most ZHA_CHAIN_PLANES planes per group.
+int chain_levels(const zha_config* cfg, int64_t n_tokens, int top) {
+    int nchain = 0;
+    int64_t planes = 0;
+    for (int l = top; l >= 1 && nchain < ZHA_MAX_CHAIN; --l) {
+        if (n_nodes(cfg, n_tokens, l) > ZHA_CHAIN_SLOTS) break;
+        planes += n_nodes(cfg, n_tokens, l) * (int64_t)cfg->n_ref;
+        if (planes > ZHA_CHAIN_PLANES) break;
+        ++nchain;
+    }
+    return nchain;
+}
 
 }  // namespace
 
@@ -233,12 +248,19 @@ int zha_tree_level_offsets(const zha_config* cfg, int32_t level, int64_t* s_off,
     return ok();
 }
 
-int zha_route_level_offsets(const zha_config* cfg, int32_t level, zha_route_offsets* out) {
+int zha_route_level_offsets(const zha_config* cfg, int64_t n_tokens, int32_t level, zha_route_offsets* out) {
     int rc = validate(cfg);
     if (rc) return rc;
     if (!out) return fail(ZHA_ERR_ARG, "out is NULL");
     if (level < 1 || level > cfg->levels) return fail(ZHA_ERR_ARG, "level %d outside 1..%d", level, cfg->levels);
+    if (n_tokens < 1 || n_tokens > cfg->capacity)
+        return fail(ZHA_ERR_ARG, "n_tokens %lld outside 1..capacity", (long long)n_tokens);
     Layout y = make_layout(cfg);
+    const int top = top_level(cfg, n_tokens);
+    const int nchain = chain_levels(cfg, n_tokens, top);
+    out->chained = (level <= top && top - level < nchain) ? 1 : 0;
+    out->kbm = (int64_t)y.kbm[level];
+    out->wcap = y.wcap[level];
     out->n_cand = (int64_t)y.ncand[level];
     out->sigma = (int64_t)y.sig[level];
     out->n_kept = (int64_t)y.nkept[level];
@@ -246,6 +268,7 @@ int zha_route_level_offsets(const zha_config* cfg, int32_t level, zha_route_offs
     out->mask = (int64_t)y.kmask[level];
     out->stats = (int64_t)y.stats[level];
     out->n_cap = y.cap[level];
+    out->sig_stride = y.sstr[level];
     return ok();
 }
 
@@ -336,32 +359,14 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     char* T = static_cast<char*>(bufs->tree);
     char* X = static_cast<char*>(bufs->scratch);
 
-    int top = 0;
-    for (int l = y.L; l >= 1; --l)
-        if (n_nodes(cfg, n_tokens, l) > 0) { top = l; break; }
+    const int top = top_level(cfg, n_tokens);
     if ((rc = record(events, 0, s))) return rc;
 
-    // The first routed levels, while small, form one chain: all their nodes scored
-    // in one launch, then selected level after level by one workgroup per group.
-    int nchain = 0;
-    {
-        int64_t planes = 0;
-        for (int l = top; l >= 1 && nchain < ZHA_MAX_CHAIN; --l) {
-            if (y.cap[l] > ZHA_SMALL_SLOTS || y.slices[l]) break;
-            planes += n_nodes(cfg, n_tokens, l) * (int64_t)R;
-            if (planes > ZHA_CHAIN_PLANES) break;
-            ++nchain;
-        }
-        if (nchain < 2) nchain = 0;   // a lone small level gains nothing
-    }
-    ZhaChainArgs chain;
-    chain.n = nchain;
-    // a large level above a routed one may leave its merge to the level below's
-    // score kernel
-    ZhaLevelArgs above;
-    bool defer_above = false;
-    for (int l = top; l >= 1; --l) {
-        ZhaLevelArgs a;
+    // Arguments of level l (parents: the kept list of level l + 1, or, at the first
+    // routed level, a small scratch region that no kernel writes, so that a kernel
+    // may issue its parent reads before it knows whether the level is the first).
+    auto level_args = [&](int l) {
+        ZhaLevelArgs a{};
         a.S = (const float*)(T + y.t_s[l]);
         a.B = (const float*)(T + y.t_b[l]);
         a.cap = y.cap[l];
@@ -370,31 +375,13 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.dc = zha_make_div((uint32_t)c);
         a.ncand = (int32_t*)(X + y.ncand[l]);
         a.sig = (float*)(X + y.sig[l]);
+        a.sstride = y.sstr[l];
         a.kbm = (uint64_t*)(X + y.kbm[l]);
         a.wcap = y.wcap[l];
         a.stats = (int32_t*)(X + y.stats[l]);
         a.klist = (int32_t*)(X + y.klist[l]);
         a.kmask = (uint32_t*)(X + y.kmask[l]);
         a.nkept = (int32_t*)(X + y.nkept[l]);
-        if (y.slices[l]) {
-            a.hblk = (float*)(X + y.hmax[l]);
-            a.hstate = (HugeCut*)(X + y.hcut[l]);
-            a.hdone = (uint32_t*)(X + y.hdone[l]);
-            a.hmass = (uint64_t*)(X + y.hmass[l]);
-            a.hcnt = (uint32_t*)(X + y.hcnt[l]);
-            a.tiem = (uint64_t*)(X + y.tiem[l]);
-            a.chunk_cnt = (uint32_t*)(X + y.chunk[l]);
-            a.slices = y.slices[l];
-        } else {
-            a.hblk = nullptr;
-            a.hstate = nullptr;
-            a.hdone = nullptr;
-            a.hmass = nullptr;
-            a.hcnt = nullptr;
-            a.tiem = nullptr;
-            a.chunk_cnt = nullptr;
-            a.slices = 0;
-        }
         if (l < top) {
             a.pklist = (const int32_t*)(X + y.klist[l + 1]);
             a.pkmask = (const uint32_t*)(X + y.kmask[l + 1]);
@@ -403,36 +390,81 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             a.orph_lo = (int64_t)c * n_nodes(cfg, n_tokens, l + 1);
             a.orph_hi = n_nodes(cfg, n_tokens, l);
         } else {
-            // the first routed level has no parents: the parent arrays point at a
-            // small scratch region that no kernel writes (their values go unused), so
-            // that a kernel may issue its parent reads before it knows whether the
-            // level is the first
             a.pklist = (const int32_t*)(X + y.noparent);
             a.pkmask = (const uint32_t*)(X + y.noparent);
             a.pnkept = (const int32_t*)(X + y.noparent);
             a.pcap = 1;
             a.orph_lo = a.orph_hi = 0;
         }
+        return a;
+    };
+
+    // The chain: the first small levels, every node scored by one launch, then each
+    // query head's workgroup selects them top-down.
+    const int nchain = chain_levels(cfg, n_tokens, top);
+    const int below = top - nchain;            // the next level to route (0: none)
+    if (nchain > 0) {
+        ZhaChainArgs sa{};
+        ZhaChainSel cs{};
+        sa.n = cs.n = nchain;
+        for (int i = 0; i < nchain; ++i) {
+            const int l = top - i;
+            sa.lv[i] = level_args(l);
+            sa.blocks[i] = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);
+            ZhaChainLevel& cl = cs.lv[i];
+            cl.sig = (const float*)(X + y.sig[l]);
+            cl.kbm = (uint64_t*)(X + y.kbm[l]);
+            cl.stats = (int32_t*)(X + y.stats[l]);
+            cl.cap = (int32_t)y.cap[l];
+            cl.n_nodes = (int32_t)n_nodes(cfg, n_tokens, l);
+            cl.orph_lo = l < top ? (int32_t)(c * n_nodes(cfg, n_tokens, l + 1)) : 0;
+            cl.orph_hi = l < top ? (int32_t)n_nodes(cfg, n_tokens, l) : 0;
+            cl.wcap = (int32_t)y.wcap[l];
+            cl.sstride = (int32_t)y.sstr[l];
+        }
+        hipError_t e = zha_launch_score_all(cfg->kv_dtype, q, sa, y.H, y.G, c, R, tau, s);
+        if (e != hipSuccess) return hip_fail(e, "score launch (chain)");
+        e = zha_launch_chain(cs, y.H, y.G, c, cfg->top_p, s);
+        if (e != hipSuccess) return hip_fail(e, "chain launch");
+        if (below == 0) {
+            // the chain reached level 1: its group kept list for the gather
+            ZhaLevelArgs a1 = level_args(1);
+            a1.top = 1;
+            a1.n_top = n_nodes(cfg, n_tokens, 1);
+            e = zha_launch_merge_ids(a1, y.H, y.G, c, s);
+            if (e != hipSuccess) return hip_fail(e, "merge launch (chain)");
+        }
+    }
+    // Every level below: score over the group's candidates, then select.  The first
+    // of them derives the chain's last level's group kept list in its score kernel.
+    for (int l = below; l >= 1; --l) {
+        ZhaLevelArgs a = level_args(l);
+        a.hblk = (float*)(X + y.hblk[l]);
+        a.ghist = (uint64_t*)(X + y.ghist[l]);
+        a.hdone = (uint32_t*)(X + y.hdone[l]);
+        a.hcut = (void*)(X + y.hcut[l]);
+        a.tick = (uint32_t*)(X + y.tick[l]);
+        a.desc = (uint32_t*)(X + y.desc[l]);
+        a.ndesc = zha_apply_chunks(y.cap[l]);
         const int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);
         a.score_blocks = blocks;
-        if (top - l < nchain) {
-            chain.lv[top - l] = a;
-            chain.blocks[top - l] = blocks;
-            if (top - l == nchain - 1) {
-                hipError_t e = zha_launch_route_chain(cfg->kv_dtype, q, chain, y.H, y.G, c, R, tau, cfg->top_p, s);
-                if (e != hipSuccess) return hip_fail(e, "route chain launch");
-            }
-            continue;
+        ZhaLevelArgs pa{};
+        const bool defer = nchain > 0 && l == below;
+        if (defer) {
+            // the chain's last level: positions are node ids, per-head bitmaps over them
+            pa = level_args(l + 1);
+            pa.top = 1;
+            pa.n_top = n_nodes(cfg, n_tokens, l + 1);
+            pa.pklist = (const int32_t*)(X + y.noparent);
+            pa.pkmask = (const uint32_t*)(X + y.noparent);
+            pa.pnkept = (const int32_t*)(X + y.noparent);
+            pa.pcap = 1;
         }
-        const bool defer = l >= 2 && y.cap[l] > ZHA_SMALL_SLOTS && !y.slices[l] &&
-                           zha_defer_fits(y.G, y.wcap[l], a.top ? 0 : a.pcap);
         hipError_t e = zha_launch_route_score(cfg->kv_dtype, q, a, y.H, y.G, c, R, tau, blocks, s,
-                                              defer_above ? &above : nullptr);
+                                              defer ? &pa : nullptr);
         if (e != hipSuccess) return hip_fail(e, "route score launch");
-        e = zha_launch_route_select(a, y.H, y.G, c, cfg->top_p, s, !defer);
+        e = zha_launch_select(a, y.H, y.G, c, cfg->top_p, s);
         if (e != hipSuccess) return hip_fail(e, "route select launch");
-        above = a;
-        defer_above = defer;
     }
 
     ZhaAttnArgs at_;
@@ -471,7 +503,10 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             r.nkept[l - 1] = (const int32_t*)(X + y.nkept[l]);
             r.hstats[l - 1] = (const int32_t*)(X + y.stats[l]);
             r.routed[l - 1] = n_nodes(cfg, n_tokens, l) > 0 ? 1 : 0;
-            r.all_nodes[l - 1] = top - l < nchain ? n_nodes(cfg, n_tokens, l) : 0;
+            r.all_nodes[l - 1] = (l <= top && top - l < nchain) ? n_nodes(cfg, n_tokens, l) : 0;
+            r.kbm[l - 1] = (const uint64_t*)(X + y.kbm[l]);
+            r.wcap[l - 1] = (int32_t)y.wcap[l];
+            r.n_nodes[l - 1] = n_nodes(cfg, n_tokens, l);
         }
         r.klist1 = at_.klist;
         r.cap1 = at_.cap1;

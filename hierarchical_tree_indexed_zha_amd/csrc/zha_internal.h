@@ -47,22 +47,13 @@ __device__ __forceinline__ uint32_t zha_div(uint32_t n, const ZhaDiv& v) {
 // are the children of the level above's kept nodes (its kept list, ascending,
 // with the heads that kept each) followed by this level's orphans, nodes
 // [orph_lo, orph_hi) seen by every head.
-// The selection cut of one query head at a sliced level, as far as the digit
-// passes have found it (one per head, written by the last slice of each pass).
-struct HugeCut {
-    uint32_t done;                        // 1 when the cut key is known
-    uint32_t ustar, ties;                 // the cut: largest kept key, keys equal to it
-    uint32_t mshift, mval, bshift, bmask; // the next pass's digit, when not done
-    uint32_t pad;
-    uint64_t need;                        // mass still needed inside the current prefix
-};
-static_assert(sizeof(HugeCut) == 40, "HugeCut layout");
+#define ZHA_HIST_BINS 2048     // bins of a selection digit histogram
 
 struct ZhaLevelArgs {
     const float* S;            // level planes [H_kv][cap][R][128]
     const float* B;            // [H_kv][cap][R]
     int64_t cap;               // node slots per head at this level
-    int top;                   // 1 at the first routed level
+    int top;                   // 1 at the first routed level (positions are node ids)
     int64_t n_top;             // candidates at the first routed level (all its nodes)
     // the level above: its kept nodes are this level's parents (at the first routed
     // level: readable memory with pcap 1, whose values go unused)
@@ -73,64 +64,69 @@ struct ZhaLevelArgs {
     int64_t orph_lo, orph_hi;  // this level's orphans
     ZhaDiv dc;                 // division by the chunk size
     int32_t* ncand;            // out [H_kv]: candidates at this level
-    float* sig;                // [H_kv][G][cap]
+    float* sig;                // [H_kv][G][sstride]
+    int64_t sstride;           // row stride of sig: cap rounded up to a multiple of 4 (16-byte rows)
     uint64_t* kbm;             // per-head kept bitmaps [H_kv][G][wcap]
     int64_t wcap;              // bitmap words per head
     int32_t* stats;            // out [H_q][2]
     int32_t* klist;            // out: kept nodes [H_kv][cap], ascending
     uint32_t* kmask;           // out: their head masks
     int32_t* nkept;            // out [H_kv]
-    // Levels with more than ZHA_SLICED_MIN_CAP node slots select over slices of
-    // ZHA_SLICE positions spread over the whole GPU (null otherwise):
+    // selection state of a level below the chain (null at chained levels):
     float* hblk;               // [H_q][ZHA_SCORE_MAXB] largest score per head in each score block
     int score_blocks;          // score blocks per group (entries of hblk per head)
-    HugeCut* hstate;           // [H_q] the cut found so far per head
-    uint32_t* hdone;           // [3][H_q] slices done per pass
-    uint64_t* hmass;           // [3][H_q][2048] per-pass digit histograms: fixed-point mass
-    uint32_t* hcnt;            // [3][H_q][2048] and count
-    uint64_t* tiem;            // [H_q][slices] mass of cut-equal keys per slice
-    uint32_t* chunk_cnt;       // [H_kv][wcap / 512] kept nodes per 512-word chunk
-    int slices;                // slices per head
+    uint64_t* ghist;           // [H_q][ZHA_HIST_BINS] first-digit mass histograms of the select slices
+    uint32_t* hdone;           // [H_q] select slice workgroups done
+    void* hcut;                // [H_q] each head's cut (16 bytes)
+    uint32_t* tick;            // [H_kv] apply chunks started
+    uint32_t* desc;            // [H_kv][ndesc] look-back descriptors of the apply chunks
+    int ndesc;                 // apply chunks per group at this level's capacity
 };
 // One field in each 64-byte line of a level's arguments, and the arguments that
 // follow them, demanded at kernel entry: the argument loads then go out in one
 // batch (the compiler otherwise fetches them in dependent rounds behind uniform
 // branches, each a memory round trip on a cold argument line).
 #define ZHA_LEVEL_ARGS_READY(a, ...) \
-    asm volatile("" ::"s"((a).S), "s"((a).pcap), "s"((a).wcap), "s"((a).hdone), "s"((a).slices), __VA_ARGS__)
-#define ZHA_LDS_KEYS 32768     // candidates per head selected in one workgroup's LDS
-#define ZHA_SLICE 32768        // positions per slice workgroup of a sliced level
-#define ZHA_SLICED_MIN_CAP 262144   // levels with more node slots select over slices
-// A large level (more than ZHA_SMALL_SLOTS node slots, not sliced) whose G heads'
-// bitmap words together number at most ZHA_DEFER_WORDS and whose parents at most
-// ZHA_DEFER_PARENTS is selected without a merge launch: the score kernel of the
-// level below (`defer` = the level above's arguments) derives its kept list from
-// the bitmaps in LDS and writes it.
+    asm volatile("" ::"s"((a).S), "s"((a).pcap), "s"((a).wcap), "s"((a).hblk), "s"((a).ndesc), __VA_ARGS__)
+#define ZHA_LDS_KEYS 32768     // a head's keys staged in LDS by the workgroup that cuts it
+// The level below the chain derives the chain's last level's group kept list from
+// the chain's per-head bitmaps (`defer` = that level's arguments: top = 1, n_top
+// its complete nodes, bitmaps over node ids) in its score kernel; at most
+// ZHA_DEFER_WORDS head words staged.
 #define ZHA_DEFER_WORDS 2048
-#define ZHA_DEFER_PARENTS 4096
-bool zha_defer_fits(int G, int64_t wcap, int64_t pcap);
-size_t zha_defer_lds_bytes(int G, int64_t wcap, int64_t pcap);
+size_t zha_defer_lds_bytes(int G, int64_t n);
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream,
                                   const ZhaLevelArgs* defer = nullptr);
-// merge = false leaves a large, unsliced level's kept list to the next level's
-// score kernel (zha_launch_route_score with `defer`)
-hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream,
-                                   bool merge = true);
+hipError_t zha_launch_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream);
+int zha_apply_chunks(int64_t cap);
 int zha_score_blocks(int64_t max_cand, int R);
-// The first routed levels while they are small (node slots <= ZHA_SMALL_SLOTS,
-// together at most ZHA_CHAIN_PLANES planes per group): every node scored by one
-// launch, then the levels selected one after the other by one workgroup per group.
-#define ZHA_SMALL_SLOTS 1024
-#define ZHA_MAX_CHAIN 6
+// The chain: the first routed levels while each has at most ZHA_CHAIN_SLOTS node
+// slots and together at most ZHA_CHAIN_PLANES planes per group; every node scored
+// by one launch, then each query head's workgroup selects them one after the other.
+#define ZHA_CHAIN_SLOTS 4096
+#define ZHA_MAX_CHAIN 8
 #define ZHA_CHAIN_PLANES 32768
-struct ZhaChainArgs {
+struct ZhaChainArgs {                 // scoring every node of the chained levels
     ZhaLevelArgs lv[ZHA_MAX_CHAIN];   // lv[0] is the first routed level
     int blocks[ZHA_MAX_CHAIN];        // score workgroups per group for each level
     int n;
 };
-hipError_t zha_launch_route_chain(int kv_dtype, const void* q, const ZhaChainArgs& m, int H_kv, int G, int c, int R,
-                                  float tau, float top_p, hipStream_t stream);
+struct ZhaChainLevel {                // selecting one chained level
+    const float* sig;                 // node-indexed scores [H_kv][G][sstride]
+    uint64_t* kbm;                    // out: per-head kept bitmaps over node ids [H_kv][G][wcap]
+    int32_t* stats;                   // out [H_q][2]: candidates, kept
+    int32_t cap, n_nodes, orph_lo, orph_hi, wcap, sstride;
+};
+struct ZhaChainSel {
+    ZhaChainLevel lv[ZHA_MAX_CHAIN];
+    int n;
+};
+hipError_t zha_launch_score_all(int kv_dtype, const void* q, const ZhaChainArgs& m, int H_kv, int G, int c, int R,
+                                float tau, hipStream_t stream);
+hipError_t zha_launch_chain(const ZhaChainSel& m, int H_kv, int G, int c, float top_p, hipStream_t stream);
+// the group kept list of a chained level 1 (bitmaps over node ids; a.top = 1)
+hipError_t zha_launch_merge_ids(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream);
 
 // ---- attention (zha_attn.hip)
 struct ZhaAttnArgs {
@@ -160,7 +156,10 @@ struct ZhaReportArgs {
     const int32_t* ncand[32];    // per level l (index l-1): [H_kv] union candidates
     const int32_t* nkept[32];    // [H_kv] nodes kept by some head
     const int32_t* hstats[32];   // [H_q][2] per head: candidates, kept
-    int64_t all_nodes[32];       // > 0: the level's every node was scored (its count per head)
+    int64_t all_nodes[32];       // > 0: a chained level, its every node scored (its count per head)
+    int64_t n_nodes[32];         // complete nodes per head
+    const uint64_t* kbm[32];     // chained levels: per-head kept bitmaps over node ids [H_kv][G][wcap]
+    int32_t wcap[32];
     int32_t routed[32];          // 1 when the level has a complete node
     const int32_t* klist1;       // level-1 kept list [H_kv][cap1]
     int64_t cap1;                // 0 when no level was routed

@@ -48,22 +48,51 @@ __global__ __launch_bounds__(kSelThreads) void zha_sel_kernel(const int32_t* __r
     if (tid == 0) row[0] = (int32_t)s_run;
 }
 
-// grid 1, 64 threads: the step's zha_stats from the per-level counts.
-__global__ __launch_bounds__(64) void zha_stats_kernel(ZhaReportArgs r, zha_stats* __restrict__ out) {
-    const int lane = threadIdx.x;
+// grid 1, 256 threads: the step's zha_stats from the per-level counts.  At a
+// chained level (every node scored, per-head kept bitmaps over node ids) the group
+// kept nodes are the popcount of the OR of the group's head bitmaps, and the group
+// candidates are the children of the level above's group kept nodes plus the
+// orphans (every node at the top).
+__global__ __launch_bounds__(256) void zha_stats_kernel(ZhaReportArgs r, zha_stats* __restrict__ out) {
+    __shared__ unsigned long long s_gk[ZHA_STATS_MAX_LEVELS];
+    const int tid = threadIdx.x;
     const int Hq = r.H * r.G;
-    for (int l = lane; l < ZHA_STATS_MAX_LEVELS; l += 64) {
+    if (tid < ZHA_STATS_MAX_LEVELS) s_gk[tid] = 0ull;
+    __syncthreads();
+    for (int l = 0; l < r.levels; ++l) {
+        if (!r.routed[l] || r.all_nodes[l] == 0) continue;   // uniform
+        unsigned long long cnt = 0;
+        const int wc = r.wcap[l];                         // row stride
+        const int nw = (int)((r.n_nodes[l] + 63) / 64);   // words holding complete nodes
+        for (int i = tid; i < r.H * nw; i += 256) {
+            const int g = i / nw, w = i - g * nw;
+            uint64_t u = 0;
+            for (int hh = 0; hh < r.G; ++hh) u |= r.kbm[l][((size_t)g * r.G + hh) * wc + w];
+            cnt += (unsigned long long)__popcll(u);
+        }
+        if (cnt) atomicAdd(&s_gk[l], cnt);
+    }
+    __syncthreads();
+    if (tid < ZHA_STATS_MAX_LEVELS) {
+        const int l = tid;
         int64_t cand = 0, kept = 0, gc = 0, gk = 0, streamed = 0;
         if (l < r.levels && r.routed[l]) {
             for (int h = 0; h < Hq; ++h) {
                 cand += r.hstats[l][2 * h + 0];
                 kept += r.hstats[l][2 * h + 1];
             }
-            for (int g = 0; g < r.H; ++g) {
-                gc += r.ncand[l][g];
-                gk += r.nkept[l][g];
+            if (r.all_nodes[l] > 0) {
+                gk = (int64_t)s_gk[l];
+                if (l + 1 == r.top) gc = r.n_nodes[l] * r.H;
+                else gc = (int64_t)r.c * (int64_t)s_gk[l + 1] + (int64_t)r.H * (r.n_nodes[l] - r.c * r.n_nodes[l + 1]);
+                streamed = r.all_nodes[l] * r.H * r.plane_bytes;
+            } else {
+                for (int g = 0; g < r.H; ++g) {
+                    gc += r.ncand[l][g];
+                    gk += r.nkept[l][g];
+                }
+                streamed = gc * r.plane_bytes;
             }
-            streamed = r.all_nodes[l] > 0 ? r.all_nodes[l] * r.H * r.plane_bytes : gc * r.plane_bytes;
         }
         out->cand[l] = cand;
         out->kept[l] = kept;
@@ -72,7 +101,7 @@ __global__ __launch_bounds__(64) void zha_stats_kernel(ZhaReportArgs r, zha_stat
         out->bytes_read[l] = gc * r.plane_bytes;
         out->bytes_streamed[l] = streamed;
     }
-    if (lane == 0) {
+    if (tid == 0) {
         // tokens attended per group: kept chunks, the sink unless chunk 0 is kept, the tail
         const int64_t n1 = r.n_tokens / r.c;
         int64_t toks = 0;
@@ -99,6 +128,6 @@ hipError_t zha_launch_sel(const int32_t* klist, const uint32_t* kmask, const int
 }
 
 hipError_t zha_launch_stats(const ZhaReportArgs& r, zha_stats* out, hipStream_t stream) {
-    hipLaunchKernelGGL(zha_stats_kernel, dim3(1), dim3(64), 0, stream, r, out);
+    hipLaunchKernelGGL(zha_stats_kernel, dim3(1), dim3(256), 0, stream, r, out);
     return hipGetLastError();
 }

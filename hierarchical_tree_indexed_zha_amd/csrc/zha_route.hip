@@ -19,13 +19,23 @@
 // as 2^40-scaled integers e_i = exp(sigma_i - max) so that every sum is exact and
 // order-free (bitwise-reproducible).  Candidates are ranked by delta_i = max -
 // sigma_i quantised to 2^-27 (monotone in sigma) and the cut is found by a
-// mass-weighted radix select; candidates whose quantised delta equals the cut's
-// are taken in ascending position (= node) order until the cumulative mass
-// reaches ceil(p * sum e).  Small frontiers (<= 1024 candidates per group) are
-// selected by one workgroup, one wave per head, with 8-bit digits; larger ones
-// by one 1024-thread workgroup per head with 11/11/10-bit digits, whose kept
-// flags go to per-head bitmaps over the candidate positions.  A merge kernel, or
-// the next level's score kernel, turns the bitmaps into the group's kept list.
+// mass-weighted radix select over 11/11/10-bit digits; candidates whose quantised
+// delta equals the cut's are taken in ascending position (= node) order until the
+// cumulative mass reaches ceil(p * sum e).
+//
+// Levels, top-down:
+//   * the chain: the first levels of at most ZHA_CHAIN_SLOTS node slots are scored
+//     whole by one launch (every node, every head), then one workgroup per query
+//     head selects them one after the other with its own kept set in LDS, and
+//     writes per-head kept bitmaps over node ids;
+//   * every level below: a score launch over the group's candidates (the children
+//     of the group's kept nodes of the level above, then the level's orphans),
+//     then one selection launch: a group whose frontier has at most 1024
+//     candidates is selected by one workgroup; larger frontiers are histogrammed
+//     over slices by up to eight workgroups per head, the head's last workgroup
+//     finishes its cut and the group's last head merges the heads' kept bitmaps
+//     into the group's kept list.  Below the chain, the first score kernel derives
+//     the chain's last level's group kept list from the per-head bitmaps.
 //
 // The candidates of a level are never written out: they are the children of the
 // level above's kept nodes (kept list and head masks, ascending) followed by the
@@ -45,6 +55,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr float kFix = 1099511627776.0f;   // 2^40: fixed-point scale of e_i in [0, 1]
 constexpr float kKeyScale = 134217728.0f;  // 2^27: delta quantum
 constexpr float kDeltaMax = 32.0f;         // e^-32 * 2^40 < 1: heavier deltas carry no mass
+constexpr int kHistBins = ZHA_HIST_BINS;    // bins of a selection digit histogram
 
 // threadIdx.x as a value that the compiler cannot hoist out of a loop: per-lane
 // addresses are recomputed where they are used instead of held in registers
@@ -77,42 +88,33 @@ __device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
 }
 
-// A level whose merge is left to the level below it: the score workgroups of the
-// level below stage its per-head kept bitmaps (position-indexed, [G][wc] words),
-// their union and its popcount prefix, and the kept list of the level above it
-// (its parents), then read any entry of its kept list from LDS.
+// The chain's last level, whose group kept list is derived by the score
+// workgroups of the level below it: they stage its per-head kept bitmaps over node
+// ids ([G][wc] words, wc = ceil(n / 64) for its n complete nodes), their union and
+// its popcount prefix, then read any entry of its kept list from LDS.
 constexpr int kDeferW = ZHA_DEFER_WORDS / kScoreThreads;    // head words per thread
-constexpr int kDeferP = ZHA_DEFER_PARENTS / kScoreThreads;  // parent entries per thread
-static_assert(kDeferW * kScoreThreads == ZHA_DEFER_WORDS && kDeferP * kScoreThreads == ZHA_DEFER_PARENTS,
-              "deferred merge staging");
+static_assert(kDeferW * kScoreThreads == ZHA_DEFER_WORDS, "deferred merge staging");
+static_assert(ZHA_MAX_GROUP * (ZHA_CHAIN_SLOTS / 64) <= ZHA_DEFER_WORDS, "a chained level's head words fit");
 
 struct DeferView {
     const uint64_t* hw;    // [G][wc] head words
-    const uint64_t* u;     // [wc] union of the head words (zero from word nw on)
+    const uint64_t* u;     // [wc] union of the head words
     const uint32_t* pre;   // [wc] kept nodes in the words below
-    const int32_t* gk;     // the level's parents (kept list of the level above it)
-    int wc, nw, gn;        // words per head, words holding candidates, parents kept
+    int wc;                // words per head
 };
 
-// Node id and head mask of the level's candidate at position qp.
-__device__ __forceinline__ void defer_node(const ZhaLevelArgs& pa, const DeferView& v, int G, int c, int qp,
-                                           int32_t& node, uint32_t& mask) {
+// Head mask of the level's node qp.
+__device__ __forceinline__ uint32_t defer_mask(const DeferView& v, int G, int qp) {
     const int w = qp >> 6, b = qp & 63;
-    if (pa.top) node = qp;
-    else if (qp < v.gn * c) {
-        const int gi = (int)zha_div((uint32_t)qp, pa.dc);
-        node = v.gk[gi] * c + (qp - gi * c);
-    } else node = (int32_t)pa.orph_lo + (qp - v.gn * c);
     uint32_t m = 0;
     for (int hh = 0; hh < G; ++hh) m |= (uint32_t)((v.hw[hh * v.wc + w] >> b) & 1ull) << hh;
-    mask = m;
+    return m;
 }
 
 // Entry r (< the kept count) of the level's kept list: the word holding it (the
 // last whose prefix is <= r), then its bit by halving popcounts.
-__device__ __forceinline__ void defer_entry(const ZhaLevelArgs& pa, const DeferView& v, int G, int c, uint32_t r,
-                                            int32_t& node, uint32_t& mask) {
-    int lo = 0, hi = v.nw - 1;
+__device__ __forceinline__ void defer_entry(const DeferView& v, int G, uint32_t r, int32_t& node, uint32_t& mask) {
+    int lo = 0, hi = v.wc - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (v.pre[mid] <= r) lo = mid;
@@ -130,7 +132,8 @@ __device__ __forceinline__ void defer_entry(const ZhaLevelArgs& pa, const DeferV
             b += sh;
         }
     }
-    defer_node(pa, v, G, c, lo * 64 + b, node, mask);
+    node = lo * 64 + b;
+    mask = defer_mask(v, G, node);
 }
 
 // Scores one level's candidates for every head of group g, as workgroup blk of
@@ -174,29 +177,19 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     uint32_t pm = 0;
     int pn_raw = 0;
     uint64_t dw[DEF ? kDeferW : 1];
-    int32_t dg[DEF ? kDeferP : 1];
     if (DEF) {
-        // the level above's head words, its parents' node ids and their count
-        const int nall = G * (int)pa->wcap;
+        // the chain's last level's head words over its complete nodes
+        const int wcd = (int)((pa->n_top + 63) >> 6), nall = G * wcd;
         const uint64_t* kb = pa->kbm + (size_t)g * G * pa->wcap;
 #pragma unroll
         for (int k = 0; k < kDeferW; ++k) {
             dw[k] = 0ull;
             if (k * kScoreThreads < nall) {           // uniform: slots wholly past the end skipped
                 const int i = (int)threadIdx.x + k * kScoreThreads;
-                if (i < nall) dw[k] = kb[i];
+                const int hh = i / wcd, w = i - hh * wcd;
+                if (i < nall) dw[k] = kb[(size_t)hh * pa->wcap + w];
             }
         }
-        const int gcap = pa->top ? 0 : (int)pa->pcap;
-#pragma unroll
-        for (int k = 0; k < kDeferP; ++k) {
-            dg[k] = 0;
-            if (k * kScoreThreads < gcap) {
-                const int i = (int)threadIdx.x + k * kScoreThreads;
-                if (i < gcap) dg[k] = pa->pklist[(size_t)g * pa->pcap + i];
-            }
-        }
-        pn_raw = pa->pnkept[g];
     } else {
         const int pi0 = min((int)zha_div((uint32_t)(it * U + cl), a.dc), pcap - 1);
         pk = a.pklist[prow + pi0];
@@ -233,59 +226,35 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
         extern __shared__ __align__(16) uint64_t zha_defer_lds[];
         __shared__ uint32_t s_wsum[kScoreThreads / 64];
         const int tid = threadIdx.x;
-        const int wc = (int)pa->wcap, nall = G * wc;
-        const int gcap = pa->top ? 0 : (int)pa->pcap;
+        const int wc = (int)((pa->n_top + 63) >> 6), nall = G * wc;
         uint64_t* hw = zha_defer_lds;
         uint64_t* uu = hw + nall;
         uint32_t* pre = reinterpret_cast<uint32_t*>(uu + wc);
-        int32_t* gk = reinterpret_cast<int32_t*>(pre + wc);
-        const int gn = pa->top ? 0 : pn_raw;
-        const int nl = pa->top ? (int)pa->n_top : gn * c + (int)(pa->orph_hi - pa->orph_lo);
-        const int nwl = (nl + 63) >> 6;
 #pragma unroll
         for (int k = 0; k < kDeferW; ++k) {
             const int i = tid + k * kScoreThreads;
             if (i < nall) hw[i] = dw[k];
         }
-#pragma unroll
-        for (int k = 0; k < kDeferP; ++k) {
-            const int i = tid + k * kScoreThreads;
-            if (i < gcap) gk[i] = dg[k];
-        }
         __syncthreads();
-        // union of words [tid P, tid P + P) (words from nwl on hold no candidate),
-        // then the workgroup's exclusive popcount prefix
-        const int P = (wc + kScoreThreads - 1) / kScoreThreads;
-        uint32_t cnt = 0;
-#pragma unroll 1
-        for (int k = 0; k < P; ++k) {
-            const int w = tid * P + k;
-            uint64_t x = 0;
-            if (w < nwl)
-                for (int hh = 0; hh < G; ++hh) x |= hw[hh * wc + w];
-            if (w < wc) uu[w] = x;
-            cnt += (uint32_t)__popcll(x);
-        }
+        // union word tid (wc <= 64 words), then the workgroup's exclusive popcount prefix
+        uint64_t x = 0;
+        if (tid < wc)
+            for (int hh = 0; hh < G; ++hh) x |= hw[hh * wc + tid];
+        if (tid < wc) uu[tid] = x;
+        const uint32_t cnt = (uint32_t)__popcll(x);
         const uint32_t inc = (uint32_t)zha_wave_incl_scan_u64(cnt);
         if (lane == 63) s_wsum[wave] = inc;
         __syncthreads();
         uint32_t run = inc - cnt, tot = 0;
 #pragma unroll
         for (int w2 = 0; w2 < kScoreThreads / 64; ++w2) {
-            const uint32_t x = s_wsum[w2];
-            run += w2 < wave ? x : 0u;
-            tot += x;
+            const uint32_t y = s_wsum[w2];
+            run += w2 < wave ? y : 0u;
+            tot += y;
         }
-#pragma unroll 1
-        for (int k = 0; k < P; ++k) {
-            const int w = tid * P + k;
-            if (w < wc) {
-                pre[w] = run;
-                run += (uint32_t)__popcll(uu[w]);
-            }
-        }
+        if (tid < wc) pre[tid] = run;
         __syncthreads();
-        dv = DeferView{hw, uu, pre, gk, wc, nwl, gn};
+        dv = DeferView{hw, uu, pre, wc};
         pn_raw = (int)tot;
     }
     if (top) {
@@ -310,7 +279,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
             } else if (pos < pn * c) {
                 // child pos % c of the kept parent at index pos / c
                 const int pi = (int)zha_div((uint32_t)pos, a.dc);
-                if (DEF) defer_entry(*pa, dv, G, c, (uint32_t)pi, pk, pm);
+                if (DEF) defer_entry(dv, G, (uint32_t)pi, pk, pm);
                 node = pk * c + (pos - pi * c);
                 cm = pm;
             } else {
@@ -365,7 +334,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int h = 4 * kq + i;
-                if (h < G) a.sig[((size_t)g * G + h) * a.cap + (size_t)pos] = ((cm >> h) & 1u) ? best[i] : zha_neg_inf();
+                if (h < G) a.sig[((size_t)g * G + h) * a.sstride + (size_t)pos] = ((cm >> h) & 1u) ? best[i] : zha_neg_inf();
             }
         }
         if (valid) {
@@ -375,30 +344,39 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
         }
     }
     // Stores issued before the loop would hold up its first loads (the memory
-    // counter waits are in order), so the counts and the derived kept list go last.
+    // counter waits are in order), so the counts, the cleared selection state and
+    // the derived kept list go last.
     if (blk == 0 && threadIdx.x == 0) a.ncand[g] = n_cand;
+    if (!ALL && a.desc) {
+        // this level's selection histograms and counters, apply tickets and look-back
+        // descriptors, for the select and apply kernels' atomics
+        if (blk == 0 && (int)threadIdx.x == 0) a.tick[g] = 0u;
+        if (blk == 0 && (int)threadIdx.x < G) a.hdone[g * G + threadIdx.x] = 0u;
+        uint32_t* desc = a.desc + (size_t)g * a.ndesc;
+        for (int i = blk * kScoreThreads + (int)threadIdx.x; i < a.ndesc; i += nblk * kScoreThreads) desc[i] = 0u;
+        uint64_t* gm = a.ghist + (size_t)g * G * kHistBins;
+        for (int i = blk * kScoreThreads + (int)threadIdx.x; i < G * kHistBins; i += nblk * kScoreThreads) gm[i] = 0ull;
+    }
     if constexpr (DEF) {
-        // this workgroup's share of the level above's kept list: words 4 blk + wave
-        // + 4 nblk k, one position per lane
+        // this workgroup's share of the chain's last level's kept list: words 4 blk +
+        // wave + 4 nblk k, one node per lane
         int32_t* kl = pa->klist + (size_t)g * pa->cap;
         uint32_t* km = pa->kmask + (size_t)g * pa->cap;
 #pragma unroll 1
-        for (int w = blk * 4 + wave; w < dv.nw; w += 4 * nblk) {
+        for (int w = blk * 4 + wave; w < dv.wc; w += 4 * nblk) {
             const uint64_t x = dv.u[w];
             if (lane_bit(x, lane)) {
-                int32_t node;
-                uint32_t msk;
-                defer_node(*pa, dv, G, c, w * 64 + lane, node, msk);
+                const int node = w * 64 + lane;
                 const uint32_t rank = dv.pre[w] + bits_below_lane(x);
                 kl[rank] = node;
-                km[rank] = msk;
+                km[rank] = defer_mask(dv, G, node);
             }
         }
         if (blk == 0 && threadIdx.x == 0) pa->nkept[g] = pn;
     }
 }
 
-// Sliced levels: the largest score of each head over this workgroup.
+// The largest score of each head over this workgroup (for the selection's maximum).
 __device__ __forceinline__ void block_head_max(const ZhaLevelArgs& a, int g, int G, const float (&hm)[4]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, kq = lane >> 4;
@@ -488,78 +466,21 @@ __device__ __forceinline__ uint64_t mass_of(uint32_t key) {
     return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// Large frontiers: 2048-bin histograms of key digits 31..21, 20..10 and 9..0.
-// Bin b sits at b + b / 32 so that one lane's 32 consecutive bins are read
-// without LDS bank conflicts.
-constexpr int kHistBins = 2048;
-constexpr int kHistPadded = kHistBins + kHistBins / 32;
-__device__ __forceinline__ int hpad(uint32_t b) { return (int)(b + (b >> 5)); }
-
-// Run by one whole wave: the bin b with before(b) < need <= before(b) + hist[b]
-// (before(b) = mass of the bins below b) goes to *out_bin / *out_before.  When
-// `need` is 0 it is first set to ceil(p * total) (clamped to [1, total]).  Two
-// scans: over the 64 lanes' 32-bin sums, then over the 32 bins of the lane
-// whose range holds the crossing.
-__device__ void wave_find_cross(const uint64_t* hist, uint64_t need, float top_p, int* out_bin,
-                                uint64_t* out_before, uint64_t* out_need) {
-    const int lane = threadIdx.x & 63;
-    const uint64_t* row = hist + lane * 33;
-    uint64_t mine = 0;
-#pragma unroll 8
-    for (int i = 0; i < 32; ++i) mine += row[i];
-    uint64_t total;
-    const uint64_t before = wave_excl_scan_u64(mine, &total);
-    if (need == 0) {
-        uint64_t T = (uint64_t)ceil((double)top_p * (double)total);
-        if (T < 1) T = 1;
-        if (T > total) T = total;
-        need = T;
-    }
-    const uint64_t hit = __ballot(before < need && before + mine >= need);
-    const int L = hit ? __ffsll((long long)hit) - 1 : 63;
-    const uint64_t base = zha_readlane_u64(before, L);
-    const uint64_t x = lane < 32 ? hist[L * 33 + lane] : 0ull;
-    uint64_t t2;
-    const uint64_t ex = wave_excl_scan_u64(x, &t2);
-    const uint64_t hit2 = __ballot(lane < 32 && base + ex < need && base + ex + x >= need);
-    const int jb = hit2 ? __ffsll((long long)hit2) - 1 : 31;
-    const uint64_t ex_j = zha_readlane_u64(ex, jb);
-    if (lane == 0) {
-        *out_bin = L * 32 + jb;
-        *out_before = base + ex_j;
-        *out_need = need;
-    }
-}
-
-constexpr int kLdsKeys = ZHA_LDS_KEYS;        // heads with at most this many candidates keep their keys in LDS
-constexpr int kSlots = kLdsKeys / kSelThreads;   // positions tid + 1024 k held in registers while staging
-constexpr int kMergeW = kLdsKeys / 64;        // bitmap words merged per step
-constexpr int kBatch = 8;                     // LDS keys read together in a pass
-constexpr int kGlobBatch = 16;                // scores re-read together from global memory
-constexpr int kMergeBlocks = 64;              // merge workgroups per group
-constexpr int kRankMax = 128;                 // crossing-bin keys ranked directly instead of histogrammed
-static_assert((kSlots & (kSlots - 1)) == 0 && kSlots % kBatch == 0, "slot batches");
+// Selection histograms: 2048 bins of key digits 31..21, 20..10 and 9..0.
+constexpr int kBT = 1024;                     // threads of a selecting workgroup
+constexpr int kBW = kBT / 64;
+constexpr int kLdsKeys = ZHA_LDS_KEYS;        // a head's keys staged in LDS by the workgroup that cuts it
 constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup
-static_assert(kSmallN == ZHA_SMALL_SLOTS, "small levels");
+static_assert(kSmallN == kSelThreads && kBT == kSelThreads, "small path: one position per thread");
 constexpr int kSmallK = kSmallN / 64;
-static_assert(kSelThreads == kSmallN, "small path: one position per thread");
-static_assert(2 * ZHA_MAX_GROUP * kMergeW + kMergeW * 32 <= kLdsKeys,
-              "merge: head words and parent ids must fit the key buffer");
-static_assert(kMergeW + kMergeW / 2 <= kHistPadded, "merge: union words and prefixes must fit the histogram");
-static_assert(kMergeW <= kSelThreads, "merge: one thread per word of a step");
 static_assert(ZHA_MAX_GROUP * (kSmallN + 2 * 256) + kSmallN <= kLdsKeys, "small path inside the key buffer");
-static_assert(ZHA_MAX_GROUP * kSmallK <= kHistPadded, "small-path kept words inside the histogram");
-
-// The cut inside a crossing bin that holds few keys.  Ordered by (key,
-// position), the bin's keys are taken while the mass before them is below
-// `need` (what the bin must still supply); the cut is the key, and the position,
-// whose own mass reaches it.  Entry e = {key, position, mass lo, mass hi}: the mass
-// before entry j is the sum over the entries that precede it in that order.
-__device__ __forceinline__ bool rank_precedes(const uint4& f, const uint4& e) {
-    return f.x < e.x || (f.x == e.x && f.y < e.y);
-}
-__device__ __forceinline__ uint64_t entry_mass(const uint4& e) { return ((uint64_t)e.w << 32) | e.z; }
-
+static_assert(ZHA_MAX_GROUP * kSmallK <= kHistBins, "small-path kept words inside the histogram");
+constexpr int kKeyRegs = kLdsKeys / kBT;       // positions per thread of a staged head
+constexpr int kSlice = 4 * kBT;                 // positions a slice workgroup histograms (four per thread)
+constexpr int kSliceW = 8;                      // slice workgroups per head
+constexpr int kChainSlots = ZHA_CHAIN_SLOTS;
+constexpr int kChainPer = kChainSlots / kBT;  // candidate positions per thread in the chain
+static_assert(kChainPer * kBT == kChainSlots && kChainPer * kBW <= 64, "chain rows: one scan lane per (row, wave)");
 // Small-path histogram bins pack a key count above a mass sum: at most kSmallN
 // keys of mass <= 2^40 sum below 2^52, so the fields never carry into each other
 // and one 64-bit LDS atomic per key updates both.
@@ -690,7 +611,7 @@ __device__ __forceinline__ int stage_small(const ZhaLevelArgs& a, int g, int G, 
 #pragma unroll
     for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
         v[hh] = zha_neg_inf();
-        if (hh < G && in) v[hh] = a.sig[((size_t)g * G + hh) * a.cap + tid];   // hh < G: uniform
+        if (hh < G && in) v[hh] = a.sig[((size_t)g * G + hh) * a.sstride + tid];   // hh < G: uniform
     }
     const int pi = (int)zha_div((uint32_t)tid, a.dc);
     const int32_t pk = pi < a.pcap ? a.pklist[(size_t)g * a.pcap + pi] : 0;   // unused at the first level
@@ -794,1008 +715,709 @@ __device__ __forceinline__ void select_small_group(const ZhaLevelArgs& a, int g,
     }
 }
 
-// grid (H_kv), 1024 threads: levels with at most kSmallN node slots.  The
-// group's workgroup stages every head's scores with one round trip and selects.
-__global__ __launch_bounds__(kSelThreads) void zha_select_small_kernel(ZhaLevelArgs a, int G, int c,
-                                                                       float top_p) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p));
-    __shared__ __align__(16) float s_sig[ZHA_MAX_GROUP * kSmallN];
-    __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
-    __shared__ int32_t s_nid[kSmallN];
-    __shared__ __align__(16) uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
 
-    const int g = blockIdx.x;
-    const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
-    const int pn = stage_small(a, g, G, c, threadIdx.x, s_sig, s_nid);
-    const int n = a.top ? (int)a.n_top : pn * c + n_orph;
+// ---- block-wide selection: the minimal top-p cut of one head over n keys, by one
+// 1024-thread workgroup.  Position p's key comes from a functor; positions are
+// walked p = tid + 1024 k.  A 2048-bin LDS histogram of the fixed-point mass of
+// the first key digit (bits 31..21) locates the bin where the cumulative mass
+// reaches ceil(p * total); the crossing bin's keys are then gathered, and if there
+// are at most kRankMax of them the cut is found by ranking them directly, else by
+// the next digit (bits 20..10, then 9..0).  Keys equal to the cut key all carry
+// the same mass m, so the first t = ceil(need / m) of them in position order are
+// kept (ties by ascending node index).
+
+struct LdsKeys {
+    const uint32_t* k;
+    __device__ uint32_t operator()(int p) const { return k[p]; }
+};
+struct GlobKeys {        // frontiers beyond the LDS keys: formed again from the scores
+    const float* sg;
+    float m;
+    __device__ uint32_t operator()(int p) const { return key_of(sg[p], m); }
+};
+
+constexpr int kRankMax = 128;  // crossing-bin keys ranked directly
+constexpr int kGather = kBT;   // crossing-bin keys listed for the later passes (one per thread)
+static_assert(kBT % kRankMax == 0 && kRankMax % (kBT / kRankMax) == 0, "rank split");
+
+struct CutShared {
+    uint64_t ws[kBW];          // per-wave sums
+    uint32_t wc[kBW];          // per-wave counts
+    int bin;
+    uint32_t nent, plim, ustar;
+    uint64_t before, need;
+    uint4 ent[kRankMax];       // the crossing bin's keys: {key, position, mass lo, mass hi}
+    uint64_t rank[kRankMax];   // mass of the entries before each
+};
+
+// The bin b of hist where before(b) < need <= before(b) + hist[b] (before(b): the
+// mass of the bins below b), found by the whole workgroup (two bins per thread).
+// need0 = 0: need = ceil(p * total), clamped to [1, total].  Results in st.
+__device__ __forceinline__ void block_find(const uint64_t* hist, uint64_t need0, float top_p, CutShared* st) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+    const uint64_t sum = h0 + h1;
+    const uint64_t inc = zha_wave_incl_scan_u64(sum);
+    if (lane == 63) st->ws[wave] = inc;
     __syncthreads();
-    select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw);
+    uint64_t wb = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kBW; ++w) {
+        const uint64_t x = st->ws[w];
+        wb += w < wave ? x : 0ull;
+        total += x;
+    }
+    uint64_t need = need0;
+    if (need == 0) {
+        need = (uint64_t)ceil((double)top_p * (double)total);
+        if (need < 1) need = 1;
+        if (need > total) need = total;
+    }
+    const uint64_t bt = wb + inc - sum;
+    if (bt < need && bt + h0 >= need) {
+        st->bin = 2 * tid;
+        st->before = bt;
+        st->need = need;
+    } else if (bt + h0 < need && bt + sum >= need) {
+        st->bin = 2 * tid + 1;
+        st->before = bt + h0;
+        st->need = need;
+    }
+    __syncthreads();
 }
 
-// grid (H_kv), 1024 threads: the first routed levels, all small, selected one
-// after the other by one workgroup per group with the kept lists in LDS.  Every
-// node of these levels was scored beforehand (positions = node ids); each level
-// gathers its candidates' scores, writes them back in candidate order, and
-// selects.
-__global__ __launch_bounds__(kSelThreads) void zha_select_chain_kernel(ZhaChainArgs m, int G, int c, float top_p) {
-    __shared__ __align__(16) float s_sig[ZHA_MAX_GROUP * kSmallN];
-    __shared__ __align__(16) uint64_t s_hist[ZHA_MAX_GROUP * 256];
-    __shared__ int32_t s_nid[kSmallN];
-    __shared__ __align__(16) uint64_t s_kw[ZHA_MAX_GROUP * kSmallK];
-    __shared__ int32_t s_pk[kSmallN];
-    __shared__ uint32_t s_pm[kSmallN];
-    __shared__ int s_pn;
-
-    const int g = blockIdx.x;
-    const uint32_t allg = all_heads(G);
+// The cut of one head: kept iff key < ustar, or key == ustar and p <= plim.  With
+// `pre0`, hist already holds the first digit's histogram over all keys.  Called by
+// the whole workgroup when the head has candidates and p < 1.  Each pass finds the
+// crossing bin of its digit, then counts the bin's keys (building the next digit's
+// histogram over them) and writes them out at their block-wide ranks: to the rank
+// table when there are at most kRankMax of them (the cut is then found by ranking
+// them), and, the first time there are at most kGather of them, to the list gl
+// [kGather] that later passes sweep instead of all n keys.
+template <class KF>
+__device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint64_t* hist, uint2* gl,
+                          CutShared* st, uint32_t& ustar, uint32_t& plim) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t pref = 0;
+    uint64_t need = 0;
+    ustar = 0;
+    plim = 0xFFFFFFFFu;
+    if (!pre0) {
+        hist[2 * tid] = 0ull;
+        hist[2 * tid + 1] = 0ull;
+        __syncthreads();
+#pragma unroll 4
+        for (int p = tid; p < n; p += kBT) {
+            const uint32_t k = key_at(p);
+            if (k < kNoMass) atomicAdd((unsigned long long*)&hist[k >> 21], (unsigned long long)mass_of(k));
+        }
+        __syncthreads();
+    }
+    int nl = -1;                               // >= 0: the crossing keys of an earlier pass are gl[0, nl)
 #pragma unroll 1
-    for (int li = 0; li < m.n; ++li) {
-        const ZhaLevelArgs& a = m.lv[li];
-        const int p = lane_tid();                      // candidate position (n <= kSmallN)
-        const int pn = li == 0 ? 0 : s_pn;
-        const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-        int32_t node = 0;
-        uint32_t msk = 0;
-        if (p < n) {
-            if (a.top) {
-                node = p;
-                msk = allg;
-            } else if (p < pn * c) {
-                const int pi = (int)zha_div((uint32_t)p, a.dc);
-                node = s_pk[pi] * c + (p - pi * c);
-                msk = s_pm[pi];
-            } else {
-                node = (int32_t)a.orph_lo + (p - pn * c);
-                msk = allg;
+    for (int pass = 0; pass < 3; ++pass) {
+        const uint32_t shift = pass == 0 ? 21u : pass == 1 ? 10u : 0u;
+        block_find(hist, need, top_p, st);     // (ends with a barrier: hist free again)
+        const uint32_t bin = (uint32_t)st->bin;
+        need = st->need - st->before;          // mass still needed inside the crossing bin
+        pref = pass == 0 ? bin : ((pref << (pass == 1 ? 11 : 10)) | bin);
+        // the next digit (bits 20..10, then 9..0) of the crossing bin's keys
+        const uint32_t nshift = pass == 0 ? 10u : 0u;
+        const uint32_t nmask = pass == 0 ? 2047u : 1023u;
+        if (pass < 2) {
+            hist[2 * tid] = 0ull;
+            hist[2 * tid + 1] = 0ull;
+        }
+        if (tid < kRankMax) st->rank[tid] = 0ull;
+        __syncthreads();
+        // this thread's crossing keys: counted (and histogrammed) first
+        uint32_t cnt = 0;
+        uint2 le = make_uint2(kNotCand, 0u);   // listed: this thread's list entry
+        if (nl >= 0) {
+            if (tid < nl) le = gl[tid];
+            const bool in = le.x < kNoMass && (le.x >> shift) == pref;
+            cnt = in;
+            if (in && pass < 2) atomicAdd((unsigned long long*)&hist[(le.x >> nshift) & nmask], (unsigned long long)mass_of(le.x));
+        } else {
+#pragma unroll 4
+            for (int p = tid; p < n; p += kBT) {
+                const uint32_t k = key_at(p);
+                const bool in = k < kNoMass && (k >> shift) == pref;
+                cnt += in;
+                if (in && pass < 2) atomicAdd((unsigned long long*)&hist[(k >> nshift) & nmask], (unsigned long long)mass_of(k));
             }
         }
-        float v[ZHA_MAX_GROUP];
-#pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
-            v[hh] = zha_neg_inf();
-            if (hh < G && p < n && ((msk >> hh) & 1u)) v[hh] = a.sig[((size_t)g * G + hh) * a.cap + node];
-        }
-        __syncthreads();                               // every gather done before the write-back below
-        // all gathered values in registers at once (otherwise the compiler waits for
-        // each write-back store before the next LDS write)
-        asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
-                     "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
-#pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-            if (hh < G) s_sig[hh * kSmallN + p] = v[hh];
-        s_nid[p] = node;
-        float* sgw = a.sig + (size_t)g * G * a.cap + p;
-        if (p < n) {
-#pragma unroll
-            for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-                if (hh < G) sgw[(size_t)hh * a.cap] = v[hh];
-        }
-        if (p == 0) a.ncand[g] = n;
+        const uint32_t inc = (uint32_t)zha_wave_incl_scan_u64(cnt);
+        if (lane == 63) st->wc[wave] = inc;
         __syncthreads();
-        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw, s_pk, s_pm, &s_pn);
+        uint32_t e = inc - cnt, ne = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kBW; ++w2) {
+            const uint32_t x = st->wc[w2];
+            e += w2 < wave ? x : 0u;
+            ne += x;
+        }
+        const bool to_rank = ne <= (uint32_t)kRankMax;
+        const bool to_list = nl < 0 && ne <= (uint32_t)kGather;
+        if (cnt && (to_rank || to_list)) {
+            if (nl >= 0) {
+                const uint64_t ms = mass_of(le.x);
+                st->ent[e] = make_uint4(le.x, le.y, (uint32_t)ms, (uint32_t)(ms >> 32));
+            } else {
+                for (int p = tid; p < n; p += kBT) {
+                    const uint32_t k = key_at(p);
+                    if (k < kNoMass && (k >> shift) == pref) {
+                        if (to_rank) {
+                            const uint64_t ms = mass_of(k);
+                            st->ent[e] = make_uint4(k, (uint32_t)p, (uint32_t)ms, (uint32_t)(ms >> 32));
+                        }
+                        if (to_list) gl[e] = make_uint2(k, (uint32_t)p);
+                        ++e;
+                    }
+                }
+            }
+        }
         __syncthreads();
+        if (to_list) nl = (int)ne;
+        if (to_rank) {
+            // rank them: entry i's mass before it in (key, position) order is summed by
+            // kBT / kRankMax threads, each over kRankMax / (kBT / kRankMax) entries j
+            // (the same j for a whole wave: broadcast reads); the entry whose own mass
+            // reaches what the bin must supply is the cut
+            {
+                constexpr int kSl = kBT / kRankMax, kPerSl = kRankMax / kSl;
+                const int i = tid % kRankMax, q = tid / kRankMax;
+                const uint4 me = st->ent[i < (int)ne ? i : 0];
+                uint64_t acc = 0;
+#pragma unroll
+                for (int jj = 0; jj < kPerSl; ++jj) {
+                    const int j = q * kPerSl + jj;
+                    if (j < (int)ne) {
+                        const uint4 f = st->ent[j];
+                        const bool prec = f.x < me.x || (f.x == me.x && f.y < me.y);
+                        acc += prec ? (((uint64_t)f.w << 32) | f.z) : 0ull;
+                    }
+                }
+                if (i < (int)ne && acc) atomicAdd((unsigned long long*)&st->rank[i], (unsigned long long)acc);
+            }
+            __syncthreads();
+            if (tid < (int)ne) {
+                const uint4 me = st->ent[tid];
+                const uint64_t before = st->rank[tid], own = ((uint64_t)me.w << 32) | me.z;
+                if (before < need && before + own >= need) {
+                    st->ustar = me.x;
+                    st->plim = me.y;
+                }
+            }
+            __syncthreads();
+            ustar = st->ustar;
+            plim = st->plim;
+            return;
+        }
+        if (pass == 2) {
+            // more than kRankMax keys equal to the cut key: the first t of them in
+            // position order
+            ustar = pref;
+            const uint64_t ms = mass_of(ustar);
+            const uint64_t t = (need + ms - 1) / ms;
+            if (tid == 0) st->plim = 0xFFFFFFFFu;
+            __syncthreads();
+            uint32_t run = 0;
+#pragma unroll 1
+            for (int base = 0; base < n; base += kBT) {
+                const int p = base + tid;
+                const bool tie = p < n && key_at(p) == ustar;
+                const uint64_t bal = __ballot(tie);
+                if (lane == 0) st->wc[wave] = (uint32_t)__popcll(bal);
+                __syncthreads();
+                uint32_t before = run, tot = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < kBW; ++w2) {
+                    const uint32_t x = st->wc[w2];
+                    before += w2 < wave ? x : 0u;
+                    tot += x;
+                }
+                if (tie && before + bits_below_lane(bal) + 1 == (uint32_t)t) st->plim = (uint32_t)p;
+                __syncthreads();
+                run += tot;
+                if (run >= (uint32_t)t) break;   // uniform
+            }
+            plim = st->plim;
+            return;
+        }
     }
 }
 
-// grid (H_q), 1024 threads: levels with more than kSmallN node slots, one query
-// head per workgroup.  Up to kLdsKeys candidates the keys stay in LDS (position
-// tid + 1024 k in slot k); larger frontiers recompute them from the scores on
-// every pass.  Each head writes its kept bitmap; the kept list is formed later.
-// A frontier of at most kSmallN candidates is instead selected for every head,
-// and its kept list written, by the group's first workgroup (the small path).
-__global__ __launch_bounds__(kSelThreads) void zha_select_large_kernel(ZhaLevelArgs a, int G, int c,
-                                                                       float top_p, int small_only) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(small_only));
-    // keys: the keys (for the ordered tie pass); merge: head words [kMergeW][16]
-    // (u64), then the step's parent node ids
-    __shared__ __align__(16) uint32_t keys[kLdsKeys];
-    __shared__ __align__(16) uint64_t hist[kHistPadded];   // merge: union words, then popcount prefixes
-    __shared__ uint32_t cntb[kHistBins];
-    __shared__ uint64_t s_wt[kSelWaves];
-    __shared__ float swf[kSelWaves];
-    __shared__ int s_bin;
-    __shared__ uint64_t s_before, s_need, s_run;
-    __shared__ uint32_t s_cnt[2];
-    // the keys of the previous pass's crossing bin {key, position, mass lo, mass hi}
-    // while there are at most kRankMax, their partial ranks, their count, the cut
-    __shared__ __align__(16) uint4 s_ent[kRankMax];
-    __shared__ uint64_t s_rank[kRankMax];
-    __shared__ uint32_t s_nent, s_cut[2];
+__device__ __forceinline__ bool kept_by(uint32_t key, uint32_t p, bool none, bool keep_all, uint32_t ustar,
+                                        uint32_t plim) {
+    return !none && key != kNotCand &&
+           (keep_all || (key < kNoMass && (key < ustar || (key == ustar && p <= plim))));
+}
 
+// Maximum over the workgroup (every thread receives it).
+__device__ __forceinline__ float block_max(float x, float* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    x = zha_wave_max(x);
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kBW; ++w) m = fmaxf(m, red[w]);
+    __syncthreads();
+    return m;
+}
+
+// ---- the chain: the first routed levels, each at most kChainSlots complete nodes,
+// every node of them scored beforehand (node-indexed scores).  One workgroup per
+// query head walks them top-down with its own kept set in LDS: its candidates at a
+// level are the children of its kept nodes of the level above, in ascending node
+// order, then the level's orphans.  Per level it writes its kept bitmap over node
+// ids and its candidate and kept counts.
+__global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, int c, float top_p) {
+    __shared__ __align__(16) uint32_t s_keys[kChainSlots];
+    __shared__ int32_t s_kept[kChainSlots];
+    __shared__ __align__(16) uint64_t s_hist[kHistBins];
+    __shared__ uint2 s_gl[kGather];
+    __shared__ uint64_t s_bm[kChainSlots / 64];
+    __shared__ uint32_t s_pre[kChainPer * kBW];
+    __shared__ uint32_t s_tot[2];
+    __shared__ float s_red[kBW];
+    __shared__ CutShared st;
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (small_only) {
-        // a sliced level: only a frontier of at most kSmallN candidates is selected
-        // here (by the group's first workgroup); the slice kernels take larger ones
-        const int pn0 = a.top ? 0 : a.pnkept[g];
-        const int n0 = a.top ? (int)a.n_top : pn0 * c + (int)(a.orph_hi - a.orph_lo);
-        if (n0 > kSmallN || hl != 0) return;
-        float* s_sig = reinterpret_cast<float*>(keys);                                   // [G][kSmallN]
-        uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
-        int32_t* s_nid = reinterpret_cast<int32_t*>(keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256);
-        stage_small(a, g, G, c, tid, s_sig, s_nid);
+    int nk = 0;
+#pragma unroll 1
+    for (int li = 0; li < m.n; ++li) {
+        const ZhaChainLevel& L = m.lv[li];
+        const int n = li == 0 ? L.n_nodes : nk * c + (L.orph_hi - L.orph_lo);
+        const float* sg = L.sig + ((size_t)g * G + hl) * (size_t)L.sstride;
+        int32_t node[kChainPer];
+        float x[kChainPer];
+#pragma unroll
+        for (int k = 0; k < kChainPer; ++k) {
+            const int p = tid + k * kBT;
+            int32_t nd = p;
+            if (li > 0) {
+                const int pc = p < nk * c ? p : 0;
+                const int pi = pc / c;
+                nd = p < nk * c ? s_kept[pi] * c + (pc - pi * c) : L.orph_lo + (p - nk * c);
+            }
+            node[k] = p < n ? nd : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kChainPer; ++k) x[k] = tid + k * kBT < n ? sg[node[k]] : zha_neg_inf();
+        float mx = zha_neg_inf();
+#pragma unroll
+        for (int k = 0; k < kChainPer; ++k) mx = fmaxf(mx, x[k]);
+        const float M = block_max(mx, s_red);   // (its barriers also end every read of s_kept)
+        uint32_t key[kChainPer];
+#pragma unroll
+        for (int k = 0; k < kChainPer; ++k) {
+            const int p = tid + k * kBT;
+            key[k] = p < n ? key_of(x[k], M) : kNotCand;
+            s_keys[p] = key[k];
+        }
+        for (int i = tid; i < kChainSlots / 64; i += kBT) s_bm[i] = 0ull;
         __syncthreads();
-        select_small_group(a, g, G, top_p, n0, s_sig, s_nid, s_hist, hist);
-        return;
-    }
-    const int n_orph = a.top ? 0 : (int)(a.orph_hi - a.orph_lo);
-    const float* sg = a.sig + ((size_t)g * G + hl) * a.cap;
-
-    // The count and the scores of the first half of the LDS positions are read
-    // together (one round trip, bounded by the capacity); the second half's reads,
-    // bounded by the count, follow as soon as it arrives.  Positions >= n are
-    // ignored afterwards.
-    // (slots that lie wholly past the bound are skipped by a uniform branch: no
-    // per-lane work for them)
-    uint32_t kr[kSlots];
-    const int lim = (int)min(a.cap, (int64_t)kLdsKeys);
+        const bool none = M == zha_neg_inf();
+        const bool keep_all = !none && top_p >= 1.0f;
+        uint32_t ustar = 0, plim = 0xFFFFFFFFu;
+        if (!none && !keep_all) block_cut(LdsKeys{s_keys}, n, top_p, false, s_hist, s_gl, &st, ustar, plim);
+        // kept flags and their ranks in position order (rows of 1024 positions)
+        bool kept[kChainPer];
+        uint64_t bal[kChainPer];
+        uint32_t ncand = 0;
 #pragma unroll
-    for (int k = 0; k < kSlots / 2; ++k) {
-        kr[k] = __float_as_uint(zha_neg_inf());
-        if (k * kSelThreads < lim) {
-            const int pos = tid + k * kSelThreads;
-            if (pos < lim) kr[k] = __float_as_uint(sg[pos]);
+        for (int k = 0; k < kChainPer; ++k) {
+            const uint32_t p = (uint32_t)(tid + k * kBT);
+            kept[k] = kept_by(key[k], p, none, keep_all, ustar, plim);
+            bal[k] = __ballot(kept[k]);
+            ncand += (uint32_t)__popcll(__ballot(key[k] != kNotCand));
+            if (lane == 0) s_pre[k * kBW + wave] = (uint32_t)__popcll(bal[k]);
         }
-    }
-    const int pn = parent_count(a, g);
-    const int n = a.top ? (int)a.n_top : pn * c + n_orph;
-    {
-        const int lim2 = min(lim, n);
-#pragma unroll
-        for (int k = kSlots / 2; k < kSlots; ++k) {
-            kr[k] = __float_as_uint(zha_neg_inf());
-            if (k * kSelThreads < lim2) {
-                const int pos = tid + k * kSelThreads;
-                if (pos < lim2) kr[k] = __float_as_uint(sg[pos]);
-            }
-        }
-    }
-    if (n <= kSmallN) {
-        // a small frontier at a large level: the group's first workgroup selects for
-        // all heads, with the key buffer as its LDS
-        if (hl != 0) return;
-        float* s_sig = reinterpret_cast<float*>(keys);                                   // [G][kSmallN]
-        uint64_t* s_hist = reinterpret_cast<uint64_t*>(keys + ZHA_MAX_GROUP * kSmallN);  // [G][256]
-        int32_t* s_nid = reinterpret_cast<int32_t*>(keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256);
-        uint64_t* s_kw = hist;                                                           // [kSmallK][16]
-        stage_small(a, g, G, c, tid, s_sig, s_nid);
         __syncthreads();
-        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hist, s_kw);
-        return;
-    }
-    const int nwords = (n + 63) >> 6;
-    const int nslot = (n + kSelThreads - 1) / kSelThreads;   // positions per thread
-    const bool staged = n <= kLdsKeys;
-
-    if (tid < 2) s_cnt[tid] = 0;
-    float m = zha_neg_inf();
-    if (staged) {
-#pragma unroll
-        for (int k = 0; k < kSlots; ++k) {
-            if (k < nslot) {
-                if (tid + k * kSelThreads >= n) kr[k] = __float_as_uint(zha_neg_inf());
-                m = fmaxf(m, __uint_as_float(kr[k]));
-            }
+        if (wave == 0) {
+            const uint32_t v = lane < kChainPer * kBW ? s_pre[lane] : 0u;
+            uint64_t tot;
+            const uint32_t ex = (uint32_t)wave_excl_scan_u64(v, &tot);
+            if (lane < kChainPer * kBW) s_pre[lane] = ex;
+            if (lane == 0) s_tot[0] = (uint32_t)tot;
         }
-    } else {
-        // frontiers beyond the LDS keys: the scores are re-read (from L2) kGlobBatch
-        // positions per thread at a time, all reads of a batch in flight together
-#pragma unroll 1
-        for (int k0 = 0; k0 < nslot; k0 += kGlobBatch) {
-            float xs[kGlobBatch];
-#pragma unroll
-            for (int j = 0; j < kGlobBatch; ++j) {
-                const int pos = tid + (k0 + j) * kSelThreads;
-                xs[j] = pos < n ? sg[pos] : zha_neg_inf();
-            }
-#pragma unroll
-            for (int j = 0; j < kGlobBatch; ++j) m = fmaxf(m, xs[j]);
-        }
-    }
-    // the first pass's histogram, cleared before the barrier below
-    for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
-    for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
-    m = zha_wave_max(m);
-    if (lane == 0) swf[wave] = m;
-    __syncthreads();
-    m = swf[0];
-#pragma unroll
-    for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, swf[w]);
-
-    // Kept rule: keep_all, or key < ustar, or key == ustar when that key is unique
-    // (a ranked cut: key == ustar at a position <= plim).
-    const bool none = m == zha_neg_inf();        // this head has no candidate at this level
-    const bool keep_all = !none && top_p >= 1.0f;
-    const bool cut = !none && !keep_all;
-    if (staged) {
-        // keys to LDS and, when there is a cut to find, the first digit pass in the
-        // same loop: every key's mass into its top-digit bin, a key without mass
-        // adding zero to its lane's unused padding entry (33 lane + 32, never read)
-        const int dummy = 33 * lane + 32;
-#pragma unroll
-        for (int k = 0; k < kSlots; ++k) {
-            if (k < nslot) {
-                const uint32_t key = key_of(__uint_as_float(kr[k]), m);
-                keys[tid + k * kSelThreads] = key;
-                if (cut) {
-                    const bool has = key < kNoMass;
-                    const int at = has ? hpad((key >> 21) & 2047u) : dummy;
-                    const uint64_t ms = has ? mass_of(key) : 0ull;
-                    atomicAdd((unsigned long long*)&hist[at], (unsigned long long)ms);
-                }
-            }
-        }
-    }
-    uint32_t ustar = 0, ties = 0, plim = 0xFFFFFFFFu;
-    uint64_t need = 0;
-    if (cut) {
-        uint32_t mshift = 31, mval = 0, bshift = 21, bmask = 2047;
-        bool rec = false;                        // this pass records the previous crossing bin's keys
-#pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-            // pass 0 adds the mass of every key that carries mass; later passes count
-            // and add only the keys whose higher digits equal the bins found so far
-            const bool all = pass == 0;
-            if (staged) {
-                // pass 0 went with the staging; later passes read the keys from LDS
-                // kBatch slots at a time (all reads in flight together), test a batch
-                // first and touch the histogram only for the few keys that match
-#pragma unroll 1
-                for (int k0 = 0; k0 < (all ? 0 : nslot); k0 += kBatch) {
-                    uint32_t kk[kBatch];
-#pragma unroll
-                    for (int j = 0; j < kBatch; ++j) kk[j] = keys[tid + ((k0 + j) & (kSlots - 1)) * kSelThreads];
-                    {
-                        uint32_t hit = 0;
-#pragma unroll
-                        for (int j = 0; j < kBatch; ++j) {
-                            const uint32_t key = kk[j];
-                            const bool mt = k0 + j < nslot && key < kNoMass && (key >> mshift) == mval;
-                            hit |= (uint32_t)mt << j;
-                        }
-                        if (hit) {
-#pragma unroll
-                            for (int j = 0; j < kBatch; ++j) {
-                                if ((hit >> j) & 1u) {
-                                    const uint32_t key = kk[j];
-                                    const uint32_t b = (key >> bshift) & bmask;
-                                    const uint64_t ms = mass_of(key);
-                                    atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)ms);
-                                    atomicAdd(&cntb[b], 1u);
-                                    if (rec) {
-                                        const uint32_t e = atomicAdd(&s_nent, 1u);
-                                        if (e < kRankMax)
-                                            s_ent[e] = make_uint4(key, (uint32_t)(tid + (k0 + j) * kSelThreads),
-                                                                  (uint32_t)ms, (uint32_t)(ms >> 32));
-                                    }
-                                }
-                            }
-                        }
-                    }
-                }
-            } else {
-#pragma unroll 1
-                for (int k0 = 0; k0 < nslot; k0 += kGlobBatch) {
-                    float xs[kGlobBatch];
-#pragma unroll
-                    for (int j = 0; j < kGlobBatch; ++j) {
-                        const int pos = tid + (k0 + j) * kSelThreads;
-                        xs[j] = pos < n ? sg[pos] : zha_neg_inf();
-                    }
-#pragma unroll
-                    for (int j = 0; j < kGlobBatch; ++j) {
-                        const uint32_t key = key_of(xs[j], m);
-                        if (key < kNoMass && (all || (key >> mshift) == mval)) {
-                            const uint32_t b = (key >> bshift) & bmask;
-                            const uint64_t ms = mass_of(key);
-                            atomicAdd((unsigned long long*)&hist[hpad(b)], (unsigned long long)ms);
-                            if (!all) {
-                                atomicAdd(&cntb[b], 1u);
-                                if (rec) {
-                                    const uint32_t e = atomicAdd(&s_nent, 1u);
-                                    if (e < kRankMax)
-                                        s_ent[e] = make_uint4(key, (uint32_t)(tid + (k0 + j) * kSelThreads),
-                                                              (uint32_t)ms, (uint32_t)(ms >> 32));
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-            const int nent = rec ? (int)s_nent : 0;
-            if (nent > 0 && nent <= kRankMax) {
-                // the previous crossing bin holds few keys: rank them directly.  Entry j's
-                // mass before it is summed in C chunks of the entries (one chunk per
-                // thread, a wave's threads sharing theirs: broadcast reads), then the entry
-                // whose own mass reaches what the bin must supply is the cut.
-                const int np = (nent + 63) & ~63;
-                const int C = kSelThreads / np;
-                const int j = tid % np, ck = tid / np;
-                const int chunk = (nent + C - 1) / C;
-                if (j < nent && ck < C) {
-                    const uint4 e = s_ent[j];
-                    const int i0 = ck * chunk, i1 = min(nent, i0 + chunk);
-                    uint64_t acc = 0;
-#pragma unroll 4
-                    for (int i = i0; i < i1; ++i) {
-                        const uint4 f = s_ent[i];
-                        acc += rank_precedes(f, e) ? entry_mass(f) : 0ull;
-                    }
-                    if (i1 > i0) atomicAdd((unsigned long long*)&s_rank[j], (unsigned long long)acc);
-                }
-                __syncthreads();
-                if (tid < nent) {
-                    const uint4 e = s_ent[tid];
-                    const uint64_t before = s_rank[tid];
-                    if (before < need && before + entry_mass(e) >= need) {
-                        s_cut[0] = e.x;
-                        s_cut[1] = e.y;
-                    }
-                }
-                __syncthreads();
-                ustar = s_cut[0];
-                plim = s_cut[1];
-                ties = 1;
-                break;
-            }
-            if (wave == 0) wave_find_cross(hist, need, top_p, &s_bin, &s_before, &s_need);
-            __syncthreads();
-            const uint32_t bin = (uint32_t)s_bin;
-            need = s_need - s_before;            // mass still needed inside this bin
-            // pass 0 counts no keys (its bins hold many at these sizes): it never ends
-            // the search
-            const uint32_t cnt = pass == 0 ? 0u : cntb[bin];
-            const uint32_t pref = pass == 0 ? bin : (mval << (pass == 1 ? 11 : 10)) | bin;
-            if (cnt == 1 || pass == 2) {
-                // the crossing bin holds one key (or the keys equal to the cut): the cut
-                // is the largest key with this prefix
-                ustar = (pref << bshift) | ((1u << bshift) - 1u);
-                ties = cnt;
-                break;
-            }
-            {
-                // every key of the crossing bin has at least the mass of its largest key,
-                // so the bin's mass over that bounds how many keys the next pass meets
-                const uint64_t mmin = mass_of((pref << bshift) | ((1u << bshift) - 1u));
-                rec = mmin > 0 && hist[hpad(bin)] <= (uint64_t)kRankMax * mmin;
-            }
-            if (pass == 0) { mshift = 21; mval = pref; bshift = 10; bmask = 2047; }
-            else { mshift = 10; mval = pref; bshift = 0; bmask = 1023; }
-            __syncthreads();                     // every thread has read this pass's result
-            for (int i = tid; i < kHistPadded; i += kSelThreads) hist[i] = 0;
-            for (int i = tid; i < kHistBins; i += kSelThreads) cntb[i] = 0;
-            for (int i = tid; i < kRankMax; i += kSelThreads) s_rank[i] = 0;
-            if (tid == 0) {
-                s_nent = 0;
-                s_cut[0] = 0;
-                s_cut[1] = 0;
-            }
-            __syncthreads();
-        }
-    }
-    const uint64_t need_tie = need;
-
-    // kept flags -> this head's bitmap: slot k of wave w is word 16 k + w
-    uint64_t* bm = a.kbm + ((size_t)g * G + hl) * a.wcap;
-    uint32_t my_cand = 0, my_kept = 0;
-    if (staged) {
-#pragma unroll 1
-        for (int k = 0; k < nslot; ++k) {
-            {
-                const uint32_t key = keys[tid + k * kSelThreads];
-                const bool cand = key != kNotCand;
-                const bool kept = !none && (keep_all ? cand
-                                                     : (key < kNoMass &&
-                                                        (key < ustar || (key == ustar && ties == 1 &&
-                                                                         (uint32_t)(tid + k * kSelThreads) <= plim))));
-                const uint64_t word = __ballot(kept);
-                const int wi = k * kSelWaves + wave;
-                if (lane == 0 && wi < nwords) bm[wi] = word;
-                my_cand += cand;
-                my_kept += kept;
-            }
-        }
-    } else {
-#pragma unroll 1
-        for (int k0 = 0; k0 < nslot; k0 += kGlobBatch) {
-            float xs[kGlobBatch];
-#pragma unroll
-            for (int j = 0; j < kGlobBatch; ++j) {
-                const int pos = tid + (k0 + j) * kSelThreads;
-                xs[j] = pos < n ? sg[pos] : zha_neg_inf();
-            }
-#pragma unroll
-            for (int j = 0; j < kGlobBatch; ++j) {
-                const int k = k0 + j;
-                if (k < nslot) {
-                    const uint32_t key = key_of(xs[j], m);
-                    const bool cand = key != kNotCand;
-                    const bool kept = !none && (keep_all ? cand
-                                                         : (key < kNoMass &&
-                                                            (key < ustar || (key == ustar && ties == 1 &&
-                                                                             (uint32_t)(tid + k * kSelThreads) <= plim))));
-                    const uint64_t word = __ballot(kept);
-                    const int wi = k * kSelWaves + wave;
-                    if (lane == 0 && wi < nwords) bm[wi] = word;
-                    my_cand += cand;
-                    my_kept += kept;
-                }
-            }
-        }
-    }
-    if (!none && !keep_all && ties > 1) {
-        // several candidates share the cut key: take them in ascending position order
+        if (tid == 0) s_tot[1] = 0;
         __syncthreads();
-        __threadfence();
-        if (tid == 0) s_run = 0;
-#pragma unroll 1
-        for (int base = 0; base < n; base += kSelThreads) {
-            const int pos = base + tid;
-            const uint32_t key = pos < n ? (staged ? keys[pos] : key_of(sg[pos], m)) : kNotCand;
-            const uint64_t w = key == ustar ? mass_of(key) : 0ull;
-            uint64_t wt;
-            const uint64_t ex = wave_excl_scan_u64(w, &wt);
-            __syncthreads();
-            if (lane == 0) s_wt[wave] = wt;
-            __syncthreads();
-            uint64_t before = s_run;
-            for (int ww = 0; ww < wave; ++ww) before += s_wt[ww];
-            uint64_t tot = 0;
-            for (int ww = 0; ww < kSelWaves; ++ww) tot += s_wt[ww];
-            if (w > 0 && before + ex < need_tie) {
-                atomicOr((unsigned long long*)&bm[pos >> 6], 1ull << (pos & 63));
-                ++my_kept;
+#pragma unroll
+        for (int k = 0; k < kChainPer; ++k) {
+            if (kept[k]) {
+                const uint32_t r = s_pre[k * kBW + wave] + bits_below_lane(bal[k]);
+                s_kept[r] = node[k];
+                atomicOr((unsigned long long*)&s_bm[node[k] >> 6], 1ull << (node[k] & 63));
             }
-            __syncthreads();
-            if (tid == 0) s_run = s_run + tot;
-            __syncthreads();
-            if (s_run >= need_tie) break;
         }
-    }
-    {
-        const uint64_t both = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)my_kept << 32) | my_cand), 63);
-        if (lane == 0) {
-            atomicAdd(&s_cnt[0], (uint32_t)both);
-            atomicAdd(&s_cnt[1], (uint32_t)(both >> 32));
+        // candidates counted per wave above are the whole wave's: lane 0 of every wave
+        // adds them once
+        if (lane == 0) atomicAdd(&s_tot[1], ncand);
+        __syncthreads();
+        nk = (int)s_tot[0];
+        // the words holding the level's complete nodes (at most kChainSlots / 64)
+        uint64_t* bm = L.kbm + ((size_t)g * G + hl) * (size_t)L.wcap;
+        for (int i = tid; i < (L.n_nodes + 63) / 64; i += kBT) bm[i] = s_bm[i];
+        if (tid == 0) {
+            L.stats[2 * h + 0] = (int32_t)s_tot[1];
+            L.stats[2 * h + 1] = nk;
         }
-    }
-
-    __syncthreads();
-    if (tid == 0) {
-        a.stats[2 * h + 0] = (int32_t)s_cnt[0];
-        a.stats[2 * h + 1] = (int32_t)s_cnt[1];
+        __syncthreads();                        // LDS reused by the next level
     }
 }
 
-// grid (blocks, H_kv), 1024 threads: the kept list of a level whose heads were
-// selected by zha_select_large_kernel.  Block b owns bitmap words [b share,
-// (b + 1) share) of its group (share <= kMergeW, a multiple of 16): it ORs the G
-// heads' words, writes the kept list entries of its positions (ascending
-// position = ascending node) with the mask of heads that kept each node, and
-// offsets their ranks by the kept nodes in the words before its share.  The
-// count, the share's words, its parents' node ids and the words before it are
-// all read before the count is known (bounded by the capacities), so they cost
-// one memory round trip together.
-__global__ __launch_bounds__(kSelThreads) void zha_route_merge_kernel(ZhaLevelArgs a, int G, int c, int share) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(share));
-    // [word][16 heads (+1 padding)], heads >= G zero: a row of 17 words, so that the
-    // threads of a wave (consecutive rows) reach distinct LDS banks
-    constexpr int kRow = ZHA_MAX_GROUP + 1;
-    __shared__ __align__(16) uint64_t hw[kMergeW * kRow];
-    __shared__ int32_t s_par[kMergeW * 32];                            // parents' node ids
-    __shared__ uint64_t s_union[kMergeW];
-    __shared__ uint32_t s_wpre[kMergeW];
-    __shared__ uint32_t s_part[kSelWaves];
+// ---- the kept list of a group from its per-head kept bitmaps over node ids (a
+// chained level 1): each position's mask of heads, the ascending ranks of the
+// union's positions, and the list.  One 1024-thread workgroup per group.
+__global__ __launch_bounds__(kBT) void zha_merge_ids_kernel(ZhaLevelArgs a, int G, int c) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c));
+    __shared__ uint32_t s_wc[kChainPer * kBW];
     __shared__ uint32_t s_tot;
-    const int g = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wcap = (int)a.wcap;
-    const int w0 = blockIdx.x * share;
-    const int wend_s = min(w0 + share, wcap);                 // words this block may own
+    const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = (int)a.n_top;                    // <= kChainSlots
     const uint64_t* gbm = a.kbm + (size_t)g * G * a.wcap;
-    const int32_t* par = a.top ? nullptr : a.pklist + (size_t)g * a.pcap;
-    const int p0 = w0 * 64;
-    const int pb0 = (int)zha_div((uint32_t)p0, a.dc);
-    const int pb_s = a.top ? pb0 : min((int)a.pcap, (int)zha_div((uint32_t)(wend_s * 64 + c - 1), a.dc));
-    const int npar_s = max(0, pb_s - pb0);
-
-    constexpr int kPerW = ZHA_MAX_GROUP * kMergeW / kSelThreads;
-    constexpr int kPerP = kMergeW * 32 / kSelThreads;
-    uint64_t hv[kPerW];
-    int32_t pv[kPerP];
-    uint64_t pw[ZHA_MAX_GROUP];
-    // (slots whose heads or parents all lie past their bound are skipped by a
-    // uniform branch)
-    constexpr int kHeadsPerSlot = kSelThreads / kMergeW;
+    uint32_t msk[kChainPer];
+    uint64_t bal[kChainPer];
 #pragma unroll
-    for (int t = 0; t < kPerW; ++t) {
-        hv[t] = 0ull;
-        if (t * kHeadsPerSlot < G) {
-            const uint32_t i = (uint32_t)(tid + t * kSelThreads);
-            const uint32_t hh = i / kMergeW, wi = i % kMergeW;
-            if (hh < (uint32_t)G && w0 + (int)wi < wend_s) hv[t] = gbm[(size_t)hh * a.wcap + w0 + wi];
-        }
-    }
+    for (int k = 0; k < kChainPer; ++k) {
+        const int p = tid + k * kBT;
+        uint64_t hw[ZHA_MAX_GROUP];
 #pragma unroll
-    for (int t = 0; t < kPerP; ++t) {
-        pv[t] = 0;
-        if (t * kSelThreads < npar_s) {
-            const int i = tid + t * kSelThreads;
-            if (i < npar_s) pv[t] = par[pb0 + i];
-        }
-    }
-    const bool chunked = a.chunk_cnt != nullptr;   // sliced level: kept counts per 512-word chunk
-    const int nch = (wcap + kMergeW - 1) / kMergeW;
-    // (one straight-line block of reads: a branch here makes the compiler wait for
-    // every read before the two paths join; a sliced level reads its chunk counts
-    // after the early return)
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+            hw[hh] = (hh < G && p < n) ? gbm[(size_t)hh * a.wcap + (p >> 6)] : 0ull;
+        uint32_t m = 0;
 #pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
-        pw[hh] = 0ull;
-        if (!chunked && hh < G && tid < w0) pw[hh] = gbm[(size_t)hh * a.wcap + tid];
-    }
-    const int pn = parent_count(a, g);
-
-    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (n <= kSmallN) return;                    // selected and merged by the select kernel
-    const int nwords = (n + 63) >> 6;
-    if (w0 >= nwords) {
-        if (blockIdx.x == 0 && nwords == 0 && tid == 0) a.nkept[g] = 0;
-        return;
-    }
-    const int w1 = min(wend_s, nwords);
-    const int nw = w1 - w0;
-    const int pnc = pn * c;
-
-    // rank offset: kept nodes in words [0, w0)
-    uint32_t cnt = 0;
-    if (chunked) {
-#pragma unroll 1
-        for (int i = tid; i < w0 / kMergeW; i += kSelThreads) cnt += a.chunk_cnt[(size_t)g * nch + i];
-    } else {
-        uint64_t u = 0;
-#pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= pw[hh];
-        cnt = (uint32_t)__popcll(u);
-#pragma unroll 1
-        for (int w = tid + kSelThreads; w < w0; w += kSelThreads) {
-            uint64_t v = 0;
-            for (int hh = 0; hh < G; ++hh) v |= gbm[(size_t)hh * a.wcap + w];
-            cnt += (uint32_t)__popcll(v);
-        }
-    }
-    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-    if (lane == 0) s_part[wave] = cnt;
-#pragma unroll
-    for (int t = 0; t < kPerW; ++t) {
-        const uint32_t i = (uint32_t)(tid + t * kSelThreads);
-        hw[(i % kMergeW) * kRow + i / kMergeW] = (int)(i % kMergeW) < nw ? hv[t] : 0ull;
-    }
-#pragma unroll
-    for (int t = 0; t < kPerP; ++t) {
-        const int i = tid + t * kSelThreads;
-        if (i < npar_s) s_par[i] = pv[t];
-    }
-    __syncthreads();
-    uint32_t run = 0;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) run += s_part[w];
-    if (tid < nw) {
-        uint64_t u = 0;
-#pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= hw[tid * kRow + hh];
-        s_union[tid] = u;
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) m |= (uint32_t)((hw[hh] >> lane) & 1ull) << hh;
+        msk[k] = m;
+        bal[k] = __ballot(m != 0u);
+        if (lane == 0) s_wc[k * kBW + wave] = (uint32_t)__popcll(bal[k]);
     }
     __syncthreads();
     if (wave == 0) {
-        // exclusive popcount prefix of the union words (kMergeW / 64 words per lane)
-        constexpr int per = kMergeW / 64;
-        uint32_t c2 = 0;
-#pragma unroll
-        for (int q = 0; q < per; ++q) {
-            const int wi = lane * per + q;
-            c2 += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
-        }
+        const uint32_t v = s_wc[lane];
         uint64_t tot;
-        uint32_t pre = (uint32_t)wave_excl_scan_u64(c2, &tot);
-#pragma unroll
-        for (int q = 0; q < per; ++q) {
-            const int wi = lane * per + q;
-            s_wpre[wi] = pre;
-            pre += wi < nw ? (uint32_t)__popcll(s_union[wi]) : 0u;
-        }
+        s_wc[lane] = (uint32_t)wave_excl_scan_u64(v, &tot);
         if (lane == 0) s_tot = (uint32_t)tot;
     }
     __syncthreads();
     int32_t* kl = a.klist + (size_t)g * a.cap;
     uint32_t* km = a.kmask + (size_t)g * a.cap;
-    // word wi = 16 k + wave, bit = lane
-#pragma unroll 1
-    for (int wi = wave; wi < nw; wi += kSelWaves) {
-        const uint64_t u = s_union[wi];
-        const uint32_t pre = s_wpre[wi];
-        uint64_t hr[ZHA_MAX_GROUP];                   // the row's head words (one address per read)
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hr[hh] = hw[wi * kRow + hh];
-        const int pos = p0 + wi * 64 + lane;
-        const bool child = par && pos < pnc;
-        const int pi = (int)zha_div((uint32_t)pos, a.dc);
-        const int32_t pnode = child ? s_par[pi - pb0] : 0;
-        if (!lane_bit(u, lane)) continue;
-        // lane's bit of each head word
-        uint32_t msk = 0;
-#pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) msk |= (uint32_t)((hr[hh] >> lane) & 1ull) << hh;
-        const uint32_t rank = run + pre + bits_below_lane(u);
-        int32_t node;
-        if (!par) node = pos;
-        else if (child) node = pnode * c + (pos - pi * c);
-        else node = (int32_t)a.orph_lo + (pos - pnc);
-        kl[rank] = node;
-        km[rank] = msk;
+    for (int k = 0; k < kChainPer; ++k) {
+        if (msk[k]) {
+            const uint32_t r = s_wc[k * kBW + wave] + bits_below_lane(bal[k]);
+            kl[r] = tid + k * kBT;
+            km[r] = msk[k];
+        }
     }
-    if (w1 == nwords && tid == 0) a.nkept[g] = (int32_t)(run + s_tot);
+    if (tid == 0) a.nkept[g] = (int32_t)s_tot;
 }
 
+// ---- levels below the chain: two launches after the score kernel.
+//
+// zha_select_kernel, grid (kSliceW, H_q), 1024 threads: a frontier of at most
+// kSmallN candidates per group is selected for every head, and its kept list
+// written, by the group's first workgroup (small path).  Otherwise workgroup w of
+// head h adds the first-digit mass histogram of slices w, w + kSliceW, ... of the
+// head's candidates (kSlice positions each) into the head's global histogram with
+// integer atomics; the head's last workgroup to finish (a counter; every wave first
+// waits for its own atomics, and the histogram is read back with device-scope
+// loads, which bypass this device's non-coherent caches) stages the head's keys in
+// LDS, finishes the cut, and writes it as the head's cut descriptor with its
+// candidate and kept counts.  The histograms and counters were cleared by this
+// level's score kernel.
+//
+// zha_apply_kernel, grid (chunks, H_kv), 1024 threads: each workgroup takes the
+// next kApplyChunk candidate positions of its group (a ticket, so chunks run in
+// order of start), forms every position's mask of the heads that keep it from the
+// heads' scores and cuts, and writes the kept positions' entries of the group's
+// kept list at ranks found by a decoupled look-back: each chunk publishes its kept
+// count, then adds its predecessors' published counts (or a predecessor's
+// published inclusive prefix) to find where its entries start.  A chunk waits only
+// on chunks that started before it, so the waits always end.  Published values are
+// device-scope atomics read with device-scope loads.
+constexpr int kApplyThreads = 256;
+constexpr int kApplyWaves = kApplyThreads / 64;
+constexpr int kApplyChunk = 4 * kApplyThreads;    // positions per apply workgroup (four per thread)
+constexpr uint32_t kDescAgg = 1u << 30;           // descriptor: the chunk's kept count is published
+constexpr uint32_t kDescInc = 2u << 30;           // descriptor: its inclusive prefix is published
+constexpr uint32_t kDescVal = kDescAgg - 1u;
+constexpr uint32_t kSpinMax = 1u << 22;           // bound on a look-back wait (a safety net)
 
-// ---- levels with more than kLdsKeys node slots: the candidates of each head are
-// cut into slices of ZHA_SLICE positions, one 256-thread workgroup per (slice,
-// head), so a pass over the keys uses the whole GPU.  Digit histograms are summed
-// per head in global memory with integer atomics (exact and order-free); each
-// pass kernel first replays the crossings of the passes before it from those
-// histograms, so every workgroup reaches the same cut.
-
-constexpr int kHugeThreads = 1024;
-constexpr int kHugeWaves = kHugeThreads / 64;
-constexpr int kHugePer = ZHA_SLICE / kHugeThreads;   // positions per thread
-static_assert(ZHA_SLICE % 64 == 0 && kHugePer * kHugeThreads == ZHA_SLICE, "slice layout");
-static_assert(ZHA_SLICE % (kHugeWaves * 64) == 0, "a slice holds whole words of every wave");
-static_assert(kHugeWaves * 64 == kHugeThreads, "slot k of wave w is bitmap word (p0 >> 6) + w + kHugeWaves k");
-
-// grid (H_q), kHugeThreads (1024) threads: clears the level's histograms and counts.
-__global__ __launch_bounds__(kHugeThreads) void zha_huge_init_kernel(ZhaLevelArgs a, int Hq) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(Hq));
-    const int h = blockIdx.x;
-    for (int i = threadIdx.x; i < 3 * kHistBins; i += kHugeThreads) {
-        const int pass = i / kHistBins, b = i - pass * kHistBins;
-        a.hmass[((size_t)pass * Hq + h) * kHistBins + b] = 0ull;
-        a.hcnt[((size_t)pass * Hq + h) * kHistBins + b] = 0u;
-    }
-    if (threadIdx.x < 3) a.hdone[threadIdx.x * Hq + h] = 0u;
-    if (threadIdx.x == 0) {
-        a.stats[2 * h + 0] = 0;
-        a.stats[2 * h + 1] = 0;
-    }
-}
-
-// The candidate count of the level and the head's largest score (from the score
-// kernel's per-block maxima); called by the whole workgroup.
-struct SliceView {
-    int n, p0;
-    float m;
+struct HeadCut {                                  // written by zha_select_kernel per head
+    float m;                                      // largest score of the head's candidates
+    uint32_t ustar, plim;                         // kept: key < ustar, or key == ustar and position <= plim
+    uint32_t mode;                                // 0 cut, 1 keep all, 2 no candidate
 };
-// Candidates of head h at this level (a uniform scalar read: idle slices leave on it).
-__device__ __forceinline__ int head_n(const ZhaLevelArgs& a, int G, int c, int h) {
-    const int pn = a.top ? 0 : a.pnkept[h / G];
-    return a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-}
-__device__ __forceinline__ SliceView slice_view(const ZhaLevelArgs& a, int G, int c, int h, int s, float* red) {
+
+__global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, int c, float top_p) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p));
+    __shared__ __align__(16) uint32_t s_keys[kLdsKeys];
+    __shared__ __align__(16) uint64_t s_hist[kHistBins];
+    __shared__ uint2 s_gl[kGather];
+    __shared__ float s_red[kBW];
+    __shared__ uint64_t s_wred[kBW];
+    __shared__ CutShared st;
+    __shared__ int s_last;
+    const int h = blockIdx.y, g = h / G, hl = h - g * G, w = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = h / G;
-    SliceView v;
-    v.p0 = s * ZHA_SLICE;
-    const int pn = a.top ? 0 : a.pnkept[g];
-    float x = tid < a.score_blocks ? a.hblk[(size_t)h * ZHA_SCORE_MAXB + tid] : zha_neg_inf();
-    x = zha_wave_max(x);
-    if (lane == 0) red[wave] = x;
-    __syncthreads();
-    v.m = red[0];
-#pragma unroll
-    for (int w = 1; w < kHugeWaves; ++w) v.m = fmaxf(v.m, red[w]);
-    v.n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    __syncthreads();
-    return v;
-}
+    const float* sg = a.sig + ((size_t)g * G + hl) * (size_t)a.sstride;
+    const float4* sg4 = reinterpret_cast<const float4*>(sg);
 
-// The slice's keys in registers: position p0 + tid + kHugeThreads k (= 1024 k) in slot k,
-// so wave w's lanes of slot k cover bitmap word (p0 >> 6) + w + kHugeWaves k.
-__device__ __forceinline__ void slice_keys(const ZhaLevelArgs& a, int h, const SliceView& v,
-                                           uint32_t (&key)[kHugePer]) {
-    const int tid = threadIdx.x;
-    const float* sg = a.sig + (size_t)h * a.cap;
-    const int lim = min(v.n, v.p0 + ZHA_SLICE);
-    float x[kHugePer];
-#pragma unroll
-    for (int k = 0; k < kHugePer; ++k) {
-        const int pos = v.p0 + tid + k * kHugeThreads;
-        x[k] = pos < lim ? sg[pos] : zha_neg_inf();
+    // one round trip: the head's per-block maxima, this workgroup's slice of
+    // kSlice positions as one 16-byte load per thread (rows are 16-byte aligned and
+    // padded to whole vectors), and, last, the parent count
+    const float hb = tid < a.score_blocks ? a.hblk[(size_t)h * ZHA_SCORE_MAXB + tid] : zha_neg_inf();
+    const int nv_cap = (int)(a.sstride / 4);
+    float4 x = make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
+    {
+        const int v = w * (kSlice / 4) + tid;
+        if (v < nv_cap) x = sg4[v];
     }
-#pragma unroll
-    for (int k = 0; k < kHugePer; ++k) {
-        const int pos = v.p0 + tid + k * kHugeThreads;
-        key[k] = pos < v.n ? key_of(x[k], v.m) : kNotCand;
+    const int pn = parent_count(a, g);
+    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (n <= kSmallN) {
+        if (w != 0 || hl != 0) return;
+        float* s_sig = reinterpret_cast<float*>(s_keys);                                   // [G][kSmallN]
+        uint64_t* s_hs = reinterpret_cast<uint64_t*>(s_keys + ZHA_MAX_GROUP * kSmallN);    // [G][256]
+        int32_t* s_nid = reinterpret_cast<int32_t*>(s_keys + ZHA_MAX_GROUP * kSmallN + 2 * ZHA_MAX_GROUP * 256);
+        stage_small(a, g, G, c, tid, s_sig, s_nid);
+        __syncthreads();
+        select_small_group(a, g, G, top_p, n, s_sig, s_nid, s_hs, s_hist);
+        return;
     }
-}
-
-
-// Run by the whole workgroup that finished pass PASS of head h last: read that
-// pass's complete histogram, find the bin where the cumulative mass crosses, and
-// record the head's cut state for the following kernels.
-__device__ void advance_cut(const ZhaLevelArgs& a, int Hq, int h, int pass, float top_p, const HugeCut& prev,
-                            uint64_t* lhist, uint32_t* lcnt, int* s_bin, uint64_t* s_before, uint64_t* s_need) {
-    const int tid = threadIdx.x;
-    const uint64_t* gm = a.hmass + ((size_t)pass * Hq + h) * kHistBins;
-    const uint32_t* gc = a.hcnt + ((size_t)pass * Hq + h) * kHistBins;
-    for (int b = tid; b < kHistBins; b += kHugeThreads) {
-        // the other workgroups' sums, read past this device's caches
-        lhist[hpad((uint32_t)b)] = __hip_atomic_load(gm + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lcnt[b] = __hip_atomic_load(gc + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (tid < 64) wave_find_cross(lhist, pass == 0 ? 0ull : prev.need, top_p, s_bin, s_before, s_need);
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t bin = (uint32_t)*s_bin;
-        const uint32_t cnt = lcnt[bin];
-        const uint32_t pref = pass == 0 ? bin : (prev.mval << (pass == 1 ? 11 : 10)) | bin;
-        const uint32_t bshift = pass == 0 ? 21u : pass == 1 ? 10u : 0u;
-        HugeCut nx;
-        nx.need = *s_need - *s_before;
-        nx.pad = 0;
-        if (cnt == 1 || pass == 2) {
-            // the crossing bin holds one key (or the keys equal to the cut): the cut is
-            // the largest key with this prefix
-            nx.done = 1;
-            nx.ustar = (pref << bshift) | ((1u << bshift) - 1u);
-            nx.ties = cnt;
-            nx.mshift = nx.mval = nx.bshift = nx.bmask = 0;
-        } else {
-            nx.done = 0;
-            nx.ustar = nx.ties = 0;
-            nx.mshift = pass == 0 ? 21u : 10u;
-            nx.mval = pref;
-            nx.bshift = pass == 0 ? 10u : 0u;
-            nx.bmask = pass == 0 ? 2047u : 1023u;
-        }
-        a.hstate[h] = nx;
-    }
-}
-
-// grid (slices, H_q): digit histogram of pass PASS over one slice, added into the
-// head's global histogram; the last slice to finish records the head's cut state.
-template <int PASS>
-__global__ __launch_bounds__(kHugeThreads) void zha_huge_pass_kernel(ZhaLevelArgs a, int G, int c, float top_p, int Hq) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(Hq));
-    __shared__ __align__(16) uint64_t lhist[kHistPadded];
-    __shared__ uint32_t lcnt[kHistBins];
-    __shared__ int s_bin, s_last;
-    __shared__ uint64_t s_before, s_need;
-    __shared__ float red[kHugeWaves];
-    const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
-    HugeCut st;
-    if (PASS > 0) {
-        st = a.hstate[h];
-        if (st.done) return;                   // an earlier pass already found the cut
-    }
-    const int nh = head_n(a, G, c, h);
-    if (nh <= kSmallN || s * ZHA_SLICE >= nh) return;   // small frontiers: selected whole elsewhere
-    const SliceView v = slice_view(a, G, c, h, s, red);
-    if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
-    const uint32_t mshift = PASS > 0 ? st.mshift : 31u, mval = PASS > 0 ? st.mval : 0u;
-    const uint32_t bshift = PASS > 0 ? st.bshift : 21u, bmask = PASS > 0 ? st.bmask : 2047u;
-    uint32_t key[kHugePer];
-    slice_keys(a, h, v, key);
-    for (int i = tid; i < kHistPadded; i += kHugeThreads) lhist[i] = 0ull;
-    for (int i = tid; i < kHistBins; i += kHugeThreads) lcnt[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kHugePer; ++k) {
-        const uint32_t kk = key[k];
-        if (kk < kNoMass && (PASS == 0 || (kk >> mshift) == mval)) {
-            const uint32_t b = (kk >> bshift) & bmask;
-            atomicAdd((unsigned long long*)&lhist[hpad(b)], (unsigned long long)mass_of(kk));
-            atomicAdd(&lcnt[b], 1u);
-        }
-    }
-    __syncthreads();
-    uint64_t* gm = a.hmass + ((size_t)PASS * Hq + h) * kHistBins;
-    uint32_t* gc = a.hcnt + ((size_t)PASS * Hq + h) * kHistBins;
-    for (int b = tid; b < kHistBins; b += kHugeThreads) {
-        const uint32_t cnt = lcnt[b];
-        if (cnt) {
-            atomicAdd((unsigned long long*)&gm[b], (unsigned long long)lhist[hpad((uint32_t)b)]);
-            atomicAdd(&gc[b], cnt);
-        }
-    }
-    // the last of the head's active slices to get here resolves this pass: every
-    // wave's histogram atomics complete, then one release fence and the counter
-    zha_wave_mem_wait();
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const int active = (v.n + ZHA_SLICE - 1) / ZHA_SLICE;
-        s_last = atomicAdd(&a.hdone[PASS * Hq + h], 1u) == (uint32_t)(active - 1);
-        if (s_last) __threadfence();
-    }
-    __syncthreads();
-    if (!s_last) return;
-    advance_cut(a, Hq, h, PASS, top_p, st, lhist, lcnt, &s_bin, &s_before, &s_need);
-}
-
-// Block-wide sums over kHugeThreads threads (all threads receive the result).
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t t;
-    wave_excl_scan_u64(v, &t);
-    __syncthreads();
-    if (lane == 0) red[wave] = t;
-    __syncthreads();
-    uint64_t sum = 0;
-#pragma unroll
-    for (int w = 0; w < kHugeWaves; ++w) sum += red[w];
-    return sum;
-}
-
-// grid (slices, H_q), kHugeThreads (1024) threads: kept flags of one slice into the head's bitmap
-// (words of 64 positions, each written by one lane), candidate and kept counts,
-// and the slice's mass of keys equal to the cut when the cut key is shared.
-__global__ __launch_bounds__(kHugeThreads) void zha_huge_bitmap_kernel(ZhaLevelArgs a, int G, int c, float top_p,
-                                                                      int Hq) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(Hq));
-    __shared__ uint64_t red[kHugeWaves];
-    __shared__ float redf[kHugeWaves];
-    const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int nh = head_n(a, G, c, h);
-    if (nh <= kSmallN || s * ZHA_SLICE >= nh) return;   // small frontiers: selected whole elsewhere
-    const HugeCut cut = a.hstate[h];
-    const SliceView v = slice_view(a, G, c, h, s, redf);
-    if (v.p0 >= v.n) return;
-    uint32_t key[kHugePer];
-    slice_keys(a, h, v, key);
-    const bool none = v.m == zha_neg_inf();
+    const int nsl = (n + kSlice - 1) / kSlice;
+    const int active = min(kSliceW, nsl);
+    if (w >= active) return;
+    const float M = block_max(hb, s_red);
+    const bool none = M == zha_neg_inf();
     const bool keep_all = !none && top_p >= 1.0f;
-    uint32_t ustar = 0, ties = 0;
-    if (!none && !keep_all) {
-        ustar = cut.ustar;
-        ties = cut.ties;
-    }
-    uint64_t* bm = a.kbm + (size_t)h * a.wcap;
-    const int nwords = (v.n + 63) >> 6;
-    uint32_t my_cand = 0, my_kept = 0;
-    uint64_t my_tie = 0;
+    const bool cut = !none && !keep_all;
+    uint64_t* gm = a.ghist + (size_t)h * kHistBins;
+    if (cut) {
+        // the first digit's mass histogram of slices w, w + kSliceW, ..., added into
+        // the head's global histogram (integer atomics: exact and order-free)
+        s_hist[2 * tid] = 0ull;
+        s_hist[2 * tid + 1] = 0ull;
+        __syncthreads();
+#pragma unroll 1
+        for (int sl = w; sl < nsl; sl += kSliceW) {
+            if (sl != w) {
+                const int v = sl * (kSlice / 4) + tid;
+                x = v < nv_cap ? sg4[v] : make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
+            }
+            const float v4[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int k = 0; k < kHugePer; ++k) {
-        const uint32_t kk = key[k];
-        const bool cand = kk != kNotCand;
-        const bool kept = !none && (keep_all ? cand : (kk < kNoMass && (kk < ustar || (kk == ustar && ties == 1))));
-        const uint64_t word = __ballot(kept);
-        const int wi = (v.p0 >> 6) + wave + kHugeWaves * k;
-        if (lane == 0 && wi < nwords) bm[wi] = word;
-        my_cand += cand;
-        my_kept += kept;
-        if (ties > 1 && kk == ustar) my_tie += mass_of(kk);
-    }
-    const uint64_t both = block_sum_u64(((uint64_t)my_kept << 32) | my_cand, red);
-    if (tid == 0) {
-        atomicAdd(&a.stats[2 * h + 0], (int32_t)(uint32_t)both);
-        atomicAdd(&a.stats[2 * h + 1], (int32_t)(both >> 32));
-    }
-    if (ties > 1) {
-        const uint64_t t = block_sum_u64(my_tie, red);
-        if (tid == 0) a.tiem[(size_t)h * a.slices + s] = t;
-    }
-}
-
-// grid (slices, H_q): when several keys equal the cut key, take them in ascending
-// position order (slice by slice, then within the slice) until the mass still
-// needed at the cut is reached.  A slice whose equal keys all come before that
-// point takes them all, one that starts after it takes none; only the slice where
-// it falls walks its positions in order.
-__global__ __launch_bounds__(kHugeThreads) void zha_huge_ties_kernel(ZhaLevelArgs a, int G, int c, float top_p,
-                                                                    int Hq) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p), "s"(Hq));
-    __shared__ uint64_t red[kHugeWaves];
-    __shared__ float redf[kHugeWaves];
-    __shared__ uint64_t wsum[kHugeWaves][kHugePer];   // equal-key mass per (wave, slot)
-    const int h = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const HugeCut st = a.hstate[h];
-    if (st.ties <= 1u) return;                 // the cut key is unique
-    const int nh = head_n(a, G, c, h);
-    if (nh <= kSmallN || s * ZHA_SLICE >= nh) return;   // small frontiers: selected whole elsewhere
-    const SliceView v = slice_view(a, G, c, h, s, redf);
-    if (v.p0 >= v.n || v.m == zha_neg_inf() || top_p >= 1.0f) return;
-    // equal-key mass of the slices before this one, and of this one
-    uint64_t prev = 0;
-    for (int i = tid; i < s; i += kHugeThreads) prev += a.tiem[(size_t)h * a.slices + i];
-    const uint64_t before_slice = block_sum_u64(prev, red);
-    const uint64_t mine = a.tiem[(size_t)h * a.slices + s];
-    const uint64_t need = st.need;
-    if (before_slice >= need) return;          // the cut was reached in an earlier slice
-    uint32_t key[kHugePer];
-    slice_keys(a, h, v, key);
-    uint64_t* bm = a.kbm + (size_t)h * a.wcap;
-    const int nwords = (v.n + 63) >> 6;
-    uint32_t my_extra = 0;
-    if (before_slice + mine <= need) {
-        // every equal key of this slice precedes the point where the cut is reached
-#pragma unroll
-        for (int k = 0; k < kHugePer; ++k) {
-            const bool take = key[k] == st.ustar;
-            const uint64_t extra = __ballot(take);
-            const int wi = (v.p0 >> 6) + wave + kHugeWaves * k;
-            if (lane == 0 && extra && wi < nwords) atomicOr((unsigned long long*)&bm[wi], (unsigned long long)extra);
-            my_extra += take;
-        }
-    } else {
-        // positions run k-major (slot k covers p0 + 1024 k .. p0 + 1024 k + 1023): the mass
-        // before (slot k, wave w) is every slot < k plus the waves < w of slot k
-#pragma unroll
-        for (int k = 0; k < kHugePer; ++k) {
-            const uint64_t wk = key[k] == st.ustar ? mass_of(key[k]) : 0ull;
-            uint64_t t;
-            wave_excl_scan_u64(wk, &t);
-            if (lane == 0) wsum[wave][k] = t;
+            for (int j = 0; j < 4; ++j) {
+                const int p = sl * kSlice + 4 * tid + j;
+                const uint32_t key = p < n ? key_of(v4[j], M) : kNotCand;
+                if (key < kNoMass) atomicAdd((unsigned long long*)&s_hist[key >> 21], (unsigned long long)mass_of(key));
+            }
         }
         __syncthreads();
-        uint64_t run = before_slice;
-#pragma unroll 1
-        for (int k = 0; k < kHugePer; ++k) {
-            uint64_t bw = 0, tot = 0;
-            for (int ww = 0; ww < kHugeWaves; ++ww) {
-                const uint64_t x = wsum[ww][k];
-                bw += ww < wave ? x : 0ull;
-                tot += x;
-            }
-            uint32_t kk = 0;                       // slot k's key, selected without indexing registers
 #pragma unroll
-            for (int q = 0; q < kHugePer; ++q) kk = q == k ? key[q] : kk;
-            const uint64_t wk = kk == st.ustar ? mass_of(kk) : 0ull;
-            uint64_t t;
-            const uint64_t ex = wave_excl_scan_u64(wk, &t);
-            const bool take = wk > 0 && run + bw + ex < need;
-            const uint64_t extra = __ballot(take);
-            const int wi = (v.p0 >> 6) + wave + kHugeWaves * k;
-            if (lane == 0 && extra && wi < nwords) atomicOr((unsigned long long*)&bm[wi], (unsigned long long)extra);
-            my_extra += take;
-            run += tot;
-            if (run >= need) break;                // uniform: every thread holds the same run
+        for (int i = 0; i < 2; ++i) {
+            const uint64_t v = s_hist[2 * tid + i];
+            if (v) atomicAdd((unsigned long long*)&gm[2 * tid + i], (unsigned long long)v);
+        }
+        zha_wave_mem_wait();                   // this wave's histogram adds have completed
+    }
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&a.hdone[h], 1u) == (uint32_t)(active - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    // ---- the head's last workgroup: the complete histogram (read past this
+    // device's caches) and the head's keys (LDS, 16-byte loads), then the cut
+    const bool staged = n <= kLdsKeys;
+    uint32_t my_cand = 0;
+    {
+        uint64_t hm2[2] = {0ull, 0ull};
+        if (cut) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) hm2[i] = __hip_atomic_load(gm + 2 * tid + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        constexpr int kVec = kKeyRegs / 4;     // float4 loads per thread
+        float4 y[kVec];
+        const int nvn = (n + 3) / 4;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+            y[k] = make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
+            if (staged && k * kBT < nvn) {     // uniform: rows wholly past n skipped
+                const int v = tid + k * kBT;
+                if (v < nvn) y[k] = sg4[v];
+            }
+        }
+        s_hist[2 * tid] = hm2[0];
+        s_hist[2 * tid + 1] = hm2[1];
+        if (staged) {
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const int p = 4 * (tid + k * kBT);
+                if (p < n) {
+                    const float v[4] = {y[k].x, y[k].y, y[k].z, y[k].w};
+                    uint32_t kk[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        kk[j] = p + j < n ? key_of(v[j], M) : kNotCand;
+                        my_cand += kk[j] != kNotCand;
+                    }
+                    *reinterpret_cast<uint4*>(s_keys + p) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+                }
+            }
+        } else {
+            for (int p = tid; p < n; p += kBT) my_cand += key_of(sg[p], M) != kNotCand;
         }
     }
-    const uint64_t tot = block_sum_u64(my_extra, red);
-    if (tid == 0 && tot) atomicAdd(&a.stats[2 * h + 1], (int32_t)tot);
-}
-
-// grid (chunks, H_kv), 512 threads: kept nodes (union over the group's heads) in
-// each chunk of kMergeW bitmap words, for the merge's rank offsets.
-__global__ __launch_bounds__(kMergeW) void zha_chunk_count_kernel(ZhaLevelArgs a, int G, int c) {
-    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c));
-    __shared__ uint32_t part[kMergeW / 64];
-    const int g = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-    const int nch = (int)((a.wcap + kMergeW - 1) / kMergeW);
-    const int w = ch * kMergeW + tid;
-    uint64_t hv[ZHA_MAX_GROUP];
-#pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-        hv[hh] = (hh < G && w < a.wcap) ? a.kbm[((size_t)g * G + hh) * a.wcap + w] : 0ull;
-    const int pn = a.top ? 0 : a.pnkept[g];
-    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
-    if (n <= kSmallN) return;                  // selected and merged by the select kernel
-    const int nwords = (n + 63) >> 6;
-    uint64_t u = 0;
-#pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) u |= hv[hh];
-    uint32_t cnt = w < nwords ? (uint32_t)__popcll(u) : 0u;
-    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-    if ((tid & 63) == 0) part[tid >> 6] = cnt;
+    __syncthreads();
+    uint32_t ustar = 0, plim = 0xFFFFFFFFu;
+    if (cut) {
+        if (staged) block_cut(LdsKeys{s_keys}, n, top_p, true, s_hist, s_gl, &st, ustar, plim);
+        else block_cut(GlobKeys{sg, M}, n, top_p, true, s_hist, s_gl, &st, ustar, plim);
+    }
+    // the head's kept count
+    uint32_t my_kept = 0;
+    if (staged) {
+#pragma unroll 8
+        for (int p = tid; p < n; p += kBT) my_kept += kept_by(s_keys[p], (uint32_t)p, none, keep_all, ustar, plim);
+    } else {
+        for (int p = tid; p < n; p += kBT) my_kept += kept_by(key_of(sg[p], M), (uint32_t)p, none, keep_all, ustar, plim);
+    }
+    const uint64_t both = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)my_kept << 32) | my_cand), 63);
+    if (lane == 0) s_wred[wave] = both;
     __syncthreads();
     if (tid == 0) {
-        uint32_t t = 0;
+        uint64_t t = 0;
 #pragma unroll
-        for (int i = 0; i < kMergeW / 64; ++i) t += part[i];
-        a.chunk_cnt[(size_t)g * nch + ch] = t;
+        for (int w2 = 0; w2 < kBW; ++w2) t += s_wred[w2];
+        a.stats[2 * h + 0] = (int32_t)(uint32_t)t;
+        a.stats[2 * h + 1] = (int32_t)(t >> 32);
+        HeadCut hc;
+        hc.m = M;
+        hc.ustar = ustar;
+        hc.plim = plim;
+        hc.mode = none ? 2u : keep_all ? 1u : 0u;
+        reinterpret_cast<HeadCut*>(a.hcut)[h] = hc;
+    }
+}
+
+__global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a, int G, int c) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c));
+    __shared__ uint32_t s_wc[kApplyWaves];
+    __shared__ uint32_t s_ticket, s_prefix;
+    __shared__ HeadCut s_hc[ZHA_MAX_GROUP];
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int pn = parent_count(a, g);
+    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (n <= kSmallN) return;                  // the select kernel wrote the kept list
+    const int nch = (n + kApplyChunk - 1) / kApplyChunk;
+    if (tid == 0) s_ticket = atomicAdd(&a.tick[g], 1u);
+    __syncthreads();
+    const int ci = (int)s_ticket;
+    if (ci >= nch) return;
+    // the heads' cuts (to LDS, one thread each) and the chunk's scores, positions
+    // p0 .. p0 + 3 of this thread for every head as one 16-byte load each (rows are
+    // 16-byte aligned; the vector holding position n - 1 may run past n, never past
+    // the row), all in flight together; scores of heads beyond G come from a valid
+    // row and are masked afterwards
+    const HeadCut mine = reinterpret_cast<const HeadCut*>(a.hcut)[(size_t)g * G + (tid < G ? tid : 0)];
+    const int p0 = ci * kApplyChunk + 4 * tid;
+    const int pv = p0 < n ? p0 : 0;
+    float4 x[ZHA_MAX_GROUP];
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        x[hh] = *reinterpret_cast<const float4*>(a.sig + ((size_t)g * G + (hh < G ? hh : 0)) * a.sstride + pv);
+    if (tid < G) s_hc[tid] = mine;
+    __syncthreads();
+    uint32_t msk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+        if (hh < G) {                          // uniform; the loads are all issued above
+            const HeadCut hc = s_hc[hh];
+            const float v[4] = {x[hh].x, x[hh].y, x[hh].z, x[hh].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = p0 + j < n ? key_of(v[j], hc.m) : kNotCand;
+                msk[j] |= (uint32_t)kept_by(key, (uint32_t)(p0 + j), hc.mode == 2u, hc.mode == 1u, hc.ustar, hc.plim)
+                          << hh;
+            }
+        }
+    }
+    // the chunk's kept positions in order (4 per thread, thread-major): this
+    // thread's count, the wave's inclusive scan, the waves' counts
+    const uint32_t mine_cnt = (msk[0] != 0u) + (msk[1] != 0u) + (msk[2] != 0u) + (msk[3] != 0u);
+    const uint32_t inc = (uint32_t)zha_wave_incl_scan_u64(mine_cnt);
+    if (lane == 63) s_wc[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        // the chunk's count (wave prefixes into s_wc), published; then the
+        // predecessors' descriptors, read by wave 0's lanes together (lane j reads
+        // chunk ci - 1 - j, 64 at a time, again while any of them has not
+        // published): the sum up to the nearest published inclusive prefix
+        uint32_t wcnt = lane < kApplyWaves ? s_wc[lane] : 0u;
+        uint64_t ctot;
+        const uint32_t wex = (uint32_t)wave_excl_scan_u64(wcnt, &ctot);
+        if (lane < kApplyWaves) s_wc[lane] = wex;
+        const uint32_t cnt = (uint32_t)ctot;
+        uint32_t* desc = a.desc + (size_t)g * a.ndesc;
+        if (lane == 0)
+            __hip_atomic_store(desc + ci, (ci == 0 ? kDescInc : kDescAgg) | cnt, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t prefix = 0;
+        int top = ci - 1;                      // nearest predecessor not yet summed
+        uint32_t spins = 0;
+        while (top >= 0) {                     // uniform
+            const int j = top - lane;
+            uint32_t d = j >= 0 ? __hip_atomic_load(desc + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kDescInc;
+            // lanes up to the first inclusive prefix (or the first unpublished chunk)
+            const uint64_t inc_b = __ballot((d & kDescInc) != 0u);
+            const uint64_t none_b = __ballot((d & (kDescInc | kDescAgg)) == 0u);
+            const int first_inc = inc_b ? __ffsll((long long)inc_b) - 1 : 64;
+            const int first_none = none_b ? __ffsll((long long)none_b) - 1 : 64;
+            const int upto = min(first_inc, first_none);       // lanes [0, upto) are aggregates
+            uint32_t v = lane < upto ? (d & kDescVal) : 0u;
+            if (first_inc < first_none && lane == first_inc) v = d & kDescVal;
+            uint64_t vt;
+            wave_excl_scan_u64(v, &vt);
+            prefix += (uint32_t)vt;
+            if (first_inc < first_none) break;                 // reached an inclusive prefix (or chunk 0)
+            top -= upto;                                       // continue below the summed aggregates
+            if (first_none < 64) {
+                if (++spins > kSpinMax) break;                 // not reached: those chunks started before this one
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        if (lane == 0) {
+            if (ci > 0)
+                __hip_atomic_store(desc + ci, kDescInc | (prefix + cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_prefix = prefix;
+            if (ci == nch - 1) a.nkept[g] = (int32_t)(prefix + cnt);
+        }
+    }
+    __syncthreads();
+    uint32_t r = s_prefix + s_wc[wave] + inc - mine_cnt;
+    int32_t* kl = a.klist + (size_t)g * a.cap;
+    uint32_t* km = a.kmask + (size_t)g * a.cap;
+    const int pnc = a.top ? 0 : pn * c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (msk[j]) {
+            const int p = p0 + j;
+            int32_t node;
+            if (a.top) node = p;
+            else if (p < pnc) {
+                const int pi = (int)zha_div((uint32_t)p, a.dc);
+                node = a.pklist[(size_t)g * a.pcap + pi] * c + (p - pi * c);
+            } else node = (int32_t)a.orph_lo + (p - pnc);
+            kl[r] = node;
+            km[r] = msk[j];
+            ++r;
+        }
     }
 }
 
@@ -1810,27 +1432,18 @@ int zha_score_blocks(int64_t max_cand, int R) {
     return (int)blocks;
 }
 
-bool zha_defer_fits(int G, int64_t wcap, int64_t pcap) {
-    return (int64_t)G * wcap <= ZHA_DEFER_WORDS && pcap <= ZHA_DEFER_PARENTS;
-}
-
-size_t zha_defer_lds_bytes(int G, int64_t wcap, int64_t pcap) {
-    return sizeof(uint64_t) * (size_t)(G + 1) * (size_t)wcap + sizeof(uint32_t) * (size_t)wcap +
-           sizeof(int32_t) * (size_t)pcap;
+// LDS of a score kernel that derives the chain's last level's kept list (n nodes).
+size_t zha_defer_lds_bytes(int G, int64_t n) {
+    const size_t wc = (size_t)((n + 63) / 64);
+    return sizeof(uint64_t) * (size_t)(G + 1) * wc + sizeof(uint32_t) * wc;
 }
 
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream, const ZhaLevelArgs* defer) {
-    if (a.hblk) {
-        hipLaunchKernelGGL(zha_huge_init_kernel, dim3((unsigned)(H_kv * G)), dim3(kHugeThreads), 0, stream, a, H_kv * G);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     dim3 grid((unsigned)blocks, (unsigned)H_kv);
     if (defer) {
-        const int64_t pcap = defer->top ? 0 : defer->pcap;
-        if (a.top || defer->hblk || !zha_defer_fits(G, defer->wcap, pcap)) return hipErrorInvalidValue;
-        const size_t lds = zha_defer_lds_bytes(G, defer->wcap, pcap);
+        if (a.top || !defer->top || defer->n_top > ZHA_CHAIN_SLOTS) return hipErrorInvalidValue;
+        const size_t lds = zha_defer_lds_bytes(G, defer->n_top);
         if (kv_dtype == 0)
             hipLaunchKernelGGL(zha_route_score_defer_kernel<true>, grid, dim3(kScoreThreads), lds, stream, q, a, *defer,
                                G, c, R, tau);
@@ -1846,64 +1459,44 @@ hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArg
     return hipGetLastError();
 }
 
-hipError_t zha_launch_route_chain(int kv_dtype, const void* q, const ZhaChainArgs& m, int H_kv, int G, int c, int R,
-                                  float tau, float top_p, hipStream_t stream) {
+hipError_t zha_launch_score_all(int kv_dtype, const void* q, const ZhaChainArgs& m, int H_kv, int G, int c, int R,
+                                float tau, hipStream_t stream) {
     int bmax = 1;
-    for (int i = 0; i < m.n; ++i) {
-        if (m.lv[i].cap > kSmallN) return hipErrorInvalidValue;
-        bmax = std::max(bmax, m.blocks[i]);
-    }
+    for (int i = 0; i < m.n; ++i) bmax = std::max(bmax, m.blocks[i]);
     const dim3 grid((unsigned)bmax, (unsigned)H_kv, (unsigned)m.n);
     if (kv_dtype == 0)
         hipLaunchKernelGGL(zha_route_score_all_kernel<true>, grid, dim3(kScoreThreads), 0, stream, q, m, G, c, R, tau);
     else
         hipLaunchKernelGGL(zha_route_score_all_kernel<false>, grid, dim3(kScoreThreads), 0, stream, q, m, G, c, R,
                            tau);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(zha_select_chain_kernel, dim3((unsigned)H_kv), dim3(kSelThreads), 0, stream, m, G, c, top_p);
     return hipGetLastError();
 }
 
-hipError_t zha_launch_route_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream,
-                                   bool merge) {
-    if (a.cap <= kSmallN) {
-        hipLaunchKernelGGL(zha_select_small_kernel, dim3((unsigned)H_kv), dim3(kSelThreads), 0, stream, a, G, c,
-                           top_p);
-        return hipGetLastError();
-    }
-    if (a.hblk) {
-        // sliced level: a frontier of at most kSmallN candidates is selected and merged
-        // by one workgroup per group; larger ones take three digit passes over slices,
-        // the bitmap, the ordered ties, chunk counts and the merge (each of which
-        // leaves at once for a small frontier)
-        const int Hq = H_kv * G;
-        hipLaunchKernelGGL(zha_select_large_kernel, dim3((unsigned)Hq), dim3(kSelThreads), 0, stream, a, G, c, top_p,
-                           1);
-        const dim3 sg((unsigned)a.slices, (unsigned)Hq);
-        hipLaunchKernelGGL(zha_huge_pass_kernel<0>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
-        hipLaunchKernelGGL(zha_huge_pass_kernel<1>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
-        hipLaunchKernelGGL(zha_huge_pass_kernel<2>, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
-        hipLaunchKernelGGL(zha_huge_bitmap_kernel, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
-        hipLaunchKernelGGL(zha_huge_ties_kernel, sg, dim3(kHugeThreads), 0, stream, a, G, c, top_p, Hq);
-        const int64_t nch = (a.wcap + kMergeW - 1) / kMergeW;
-        hipLaunchKernelGGL(zha_chunk_count_kernel, dim3((unsigned)nch, (unsigned)H_kv), dim3(kMergeW), 0, stream, a,
-                           G, c);
-        hipLaunchKernelGGL(zha_route_merge_kernel, dim3((unsigned)nch, (unsigned)H_kv), dim3(kSelThreads), 0, stream,
-                           a, G, c, kMergeW);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(zha_select_large_kernel, dim3((unsigned)(H_kv * G)), dim3(kSelThreads), 0, stream, a, G,
-                       c, top_p, 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !merge) return e;   // without merge: the next level's score kernel derives the list
-    // bitmap words per merge block: a multiple of 16, at most kMergeW, over at
-    // least kMergeBlocks blocks when the level is large enough
-    const int64_t wcap = a.wcap;
-    int64_t share = (wcap + kMergeBlocks - 1) / kMergeBlocks;
-    share = std::min<int64_t>(kMergeW, (share + kSelWaves - 1) / kSelWaves * kSelWaves);
-    const int64_t blocks = (wcap + share - 1) / share;
-    hipLaunchKernelGGL(zha_route_merge_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(kSelThreads), 0, stream,
-                       a, G, c, (int)share);
+hipError_t zha_launch_chain(const ZhaChainSel& m, int H_kv, int G, int c, float top_p, hipStream_t stream) {
+    for (int i = 0; i < m.n; ++i)
+        if (m.lv[i].n_nodes > kChainSlots) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(zha_chain_kernel, dim3((unsigned)(H_kv * G)), dim3(kBT), 0, stream, m, G, c, top_p);
     return hipGetLastError();
 }
+
+hipError_t zha_launch_merge_ids(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream) {
+    if (a.n_top > kChainSlots) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(zha_merge_ids_kernel, dim3((unsigned)H_kv), dim3(kBT), 0, stream, a, G, c);
+    return hipGetLastError();
+}
+
+hipError_t zha_launch_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream) {
+    if (!a.hblk || !a.hcut || !a.tick || !a.desc || !a.ghist || !a.hdone) return hipErrorInvalidValue;
+    int64_t w = (a.cap + kSlice - 1) / kSlice;
+    if (w > kSliceW) w = kSliceW;
+    if (w < 1) w = 1;
+    hipLaunchKernelGGL(zha_select_kernel, dim3((unsigned)w, (unsigned)(H_kv * G)), dim3(kBT), 0, stream, a, G, c,
+                       top_p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)a.ndesc, (unsigned)H_kv);
+    hipLaunchKernelGGL(zha_apply_kernel, grid, dim3(kApplyThreads), 0, stream, a, G, c);
+    return hipGetLastError();
+}
+
+int zha_apply_chunks(int64_t cap) { return (int)((cap + kApplyChunk - 1) / kApplyChunk); }

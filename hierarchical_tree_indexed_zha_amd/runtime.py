@@ -125,18 +125,67 @@ class ZhaLayer:
                 self._view(self.tree, o["lse"], torch.float32, (H, n, R)))
 
     def route_level(self, level: int) -> dict:
-        """Routing the last decode step left for `level` (copied to host)."""
-        o = B.zha_route_level_offsets(self.cfg, level)
-        H, G, n = self.cfg.n_kv_heads, self.cfg.n_q_heads // self.cfg.n_kv_heads, o["n_cap"]
+        """Routing the last decode step left for `level` (copied to host), in the layout of
+        a level scored over its group candidates: n_cand [H], sigma [H][G][n_cap] by
+        group candidate position, n_kept [H], kept [H][n_cap], mask [H][n_cap] and per-head
+        stats [H_q][2].  A chained level (every node scored, per-head kept bitmaps over node
+        ids) is laid out that way on the host from the device's node scores, bitmaps and
+        stats; its group kept list as the device wrote it (at the chain's last level only)
+        is returned as `dev_n_kept`, `dev_kept`, `dev_mask`."""
+        o = B.zha_route_level_offsets(self.cfg, self.n_tokens, level)
+        cfg = self.cfg
+        H, G, n = cfg.n_kv_heads, cfg.n_q_heads // cfg.n_kv_heads, o["n_cap"]
         v = lambda off, dt, shape: self._view(self.scratch, off, dt, shape).cpu()
-        return {
+        out = {
             "n_cand": v(o["n_cand"], torch.int32, (H,)),
-            "sigma": v(o["sigma"], torch.float32, (H, G, n)),
+            "sigma": v(o["sigma"], torch.float32, (H, G, o["sig_stride"]))[:, :, :n],
             "n_kept": v(o["n_kept"], torch.int32, (H,)),
             "kept": v(o["kept"], torch.int32, (H, n)),
             "mask": v(o["mask"], torch.int32, (H, n)),
             "stats": v(o["stats"], torch.int32, (H * G, 2)),
+            "chained": bool(o["chained"]),
         }
+        if not o["chained"]:
+            return out
+        import numpy as np
+        c, N = cfg.chunk, self.n_tokens
+        words = v(o["kbm"], torch.int64, (H, G, o["wcap"])).numpy().view(np.uint64)
+        nn = N // c ** level
+        bits = ((words[..., :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).reshape(H, G, -1)[..., :nn]
+        kept_h = [[np.nonzero(bits[g, hl])[0] for hl in range(G)] for g in range(H)]
+        top = max(lv for lv in range(1, cfg.levels + 1) if N // c ** lv > 0)
+        if level < top:
+            up = self.route_level(level + 1)
+            assert up["chained"], "the chain is a contiguous run of levels from the top"
+            prev = up["kept_by_head"]
+            orph = np.arange(c * (N // c ** (level + 1)), nn, dtype=np.int64)
+        sig_nodes = out["sigma"].numpy()
+        sigma = np.full((H, G, n), -np.inf, dtype=np.float32)
+        n_cand = np.zeros(H, dtype=np.int32)
+        n_kept = np.zeros(H, dtype=np.int32)
+        kept = np.zeros((H, n), dtype=np.int32)
+        mask = np.zeros((H, n), dtype=np.int32)
+        for g in range(H):
+            if level == top:
+                cands = [np.arange(nn, dtype=np.int64)] * G
+            else:
+                cands = [np.concatenate([(prev[g][hl][:, None] * c + np.arange(c)[None, :]).ravel(), orph])
+                         for hl in range(G)]
+            union = np.unique(np.concatenate(cands))
+            n_cand[g] = len(union)
+            for hl in range(G):
+                pos = np.searchsorted(union, cands[hl])
+                sigma[g, hl, pos] = sig_nodes[g, hl, cands[hl]]
+            uk = np.unique(np.concatenate(kept_h[g]))
+            n_kept[g] = len(uk)
+            kept[g, :len(uk)] = uk
+            for hl in range(G):
+                mask[g, np.searchsorted(uk, kept_h[g][hl])] |= 1 << hl
+        out.update({"dev_n_kept": out["n_kept"], "dev_kept": out["kept"], "dev_mask": out["mask"],
+                    "n_cand": torch.from_numpy(n_cand), "sigma": torch.from_numpy(sigma),
+                    "n_kept": torch.from_numpy(n_kept), "kept": torch.from_numpy(kept),
+                    "mask": torch.from_numpy(mask), "kept_by_head": kept_h})
+        return out
 
     def kept_sets(self, level: int) -> list[list[int]]:
         """Per query head, the ascending node ids it kept at `level` in the last decode step."""

@@ -114,24 +114,33 @@ size_t zha_dense_scratch_bytes(const zha_config* cfg);
 int zha_tree_level_offsets(const zha_config* cfg, int32_t level,
                            int64_t* s_off, int64_t* b_off, int64_t* lse_off, int64_t* n_cap);
 
-/* Where the last decode step left its routing of level `level` inside `scratch`
- * (byte offsets; host-only):
- *   n_cand  int32  [H_kv]          candidates scored at this level, per KV group
- *   sigma   float32[H_kv][G][n_cap] score of candidate position i for query head
- *                                   g*G+j (-inf where the candidate is not the
- *                                   head's); candidate positions follow ascending
- *                                   node index
- *   n_kept  int32  [H_kv]          nodes kept by at least one head of the group
- *   kept    int32  [H_kv][n_cap]   those node indices, ascending
- *   mask    uint32 [H_kv][n_cap]   bit j set when query head g*G+j kept the node
- *   stats   int32  [H_q][2]        per query head: candidates, kept
+/* Where a decode step over n_tokens tokens leaves its routing of level `level`
+ * inside `scratch` (byte offsets; host-only).  `chained` tells which layout holds:
+ *   chained = 0 (a level scored over its group candidates):
+ *     n_cand  int32  [H_kv]          candidates scored at this level, per KV group
+ *     sigma   float32[H_kv][G][sig_stride] score of candidate position i for query head
+ *                                     g*G+j (-inf where the candidate is not the
+ *                                     head's); candidate positions follow ascending
+ *                                     node index
+ *     n_kept  int32  [H_kv]          nodes kept by at least one head of the group
+ *     kept    int32  [H_kv][n_cap]   those node indices, ascending
+ *     mask    uint32 [H_kv][n_cap]   bit j set when query head g*G+j kept the node
+ *     stats   int32  [H_q][2]        per query head: candidates, kept
+ *   chained = 1 (one of the first, small levels, every node scored):
+ *     sigma   float32[H_kv][G][sig_stride] score of node i for query head g*G+j
+ *     kbm     uint64 [H_kv][G][wcap] per-head kept bitmap over node ids
+ *     stats   int32  [H_q][2]        per query head: candidates, kept
+ *     (n_kept, kept and mask hold the group kept list only at the last chained
+ *     level)
  * Values are valid only for levels the step routed (levels with at least one
  * complete node).  ZHA_OK or ZHA_ERR_ARG. */
 typedef struct zha_route_offsets {
-    int64_t n_cand, sigma, n_kept, kept, mask, stats;
-    int64_t n_cap;
+    int64_t n_cand, sigma, n_kept, kept, mask, stats, kbm;
+    int64_t n_cap, wcap;
+    int64_t chained;
+    int64_t sig_stride;        /* row stride of sigma: n_cap rounded up to a multiple of 4 */
 } zha_route_offsets;
-int zha_route_level_offsets(const zha_config* cfg, int32_t level, zha_route_offsets* out);
+int zha_route_level_offsets(const zha_config* cfg, int64_t n_tokens, int32_t level, zha_route_offsets* out);
 
 /* Summarise every complete node over tokens [0, n_tokens) of K (levels 1..L):
  * leaves from raw keys, higher levels by the exact log-sum-exp merge of their

@@ -74,6 +74,17 @@ def check_routing(layer: ZhaLayer, qh, n_tokens: int, tree: O.SummaryTree, p: fl
     G = cfg.n_q_heads // H
     top = max([lv for lv in range(1, L + 1) if n_tokens // c ** lv > 0], default=0)
     routes = {lv: layer.route_level(lv) for lv in range(1, top + 1)}
+    # the chain's last level: the group kept list the device derived from the heads'
+    # bitmaps (in the next level's score kernel, or a merge at level 1) is theirs
+    chained = [lv for lv in routes if routes[lv]["chained"]]
+    if chained:
+        lo = min(chained)
+        r = routes[lo]
+        for g in (range(H) if groups is None else groups):
+            nk = int(r["n_kept"][g])
+            assert int(r["dev_n_kept"][g]) == nk, f"{label} level {lo} group {g}: device kept count"
+            assert torch.equal(r["dev_kept"][g, :nk], r["kept"][g, :nk]), f"{label} level {lo} group {g}: kept list"
+            assert torch.equal(r["dev_mask"][g, :nk], r["mask"][g, :nk]), f"{label} level {lo} group {g}: masks"
     worst = 0.0
     kept_all = {lv: [None] * cfg.n_q_heads for lv in routes}
     for g in (range(H) if groups is None else groups):

@@ -84,7 +84,7 @@ def test_valid_configs_pass_and_sizes_match_layout():
         assert B.zha_sel_bytes(cfg) == 4 * w.n_q_heads * (w.capacity // w.chunk + 1)
         o = B.zha_tree_level_offsets(cfg, w.levels)
         assert o["n_cap"] == w.capacity // w.chunk ** w.levels
-        r = B.zha_route_level_offsets(cfg, 1)
+        r = B.zha_route_level_offsets(cfg, w.n_tokens, 1)
         assert r["n_cap"] == w.capacity // w.chunk
         assert max(r["n_cand"], r["sigma"], r["kept"], r["mask"], r["stats"]) < B.zha_scratch_bytes(cfg)
 
@@ -108,7 +108,9 @@ def test_entry_points_reject_bad_arguments_before_touching_the_device():
         (lambda: B.dense_decode(cfg, fake, fake, 1001, fake, fake, fake, 0), B.ZHA_ERR_CAPACITY),
         (lambda: B.dense_decode(cfg, fake, fake, 10, fake, fake, None, 0), B.ZHA_ERR_ARG),
         (lambda: B.zha_tree_level_offsets(cfg, 0), B.ZHA_ERR_ARG),
-        (lambda: B.zha_route_level_offsets(cfg, 5), B.ZHA_ERR_ARG),
+        (lambda: B.zha_route_level_offsets(cfg, 10, 5), B.ZHA_ERR_ARG),
+        (lambda: B.zha_route_level_offsets(cfg, 0, 1), B.ZHA_ERR_ARG),
+        (lambda: B.zha_route_level_offsets(cfg, 1001, 1), B.ZHA_ERR_ARG),
     ]
     for fn, code in cases:
         with pytest.raises(B.ZhaError) as e:
@@ -141,3 +143,20 @@ def test_config_struct_layout_matches_header():
     body = src[src.index("typedef struct zha_config"):src.index("} zha_config;")]
     names = re.findall(r"^\s*(?:int64_t|int32_t|float)\s+(\w+)", body, flags=re.M)
     assert names == [f for f, _ in B.Config._fields_]
+
+
+def test_chained_levels_follow_the_slot_and_plane_bounds():
+    """The first routed levels form the chain while each has at most 4,096 node slots and
+    together at most 32,768 planes per group; the rest are routed over group candidates."""
+    def chained(name, n=None):
+        w = W.get(name)
+        cfg = B.config_of(w)
+        n = w.n_tokens if n is None else n
+        return [lv for lv in range(1, w.levels + 1) if B.zha_route_level_offsets(cfg, n, lv)["chained"]]
+    assert chained("light") == [2, 3, 4]          # 4096 + 512 + 64 planes; level 1 has 32,768 slots
+    assert chained("tiny") == [2, 3, 4, 5, 6]     # R = 16: 21,824 planes; level 1 would add 65,536
+    assert chained("deep") == [4, 5, 6]           # 1,344 nodes * 16 planes; level 3 has 4,096 slots but 65,536 planes
+    assert chained("wide") == [1]                 # 1,024 nodes * 16 planes
+    assert chained("ultra") == [4, 5, 6, 7]       # 2,560 + 320 + 40 + 5 nodes
+    assert chained("light", 100) == [1, 2]        # 12 level-1 nodes, one level-2 node
+    assert chained("light", 60) == [1]            # only level 1 complete: 7 nodes

@@ -479,6 +479,7 @@ constexpr int kKeyRegs = kLdsKeys / kBT;       // positions per thread of a stag
 constexpr int kSlice = 4 * kBT;                 // positions a slice workgroup histograms (four per thread)
 constexpr int kSliceW = 8;                      // slice workgroups per head
 constexpr int kChainSlots = ZHA_CHAIN_SLOTS;
+constexpr int kChainStage = 16384;              // chained scores of one head staged in LDS (floats)
 constexpr int kChainPer = kChainSlots / kBT;  // candidate positions per thread in the chain
 static_assert(kChainPer * kBT == kChainSlots && kChainPer * kBW <= 64, "chain rows: one scan lane per (row, wave)");
 // Small-path histogram bins pack a key count above a mass sum: at most kSmallN
@@ -736,9 +737,9 @@ struct GlobKeys {        // frontiers beyond the LDS keys: formed again from the
     __device__ uint32_t operator()(int p) const { return key_of(sg[p], m); }
 };
 
-constexpr int kRankMax = 128;  // crossing-bin keys ranked directly
+constexpr int kRankMax = 64;   // crossing-bin keys ranked directly (one per lane of a wave)
 constexpr int kGather = kBT;   // crossing-bin keys listed for the later passes (one per thread)
-static_assert(kBT % kRankMax == 0 && kRankMax % (kBT / kRankMax) == 0, "rank split");
+static_assert(kRankMax == 64 && kBT % 64 == 0, "rank: entry = lane, j split over the waves");
 
 struct CutShared {
     uint64_t ws[kBW];          // per-wave sums
@@ -751,39 +752,114 @@ struct CutShared {
 };
 
 // The bin b of hist where before(b) < need <= before(b) + hist[b] (before(b): the
-// mass of the bins below b), found by the whole workgroup (two bins per thread).
-// need0 = 0: need = ceil(p * total), clamped to [1, total].  Results in st.
+// mass of the bins below b).  need0 = 0: need = ceil(p * total), clamped to
+// [1, total].  Found by the first kFindW waves, kFindPer consecutive bins per
+// thread (the other waves wait at the barriers: every instruction here would
+// otherwise run on all the workgroup's waves).  Results in st.
+constexpr int kFindW = 4;
+constexpr int kFindPer = kHistBins / (kFindW * 64);
+static_assert(kFindPer % 2 == 0 && kFindW <= kBW, "find split");
 __device__ __forceinline__ void block_find(const uint64_t* hist, uint64_t need0, float top_p, CutShared* st) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
-    const uint64_t sum = h0 + h1;
-    const uint64_t inc = zha_wave_incl_scan_u64(sum);
-    if (lane == 63) st->ws[wave] = inc;
-    __syncthreads();
-    uint64_t wb = 0, total = 0;
+    uint64_t h[kFindPer];
+    uint64_t sum = 0, inc = 0;
+    if (wave < kFindW) {
+        const ulonglong2* hv = reinterpret_cast<const ulonglong2*>(hist) + tid * (kFindPer / 2);
 #pragma unroll
-    for (int w = 0; w < kBW; ++w) {
-        const uint64_t x = st->ws[w];
-        wb += w < wave ? x : 0ull;
-        total += x;
-    }
-    uint64_t need = need0;
-    if (need == 0) {
-        need = (uint64_t)ceil((double)top_p * (double)total);
-        if (need < 1) need = 1;
-        if (need > total) need = total;
-    }
-    const uint64_t bt = wb + inc - sum;
-    if (bt < need && bt + h0 >= need) {
-        st->bin = 2 * tid;
-        st->before = bt;
-        st->need = need;
-    } else if (bt + h0 < need && bt + sum >= need) {
-        st->bin = 2 * tid + 1;
-        st->before = bt + h0;
-        st->need = need;
+        for (int k = 0; k < kFindPer / 2; ++k) {
+            const ulonglong2 v = hv[k];
+            h[2 * k] = v.x;
+            h[2 * k + 1] = v.y;
+        }
+#pragma unroll
+        for (int k = 0; k < kFindPer; ++k) sum += h[k];
+        inc = zha_wave_incl_scan_u64(sum);
+        if (lane == 63) st->ws[wave] = inc;
     }
     __syncthreads();
+    if (wave < kFindW) {
+        uint64_t wb = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kFindW; ++w) {
+            const uint64_t x = st->ws[w];
+            wb += w < wave ? x : 0ull;
+            total += x;
+        }
+        uint64_t need = need0;
+        if (need == 0) {
+            need = (uint64_t)ceil((double)top_p * (double)total);
+            if (need < 1) need = 1;
+            if (need > total) need = total;
+        }
+        uint64_t bt = wb + inc - sum;          // mass below this thread's first bin
+        if (bt < need && bt + sum >= need) {   // the one thread whose bins cross
+#pragma unroll
+            for (int k = 0; k < kFindPer; ++k) {
+                if (bt < need && bt + h[k] >= need) {
+                    st->bin = tid * kFindPer + k;
+                    st->before = bt;
+                    st->need = need;
+                }
+                bt += h[k];
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// The cut among ne <= kRankMax keys listed in st->ent (st->rank cleared): entry
+// i = lane's mass before it in (key, position) order is summed by every wave over
+// its own kRankMax / kBW entries j (the same j for the whole wave: broadcast
+// reads); the entry whose own mass reaches `need` is the cut.
+__device__ __forceinline__ void rank_entries(CutShared* st, int ne, uint64_t need, uint32_t& ustar, uint32_t& plim) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int kPerW = kRankMax / kBW;
+    {
+        const uint4 me = st->ent[lane < ne ? lane : 0];
+        const uint64_t mk = ((uint64_t)me.x << 32) | me.y;      // (key, position) order
+        uint64_t acc = 0;
+#pragma unroll
+        for (int jj = 0; jj < kPerW; ++jj) {
+            const int j = wave * kPerW + jj;
+            if (j < ne) {
+                const uint4 f = st->ent[j];
+                acc += (((uint64_t)f.x << 32) | f.y) < mk ? (((uint64_t)f.w << 32) | f.z) : 0ull;
+            }
+        }
+        if (lane < ne && acc) atomicAdd((unsigned long long*)&st->rank[lane], (unsigned long long)acc);
+    }
+    __syncthreads();
+    if (tid < ne) {
+        const uint4 me = st->ent[tid];
+        const uint64_t before = st->rank[tid], own = ((uint64_t)me.w << 32) | me.z;
+        if (before < need && before + own >= need) {
+            st->ustar = me.x;
+            st->plim = me.y;
+        }
+    }
+    __syncthreads();
+    ustar = st->ustar;
+    plim = st->plim;
+}
+
+// Visits every position p = tid + kBT i < n with its key, in batches of
+// kSweepB per thread whose keys are all read before any is used: the visitors'
+// LDS atomics and stores would otherwise order each later key read after them.
+constexpr int kSweepB = 8;
+template <class KF, class F>
+__device__ __forceinline__ void sweep_keys(const KF& key_at, int n, F&& f) {
+#pragma unroll 1
+    for (int base = threadIdx.x; base < n; base += kSweepB * kBT) {
+        uint32_t kk[kSweepB];
+#pragma unroll
+        for (int j = 0; j < kSweepB; ++j) {
+            const int p = base + j * kBT;
+            kk[j] = kNotCand;
+            if (p < n) kk[j] = key_at(p);
+        }
+#pragma unroll
+        for (int j = 0; j < kSweepB; ++j) f(kk[j], base + j * kBT);
+    }
 }
 
 // The cut of one head: kept iff key < ustar, or key == ustar and p <= plim.  With
@@ -802,15 +878,32 @@ __device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint6
     uint64_t need = 0;
     ustar = 0;
     plim = 0xFFFFFFFFu;
+    if (n <= kRankMax) {
+        // every key ranked directly: massless keys and non-candidates enter with
+        // mass 0, which never reaches the cut
+        if (tid < kRankMax) {
+            const uint32_t k = tid < n ? key_at(tid) : kNotCand;
+            const uint64_t ms = k < kNoMass ? mass_of(k) : 0ull;
+            st->ent[tid] = make_uint4(k, (uint32_t)tid, (uint32_t)ms, (uint32_t)(ms >> 32));
+            st->rank[tid] = 0ull;
+        }
+        __syncthreads();
+        // the total over the entries (one per lane), formed by every wave
+        const uint4 e0 = st->ent[lane];
+        const uint64_t total = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)e0.w << 32) | e0.z), 63);
+        need = (uint64_t)ceil((double)top_p * (double)total);
+        if (need < 1) need = 1;
+        if (need > total) need = total;
+        rank_entries(st, n, need, ustar, plim);
+        return;
+    }
     if (!pre0) {
         hist[2 * tid] = 0ull;
         hist[2 * tid + 1] = 0ull;
         __syncthreads();
-#pragma unroll 4
-        for (int p = tid; p < n; p += kBT) {
-            const uint32_t k = key_at(p);
+        sweep_keys(key_at, n, [&](uint32_t k, int) {
             if (k < kNoMass) atomicAdd((unsigned long long*)&hist[k >> 21], (unsigned long long)mass_of(k));
-        }
+        });
         __syncthreads();
     }
     int nl = -1;                               // >= 0: the crossing keys of an earlier pass are gl[0, nl)
@@ -829,89 +922,68 @@ __device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint6
             hist[2 * tid + 1] = 0ull;
         }
         if (tid < kRankMax) st->rank[tid] = 0ull;
+        if (tid == 0) st->nent = 0u;
         __syncthreads();
-        // this thread's crossing keys: counted (and histogrammed) first
-        uint32_t cnt = 0;
-        uint2 le = make_uint2(kNotCand, 0u);   // listed: this thread's list entry
-        if (nl >= 0) {
-            if (tid < nl) le = gl[tid];
-            const bool in = le.x < kNoMass && (le.x >> shift) == pref;
-            cnt = in;
-            if (in && pass < 2) atomicAdd((unsigned long long*)&hist[(le.x >> nshift) & nmask], (unsigned long long)mass_of(le.x));
-        } else {
-#pragma unroll 4
-            for (int p = tid; p < n; p += kBT) {
-                const uint32_t k = key_at(p);
-                const bool in = k < kNoMass && (k >> shift) == pref;
-                cnt += in;
-                if (in && pass < 2) atomicAdd((unsigned long long*)&hist[(k >> nshift) & nmask], (unsigned long long)mass_of(k));
-            }
-        }
-        const uint32_t inc = (uint32_t)zha_wave_incl_scan_u64(cnt);
-        if (lane == 63) st->wc[wave] = inc;
-        __syncthreads();
-        uint32_t e = inc - cnt, ne = 0;
+        // the crossing bin's keys, appended a wave and a batch at a time (one LDS
+        // atomic per wave and batch reserves their slots): the first kRankMax to the
+        // rank table, the first kGather to the list while none is kept yet; each adds
+        // its mass to the next digit's histogram
+        const bool listing = nl < 0;
+        const auto append = [&](const uint32_t* kk, const int* pp, int nb) {
+            bool in[kSweepB];
+            uint64_t bal[kSweepB];
+            uint32_t tot = 0;
 #pragma unroll
-        for (int w2 = 0; w2 < kBW; ++w2) {
-            const uint32_t x = st->wc[w2];
-            e += w2 < wave ? x : 0u;
-            ne += x;
-        }
-        const bool to_rank = ne <= (uint32_t)kRankMax;
-        const bool to_list = nl < 0 && ne <= (uint32_t)kGather;
-        if (cnt && (to_rank || to_list)) {
-            if (nl >= 0) {
-                const uint64_t ms = mass_of(le.x);
-                st->ent[e] = make_uint4(le.x, le.y, (uint32_t)ms, (uint32_t)(ms >> 32));
-            } else {
-                for (int p = tid; p < n; p += kBT) {
-                    const uint32_t k = key_at(p);
-                    if (k < kNoMass && (k >> shift) == pref) {
-                        if (to_rank) {
-                            const uint64_t ms = mass_of(k);
-                            st->ent[e] = make_uint4(k, (uint32_t)p, (uint32_t)ms, (uint32_t)(ms >> 32));
-                        }
-                        if (to_list) gl[e] = make_uint2(k, (uint32_t)p);
-                        ++e;
-                    }
+            for (int j = 0; j < kSweepB; ++j) {
+                in[j] = j < nb && (kk[j] < kNoMass) & ((kk[j] >> shift) == pref);
+                bal[j] = __ballot(in[j]);
+                tot += (uint32_t)__popcll(bal[j]);
+            }
+            if (tot == 0u) return;             // uniform over the wave
+            uint32_t e0 = 0;
+            if (lane == 0) e0 = atomicAdd(&st->nent, tot);
+            e0 = (uint32_t)__shfl((int)e0, 0);
+#pragma unroll
+            for (int j = 0; j < kSweepB; ++j) {
+                if (in[j]) {
+                    const uint32_t k = kk[j];
+                    const uint32_t e = e0 + bits_below_lane(bal[j]);
+                    const uint64_t ms = mass_of(k);
+                    if (e < (uint32_t)kRankMax) st->ent[e] = make_uint4(k, (uint32_t)pp[j], (uint32_t)ms, (uint32_t)(ms >> 32));
+                    if (listing && e < (uint32_t)kGather) gl[e] = make_uint2(k, (uint32_t)pp[j]);
+                    if (pass < 2) atomicAdd((unsigned long long*)&hist[(k >> nshift) & nmask], (unsigned long long)ms);
                 }
+                e0 += (uint32_t)__popcll(bal[j]);
+            }
+        };
+        if (!listing) {
+            uint32_t kk[kSweepB];
+            int pp[kSweepB];
+            const uint2 le = tid < nl ? gl[tid] : make_uint2(kNotCand, 0u);
+            kk[0] = le.x;
+            pp[0] = (int)le.y;
+            append(kk, pp, 1);
+        } else {
+#pragma unroll 1
+            for (int base = tid; base - tid < n; base += kSweepB * kBT) {   // uniform
+                uint32_t kk[kSweepB];
+                int pp[kSweepB];
+#pragma unroll
+                for (int j = 0; j < kSweepB; ++j) {
+                    pp[j] = base + j * kBT;
+                    kk[j] = kNotCand;
+                    if (pp[j] < n) kk[j] = key_at(pp[j]);
+                }
+                append(kk, pp, kSweepB);
             }
         }
         __syncthreads();
+        const uint32_t ne = st->nent;
+        const bool to_rank = ne <= (uint32_t)kRankMax;
+        const bool to_list = listing && ne <= (uint32_t)kGather;
         if (to_list) nl = (int)ne;
         if (to_rank) {
-            // rank them: entry i's mass before it in (key, position) order is summed by
-            // kBT / kRankMax threads, each over kRankMax / (kBT / kRankMax) entries j
-            // (the same j for a whole wave: broadcast reads); the entry whose own mass
-            // reaches what the bin must supply is the cut
-            {
-                constexpr int kSl = kBT / kRankMax, kPerSl = kRankMax / kSl;
-                const int i = tid % kRankMax, q = tid / kRankMax;
-                const uint4 me = st->ent[i < (int)ne ? i : 0];
-                uint64_t acc = 0;
-#pragma unroll
-                for (int jj = 0; jj < kPerSl; ++jj) {
-                    const int j = q * kPerSl + jj;
-                    if (j < (int)ne) {
-                        const uint4 f = st->ent[j];
-                        const bool prec = f.x < me.x || (f.x == me.x && f.y < me.y);
-                        acc += prec ? (((uint64_t)f.w << 32) | f.z) : 0ull;
-                    }
-                }
-                if (i < (int)ne && acc) atomicAdd((unsigned long long*)&st->rank[i], (unsigned long long)acc);
-            }
-            __syncthreads();
-            if (tid < (int)ne) {
-                const uint4 me = st->ent[tid];
-                const uint64_t before = st->rank[tid], own = ((uint64_t)me.w << 32) | me.z;
-                if (before < need && before + own >= need) {
-                    st->ustar = me.x;
-                    st->plim = me.y;
-                }
-            }
-            __syncthreads();
-            ustar = st->ustar;
-            plim = st->plim;
+            rank_entries(st, (int)ne, need, ustar, plim);
             return;
         }
         if (pass == 2) {
@@ -950,8 +1022,10 @@ __device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint6
 
 __device__ __forceinline__ bool kept_by(uint32_t key, uint32_t p, bool none, bool keep_all, uint32_t ustar,
                                         uint32_t plim) {
-    return !none && key != kNotCand &&
-           (keep_all || (key < kNoMass && (key < ustar || (key == ustar && p <= plim))));
+    // branch-free (bitwise, not short-circuit): keeps loads ahead of it batched
+    const bool cand = key != kNotCand;
+    const bool below = (key < kNoMass) & ((key < ustar) | ((key == ustar) & (p <= plim)));
+    return (!none) & cand & (keep_all | below);
 }
 
 // Maximum over the workgroup (every thread receives it).
@@ -976,6 +1050,7 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, int c, float top_p) {
     __shared__ __align__(16) uint32_t s_keys[kChainSlots];
     __shared__ int32_t s_kept[kChainSlots];
+    __shared__ int32_t s_node[kChainSlots];
     __shared__ __align__(16) uint64_t s_hist[kHistBins];
     __shared__ uint2 s_gl[kGather];
     __shared__ uint64_t s_bm[kChainSlots / 64];
@@ -983,15 +1058,50 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
     __shared__ uint32_t s_tot[2];
     __shared__ float s_red[kBW];
     __shared__ CutShared st;
+    __shared__ __align__(16) float s_sig[kChainStage];
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the head's scores of every chained level, staged in LDS together (one round
+    // trip) when they fit: level li's complete nodes at soff[li] (rows read as
+    // whole 16-byte vectors, which never pass a row's padded end)
+    int soff[ZHA_MAX_CHAIN + 1];
+    soff[0] = 0;
+#pragma unroll
+    for (int li = 0; li < ZHA_MAX_CHAIN; ++li)
+        soff[li + 1] = soff[li] + (li < m.n ? (m.lv[li].n_nodes + 3) / 4 * 4 : 0);
+    const bool staged = soff[ZHA_MAX_CHAIN] <= kChainStage;
+    if (staged) {
+        constexpr int kStageV = kChainStage / 4 / kBT;     // 16-byte vectors per thread
+        float4 t[kStageV];
+#pragma unroll
+        for (int k = 0; k < kStageV; ++k) {
+            const int o = 4 * (tid + k * kBT);               // staged float index
+            const float* row = m.lv[0].sig + ((size_t)g * G + hl) * (size_t)m.lv[0].sstride;
+            int base = 0;
+#pragma unroll
+            for (int j = 1; j < ZHA_MAX_CHAIN; ++j) {
+                if (j < m.n && o >= soff[j]) {
+                    row = m.lv[j].sig + ((size_t)g * G + hl) * (size_t)m.lv[j].sstride;
+                    base = soff[j];
+                }
+            }
+            t[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (o < soff[ZHA_MAX_CHAIN]) t[k] = *reinterpret_cast<const float4*>(row + (o - base));
+        }
+#pragma unroll
+        for (int k = 0; k < kStageV; ++k) {
+            const int o = 4 * (tid + k * kBT);
+            if (o < soff[ZHA_MAX_CHAIN]) *reinterpret_cast<float4*>(s_sig + o) = t[k];
+        }
+        __syncthreads();
+    }
     int nk = 0;
 #pragma unroll 1
     for (int li = 0; li < m.n; ++li) {
         const ZhaChainLevel& L = m.lv[li];
         const int n = li == 0 ? L.n_nodes : nk * c + (L.orph_hi - L.orph_lo);
         const float* sg = L.sig + ((size_t)g * G + hl) * (size_t)L.sstride;
-        int32_t node[kChainPer];
+        const float* ss = s_sig + soff[li];
         float x[kChainPer];
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) {
@@ -1002,20 +1112,18 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
                 const int pi = pc / c;
                 nd = p < nk * c ? s_kept[pi] * c + (pc - pi * c) : L.orph_lo + (p - nk * c);
             }
-            node[k] = p < n ? nd : 0;
+            nd = p < n ? nd : 0;
+            s_node[p] = nd;
+            x[k] = p < n ? (staged ? ss[nd] : sg[nd]) : zha_neg_inf();
         }
-#pragma unroll
-        for (int k = 0; k < kChainPer; ++k) x[k] = tid + k * kBT < n ? sg[node[k]] : zha_neg_inf();
         float mx = zha_neg_inf();
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) mx = fmaxf(mx, x[k]);
         const float M = block_max(mx, s_red);   // (its barriers also end every read of s_kept)
-        uint32_t key[kChainPer];
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) {
             const int p = tid + k * kBT;
-            key[k] = p < n ? key_of(x[k], M) : kNotCand;
-            s_keys[p] = key[k];
+            s_keys[p] = p < n ? key_of(x[k], M) : kNotCand;
         }
         for (int i = tid; i < kChainSlots / 64; i += kBT) s_bm[i] = 0ull;
         __syncthreads();
@@ -1023,16 +1131,18 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
         const bool keep_all = !none && top_p >= 1.0f;
         uint32_t ustar = 0, plim = 0xFFFFFFFFu;
         if (!none && !keep_all) block_cut(LdsKeys{s_keys}, n, top_p, false, s_hist, s_gl, &st, ustar, plim);
-        // kept flags and their ranks in position order (rows of 1024 positions)
+        // kept flags and their ranks in position order (rows of 1024 positions);
+        // keys and node ids read back from LDS (not held across the cut)
         bool kept[kChainPer];
         uint64_t bal[kChainPer];
         uint32_t ncand = 0;
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) {
             const uint32_t p = (uint32_t)(tid + k * kBT);
-            kept[k] = kept_by(key[k], p, none, keep_all, ustar, plim);
+            const uint32_t key = s_keys[p];
+            kept[k] = kept_by(key, p, none, keep_all, ustar, plim);
             bal[k] = __ballot(kept[k]);
-            ncand += (uint32_t)__popcll(__ballot(key[k] != kNotCand));
+            ncand += (uint32_t)__popcll(__ballot(key != kNotCand));
             if (lane == 0) s_pre[k * kBW + wave] = (uint32_t)__popcll(bal[k]);
         }
         __syncthreads();
@@ -1048,9 +1158,10 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) {
             if (kept[k]) {
+                const int32_t nd = s_node[tid + k * kBT];
                 const uint32_t r = s_pre[k * kBW + wave] + bits_below_lane(bal[k]);
-                s_kept[r] = node[k];
-                atomicOr((unsigned long long*)&s_bm[node[k] >> 6], 1ull << (node[k] & 63));
+                s_kept[r] = nd;
+                atomicOr((unsigned long long*)&s_bm[nd >> 6], 1ull << (nd & 63));
             }
         }
         // candidates counted per wave above are the whole wave's: lane 0 of every wave
@@ -1281,12 +1392,9 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
     }
     // the head's kept count
     uint32_t my_kept = 0;
-    if (staged) {
-#pragma unroll 8
-        for (int p = tid; p < n; p += kBT) my_kept += kept_by(s_keys[p], (uint32_t)p, none, keep_all, ustar, plim);
-    } else {
-        for (int p = tid; p < n; p += kBT) my_kept += kept_by(key_of(sg[p], M), (uint32_t)p, none, keep_all, ustar, plim);
-    }
+    const auto count_kept = [&](uint32_t k, int p) { my_kept += kept_by(k, (uint32_t)p, none, keep_all, ustar, plim); };
+    if (staged) sweep_keys(LdsKeys{s_keys}, n, count_kept);
+    else sweep_keys(GlobKeys{sg, M}, n, count_kept);
     const uint64_t both = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)my_kept << 32) | my_cand), 63);
     if (lane == 0) s_wred[wave] = both;
     __syncthreads();
@@ -1334,18 +1442,20 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
         x[hh] = *reinterpret_cast<const float4*>(a.sig + ((size_t)g * G + (hh < G ? hh : 0)) * a.sstride + pv);
     if (tid < G) s_hc[tid] = mine;
     __syncthreads();
+    // every head's cut read from LDS at once, then the masks without branches
+    HeadCut hcs[ZHA_MAX_GROUP];
+#pragma unroll
+    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hcs[hh] = s_hc[hh < G ? hh : 0];
     uint32_t msk[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
-        if (hh < G) {                          // uniform; the loads are all issued above
-            const HeadCut hc = s_hc[hh];
-            const float v[4] = {x[hh].x, x[hh].y, x[hh].z, x[hh].w};
+        const HeadCut& hc = hcs[hh];
+        const float v[4] = {x[hh].x, x[hh].y, x[hh].z, x[hh].w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t key = p0 + j < n ? key_of(v[j], hc.m) : kNotCand;
-                msk[j] |= (uint32_t)kept_by(key, (uint32_t)(p0 + j), hc.mode == 2u, hc.mode == 1u, hc.ustar, hc.plim)
-                          << hh;
-            }
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t key = p0 + j < n ? key_of(v[j], hc.m) : kNotCand;
+            const bool k = (hh < G) & kept_by(key, (uint32_t)(p0 + j), hc.mode == 2u, hc.mode == 1u, hc.ustar, hc.plim);
+            msk[j] |= (uint32_t)k << hh;
         }
     }
     // the chunk's kept positions in order (4 per thread, thread-major): this

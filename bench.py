@@ -9,8 +9,12 @@ tokens, the sink and the tail).  The default workload is the light router
 4 levels, p 0.75) with 256 appended+decoded tokens; inputs are seeded
 synthetic caches resident in HBM before the timed region.
 
-Prints one JSON line.  `--sweep` adds the latency-vs-context curve
-(16K .. 10M tokens, light shape) against dense decode, one JSON line per point.
+Prints one JSON line: the light workload's step, a per-kernel event trace of the
+router, a cold-cache variant of the gather (1 GiB written between steps), the
+oracle timed on the host cores on a bounded sample, the latency-vs-context curve
+(16K .. 10M tokens, light shape) against dense decode and the ultra-long point
+(10,485,760 tokens with appends).  `--geometry` instead sweeps (chunk, levels, R,
+p) at 262,144 tokens.
 """
 from __future__ import annotations
 
@@ -36,9 +40,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="light")
-    ap.add_argument("--sweep", action="store_true", help="also run the 16K..10M context sweep")
-    ap.add_argument("--sweep-points", default="16384,32768,65536,131072,262144,524288,1048576,2097152,4194304,10485760")
-    ap.add_argument("--sweep-steps", type=int, default=32)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 16K..10M context sweep and the ultra point")
+    ap.add_argument("--sweep-points", default="16384,65536,262144,1048576,4194304,10485760")
+    ap.add_argument("--sweep-steps", type=int, default=16)
+    ap.add_argument("--ultra-steps", type=int, default=64)
+    ap.add_argument("--trace-steps", type=int, default=32, help="steps of the per-kernel event trace")
+    ap.add_argument("--cold-steps", type=int, default=32, help="steps of the cold-cache gather variant")
+    ap.add_argument("--flush-bytes", type=int, default=1 << 30, help="bytes written between cold steps")
+    ap.add_argument("--geometry", action="store_true", help="only run the (c, L, R, p) geometry sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--out", default=None, help="also append the JSON line(s) to this file")
@@ -196,30 +205,28 @@ def bench_workload(args, torch, W, B, ZhaLayer):
     step_us = sorted(r[0].elapsed_time(r[3]) * 1e3 for r in evs)      # each decode between its first and last event
     dec_med_us = step_us[len(step_us) // 2]
 
-    # Algorithmic bytes of the same steps: replayed once more, reading each step's
-    # kept lists on the host (the selection is deterministic).
+    # Algorithmic bytes of the same steps: replayed once more with the step's device
+    # stats (the selection is deterministic) and the level-1 kept lists on the host.
     layer.n_tokens = N
     gather_bytes = router_bytes = 0
     keys_read = []
     keys_head = []
+    stats = layer.new_stats()
+    G = w.n_q_heads // w.n_kv_heads
     R = w.n_ref
     for t in range(args.steps):
         i = t % x["q"].shape[0]
         if w.append:
             layer.append(x["k_app"][i], x["v_app"][i])
-        layer.decode(x["q"][i])
-        torch.cuda.synchronize()
+        layer.decode(x["q"][i], stats=stats)
+        st = layer.read_stats(stats)
         n = layer.n_tokens
+        gather_bytes += st["gather_bytes"]
+        router_bytes += sum(st["bytes_streamed"])
+        keys_read.append(st["gather_tokens"] / (w.n_kv_heads * n))
         r1 = layer.route_level(1)
-        ut = [union_tokens(r1, g, n, c) for g in range(w.n_kv_heads)]
-        gather_bytes += sum(ut) * 2 * d * e_kv
-        keys_read.append(sum(ut) / (w.n_kv_heads * n))
-        G = w.n_q_heads // w.n_kv_heads
         keys_head.append(sum(head_tokens(r1, g, hl, n, c) for g in range(w.n_kv_heads) for hl in range(G))
                          / (w.n_q_heads * n))
-        for lv in range(1, w.levels + 1):
-            if n // c ** lv:
-                router_bytes += int(layer.route_level(lv)["n_cand"].sum()) * R * (d + 1) * 4
     layer.n_tokens = N
     K = args.steps
     gather_us = gather_ms / K * 1e3
@@ -327,32 +334,194 @@ def cpu_baseline(args, layer, x, w, torch):
                       f"value_one_core: {done1} decode steps with BLAS on one thread"}
 
 
+def _events(torch, n):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    st = torch.cuda.current_stream()
+    for e in evs:
+        e.record(st)          # creates the underlying HIP events
+    torch.cuda.synchronize()
+    return evs
+
+
+def trace_kernels(args, layer, x, w, torch, B):
+    """Per-kernel device time of decode steps (an event after every kernel, on the
+    step's stream) and each kernel's algorithmic bytes from the step's own stats
+    (the same query decoded again with stats: the routing is deterministic)."""
+    N, c, G = layer.n_tokens, w.chunk, w.n_q_heads // w.n_kv_heads
+    evs = _events(torch, 40)
+    handles = [e.cuda_event for e in evs]
+    stats = layer.new_stats()
+    acc = {}
+    K = args.trace_steps
+    for t in range(K):
+        q = x["q"][t % x["q"].shape[0]]
+        kinds = B.zha_decode_step_traced(layer.cfg, layer.bufs, N, q, layer.out, handles)
+        torch.cuda.synchronize()
+        layer.decode(q, stats=stats)
+        st = layer.read_stats(stats)
+        kinds_l = [k for k in kinds]
+        chain_lv = []
+        if any(k == "chain" for k, _ in kinds_l):
+            top = kinds_l[0][1]
+            scored = [lv for k, lv in kinds_l if k == "score"]
+            low = (max(scored) + 1) if scored else 1
+            chain_lv = list(range(low, top + 1))
+        for i in range(1, len(kinds_l)):
+            name, lv = kinds_l[i]
+            us = evs[i - 1].elapsed_time(evs[i]) * 1e3
+            if name == "score_all":
+                byts = sum(st["bytes_streamed"][l - 1] + (N // c ** l) * w.n_q_heads * 4 for l in chain_lv)
+            elif name == "chain":
+                byts = sum((N // c ** l) * w.n_q_heads * 4 for l in chain_lv)
+            elif name == "score":
+                byts = st["bytes_read"][lv - 1] + st["group_cand"][lv - 1] * G * 4
+            elif name == "select":
+                byts = st["group_cand"][lv - 1] * G * 4
+            elif name == "cross":
+                byts = st["group_cand"][lv - 1] * G * 4
+            elif name == "resolve":
+                byts = 0
+            elif name == "apply":
+                byts = st["group_cand"][lv - 1] * G * 4 + st["group_kept"][lv - 1] * 8
+            elif name == "gather":
+                byts = st["gather_bytes"]
+            else:
+                byts = None
+            key = f"{name} L{lv}" if name in ("score", "select", "cross", "resolve", "apply") else name
+            a = acc.setdefault(key, {"us": 0.0, "bytes": 0, "n": 0, "counted": byts is not None})
+            a["us"] += us
+            a["n"] += 1
+            if byts is not None:
+                a["bytes"] += byts
+    out = []
+    for key, a in acc.items():
+        us = a["us"] / a["n"]
+        row = {"kernel": key, "us": round(us, 3)}
+        if a["counted"]:
+            byts = a["bytes"] / a["n"]
+            row["alg_bytes"] = int(byts)
+            row["gbs"] = round(byts / (us * 1e-6) / 1e9, 1)
+            row["frac"] = round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        out.append(row)
+    return out
+
+
+def cold_gather(args, layer, x, w, torch, B):
+    """Decode steps with args.flush_bytes written to a scratch buffer before each (outside
+    the step's events): the 256 MB Infinity Cache and the L2s hold none of the cache's
+    rows when the gather starts.  Returns the gather kernel's and the step's device time."""
+    N = layer.n_tokens
+    flush = torch.empty(args.flush_bytes, dtype=torch.uint8, device="cuda")
+    K = args.cold_steps
+    rows = [_events(torch, 4) for _ in range(K)]
+    stats = layer.new_stats()
+    gb = 0
+    for t in range(K):
+        q = x["q"][t % x["q"].shape[0]]
+        flush.fill_(t & 255)
+        B.zha_decode_step_timed(layer.cfg, layer.bufs, N, q, layer.out, [e.cuda_event for e in rows[t]])
+    torch.cuda.synchronize()
+    for t in range(K):
+        layer.decode(x["q"][t % x["q"].shape[0]], stats=stats)
+        gb += layer.read_stats(stats)["gather_bytes"]
+    g_us = sum(r[1].elapsed_time(r[2]) for r in rows) / K * 1e3
+    d_us = sum(r[0].elapsed_time(r[3]) for r in rows) / K * 1e3
+    del flush
+    torch.cuda.empty_cache()
+    return {"gather_us": round(g_us, 3), "decode_us": round(d_us, 3),
+            "gather_gbs": round(gb / K / (g_us * 1e-6) / 1e9, 1), "flush_bytes": args.flush_bytes}
+
+
+def point(torch, W, B, ZhaLayer, w, steps, dense_steps, append):
+    """Decode latency of workload w at its own size against dense, with the route/gather
+    split (HIP events), keys read and summary bytes; appends before each step if asked."""
+    x = W.generate(w, device="cuda")
+    layer = ZhaLayer(B.config_of(w), x["k"], x["v"], x["ref_q"])
+    n = w.n_tokens
+    t0 = time.perf_counter()
+    layer.build(n)
+    torch.cuda.synchronize()
+    build_ms = (time.perf_counter() - t0) * 1e3
+    nq = x["q"].shape[0]
+    for t in range(4):
+        layer.decode(x["q"][t % nq])
+        layer.dense(x["q"][t % nq])
+    if append:
+        run_steps(layer, x, w, n, min(8, steps), True)
+        layer.n_tokens = n
+    us_z = timed(lambda: run_steps(layer, x, w, n, steps, append), torch) / steps * 1e6
+    layer.n_tokens = n
+    us_d = timed(lambda: [layer.dense(x["q"][t % nq]) for t in range(dense_steps)], torch) / dense_steps * 1e6
+    rows = [_events(torch, 4) for _ in range(min(steps, 16))]
+    for t, r in enumerate(rows):
+        if append:
+            layer.append(x["k_app"][t % nq], x["v_app"][t % nq])
+        B.zha_decode_step_timed(layer.cfg, layer.bufs, layer.n_tokens, x["q"][t % nq], layer.out,
+                                [e.cuda_event for e in r])
+    torch.cuda.synchronize()
+    route = sum(r[0].elapsed_time(r[1]) for r in rows) / len(rows) * 1e3
+    gather = sum(r[1].elapsed_time(r[2]) for r in rows) / len(rows) * 1e3
+    stats = layer.new_stats()
+    layer.decode(x["q"][0], stats=stats)
+    st = layer.read_stats(stats)
+    H = w.n_kv_heads
+    line = {"n_tokens": n, "levels": w.levels, "chunk": w.chunk, "n_ref": w.n_ref, "top_p": w.top_p,
+            "zha_decode_us": round(us_z, 2), "dense_decode_us": round(us_d, 2),
+            "speedup_vs_dense": round(us_d / us_z, 3), "route_us": round(route, 2), "gather_us": round(gather, 2),
+            "keys_read_frac": round(st["gather_tokens"] / (H * layer.n_tokens), 5),
+            "router_bytes": int(sum(st["bytes_streamed"])),
+            "dense_gbs_alg": round(H * layer.n_tokens * 2 * w.head_dim * (2 if w.kv_dtype == "bf16" else 4)
+                                   / (us_d * 1e-6) / 1e9, 1),
+            "build_ms": round(build_ms, 2)}
+    del layer, x
+    torch.cuda.empty_cache()
+    return line
+
+
 def sweep(args, torch, W, B, ZhaLayer):
+    """Light-shape decode latency against dense from 16K to 10M tokens (levels chosen so
+    the top level has at most 64 nodes), no appends."""
     base = W.get("light")
     lines = []
     for n in [int(v) for v in args.sweep_points.split(",")]:
         L = W.levels_for(n, base.chunk)
-        w = dataclasses.replace(base, name=f"light@{n}", n_tokens=n, levels=L, steps=args.sweep_steps, append=False)
+        w = dataclasses.replace(base, name=f"light@{n}", n_tokens=n, levels=L, steps=max(args.sweep_steps, 8),
+                                append=False)
         _log(f"[sweep] N={n} L={L}")
-        x = W.generate(w, device="cuda")
-        layer = ZhaLayer(B.config_of(w), x["k"], x["v"], x["ref_q"])
-        layer.build(n)
-        for t in range(4):
-            layer.decode(x["q"][t % w.steps])
-            layer.dense(x["q"][t % w.steps])
-        K = args.sweep_steps
-        us_z = timed(lambda: [layer.decode(x["q"][t % w.steps]) for t in range(K)], torch) / K * 1e6
-        us_d = timed(lambda: [layer.dense(x["q"][t % w.steps]) for t in range(K)], torch) / K * 1e6
-        r1 = layer.route_level(1)
-        kr = sum(union_tokens(r1, g, n, w.chunk) for g in range(w.n_kv_heads)) / (w.n_kv_heads * n)
-        line = {"sweep": "light", "n_tokens": n, "levels": L, "zha_decode_us": round(us_z, 2),
-                "dense_decode_us": round(us_d, 2), "speedup_vs_dense": round(us_d / us_z, 3),
-                "keys_read_frac": round(kr, 5),
-                "dense_gbs_alg": round(w.n_kv_heads * n * 2 * w.head_dim * 2 / (us_d * 1e-6) / 1e9, 1)}
+        line = point(torch, W, B, ZhaLayer, w, args.sweep_steps, args.sweep_steps, False)
         _log(json.dumps(line))
         lines.append(line)
-        del layer, x
-        torch.cuda.empty_cache()
+    return lines
+
+
+def ultra_point(args, torch, W, B, ZhaLayer):
+    """The ultra-long light workload (10,485,760 tokens, 7 levels): append + decode steps."""
+    w = dataclasses.replace(W.get("ultra"), steps=max(W.get("ultra").steps, args.ultra_steps))
+    _log(f"[ultra] N={w.n_tokens} L={w.levels} steps={args.ultra_steps}")
+    line = point(torch, W, B, ZhaLayer, w, args.ultra_steps, 8, True)
+    line["workload"] = "ultra"
+    line["append_per_step"] = True
+    _log(json.dumps(line))
+    return line
+
+
+GEOMETRY = [  # (chunk, levels, n_ref, top_p) at 262,144 tokens, light heads and generator
+    (4, 8, 1, 0.75), (8, 4, 1, 0.75), (16, 3, 1, 0.75), (32, 2, 1, 0.75), (64, 2, 1, 0.75), (256, 1, 1, 0.75),
+    (8, 4, 4, 0.75), (8, 4, 16, 0.75), (4, 6, 16, 0.95), (256, 1, 16, 0.95),
+    (8, 4, 1, 0.5), (8, 4, 1, 0.9), (8, 4, 1, 0.95), (8, 4, 1, 0.99),
+]
+
+
+def geometry(args, torch, W, B, ZhaLayer):
+    base = W.get("light")
+    lines = []
+    for c, L, R, p in GEOMETRY:
+        w = dataclasses.replace(base, name=f"light-c{c}-L{L}-R{R}-p{p}", chunk=c, levels=L, n_ref=R, top_p=p,
+                                steps=16, append=False)
+        _log(f"[geometry] c={c} L={L} R={R} p={p}")
+        line = point(torch, W, B, ZhaLayer, w, 16, 16, False)
+        _log(json.dumps(line))
+        lines.append(line)
     return lines
 
 
@@ -374,14 +543,37 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     B.lib()
+    if args.geometry:
+        line = json.dumps({"geometry": geometry(args, torch, W, B, ZhaLayer), "tokens": 262144})
+        print(line, flush=True)
+        if args.out:
+            with open(args.out, "a") as f:
+                f.write(line + "\n")
+        return
     result, layer, x, w = bench_workload(args, torch, W, B, ZhaLayer)
+    kern = trace_kernels(args, layer, x, w, torch, B)
+    result["router_kernels"] = [r for r in kern if r["kernel"] not in ("gather", "combine")]
+    rt_us = sum(r["us"] for r in result["router_kernels"])
+    rt_b = sum(r.get("alg_bytes", 0) for r in result["router_kernels"])
+    result["router_roofline"] = {"bound": "latency", "us": round(rt_us, 3), "alg_bytes": rt_b,
+                                 "achieved": round(rt_b / (rt_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(rt_b / (rt_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "note": "traced steps, an event after every kernel (its dispatch gap included)"}
+    cold = cold_gather(args, layer, x, w, torch, B)
+    rf = result["roofline"]
+    rf["warm_source"] = "hbm_or_mall"
+    rf["achieved_cold"] = cold["gather_gbs"]
+    rf["frac_cold"] = round(cold["gather_gbs"] / HBM_PEAK_GBS, 4)
+    result["cold"] = cold
+    _log(f"[bench] cold gather {cold['gather_us']:.1f} us ({cold['gather_gbs']:.0f} GB/s), "
+         f"cold decode {cold['decode_us']:.1f} us; router kernels {rt_us:.1f} us")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, layer, x, w, torch)
-    del layer
+    del layer, x
     torch.cuda.empty_cache()
-    lines = [result]
-    if args.sweep:
+    if not args.no_sweep:
         result["sweep"] = sweep(args, torch, W, B, ZhaLayer)
+        result["ultra"] = ultra_point(args, torch, W, B, ZhaLayer)
     line = json.dumps(result)
     print(line, flush=True)
     if args.out:

@@ -24,8 +24,12 @@ ZHA_F32 = 1
 EXPORTS = [
     "zha_check_config", "zha_tree_bytes", "zha_scratch_bytes", "zha_dense_scratch_bytes", "zha_sel_bytes",
     "zha_tree_level_offsets", "zha_route_level_offsets", "zha_build_tree", "zha_append_token",
-    "zha_decode_step", "zha_decode_step_timed", "dense_decode", "zha_last_error", "zha_decode_step_noalloc",
+    "zha_decode_step", "zha_decode_step_timed", "zha_decode_step_traced", "dense_decode", "zha_last_error",
+    "zha_decode_step_noalloc",
 ]
+# kinds of a traced step's kernels (kinds[i] = 100 * kind + level)
+TRACE_KINDS = {0: "start", 1: "score_all", 2: "chain", 3: "merge_ids", 4: "score", 5: "select", 6: "apply",
+               7: "gather", 8: "combine", 9: "cross", 10: "resolve"}
 NOALLOC_SCRATCH_BYTES = 32 << 20
 STATS_MAX_LEVELS = 32
 
@@ -121,6 +125,9 @@ def lib() -> ctypes.CDLL:
             "zha_decode_step_timed": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p,
                                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                      P(ctypes.c_void_p), ctypes.c_void_p]),
+            "zha_decode_step_traced": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p,
+                                                      ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_int32,
+                                                      P(ctypes.c_int32), P(ctypes.c_int32), ctypes.c_void_p]),
             "dense_decode": (ctypes.c_int, [cfgp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
             "zha_last_error": (ctypes.c_char_p, []),
@@ -244,6 +251,18 @@ def zha_decode_step_timed(cfg: Config, bufs: Buffers, n_tokens: int, q, out, eve
     arr = (ctypes.c_void_p * 4)(*[e if e else None for e in events])
     _check(lib().zha_decode_step_timed(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out),
                                        _ptr(sel), _ptr(stats), arr, _stream(stream)))
+
+
+def zha_decode_step_traced(cfg: Config, bufs: Buffers, n_tokens: int, q, out, events, stream=None):
+    """events: raw hipEvent_t handles (ints), one recorded before the step and one after each
+    kernel.  Returns [(kind name, level)] for events[0 .. n) as recorded."""
+    n_ev = len(events)
+    arr = (ctypes.c_void_p * n_ev)(*events)
+    kinds = (ctypes.c_int32 * n_ev)()
+    got = ctypes.c_int32(0)
+    _check(lib().zha_decode_step_traced(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out), arr,
+                                        n_ev, kinds, ctypes.byref(got), _stream(stream)))
+    return [(TRACE_KINDS.get(kinds[i] // 100, "?"), kinds[i] % 100) for i in range(got.value)]
 
 
 def dense_decode(cfg: Config, k, v, n_tokens: int, q, out, scratch, stream=None) -> None:

@@ -92,6 +92,7 @@ struct Layout {
     // decode scratch
     std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, stats;
     std::vector<size_t> hblk, ghist, hdone, hcut, tick, desc;   // selection state of a level below the chain
+    std::vector<size_t> pub, gcnt, gpart, glist;  // frontiers beyond ZHA_LDS_KEYS (glist 0: the level never has one)
     std::vector<int64_t> wcap;            // bitmap words per head per level
     std::vector<int64_t> sstr;            // score row stride per level (slots rounded up to 4)
     size_t pm = 0, pl = 0, po = 0, nact = 0;
@@ -129,7 +130,7 @@ Layout make_layout(const zha_config* cfg) {
 
     off = 0;
     for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.stats, &y.hblk, &y.ghist, &y.hdone, &y.hcut,
-                    &y.tick, &y.desc})
+                    &y.tick, &y.desc, &y.pub, &y.gcnt, &y.gpart, &y.glist})
         v->assign(y.L + 1, 0);
     y.wcap.assign(y.L + 1, 0);
     y.sstr.assign(y.L + 1, 0);
@@ -150,6 +151,12 @@ Layout make_layout(const zha_config* cfg) {
         y.hcut[l] = off;  off = align_up(off + 16 * H * G);
         y.tick[l] = off;  off = align_up(off + sizeof(uint32_t) * H);
         y.desc[l] = off;  off = align_up(off + sizeof(uint32_t) * H * (size_t)zha_apply_chunks((int64_t)n));
+        if (n > (size_t)ZHA_LDS_KEYS) {
+            y.pub[l] = off;   off = align_up(off + 16 * H * G);
+            y.gcnt[l] = off;  off = align_up(off + 16 * H * G);
+            y.gpart[l] = off; off = align_up(off + 8 * H * G * (size_t)ZHA_CROSS_MAXW);
+            y.glist[l] = off; off = align_up(off + 8 * H * G * (size_t)ZHA_GLIST);
+        }
     }
     attn_partials(cfg, off, y.pm, y.pl, y.po, y.nact);
     y.noparent = off; off = align_up(off + sizeof(int32_t) * std::max<size_t>(64, H));   // one entry per group
@@ -342,8 +349,22 @@ int record(void* const* events, int i, hipStream_t s) {
     return e == hipSuccess ? ZHA_OK : hip_fail(e, "event record");
 }
 
+// An event after each kernel of a traced step (none when ev is null).
+struct Trace {
+    void* const* ev = nullptr;
+    int32_t* kinds = nullptr;
+    int max = 0, n = 0;
+    int mark(int kind, int level, hipStream_t s) {
+        if (!ev || n >= max) return ZHA_OK;
+        if (kinds) kinds[n] = kind * 100 + level;
+        return record(ev, n++, s);
+    }
+};
+
 int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q, float* out,
-                int32_t* sel, zha_stats* stats, void* const* events, void* stream) {
+                int32_t* sel, zha_stats* stats, void* const* events, void* stream, Trace* tr = nullptr) {
+    Trace untraced;
+    Trace& TR = tr ? *tr : untraced;
     int rc = validate(cfg);
     if (rc) return rc;
     if (!bufs || !bufs->k || !bufs->v || !bufs->tree || !bufs->scratch || !q || !out)
@@ -422,10 +443,13 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             cl.wcap = (int32_t)y.wcap[l];
             cl.sstride = (int32_t)y.sstr[l];
         }
+        if ((rc = TR.mark(0, top, s))) return rc;
         hipError_t e = zha_launch_score_all(cfg->kv_dtype, q, sa, y.H, y.G, c, R, tau, s);
         if (e != hipSuccess) return hip_fail(e, "score launch (chain)");
+        if ((rc = TR.mark(ZHA_TRACE_SCORE_ALL, top, s))) return rc;
         e = zha_launch_chain(cs, y.H, y.G, c, cfg->top_p, s);
         if (e != hipSuccess) return hip_fail(e, "chain launch");
+        if ((rc = TR.mark(ZHA_TRACE_CHAIN, top, s))) return rc;
         if (below == 0) {
             // the chain reached level 1: its group kept list for the gather
             ZhaLevelArgs a1 = level_args(1);
@@ -433,6 +457,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             a1.n_top = n_nodes(cfg, n_tokens, 1);
             e = zha_launch_merge_ids(a1, y.H, y.G, c, s);
             if (e != hipSuccess) return hip_fail(e, "merge launch (chain)");
+            if ((rc = TR.mark(ZHA_TRACE_MERGE_IDS, 1, s))) return rc;
         }
     }
     // Every level below: score over the group's candidates, then select.  The first
@@ -445,6 +470,12 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.hcut = (void*)(X + y.hcut[l]);
         a.tick = (uint32_t*)(X + y.tick[l]);
         a.desc = (uint32_t*)(X + y.desc[l]);
+        if (y.glist[l]) {
+            a.pub = (uint4*)(X + y.pub[l]);
+            a.gcnt = (uint4*)(X + y.gcnt[l]);
+            a.gpart = (uint2*)(X + y.gpart[l]);
+            a.glist = (uint2*)(X + y.glist[l]);
+        }
         a.ndesc = zha_apply_chunks(y.cap[l]);
         const int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);
         a.score_blocks = blocks;
@@ -460,11 +491,25 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             pa.pnkept = (const int32_t*)(X + y.noparent);
             pa.pcap = 1;
         }
+        if (nchain == 0 && l == top && (rc = TR.mark(0, l, s))) return rc;
         hipError_t e = zha_launch_route_score(cfg->kv_dtype, q, a, y.H, y.G, c, R, tau, blocks, s,
                                               defer ? &pa : nullptr);
         if (e != hipSuccess) return hip_fail(e, "route score launch");
+        if ((rc = TR.mark(ZHA_TRACE_SCORE, l, s))) return rc;
         e = zha_launch_select(a, y.H, y.G, c, cfg->top_p, s);
         if (e != hipSuccess) return hip_fail(e, "route select launch");
+        if ((rc = TR.mark(ZHA_TRACE_SELECT, l, s))) return rc;
+        if (a.glist) {
+            e = zha_launch_cross(a, y.H, y.G, c, s);
+            if (e != hipSuccess) return hip_fail(e, "route cross launch");
+            if ((rc = TR.mark(ZHA_TRACE_CROSS, l, s))) return rc;
+            e = zha_launch_resolve(a, y.H, y.G, c, cfg->top_p, s);
+            if (e != hipSuccess) return hip_fail(e, "route resolve launch");
+            if ((rc = TR.mark(ZHA_TRACE_RESOLVE, l, s))) return rc;
+        }
+        e = zha_launch_apply(a, y.H, y.G, c, s);
+        if (e != hipSuccess) return hip_fail(e, "route apply launch");
+        if ((rc = TR.mark(ZHA_TRACE_APPLY, l, s))) return rc;
     }
 
     ZhaAttnArgs at_;
@@ -484,13 +529,16 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     at_.po = (float*)(X + y.po);
     at_.nact = (int32_t*)(X + y.nact);
     const int Bg = attn_blocks(n_tokens + 1, y.H, cfg->kv_dtype);
+    if (top == 0 && (rc = TR.mark(0, 0, s))) return rc;
     // events 1 and 2 bracket the gather kernel's own execution
     hipError_t e = zha_launch_attention(cfg->kv_dtype, false, at_, y.H, y.G, c, tau, Bg, s,
                                         events ? static_cast<hipEvent_t>(events[1]) : nullptr,
                                         events ? static_cast<hipEvent_t>(events[2]) : nullptr);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if ((rc = TR.mark(ZHA_TRACE_GATHER, 0, s))) return rc;
     e = zha_launch_combine(at_, y.H, y.G, Bg, out, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
+    if ((rc = TR.mark(ZHA_TRACE_COMBINE, 0, s))) return rc;
     if ((rc = record(events, 3, s))) return rc;
     if (sel) {
         e = zha_launch_sel(at_.klist, at_.kmask, at_.nkept, at_.cap1, y.H, y.G, sel, s);
@@ -535,6 +583,23 @@ int zha_decode_step(const zha_config* cfg, const zha_buffers* bufs, int64_t n_to
 int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q,
                           float* out, int32_t* sel, zha_stats* stats, void* const* events, void* stream) {
     return decode_impl(cfg, bufs, n_tokens, q, out, sel, stats, events, stream);
+}
+
+int zha_decode_step_traced(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q,
+                           float* out, void* const* events, int32_t max_events, int32_t* kinds, int32_t* n_events,
+                           void* stream) {
+    if (!events || max_events < 1 || !kinds || !n_events)
+        return fail(ZHA_ERR_ARG, "traced step: events, kinds and n_events must be non-NULL, max_events >= 1");
+    for (int32_t i = 0; i < max_events; ++i)
+        if (!events[i]) return fail(ZHA_ERR_ARG, "traced step: every one of the max_events events must be non-NULL");
+    Trace tr;
+    tr.ev = events;
+    tr.kinds = kinds;
+    tr.max = max_events;
+    *n_events = 0;
+    const int rc = decode_impl(cfg, bufs, n_tokens, q, out, nullptr, nullptr, nullptr, stream, &tr);
+    *n_events = tr.n;
+    return rc;
 }
 
 int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_tokens, const void* q, float* out,

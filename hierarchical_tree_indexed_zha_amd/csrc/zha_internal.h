@@ -78,6 +78,13 @@ struct ZhaLevelArgs {
     uint64_t* ghist;           // [H_q][ZHA_HIST_BINS] first-digit mass histograms of the select slices
     uint32_t* hdone;           // [H_q] select slice workgroups done
     void* hcut;                // [H_q] each head's cut (16 bytes)
+    // frontiers beyond ZHA_LDS_KEYS candidates per head (null when the level's
+    // capacity never exceeds it): the select kernel publishes each head's first
+    // crossing bin, the cross kernel lists that bin's keys, the resolve kernel cuts
+    uint4* pub;                // [H_q] {crossing bin, mass still needed (lo, hi), head max bits}
+    uint4* gcnt;               // [H_q] {listed keys, -, -, overflow}
+    uint2* gpart;              // [H_q][ZHA_CROSS_MAXW] per cross workgroup {keys below the bin, candidates}
+    uint2* glist;              // [H_q][ZHA_GLIST] listed keys {key, position}
     uint32_t* tick;            // [H_kv] apply chunks started
     uint32_t* desc;            // [H_kv][ndesc] look-back descriptors of the apply chunks
     int ndesc;                 // apply chunks per group at this level's capacity
@@ -89,6 +96,14 @@ struct ZhaLevelArgs {
 #define ZHA_LEVEL_ARGS_READY(a, ...) \
     asm volatile("" ::"s"((a).S), "s"((a).pcap), "s"((a).wcap), "s"((a).hblk), "s"((a).ndesc), __VA_ARGS__)
 #define ZHA_LDS_KEYS 32768     // a head's keys staged in LDS by the workgroup that cuts it
+#define ZHA_GLIST 16384        // a large frontier's crossing-bin keys listed per head
+#define ZHA_CROSS_MAXW 32      // cross workgroups per head
+// Cross workgroups per head for a level of `cap` node slots: 4 slices of 1024
+// positions each at least, at most ZHA_CROSS_MAXW.
+__host__ __device__ inline int zha_cross_blocks(int64_t cap) {
+    int64_t w = (cap + 4 * 1024 - 1) / (4 * 1024);
+    return (int)(w < 1 ? 1 : w > ZHA_CROSS_MAXW ? ZHA_CROSS_MAXW : w);
+}
 // The level below the chain derives the chain's last level's group kept list from
 // the chain's per-head bitmaps (`defer` = that level's arguments: top = 1, n_top
 // its complete nodes, bitmaps over node ids) in its score kernel; at most
@@ -99,6 +114,11 @@ hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArg
                                   int R, float tau, int blocks, hipStream_t stream,
                                   const ZhaLevelArgs* defer = nullptr);
 hipError_t zha_launch_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream);
+hipError_t zha_launch_apply(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream);
+// frontiers beyond ZHA_LDS_KEYS: list the crossing bin's keys over many workgroups,
+// then cut each head from its list (both return at once for other heads)
+hipError_t zha_launch_cross(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream);
+hipError_t zha_launch_resolve(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream);
 int zha_apply_chunks(int64_t cap);
 int zha_score_blocks(int64_t max_cand, int R);
 // The chain: the first routed levels while each has at most ZHA_CHAIN_SLOTS node

@@ -470,6 +470,8 @@ __device__ __forceinline__ uint64_t mass_of(uint32_t key) {
 constexpr int kBT = 1024;                     // threads of a selecting workgroup
 constexpr int kBW = kBT / 64;
 constexpr int kLdsKeys = ZHA_LDS_KEYS;        // a head's keys staged in LDS by the workgroup that cuts it
+constexpr int kGList = ZHA_GLIST;             // a large frontier's crossing-bin keys listed per head
+constexpr uint32_t kNotLarge = 0xFFFFFFFFu;   // published for a head the select kernel cut itself
 constexpr int kSmallN = 1024;                 // groups with at most this many candidates select in one workgroup
 static_assert(kSmallN == kSelThreads && kBT == kSelThreads, "small path: one position per thread");
 constexpr int kSmallK = kSmallN / 64;
@@ -870,12 +872,21 @@ __device__ __forceinline__ void sweep_keys(const KF& key_at, int n, F&& f) {
 // table when there are at most kRankMax of them (the cut is then found by ranking
 // them), and, the first time there are at most kGather of them, to the list gl
 // [kGather] that later passes sweep instead of all n keys.
-template <class KF>
-__device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint64_t* hist, uint2* gl,
-                          CutShared* st, uint32_t& ustar, uint32_t& plim) {
+// Entry i of a key set is the candidate at position pos_at(i) (the identity for a
+// head's whole frontier).  need0 > 0: the cut must supply exactly that mass (keys
+// gathered from one crossing bin); 0: ceil(p * total).  Returns false, leaving
+// the cut unset, only when more than kRankMax keys equal the cut key and
+// `ties_in_order` is false (their entries are then not in position order).
+struct IdPos {
+    __device__ uint32_t operator()(int i) const { return (uint32_t)i; }
+};
+template <class KF, class PF>
+__device__ bool block_cut(const KF& key_at, const PF& pos_at, int n, float top_p, uint64_t need0, bool pre0,
+                          bool ties_in_order, uint64_t* hist, uint2* gl, CutShared* st, uint32_t& ustar,
+                          uint32_t& plim) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t pref = 0;
-    uint64_t need = 0;
+    uint64_t need = need0;
     ustar = 0;
     plim = 0xFFFFFFFFu;
     if (n <= kRankMax) {
@@ -883,19 +894,22 @@ __device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint6
         // mass 0, which never reaches the cut
         if (tid < kRankMax) {
             const uint32_t k = tid < n ? key_at(tid) : kNotCand;
+            const uint32_t pos = tid < n ? pos_at(tid) : 0xFFFFFFFFu;
             const uint64_t ms = k < kNoMass ? mass_of(k) : 0ull;
-            st->ent[tid] = make_uint4(k, (uint32_t)tid, (uint32_t)ms, (uint32_t)(ms >> 32));
+            st->ent[tid] = make_uint4(k, pos, (uint32_t)ms, (uint32_t)(ms >> 32));
             st->rank[tid] = 0ull;
         }
         __syncthreads();
-        // the total over the entries (one per lane), formed by every wave
-        const uint4 e0 = st->ent[lane];
-        const uint64_t total = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)e0.w << 32) | e0.z), 63);
-        need = (uint64_t)ceil((double)top_p * (double)total);
-        if (need < 1) need = 1;
-        if (need > total) need = total;
+        if (need == 0) {
+            // the total over the entries (one per lane), formed by every wave
+            const uint4 e0 = st->ent[lane];
+            const uint64_t total = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)e0.w << 32) | e0.z), 63);
+            need = (uint64_t)ceil((double)top_p * (double)total);
+            if (need < 1) need = 1;
+            if (need > total) need = total;
+        }
         rank_entries(st, n, need, ustar, plim);
-        return;
+        return true;
     }
     if (!pre0) {
         hist[2 * tid] = 0ull;
@@ -970,9 +984,13 @@ __device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint6
                 int pp[kSweepB];
 #pragma unroll
                 for (int j = 0; j < kSweepB; ++j) {
-                    pp[j] = base + j * kBT;
+                    const int i = base + j * kBT;
                     kk[j] = kNotCand;
-                    if (pp[j] < n) kk[j] = key_at(pp[j]);
+                    pp[j] = 0;
+                    if (i < n) {
+                        kk[j] = key_at(i);
+                        pp[j] = (int)pos_at(i);
+                    }
                 }
                 append(kk, pp, kSweepB);
             }
@@ -984,9 +1002,10 @@ __device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint6
         if (to_list) nl = (int)ne;
         if (to_rank) {
             rank_entries(st, (int)ne, need, ustar, plim);
-            return;
+            return true;
         }
         if (pass == 2) {
+            if (!ties_in_order) return false;
             // more than kRankMax keys equal to the cut key: the first t of them in
             // position order
             ustar = pref;
@@ -1015,9 +1034,10 @@ __device__ void block_cut(const KF& key_at, int n, float top_p, bool pre0, uint6
                 if (run >= (uint32_t)t) break;   // uniform
             }
             plim = st->plim;
-            return;
+            return true;
         }
     }
+    return true;                               // (not reached: the third pass always returns)
 }
 
 __device__ __forceinline__ bool kept_by(uint32_t key, uint32_t p, bool none, bool keep_all, uint32_t ustar,
@@ -1130,7 +1150,7 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
         const bool none = M == zha_neg_inf();
         const bool keep_all = !none && top_p >= 1.0f;
         uint32_t ustar = 0, plim = 0xFFFFFFFFu;
-        if (!none && !keep_all) block_cut(LdsKeys{s_keys}, n, top_p, false, s_hist, s_gl, &st, ustar, plim);
+        if (!none && !keep_all) block_cut(LdsKeys{s_keys}, IdPos{}, n, top_p, 0, false, true, s_hist, s_gl, &st, ustar, plim);
         // kept flags and their ranks in position order (rows of 1024 positions);
         // keys and node ids read back from LDS (not held across the cut)
         bool kept[kChainPer];
@@ -1241,8 +1261,8 @@ __global__ __launch_bounds__(kBT) void zha_merge_ids_kernel(ZhaLevelArgs a, int 
 // candidate and kept counts.  The histograms and counters were cleared by this
 // level's score kernel.
 //
-// zha_apply_kernel, grid (chunks, H_kv), 1024 threads: each workgroup takes the
-// next kApplyChunk candidate positions of its group (a ticket, so chunks run in
+// zha_apply_kernel, grid (chunks, H_kv), 256 or 1024 threads: each workgroup takes
+// the next kApplyChunk candidate positions of its group (a ticket, so chunks run in
 // order of start), forms every position's mask of the heads that keep it from the
 // heads' scores and cuts, and writes the kept positions' entries of the group's
 // kept list at ranks found by a decoupled look-back: each chunk publishes its kept
@@ -1250,9 +1270,10 @@ __global__ __launch_bounds__(kBT) void zha_merge_ids_kernel(ZhaLevelArgs a, int 
 // published inclusive prefix) to find where its entries start.  A chunk waits only
 // on chunks that started before it, so the waits always end.  Published values are
 // device-scope atomics read with device-scope loads.
-constexpr int kApplyThreads = 256;
-constexpr int kApplyWaves = kApplyThreads / 64;
-constexpr int kApplyChunk = 4 * kApplyThreads;    // positions per apply workgroup (four per thread)
+// Apply workgroups take four positions per thread: 256 threads at levels of at most
+// kApplyWideCap slots, else 1024 (fewer chunks, fewer tickets drawn on one word).
+constexpr int kApplyWideCap = 131072;
+__host__ __device__ constexpr int apply_threads(int64_t cap) { return cap > kApplyWideCap ? 1024 : 256; }
 constexpr uint32_t kDescAgg = 1u << 30;           // descriptor: the chunk's kept count is published
 constexpr uint32_t kDescInc = 2u << 30;           // descriptor: its inclusive prefix is published
 constexpr uint32_t kDescVal = kDescAgg - 1u;
@@ -1345,7 +1366,23 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
     // ---- the head's last workgroup: the complete histogram (read past this
     // device's caches) and the head's keys (LDS, 16-byte loads), then the cut
     const bool staged = n <= kLdsKeys;
+    const bool large = !staged && cut && a.glist != nullptr;
     uint32_t my_cand = 0;
+    if (large) {
+        // a frontier beyond the LDS keys: publish the first digit's crossing bin and
+        // the mass still needed inside it; the cross and resolve kernels finish
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            s_hist[2 * tid + i] = __hip_atomic_load(gm + 2 * tid + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        block_find(s_hist, 0, top_p, &st);
+        if (tid == 0) {
+            const uint64_t need = st.need - st.before;
+            a.pub[h] = make_uint4((uint32_t)st.bin, (uint32_t)need, (uint32_t)(need >> 32), __float_as_uint(M));
+            a.gcnt[h] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        return;
+    }
     {
         uint64_t hm2[2] = {0ull, 0ull};
         if (cut) {
@@ -1387,8 +1424,8 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
     __syncthreads();
     uint32_t ustar = 0, plim = 0xFFFFFFFFu;
     if (cut) {
-        if (staged) block_cut(LdsKeys{s_keys}, n, top_p, true, s_hist, s_gl, &st, ustar, plim);
-        else block_cut(GlobKeys{sg, M}, n, top_p, true, s_hist, s_gl, &st, ustar, plim);
+        if (staged) block_cut(LdsKeys{s_keys}, IdPos{}, n, top_p, 0, true, true, s_hist, s_gl, &st, ustar, plim);
+        else block_cut(GlobKeys{sg, M}, IdPos{}, n, top_p, 0, true, true, s_hist, s_gl, &st, ustar, plim);
     }
     // the head's kept count
     uint32_t my_kept = 0;
@@ -1410,10 +1447,229 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
         hc.plim = plim;
         hc.mode = none ? 2u : keep_all ? 1u : 0u;
         reinterpret_cast<HeadCut*>(a.hcut)[h] = hc;
+        if (a.glist) a.pub[h] = make_uint4(kNotLarge, 0u, 0u, 0u);   // the cross and resolve kernels skip it
     }
 }
 
+// ---- frontiers beyond the LDS keys (n > kLdsKeys candidates per head, at a
+// level whose capacity allows it): the select kernel's last workgroup of a head
+// published the first digit's crossing bin b0 and the mass still needed in it.
+//
+// zha_cross_kernel, grid (workgroups per head, H_q), 256 threads: workgroup w
+// takes slices w, w + gridDim.x, ... of kCrossSlice positions (four per thread,
+// 16-byte loads), counts the head's candidates and its keys below b0 (all of
+// them kept), and lists b0's keys {key, position} in LDS; then it reserves
+// room in the head's global list with one atomic and copies them there.  A
+// list that would pass ZHA_GLIST entries (or a workgroup's LDS) sets the
+// overflow word, and the resolve kernel falls back to every key.
+constexpr int kCrossThreads = 256;
+constexpr int kCrossWaves = kCrossThreads / 64;
+constexpr int kCrossSlice = 4 * kCrossThreads;
+static_assert(kCrossSlice == 1024, "zha_cross_blocks counts slices of 1024 positions");
+constexpr int kCrossLocal = 4096;                 // listed keys a workgroup holds
+constexpr int kCrossMaxW = ZHA_CROSS_MAXW;        // workgroups per head (each writes its counts to its own slot)
+
+__global__ __launch_bounds__(kCrossThreads) void zha_cross_kernel(ZhaLevelArgs a, int G, int c) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c));
+    __shared__ uint2 s_list[kCrossLocal];
+    __shared__ uint32_t s_n, s_base;
+    __shared__ uint32_t s_cnt[2][kCrossWaves];
+    const int h = blockIdx.y, g = h / G, hl = h - g * G, w = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint4 pub = a.pub[h];
+    const int pn = parent_count(a, g);
+    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (n <= kLdsKeys || pub.x == kNotLarge) return;   // (uniform) cut by the select kernel
+    const uint32_t b0 = pub.x;
+    const float M = __uint_as_float(pub.w);
+    const float4* sg4 = reinterpret_cast<const float4*>(a.sig + ((size_t)g * G + hl) * (size_t)a.sstride);
+    const int nv_cap = (int)(a.sstride / 4);
+    const int nsl = (n + kCrossSlice - 1) / kCrossSlice;
+    if (tid == 0) s_n = 0u;
+    __syncthreads();
+    uint32_t cand = 0, below = 0;
+#pragma unroll 1
+    for (int sl0 = w; sl0 < nsl; sl0 += 4 * (int)gridDim.x) {
+        // up to four slices' scores in flight together
+        float4 x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int v = (sl0 + r * (int)gridDim.x) * (kCrossSlice / 4) + tid;
+            x[r] = make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
+            if (sl0 + r * (int)gridDim.x < nsl && v < nv_cap) x[r] = sg4[v];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v4[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
+            const int p0 = (sl0 + r * (int)gridDim.x) * kCrossSlice + 4 * tid;
+            bool in[4];
+            uint64_t bal[4];
+            uint32_t tot = 0;
+            uint32_t k[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                k[j] = p0 + j < n ? key_of(v4[j], M) : kNotCand;
+                cand += k[j] != kNotCand;
+                below += (k[j] < kNoMass) & ((k[j] >> 21) < b0);
+                in[j] = (k[j] < kNoMass) & ((k[j] >> 21) == b0);
+                bal[j] = __ballot(in[j]);
+                tot += (uint32_t)__popcll(bal[j]);
+            }
+            if (tot) {                         // uniform over the wave
+                uint32_t e0 = 0;
+                if (lane == 0) e0 = atomicAdd(&s_n, tot);
+                e0 = (uint32_t)__shfl((int)e0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t e = e0 + bits_below_lane(bal[j]);
+                    if (in[j] && e < (uint32_t)kCrossLocal) s_list[e] = make_uint2(k[j], (uint32_t)(p0 + j));
+                    e0 += (uint32_t)__popcll(bal[j]);
+                }
+            }
+        }
+    }
+    // the workgroup's counts to its own slot (no atomics on one word from every
+    // workgroup), then its room in the head's list (one atomic, when it has keys)
+    const uint64_t both = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)below << 32) | cand), 63);
+    if (lane == 0) {
+        s_cnt[0][wave] = (uint32_t)both;
+        s_cnt[1][wave] = (uint32_t)(both >> 32);
+    }
+    __syncthreads();
+    const uint32_t nl = s_n;
+    if (tid == 0) {
+        uint32_t tc = 0, tb = 0;
+#pragma unroll
+        for (int i = 0; i < kCrossWaves; ++i) {
+            tc += s_cnt[0][i];
+            tb += s_cnt[1][i];
+        }
+        uint4* gc = a.gcnt + h;
+        const uint32_t base = nl ? atomicAdd(&gc->x, nl) : 0u;
+        if (nl > (uint32_t)kCrossLocal || base + nl > (uint32_t)kGList) atomicOr(&gc->w, 1u);
+        a.gpart[(size_t)h * kCrossMaxW + w] = make_uint2(tb, tc);
+        s_base = base;
+    }
+    __syncthreads();
+    const uint32_t base = s_base;
+    uint2* gl = a.glist + (size_t)h * kGList;
+    const uint32_t m = nl < (uint32_t)kCrossLocal ? nl : (uint32_t)kCrossLocal;
+    for (uint32_t i = tid; i < m; i += kCrossThreads)
+        if (base + i < (uint32_t)kGList) gl[base + i] = s_list[i];
+}
+
+// zha_resolve_kernel, grid (H_q), 1024 threads: a large frontier's cut from its
+// listed crossing-bin keys (LDS), kept = keys below the bin + listed keys kept;
+// after an overflow, or more than kRankMax keys equal to the cut key (the list is
+// not in position order), the cut is taken again over every key from the first
+// digit's complete histogram.  Writes the head's counts and cut descriptor.
+struct PairKey {
+    const uint2* e;
+    __device__ uint32_t operator()(int i) const { return e[i].x; }
+};
+struct PairPos {
+    const uint2* e;
+    __device__ uint32_t operator()(int i) const { return e[i].y; }
+};
+
+__global__ __launch_bounds__(kBT) void zha_resolve_kernel(ZhaLevelArgs a, int G, int c, float top_p) {
+    ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c), "s"(top_p));
+    __shared__ __align__(16) uint2 s_pairs[kGList];
+    __shared__ __align__(16) uint64_t s_hist[kHistBins];
+    __shared__ uint2 s_gl[kGather];
+    __shared__ uint32_t s_wred[kBW];
+    __shared__ CutShared st;
+    const int h = blockIdx.x, g = h / G, hl = h - g * G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint4 pub = a.pub[h];
+    const uint4 cnt = a.gcnt[h];
+    const int pn = parent_count(a, g);
+    const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
+    if (n <= kLdsKeys || pub.x == kNotLarge) return;   // (uniform)
+    const float M = __uint_as_float(pub.w);
+    const uint64_t need = ((uint64_t)pub.z << 32) | pub.y;
+    const float* sg = a.sig + ((size_t)g * G + hl) * (size_t)a.sstride;
+    // the cross kernel's per-workgroup counts: keys below the crossing bin, candidates
+    __shared__ uint32_t s_below, s_cand;
+    if (wave == 0) {
+        const int nw = zha_cross_blocks(a.cap);
+        uint2 v = make_uint2(0u, 0u);
+        for (int i = lane; i < nw; i += 64) {
+            const uint2 t2 = a.gpart[(size_t)h * kCrossMaxW + i];
+            v.x += t2.x;
+            v.y += t2.y;
+        }
+        const uint64_t s2 = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)v.x << 32) | v.y), 63);
+        if (lane == 0) {
+            s_below = (uint32_t)(s2 >> 32);
+            s_cand = (uint32_t)s2;
+        }
+    }
+    __syncthreads();
+    const uint32_t below = s_below, ncand = s_cand;
+    uint32_t ustar = 0, plim = 0xFFFFFFFFu, kept = 0;
+    bool ok = false;
+    if (cnt.w == 0u && cnt.x <= (uint32_t)kGList) {
+        const int ne = (int)cnt.x;
+        const uint2* gl = a.glist + (size_t)h * kGList;
+        constexpr int kPer = kGList / kBT;
+        uint2 t[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = tid + k * kBT;
+            t[k] = make_uint2(kNotCand, 0u);
+            if (i < ne) t[k] = gl[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) s_pairs[tid + k * kBT] = t[k];
+        __syncthreads();
+        ok = block_cut(PairKey{s_pairs}, PairPos{s_pairs}, ne, top_p, need, false, false, s_hist, s_gl, &st, ustar,
+                       plim);
+        if (ok) {
+            uint32_t mine = 0;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) mine += kept_by(t[k].x, t[k].y, false, false, ustar, plim);
+            mine = (uint32_t)zha_readlane_u64(zha_wave_incl_scan_u64(mine), 63);
+            if (lane == 0) s_wred[wave] = mine;
+            __syncthreads();
+#pragma unroll
+            for (int w2 = 0; w2 < kBW; ++w2) kept += s_wred[w2];
+            kept += below;
+        }
+    }
+    if (!ok) {
+        // every key again, from the first digit's complete histogram
+        const uint64_t* gm = a.ghist + (size_t)h * kHistBins;
+        s_hist[2 * tid] = gm[2 * tid];
+        s_hist[2 * tid + 1] = gm[2 * tid + 1];
+        __syncthreads();
+        block_cut(GlobKeys{sg, M}, IdPos{}, n, top_p, 0, true, true, s_hist, s_gl, &st, ustar, plim);
+        uint32_t mine = 0;
+        sweep_keys(GlobKeys{sg, M}, n, [&](uint32_t k, int p) { mine += kept_by(k, (uint32_t)p, false, false, ustar, plim); });
+        mine = (uint32_t)zha_readlane_u64(zha_wave_incl_scan_u64(mine), 63);
+        __syncthreads();
+        if (lane == 0) s_wred[wave] = mine;
+        __syncthreads();
+        kept = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kBW; ++w2) kept += s_wred[w2];
+    }
+    if (tid == 0) {
+        a.stats[2 * h + 0] = (int32_t)ncand;
+        a.stats[2 * h + 1] = (int32_t)kept;
+        HeadCut hc;
+        hc.m = M;
+        hc.ustar = ustar;
+        hc.plim = plim;
+        hc.mode = 0u;
+        reinterpret_cast<HeadCut*>(a.hcut)[h] = hc;
+    }
+}
+
+template <int kApplyThreads>
 __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a, int G, int c) {
+    constexpr int kApplyWaves = kApplyThreads / 64;
+    constexpr int kApplyChunk = 4 * kApplyThreads;    // positions per apply workgroup (four per thread)
     ZHA_LEVEL_ARGS_READY(a, "s"(G), "s"(c));
     __shared__ uint32_t s_wc[kApplyWaves];
     __shared__ uint32_t s_ticket, s_prefix;
@@ -1602,11 +1858,34 @@ hipError_t zha_launch_select(const ZhaLevelArgs& a, int H_kv, int G, int c, floa
     if (w < 1) w = 1;
     hipLaunchKernelGGL(zha_select_kernel, dim3((unsigned)w, (unsigned)(H_kv * G)), dim3(kBT), 0, stream, a, G, c,
                        top_p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)a.ndesc, (unsigned)H_kv);
-    hipLaunchKernelGGL(zha_apply_kernel, grid, dim3(kApplyThreads), 0, stream, a, G, c);
     return hipGetLastError();
 }
 
-int zha_apply_chunks(int64_t cap) { return (int)((cap + kApplyChunk - 1) / kApplyChunk); }
+hipError_t zha_launch_apply(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream) {
+    if (!a.hcut || !a.tick || !a.desc) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.ndesc, (unsigned)H_kv);
+    if (apply_threads(a.cap) == 1024)
+        hipLaunchKernelGGL(zha_apply_kernel<1024>, grid, dim3(1024), 0, stream, a, G, c);
+    else
+        hipLaunchKernelGGL(zha_apply_kernel<256>, grid, dim3(256), 0, stream, a, G, c);
+    return hipGetLastError();
+}
+
+hipError_t zha_launch_cross(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream) {
+    if (!a.pub || !a.gcnt || !a.glist || !a.gpart) return hipErrorInvalidValue;
+    const int w = zha_cross_blocks(a.cap);
+    hipLaunchKernelGGL(zha_cross_kernel, dim3((unsigned)w, (unsigned)(H_kv * G)), dim3(kCrossThreads), 0, stream, a,
+                       G, c);
+    return hipGetLastError();
+}
+
+hipError_t zha_launch_resolve(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream) {
+    if (!a.pub || !a.gcnt || !a.glist || !a.gpart || !a.hcut || !a.ghist) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(zha_resolve_kernel, dim3((unsigned)(H_kv * G)), dim3(kBT), 0, stream, a, G, c, top_p);
+    return hipGetLastError();
+}
+
+int zha_apply_chunks(int64_t cap) {
+    const int64_t chunk = 4 * apply_threads(cap);
+    return (int)((cap + chunk - 1) / chunk);
+}

@@ -218,6 +218,32 @@ int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_
                           const void* q, float* out, int32_t* sel, zha_stats* stats,
                           void* const* events, void* stream);
 
+/* zha_decode_step with a HIP event recorded on `stream` before the step's first
+ * kernel (events[0]) and after each kernel it launches (events[1], events[2],
+ * ...), up to max_events events in all; kinds[i] names the kernel that ends at
+ * events[i] as 100 * kind + level (kinds[0] = 100 * 0 + the first routed
+ * level).  *n_events receives how many events were recorded.  The step then
+ * writes no sel/stats.  The event packets between kernels take a little time of
+ * their own: for a per-kernel breakdown, not for the step's latency.  Returns
+ * ZHA_ERR_ARG when events, kinds or n_events is NULL, max_events < 1 or one of
+ * events[0 .. max_events) is NULL (hipEvent_t values created by the caller).
+ * Same definition as zha_decode_step. */
+enum {
+    ZHA_TRACE_SCORE_ALL = 1,   /* scores of every node of the chained levels */
+    ZHA_TRACE_CHAIN = 2,       /* per-head selection of the chained levels */
+    ZHA_TRACE_MERGE_IDS = 3,   /* level-1 group list when the chain reaches level 1 */
+    ZHA_TRACE_SCORE = 4,       /* a level's candidate scores */
+    ZHA_TRACE_SELECT = 5,      /* a level's per-head cut */
+    ZHA_TRACE_APPLY = 6,       /* a level's head masks and group kept list */
+    ZHA_TRACE_GATHER = 7,      /* sparse attention over the kept chunks, sink and tail */
+    ZHA_TRACE_COMBINE = 8,     /* merge of the gather's split partials */
+    ZHA_TRACE_CROSS = 9,       /* a large frontier's crossing-bin keys listed */
+    ZHA_TRACE_RESOLVE = 10     /* a large frontier's cut from that list */
+};
+int zha_decode_step_traced(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens,
+                           const void* q, float* out, void* const* events, int32_t max_events,
+                           int32_t* kinds, int32_t* n_events, void* stream);
+
 /* Dense baseline: exact softmax attention of every query head over all
  * n_tokens tokens (1 <= n_tokens <= capacity); scratch of
  * zha_dense_scratch_bytes(cfg) bytes (its split partials: the library

@@ -105,6 +105,8 @@ def test_entry_points_reject_bad_arguments_before_touching_the_device():
          B.ZHA_ERR_ARG),
         (lambda: B.zha_decode_step(B.make_config(**{**_base(), "capacity": 1000, "sink": 0}), bufs, 10, fake, fake,
                                    stream=0), B.ZHA_ERR_UNSUPPORTED),
+        (lambda: B.zha_decode_step_traced(cfg, bufs, 10, fake, fake, [], stream=0), B.ZHA_ERR_ARG),
+        (lambda: B.zha_decode_step_traced(cfg, bufs, 10, fake, fake, [fake, None], stream=0), B.ZHA_ERR_ARG),
         (lambda: B.dense_decode(cfg, fake, fake, 1001, fake, fake, fake, 0), B.ZHA_ERR_CAPACITY),
         (lambda: B.dense_decode(cfg, fake, fake, 10, fake, fake, None, 0), B.ZHA_ERR_ARG),
         (lambda: B.zha_tree_level_offsets(cfg, 0), B.ZHA_ERR_ARG),

@@ -68,3 +68,21 @@ def test_full_size_one_kv_group():
     derr = float(np.abs(out.cpu().numpy() - ref).max())
     say(f"[full] light one group: exempt heads {ex}/8, attention err {err:.2e}, dense err {derr:.2e}")
     assert derr <= ATOL
+
+
+def test_large_frontier_light_one_group():
+    """light's shape at 1,048,576 tokens (5 levels): level 1's frontier (about 48,000 of
+    131,072 nodes per head) exceeds the keys one workgroup stages, so its cut goes
+    through the listed crossing bin (cross and resolve kernels).  Group 0, all 8 heads."""
+    w = W.scaled(W.get("light"), 1 << 20, steps=2, levels=5)
+    say(f"[full] light@{w.n_tokens} L={w.levels}: large level-1 frontier, group 0")
+    layer, x, n = _prepare(w)
+    kh = to_host(layer.k[0:1])
+    vh = to_host(layer.v[0:1])
+    _, tree = oracle_tree(layer, n, keys_host=kh)
+    tree.qref = tree.qref[0:1]
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label="light@1M group 0",
+                                 heads=list(range(8)), groups=[0])
+    r1 = layer.route_level(1)                  # the step compare_decode just ran
+    assert int(r1["stats"][:8, 0].min()) > 32768, "the case must take the large-frontier path"
+    say(f"[full] light@1M: exempt heads {ex}/8, attention err {err:.2e}, score err {es:.2e}")

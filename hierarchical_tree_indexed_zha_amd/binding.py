@@ -25,7 +25,7 @@ EXPORTS = [
     "zha_check_config", "zha_tree_bytes", "zha_scratch_bytes", "zha_dense_scratch_bytes", "zha_sel_bytes",
     "zha_tree_level_offsets", "zha_route_level_offsets", "zha_build_tree", "zha_append_token",
     "zha_decode_step", "zha_decode_step_timed", "zha_decode_step_traced", "dense_decode", "zha_last_error",
-    "zha_decode_step_noalloc",
+    "zha_decode_step_noalloc", "zha_fidelity_work_bytes", "zha_route_fidelity",
 ]
 # kinds of a traced step's kernels (kinds[i] = 100 * kind + level)
 TRACE_KINDS = {0: "start", 1: "score_all", 2: "chain", 3: "merge_ids", 4: "score", 5: "select", 6: "apply",
@@ -52,6 +52,7 @@ class Config(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("capacity", ctypes.c_int64),
         ("sink", ctypes.c_int32),
+        ("plane_format", ctypes.c_int32),
     ]
 
 
@@ -115,7 +116,7 @@ def lib() -> ctypes.CDLL:
             "zha_dense_scratch_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_sel_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_tree_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int32, P(ctypes.c_int64), P(ctypes.c_int64),
-                                                      P(ctypes.c_int64), P(ctypes.c_int64)]),
+                                                      P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64)]),
             "zha_route_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int64, ctypes.c_int32, P(RouteOffsets)]),
             "zha_build_tree": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p]),
             "zha_append_token": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -128,6 +129,9 @@ def lib() -> ctypes.CDLL:
             "zha_decode_step_traced": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p,
                                                       ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_int32,
                                                       P(ctypes.c_int32), P(ctypes.c_int32), ctypes.c_void_p]),
+            "zha_fidelity_work_bytes": (ctypes.c_size_t, [cfgp, ctypes.c_int64]),
+            "zha_route_fidelity": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p]),
             "dense_decode": (ctypes.c_int, [cfgp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
             "zha_last_error": (ctypes.c_char_p, []),
@@ -167,16 +171,23 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity, sink=1) -> Config:
+PLANE_FORMATS = {"f32": 0, "bf16": 1}   # ZHA_PLANES_F32, ZHA_PLANES_BF16
+
+
+def make_config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity, sink=1,
+                plane_format=0) -> Config:
     if isinstance(kv_dtype, str):
         kv_dtype = ZHA_BF16 if kv_dtype == "bf16" else ZHA_F32
-    return Config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity, sink)
+    if isinstance(plane_format, str):
+        plane_format = PLANE_FORMATS[plane_format]
+    return Config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity, sink,
+                  plane_format)
 
 
-def config_of(w, capacity: int | None = None) -> Config:
-    """Config of a workloads.Workload."""
+def config_of(w, capacity: int | None = None, plane_format=0) -> Config:
+    """Config of a workloads.Workload (router planes float32 unless plane_format says otherwise)."""
     return make_config(w.n_kv_heads, w.n_q_heads, w.head_dim, w.chunk, w.levels, w.n_ref, w.top_p, w.kv_dtype,
-                       w.capacity if capacity is None else capacity)
+                       w.capacity if capacity is None else capacity, plane_format=plane_format)
 
 
 def zha_check_config(cfg: Config) -> None:
@@ -212,10 +223,10 @@ def zha_sel_bytes(cfg: Config) -> int:
 
 
 def zha_tree_level_offsets(cfg: Config, level: int) -> dict:
-    s, b, l, n = (ctypes.c_int64() for _ in range(4))
+    s, b, l, n, s16 = (ctypes.c_int64() for _ in range(5))
     _check(lib().zha_tree_level_offsets(ctypes.byref(cfg), level, ctypes.byref(s), ctypes.byref(b), ctypes.byref(l),
-                                        ctypes.byref(n)))
-    return {"s": s.value, "b": b.value, "lse": l.value, "n_cap": n.value}
+                                        ctypes.byref(n), ctypes.byref(s16)))
+    return {"s": s.value, "b": b.value, "lse": l.value, "n_cap": n.value, "s16": s16.value}
 
 
 def zha_route_level_offsets(cfg: Config, n_tokens: int, level: int) -> dict:
@@ -263,6 +274,18 @@ def zha_decode_step_traced(cfg: Config, bufs: Buffers, n_tokens: int, q, out, ev
     _check(lib().zha_decode_step_traced(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out), arr,
                                         n_ev, kinds, ctypes.byref(got), _stream(stream)))
     return [(TRACE_KINDS.get(kinds[i] // 100, "?"), kinds[i] % 100) for i in range(got.value)]
+
+
+def zha_fidelity_work_bytes(cfg: Config, n_tokens: int) -> int:
+    n = lib().zha_fidelity_work_bytes(ctypes.byref(cfg), n_tokens)
+    if n == 0:
+        raise ZhaError(ZHA_ERR_ARG, last_error())
+    return n
+
+
+def zha_route_fidelity(cfg: Config, bufs: Buffers, n_tokens: int, q, recall, work, stream=None) -> None:
+    _check(lib().zha_route_fidelity(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(recall),
+                                    _ptr(work), _stream(stream)))
 
 
 def dense_decode(cfg: Config, k, v, n_tokens: int, q, out, scratch, stream=None) -> None:

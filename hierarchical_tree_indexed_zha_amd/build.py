@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzha.so")
-SOURCES = ["zha_api.cpp", "zha_summary.hip", "zha_route.hip", "zha_attn.hip", "zha_report.hip"]
+SOURCES = ["zha_api.cpp", "zha_summary.hip", "zha_route.hip", "zha_attn.hip", "zha_report.hip", "zha_fidelity.hip"]
 ARCH = "gfx950"
 
 

@@ -68,6 +68,8 @@ int validate(const zha_config* cfg) {
         return fail(ZHA_ERR_UNSUPPORTED, "capacity must be < 2^31 (got %lld)", (long long)cfg->capacity);
     if (cfg->sink == 0) return fail(ZHA_ERR_UNSUPPORTED, "sink = 0 (no attention sink) is not implemented");
     if (cfg->sink != 1) return fail(ZHA_ERR_ARG, "sink must be 1 (got %d)", cfg->sink);
+    if (cfg->plane_format != ZHA_PLANES_F32 && cfg->plane_format != ZHA_PLANES_BF16)
+        return fail(ZHA_ERR_ARG, "plane_format must be ZHA_PLANES_F32 or ZHA_PLANES_BF16 (got %d)", cfg->plane_format);
     return ZHA_OK;
 }
 
@@ -87,7 +89,7 @@ struct Layout {
     int L = 0, G = 0, H = 0, R = 0;
     std::vector<int64_t> cap;             // node slots per level (index 1..L)
     // tree
-    std::vector<size_t> t_s, t_b, t_l;
+    std::vector<size_t> t_s, t_b, t_l, t_s16;   // t_s16: bfloat16 router copy of s (0: none)
     size_t tree_bytes = 0;
     // decode scratch
     std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, stats;
@@ -118,13 +120,16 @@ Layout make_layout(const zha_config* cfg) {
     const size_t H = y.H, G = y.G, R = y.R;
     y.cap.assign(y.L + 2, 0);
     for (int l = 1; l <= y.L; ++l) y.cap[l] = n_nodes(cfg, cfg->capacity, l);
-    y.t_s.assign(y.L + 1, 0); y.t_b.assign(y.L + 1, 0); y.t_l.assign(y.L + 1, 0);
+    y.t_s.assign(y.L + 1, 0); y.t_b.assign(y.L + 1, 0); y.t_l.assign(y.L + 1, 0); y.t_s16.assign(y.L + 1, 0);
     size_t off = 0;
     for (int l = 1; l <= y.L; ++l) {
         const size_t n = (size_t)y.cap[l];
         y.t_s[l] = off; off = align_up(off + sizeof(float) * H * n * R * ZHA_D);
         y.t_b[l] = off; off = align_up(off + sizeof(float) * H * n * R);
         y.t_l[l] = off; off = align_up(off + sizeof(float) * H * n * R);
+        if (cfg->plane_format == ZHA_PLANES_BF16) {
+            y.t_s16[l] = off; off = align_up(off + sizeof(uint16_t) * H * n * R * ZHA_D);
+        }
     }
     y.tree_bytes = off;
 
@@ -169,6 +174,15 @@ Layout make_layout(const zha_config* cfg) {
 }
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+// The router's bfloat16 copy of level l's planes s for nodes [first, first + n)
+// (nothing unless plane_format is ZHA_PLANES_BF16).
+int planes16(const zha_config* cfg, const Layout& y, void* T, int l, int64_t first, int64_t n, hipStream_t s) {
+    if (cfg->plane_format != ZHA_PLANES_BF16 || n <= 0) return ZHA_OK;
+    hipError_t e = zha_launch_planes16((const float*)at(T, y.t_s[l]), (uint16_t*)at(T, y.t_s16[l]), y.H, y.cap[l],
+                                       cfg->n_ref, first, n, s);
+    return e == hipSuccess ? ZHA_OK : hip_fail(e, "plane copy launch");
+}
 
 // Attention workgroups per KV group: about 8 tiles of 32 slots each, at most one
 // resident round of the whole device (768 workgroups: 256 CUs x 3 resident) so
@@ -243,7 +257,7 @@ size_t zha_sel_bytes(const zha_config* cfg) {
 }
 
 int zha_tree_level_offsets(const zha_config* cfg, int32_t level, int64_t* s_off, int64_t* b_off, int64_t* lse_off,
-                           int64_t* n_cap) {
+                           int64_t* n_cap, int64_t* s16_off) {
     int rc = validate(cfg);
     if (rc) return rc;
     if (level < 1 || level > cfg->levels) return fail(ZHA_ERR_ARG, "level %d outside 1..%d", level, cfg->levels);
@@ -252,6 +266,7 @@ int zha_tree_level_offsets(const zha_config* cfg, int32_t level, int64_t* s_off,
     if (b_off) *b_off = (int64_t)y.t_b[level];
     if (lse_off) *lse_off = (int64_t)y.t_l[level];
     if (n_cap) *n_cap = y.cap[level];
+    if (s16_off) *s16_off = cfg->plane_format == ZHA_PLANES_BF16 ? (int64_t)y.t_s16[level] : -1;
     return ok();
 }
 
@@ -296,6 +311,7 @@ int zha_build_tree(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tok
         cfg->kv_dtype, bufs->k, bufs->ref_q, (float*)at(T, y.t_s[1]), (float*)at(T, y.t_b[1]), (float*)at(T, y.t_l[1]),
         y.H, cfg->capacity, y.cap[1], c, R, 0, n_nodes(cfg, n_tokens, 1), tau_of(cfg), s);
     if (e != hipSuccess) return hip_fail(e, "leaf summary launch");
+    if ((rc = planes16(cfg, y, T, 1, 0, n_nodes(cfg, n_tokens, 1), s))) return rc;
     for (int l = 2; l <= y.L; ++l) {
         const int64_t n = n_nodes(cfg, n_tokens, l);
         if (n == 0) break;
@@ -303,6 +319,7 @@ int zha_build_tree(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tok
                              (float*)at(T, y.t_s[l]), (float*)at(T, y.t_b[l]), (float*)at(T, y.t_l[l]), y.H,
                              y.cap[l - 1], y.cap[l], c, R, 0, n, s);
         if (e != hipSuccess) return hip_fail(e, "merge launch");
+        if ((rc = planes16(cfg, y, T, l, 0, n, s))) return rc;
     }
     return ok();
 }
@@ -329,6 +346,7 @@ int zha_append_token(const zha_config* cfg, const zha_buffers* bufs, int64_t n_b
                                 (float*)at(T, y.t_l[1]), y.H, cfg->capacity, y.cap[1], c, R, n / c - 1, 1,
                                 tau_of(cfg), s);
     if (e != hipSuccess) return hip_fail(e, "leaf summary launch");
+    if ((rc = planes16(cfg, y, T, 1, n / c - 1, 1, s))) return rc;
     for (int l = 2; l <= y.L; ++l) {
         const int64_t span = span_of(cfg, l);
         if (span > cfg->capacity || n % span != 0) break;
@@ -336,6 +354,7 @@ int zha_append_token(const zha_config* cfg, const zha_buffers* bufs, int64_t n_b
                              (float*)at(T, y.t_s[l]), (float*)at(T, y.t_b[l]), (float*)at(T, y.t_l[l]), y.H,
                              y.cap[l - 1], y.cap[l], c, R, n / span - 1, 1, s);
         if (e != hipSuccess) return hip_fail(e, "merge launch");
+        if ((rc = planes16(cfg, y, T, l, n / span - 1, 1, s))) return rc;
     }
     return ok();
 }
@@ -389,6 +408,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     auto level_args = [&](int l) {
         ZhaLevelArgs a{};
         a.S = (const float*)(T + y.t_s[l]);
+        a.S16 = cfg->plane_format == ZHA_PLANES_BF16 ? (const uint16_t*)(T + y.t_s16[l]) : nullptr;
         a.B = (const float*)(T + y.t_b[l]);
         a.cap = y.cap[l];
         a.top = l == top ? 1 : 0;
@@ -559,7 +579,9 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         r.klist1 = at_.klist;
         r.cap1 = at_.cap1;
         r.n_tokens = n_tokens;
-        r.plane_bytes = (int64_t)R * (ZHA_D + 1) * 4;
+        // one node's summary bytes the router reads: planes s (float32 or their
+        // bfloat16 copy) and offsets b (float32)
+        r.plane_bytes = (int64_t)R * (ZHA_D * (cfg->plane_format == ZHA_PLANES_BF16 ? 2 : 4) + 4);
         r.kv_row_bytes = 2 * ZHA_D * (cfg->kv_dtype == ZHA_BF16 ? 2 : 4);
         r.H = y.H;
         r.G = y.G;
@@ -600,6 +622,47 @@ int zha_decode_step_traced(const zha_config* cfg, const zha_buffers* bufs, int64
     const int rc = decode_impl(cfg, bufs, n_tokens, q, out, nullptr, nullptr, nullptr, stream, &tr);
     *n_events = tr.n;
     return rc;
+}
+
+size_t zha_fidelity_work_bytes(const zha_config* cfg, int64_t n_tokens) {
+    if (validate(cfg) || n_tokens < 1) return 0;
+    return zha_fid_work_bytes(cfg->n_q_heads, n_tokens);
+}
+
+int zha_route_fidelity(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q, float* recall,
+                       void* work, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!bufs || !bufs->k || !bufs->scratch || !q || !recall || !work)
+        return fail(ZHA_ERR_ARG, "buffers k and scratch and q, recall, work must be non-NULL");
+    if (n_tokens < 1) return fail(ZHA_ERR_ARG, "n_tokens must be >= 1 (got %lld)", (long long)n_tokens);
+    if (n_tokens > cfg->capacity)
+        return fail(ZHA_ERR_CAPACITY, "n_tokens %lld exceeds capacity %lld", (long long)n_tokens,
+                    (long long)cfg->capacity);
+    Layout y = make_layout(cfg);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* X = static_cast<char*>(bufs->scratch);
+    const int top = top_level(cfg, n_tokens);
+    const int below = top - chain_levels(cfg, n_tokens, top);
+    // levels below the chain: their per-head bitmaps from the group kept lists
+    for (int l = below; l >= 1; --l) {
+        hipError_t e = zha_launch_fid_bitmap((const int32_t*)(X + y.klist[l]), (const uint32_t*)(X + y.kmask[l]),
+                                             (const int32_t*)(X + y.nkept[l]), y.cap[l], (uint64_t*)(X + y.kbm[l]),
+                                             y.wcap[l], y.H, y.G, s);
+        if (e != hipSuccess) return hip_fail(e, "fidelity bitmap launch");
+    }
+    ZhaFidLevels lv{};
+    lv.n = y.L;
+    for (int l = 1; l <= y.L; ++l) {
+        lv.kbm[l - 1] = (const uint64_t*)(X + y.kbm[l]);
+        lv.wcap[l - 1] = y.wcap[l];
+        lv.span[l - 1] = span_of(cfg, l);
+        lv.n_nodes[l - 1] = n_nodes(cfg, n_tokens, l);
+    }
+    hipError_t e = zha_launch_fidelity(cfg->kv_dtype, bufs->k, q, cfg->capacity, n_tokens, y.H, y.G, tau_of(cfg), lv,
+                                       work, recall, s);
+    if (e != hipSuccess) return hip_fail(e, "fidelity launch");
+    return ok();
 }
 
 int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_tokens, const void* q, float* out,

@@ -14,6 +14,10 @@ hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qre
 hipError_t zha_launch_merge(const float* Sc, const float* Bc, const float* Lc, float* Sp, float* Bp, float* Lp,
                             int H_kv, int64_t cap_c, int64_t cap_p, int c, int R, int64_t first_parent,
                             int64_t n_parents, hipStream_t stream);
+// the router's bfloat16 copy (round-to-nearest-even) of planes s of nodes
+// [first, first + n) of one level, every KV head
+hipError_t zha_launch_planes16(const float* S, uint16_t* S16, int H_kv, int64_t cap, int R, int64_t first, int64_t n,
+                               hipStream_t stream);
 hipError_t zha_launch_kv_write(int kv_dtype, void* K, void* V, const void* kn, const void* vn, int H_kv,
                                int64_t cap_tok, int64_t row, hipStream_t stream);
 
@@ -51,6 +55,7 @@ __device__ __forceinline__ uint32_t zha_div(uint32_t n, const ZhaDiv& v) {
 
 struct ZhaLevelArgs {
     const float* S;            // level planes [H_kv][cap][R][128]
+    const uint16_t* S16;       // their bfloat16 copy, read instead when non-null
     const float* B;            // [H_kv][cap][R]
     int64_t cap;               // node slots per head at this level
     int top;                   // 1 at the first routed level (positions are node ids)
@@ -170,6 +175,22 @@ hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, 
                                 hipEvent_t stop = nullptr);
 hipError_t zha_launch_combine(const ZhaAttnArgs& a, int H_kv, int G, int Bg, float* out, hipStream_t stream);
 
+// ---- router fidelity (zha_fidelity.hip)
+#define ZHA_FID_MAXL 32
+struct ZhaFidLevels {                  // level l at index l - 1
+    const uint64_t* kbm[ZHA_FID_MAXL]; // per-head kept bitmaps over node ids [H_kv][G][wcap]
+    int64_t wcap[ZHA_FID_MAXL];
+    int64_t span[ZHA_FID_MAXL];        // tokens per node, c^l
+    int64_t n_nodes[ZHA_FID_MAXL];     // complete nodes (tokens past them count as kept)
+    int n;                             // levels
+};
+size_t zha_fid_work_bytes(int H_q, int64_t n_tokens);
+hipError_t zha_launch_fid_bitmap(const int32_t* klist, const uint32_t* kmask, const int32_t* nkept, int64_t cap,
+                                 uint64_t* kbm, int64_t wcap, int H_kv, int G, hipStream_t stream);
+hipError_t zha_launch_fidelity(int kv_dtype, const void* K, const void* q, int64_t cap_tok, int64_t n_tokens,
+                               int H_kv, int G, float tau, const ZhaFidLevels& lv, void* work, float* recall,
+                               hipStream_t stream);
+
 // ---- optional outputs of a decode step (zha_report.hip)
 struct zha_stats;
 struct ZhaReportArgs {
@@ -184,7 +205,7 @@ struct ZhaReportArgs {
     const int32_t* klist1;       // level-1 kept list [H_kv][cap1]
     int64_t cap1;                // 0 when no level was routed
     int64_t n_tokens;
-    int64_t plane_bytes;         // R (d + 1) 4: summary bytes of one node
+    int64_t plane_bytes;         // R (d e + 4), e = 4 or 2 (bfloat16 planes): summary bytes of one node
     int64_t kv_row_bytes;        // 2 d e_kv: K and V bytes of one token
     int H, G, c, levels, top;
 };

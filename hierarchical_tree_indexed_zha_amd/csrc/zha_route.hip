@@ -145,7 +145,7 @@ __device__ __forceinline__ void defer_entry(const DeferView& v, int G, uint32_t 
 // derived here from its bitmaps (dynamic LDS), and this workgroup writes its
 // share of it (all of it together with the other workgroups).
 // Candidate positions and node ids fit in 32 bits (capacity < 2^31).
-template <bool BF16, bool ALL, bool DEF = false>
+template <bool BF16, bool ALL, bool DEF = false, bool P16 = false>
 __device__ __forceinline__ void score_level(const void* __restrict__ q, const ZhaLevelArgs& a, int G, int c, int R,
                                             float tau, int g, int blk, int nblk, float (&hm)[4],
                                             const ZhaLevelArgs* pa = nullptr) {
@@ -300,7 +300,17 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
             const int r = R <= 16 ? (j % R) : (cb * 16 + j);
             const size_t prw = (lrow + (size_t)node) * R + r;
             float4 sv[8];
-            if (valid) {
+            if (valid && P16) {
+                // the router's bfloat16 copy: the same four elements per lane, widened exactly
+                const uint2* plane = reinterpret_cast<const uint2*>(a.S16 + prw * ZHA_D);
+                uint2 u[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) u[m] = plane[4 * m + kq];
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    sv[m] = make_float4(__uint_as_float(u[m].x << 16), __uint_as_float(u[m].x & 0xFFFF0000u),
+                                        __uint_as_float(u[m].y << 16), __uint_as_float(u[m].y & 0xFFFF0000u));
+            } else if (valid) {
                 const float4* plane = reinterpret_cast<const float4*>(a.S + prw * ZHA_D);
 #pragma unroll
                 for (int m = 0; m < 8; ++m) sv[m] = plane[4 * m + kq];
@@ -395,41 +405,41 @@ __device__ __forceinline__ void block_head_max(const ZhaLevelArgs& a, int g, int
 }
 
 // grid (blocks, H_kv), 256 threads: one level's candidate scores.
-template <bool BF16>
+template <bool BF16, bool P16>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const void* __restrict__ q,
                                                                         ZhaLevelArgs a, int G, int c, int R,
                                                                         float tau) {
     const int g = blockIdx.y;
     float hm[4];
-    score_level<BF16, false>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm);
+    score_level<BF16, false, false, P16>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm);
     if (a.hblk) block_head_max(a, g, G, hm);
 }
 
 // As zha_route_score_kernel, for a level whose parent level (pa) was selected but
 // not merged: the workgroups derive and write that level's kept list themselves
 // (dynamic LDS: zha_defer_lds_bytes).
-template <bool BF16>
+template <bool BF16, bool P16>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_defer_kernel(const void* __restrict__ q,
                                                                               ZhaLevelArgs a, ZhaLevelArgs pa,
                                                                               int G, int c, int R, float tau) {
     ZHA_LEVEL_ARGS_READY(pa, "s"(G));
     const int g = blockIdx.y;
     float hm[4];
-    score_level<BF16, false, true>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm, &pa);
+    score_level<BF16, false, true, P16>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm, &pa);
     if (a.hblk) block_head_max(a, g, G, hm);
 }
 
 // grid (max blocks, H_kv, levels), 256 threads: every node of each of the first
 // routed levels scored for every head of the group, positions = node ids (the
 // levels' selection then gathers its candidates' scores from these).
-template <bool BF16>
+template <bool BF16, bool P16>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_all_kernel(const void* __restrict__ q,
                                                                             ZhaChainArgs m, int G, int c, int R,
                                                                             float tau) {
     const int z = blockIdx.z;
     if ((int)blockIdx.x >= m.blocks[z]) return;
     float hm[4];
-    score_level<BF16, true>(q, m.lv[z], G, c, R, tau, blockIdx.y, blockIdx.x, m.blocks[z], hm);
+    score_level<BF16, true, false, P16>(q, m.lv[z], G, c, R, tau, blockIdx.y, blockIdx.x, m.blocks[z], hm);
 }
 
 // ---- selection helpers
@@ -1804,24 +1814,30 @@ size_t zha_defer_lds_bytes(int G, int64_t n) {
     return sizeof(uint64_t) * (size_t)(G + 1) * wc + sizeof(uint32_t) * wc;
 }
 
+// A launch of kernel template K<bf16 q, bf16 planes> picked by the cache and plane formats.
+#define ZHA_SCORE_LAUNCH(K, grid, lds, stream, p16, ...)                                                   \
+    do {                                                                                                     \
+        if (kv_dtype == 0 && p16)                                                                            \
+            hipLaunchKernelGGL((K<true, true>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);       \
+        else if (kv_dtype == 0)                                                                              \
+            hipLaunchKernelGGL((K<true, false>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);      \
+        else if (p16)                                                                                        \
+            hipLaunchKernelGGL((K<false, true>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);      \
+        else                                                                                                 \
+            hipLaunchKernelGGL((K<false, false>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);     \
+    } while (0)
+
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream, const ZhaLevelArgs* defer) {
     dim3 grid((unsigned)blocks, (unsigned)H_kv);
+    const bool p16 = a.S16 != nullptr;
     if (defer) {
         if (a.top || !defer->top || defer->n_top > ZHA_CHAIN_SLOTS) return hipErrorInvalidValue;
         const size_t lds = zha_defer_lds_bytes(G, defer->n_top);
-        if (kv_dtype == 0)
-            hipLaunchKernelGGL(zha_route_score_defer_kernel<true>, grid, dim3(kScoreThreads), lds, stream, q, a, *defer,
-                               G, c, R, tau);
-        else
-            hipLaunchKernelGGL(zha_route_score_defer_kernel<false>, grid, dim3(kScoreThreads), lds, stream, q, a,
-                               *defer, G, c, R, tau);
+        ZHA_SCORE_LAUNCH(zha_route_score_defer_kernel, grid, lds, stream, p16, q, a, *defer, G, c, R, tau);
         return hipGetLastError();
     }
-    if (kv_dtype == 0)
-        hipLaunchKernelGGL(zha_route_score_kernel<true>, grid, dim3(kScoreThreads), 0, stream, q, a, G, c, R, tau);
-    else
-        hipLaunchKernelGGL(zha_route_score_kernel<false>, grid, dim3(kScoreThreads), 0, stream, q, a, G, c, R, tau);
+    ZHA_SCORE_LAUNCH(zha_route_score_kernel, grid, 0, stream, p16, q, a, G, c, R, tau);
     return hipGetLastError();
 }
 
@@ -1830,11 +1846,8 @@ hipError_t zha_launch_score_all(int kv_dtype, const void* q, const ZhaChainArgs&
     int bmax = 1;
     for (int i = 0; i < m.n; ++i) bmax = std::max(bmax, m.blocks[i]);
     const dim3 grid((unsigned)bmax, (unsigned)H_kv, (unsigned)m.n);
-    if (kv_dtype == 0)
-        hipLaunchKernelGGL(zha_route_score_all_kernel<true>, grid, dim3(kScoreThreads), 0, stream, q, m, G, c, R, tau);
-    else
-        hipLaunchKernelGGL(zha_route_score_all_kernel<false>, grid, dim3(kScoreThreads), 0, stream, q, m, G, c, R,
-                           tau);
+    const bool p16 = m.lv[0].S16 != nullptr;
+    ZHA_SCORE_LAUNCH(zha_route_score_all_kernel, grid, 0, stream, p16, q, m, G, c, R, tau);
     return hipGetLastError();
 }
 

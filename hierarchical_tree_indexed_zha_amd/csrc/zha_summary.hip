@@ -250,6 +250,28 @@ __global__ __launch_bounds__(256) void zha_merge_kernel(
     }
 }
 
+// grid (blocks, H_kv), 256 threads: S16 <- bfloat16(S), round to nearest, ties to
+// even, over one KV head's contiguous planes of nodes [first, first + n), four
+// elements per thread step.  Planes are finite, so no NaN case arises.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__global__ __launch_bounds__(256) void zha_planes16_kernel(const float* __restrict__ S, uint16_t* __restrict__ S16,
+                                                          int64_t cap, int R, int64_t first, int64_t n) {
+    const int g = blockIdx.y;
+    const size_t row = (size_t)R * ZHA_D;               // elements per node
+    const size_t base = ((size_t)g * cap + (size_t)first) * row;
+    const size_t count4 = (size_t)n * row / 4;
+    const float4* src = reinterpret_cast<const float4*>(S + base);
+    uint2* dst = reinterpret_cast<uint2*>(S16 + base);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < count4; i += (size_t)gridDim.x * 256) {
+        const float4 v = src[i];
+        dst[i] = make_uint2(f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16),
+                            f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16));
+    }
+}
+
 // grid (H_kv), 128 threads: row `row` of K and V <- k_new, v_new.
 template <typename T>
 __global__ void zha_kv_write_kernel(T* __restrict__ K, T* __restrict__ V, const T* __restrict__ kn,
@@ -298,6 +320,17 @@ hipError_t zha_launch_merge(const float* Sc, const float* Bc, const float* Lc, f
     dim3 grid((unsigned)((n_parents + ppb - 1) / ppb), (unsigned)H_kv);
     hipLaunchKernelGGL(zha_merge_kernel, grid, dim3(256), zha_merge_lds_bytes(c, R), stream, Sc, Bc, Lc, Sp,
                        Bp, Lp, cap_c, cap_p, c, R, first_parent, n_parents);
+    return hipGetLastError();
+}
+
+hipError_t zha_launch_planes16(const float* S, uint16_t* S16, int H_kv, int64_t cap, int R, int64_t first, int64_t n,
+                               hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t count4 = n * R * ZHA_D / 4;
+    int64_t blocks = (count4 + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(zha_planes16_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(256), 0, stream, S, S16, cap,
+                       R, first, n);
     return hipGetLastError();
 }
 

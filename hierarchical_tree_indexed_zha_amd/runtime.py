@@ -124,6 +124,25 @@ class ZhaLayer:
                 self._view(self.tree, o["b"], torch.float32, (H, n, R)),
                 self._view(self.tree, o["lse"], torch.float32, (H, n, R)))
 
+    def tree_level16(self, level: int) -> torch.Tensor:
+        """The router's bfloat16 copy of level `level`'s planes s [H][n_cap][R][d] (plane_format bf16)."""
+        o = B.zha_tree_level_offsets(self.cfg, level)
+        if o["s16"] < 0:
+            raise ValueError("the tree keeps no bfloat16 planes (plane_format is float32)")
+        H, R, d, n = self.cfg.n_kv_heads, self.cfg.n_ref, self.cfg.head_dim, o["n_cap"]
+        return self._view(self.tree, o["s16"], torch.bfloat16, (H, n, R, d))
+
+    def fidelity(self, q: torch.Tensor) -> torch.Tensor:
+        """Router fidelity of the step the last decode(q) ran (same q, same n_tokens): float32
+        [H_q][L + 1], per level the exact attention mass of the tokens the head kept, and
+        last the mass of the attended token set."""
+        self._check_q_out(q, self.out)
+        recall = torch.empty((self.cfg.n_q_heads, self.cfg.levels + 1), dtype=torch.float32, device=self.k.device)
+        work = torch.empty(B.zha_fidelity_work_bytes(self.cfg, self.n_tokens), dtype=torch.uint8,
+                           device=self.k.device)
+        B.zha_route_fidelity(self.cfg, self.bufs, self.n_tokens, q, recall, work)
+        return recall
+
     def route_level(self, level: int) -> dict:
         """Routing the last decode step left for `level` (copied to host), in the layout of
         a level scored over its group candidates: n_cand [H], sigma [H][G][n_cap] by

@@ -80,7 +80,16 @@ typedef struct zha_config {
     int32_t sink;        /* 1: token 0 is always attended (the attention sink).  0 (no sink)
                           * is valid but not implemented (ZHA_ERR_UNSUPPORTED); other values
                           * are ZHA_ERR_ARG */
+    int32_t plane_format;/* format of the planes s the router reads: ZHA_PLANES_F32 (0, the
+                          * float32 planes themselves) or ZHA_PLANES_BF16 (1, a bfloat16 copy
+                          * of them, round-to-nearest-even, kept beside the float32 planes
+                          * that the tree's merges use; b stays float32).  Page "ZHA
+                          * 用树形稀疏注意力改造现有大模型", section 几百倍加速 (a narrow-format
+                          * router variant). */
 } zha_config;
+
+#define ZHA_PLANES_F32  0
+#define ZHA_PLANES_BF16 1
 
 typedef struct zha_buffers {
     void*        k;        /* device K [H_kv][capacity][d] */
@@ -95,7 +104,8 @@ int zha_check_config(const zha_config* cfg);
 
 /* Bytes of summary storage for a tree over `capacity` tokens (0 if cfg is invalid).
  * Per level l and KV head: float32 planes s[n][R][d], b[n][R] and log-sum-exp
- * lse[n][R] for n < capacity / c^l. */
+ * lse[n][R] for n < capacity / c^l, and with plane_format = ZHA_PLANES_BF16 a
+ * bfloat16 copy of s. */
 size_t zha_tree_bytes(const zha_config* cfg);
 
 /* Bytes of decode scratch (0 if cfg is invalid): candidate scores and kept
@@ -110,9 +120,13 @@ size_t zha_dense_scratch_bytes(const zha_config* cfg);
  *   s   float32 [H_kv][n_cap][R][d]
  *   b   float32 [H_kv][n_cap][R]
  *   lse float32 [H_kv][n_cap][R]
- * with n_cap = capacity / c^level.  Host-only; ZHA_OK or ZHA_ERR_ARG. */
+ *   s16 bfloat16 [H_kv][n_cap][R][d], the router's copy of s when plane_format is
+ *       ZHA_PLANES_BF16 (*s16_off = -1 otherwise)
+ * with n_cap = capacity / c^level.  Any output pointer may be NULL.  Host-only;
+ * ZHA_OK or ZHA_ERR_ARG. */
 int zha_tree_level_offsets(const zha_config* cfg, int32_t level,
-                           int64_t* s_off, int64_t* b_off, int64_t* lse_off, int64_t* n_cap);
+                           int64_t* s_off, int64_t* b_off, int64_t* lse_off, int64_t* n_cap,
+                           int64_t* s16_off);
 
 /* Where a decode step over n_tokens tokens leaves its routing of level `level`
  * inside `scratch` (byte offsets; host-only).  `chained` tells which layout holds:
@@ -177,12 +191,13 @@ typedef struct zha_stats {
     int64_t group_cand[ZHA_STATS_MAX_LEVELS];        /* union candidates, summed over KV groups */
     int64_t group_kept[ZHA_STATS_MAX_LEVELS];        /* nodes kept by some head of a group, summed over groups */
     int64_t bytes_read[ZHA_STATS_MAX_LEVELS];        /* summary bytes the level's routing needs:
-                                                        group_cand * n_ref * (head_dim + 1) * 4 */
+                                                        group_cand * n_ref * (head_dim * e + 4), e = 4
+                                                        (float32 planes) or 2 (ZHA_PLANES_BF16) */
     int64_t bytes_streamed[ZHA_STATS_MAX_LEVELS];    /* summary bytes the kernels streamed for the level:
                                                         equal to bytes_read, except at the small top levels
                                                         whose every complete node is scored ahead of their
                                                         selection (then n_nodes * n_kv_heads * n_ref *
-                                                        (head_dim + 1) * 4) */
+                                                        (head_dim * e + 4)) */
     int64_t gather_tokens;                           /* distinct tokens attended, summed over KV groups */
     int64_t gather_bytes;                            /* K and V bytes those tokens occupy */
 } zha_stats;
@@ -253,6 +268,22 @@ int zha_decode_step_traced(const zha_config* cfg, const zha_buffers* bufs, int64
  * every new token). */
 int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_tokens,
                  const void* q, float* out, void* scratch, void* stream);
+
+/* Router fidelity of the last decode step, a diagnostic beside the hot path: for
+ * query head h and level l (1..L), recall[h][l - 1] is the exact attention
+ * probability mass at q (softmax over all n_tokens tokens) of the tokens whose
+ * level-l node the head kept, tokens under no complete level-l node counting as
+ * kept; recall[h][L] is the mass of the token set the step attended (its kept
+ * level-1 chunks, token 0 and the raw tail).  recall: device float32
+ * [n_q_heads][levels + 1].  work: device, zha_fidelity_work_bytes(cfg, n_tokens)
+ * bytes.  Reads the routing a zha_decode_step with the same cfg, bufs, n_tokens
+ * and q left in scratch, and rewrites the per-head kept bitmaps of the levels it
+ * selected below its first small levels there.  Runs three passes over the
+ * cache.  Defined by: page "ZHA 用树形稀疏注意力改造现有大模型", section
+ * 256K 的质量结果 (how much of the true attention the router keeps). */
+size_t zha_fidelity_work_bytes(const zha_config* cfg, int64_t n_tokens);
+int zha_route_fidelity(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens,
+                       const void* q, float* recall, void* work, void* stream);
 
 /* zha_decode_step without caller scratch, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses

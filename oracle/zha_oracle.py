@@ -68,6 +68,7 @@ import numpy as np
 
 __all__ = [
     "widen",
+    "round_bf16",
     "n_complete",
     "summarize_nodes",
     "SummaryTree",
@@ -79,6 +80,7 @@ __all__ = [
     "decode_step",
     "dense_decode",
     "append_token",
+    "level_mass_recall",
     "HeadRoute",
     "LevelRoute",
 ]
@@ -93,6 +95,21 @@ def widen(a) -> np.ndarray:
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return a.astype(np.float64, copy=False)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to bfloat16 (8 significant bits, float32's exponent
+    range), to nearest with ties to even, and return them as float64.
+
+    The narrow-format router of [fe] speed (几百倍加速, a router reading its
+    summaries in a narrow format): the planes are computed in full precision and
+    rounded once.  Written from the definition: x = m 2**e with 1/2 <= |m| < 1,
+    the representable neighbours are multiples of 2**(e - 8), and np.round rounds
+    half to even.  Values here are normal and finite (no subnormal or overflow case).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
 
 
 def n_complete(n_tokens: int, chunk: int, level: int) -> int:
@@ -151,7 +168,11 @@ class SummaryTree:
     Reference queries are one set per KV head shared by all levels (R3).
     """
 
-    def __init__(self, keys, qref, n_tokens: int, chunk: int, levels: int, tau: float | None = None):
+    def __init__(self, keys, qref, n_tokens: int, chunk: int, levels: int, tau: float | None = None,
+                 plane_format: str = "f32"):
+        if plane_format not in ("f32", "bf16"):
+            raise ValueError(f"plane_format must be 'f32' or 'bf16' (got {plane_format!r})")
+        self.plane_format = plane_format     # what the router reads: exact planes, or s rounded to bf16
         self.keys = keys                     # [H_kv][>= n_tokens][d] (any float or bf16 bits)
         self.qref = widen(qref)              # [H_kv][R][d]
         self.n_tokens = int(n_tokens)
@@ -182,6 +203,12 @@ class SummaryTree:
         for i, n in enumerate(nodes.tolist()):
             s[i], b[i], lse[i] = cache[n]
         return s, b, lse
+
+    def router_planes(self, level: int, g: int, nodes):
+        """The planes the router scores with: (s, b), s rounded to bfloat16 when the
+        tree's plane_format is 'bf16' (b is kept in full precision)."""
+        s, b, _ = self.get(level, g, nodes)
+        return (round_bf16(s) if self.plane_format == "bf16" else s), b
 
     def full_level(self, level: int, g: int):
         """Planes of every complete node of one level (for whole-tree comparisons)."""
@@ -291,7 +318,7 @@ def route_head(q_h, tree: SummaryTree, g: int, p: float) -> HeadRoute:
         if len(cand) == 0:
             lv = LevelRoute(level, cand, np.zeros(0), np.zeros(0), cand, math.inf)
         else:
-            s, b, _ = tree.get(level, g, cand)
+            s, b = tree.router_planes(level, g, cand)
             sigma = plane_scores(q_h, s, b, tree.tau)
             kept, pi, margin = top_p_cut(sigma, cand, p)
             lv = LevelRoute(level, cand, sigma, pi, np.sort(kept), margin)
@@ -348,6 +375,36 @@ def decode_step(q, keys, values, tree: SummaryTree, p: float):
         out[h] = attend(q[h], keys[g], values[g], r.tokens, tree.tau)
         routes.append(r)
     return out, routes
+
+
+def level_mass_recall(q_h, keys_g, kept_by_level: dict, tokens, n_tokens: int, chunk: int, levels: int,
+                      tau: float):
+    """How much of the exact attention the routing of one query head kept.
+
+    p_t = softmax_t(tau q.k_t) over all n_tokens tokens (the dense attention the
+    method approximates; [fe] quality 256K 的质量结果 judges the router by it).
+    For level l (1..levels): recall_l = sum of p_t over the tokens whose level-l
+    node is in kept_by_level[l] (node ids), tokens under no complete level-l node
+    counting as kept (they are never dropped at that level; R8).  A level absent
+    from kept_by_level keeps every node.  captured = sum of p_t over `tokens`,
+    the attended set.  Returns (recall [levels], captured).
+    """
+    keys = widen(keys_g[:n_tokens])
+    z = tau * (keys @ widen(q_h))
+    z = z - z.max()
+    p = np.exp(z)
+    p = p / p.sum()
+    t = np.arange(n_tokens, dtype=np.int64)
+    recall = np.ones(levels)
+    for level in range(1, levels + 1):
+        if level not in kept_by_level:
+            continue
+        span = chunk ** level
+        node = t // span
+        keep = (node >= n_complete(n_tokens, chunk, level)) | np.isin(node, np.asarray(kept_by_level[level]))
+        recall[level - 1] = p[keep].sum()
+    captured = p[np.asarray(tokens, dtype=np.int64)].sum()
+    return recall, float(captured)
 
 
 def dense_decode(q, keys, values, n_tokens: int, tau: float | None = None):

@@ -1,0 +1,162 @@
+"""Router fidelity (exact attention mass kept per level, captured mass of the attended
+set) and the bfloat16 router planes, through the C ABI, against the fp64 oracle.
+
+Fidelity: the HIP kernels' recall per head and level against the oracle's on the
+GPU's own kept sets (float32 exponentials summed per workgroup, then in double:
+within 1e-4 absolute).  bfloat16 planes: the router copy is the round-to-nearest-even
+of the GPU's own float32 planes bit for bit; decodes match the oracle whose planes are
+rounded the same way from float64, with the tolerances that rounding flips allow."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hierarchical_tree_indexed_zha_amd import workloads as W
+from tests.gpu_util import compare_decode, make_layer, oracle_tree, say, to_host
+
+pytestmark = pytest.mark.gpu
+
+RECALL_ATOL = 1e-4
+
+
+def _w(name, n, levels=None, steps=4, **kw):
+    return W.scaled(W.get(name), n, steps=steps, levels=levels, **kw)
+
+
+def _kept_by_level(layer, n, h):
+    """The GPU's kept node ids of query head h at every routed level."""
+    cfg = layer.cfg
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    g, hl = divmod(h, G)
+    out = {}
+    for lv in range(1, cfg.levels + 1):
+        if n // cfg.chunk ** lv == 0:
+            continue
+        r = layer.route_level(lv)
+        nk = int(r["n_kept"][g])
+        nodes = r["kept"][g, :nk].numpy().astype(np.int64)
+        masks = r["mask"][g, :nk].numpy().astype(np.int64)
+        out[lv] = nodes[(masks >> hl) & 1 == 1]
+    return out
+
+
+FID_CASES = [
+    ("tiny", W.get("tiny")),
+    ("light@65536", _w("light", 65536)),
+    ("deep@16384", _w("deep", 16384, levels=6)),
+    ("ultra@65536", _w("ultra", 65536, levels=5)),
+    ("light@131075-L2", _w("light", 131075, levels=2)),
+]
+
+
+@pytest.mark.parametrize("name,w", FID_CASES, ids=[c[0] for c in FID_CASES])
+def test_recall_matches_oracle(name, w):
+    say(f"[fidelity] {name}")
+    layer, x = make_layer(w)
+    n = w.n_tokens
+    layer.build(n)
+    q = x["q"][0]
+    layer.decode(q)
+    rec = layer.fidelity(q).cpu().numpy().astype(np.float64)
+    kh = to_host(layer.k)
+    qh = to_host(q)
+    G = w.n_q_heads // w.n_kv_heads
+    worst = 0.0
+    for h in range(0, w.n_q_heads, max(1, w.n_q_heads // 8)):
+        kept = _kept_by_level(layer, n, h)
+        toks = O.final_token_set(np.asarray(kept.get(1, []), dtype=np.int64), n, w.chunk)
+        ro, co = O.level_mass_recall(qh[h], kh[h // G], kept, toks, n, w.chunk, w.levels, 1.0 / np.sqrt(w.head_dim))
+        err = max(float(np.abs(rec[h, :w.levels] - ro).max()), abs(rec[h, w.levels] - co))
+        worst = max(worst, err)
+        assert err <= RECALL_ATOL, f"{name} head {h}: recall {rec[h]} vs oracle {ro}, {co}"
+        assert np.all(np.diff(rec[h, :w.levels]) >= -RECALL_ATOL)
+    say(f"[fidelity] {name}: max recall error {worst:.2e}; head 0 recall {np.round(rec[0], 4).tolist()}")
+
+
+def test_recall_is_one_at_p_one():
+    w = _w("light", 32768)
+    layer, x = make_layer(w, top_p=1.0)
+    layer.build(w.n_tokens)
+    q = x["q"][1]
+    layer.decode(q)
+    rec = layer.fidelity(q).cpu().numpy()
+    assert np.all(np.abs(rec - 1.0) <= RECALL_ATOL), rec.min()
+
+
+PLANE_CASES = [
+    ("tiny", W.get("tiny")),                          # fp32 cache, R = 16
+    ("light@32768", _w("light", 32768)),
+    ("deep@16384", _w("deep", 16384, levels=6)),
+    ("wide@16384", _w("wide", 16384)),
+    ("ultra@65536", _w("ultra", 65536, levels=5)),
+]
+
+
+@pytest.mark.parametrize("name,w", PLANE_CASES, ids=[c[0] for c in PLANE_CASES])
+def test_bf16_planes_decode_matches_oracle(name, w):
+    say(f"[planes16] {name}")
+    layer, x = make_layer(w, plane_format="bf16")
+    n = w.n_tokens
+    layer.build(n)
+    torch.cuda.synchronize()
+    # the router copy is the round-to-nearest-even of the float32 planes, bit for bit
+    for lv in range(1, w.levels + 1):
+        nn = n // w.chunk ** lv
+        if nn == 0:
+            continue
+        s32 = layer.tree_level(lv)[0][:, :nn]
+        s16 = layer.tree_level16(lv)[:, :nn]
+        assert torch.equal(s16.view(torch.int16), s32.to(torch.bfloat16).view(torch.int16)), f"{name} level {lv}"
+    kh, tree = oracle_tree(layer, n)
+    vh = to_host(layer.v)
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label=f"{name} bf16 planes")
+    say(f"[planes16] {name}: exempt heads {ex}/{w.n_q_heads}, attention err {err:.2e}, score err {es:.2e}")
+
+
+def test_bf16_planes_follow_appends():
+    """Appends that complete leaves and parents refresh the router copy as well."""
+    w = _w("light", 4096 - 3, levels=3, steps=80)
+    layer, x = make_layer(w, plane_format="bf16")
+    layer.build(w.n_tokens)
+    for t in range(70):
+        layer.append(x["k_app"][t], x["v_app"][t])
+    torch.cuda.synchronize()
+    n = layer.n_tokens
+    for lv in range(1, w.levels + 1):
+        nn = n // w.chunk ** lv
+        s32 = layer.tree_level(lv)[0][:, :nn]
+        s16 = layer.tree_level16(lv)[:, :nn]
+        assert torch.equal(s16.view(torch.int16), s32.to(torch.bfloat16).view(torch.int16)), f"level {lv}"
+    kh, tree = oracle_tree(layer, n)
+    compare_decode(layer, x["q"][1], n, tree, kh, to_host(layer.v), w.top_p, label="bf16 planes after appends")
+
+
+def test_bf16_planes_drift_and_captured_mass():
+    """The narrow router against the float32 one on the same cache and queries: the
+    share of heads whose leaf sets differ, and the captured attention mass of each
+    (reported; averaged over heads and steps the bfloat16 router must capture within
+    0.02 of the float32 one: single heads can swing further, as a cluster near the
+    cut falls on the other side)."""
+    w = _w("light", 65536, steps=8)
+    out = {}
+    for fmt in ("f32", "bf16"):
+        layer, x = make_layer(w, plane_format=fmt)
+        layer.build(w.n_tokens)
+        leaves, caps = [], []
+        for t in range(4):
+            q = x["q"][t]
+            sel = layer.new_sel()
+            layer.decode(q, sel=sel)
+            caps.append(layer.fidelity(q)[:, -1].cpu().numpy())
+            leaves.append(layer.read_sel(sel))
+        out[fmt] = (leaves, np.stack(caps))
+        del layer
+    same = total = 0
+    for a, b in zip(out["f32"][0], out["bf16"][0]):
+        for ha, hb in zip(a, b):
+            total += 1
+            same += list(ha) == list(hb)
+    c32, c16 = out["f32"][1], out["bf16"][1]
+    say(f"[planes16] drift: leaf sets identical for {same}/{total} (step, head) pairs; captured mass "
+        f"f32 {c32.mean():.4f} bf16 {c16.mean():.4f}, max |diff| {np.abs(c32 - c16).max():.4f}")
+    assert abs(float(c32.mean()) - float(c16.mean())) <= 0.02

@@ -17,6 +17,41 @@ _orig_summarize = Z.summarize_nodes
 _orig_cut = Z.top_p_cut
 _orig_final = Z.final_token_set
 _orig_attend = Z.attend
+_orig_round = Z.round_bf16
+_orig_recall = Z.level_mass_recall
+
+
+def _recall_tail_dropped(q_h, keys_g, kept_by_level, tokens, n_tokens, chunk, levels, tau):
+    # tokens under no complete node counted as dropped
+    keys = O.widen(keys_g[:n_tokens])
+    z = tau * (keys @ O.widen(q_h))
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    t = np.arange(n_tokens)
+    rec = np.ones(levels)
+    for level, kept in kept_by_level.items():
+        rec[level - 1] = p[np.isin(t // chunk ** level, np.asarray(kept))].sum()
+    return rec, float(p[np.asarray(tokens)].sum())
+
+
+def _recall_unnormalised_by_level(q_h, keys_g, kept_by_level, tokens, n_tokens, chunk, levels, tau):
+    rec, cap = _orig_recall(q_h, keys_g, kept_by_level, tokens, n_tokens, chunk, levels, tau)
+    return rec[::-1].copy(), cap
+
+
+def _round_truncate(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
+
+
+def _round_via_float32(x):
+    return _orig_round(np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+def _round_half_away(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    y = np.ldexp(m, 8)
+    return np.ldexp(np.sign(y) * np.floor(np.abs(y) + 0.5), e - 8)
 
 
 def _summ_no_tau_in_b(keys_g, qref_g, chunk, level, nodes, tau):
@@ -104,6 +139,11 @@ def _pins():
     for ex, case in P._golden_cases():
         out.append((f"golden[{ex['name']},{case['p']}]", lambda ex=ex, case=case: P.test_golden_worked_examples(ex, case)))
     out.append(("ties", P.test_cut_ties_break_by_ascending_index_and_margin_flags_them))
+    out.append(("p13-library", P.test_p13_round_bf16_matches_library_rounding_of_float32_values))
+    out.append(("p13-hand", P.test_p13_round_bf16_hand_values))
+    out.append(("p13-scores", P.test_p13_bf16_router_scores_use_rounded_planes_only))
+    out.append(("p14-one", P.test_p14_recall_is_one_everywhere_at_p_one))
+    out.append(("p14-lse", P.test_p14_recall_equals_node_logsumexp_form_and_is_monotone))
     return out
 
 
@@ -117,6 +157,11 @@ MUTATIONS = {
     "no_tail": ("final_token_set", _final_no_tail),
     "wrong_attention_scale": ("attend", _attend_no_max_shift_wrong_scale),
     "no_orphans": ("route_head", _route_no_orphans),
+    "bf16_truncates": ("round_bf16", _round_truncate),
+    "bf16_double_rounding_via_float32": ("round_bf16", _round_via_float32),
+    "bf16_ties_away_from_zero": ("round_bf16", _round_half_away),
+    "recall_drops_the_tail": ("level_mass_recall", _recall_tail_dropped),
+    "recall_levels_reversed": ("level_mass_recall", _recall_unnormalised_by_level),
 }
 
 

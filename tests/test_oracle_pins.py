@@ -381,3 +381,97 @@ def test_bf16_bits_widen_exactly():
     x = torch.randn(1000).to(torch.bfloat16)
     bits = x.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(O.widen(bits), x.double().numpy())
+
+
+# ---------------------------------------------------------------- narrow router planes (P13)
+
+def test_p13_round_bf16_matches_library_rounding_of_float32_values():
+    """On float32-representable inputs one rounding to bfloat16 is the library's own
+    float32 -> bfloat16 conversion (round to nearest, ties to even)."""
+    x32 = (torch.randn(20000, dtype=torch.float64) * torch.exp(torch.randn(20000, dtype=torch.float64) * 4)).float()
+    ref = x32.to(torch.bfloat16).double().numpy()
+    assert np.array_equal(O.round_bf16(x32.double().numpy()), ref)
+
+
+def test_p13_round_bf16_hand_values():
+    """bfloat16 spacing is 2**-7 on [1, 2): exact ties go to the even neighbour, values
+    past a tie go up, signs are symmetric, and a float64 value just past a tie is not
+    first rounded to float32 (that double rounding would land on the tie and go down)."""
+    u = 2.0 ** -7
+    cases = [
+        (1.0 + u / 2, 1.0),                     # tie: 1 (even) vs 1 + u (odd)
+        (1.0 + 3 * u / 2, 1.0 + 2 * u),         # tie: 1 + u (odd) vs 1 + 2u (even)
+        (1.0 + u / 2 + 2.0 ** -30, 1.0 + u),    # just past the tie
+        (1.0 + u / 2 + 2.0 ** -40, 1.0 + u),    # past the tie by less than float32 resolves
+        (-(1.0 + 3 * u / 2), -(1.0 + 2 * u)),
+        (3.0 * 2.0 ** 20 + 2.0 ** 13, 3.0 * 2.0 ** 20),   # spacing 2**14 on [2**21, 2**22): tie to even
+        (0.0, 0.0),
+        (2.0 ** -100 * (1 + u / 4), 2.0 ** -100),
+    ]
+    got = O.round_bf16(np.array([c[0] for c in cases]))
+    assert got.tolist() == [c[1] for c in cases]
+
+
+def test_p13_bf16_router_scores_use_rounded_planes_only():
+    """A 'bf16' tree scores with s rounded to bfloat16 and b unchanged: the score equals
+    the plane formula on round_bf16(s), and differs from the exact score by at most
+    tau * sum_d |q_d| |s_d| 2**-8 (half a bfloat16 spacing per element)."""
+    keys, _ = _rand_cache(1, 256, 32, seed=11)
+    qref = RNG(12).normal(size=(1, 2, 32))
+    t32 = O.SummaryTree(keys, qref, 256, 4, 2)
+    t16 = O.SummaryTree(keys, qref, 256, 4, 2, plane_format="bf16")
+    q = RNG(13).normal(size=32)
+    nodes = np.arange(16)
+    s, b, _ = t32.get(2, 0, nodes)
+    s16, b16 = t16.router_planes(2, 0, nodes)
+    assert np.array_equal(b16, b) and np.array_equal(s16, O.round_bf16(s))
+    exact = O.plane_scores(q, s, b, t32.tau)
+    narrow = O.plane_scores(q, s16, b16, t16.tau)
+    bound = t32.tau * (np.abs(q)[None, None, :] * np.abs(s) * 2.0 ** -8).sum(-1).max(-1)
+    assert np.all(np.abs(narrow - exact) <= bound + 1e-12)
+    assert not np.array_equal(narrow, exact)
+    with pytest.raises(ValueError):
+        O.SummaryTree(keys, qref, 256, 4, 2, plane_format="fp8")
+
+
+# ---------------------------------------------------------------- router fidelity (P14)
+
+def _route_kept(r):
+    return {lv.level: lv.kept for lv in r.levels}
+
+
+def test_p14_recall_is_one_everywhere_at_p_one():
+    keys, _ = _rand_cache(1, 300, 16, seed=21)
+    tree = O.SummaryTree(keys, RNG(22).normal(size=(1, 2, 16)), 300, 4, 3)
+    q = RNG(23).normal(size=16) * 2
+    r = O.route_head(q, tree, 0, 1.0)
+    rec, cap = O.level_mass_recall(q, keys[0], _route_kept(r), r.tokens, 300, 4, 3, tree.tau)
+    assert np.allclose(rec, 1.0, atol=1e-12) and abs(cap - 1.0) < 1e-12
+
+
+def test_p14_recall_equals_node_logsumexp_form_and_is_monotone():
+    """recall_l = sum over kept nodes n of e^{LSE_n - LSE} (node log-sum-exp over its raw
+    keys, a separate formula) plus the mass of the tokens under no complete level-l
+    node; it never grows going down the levels; captured = recall_1 plus the sink's
+    mass when its chunk was dropped."""
+    n, c, L, d = 203, 3, 3, 8
+    keys, _ = _rand_cache(1, n, d, seed=31, scale=1.5)
+    tree = O.SummaryTree(keys, RNG(32).normal(size=(1, 1, d)), n, c, L)
+    for seed in range(6):
+        q = RNG(40 + seed).normal(size=d) * 3
+        r = O.route_head(q, tree, 0, 0.6)
+        kept = _route_kept(r)
+        rec, cap = O.level_mass_recall(q, keys[0], kept, r.tokens, n, c, L, tree.tau)
+        z = tree.tau * (keys[0] @ q)
+        lse_all = scipy.special.logsumexp(z)
+        for level in range(1, L + 1):
+            span = c ** level
+            nl = n // span
+            s = sum(math.exp(scipy.special.logsumexp(z[k * span:(k + 1) * span]) - lse_all) for k in kept[level])
+            if nl * span < n:
+                s += math.exp(scipy.special.logsumexp(z[nl * span:]) - lse_all)
+            assert abs(rec[level - 1] - s) < 1e-12
+        assert np.all(np.diff(rec) >= -1e-12)               # recall_1 <= recall_2 <= ... <= recall_L
+        p0 = math.exp(z[0] - lse_all)
+        sink_dropped = 0 not in set(kept[1].tolist())
+        assert abs(cap - (rec[0] + (p0 if sink_dropped else 0.0))) < 1e-12

@@ -432,11 +432,28 @@ def cold_gather(args, layer, x, w, torch, B):
             "gather_gbs": round(gb / K / (g_us * 1e-6) / 1e9, 1), "flush_bytes": args.flush_bytes}
 
 
-def point(torch, W, B, ZhaLayer, w, steps, dense_steps, append):
+def fidelity_of(layer, x, steps):
+    """Mean over `steps` decode steps and all query heads of the router's per-level
+    exact-mass recall and of the attended set's captured mass (zha_route_fidelity)."""
+    import numpy as np
+    nq = x["q"].shape[0]
+    recs = []
+    for t in range(steps):
+        q = x["q"][t % nq]
+        layer.decode(q)
+        recs.append(layer.fidelity(q).cpu().numpy())
+    r = np.stack(recs).mean(axis=(0, 1))
+    L = layer.cfg.levels
+    return {"recall_by_level": {f"L{l}": round(float(r[l - 1]), 5) for l in range(1, L + 1)},
+            "captured_mass": round(float(r[L]), 5), "steps": steps}
+
+
+def point(torch, W, B, ZhaLayer, w, steps, dense_steps, append, plane_format=0, fid_steps=0):
     """Decode latency of workload w at its own size against dense, with the route/gather
-    split (HIP events), keys read and summary bytes; appends before each step if asked."""
+    split (HIP events), keys read and summary bytes; appends before each step if asked;
+    with fid_steps, the router's fidelity over that many steps."""
     x = W.generate(w, device="cuda")
-    layer = ZhaLayer(B.config_of(w), x["k"], x["v"], x["ref_q"])
+    layer = ZhaLayer(B.config_of(w, plane_format=plane_format), x["k"], x["v"], x["ref_q"])
     n = w.n_tokens
     t0 = time.perf_counter()
     layer.build(n)
@@ -473,6 +490,10 @@ def point(torch, W, B, ZhaLayer, w, steps, dense_steps, append):
             "dense_gbs_alg": round(H * layer.n_tokens * 2 * w.head_dim * (2 if w.kv_dtype == "bf16" else 4)
                                    / (us_d * 1e-6) / 1e9, 1),
             "build_ms": round(build_ms, 2)}
+    if plane_format:
+        line["plane_format"] = "bf16"
+    if fid_steps:
+        line["fidelity"] = fidelity_of(layer, x, fid_steps)
     del layer, x
     torch.cuda.empty_cache()
     return line
@@ -498,11 +519,31 @@ def ultra_point(args, torch, W, B, ZhaLayer):
     """The ultra-long light workload (10,485,760 tokens, 7 levels): append + decode steps."""
     w = dataclasses.replace(W.get("ultra"), steps=max(W.get("ultra").steps, args.ultra_steps))
     _log(f"[ultra] N={w.n_tokens} L={w.levels} steps={args.ultra_steps}")
-    line = point(torch, W, B, ZhaLayer, w, args.ultra_steps, 8, True)
+    line = point(torch, W, B, ZhaLayer, w, args.ultra_steps, 8, True, fid_steps=2)
     line["workload"] = "ultra"
     line["append_per_step"] = True
     _log(json.dumps(line))
     return line
+
+
+def others(args, torch, W, B, ZhaLayer):
+    """deep at full size (route time, keys read, fidelity), and light and wide with
+    float32 and bfloat16 router planes (router time and bytes, fidelity)."""
+    out = {}
+    w = dataclasses.replace(W.get("deep"), steps=16, append=False)
+    _log("[deep] full size")
+    out["deep"] = point(torch, W, B, ZhaLayer, w, 16, 16, False, fid_steps=2)
+    planes = {}
+    for name in ("light", "wide"):
+        w = dataclasses.replace(W.get(name), steps=16, append=False)
+        planes[name] = {}
+        for fmt in (0, 1):
+            _log(f"[planes] {name} plane_format={fmt}")
+            line = point(torch, W, B, ZhaLayer, w, 16, 16, False, plane_format=fmt, fid_steps=2)
+            planes[name]["bf16" if fmt else "f32"] = {k: line[k] for k in (
+                "zha_decode_us", "route_us", "gather_us", "router_bytes", "keys_read_frac", "fidelity")}
+    out["planes16"] = planes
+    return out
 
 
 GEOMETRY = [  # (chunk, levels, n_ref, top_p) at 262,144 tokens, light heads and generator
@@ -567,13 +608,19 @@ def main():
     result["cold"] = cold
     _log(f"[bench] cold gather {cold['gather_us']:.1f} us ({cold['gather_gbs']:.0f} GB/s), "
          f"cold decode {cold['decode_us']:.1f} us; router kernels {rt_us:.1f} us")
+    result["fidelity"] = {"light": fidelity_of(layer, x, 4)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, layer, x, w, torch)
     del layer, x
     torch.cuda.empty_cache()
     if not args.no_sweep:
+        oth = others(args, torch, W, B, ZhaLayer)
+        result["deep"] = oth["deep"]
+        result["fidelity"]["deep"] = oth["deep"]["fidelity"]
+        result["planes16"] = oth["planes16"]
         result["sweep"] = sweep(args, torch, W, B, ZhaLayer)
         result["ultra"] = ultra_point(args, torch, W, B, ZhaLayer)
+        result["fidelity"]["ultra"] = result["ultra"]["fidelity"]
     line = json.dumps(result)
     print(line, flush=True)
     if args.out:

@@ -490,7 +490,10 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.hcut = (void*)(X + y.hcut[l]);
         a.tick = (uint32_t*)(X + y.tick[l]);
         a.desc = (uint32_t*)(X + y.desc[l]);
-        if (y.glist[l]) {
+        // the cross and resolve kernels, when this level may hold frontiers well past
+        // the keys one workgroup stages (else a head past them is cut by the select
+        // kernel over every key, which stays rare)
+        if (y.glist[l] && n_nodes(cfg, n_tokens, l) > ZHA_CROSS_MIN_NODES) {
             a.pub = (uint4*)(X + y.pub[l]);
             a.gcnt = (uint4*)(X + y.gcnt[l]);
             a.gpart = (uint2*)(X + y.gpart[l]);

@@ -103,6 +103,7 @@ struct ZhaLevelArgs {
 #define ZHA_LDS_KEYS 32768     // a head's keys staged in LDS by the workgroup that cuts it
 #define ZHA_GLIST 16384        // a large frontier's crossing-bin keys listed per head
 #define ZHA_CROSS_MAXW 32      // cross workgroups per head
+#define ZHA_CROSS_MIN_NODES (2 * ZHA_LDS_KEYS)   // levels of more complete nodes take the cross path
 // Cross workgroups per head for a level of `cap` node slots: 4 slices of 1024
 // positions each at least, at most ZHA_CROSS_MAXW.
 __host__ __device__ inline int zha_cross_blocks(int64_t cap) {

@@ -152,7 +152,8 @@ def bench_workload(args, torch, W, B, ZhaLayer):
     N = w.n_tokens
 
     t_build = timed(lambda: layer.build(N), torch)
-    _log(f"[bench] build {t_build * 1e3:.2f} ms")
+    bd = build_device(layer, N, w, torch)
+    _log(f"[bench] build {t_build * 1e3:.2f} ms (device {bd['us']:.1f} us, {bd['gbs']:.0f} GB/s alg)")
 
     # warm-up steps, then rewind: appends overwrite the same rows and nodes again
     run_steps(layer, x, w, N, args.warmup, w.append)
@@ -169,9 +170,12 @@ def bench_workload(args, torch, W, B, ZhaLayer):
     t_dec = timed(lambda: run_steps(layer, x, w, N, args.steps, False), torch)
     us_dec = t_dec / args.steps * 1e6
     us_app = None
+    app_dev = None
     if w.append:
         layer.n_tokens = N
         us_app = timed(lambda: run_steps(layer, x, w, N, args.steps, True, decode=False), torch) / args.steps * 1e6
+        layer.n_tokens = N
+        app_dev = append_device(layer, x, args.steps, torch)
     layer.n_tokens = N
 
     # dense baseline at the same context
@@ -267,6 +271,8 @@ def bench_workload(args, torch, W, B, ZhaLayer):
         "router_gbs_alg": round(router_gbs, 1),
         "dense_gbs_alg": round(dense_bytes / (us_dense * 1e-6) / 1e9, 1),
         "build_ms": round(t_build * 1e3, 3),
+        "build_device": bd,
+        "append_device": app_dev,
         "roofline": {"bound": "hbm", "kernel": "zha_attn_kernel<bf16, sparse> (gather)",
                      "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
@@ -275,6 +281,47 @@ def bench_workload(args, torch, W, B, ZhaLayer):
                      "traffic_over_alg": None if traffic is None else round(traffic / (gather_bytes / K), 4)},
     }
     return result, layer, x, w
+
+
+def build_device(layer, N, w, torch, reps=3):
+    """The tree build's device time (HIP events around zha_build_tree, best of reps) and its
+    algorithmic bytes: the keys read once, every level's planes (s, b, lse) written, and
+    the child planes each merge reads."""
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.build(N)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    us = min(ts)
+    H, d, R, c = w.n_kv_heads, w.head_dim, w.n_ref, w.chunk
+    e_kv = 2 if w.kv_dtype == "bf16" else 4
+    node = R * (d + 2) * 4
+    byts = H * N * d * e_kv
+    for lv in range(1, w.levels + 1):
+        n = N // c ** lv
+        byts += H * n * node                      # written
+        if lv > 1:
+            byts += H * n * c * node              # children read by the merge
+    return {"us": round(us, 2), "alg_bytes": int(byts), "gbs": round(byts / (us * 1e-6) / 1e9, 1)}
+
+
+def append_device(layer, x, steps, torch):
+    """Device time of each append (HIP events around zha_append_token: the KV row write and,
+    when a chunk completes, its leaf summary and the merges above it), mean and max."""
+    rows = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    nq = x["q"].shape[0]
+    N = layer.n_tokens
+    for t in range(steps):
+        rows[t][0].record()
+        layer.append(x["k_app"][t % nq], x["v_app"][t % nq])
+        rows[t][1].record()
+    torch.cuda.synchronize()
+    layer.n_tokens = N
+    us = [a.elapsed_time(b) * 1e3 for a, b in rows]
+    return {"mean_us": round(sum(us) / len(us), 3), "max_us": round(max(us), 3), "steps": steps}
 
 
 def cpu_baseline(args, layer, x, w, torch):
@@ -490,6 +537,9 @@ def point(torch, W, B, ZhaLayer, w, steps, dense_steps, append, plane_format=0, 
             "dense_gbs_alg": round(H * layer.n_tokens * 2 * w.head_dim * (2 if w.kv_dtype == "bf16" else 4)
                                    / (us_d * 1e-6) / 1e9, 1),
             "build_ms": round(build_ms, 2)}
+    line["build_device"] = build_device(layer, n, w, torch, reps=2)
+    if append:
+        layer.n_tokens = n
     if plane_format:
         line["plane_format"] = "bf16"
     if fid_steps:

@@ -197,6 +197,231 @@ __global__ __launch_bounds__(256) void zha_leaf_summary_kernel(
     }
 }
 
+// ---- leaf summaries on the matrix cores (R <= 16, c a power of two).
+//
+// One wave takes a unit of 16 consecutive tokens (16 / c leaves for c <= 16) or one
+// whole leaf (c >= 32, its c / 16 tiles of 16 tokens in turn, the next tile's keys
+// requested before the current one is computed; a leaf dealt to the four waves of a
+// workgroup and combined measured slower).  Per tile:
+//   Z = tau Q K^T      16 refs x 16 tokens, 32 v_mfma_f32_16x16x4_f32 (refs past R zero);
+//                      lane (j, q4) brings K[t0 + j][32 q4 .. 32 q4 + 31] (the
+//                      contraction index d = 32 q4 + m of step m), Q likewise;
+//   softmax per (r, leaf) over the tile's lanes j (segmented shuffles), or online
+//                      across the tiles of one leaf (running max, sum, sum of w z);
+//   S += W K           per 16-column slice, the tile's tokens in groups of four:
+//                      W from LDS as the A operand (row r, token 4 kk + q4), K from
+//                      LDS as the B operand (token 4 kk + q4, column 16 s + j).
+// Outputs as the scalar kernel's: S[leaf][r][d], B, LSE (rows r < R).
+constexpr int kLmMinR = 4;         // fewer reference queries leave most MFMA rows empty:
+                                   // the scalar kernel is faster there (measured at R = 1)
+constexpr int kLmStride = 144;     // LDS row of a staged key tile (floats): the B reads of
+                                   // a half-wave (rows q4 and q4 + 1) fall 16 banks apart
+
+__device__ __forceinline__ float seg_max(float x, int c) {
+    for (int o = 1; o < c && o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float seg_sum(float x, int c) {
+    for (int o = 1; o < c && o < 16; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
+    const void* __restrict__ Kv, const float* __restrict__ Qref,
+    float* __restrict__ S, float* __restrict__ B, float* __restrict__ LSE,
+    int64_t cap_tok, int64_t cap1, int c, int R, int64_t first_leaf, int64_t n_leaves, float tau) {
+    __shared__ __align__(16) float s_k[4][16 * kLmStride];
+    __shared__ float s_w[4][16 * 17];
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, q4 = lane >> 4;
+    float* sk = s_k[wave];
+    float* sw = s_w[wave];
+
+    // the reference queries as the A operand of Z: row j (zero past R), d = 32 q4 + m
+    float qa[32];
+    {
+        const float* qr = Qref + ((size_t)g * R + (j < R ? j : 0)) * ZHA_D + 32 * q4;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const float4 x = reinterpret_cast<const float4*>(qr)[v];
+            qa[4 * v + 0] = j < R ? x.x : 0.f;
+            qa[4 * v + 1] = j < R ? x.y : 0.f;
+            qa[4 * v + 2] = j < R ? x.z : 0.f;
+            qa[4 * v + 3] = j < R ? x.w : 0.f;
+        }
+    }
+    const bool big = c > 16;                            // a leaf spans several tiles
+    const int lpu = big ? 1 : 16 / c;                   // leaves per unit
+    const int tpu = big ? c / 16 : 1;                   // tiles per unit
+    const int64_t n_units = (n_leaves + lpu - 1) / lpu;
+    const size_t head_row0 = (size_t)g * cap_tok;
+
+    for (int64_t u = (int64_t)blockIdx.x * 4 + wave; u < n_units; u += (int64_t)gridDim.x * 4) {
+        const int64_t leaf0 = first_leaf + u * lpu;
+        const int nl = (int)min((int64_t)lpu, first_leaf + n_leaves - leaf0);
+        const int ntok = big ? 16 : nl * c;              // valid tokens of each tile
+        float m_run[4], l_run[4], ez_run[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { m_run[i] = zha_neg_inf(); l_run[i] = 0.f; ez_run[i] = 0.f; }
+        zha_f32x4 acc[8];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) acc[sl] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // K row j of a tile, columns 32 q4 .. 32 q4 + 31, as raw 16-byte vectors: the
+        // next tile's are requested before the current one is computed
+        uint4 raw[BF16 ? 4 : 8];
+        auto fetch = [&](int tt) {
+#pragma unroll
+            for (int v = 0; v < (BF16 ? 4 : 8); ++v) raw[v] = make_uint4(0u, 0u, 0u, 0u);
+            if (tt < tpu && j < ntok) {
+                const size_t row = head_row0 + (size_t)(leaf0 * c + 16 * tt + j);
+                const uint4* src = BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Kv) + row * ZHA_D + 32 * q4)
+                                        : reinterpret_cast<const uint4*>(static_cast<const float*>(Kv) + row * ZHA_D + 32 * q4);
+#pragma unroll
+                for (int v = 0; v < (BF16 ? 4 : 8); ++v) raw[v] = src[v];
+            }
+        };
+        fetch(0);
+        for (int tt = 0; tt < tpu; ++tt) {
+            // widened exactly (bf16 bits, or float32), then staged in LDS
+            float kb[32];
+            if (BF16) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t w4[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kb[8 * v + 2 * e] = __uint_as_float(w4[e] << 16);
+                        kb[8 * v + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    kb[4 * v] = __uint_as_float(raw[v].x);
+                    kb[4 * v + 1] = __uint_as_float(raw[v].y);
+                    kb[4 * v + 2] = __uint_as_float(raw[v].z);
+                    kb[4 * v + 3] = __uint_as_float(raw[v].w);
+                }
+            }
+            fetch(tt + 1);
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                *reinterpret_cast<float4*>(sk + j * kLmStride + 32 * q4 + 4 * v) =
+                    make_float4(kb[4 * v], kb[4 * v + 1], kb[4 * v + 2], kb[4 * v + 3]);
+            // Z: lane holds refs 4 q4 + i against token j
+            zha_f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 32; ++m) z4 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[m], kb[m], z4, 0, 0, 0);
+            const bool tv = j < ntok;
+            float w[4];
+            if (c <= 16) {
+                // one leaf per c lanes: its log-sum-exp, weights and offset
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float z = tv ? tau * z4[i] : zha_neg_inf();
+                    const float mx = seg_max(z, c);
+                    const float e = (tv && mx != zha_neg_inf()) ? expf(z - mx) : 0.f;
+                    const float sum = seg_sum(e, c);
+                    const float lse = mx + logf(sum);
+                    const float wi = tv ? e / sum : 0.f;
+                    const float wz = seg_sum(tv ? wi * z : 0.f, c);
+                    w[i] = wi;
+                    const int r = 4 * q4 + i;
+                    if (tv && (j & (c - 1)) == 0 && r < R) {
+                        const size_t o = ((size_t)g * cap1 + (size_t)(leaf0 + j / c)) * R + r;
+                        LSE[o] = lse;
+                        B[o] = lse - wz;
+                    }
+                }
+            } else {
+                // online across the leaf's tiles
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float z = tau * z4[i];
+                    float mt = z;
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+                    const float mn = fmaxf(m_run[i], mt);
+                    const float alpha = expf(m_run[i] - mn);   // 0 on the first tile
+                    const float e = expf(z - mn);
+                    float es = e, ezs = e * z;
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) {
+                        es += __shfl_xor(es, o);
+                        ezs += __shfl_xor(ezs, o);
+                    }
+                    l_run[i] = l_run[i] * alpha + es;
+                    ez_run[i] = ez_run[i] * alpha + ezs;
+                    m_run[i] = mn;
+#pragma unroll
+                    for (int sl = 0; sl < 8; ++sl) acc[sl][i] *= alpha;
+                    w[i] = e;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sw[(4 * q4 + i) * 17 + j] = w[i];
+            zha_wave_lds_sync();
+            // S: the tile's tokens in groups of four (kk), each slice of 16 columns
+            if (c > 16) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const float a = sw[j * 17 + 4 * kk + q4];
+#pragma unroll
+                    for (int sl = 0; sl < 8; ++sl)
+                        acc[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sk[(4 * kk + q4) * kLmStride + 16 * sl + j],
+                                                                       acc[sl], 0, 0, 0);
+                }
+            } else {
+                for (int f = 0; f < nl; ++f) {
+                    zha_f32x4 o[8];
+#pragma unroll
+                    for (int sl = 0; sl < 8; ++sl) o[sl] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
+                    const int kk0 = (f * c) >> 2, kk1 = ((f + 1) * c - 1) >> 2;
+                    for (int kk = kk0; kk <= kk1; ++kk) {
+                        const int tok = 4 * kk + q4;
+                        const float a = (tok >= f * c && tok < (f + 1) * c) ? sw[j * 17 + tok] : 0.f;
+#pragma unroll
+                        for (int sl = 0; sl < 8; ++sl)
+                            o[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sk[tok * kLmStride + 16 * sl + j], o[sl],
+                                                                         0, 0, 0);
+                    }
+                    float* so = S + ((size_t)g * cap1 + (size_t)(leaf0 + f)) * R * ZHA_D;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * q4 + i;
+                        if (r < R)
+#pragma unroll
+                            for (int sl = 0; sl < 8; ++sl) so[r * ZHA_D + 16 * sl + j] = o[sl][i];
+                    }
+                }
+            }
+            zha_wave_lds_sync();                        // the next tile overwrites sk, sw
+        }
+        if (big) {
+            float* so = S + ((size_t)g * cap1 + (size_t)leaf0) * R * ZHA_D;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q4 + i;
+                if (r < R) {
+                    const float inv = 1.f / l_run[i];
+#pragma unroll
+                    for (int sl = 0; sl < 8; ++sl) so[r * ZHA_D + 16 * sl + j] = acc[sl][i] * inv;
+                    if (j == 0) {
+                        const size_t o = ((size_t)g * cap1 + (size_t)leaf0) * R + r;
+                        const float lse = m_run[i] + logf(l_run[i]);
+                        LSE[o] = lse;
+                        B[o] = lse - ez_run[i] * inv;
+                    }
+                }
+            }
+        }
+
+    }
+}
+
 // grid (ceil(n_parents / parents_per_block), H_kv), 256 threads.
 __global__ __launch_bounds__(256) void zha_merge_kernel(
     const float* __restrict__ Sc, const float* __restrict__ Bc, const float* __restrict__ Lc,
@@ -293,6 +518,21 @@ hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qre
                                    float* LSE, int H_kv, int64_t cap_tok, int64_t cap1, int c, int R,
                                    int64_t first_leaf, int64_t n_leaves, float tau, hipStream_t stream) {
     if (n_leaves <= 0) return hipSuccess;
+    if (R >= kLmMinR && R <= 16 && (c & (c - 1)) == 0) {
+        // matrix-core kernel: units of 16 tokens (c <= 16) or whole leaves, four per workgroup
+        const int64_t lpu = c <= 16 ? 16 / c : 1;
+        const int64_t units = (n_leaves + lpu - 1) / lpu;
+        int64_t blocks = (units + 3) / 4;
+        if (blocks > 2048) blocks = 2048;
+        dim3 grid((unsigned)blocks, (unsigned)H_kv);
+        if (kv_dtype == 0)
+            hipLaunchKernelGGL(zha_leaf_mfma_kernel<true>, grid, dim3(256), 0, stream, K, Qref, S, B, LSE, cap_tok,
+                               cap1, c, R, first_leaf, n_leaves, tau);
+        else
+            hipLaunchKernelGGL(zha_leaf_mfma_kernel<false>, grid, dim3(256), 0, stream, K, Qref, S, B, LSE, cap_tok,
+                               cap1, c, R, first_leaf, n_leaves, tau);
+        return hipGetLastError();
+    }
     const int64_t lpb = c <= kTile ? kTile / c : 1;
     dim3 grid((unsigned)((n_leaves + lpb - 1) / lpb), (unsigned)H_kv);
     size_t lds = zha_leaf_summary_lds_bytes(R);

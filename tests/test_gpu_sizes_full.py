@@ -36,17 +36,40 @@ def test_full_size_decode(name):
         f"attention err {err:.2e}, score err {es:.2e}")
 
 
-def test_full_size_ultra_one_group():
-    w = W.get("ultra")
-    say(f"[full] ultra: N={w.n_tokens} c={w.chunk} L={w.levels}, group 0")
-    layer, x, n = _prepare(w)
+def _ultra_group0(layer, x, n, label):
     kh = to_host(layer.k[0:1])
     vh = to_host(layer.v[0:1])
     _, tree = oracle_tree(layer, n, keys_host=kh)
     tree.qref = tree.qref[0:1]
-    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label="ultra full",
-                                 heads=[0, 5], groups=[0])
-    say(f"[full] ultra: exempt heads {ex}/2, attention err {err:.2e}, score err {es:.2e}")
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, W.get("ultra").top_p, label=label,
+                                 heads=list(range(8)), groups=[0])
+    say(f"[full] {label}: exempt heads {ex}/8, attention err {err:.2e}, score err {es:.2e}")
+
+
+def test_full_size_ultra_one_group():
+    """ultra (10,485,760 tokens, 7 levels) after one appended token: all 8 query heads
+    of KV group 0 against the oracle."""
+    w = W.get("ultra")
+    say(f"[full] ultra: N={w.n_tokens} c={w.chunk} L={w.levels}, group 0")
+    layer, x, n = _prepare(w)
+    _ultra_group0(layer, x, n, "ultra full")
+
+
+def test_full_size_ultra_appends_through_a_level_two_node():
+    """ultra after 64 appended tokens: the 64th completes 8 new leaves and the first new
+    level-2 node (10,485,760 is a multiple of 64), whose planes the appends built by
+    merges; then one decode step, group 0, all 8 heads, against the oracle summarising
+    the same cache from its raw keys."""
+    w = W.get("ultra")
+    say(f"[full] ultra + 64 appends: N={w.n_tokens} -> {w.n_tokens + 64}")
+    layer, x = make_layer(w)
+    layer.build(w.n_tokens)
+    for t in range(64):
+        layer.append(x["k_app"][t], x["v_app"][t])
+    torch.cuda.synchronize()
+    n = layer.n_tokens
+    assert n == w.n_tokens + 64 and n % (w.chunk ** 2) == 0
+    _ultra_group0(layer, x, n, "ultra + 64 appends")
 
 
 def test_full_size_one_kv_group():

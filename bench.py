@@ -593,6 +593,39 @@ def others(args, torch, W, B, ZhaLayer):
             planes[name]["bf16" if fmt else "f32"] = {k: line[k] for k in (
                 "zha_decode_us", "route_us", "gather_us", "router_bytes", "keys_read_frac", "fidelity")}
     out["planes16"] = planes
+    out["batch"] = batch_points(torch, W, B, ZhaLayer)
+    return out
+
+
+def batch_points(torch, W, B, ZhaLayer, sizes=(1, 2, 4, 8, 16)):
+    """light at full size: batches of Q queries routed together (zha_decode_batch),
+    device time per batch and per query, against Q single steps."""
+    w = dataclasses.replace(W.get("light"), steps=max(sizes), append=False)
+    x = W.generate(w, device="cuda")
+    layer = ZhaLayer(B.config_of(w), x["k"], x["v"], x["ref_q"])
+    layer.build(w.n_tokens)
+    out = []
+    for nq in sizes:
+        q = x["q"][:nq].contiguous()
+        for _ in range(3):
+            layer.decode_batch(q)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(10):
+            layer.decode_batch(q)
+        e[1].record()
+        for _ in range(10):
+            for i in range(nq):
+                layer.decode(q[i])
+        e[2].record()
+        torch.cuda.synchronize()
+        tb = e[0].elapsed_time(e[1]) / 10 * 1e3
+        ts = e[1].elapsed_time(e[2]) / 10 * 1e3
+        out.append({"queries": nq, "batch_us": round(tb, 2), "us_per_query": round(tb / nq, 2),
+                    "single_steps_us": round(ts, 2), "speedup_vs_single": round(ts / tb, 3)})
+        _log(f"[batch] {out[-1]}")
+    del layer, x
+    torch.cuda.empty_cache()
     return out
 
 
@@ -668,6 +701,7 @@ def main():
         result["deep"] = oth["deep"]
         result["fidelity"]["deep"] = oth["deep"]["fidelity"]
         result["planes16"] = oth["planes16"]
+        result["batch"] = oth["batch"]
         result["sweep"] = sweep(args, torch, W, B, ZhaLayer)
         result["ultra"] = ultra_point(args, torch, W, B, ZhaLayer)
         result["fidelity"]["ultra"] = result["ultra"]["fidelity"]

@@ -25,7 +25,8 @@ EXPORTS = [
     "zha_check_config", "zha_tree_bytes", "zha_scratch_bytes", "zha_dense_scratch_bytes", "zha_sel_bytes",
     "zha_tree_level_offsets", "zha_route_level_offsets", "zha_build_tree", "zha_append_token",
     "zha_decode_step", "zha_decode_step_timed", "zha_decode_step_traced", "dense_decode", "zha_last_error",
-    "zha_decode_step_noalloc", "zha_fidelity_work_bytes", "zha_route_fidelity",
+    "zha_decode_step_noalloc", "zha_fidelity_work_bytes", "zha_route_fidelity", "zha_batch_scratch_bytes",
+    "zha_decode_batch",
 ]
 # kinds of a traced step's kernels (kinds[i] = 100 * kind + level)
 TRACE_KINDS = {0: "start", 1: "score_all", 2: "chain", 3: "merge_ids", 4: "score", 5: "select", 6: "apply",
@@ -130,6 +131,9 @@ def lib() -> ctypes.CDLL:
                                                       ctypes.c_void_p, P(ctypes.c_void_p), ctypes.c_int32,
                                                       P(ctypes.c_int32), P(ctypes.c_int32), ctypes.c_void_p]),
             "zha_fidelity_work_bytes": (ctypes.c_size_t, [cfgp, ctypes.c_int64]),
+            "zha_batch_scratch_bytes": (ctypes.c_size_t, [cfgp, ctypes.c_int32]),
+            "zha_decode_batch": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
             "zha_route_fidelity": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_void_p]),
             "dense_decode": (ctypes.c_int, [cfgp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -274,6 +278,19 @@ def zha_decode_step_traced(cfg: Config, bufs: Buffers, n_tokens: int, q, out, ev
     _check(lib().zha_decode_step_traced(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, _ptr(q), _ptr(out), arr,
                                         n_ev, kinds, ctypes.byref(got), _stream(stream)))
     return [(TRACE_KINDS.get(kinds[i] // 100, "?"), kinds[i] % 100) for i in range(got.value)]
+
+
+def zha_batch_scratch_bytes(cfg: Config, n_queries: int) -> int:
+    n = lib().zha_batch_scratch_bytes(ctypes.byref(cfg), n_queries)
+    if n == 0:
+        raise ZhaError(ZHA_ERR_ARG, last_error())
+    return n
+
+
+def zha_decode_batch(cfg: Config, bufs: Buffers, n_tokens: int, n_queries: int, q, out, sel=None,
+                     stream=None) -> None:
+    _check(lib().zha_decode_batch(ctypes.byref(cfg), ctypes.byref(bufs), n_tokens, n_queries, _ptr(q), _ptr(out),
+                                  _ptr(sel), _stream(stream)))
 
 
 def zha_fidelity_work_bytes(cfg: Config, n_tokens: int) -> int:

@@ -380,19 +380,35 @@ struct Trace {
     }
 };
 
+// A batch of n_queries decode queries routes as n_queries x H_kv virtual KV groups:
+// virtual group v = query * H_kv + g has its own frontiers, kept lists and
+// partials in scratch (laid out for n_queries x H_kv groups), while the tree
+// planes and the cache rows it reads are those of group g = v % H_kv.
+zha_config virtual_config(const zha_config* cfg, int n_queries) {
+    zha_config v = *cfg;
+    v.n_kv_heads = cfg->n_kv_heads * n_queries;
+    v.n_q_heads = cfg->n_q_heads * n_queries;
+    return v;
+}
+
 int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q, float* out,
-                int32_t* sel, zha_stats* stats, void* const* events, void* stream, Trace* tr = nullptr) {
+                int32_t* sel, zha_stats* stats, void* const* events, void* stream, Trace* tr = nullptr,
+                int n_queries = 1) {
     Trace untraced;
     Trace& TR = tr ? *tr : untraced;
     int rc = validate(cfg);
     if (rc) return rc;
+    if (n_queries < 1) return fail(ZHA_ERR_ARG, "n_queries must be >= 1 (got %d)", n_queries);
     if (!bufs || !bufs->k || !bufs->v || !bufs->tree || !bufs->scratch || !q || !out)
         return fail(ZHA_ERR_ARG, "buffers k, v, tree, scratch and q, out must be non-NULL");
     if (n_tokens < 1) return fail(ZHA_ERR_ARG, "n_tokens must be >= 1 (got %lld)", (long long)n_tokens);
     if (n_tokens > cfg->capacity)
         return fail(ZHA_ERR_CAPACITY, "n_tokens %lld exceeds capacity %lld", (long long)n_tokens,
                     (long long)cfg->capacity);
-    Layout y = make_layout(cfg);
+    const zha_config vcfg = virtual_config(cfg, n_queries);
+    Layout y = make_layout(&vcfg);             // scratch: every virtual group
+    Layout yt = make_layout(cfg);              // tree: the real groups
+    const int hkv = cfg->n_kv_heads;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int c = cfg->chunk, R = cfg->n_ref;
     const float tau = tau_of(cfg);
@@ -407,9 +423,10 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     // may issue its parent reads before it knows whether the level is the first).
     auto level_args = [&](int l) {
         ZhaLevelArgs a{};
-        a.S = (const float*)(T + y.t_s[l]);
-        a.S16 = cfg->plane_format == ZHA_PLANES_BF16 ? (const uint16_t*)(T + y.t_s16[l]) : nullptr;
-        a.B = (const float*)(T + y.t_b[l]);
+        a.S = (const float*)(T + yt.t_s[l]);
+        a.S16 = cfg->plane_format == ZHA_PLANES_BF16 ? (const uint16_t*)(T + yt.t_s16[l]) : nullptr;
+        a.B = (const float*)(T + yt.t_b[l]);
+        a.hkv = hkv;
         a.cap = y.cap[l];
         a.top = l == top ? 1 : 0;
         a.n_top = n_nodes(cfg, n_tokens, l);
@@ -551,6 +568,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     at_.pl = (float*)(X + y.pl);
     at_.po = (float*)(X + y.po);
     at_.nact = (int32_t*)(X + y.nact);
+    at_.hkv = hkv;
     const int Bg = attn_blocks(n_tokens + 1, y.H, cfg->kv_dtype);
     if (top == 0 && (rc = TR.mark(0, 0, s))) return rc;
     // events 1 and 2 bracket the gather kernel's own execution
@@ -608,6 +626,27 @@ int zha_decode_step(const zha_config* cfg, const zha_buffers* bufs, int64_t n_to
 int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q,
                           float* out, int32_t* sel, zha_stats* stats, void* const* events, void* stream) {
     return decode_impl(cfg, bufs, n_tokens, q, out, sel, stats, events, stream);
+}
+
+size_t zha_batch_scratch_bytes(const zha_config* cfg, int32_t n_queries) {
+    if (validate(cfg)) return 0;
+    if (n_queries < 1) {
+        fail(ZHA_ERR_ARG, "n_queries must be >= 1 (got %d)", n_queries);
+        return 0;
+    }
+    const zha_config v = virtual_config(cfg, n_queries);
+    if (validate(&v)) return 0;
+    return make_layout(&v).scratch_bytes;
+}
+
+int zha_decode_batch(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, int32_t n_queries,
+                     const void* q, float* out, int32_t* sel, void* stream) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (n_queries < 1) return fail(ZHA_ERR_ARG, "n_queries must be >= 1 (got %d)", n_queries);
+    const zha_config v = virtual_config(cfg, n_queries);
+    if ((rc = validate(&v))) return rc;
+    return decode_impl(cfg, bufs, n_tokens, q, out, sel, nullptr, nullptr, stream, nullptr, n_queries);
 }
 
 int zha_decode_step_traced(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, const void* q,
@@ -695,6 +734,7 @@ int dense_decode(const zha_config* cfg, const void* k, const void* v, int64_t n_
     a.pl = (float*)(X + pl);
     a.po = (float*)(X + po);
     a.nact = (int32_t*)(X + nact);
+    a.hkv = cfg->n_kv_heads;
     const int Bg = attn_blocks(n_tokens, H, cfg->kv_dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = zha_launch_attention(cfg->kv_dtype, true, a, H, G, cfg->chunk, tau_of(cfg), Bg, s);

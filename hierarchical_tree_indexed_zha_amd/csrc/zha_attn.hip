@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? ZHA_ATTN_BLOCKS_BF16 : ZHA_ATTN_BL
     const float scale = tau * kLog2e;                     // logits in log2 units
     float* s_p = s_buf + wave * 16 * 33;                  // [16 heads][33]
 
-    const size_t head_row0 = (size_t)g * (size_t)a.cap_tok;
+    const size_t head_row0 = (size_t)(g % a.hkv) * (size_t)a.cap_tok;   // (a batch routes virtual groups)
 
     // Q as the A operand: row = head j (zero beyond G)
     uint4 qa16[4];

@@ -56,6 +56,7 @@ __device__ __forceinline__ uint32_t zha_div(uint32_t n, const ZhaDiv& v) {
 struct ZhaLevelArgs {
     const float* S;            // level planes [H_kv][cap][R][128]
     const uint16_t* S16;       // their bfloat16 copy, read instead when non-null
+    int hkv;                   // KV groups of the tree: virtual group g reads the planes of g % hkv
     const float* B;            // [H_kv][cap][R]
     int64_t cap;               // node slots per head at this level
     int top;                   // 1 at the first routed level (positions are node ids)
@@ -169,6 +170,7 @@ struct ZhaAttnArgs {
     float* pl;                 // [H_kv][Bg][G]
     float* po;                 // [H_kv][Bg][G][128]
     int32_t* nact;             // [H_kv]
+    int hkv;                   // KV groups of the cache: virtual group g reads the rows of g % hkv
 };
 #define ZHA_ATTN_ARGS_READY(a, ...) asm volatile("" ::"s"((a).K), "s"((a).n_tokens), __VA_ARGS__)
 hipError_t zha_launch_attention(int kv_dtype, bool dense, const ZhaAttnArgs& a, int H_kv, int G, int c,

@@ -163,7 +163,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     const int span = R <= 16 ? R : 16;
     const int cl = R <= 16 ? j / R : 0;
     const uint32_t allg = all_heads(G);
-    const size_t lrow = (size_t)g * a.cap;
+    const size_t lrow = (size_t)(g % a.hkv) * a.cap;   // the tree's group (a batch routes virtual groups)
     const size_t prow = (size_t)g * a.pcap;
     const int stride = nblk * 4;
     const int pcap = (int)a.pcap;

@@ -124,6 +124,28 @@ class ZhaLayer:
                 self._view(self.tree, o["b"], torch.float32, (H, n, R)),
                 self._view(self.tree, o["lse"], torch.float32, (H, n, R)))
 
+    def decode_batch(self, q: torch.Tensor, out: torch.Tensor | None = None,
+                     sel: torch.Tensor | None = None) -> torch.Tensor:
+        """A batch of decode queries q [Q][H_q][d] routed together over the current cache
+        (zha_decode_batch); returns out [Q][H_q][d] float32.  sel: optional int32
+        [Q][H_q][1 + capacity // chunk]."""
+        cfg = self.cfg
+        if q.dim() != 3 or tuple(q.shape[1:]) != (cfg.n_q_heads, cfg.head_dim):
+            raise ValueError(f"q must be [Q][{cfg.n_q_heads}][{cfg.head_dim}] (got {tuple(q.shape)})")
+        nq = q.shape[0]
+        self._need("q", q, tuple(q.shape), self.kv_torch_dtype)
+        if out is None:
+            out = torch.empty((nq, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device=self.k.device)
+        self._need("out", out, (nq, cfg.n_q_heads, cfg.head_dim), torch.float32)
+        if sel is not None:
+            self._need("sel", sel, (nq,) + self.sel_shape(), torch.int32)
+        need = B.zha_batch_scratch_bytes(cfg, nq)
+        if getattr(self, "_bscratch", None) is None or self._bscratch.numel() < need:
+            self._bscratch = torch.empty(need, dtype=torch.uint8, device=self.k.device)
+        bufs = B.Buffers(self.bufs.k, self.bufs.v, self.bufs.ref_q, self.bufs.tree, self._bscratch.data_ptr())
+        B.zha_decode_batch(cfg, bufs, self.n_tokens, nq, q, out, sel)
+        return out
+
     def tree_level16(self, level: int) -> torch.Tensor:
         """The router's bfloat16 copy of level `level`'s planes s [H][n_cap][R][d] (plane_format bf16)."""
         o = B.zha_tree_level_offsets(self.cfg, level)

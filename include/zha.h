@@ -233,6 +233,23 @@ int zha_decode_step_timed(const zha_config* cfg, const zha_buffers* bufs, int64_
                           const void* q, float* out, int32_t* sel, zha_stats* stats,
                           void* const* events, void* stream);
 
+/* A batch of n_queries decode queries over the same cache and tree, routed
+ * together: every launch of the step serves all of them (each query keeps its
+ * own frontiers, cuts and token sets; its results equal those of
+ * zha_decode_step on that query alone up to the attention's summation order).
+ *   q      [n_queries][n_q_heads][d] in kv_dtype.
+ *   out    [n_queries][n_q_heads][d] float32.
+ *   sel    NULL, or int32 [n_queries][n_q_heads][1 + capacity / chunk], as
+ *          zha_decode_step's per query.
+ *   bufs->scratch must hold zha_batch_scratch_bytes(cfg, n_queries) bytes.
+ * Returns ZHA_ERR_ARG for n_queries < 1.  Defined by: page rit.work
+ * "zha-tree-indexer-long-context", section "Дерево сокращает сам поиск нужных
+ * ключей" (the tree serves every query: the search is sub-quadratic over a
+ * sequence of queries, not one). */
+size_t zha_batch_scratch_bytes(const zha_config* cfg, int32_t n_queries);
+int zha_decode_batch(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens, int32_t n_queries,
+                     const void* q, float* out, int32_t* sel, void* stream);
+
 /* zha_decode_step with a HIP event recorded on `stream` before the step's first
  * kernel (events[0]) and after each kernel it launches (events[1], events[2],
  * ...), up to max_events events in all; kinds[i] names the kernel that ends at

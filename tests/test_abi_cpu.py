@@ -106,6 +106,9 @@ def test_entry_points_reject_bad_arguments_before_touching_the_device():
         (lambda: B.zha_decode_step(B.make_config(**{**_base(), "capacity": 1000, "sink": 0}), bufs, 10, fake, fake,
                                    stream=0), B.ZHA_ERR_UNSUPPORTED),
         (lambda: B.zha_decode_step_traced(cfg, bufs, 10, fake, fake, [], stream=0), B.ZHA_ERR_ARG),
+        (lambda: B.zha_decode_batch(cfg, bufs, 10, 0, fake, fake, stream=0), B.ZHA_ERR_ARG),
+        (lambda: B.zha_decode_batch(cfg, bufs, 1001, 2, fake, fake, stream=0), B.ZHA_ERR_CAPACITY),
+        (lambda: B.zha_batch_scratch_bytes(cfg, 0), B.ZHA_ERR_ARG),
         (lambda: B.zha_decode_step_traced(cfg, bufs, 10, fake, fake, [fake, None], stream=0), B.ZHA_ERR_ARG),
         (lambda: B.dense_decode(cfg, fake, fake, 1001, fake, fake, fake, 0), B.ZHA_ERR_CAPACITY),
         (lambda: B.dense_decode(cfg, fake, fake, 10, fake, fake, None, 0), B.ZHA_ERR_ARG),
@@ -162,3 +165,14 @@ def test_chained_levels_follow_the_slot_and_plane_bounds():
     assert chained("ultra") == [4, 5, 6, 7]       # 2,560 + 320 + 40 + 5 nodes
     assert chained("light", 100) == [1, 2]        # 12 level-1 nodes, one level-2 node
     assert chained("light", 60) == [1]            # only level 1 complete: 7 nodes
+
+
+def test_batch_scratch_covers_every_query():
+    """The batch's scratch grows with the number of queries and one query needs exactly
+    the single step's scratch."""
+    cfg = _cfg(capacity=50000)
+    one = B.zha_scratch_bytes(cfg)
+    assert B.zha_batch_scratch_bytes(cfg, 1) == one
+    sizes = [B.zha_batch_scratch_bytes(cfg, q) for q in (1, 2, 4, 8)]
+    assert all(b > a for a, b in zip(sizes, sizes[1:]))
+    assert sizes[-1] >= 8 * (one // 2)

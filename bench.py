@@ -460,6 +460,8 @@ def cold_gather(args, layer, x, w, torch, B):
     N = layer.n_tokens
     flush = torch.empty(args.flush_bytes, dtype=torch.uint8, device="cuda")
     K = args.cold_steps
+    if K < 1:
+        return None
     rows = [_events(torch, 4) for _ in range(K)]
     stats = layer.new_stats()
     gb = 0
@@ -686,12 +688,14 @@ def main():
     cold = cold_gather(args, layer, x, w, torch, B)
     rf = result["roofline"]
     rf["warm_source"] = "hbm_or_mall"
-    rf["achieved_cold"] = cold["gather_gbs"]
-    rf["frac_cold"] = round(cold["gather_gbs"] / HBM_PEAK_GBS, 4)
-    result["cold"] = cold
-    _log(f"[bench] cold gather {cold['gather_us']:.1f} us ({cold['gather_gbs']:.0f} GB/s), "
-         f"cold decode {cold['decode_us']:.1f} us; router kernels {rt_us:.1f} us")
-    result["fidelity"] = {"light": fidelity_of(layer, x, 4)}
+    if cold is not None:
+        rf["achieved_cold"] = cold["gather_gbs"]
+        rf["frac_cold"] = round(cold["gather_gbs"] / HBM_PEAK_GBS, 4)
+        result["cold"] = cold
+        _log(f"[bench] cold gather {cold['gather_us']:.1f} us ({cold['gather_gbs']:.0f} GB/s), "
+             f"cold decode {cold['decode_us']:.1f} us")
+    _log(f"[bench] router kernels {rt_us:.1f} us")
+    result["fidelity"] = {w.name: fidelity_of(layer, x, 4)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, layer, x, w, torch)
     del layer, x

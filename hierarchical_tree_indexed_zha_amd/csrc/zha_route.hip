@@ -30,12 +30,16 @@
 //     writes per-head kept bitmaps over node ids;
 //   * every level below: a score launch over the group's candidates (the children
 //     of the group's kept nodes of the level above, then the level's orphans),
-//     then one selection launch: a group whose frontier has at most 1024
-//     candidates is selected by one workgroup; larger frontiers are histogrammed
-//     over slices by up to eight workgroups per head, the head's last workgroup
-//     finishes its cut and the group's last head merges the heads' kept bitmaps
-//     into the group's kept list.  Below the chain, the first score kernel derives
-//     the chain's last level's group kept list from the per-head bitmaps.
+//     then a selection launch: a group whose frontier has at most 1024
+//     candidates is selected, and its kept list written, by one workgroup; larger
+//     frontiers are histogrammed over slices by up to eight workgroups per head
+//     and the head's last workgroup finishes its cut (at levels that can hold
+//     frontiers past the keys one workgroup stages, a cross launch lists the
+//     crossing bin's keys over the whole GPU and a resolve launch cuts them);
+//     then an apply launch forms every candidate's mask of the heads that keep
+//     it and writes the group's kept list in order (decoupled look-back).  Below
+//     the chain, the first score kernel derives the chain's last level's group
+//     kept list from the per-head bitmaps.
 //
 // The candidates of a level are never written out: they are the children of the
 // level above's kept nodes (kept list and head masks, ascending) followed by the
@@ -1686,11 +1690,13 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
     __shared__ HeadCut s_hc[ZHA_MAX_GROUP];
     const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the ticket is drawn in the parent count's round trip (a workgroup that then
+    // finds nothing to do leaves with it: later tickets only run past the chunks)
+    if (tid == 0) s_ticket = atomicAdd(&a.tick[g], 1u);
     const int pn = parent_count(a, g);
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
     if (n <= kSmallN) return;                  // the select kernel wrote the kept list
     const int nch = (n + kApplyChunk - 1) / kApplyChunk;
-    if (tid == 0) s_ticket = atomicAdd(&a.tick[g], 1u);
     __syncthreads();
     const int ci = (int)s_ticket;
     if (ci >= nch) return;
@@ -1706,6 +1712,15 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
 #pragma unroll
     for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
         x[hh] = *reinterpret_cast<const float4*>(a.sig + ((size_t)g * G + (hh < G ? hh : 0)) * a.sstride + pv);
+    // the parents' kept entries of the thread's positions, in the same round trip
+    const int pnc = a.top ? 0 : pn * c;
+    int32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int p = p0 + j;
+        pk[j] = 0;
+        if (p < pnc) pk[j] = a.pklist[(size_t)g * a.pcap + zha_div((uint32_t)p, a.dc)];
+    }
     if (tid < G) s_hc[tid] = mine;
     __syncthreads();
     // every head's cut read from LDS at once, then the masks without branches
@@ -1779,17 +1794,14 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
     uint32_t r = s_prefix + s_wc[wave] + inc - mine_cnt;
     int32_t* kl = a.klist + (size_t)g * a.cap;
     uint32_t* km = a.kmask + (size_t)g * a.cap;
-    const int pnc = a.top ? 0 : pn * c;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (msk[j]) {
             const int p = p0 + j;
             int32_t node;
             if (a.top) node = p;
-            else if (p < pnc) {
-                const int pi = (int)zha_div((uint32_t)p, a.dc);
-                node = a.pklist[(size_t)g * a.pcap + pi] * c + (p - pi * c);
-            } else node = (int32_t)a.orph_lo + (p - pnc);
+            else if (p < pnc) node = pk[j] * c + (p - (int)zha_div((uint32_t)p, a.dc) * c);
+            else node = (int32_t)a.orph_lo + (p - pnc);
             kl[r] = node;
             km[r] = msk[j];
             ++r;

@@ -139,11 +139,11 @@ def _pins():
     for ex, case in P._golden_cases():
         out.append((f"golden[{ex['name']},{case['p']}]", lambda ex=ex, case=case: P.test_golden_worked_examples(ex, case)))
     out.append(("ties", P.test_cut_ties_break_by_ascending_index_and_margin_flags_them))
-    out.append(("p13-library", P.test_p13_round_bf16_matches_library_rounding_of_float32_values))
-    out.append(("p13-hand", P.test_p13_round_bf16_hand_values))
-    out.append(("p13-scores", P.test_p13_bf16_router_scores_use_rounded_planes_only))
-    out.append(("p14-one", P.test_p14_recall_is_one_everywhere_at_p_one))
-    out.append(("p14-lse", P.test_p14_recall_equals_node_logsumexp_form_and_is_monotone))
+    out.append(("p14-library", P.test_p14_round_bf16_matches_library_rounding_of_float32_values))
+    out.append(("p14-hand", P.test_p14_round_bf16_hand_values))
+    out.append(("p14-scores", P.test_p14_bf16_router_scores_use_rounded_planes_only))
+    out.append(("p15-one", P.test_p15_recall_is_one_everywhere_at_p_one))
+    out.append(("p15-lse", P.test_p15_recall_equals_node_logsumexp_form_and_is_monotone))
     return out
 
 

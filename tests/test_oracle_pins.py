@@ -383,9 +383,9 @@ def test_bf16_bits_widen_exactly():
     assert np.array_equal(O.widen(bits), x.double().numpy())
 
 
-# ---------------------------------------------------------------- narrow router planes (P13)
+# ---------------------------------------------------------------- narrow router planes (P14)
 
-def test_p13_round_bf16_matches_library_rounding_of_float32_values():
+def test_p14_round_bf16_matches_library_rounding_of_float32_values():
     """On float32-representable inputs one rounding to bfloat16 is the library's own
     float32 -> bfloat16 conversion (round to nearest, ties to even)."""
     x32 = (torch.randn(20000, dtype=torch.float64) * torch.exp(torch.randn(20000, dtype=torch.float64) * 4)).float()
@@ -393,7 +393,7 @@ def test_p13_round_bf16_matches_library_rounding_of_float32_values():
     assert np.array_equal(O.round_bf16(x32.double().numpy()), ref)
 
 
-def test_p13_round_bf16_hand_values():
+def test_p14_round_bf16_hand_values():
     """bfloat16 spacing is 2**-7 on [1, 2): exact ties go to the even neighbour, values
     past a tie go up, signs are symmetric, and a float64 value just past a tie is not
     first rounded to float32 (that double rounding would land on the tie and go down)."""
@@ -412,7 +412,7 @@ def test_p13_round_bf16_hand_values():
     assert got.tolist() == [c[1] for c in cases]
 
 
-def test_p13_bf16_router_scores_use_rounded_planes_only():
+def test_p14_bf16_router_scores_use_rounded_planes_only():
     """A 'bf16' tree scores with s rounded to bfloat16 and b unchanged: the score equals
     the plane formula on round_bf16(s), and differs from the exact score by at most
     tau * sum_d |q_d| |s_d| 2**-8 (half a bfloat16 spacing per element)."""
@@ -434,13 +434,13 @@ def test_p13_bf16_router_scores_use_rounded_planes_only():
         O.SummaryTree(keys, qref, 256, 4, 2, plane_format="fp8")
 
 
-# ---------------------------------------------------------------- router fidelity (P14)
+# ---------------------------------------------------------------- router fidelity (P15)
 
 def _route_kept(r):
     return {lv.level: lv.kept for lv in r.levels}
 
 
-def test_p14_recall_is_one_everywhere_at_p_one():
+def test_p15_recall_is_one_everywhere_at_p_one():
     keys, _ = _rand_cache(1, 300, 16, seed=21)
     tree = O.SummaryTree(keys, RNG(22).normal(size=(1, 2, 16)), 300, 4, 3)
     q = RNG(23).normal(size=16) * 2
@@ -449,7 +449,7 @@ def test_p14_recall_is_one_everywhere_at_p_one():
     assert np.allclose(rec, 1.0, atol=1e-12) and abs(cap - 1.0) < 1e-12
 
 
-def test_p14_recall_equals_node_logsumexp_form_and_is_monotone():
+def test_p15_recall_equals_node_logsumexp_form_and_is_monotone():
     """recall_l = sum over kept nodes n of e^{LSE_n - LSE} (node log-sum-exp over its raw
     keys, a separate formula) plus the mass of the tokens under no complete level-l
     node; it never grows going down the levels; captured = recall_1 plus the sink's

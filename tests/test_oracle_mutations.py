@@ -123,6 +123,44 @@ def _route_no_orphans(q_h, tree, g, p):
     return route
 
 
+_orig_fp8_scale = Z.fp8_plane_scale_exp
+
+
+def _fp8_truncate(s):
+    s = np.asarray(s, dtype=np.float64)
+    k = _orig_fp8_scale(s)[..., None]
+    x = np.ldexp(s, -k)
+    _, ex = np.frexp(x)
+    qe = np.maximum(ex, -5) - 4
+    return np.ldexp(np.trunc(np.ldexp(x, -qe)), qe + k)
+
+
+def _fp8_node_scale(s):
+    s = np.asarray(s, dtype=np.float64)
+    k = _orig_fp8_scale(s.reshape(s.shape[:-2] + (-1,)) if s.ndim >= 2 else s)
+    k = k[..., None, None] if s.ndim >= 2 else k[..., None]
+    x = np.ldexp(s, -k)
+    _, ex = np.frexp(x)
+    qe = np.maximum(ex, -5) - 4
+    return np.ldexp(np.round(np.ldexp(x, -qe)), qe + k)
+
+
+def _fp8_no_subnormals(s):
+    s = np.asarray(s, dtype=np.float64)
+    k = _orig_fp8_scale(s)[..., None]
+    x = np.ldexp(s, -k)
+    _, ex = np.frexp(x)
+    qe = ex - 4
+    y = np.ldexp(np.round(np.ldexp(x, -qe)), qe)
+    return np.ldexp(np.where(np.abs(x) < 2.0 ** -6, 0.0, y), k)
+
+
+def _fp8_scale_low(s):
+    m = np.abs(np.asarray(s, dtype=np.float64)).max(axis=-1)
+    _, e = np.frexp(m)
+    return np.where(m == 0, 0, np.maximum(e - 9, -126)).astype(np.int64)
+
+
 def _pins():
     """The pins run against every mutation (name, callable)."""
     out = []
@@ -142,6 +180,9 @@ def _pins():
     out.append(("p14-library", P.test_p14_round_bf16_matches_library_rounding_of_float32_values))
     out.append(("p14-hand", P.test_p14_round_bf16_hand_values))
     out.append(("p14-scores", P.test_p14_bf16_router_scores_use_rounded_planes_only))
+    out.append(("p14-fp8-library", P.test_p14_round_fp8_matches_library_rounding_of_scaled_float32_values))
+    out.append(("p14-fp8-hand", P.test_p14_fp8_scale_and_hand_values))
+    out.append(("p14-fp8-scores", P.test_p14_fp8_router_scores_use_rounded_planes_only))
     out.append(("p15-one", P.test_p15_recall_is_one_everywhere_at_p_one))
     out.append(("p15-lse", P.test_p15_recall_equals_node_logsumexp_form_and_is_monotone))
     return out
@@ -160,6 +201,10 @@ MUTATIONS = {
     "bf16_truncates": ("round_bf16", _round_truncate),
     "bf16_double_rounding_via_float32": ("round_bf16", _round_via_float32),
     "bf16_ties_away_from_zero": ("round_bf16", _round_half_away),
+    "fp8_truncates": ("round_fp8", _fp8_truncate),
+    "fp8_one_scale_per_node": ("round_fp8", _fp8_node_scale),
+    "fp8_flushes_subnormals": ("round_fp8", _fp8_no_subnormals),
+    "fp8_scale_one_binade_low": ("fp8_plane_scale_exp", _fp8_scale_low),
     "recall_drops_the_tail": ("level_mass_recall", _recall_tail_dropped),
     "recall_levels_reversed": ("level_mass_recall", _recall_unnormalised_by_level),
 }

@@ -431,7 +431,62 @@ def test_p14_bf16_router_scores_use_rounded_planes_only():
     assert np.all(np.abs(narrow - exact) <= bound + 1e-12)
     assert not np.array_equal(narrow, exact)
     with pytest.raises(ValueError):
-        O.SummaryTree(keys, qref, 256, 4, 2, plane_format="fp8")
+        O.SummaryTree(keys, qref, 256, 4, 2, plane_format="fp4")
+
+
+def test_p14_round_fp8_matches_library_rounding_of_scaled_float32_values():
+    """Each plane divided by its power-of-two scale and rounded is the library's own
+    float32 -> float8_e4m3fn conversion (round to nearest, ties to even), over planes
+    whose magnitudes span many binades and reach the subnormals."""
+    g = torch.Generator().manual_seed(5)
+    s32 = (torch.randn(400, 2, 128, dtype=torch.float64, generator=g)
+           * torch.exp(torch.randn(400, 2, 1, dtype=torch.float64, generator=g) * 5)
+           * torch.exp(torch.randn(400, 2, 128, dtype=torch.float64, generator=g) * 2)).float()
+    s = s32.double().numpy()
+    k = O.fp8_plane_scale_exp(s)
+    x = torch.from_numpy(np.ldexp(s, -k[..., None]))        # exact: power-of-two scaling
+    assert torch.equal(x.float().double(), x)                # still float32-representable
+    ref = np.ldexp(x.float().to(torch.float8_e4m3fn).double().numpy(), k[..., None])
+    assert np.array_equal(O.round_fp8(s), ref)
+    assert np.abs(np.ldexp(s, -k[..., None])).max() <= 448.0
+
+
+def test_p14_fp8_scale_and_hand_values():
+    """The scale puts a plane's largest magnitude in (224, 448]; E4M3 spacing is 2**-3
+    on [1, 2), 32 on [256, 512) and 2**-9 below 2**-6 (subnormals); ties go to the
+    even neighbour."""
+    planes = np.array([[448.0, 1.0], [449.0, 1.0], [1.0, -0.5], [0.875, 0.1], [0.8750001, 0.1],
+                       [0.0, 0.0], [-3.0, 2.0 ** -130]])
+    assert O.fp8_plane_scale_exp(planes).tolist() == [0, 1, -8, -9, -8, 0, -7]
+    u = 2.0 ** -9
+    cases = [(1.0625, 1.0), (1.1875, 1.25), (1.97, 2.0), (-3.3, -3.25), (300.0, 288.0), (304.0, 320.0),
+             (2.0 ** -10, 0.0), (1.5 * u, 2 * u), (2.5 * u, 2 * u), (0.51 * u, u), (2.0 ** -6 + u / 2, 2.0 ** -6),
+             (0.0, 0.0)]
+    x = np.array([[448.0] + [c[0] for c in cases]])          # scale 1 (k = 0) for every case
+    got = O.round_fp8(x)[0, 1:]
+    assert got.tolist() == [c[1] for c in cases]
+    assert O.round_fp8(np.zeros((1, 4))).tolist() == [[0.0] * 4]
+
+
+def test_p14_fp8_router_scores_use_rounded_planes_only():
+    """An 'fp8' tree scores with s rounded to its scaled 8-bit form and b unchanged,
+    within half a spacing per element of the exact score."""
+    keys, _ = _rand_cache(1, 256, 32, seed=11)
+    qref = RNG(12).normal(size=(1, 2, 32))
+    t32 = O.SummaryTree(keys, qref, 256, 4, 2)
+    t8 = O.SummaryTree(keys, qref, 256, 4, 2, plane_format="fp8")
+    q = RNG(13).normal(size=32)
+    nodes = np.arange(16)
+    s, b, _ = t32.get(2, 0, nodes)
+    s8, b8 = t8.router_planes(2, 0, nodes)
+    assert np.array_equal(b8, b) and np.array_equal(s8, O.round_fp8(s))
+    k = O.fp8_plane_scale_exp(s)[..., None]
+    exact = O.plane_scores(q, s, b, t32.tau)
+    narrow = O.plane_scores(q, s8, b8, t8.tau)
+    half = np.maximum(2.0 ** -4 * np.abs(s), np.ldexp(1.0, k - 10))
+    bound = t32.tau * (np.abs(q)[None, None, :] * half).sum(-1).max(-1)
+    assert np.all(np.abs(narrow - exact) <= bound + 1e-12)
+    assert not np.array_equal(narrow, exact)
 
 
 # ---------------------------------------------------------------- router fidelity (P15)

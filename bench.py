@@ -543,7 +543,7 @@ def point(torch, W, B, ZhaLayer, w, steps, dense_steps, append, plane_format=0, 
     if append:
         layer.n_tokens = n
     if plane_format:
-        line["plane_format"] = "bf16"
+        line["plane_format"] = {v: k for k, v in B.PLANE_FORMATS.items()}[plane_format]
     if fid_steps:
         line["fidelity"] = fidelity_of(layer, x, fid_steps)
     del layer, x
@@ -580,7 +580,7 @@ def ultra_point(args, torch, W, B, ZhaLayer):
 
 def others(args, torch, W, B, ZhaLayer):
     """deep at full size (route time, keys read, fidelity), and light and wide with
-    float32 and bfloat16 router planes (router time and bytes, fidelity)."""
+    float32, bfloat16 and 8-bit router planes (router time and bytes, fidelity)."""
     out = {}
     w = dataclasses.replace(W.get("deep"), steps=16, append=False)
     _log("[deep] full size")
@@ -589,12 +589,12 @@ def others(args, torch, W, B, ZhaLayer):
     for name in ("light", "wide"):
         w = dataclasses.replace(W.get(name), steps=16, append=False)
         planes[name] = {}
-        for fmt in (0, 1):
-            _log(f"[planes] {name} plane_format={fmt}")
+        for fname, fmt in B.PLANE_FORMATS.items():
+            _log(f"[planes] {name} plane_format={fname}")
             line = point(torch, W, B, ZhaLayer, w, 16, 16, False, plane_format=fmt, fid_steps=2)
-            planes[name]["bf16" if fmt else "f32"] = {k: line[k] for k in (
+            planes[name][fname] = {k: line[k] for k in (
                 "zha_decode_us", "route_us", "gather_us", "router_bytes", "keys_read_frac", "fidelity")}
-    out["planes16"] = planes
+    out["planes"] = planes
     out["batch"] = batch_points(torch, W, B, ZhaLayer)
     return out
 
@@ -704,7 +704,7 @@ def main():
         oth = others(args, torch, W, B, ZhaLayer)
         result["deep"] = oth["deep"]
         result["fidelity"]["deep"] = oth["deep"]["fidelity"]
-        result["planes16"] = oth["planes16"]
+        result["planes"] = oth["planes"]
         result["batch"] = oth["batch"]
         result["sweep"] = sweep(args, torch, W, B, ZhaLayer)
         result["ultra"] = ultra_point(args, torch, W, B, ZhaLayer)

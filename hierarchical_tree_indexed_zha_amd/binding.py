@@ -117,7 +117,8 @@ def lib() -> ctypes.CDLL:
             "zha_dense_scratch_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_sel_bytes": (ctypes.c_size_t, [cfgp]),
             "zha_tree_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int32, P(ctypes.c_int64), P(ctypes.c_int64),
-                                                      P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64)]),
+                                                      P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64),
+                                                      P(ctypes.c_int64), P(ctypes.c_int64)]),
             "zha_route_level_offsets": (ctypes.c_int, [cfgp, ctypes.c_int64, ctypes.c_int32, P(RouteOffsets)]),
             "zha_build_tree": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p]),
             "zha_append_token": (ctypes.c_int, [cfgp, P(Buffers), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -175,7 +176,7 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
-PLANE_FORMATS = {"f32": 0, "bf16": 1}   # ZHA_PLANES_F32, ZHA_PLANES_BF16
+PLANE_FORMATS = {"f32": 0, "bf16": 1, "fp8": 2}   # ZHA_PLANES_F32, ZHA_PLANES_BF16, ZHA_PLANES_FP8
 
 
 def make_config(n_kv_heads, n_q_heads, head_dim, chunk, levels, n_ref, top_p, kv_dtype, capacity, sink=1,
@@ -227,10 +228,11 @@ def zha_sel_bytes(cfg: Config) -> int:
 
 
 def zha_tree_level_offsets(cfg: Config, level: int) -> dict:
-    s, b, l, n, s16 = (ctypes.c_int64() for _ in range(5))
+    s, b, l, n, s16, s8, sc = (ctypes.c_int64() for _ in range(7))
     _check(lib().zha_tree_level_offsets(ctypes.byref(cfg), level, ctypes.byref(s), ctypes.byref(b), ctypes.byref(l),
-                                        ctypes.byref(n), ctypes.byref(s16)))
-    return {"s": s.value, "b": b.value, "lse": l.value, "n_cap": n.value, "s16": s16.value}
+                                        ctypes.byref(n), ctypes.byref(s16), ctypes.byref(s8), ctypes.byref(sc)))
+    return {"s": s.value, "b": b.value, "lse": l.value, "n_cap": n.value, "s16": s16.value, "s8": s8.value,
+            "sc": sc.value}
 
 
 def zha_route_level_offsets(cfg: Config, n_tokens: int, level: int) -> dict:

@@ -68,8 +68,10 @@ int validate(const zha_config* cfg) {
         return fail(ZHA_ERR_UNSUPPORTED, "capacity must be < 2^31 (got %lld)", (long long)cfg->capacity);
     if (cfg->sink == 0) return fail(ZHA_ERR_UNSUPPORTED, "sink = 0 (no attention sink) is not implemented");
     if (cfg->sink != 1) return fail(ZHA_ERR_ARG, "sink must be 1 (got %d)", cfg->sink);
-    if (cfg->plane_format != ZHA_PLANES_F32 && cfg->plane_format != ZHA_PLANES_BF16)
-        return fail(ZHA_ERR_ARG, "plane_format must be ZHA_PLANES_F32 or ZHA_PLANES_BF16 (got %d)", cfg->plane_format);
+    if (cfg->plane_format != ZHA_PLANES_F32 && cfg->plane_format != ZHA_PLANES_BF16 &&
+        cfg->plane_format != ZHA_PLANES_FP8)
+        return fail(ZHA_ERR_ARG, "plane_format must be ZHA_PLANES_F32, ZHA_PLANES_BF16 or ZHA_PLANES_FP8 (got %d)",
+                    cfg->plane_format);
     return ZHA_OK;
 }
 
@@ -90,6 +92,7 @@ struct Layout {
     std::vector<int64_t> cap;             // node slots per level (index 1..L)
     // tree
     std::vector<size_t> t_s, t_b, t_l, t_s16;   // t_s16: bfloat16 router copy of s (0: none)
+    std::vector<size_t> t_s8, t_sc;             // 8-bit router copy of s and its per-plane scales (0: none)
     size_t tree_bytes = 0;
     // decode scratch
     std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, stats;
@@ -121,6 +124,7 @@ Layout make_layout(const zha_config* cfg) {
     y.cap.assign(y.L + 2, 0);
     for (int l = 1; l <= y.L; ++l) y.cap[l] = n_nodes(cfg, cfg->capacity, l);
     y.t_s.assign(y.L + 1, 0); y.t_b.assign(y.L + 1, 0); y.t_l.assign(y.L + 1, 0); y.t_s16.assign(y.L + 1, 0);
+    y.t_s8.assign(y.L + 1, 0); y.t_sc.assign(y.L + 1, 0);
     size_t off = 0;
     for (int l = 1; l <= y.L; ++l) {
         const size_t n = (size_t)y.cap[l];
@@ -129,6 +133,10 @@ Layout make_layout(const zha_config* cfg) {
         y.t_l[l] = off; off = align_up(off + sizeof(float) * H * n * R);
         if (cfg->plane_format == ZHA_PLANES_BF16) {
             y.t_s16[l] = off; off = align_up(off + sizeof(uint16_t) * H * n * R * ZHA_D);
+        }
+        if (cfg->plane_format == ZHA_PLANES_FP8) {
+            y.t_s8[l] = off; off = align_up(off + sizeof(uint8_t) * H * n * R * ZHA_D);
+            y.t_sc[l] = off; off = align_up(off + sizeof(float) * H * n * R);
         }
     }
     y.tree_bytes = off;
@@ -175,12 +183,17 @@ Layout make_layout(const zha_config* cfg) {
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
-// The router's bfloat16 copy of level l's planes s for nodes [first, first + n)
-// (nothing unless plane_format is ZHA_PLANES_BF16).
+// The router's narrow copy of level l's planes s for nodes [first, first + n):
+// bfloat16, or 8-bit with per-plane scales (nothing for float32 planes).
 int planes16(const zha_config* cfg, const Layout& y, void* T, int l, int64_t first, int64_t n, hipStream_t s) {
-    if (cfg->plane_format != ZHA_PLANES_BF16 || n <= 0) return ZHA_OK;
-    hipError_t e = zha_launch_planes16((const float*)at(T, y.t_s[l]), (uint16_t*)at(T, y.t_s16[l]), y.H, y.cap[l],
-                                       cfg->n_ref, first, n, s);
+    if (n <= 0) return ZHA_OK;
+    hipError_t e = hipSuccess;
+    if (cfg->plane_format == ZHA_PLANES_BF16)
+        e = zha_launch_planes16((const float*)at(T, y.t_s[l]), (uint16_t*)at(T, y.t_s16[l]), y.H, y.cap[l],
+                                cfg->n_ref, first, n, s);
+    else if (cfg->plane_format == ZHA_PLANES_FP8)
+        e = zha_launch_planes8((const float*)at(T, y.t_s[l]), (uint8_t*)at(T, y.t_s8[l]), (float*)at(T, y.t_sc[l]),
+                               y.H, y.cap[l], cfg->n_ref, first, n, s);
     return e == hipSuccess ? ZHA_OK : hip_fail(e, "plane copy launch");
 }
 
@@ -257,7 +270,7 @@ size_t zha_sel_bytes(const zha_config* cfg) {
 }
 
 int zha_tree_level_offsets(const zha_config* cfg, int32_t level, int64_t* s_off, int64_t* b_off, int64_t* lse_off,
-                           int64_t* n_cap, int64_t* s16_off) {
+                           int64_t* n_cap, int64_t* s16_off, int64_t* s8_off, int64_t* sc_off) {
     int rc = validate(cfg);
     if (rc) return rc;
     if (level < 1 || level > cfg->levels) return fail(ZHA_ERR_ARG, "level %d outside 1..%d", level, cfg->levels);
@@ -267,6 +280,8 @@ int zha_tree_level_offsets(const zha_config* cfg, int32_t level, int64_t* s_off,
     if (lse_off) *lse_off = (int64_t)y.t_l[level];
     if (n_cap) *n_cap = y.cap[level];
     if (s16_off) *s16_off = cfg->plane_format == ZHA_PLANES_BF16 ? (int64_t)y.t_s16[level] : -1;
+    if (s8_off) *s8_off = cfg->plane_format == ZHA_PLANES_FP8 ? (int64_t)y.t_s8[level] : -1;
+    if (sc_off) *sc_off = cfg->plane_format == ZHA_PLANES_FP8 ? (int64_t)y.t_sc[level] : -1;
     return ok();
 }
 
@@ -425,6 +440,8 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         ZhaLevelArgs a{};
         a.S = (const float*)(T + yt.t_s[l]);
         a.S16 = cfg->plane_format == ZHA_PLANES_BF16 ? (const uint16_t*)(T + yt.t_s16[l]) : nullptr;
+        a.S8 = cfg->plane_format == ZHA_PLANES_FP8 ? (const uint8_t*)(T + yt.t_s8[l]) : nullptr;
+        a.SC = cfg->plane_format == ZHA_PLANES_FP8 ? (const float*)(T + yt.t_sc[l]) : nullptr;
         a.B = (const float*)(T + yt.t_b[l]);
         a.hkv = hkv;
         a.cap = y.cap[l];
@@ -600,9 +617,10 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         r.klist1 = at_.klist;
         r.cap1 = at_.cap1;
         r.n_tokens = n_tokens;
-        // one node's summary bytes the router reads: planes s (float32 or their
-        // bfloat16 copy) and offsets b (float32)
-        r.plane_bytes = (int64_t)R * (ZHA_D * (cfg->plane_format == ZHA_PLANES_BF16 ? 2 : 4) + 4);
+        // one node's summary bytes the router reads: planes s (float32, or their
+        // bfloat16 copy, or their 8-bit copy and its per-plane scale) and offsets b
+        r.plane_bytes = cfg->plane_format == ZHA_PLANES_FP8 ? (int64_t)R * (ZHA_D + 8)
+                        : (int64_t)R * (ZHA_D * (cfg->plane_format == ZHA_PLANES_BF16 ? 2 : 4) + 4);
         r.kv_row_bytes = 2 * ZHA_D * (cfg->kv_dtype == ZHA_BF16 ? 2 : 4);
         r.H = y.H;
         r.G = y.G;

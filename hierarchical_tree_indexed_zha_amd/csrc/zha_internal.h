@@ -18,6 +18,10 @@ hipError_t zha_launch_merge(const float* Sc, const float* Bc, const float* Lc, f
 // [first, first + n) of one level, every KV head
 hipError_t zha_launch_planes16(const float* S, uint16_t* S16, int H_kv, int64_t cap, int R, int64_t first, int64_t n,
                                hipStream_t stream);
+// the router's 8-bit copy of planes s of nodes [first, first + n) of one level,
+// every KV head: per plane a power-of-two scale SC and FP8 E4M3 codes S8
+hipError_t zha_launch_planes8(const float* S, uint8_t* S8, float* SC, int H_kv, int64_t cap, int R, int64_t first,
+                              int64_t n, hipStream_t stream);
 hipError_t zha_launch_kv_write(int kv_dtype, void* K, void* V, const void* kn, const void* vn, int H_kv,
                                int64_t cap_tok, int64_t row, hipStream_t stream);
 
@@ -56,6 +60,8 @@ __device__ __forceinline__ uint32_t zha_div(uint32_t n, const ZhaDiv& v) {
 struct ZhaLevelArgs {
     const float* S;            // level planes [H_kv][cap][R][128]
     const uint16_t* S16;       // their bfloat16 copy, read instead when non-null
+    const uint8_t* S8;         // their 8-bit copy (FP8 E4M3 codes), read instead when non-null
+    const float* SC;           // [H_kv][cap][R] the 8-bit planes' scales (powers of two)
     int hkv;                   // KV groups of the tree: virtual group g reads the planes of g % hkv
     const float* B;            // [H_kv][cap][R]
     int64_t cap;               // node slots per head at this level

@@ -140,6 +140,14 @@ __device__ __forceinline__ void defer_entry(const DeferView& v, int G, uint32_t 
     mask = defer_mask(v, G, node);
 }
 
+// An FP8 E4M3 code (sign, 4 exponent bits of bias 7, 3 mantissa bits; exponent 0
+// holds the subnormals m 2^-9) as the float32 it stands for, exactly.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
 // Scores one level's candidates for every head of group g, as workgroup blk of
 // nblk (256 threads).  Each wave scores items of U = 16/R candidates (R <= 16)
 // or one candidate over R/16 column blocks (R > 16).  ALL: every node of the
@@ -149,7 +157,7 @@ __device__ __forceinline__ void defer_entry(const DeferView& v, int G, uint32_t 
 // derived here from its bitmaps (dynamic LDS), and this workgroup writes its
 // share of it (all of it together with the other workgroups).
 // Candidate positions and node ids fit in 32 bits (capacity < 2^31).
-template <bool BF16, bool ALL, bool DEF = false, bool P16 = false>
+template <bool BF16, bool ALL, bool DEF = false, int PF = 0>
 __device__ __forceinline__ void score_level(const void* __restrict__ q, const ZhaLevelArgs& a, int G, int c, int R,
                                             float tau, int g, int blk, int nblk, float (&hm)[4],
                                             const ZhaLevelArgs* pa = nullptr) {
@@ -304,7 +312,18 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
             const int r = R <= 16 ? (j % R) : (cb * 16 + j);
             const size_t prw = (lrow + (size_t)node) * R + r;
             float4 sv[8];
-            if (valid && P16) {
+            if (valid && PF == 2) {
+                // the router's 8-bit copy: the same four elements per lane (one 4-byte
+                // load each), decoded exactly; the plane's scale multiplies the product
+                const uint32_t* plane = reinterpret_cast<const uint32_t*>(a.S8 + prw * ZHA_D);
+                uint32_t u[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) u[m] = plane[4 * m + kq];
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    sv[m] = make_float4(e4m3_to_f32(u[m] & 0xFFu), e4m3_to_f32((u[m] >> 8) & 0xFFu),
+                                        e4m3_to_f32((u[m] >> 16) & 0xFFu), e4m3_to_f32(u[m] >> 24));
+            } else if (valid && PF == 1) {
                 // the router's bfloat16 copy: the same four elements per lane, widened exactly
                 const uint2* plane = reinterpret_cast<const uint2*>(a.S16 + prw * ZHA_D);
                 uint2 u[8];
@@ -323,6 +342,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
                 for (int m = 0; m < 8; ++m) sv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
             const float bv = valid ? a.B[prw] : zha_neg_inf();
+            const float ts = PF == 2 && valid ? tau * a.SC[prw] : tau;    // the scale is a power of two
             zha_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -333,7 +353,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
             }
             // lane holds heads 4kq+i against plane j
 #pragma unroll
-            for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], fmaf(tau, acc[i], bv));
+            for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], fmaf(ts, acc[i], bv));
         }
         // max over the planes of one candidate (adjacent columns)
         if (span == 16) {
@@ -409,41 +429,41 @@ __device__ __forceinline__ void block_head_max(const ZhaLevelArgs& a, int g, int
 }
 
 // grid (blocks, H_kv), 256 threads: one level's candidate scores.
-template <bool BF16, bool P16>
+template <bool BF16, int PF>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const void* __restrict__ q,
                                                                         ZhaLevelArgs a, int G, int c, int R,
                                                                         float tau) {
     const int g = blockIdx.y;
     float hm[4];
-    score_level<BF16, false, false, P16>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm);
+    score_level<BF16, false, false, PF>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm);
     if (a.hblk) block_head_max(a, g, G, hm);
 }
 
 // As zha_route_score_kernel, for a level whose parent level (pa) was selected but
 // not merged: the workgroups derive and write that level's kept list themselves
 // (dynamic LDS: zha_defer_lds_bytes).
-template <bool BF16, bool P16>
+template <bool BF16, int PF>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_defer_kernel(const void* __restrict__ q,
                                                                               ZhaLevelArgs a, ZhaLevelArgs pa,
                                                                               int G, int c, int R, float tau) {
     ZHA_LEVEL_ARGS_READY(pa, "s"(G));
     const int g = blockIdx.y;
     float hm[4];
-    score_level<BF16, false, true, P16>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm, &pa);
+    score_level<BF16, false, true, PF>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm, &pa);
     if (a.hblk) block_head_max(a, g, G, hm);
 }
 
 // grid (max blocks, H_kv, levels), 256 threads: every node of each of the first
 // routed levels scored for every head of the group, positions = node ids (the
 // levels' selection then gathers its candidates' scores from these).
-template <bool BF16, bool P16>
+template <bool BF16, int PF>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_all_kernel(const void* __restrict__ q,
                                                                             ZhaChainArgs m, int G, int c, int R,
                                                                             float tau) {
     const int z = blockIdx.z;
     if ((int)blockIdx.x >= m.blocks[z]) return;
     float hm[4];
-    score_level<BF16, true, false, P16>(q, m.lv[z], G, c, R, tau, blockIdx.y, blockIdx.x, m.blocks[z], hm);
+    score_level<BF16, true, false, PF>(q, m.lv[z], G, c, R, tau, blockIdx.y, blockIdx.x, m.blocks[z], hm);
 }
 
 // ---- selection helpers
@@ -1826,30 +1846,39 @@ size_t zha_defer_lds_bytes(int G, int64_t n) {
     return sizeof(uint64_t) * (size_t)(G + 1) * wc + sizeof(uint32_t) * wc;
 }
 
-// A launch of kernel template K<bf16 q, bf16 planes> picked by the cache and plane formats.
-#define ZHA_SCORE_LAUNCH(K, grid, lds, stream, p16, ...)                                                   \
+// A launch of kernel template K<bf16 q, plane format> picked by the cache and plane formats.
+#define ZHA_SCORE_LAUNCH_PF(K, BQ, grid, lds, stream, pf, ...)                                              \
     do {                                                                                                     \
-        if (kv_dtype == 0 && p16)                                                                            \
-            hipLaunchKernelGGL((K<true, true>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);       \
-        else if (kv_dtype == 0)                                                                              \
-            hipLaunchKernelGGL((K<true, false>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);      \
-        else if (p16)                                                                                        \
-            hipLaunchKernelGGL((K<false, true>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);      \
+        if (pf == 2)                                                                                         \
+            hipLaunchKernelGGL((K<BQ, 2>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);             \
+        else if (pf == 1)                                                                                    \
+            hipLaunchKernelGGL((K<BQ, 1>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);             \
         else                                                                                                 \
-            hipLaunchKernelGGL((K<false, false>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);     \
+            hipLaunchKernelGGL((K<BQ, 0>), grid, dim3(kScoreThreads), lds, stream, __VA_ARGS__);             \
     } while (0)
+#define ZHA_SCORE_LAUNCH(K, grid, lds, stream, pf, ...)                                                    \
+    do {                                                                                                     \
+        if (kv_dtype == 0)                                                                                   \
+            ZHA_SCORE_LAUNCH_PF(K, true, grid, lds, stream, pf, __VA_ARGS__);                                \
+        else                                                                                                 \
+            ZHA_SCORE_LAUNCH_PF(K, false, grid, lds, stream, pf, __VA_ARGS__);                               \
+    } while (0)
+
+// The plane format a level's arguments ask for: 2 with an 8-bit copy, 1 with a
+// bfloat16 copy, else 0 (the float32 planes).
+static int plane_format_of(const ZhaLevelArgs& a) { return a.S8 ? 2 : a.S16 ? 1 : 0; }
 
 hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArgs& a, int H_kv, int G, int c,
                                   int R, float tau, int blocks, hipStream_t stream, const ZhaLevelArgs* defer) {
     dim3 grid((unsigned)blocks, (unsigned)H_kv);
-    const bool p16 = a.S16 != nullptr;
+    const int pf = plane_format_of(a);
     if (defer) {
         if (a.top || !defer->top || defer->n_top > ZHA_CHAIN_SLOTS) return hipErrorInvalidValue;
         const size_t lds = zha_defer_lds_bytes(G, defer->n_top);
-        ZHA_SCORE_LAUNCH(zha_route_score_defer_kernel, grid, lds, stream, p16, q, a, *defer, G, c, R, tau);
+        ZHA_SCORE_LAUNCH(zha_route_score_defer_kernel, grid, lds, stream, pf, q, a, *defer, G, c, R, tau);
         return hipGetLastError();
     }
-    ZHA_SCORE_LAUNCH(zha_route_score_kernel, grid, 0, stream, p16, q, a, G, c, R, tau);
+    ZHA_SCORE_LAUNCH(zha_route_score_kernel, grid, 0, stream, pf, q, a, G, c, R, tau);
     return hipGetLastError();
 }
 
@@ -1858,8 +1887,8 @@ hipError_t zha_launch_score_all(int kv_dtype, const void* q, const ZhaChainArgs&
     int bmax = 1;
     for (int i = 0; i < m.n; ++i) bmax = std::max(bmax, m.blocks[i]);
     const dim3 grid((unsigned)bmax, (unsigned)H_kv, (unsigned)m.n);
-    const bool p16 = m.lv[0].S16 != nullptr;
-    ZHA_SCORE_LAUNCH(zha_route_score_all_kernel, grid, 0, stream, p16, q, m, G, c, R, tau);
+    const int pf = plane_format_of(m.lv[0]);
+    ZHA_SCORE_LAUNCH(zha_route_score_all_kernel, grid, 0, stream, pf, q, m, G, c, R, tau);
     return hipGetLastError();
 }
 

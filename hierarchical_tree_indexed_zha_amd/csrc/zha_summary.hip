@@ -497,6 +497,52 @@ __global__ __launch_bounds__(256) void zha_planes16_kernel(const float* __restri
     }
 }
 
+// grid (blocks, H_kv), 256 threads: the router's 8-bit copy of the planes s of
+// nodes [first, first + n), one wave per plane (R per node), two elements per lane.
+// Per plane: k, the exponent of the smallest power of two with max_d |s_d| <= 448
+// 2^k (k >= -126; 0 for an all-zero plane), SC <- 2^k, and S8 <- the FP8 E4M3
+// codes (sign, 4 exponent bits of bias 7, 3 mantissa bits, subnormals below 2^-6,
+// largest 448) of s_d / 2^k, rounded to nearest, ties to even.
+__device__ __forceinline__ int fp8_scale_exp(float m) {
+    if (m == 0.f) return 0;
+    const uint32_t u = __float_as_uint(m);
+    const int e = (int)((u >> 23) & 0xFFu) - 127;              // m = 1.f 2^e
+    const int k = (u & 0x7FFFFFu) <= 0x600000u ? e - 8 : e - 7;  // 1.f <= 1.75: 448 2^(e-8) >= m
+    return k < -126 ? -126 : k;
+}
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float x) {     // |x| <= 448
+    const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);          // spacing 2^-9; 8 is the smallest normal
+    } else {
+        const uint32_t u = __float_as_uint(a);
+        const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);    // three mantissa bits, ties to even
+        code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    }
+    return sgn | code;
+}
+__global__ __launch_bounds__(256) void zha_planes8_kernel(const float* __restrict__ S, uint8_t* __restrict__ S8,
+                                                         float* __restrict__ SC, int64_t cap, int R, int64_t first,
+                                                         int64_t n) {
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const size_t p0 = ((size_t)g * (size_t)cap + (size_t)first) * (size_t)R;
+    const size_t np = (size_t)n * (size_t)R;
+    for (size_t i = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < np; i += (size_t)gridDim.x * 4) {
+        const size_t p = p0 + i;
+        const float2 v = reinterpret_cast<const float2*>(S + p * ZHA_D)[lane];
+        float m = fmaxf(fabsf(v.x), fabsf(v.y));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const int k = fp8_scale_exp(m);
+        const uint32_t lo = f32_to_e4m3_rne(ldexpf(v.x, -k)), hi = f32_to_e4m3_rne(ldexpf(v.y, -k));
+        reinterpret_cast<uint16_t*>(S8 + p * ZHA_D)[lane] = (uint16_t)(lo | (hi << 8));
+        if (lane == 0) SC[p] = ldexpf(1.0f, k);
+    }
+}
+
 // grid (H_kv), 128 threads: row `row` of K and V <- k_new, v_new.
 template <typename T>
 __global__ void zha_kv_write_kernel(T* __restrict__ K, T* __restrict__ V, const T* __restrict__ kn,
@@ -571,6 +617,16 @@ hipError_t zha_launch_planes16(const float* S, uint16_t* S16, int H_kv, int64_t 
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(zha_planes16_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(256), 0, stream, S, S16, cap,
                        R, first, n);
+    return hipGetLastError();
+}
+
+hipError_t zha_launch_planes8(const float* S, uint8_t* S8, float* SC, int H_kv, int64_t cap, int R, int64_t first,
+                              int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n * R + 3) / 4;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(zha_planes8_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(256), 0, stream, S, S8, SC,
+                       cap, R, first, n);
     return hipGetLastError();
 }
 

@@ -150,9 +150,19 @@ class ZhaLayer:
         """The router's bfloat16 copy of level `level`'s planes s [H][n_cap][R][d] (plane_format bf16)."""
         o = B.zha_tree_level_offsets(self.cfg, level)
         if o["s16"] < 0:
-            raise ValueError("the tree keeps no bfloat16 planes (plane_format is float32)")
+            raise ValueError("the tree keeps no bfloat16 planes (plane_format is not bf16)")
         H, R, d, n = self.cfg.n_kv_heads, self.cfg.n_ref, self.cfg.head_dim, o["n_cap"]
         return self._view(self.tree, o["s16"], torch.bfloat16, (H, n, R, d))
+
+    def tree_level8(self, level: int):
+        """The router's 8-bit copy of level `level`'s planes s (plane_format fp8): the FP8
+        E4M3 codes uint8 [H][n_cap][R][d] and the per-plane scales float32 [H][n_cap][R]."""
+        o = B.zha_tree_level_offsets(self.cfg, level)
+        if o["s8"] < 0:
+            raise ValueError("the tree keeps no 8-bit planes (plane_format is not fp8)")
+        H, R, d, n = self.cfg.n_kv_heads, self.cfg.n_ref, self.cfg.head_dim, o["n_cap"]
+        return (self._view(self.tree, o["s8"], torch.uint8, (H, n, R, d)),
+                self._view(self.tree, o["sc"], torch.float32, (H, n, R)))
 
     def fidelity(self, q: torch.Tensor) -> torch.Tensor:
         """Router fidelity of the step the last decode(q) ran (same q, same n_tokens): float32

@@ -81,15 +81,20 @@ typedef struct zha_config {
                           * is valid but not implemented (ZHA_ERR_UNSUPPORTED); other values
                           * are ZHA_ERR_ARG */
     int32_t plane_format;/* format of the planes s the router reads: ZHA_PLANES_F32 (0, the
-                          * float32 planes themselves) or ZHA_PLANES_BF16 (1, a bfloat16 copy
-                          * of them, round-to-nearest-even, kept beside the float32 planes
-                          * that the tree's merges use; b stays float32).  Page "ZHA
-                          * 用树形稀疏注意力改造现有大模型", section 几百倍加速 (a narrow-format
-                          * router variant). */
+                          * float32 planes themselves), ZHA_PLANES_BF16 (1, a bfloat16 copy
+                          * of them, round-to-nearest-even) or ZHA_PLANES_FP8 (2, an 8-bit
+                          * copy: per plane a power-of-two scale 2^k, the smallest with
+                          * max_d |s_d| <= 448 * 2^k (k >= -126), and the FP8 E4M3 codes
+                          * (sign, 4 exponent bits of bias 7, 3 mantissa bits, subnormals,
+                          * largest 448) of s_d / 2^k rounded to nearest even).  Narrow
+                          * copies sit beside the float32 planes that the tree's merges use;
+                          * b stays float32.  Page "ZHA 用树形稀疏注意力改造现有大模型",
+                          * section 几百倍加速 (a narrow-format router variant). */
 } zha_config;
 
 #define ZHA_PLANES_F32  0
 #define ZHA_PLANES_BF16 1
+#define ZHA_PLANES_FP8  2
 
 typedef struct zha_buffers {
     void*        k;        /* device K [H_kv][capacity][d] */
@@ -105,7 +110,8 @@ int zha_check_config(const zha_config* cfg);
 /* Bytes of summary storage for a tree over `capacity` tokens (0 if cfg is invalid).
  * Per level l and KV head: float32 planes s[n][R][d], b[n][R] and log-sum-exp
  * lse[n][R] for n < capacity / c^l, and with plane_format = ZHA_PLANES_BF16 a
- * bfloat16 copy of s. */
+ * bfloat16 copy of s, with ZHA_PLANES_FP8 an 8-bit copy of s and its per-plane
+ * float32 scales. */
 size_t zha_tree_bytes(const zha_config* cfg);
 
 /* Bytes of decode scratch (0 if cfg is invalid): candidate scores and kept
@@ -122,11 +128,15 @@ size_t zha_dense_scratch_bytes(const zha_config* cfg);
  *   lse float32 [H_kv][n_cap][R]
  *   s16 bfloat16 [H_kv][n_cap][R][d], the router's copy of s when plane_format is
  *       ZHA_PLANES_BF16 (*s16_off = -1 otherwise)
+ *   s8  uint8 [H_kv][n_cap][R][d] FP8 E4M3 codes and
+ *   sc  float32 [H_kv][n_cap][R] their per-plane scales (powers of two), the router's
+ *       8-bit copy of s when plane_format is ZHA_PLANES_FP8 (*s8_off = *sc_off = -1
+ *       otherwise)
  * with n_cap = capacity / c^level.  Any output pointer may be NULL.  Host-only;
  * ZHA_OK or ZHA_ERR_ARG. */
 int zha_tree_level_offsets(const zha_config* cfg, int32_t level,
                            int64_t* s_off, int64_t* b_off, int64_t* lse_off, int64_t* n_cap,
-                           int64_t* s16_off);
+                           int64_t* s16_off, int64_t* s8_off, int64_t* sc_off);
 
 /* Where a decode step over n_tokens tokens leaves its routing of level `level`
  * inside `scratch` (byte offsets; host-only).  `chained` tells which layout holds:
@@ -192,12 +202,14 @@ typedef struct zha_stats {
     int64_t group_kept[ZHA_STATS_MAX_LEVELS];        /* nodes kept by some head of a group, summed over groups */
     int64_t bytes_read[ZHA_STATS_MAX_LEVELS];        /* summary bytes the level's routing needs:
                                                         group_cand * n_ref * (head_dim * e + 4), e = 4
-                                                        (float32 planes) or 2 (ZHA_PLANES_BF16) */
+                                                        (float32 planes) or 2 (ZHA_PLANES_BF16); with
+                                                        ZHA_PLANES_FP8 group_cand * n_ref * (head_dim + 8)
+                                                        (codes, scale and b) */
     int64_t bytes_streamed[ZHA_STATS_MAX_LEVELS];    /* summary bytes the kernels streamed for the level:
                                                         equal to bytes_read, except at the small top levels
                                                         whose every complete node is scored ahead of their
-                                                        selection (then n_nodes * n_kv_heads * n_ref *
-                                                        (head_dim * e + 4)) */
+                                                        selection (then n_nodes * n_kv_heads times the
+                                                        same bytes per node) */
     int64_t gather_tokens;                           /* distinct tokens attended, summed over KV groups */
     int64_t gather_bytes;                            /* K and V bytes those tokens occupy */
 } zha_stats;

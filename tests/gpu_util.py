@@ -23,6 +23,9 @@ ATOL = 2e-2
 # up to tau |q_d| 2**-7 |s_d| for such an element (about 1e-3 for one flip at these
 # sizes), so cuts closer than this to changing are either side's.
 NARROW_MARGIN = 1e-2
+# With 8-bit planes a flipped element moves a score by up to tau |q_d| 2**-3 |s_d|
+# (one E4M3 spacing), about ten times the bfloat16 figure.
+FP8_MARGIN = 3e-2
 # Routing checks on the GPU's own candidate sets: scores (relative to 1 + |sigma|),
 # cumulative mass, and the ordering of kept vs dropped probabilities.  fp32 scores
 # and sums carry ~1e-6 relative error.
@@ -55,21 +58,41 @@ def make_layer(w: W.Workload, device="cuda", seed=None, top_p=None, capacity=Non
 
 def oracle_tree(layer: ZhaLayer, n_tokens: int, keys_host=None):
     kh = to_host(layer.k) if keys_host is None else keys_host
-    fmt = "bf16" if layer.cfg.plane_format == B.PLANE_FORMATS["bf16"] else "f32"
+    fmt = {v: k for k, v in B.PLANE_FORMATS.items()}[layer.cfg.plane_format]
     return kh, O.SummaryTree(kh, to_host(layer.ref_q), n_tokens, layer.cfg.chunk, layer.cfg.levels, plane_format=fmt)
 
 
+PLANE_REL = 2e-5   # the GPU's float32 planes against the oracle's, relative to the plane's largest element
+
+
 def narrow_tolerance(q, s, tree) -> np.ndarray:
-    """Per candidate, how far the GPU's score may sit from the oracle's when the router
-    reads bfloat16 planes: the GPU rounds its float32 planes, the oracle its float64
-    ones, and where the two straddle a rounding boundary they land one bfloat16
-    spacing apart (at most 2**-7 |s_d|); the score moves by tau |q_d| times that.
-    Summed over d and maximised over planes, as the worst case of every element
-    flipping.  Zero for float32 planes."""
-    if getattr(tree, "plane_format", "f32") != "bf16" or s is None or len(s) == 0:
+    """s: the candidates' exact (unrounded) planes.  Per candidate, how far the GPU's score may sit from the oracle's when the router
+    reads narrow planes.  The GPU rounds its float32 planes, the oracle its float64
+    ones; they differ by at most PLANE_REL times the plane's largest element (the
+    tree summaries' bar), and rounding is monotone, so the GPU's narrow element lies
+    between the roundings of the two ends of that interval, as does the oracle's: the
+    width of that bracket is the element's possible difference (zero unless the
+    element sits next to a rounding boundary).  For 8-bit planes whose scale could
+    differ between the two ends, every element may move by a spacing at the coarser
+    scale (at most 2**-3 |s_d|, or 2**-9 times the scale below the smallest normal).
+    The score moves by tau sum_d |q_d| times those differences, maximised over
+    planes.  Zero for float32 planes."""
+    fmt = getattr(tree, "plane_format", "f32")
+    if fmt == "f32" or s is None or len(s) == 0:
         return np.zeros(0 if s is None else len(s))
     qa = np.abs(O.widen(q))
-    return tree.tau * (qa[None, None, :] * np.abs(s) * 2.0 ** -7).sum(-1).max(-1)
+    m = np.abs(s).max(axis=-1, keepdims=True) * PLANE_REL
+    lo, hi = s - m, s + m
+    if fmt == "bf16":
+        step = np.abs(O.round_bf16(hi) - O.round_bf16(lo))
+    else:
+        m0 = np.abs(s).max(axis=-1)
+        k0 = O.fp8_plane_scale_exp(m0[..., None] * (1 - PLANE_REL))
+        k1 = O.fp8_plane_scale_exp(m0[..., None] * (1 + PLANE_REL))
+        step = np.abs(O.round_fp8(hi, k0) - O.round_fp8(lo, k0))
+        loose = np.maximum(np.abs(s) * 2.0 ** -3, np.ldexp(1.0, k1[..., None] - 8))
+        step = np.where((k0 != k1)[..., None], loose, step)
+    return tree.tau * (qa[None, None, :] * step).sum(-1).max(-1)
 
 
 def _kept_by_head(route, g, G):
@@ -124,6 +147,8 @@ def check_routing(layer: ZhaLayer, qh, n_tokens: int, tree: O.SummaryTree, p: fl
             sig = r["sigma"][g, :, :len(nodes)].numpy().astype(np.float64)
             kept_h = _kept_by_head(r, g, G)
             s_all, b_all = tree.router_planes(lv, tg, nodes) if len(nodes) else (None, None)
+            # the exact planes, around which the narrow copies' rounding is bracketed
+            s_ex = tree.get(lv, tg, nodes)[0] if len(nodes) and tree.plane_format != "f32" else s_all
             for hl in range(G):
                 h = g * G + hl
                 is_c = sig[hl] > -np.inf
@@ -142,7 +167,7 @@ def check_routing(layer: ZhaLayer, qh, n_tokens: int, tree: O.SummaryTree, p: fl
                     assert len(kept) == 0
                     continue
                 so = O.plane_scores(qh[h], s_all[is_c], b_all[is_c], tree.tau)
-                tol = narrow_tolerance(qh[h], s_all[is_c], tree)     # 0 for float32 planes
+                tol = narrow_tolerance(qh[h], s_ex[is_c], tree)      # 0 for float32 planes
                 err = float((np.maximum(np.abs(sig[hl][is_c] - so) - tol, 0.0) / (1.0 + np.abs(so))).max())
                 worst = max(worst, err)
                 assert err <= SCORE_RTOL, f"{label} level {lv} head {h}: score error {err:.3g}"
@@ -201,7 +226,7 @@ def compare_decode(layer: ZhaLayer, x_q: torch.Tensor, n_tokens: int, tree: O.Su
     n_exact = n_ambiguous = 0
     if heads is None:
         heads = range(layer.cfg.n_q_heads) if groups is None else [g * G + j for g in groups for j in range(G)]
-    margin_bar = MARGIN if getattr(tree, "plane_format", "f32") != "bf16" else NARROW_MARGIN
+    margin_bar = {"bf16": NARROW_MARGIN, "fp8": FP8_MARGIN}.get(getattr(tree, "plane_format", "f32"), MARGIN)
     for h in heads:
         tg = h // G if groups is None else list(groups).index(h // G)
         r = O.route_head(qh[h], tree, tg, p)
@@ -285,7 +310,10 @@ def check_sel_stats(layer: ZhaLayer, sel: torch.Tensor, stats: torch.Tensor, n_t
             assert got_sel[h] == r.kept_leaves().tolist(), f"{label} head {h}: sel vs oracle leaves"
             toks = O.final_token_set(np.array(got_sel[h], dtype=np.int64), n_tokens, c)
             assert toks.tolist() == r.tokens.tolist(), f"{label} head {h}: token set vs oracle"
-    plane = R * (d * (2 if cfg.plane_format == B.PLANE_FORMATS["bf16"] else 4) + 4)
+    if cfg.plane_format == B.PLANE_FORMATS["fp8"]:
+        plane = R * (d + 8)                     # codes, the plane's scale and b
+    else:
+        plane = R * (d * (2 if cfg.plane_format == B.PLANE_FORMATS["bf16"] else 4) + 4)
     e_kv = 2 if cfg.kv_dtype == B.ZHA_BF16 else 4
     for lv in range(1, B.STATS_MAX_LEVELS + 1):
         i = lv - 1

@@ -59,6 +59,8 @@ def _cfg(**kw):
     (dict(sink=0), B.ZHA_ERR_UNSUPPORTED),
     (dict(sink=2), B.ZHA_ERR_ARG),
     (dict(sink=-1), B.ZHA_ERR_ARG),
+    (dict(plane_format=3), B.ZHA_ERR_ARG),
+    (dict(plane_format=-1), B.ZHA_ERR_ARG),
 ])
 def test_config_validation(kw, code):
     with pytest.raises(B.ZhaError) as e:
@@ -84,9 +86,29 @@ def test_valid_configs_pass_and_sizes_match_layout():
         assert B.zha_sel_bytes(cfg) == 4 * w.n_q_heads * (w.capacity // w.chunk + 1)
         o = B.zha_tree_level_offsets(cfg, w.levels)
         assert o["n_cap"] == w.capacity // w.chunk ** w.levels
+        assert o["s16"] == o["s8"] == o["sc"] == -1
         r = B.zha_route_level_offsets(cfg, w.n_tokens, 1)
         assert r["n_cap"] == w.capacity // w.chunk
         assert max(r["n_cand"], r["sigma"], r["kept"], r["mask"], r["stats"]) < B.zha_scratch_bytes(cfg)
+
+
+def test_narrow_plane_layouts():
+    """bf16 planes add a [H][n][R][d] 2-byte copy per level; 8-bit planes a 1-byte copy
+    and a float32 scale per plane, each 256-byte aligned after the float32 pieces."""
+    w = W.get("light")
+    base = B.zha_tree_bytes(B.config_of(w))
+    al = lambda x: (x + 255) // 256 * 256
+    extra16 = extra8 = 0
+    for lv in range(1, w.levels + 1):
+        n = w.capacity // w.chunk ** lv
+        extra16 += al(2 * w.n_kv_heads * n * w.n_ref * w.head_dim)
+        extra8 += al(w.n_kv_heads * n * w.n_ref * w.head_dim) + al(4 * w.n_kv_heads * n * w.n_ref)
+    c16, c8 = B.config_of(w, plane_format="bf16"), B.config_of(w, plane_format="fp8")
+    assert B.zha_tree_bytes(c16) == base + extra16
+    assert B.zha_tree_bytes(c8) == base + extra8
+    o16, o8 = B.zha_tree_level_offsets(c16, 1), B.zha_tree_level_offsets(c8, 1)
+    assert o16["s16"] > o16["lse"] and o16["s8"] == o16["sc"] == -1
+    assert o8["s16"] == -1 and o8["lse"] < o8["s8"] < o8["sc"] and o8["s8"] % 256 == 0 and o8["sc"] % 256 == 0
 
 
 def test_entry_points_reject_bad_arguments_before_touching_the_device():

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle as O
+from hierarchical_tree_indexed_zha_amd import binding as B
 from hierarchical_tree_indexed_zha_amd import workloads as W
 from tests.gpu_util import compare_decode, make_layer, oracle_tree, say, to_host
 
@@ -92,54 +93,71 @@ PLANE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,w", PLANE_CASES, ids=[c[0] for c in PLANE_CASES])
-def test_bf16_planes_decode_matches_oracle(name, w):
-    say(f"[planes16] {name}")
-    layer, x = make_layer(w, plane_format="bf16")
-    n = w.n_tokens
-    layer.build(n)
-    torch.cuda.synchronize()
-    # the router copy is the round-to-nearest-even of the float32 planes, bit for bit
-    for lv in range(1, w.levels + 1):
-        nn = n // w.chunk ** lv
+def check_narrow_copy(layer, n, label):
+    """The router's narrow copy of every level's complete nodes, bit for bit: bfloat16
+    is torch's round-to-nearest-even of the float32 planes; the 8-bit copy is, per
+    plane, the power-of-two scale 2^k with the largest element in (224, 448] (k >=
+    -126) and torch's float8_e4m3fn conversion of the planes divided by it."""
+    cfg = layer.cfg
+    for lv in range(1, cfg.levels + 1):
+        nn = n // cfg.chunk ** lv
         if nn == 0:
             continue
         s32 = layer.tree_level(lv)[0][:, :nn]
-        s16 = layer.tree_level16(lv)[:, :nn]
-        assert torch.equal(s16.view(torch.int16), s32.to(torch.bfloat16).view(torch.int16)), f"{name} level {lv}"
+        if cfg.plane_format == B.PLANE_FORMATS["bf16"]:
+            s16 = layer.tree_level16(lv)[:, :nn]
+            assert torch.equal(s16.view(torch.int16), s32.to(torch.bfloat16).view(torch.int16)), f"{label} level {lv}"
+        else:
+            s8, sc = layer.tree_level8(lv)
+            s8, sc = s8[:, :nn], sc[:, :nn]
+            m = s32.abs().amax(dim=-1)
+            f, e = torch.frexp(m)
+            k = torch.where(f <= 0.875, e - 9, e - 8).clamp(min=-126)
+            k = torch.where(m == 0, torch.zeros_like(k), k)
+            assert torch.equal(sc, torch.ldexp(torch.ones_like(m), k.float())), f"{label} level {lv}: scales"
+            ref = torch.ldexp(s32, -k.float()[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+            assert torch.equal(s8, ref), f"{label} level {lv}: codes ({int((s8 != ref).sum())} differ)"
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("name,w", PLANE_CASES, ids=[c[0] for c in PLANE_CASES])
+def test_narrow_planes_decode_matches_oracle(name, w, fmt):
+    say(f"[planes] {name} {fmt}")
+    layer, x = make_layer(w, plane_format=fmt)
+    n = w.n_tokens
+    layer.build(n)
+    torch.cuda.synchronize()
+    check_narrow_copy(layer, n, f"{name} {fmt}")
     kh, tree = oracle_tree(layer, n)
     vh = to_host(layer.v)
-    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label=f"{name} bf16 planes")
-    say(f"[planes16] {name}: exempt heads {ex}/{w.n_q_heads}, attention err {err:.2e}, score err {es:.2e}")
+    ex, err, es = compare_decode(layer, x["q"][0], n, tree, kh, vh, w.top_p, label=f"{name} {fmt} planes")
+    say(f"[planes] {name} {fmt}: exempt heads {ex}/{w.n_q_heads}, attention err {err:.2e}, score err {es:.2e}")
 
 
-def test_bf16_planes_follow_appends():
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_narrow_planes_follow_appends(fmt):
     """Appends that complete leaves and parents refresh the router copy as well."""
     w = _w("light", 4096 - 3, levels=3, steps=80)
-    layer, x = make_layer(w, plane_format="bf16")
+    layer, x = make_layer(w, plane_format=fmt)
     layer.build(w.n_tokens)
     for t in range(70):
         layer.append(x["k_app"][t], x["v_app"][t])
     torch.cuda.synchronize()
     n = layer.n_tokens
-    for lv in range(1, w.levels + 1):
-        nn = n // w.chunk ** lv
-        s32 = layer.tree_level(lv)[0][:, :nn]
-        s16 = layer.tree_level16(lv)[:, :nn]
-        assert torch.equal(s16.view(torch.int16), s32.to(torch.bfloat16).view(torch.int16)), f"level {lv}"
+    check_narrow_copy(layer, n, f"{fmt} after appends")
     kh, tree = oracle_tree(layer, n)
-    compare_decode(layer, x["q"][1], n, tree, kh, to_host(layer.v), w.top_p, label="bf16 planes after appends")
+    compare_decode(layer, x["q"][1], n, tree, kh, to_host(layer.v), w.top_p, label=f"{fmt} planes after appends")
 
 
-def test_bf16_planes_drift_and_captured_mass():
-    """The narrow router against the float32 one on the same cache and queries: the
+def test_narrow_planes_drift_and_captured_mass():
+    """The narrow routers against the float32 one on the same cache and queries: the
     share of heads whose leaf sets differ, and the captured attention mass of each
     (reported; averaged over heads and steps the bfloat16 router must capture within
-    0.02 of the float32 one: single heads can swing further, as a cluster near the
-    cut falls on the other side)."""
+    0.02 of the float32 one and the 8-bit router within 0.05: single heads can swing
+    further, as a cluster near the cut falls on the other side)."""
     w = _w("light", 65536, steps=8)
     out = {}
-    for fmt in ("f32", "bf16"):
+    for fmt in ("f32", "bf16", "fp8"):
         layer, x = make_layer(w, plane_format=fmt)
         layer.build(w.n_tokens)
         leaves, caps = [], []
@@ -151,12 +169,14 @@ def test_bf16_planes_drift_and_captured_mass():
             leaves.append(layer.read_sel(sel))
         out[fmt] = (leaves, np.stack(caps))
         del layer
-    same = total = 0
-    for a, b in zip(out["f32"][0], out["bf16"][0]):
-        for ha, hb in zip(a, b):
-            total += 1
-            same += list(ha) == list(hb)
-    c32, c16 = out["f32"][1], out["bf16"][1]
-    say(f"[planes16] drift: leaf sets identical for {same}/{total} (step, head) pairs; captured mass "
-        f"f32 {c32.mean():.4f} bf16 {c16.mean():.4f}, max |diff| {np.abs(c32 - c16).max():.4f}")
-    assert abs(float(c32.mean()) - float(c16.mean())) <= 0.02
+    c32 = out["f32"][1]
+    for fmt, bar in (("bf16", 0.02), ("fp8", 0.05)):
+        same = total = 0
+        for a, b in zip(out["f32"][0], out[fmt][0]):
+            for ha, hb in zip(a, b):
+                total += 1
+                same += list(ha) == list(hb)
+        cn = out[fmt][1]
+        say(f"[planes] {fmt} drift: leaf sets identical for {same}/{total} (step, head) pairs; captured mass "
+            f"f32 {c32.mean():.4f} {fmt} {cn.mean():.4f}, max |diff| {np.abs(c32 - cn).max():.4f}")
+        assert abs(float(c32.mean()) - float(cn.mean())) <= bar, fmt

@@ -126,7 +126,7 @@ def _route_no_orphans(q_h, tree, g, p):
 _orig_fp8_scale = Z.fp8_plane_scale_exp
 
 
-def _fp8_truncate(s):
+def _fp8_truncate(s, k=None):
     s = np.asarray(s, dtype=np.float64)
     k = _orig_fp8_scale(s)[..., None]
     x = np.ldexp(s, -k)
@@ -135,7 +135,7 @@ def _fp8_truncate(s):
     return np.ldexp(np.trunc(np.ldexp(x, -qe)), qe + k)
 
 
-def _fp8_node_scale(s):
+def _fp8_node_scale(s, k=None):
     s = np.asarray(s, dtype=np.float64)
     k = _orig_fp8_scale(s.reshape(s.shape[:-2] + (-1,)) if s.ndim >= 2 else s)
     k = k[..., None, None] if s.ndim >= 2 else k[..., None]
@@ -145,7 +145,7 @@ def _fp8_node_scale(s):
     return np.ldexp(np.round(np.ldexp(x, -qe)), qe + k)
 
 
-def _fp8_no_subnormals(s):
+def _fp8_no_subnormals(s, k=None):
     s = np.asarray(s, dtype=np.float64)
     k = _orig_fp8_scale(s)[..., None]
     x = np.ldexp(s, -k)

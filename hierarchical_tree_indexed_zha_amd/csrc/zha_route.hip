@@ -140,12 +140,14 @@ __device__ __forceinline__ void defer_entry(const DeferView& v, int G, uint32_t 
     mask = defer_mask(v, G, node);
 }
 
-// An FP8 E4M3 code (sign, 4 exponent bits of bias 7, 3 mantissa bits; exponent 0
-// holds the subnormals m 2^-9) as the float32 it stands for, exactly.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-    return (c & 0x80u) ? -mag : mag;
+// Four FP8 E4M3 codes (bytes of w, low first: sign, 4 exponent bits of bias 7, 3
+// mantissa bits, subnormals m 2^-9) as the float32 values they stand for, exactly:
+// gfx950's packed conversion decodes this (OCP) layout.
+typedef float zha_f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 e4m3x4_to_f32(uint32_t w) {
+    const zha_f32x2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const zha_f32x2v hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    return make_float4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // Scores one level's candidates for every head of group g, as workgroup blk of
@@ -320,9 +322,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
 #pragma unroll
                 for (int m = 0; m < 8; ++m) u[m] = plane[4 * m + kq];
 #pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    sv[m] = make_float4(e4m3_to_f32(u[m] & 0xFFu), e4m3_to_f32((u[m] >> 8) & 0xFFu),
-                                        e4m3_to_f32((u[m] >> 16) & 0xFFu), e4m3_to_f32(u[m] >> 24));
+                for (int m = 0; m < 8; ++m) sv[m] = e4m3x4_to_f32(u[m]);
             } else if (valid && PF == 1) {
                 // the router's bfloat16 copy: the same four elements per lane, widened exactly
                 const uint2* plane = reinterpret_cast<const uint2*>(a.S16 + prw * ZHA_D);

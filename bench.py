@@ -407,6 +407,7 @@ def trace_kernels(args, layer, x, w, torch, B):
         layer.decode(q, stats=stats)
         st = layer.read_stats(stats)
         kinds_l = [k for k in kinds]
+        crossed = {lv for k, lv in kinds_l if k == "cross"}
         chain_lv = []
         if any(k == "chain" for k, _ in kinds_l):
             top = kinds_l[0][1]
@@ -429,7 +430,10 @@ def trace_kernels(args, layer, x, w, torch, B):
             elif name == "resolve":
                 byts = 0
             elif name == "apply":
-                byts = st["group_cand"][lv - 1] * G * 4 + st["group_kept"][lv - 1] * 8
+                # the heads' kept bitmaps (G bits per candidate), or with the cross launch
+                # their scores; the kept list written
+                per = G * 4 if lv in crossed else G / 8
+                byts = st["group_cand"][lv - 1] * per + st["group_kept"][lv - 1] * 8
             elif name == "gather":
                 byts = st["gather_bytes"]
             else:

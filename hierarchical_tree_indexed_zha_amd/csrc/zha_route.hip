@@ -1335,14 +1335,29 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
 
     // one round trip: the head's per-block maxima, this workgroup's slice of
     // kSlice positions as one 16-byte load per thread (rows are 16-byte aligned and
-    // padded to whole vectors), and, last, the parent count
+    // padded to whole vectors), with one workgroup per head every position of the
+    // level's capacity (at most kLdsKeys), and, last, the parent count
+    const bool single = gridDim.x == 1;        // the host's choice: every frontier of the level fits the LDS keys
     const float hb = tid < a.score_blocks ? a.hblk[(size_t)h * ZHA_SCORE_MAXB + tid] : zha_neg_inf();
     const int nv_cap = (int)(a.sstride / 4);
-    float4 x = make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
+    constexpr int kVec = kKeyRegs / 4;         // float4 loads per thread of a staged head
+    float4 y[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) y[k] = make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
     {
         const int v = w * (kSlice / 4) + tid;
-        if (v < nv_cap) x = sg4[v];
+        if (v < nv_cap) y[0] = sg4[v];
     }
+    if (single) {
+#pragma unroll
+        for (int k = 1; k < kVec; ++k) {
+            if (k * kBT < nv_cap) {            // uniform: rows wholly past the capacity skipped
+                const int v = tid + k * kBT;
+                if (v < nv_cap) y[k] = sg4[v];
+            }
+        }
+    }
+    float4 x = y[0];
     const int pn = parent_count(a, g);
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
     if (n <= kSmallN) {
@@ -1363,7 +1378,7 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
     const bool keep_all = !none && top_p >= 1.0f;
     const bool cut = !none && !keep_all;
     uint64_t* gm = a.ghist + (size_t)h * kHistBins;
-    if (cut) {
+    if (cut && !single) {
         // the first digit's mass histogram of slices w, w + kSliceW, ..., added into
         // the head's global histogram (integer atomics: exact and order-free)
         s_hist[2 * tid] = 0ull;
@@ -1391,17 +1406,18 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
         }
         zha_wave_mem_wait();                   // this wave's histogram adds have completed
     }
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.hdone[h], 1u) == (uint32_t)(active - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (!single) {
+        __syncthreads();
+        if (tid == 0) s_last = atomicAdd(&a.hdone[h], 1u) == (uint32_t)(active - 1);
+        __syncthreads();
+        if (!s_last) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
 
     // ---- the head's last workgroup: the complete histogram (read past this
     // device's caches) and the head's keys (LDS, 16-byte loads), then the cut
-    const bool staged = n <= kLdsKeys;
+    const bool staged = n <= kLdsKeys;        // (always, with one workgroup per head)
     const bool large = !staged && cut && a.glist != nullptr;
-    uint32_t my_cand = 0;
     if (large) {
         // a frontier beyond the LDS keys: publish the first digit's crossing bin and
         // the mass still needed inside it; the cross and resolve kernels finish
@@ -1419,19 +1435,20 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
     }
     {
         uint64_t hm2[2] = {0ull, 0ull};
-        if (cut) {
+        if (cut && !single) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) hm2[i] = __hip_atomic_load(gm + 2 * tid + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        constexpr int kVec = kKeyRegs / 4;     // float4 loads per thread
-        float4 y[kVec];
         const int nvn = (n + 3) / 4;
+        if (!single) {
+            // the head's keys, read again by its last slice workgroup
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-            y[k] = make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
-            if (staged && k * kBT < nvn) {     // uniform: rows wholly past n skipped
-                const int v = tid + k * kBT;
-                if (v < nvn) y[k] = sg4[v];
+            for (int k = 0; k < kVec; ++k) {
+                y[k] = make_float4(zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf());
+                if (staged && k * kBT < nvn) {     // uniform: rows wholly past n skipped
+                    const int v = tid + k * kBT;
+                    if (v < nvn) y[k] = sg4[v];
+                }
             }
         }
         s_hist[2 * tid] = hm2[0];
@@ -1444,30 +1461,46 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
                     const float v[4] = {y[k].x, y[k].y, y[k].z, y[k].w};
                     uint32_t kk[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        kk[j] = p + j < n ? key_of(v[j], M) : kNotCand;
-                        my_cand += kk[j] != kNotCand;
-                    }
+                    for (int j = 0; j < 4; ++j) kk[j] = p + j < n ? key_of(v[j], M) : kNotCand;
                     *reinterpret_cast<uint4*>(s_keys + p) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
                 }
             }
-        } else {
-            for (int p = tid; p < n; p += kBT) my_cand += key_of(sg[p], M) != kNotCand;
         }
     }
     __syncthreads();
     uint32_t ustar = 0, plim = 0xFFFFFFFFu;
     if (cut) {
-        if (staged) block_cut(LdsKeys{s_keys}, IdPos{}, n, top_p, 0, true, true, s_hist, s_gl, &st, ustar, plim);
+        // (one workgroup per head: block_cut builds the first digit's histogram itself)
+        if (staged) block_cut(LdsKeys{s_keys}, IdPos{}, n, top_p, 0, !single, true, s_hist, s_gl, &st, ustar, plim);
         else block_cut(GlobKeys{sg, M}, IdPos{}, n, top_p, 0, true, true, s_hist, s_gl, &st, ustar, plim);
     }
-    // the head's kept count
-    uint32_t my_kept = 0;
-    const auto count_kept = [&](uint32_t k, int p) { my_kept += kept_by(k, (uint32_t)p, none, keep_all, ustar, plim); };
-    if (staged) sweep_keys(LdsKeys{s_keys}, n, count_kept);
-    else sweep_keys(GlobKeys{sg, M}, n, count_kept);
-    const uint64_t both = zha_readlane_u64(zha_wave_incl_scan_u64(((uint64_t)my_kept << 32) | my_cand), 63);
-    if (lane == 0) s_wred[wave] = both;
+    // the head's kept flags as a bitmap over positions, one word per 64 (read by the
+    // apply), and its kept and candidate counts: wave w takes words w, w + kBW, ...
+    // in batches whose keys are all read before any is used
+    {
+        const int nw = (n + 63) >> 6;
+        uint64_t* hbits = a.kbm + ((size_t)g * G + hl) * (size_t)a.wcap;
+        uint32_t w_kept = 0, w_cand = 0;
+#pragma unroll 1
+        for (int w0 = wave; w0 < nw; w0 += kBW * kSweepB) {   // uniform per wave
+            uint32_t kk[kSweepB];
+#pragma unroll
+            for (int j = 0; j < kSweepB; ++j) {
+                const int p = (w0 + j * kBW) * 64 + lane;
+                kk[j] = kNotCand;
+                if (p < n) kk[j] = staged ? s_keys[p] : key_of(sg[p], M);
+            }
+#pragma unroll
+            for (int j = 0; j < kSweepB; ++j) {
+                const int wd = w0 + j * kBW;
+                const uint64_t bits = __ballot(kept_by(kk[j], (uint32_t)(wd * 64 + lane), none, keep_all, ustar, plim));
+                w_cand += (uint32_t)__popcll(__ballot(kk[j] != kNotCand));
+                w_kept += (uint32_t)__popcll(bits);
+                if (lane == 0 && wd < nw) hbits[wd] = bits;
+            }
+        }
+        if (lane == 0) s_wred[wave] = ((uint64_t)w_kept << 32) | w_cand;
+    }
     __syncthreads();
     if (tid == 0) {
         uint64_t t = 0;
@@ -1700,7 +1733,7 @@ __global__ __launch_bounds__(kBT) void zha_resolve_kernel(ZhaLevelArgs a, int G,
     }
 }
 
-template <int kApplyThreads>
+template <int kApplyThreads, bool BITS>
 __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a, int G, int c) {
     constexpr int kApplyWaves = kApplyThreads / 64;
     constexpr int kApplyChunk = 4 * kApplyThreads;    // positions per apply workgroup (four per thread)
@@ -1720,43 +1753,67 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
     __syncthreads();
     const int ci = (int)s_ticket;
     if (ci >= nch) return;
-    // the heads' cuts (to LDS, one thread each) and the chunk's scores, positions
-    // p0 .. p0 + 3 of this thread for every head as one 16-byte load each (rows are
-    // 16-byte aligned; the vector holding position n - 1 may run past n, never past
-    // the row), all in flight together; scores of heads beyond G come from a valid
-    // row and are masked afterwards
-    const HeadCut mine = reinterpret_cast<const HeadCut*>(a.hcut)[(size_t)g * G + (tid < G ? tid : 0)];
     const int p0 = ci * kApplyChunk + 4 * tid;
-    const int pv = p0 < n ? p0 : 0;
-    float4 x[ZHA_MAX_GROUP];
-#pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
-        x[hh] = *reinterpret_cast<const float4*>(a.sig + ((size_t)g * G + (hh < G ? hh : 0)) * a.sstride + pv);
-    // the parents' kept entries of the thread's positions, in the same round trip
     const int pnc = a.top ? 0 : pn * c;
     int32_t pk[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int p = p0 + j;
-        pk[j] = 0;
-        if (p < pnc) pk[j] = a.pklist[(size_t)g * a.pcap + zha_div((uint32_t)p, a.dc)];
-    }
-    if (tid < G) s_hc[tid] = mine;
-    __syncthreads();
-    // every head's cut read from LDS at once, then the masks without branches
-    HeadCut hcs[ZHA_MAX_GROUP];
-#pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hcs[hh] = s_hc[hh < G ? hh : 0];
     uint32_t msk[4] = {0u, 0u, 0u, 0u};
+    if constexpr (BITS) {
+        // the heads' kept bitmaps over positions (written by the select kernel): bits
+        // p0 .. p0 + 3 of word p0 / 64 of every head, with the parents' kept entries
+        // of the thread's positions, in one round trip
+        const int wd = (p0 < n ? p0 : 0) >> 6;
+        uint64_t hw[ZHA_MAX_GROUP];
 #pragma unroll
-    for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
-        const HeadCut& hc = hcs[hh];
-        const float v[4] = {x[hh].x, x[hh].y, x[hh].z, x[hh].w};
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+            hw[hh] = 0ull;
+            if (hh < G) hw[hh] = a.kbm[((size_t)g * G + hh) * (size_t)a.wcap + wd];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t key = p0 + j < n ? key_of(v[j], hc.m) : kNotCand;
-            const bool k = (hh < G) & kept_by(key, (uint32_t)(p0 + j), hc.mode == 2u, hc.mode == 1u, hc.ustar, hc.plim);
-            msk[j] |= (uint32_t)k << hh;
+            const int p = p0 + j;
+            pk[j] = 0;
+            if (p < pnc) pk[j] = a.pklist[(size_t)g * a.pcap + zha_div((uint32_t)p, a.dc)];
+        }
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                msk[j] |= (uint32_t)(p0 + j < n ? (hw[hh] >> ((p0 + j) & 63)) & 1ull : 0ull) << hh;
+    } else {
+        // the heads' cuts (to LDS, one thread each) and the chunk's scores, positions
+        // p0 .. p0 + 3 of this thread for every head as one 16-byte load each (rows are
+        // 16-byte aligned; the vector holding position n - 1 may run past n, never past
+        // the row), all in flight together; scores of heads beyond G come from a valid
+        // row and are masked afterwards
+        const HeadCut mine = reinterpret_cast<const HeadCut*>(a.hcut)[(size_t)g * G + (tid < G ? tid : 0)];
+        const int pv = p0 < n ? p0 : 0;
+        float4 x[ZHA_MAX_GROUP];
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+            x[hh] = *reinterpret_cast<const float4*>(a.sig + ((size_t)g * G + (hh < G ? hh : 0)) * a.sstride + pv);
+        // the parents' kept entries of the thread's positions, in the same round trip
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = p0 + j;
+            pk[j] = 0;
+            if (p < pnc) pk[j] = a.pklist[(size_t)g * a.pcap + zha_div((uint32_t)p, a.dc)];
+        }
+        if (tid < G) s_hc[tid] = mine;
+        __syncthreads();
+        // every head's cut read from LDS at once, then the masks without branches
+        HeadCut hcs[ZHA_MAX_GROUP];
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hcs[hh] = s_hc[hh < G ? hh : 0];
+#pragma unroll
+        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+            const HeadCut& hc = hcs[hh];
+            const float v[4] = {x[hh].x, x[hh].y, x[hh].z, x[hh].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = p0 + j < n ? key_of(v[j], hc.m) : kNotCand;
+                const bool k = (hh < G) & kept_by(key, (uint32_t)(p0 + j), hc.mode == 2u, hc.mode == 1u, hc.ustar, hc.plim);
+                msk[j] |= (uint32_t)k << hh;
+            }
         }
     }
     // the chunk's kept positions in order (4 per thread, thread-major): this
@@ -1907,7 +1964,8 @@ hipError_t zha_launch_merge_ids(const ZhaLevelArgs& a, int H_kv, int G, int c, h
 
 hipError_t zha_launch_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream) {
     if (!a.hblk || !a.hcut || !a.tick || !a.desc || !a.ghist || !a.hdone) return hipErrorInvalidValue;
-    int64_t w = (a.cap + kSlice - 1) / kSlice;
+    // one workgroup per head when every frontier of the level fits the LDS keys
+    int64_t w = a.cap <= kLdsKeys ? 1 : (a.cap + kSlice - 1) / kSlice;
     if (w > kSliceW) w = kSliceW;
     if (w < 1) w = 1;
     hipLaunchKernelGGL(zha_select_kernel, dim3((unsigned)w, (unsigned)(H_kv * G)), dim3(kBT), 0, stream, a, G, c,
@@ -1918,10 +1976,15 @@ hipError_t zha_launch_select(const ZhaLevelArgs& a, int H_kv, int G, int c, floa
 hipError_t zha_launch_apply(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream) {
     if (!a.hcut || !a.tick || !a.desc) return hipErrorInvalidValue;
     const dim3 grid((unsigned)a.ndesc, (unsigned)H_kv);
-    if (apply_threads(a.cap) == 1024)
-        hipLaunchKernelGGL(zha_apply_kernel<1024>, grid, dim3(1024), 0, stream, a, G, c);
-    else
-        hipLaunchKernelGGL(zha_apply_kernel<256>, grid, dim3(256), 0, stream, a, G, c);
+    // without the cross launch every head's kept bitmap was written by the select kernel
+    const bool bits = a.glist == nullptr;
+    if (apply_threads(a.cap) == 1024) {
+        if (bits) hipLaunchKernelGGL((zha_apply_kernel<1024, true>), grid, dim3(1024), 0, stream, a, G, c);
+        else hipLaunchKernelGGL((zha_apply_kernel<1024, false>), grid, dim3(1024), 0, stream, a, G, c);
+    } else {
+        if (bits) hipLaunchKernelGGL((zha_apply_kernel<256, true>), grid, dim3(256), 0, stream, a, G, c);
+        else hipLaunchKernelGGL((zha_apply_kernel<256, false>), grid, dim3(256), 0, stream, a, G, c);
+    }
     return hipGetLastError();
 }
 

@@ -1074,12 +1074,18 @@ __device__ bool block_cut(const KF& key_at, const PF& pos_at, int n, float top_p
     return true;                               // (not reached: the third pass always returns)
 }
 
+// Kept iff (key, position) <= the head's limit in lexicographic order: the cut's
+// (key, position) (a cut key always carries mass, so it lies below kNoMass); with
+// keep_all every candidate key, massless ones included; with none nothing (a head
+// with no candidate has only kNotCand keys, which pass no limit).  One 64-bit
+// comparison per key, its mask usable as a ballot: no per-key mask arithmetic on
+// the scalar unit, which every wave of a workgroup shares.
+__device__ __forceinline__ uint64_t kept_limit(bool none, bool keep_all, uint32_t ustar, uint32_t plim) {
+    return none ? 0ull : keep_all ? (((uint64_t)kNoMass << 32) | 0xFFFFFFFFull) : (((uint64_t)ustar << 32) | plim);
+}
 __device__ __forceinline__ bool kept_by(uint32_t key, uint32_t p, bool none, bool keep_all, uint32_t ustar,
                                         uint32_t plim) {
-    // branch-free (bitwise, not short-circuit): keeps loads ahead of it batched
-    const bool cand = key != kNotCand;
-    const bool below = (key < kNoMass) & ((key < ustar) | ((key == ustar) & (p <= plim)));
-    return (!none) & cand & (keep_all | below);
+    return ((((uint64_t)key) << 32) | p) <= kept_limit(none, keep_all, ustar, plim);
 }
 
 // Maximum over the workgroup (every thread receives it).
@@ -1281,6 +1287,37 @@ __global__ __launch_bounds__(kBT) void zha_merge_ids_kernel(ZhaLevelArgs a, int 
     if (tid == 0) a.nkept[g] = (int32_t)s_tot;
 }
 
+// A head's kept flags over positions [0, n) as bitmap words (one per 64 positions,
+// to `bits`), wave w taking words w, w + kBW, ... in batches whose keys are all read
+// before any is used.  Returns the wave's kept count (high word) and candidate
+// count (low word), the same in every lane.
+template <class KF>
+__device__ __forceinline__ uint64_t head_words(const KF& key_at, int n, bool none, bool keep_all, uint32_t ustar,
+                                               uint32_t plim, uint64_t* bits) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = (n + 63) >> 6;
+    uint32_t w_kept = 0, w_cand = 0;
+#pragma unroll 1
+    for (int w0 = wave; w0 < nw; w0 += kBW * kSweepB) {   // uniform per wave
+        uint32_t kk[kSweepB];
+#pragma unroll
+        for (int j = 0; j < kSweepB; ++j) {
+            const int p = (w0 + j * kBW) * 64 + lane;
+            kk[j] = kNotCand;
+            if (p < n) kk[j] = key_at(p);
+        }
+#pragma unroll
+        for (int j = 0; j < kSweepB; ++j) {
+            const int wd = w0 + j * kBW;
+            const uint64_t b = __ballot(kept_by(kk[j], (uint32_t)(wd * 64 + lane), none, keep_all, ustar, plim));
+            w_cand += (uint32_t)__popcll(__ballot(kk[j] != kNotCand));
+            w_kept += (uint32_t)__popcll(b);
+            if (lane == 0 && wd < nw) bits[wd] = b;
+        }
+    }
+    return ((uint64_t)w_kept << 32) | w_cand;
+}
+
 // ---- levels below the chain: two launches after the score kernel.
 //
 // zha_select_kernel, grid (kSliceW, H_q), 1024 threads: a frontier of at most
@@ -1475,31 +1512,12 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
         else block_cut(GlobKeys{sg, M}, IdPos{}, n, top_p, 0, true, true, s_hist, s_gl, &st, ustar, plim);
     }
     // the head's kept flags as a bitmap over positions, one word per 64 (read by the
-    // apply), and its kept and candidate counts: wave w takes words w, w + kBW, ...
-    // in batches whose keys are all read before any is used
+    // apply), and its kept and candidate counts
     {
-        const int nw = (n + 63) >> 6;
         uint64_t* hbits = a.kbm + ((size_t)g * G + hl) * (size_t)a.wcap;
-        uint32_t w_kept = 0, w_cand = 0;
-#pragma unroll 1
-        for (int w0 = wave; w0 < nw; w0 += kBW * kSweepB) {   // uniform per wave
-            uint32_t kk[kSweepB];
-#pragma unroll
-            for (int j = 0; j < kSweepB; ++j) {
-                const int p = (w0 + j * kBW) * 64 + lane;
-                kk[j] = kNotCand;
-                if (p < n) kk[j] = staged ? s_keys[p] : key_of(sg[p], M);
-            }
-#pragma unroll
-            for (int j = 0; j < kSweepB; ++j) {
-                const int wd = w0 + j * kBW;
-                const uint64_t bits = __ballot(kept_by(kk[j], (uint32_t)(wd * 64 + lane), none, keep_all, ustar, plim));
-                w_cand += (uint32_t)__popcll(__ballot(kk[j] != kNotCand));
-                w_kept += (uint32_t)__popcll(bits);
-                if (lane == 0 && wd < nw) hbits[wd] = bits;
-            }
-        }
-        if (lane == 0) s_wred[wave] = ((uint64_t)w_kept << 32) | w_cand;
+        const uint64_t kc = staged ? head_words(LdsKeys{s_keys}, n, none, keep_all, ustar, plim, hbits)
+                                   : head_words(GlobKeys{sg, M}, n, none, keep_all, ustar, plim, hbits);
+        if (lane == 0) s_wred[wave] = kc;
     }
     __syncthreads();
     if (tid == 0) {

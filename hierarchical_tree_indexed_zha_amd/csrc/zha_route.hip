@@ -1374,7 +1374,7 @@ __global__ __launch_bounds__(kBT) void zha_select_kernel(ZhaLevelArgs a, int G, 
     // kSlice positions as one 16-byte load per thread (rows are 16-byte aligned and
     // padded to whole vectors), with one workgroup per head every position of the
     // level's capacity (at most kLdsKeys), and, last, the parent count
-    const bool single = gridDim.x == 1;        // the host's choice: every frontier of the level fits the LDS keys
+    const bool single = gridDim.x == 1;        // the level's capacity is one slice: one workgroup per head
     const float hb = tid < a.score_blocks ? a.hblk[(size_t)h * ZHA_SCORE_MAXB + tid] : zha_neg_inf();
     const int nv_cap = (int)(a.sstride / 4);
     constexpr int kVec = kKeyRegs / 4;         // float4 loads per thread of a staged head
@@ -1982,8 +1982,10 @@ hipError_t zha_launch_merge_ids(const ZhaLevelArgs& a, int H_kv, int G, int c, h
 
 hipError_t zha_launch_select(const ZhaLevelArgs& a, int H_kv, int G, int c, float top_p, hipStream_t stream) {
     if (!a.hblk || !a.hcut || !a.tick || !a.desc || !a.ghist || !a.hdone) return hipErrorInvalidValue;
-    // one workgroup per head when every frontier of the level fits the LDS keys
-    int64_t w = a.cap <= kLdsKeys ? 1 : (a.cap + kSlice - 1) / kSlice;
+    // slices of kSlice positions, at most kSliceW per head (one slice: one workgroup
+    // per head selects alone; a frontier of several slices is histogrammed by them
+    // first, measured faster than one workgroup building the histogram itself)
+    int64_t w = (a.cap + kSlice - 1) / kSlice;
     if (w > kSliceW) w = kSliceW;
     if (w < 1) w = 1;
     hipLaunchKernelGGL(zha_select_kernel, dim3((unsigned)w, (unsigned)(H_kv * G)), dim3(kBT), 0, stream, a, G, c,

@@ -1344,6 +1344,7 @@ __device__ __forceinline__ uint64_t head_words(const KF& key_at, int n, bool non
 // Apply workgroups take four positions per thread: 256 threads at levels of at most
 // kApplyWideCap slots, else 1024 (fewer chunks, fewer tickets drawn on one word).
 constexpr int kApplyWideCap = 131072;
+constexpr int kApplyEarly = 64;                   // apply workgroups per group drawing their ticket at once
 __host__ __device__ constexpr int apply_threads(int64_t cap) { return cap > kApplyWideCap ? 1024 : 256; }
 constexpr uint32_t kDescAgg = 1u << 30;           // descriptor: the chunk's kept count is published
 constexpr uint32_t kDescInc = 2u << 30;           // descriptor: its inclusive prefix is published
@@ -1751,7 +1752,9 @@ __global__ __launch_bounds__(kBT) void zha_resolve_kernel(ZhaLevelArgs a, int G,
     }
 }
 
-template <int kApplyThreads, bool BITS>
+// MG: the largest group the launch serves (8 or ZHA_MAX_GROUP): the per-head
+// registers of a 1024-thread workgroup stay within its register budget at G <= 8.
+template <int kApplyThreads, bool BITS, int MG = ZHA_MAX_GROUP>
 __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a, int G, int c) {
     constexpr int kApplyWaves = kApplyThreads / 64;
     constexpr int kApplyChunk = 4 * kApplyThreads;    // positions per apply workgroup (four per thread)
@@ -1761,13 +1764,22 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
     __shared__ HeadCut s_hc[ZHA_MAX_GROUP];
     const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // the ticket is drawn in the parent count's round trip (a workgroup that then
-    // finds nothing to do leaves with it: later tickets only run past the chunks)
-    if (tid == 0) s_ticket = atomicAdd(&a.tick[g], 1u);
+    // the first kApplyEarly workgroups of a group draw their ticket in the parent
+    // count's round trip (one that then finds nothing to do leaves with it: later
+    // tickets only run past the chunks); the others first learn the chunk count and
+    // draw one only when a chunk is left for them, so a wide level's idle workgroups
+    // add no atomics on the group's ticket word.  Every ticket drawn below the chunk
+    // count belongs to a running workgroup, so the look-back waits always end.
+    const bool early = blockIdx.x < kApplyEarly;
+    if (early && tid == 0) s_ticket = atomicAdd(&a.tick[g], 1u);
     const int pn = parent_count(a, g);
     const int n = a.top ? (int)a.n_top : pn * c + (int)(a.orph_hi - a.orph_lo);
     if (n <= kSmallN) return;                  // the select kernel wrote the kept list
     const int nch = (n + kApplyChunk - 1) / kApplyChunk;
+    if (!early) {
+        if ((int)blockIdx.x >= nch) return;
+        if (tid == 0) s_ticket = atomicAdd(&a.tick[g], 1u);
+    }
     __syncthreads();
     const int ci = (int)s_ticket;
     if (ci >= nch) return;
@@ -1780,9 +1792,9 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
         // p0 .. p0 + 3 of word p0 / 64 of every head, with the parents' kept entries
         // of the thread's positions, in one round trip
         const int wd = (p0 < n ? p0 : 0) >> 6;
-        uint64_t hw[ZHA_MAX_GROUP];
+        uint64_t hw[MG];
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+        for (int hh = 0; hh < MG; ++hh) {
             hw[hh] = 0ull;
             if (hh < G) hw[hh] = a.kbm[((size_t)g * G + hh) * (size_t)a.wcap + wd];
         }
@@ -1793,7 +1805,7 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
             if (p < pnc) pk[j] = a.pklist[(size_t)g * a.pcap + zha_div((uint32_t)p, a.dc)];
         }
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        for (int hh = 0; hh < MG; ++hh)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 msk[j] |= (uint32_t)(p0 + j < n ? (hw[hh] >> ((p0 + j) & 63)) & 1ull : 0ull) << hh;
@@ -1805,9 +1817,9 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
         // row and are masked afterwards
         const HeadCut mine = reinterpret_cast<const HeadCut*>(a.hcut)[(size_t)g * G + (tid < G ? tid : 0)];
         const int pv = p0 < n ? p0 : 0;
-        float4 x[ZHA_MAX_GROUP];
+        float4 x[MG];
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh)
+        for (int hh = 0; hh < MG; ++hh)
             x[hh] = *reinterpret_cast<const float4*>(a.sig + ((size_t)g * G + (hh < G ? hh : 0)) * a.sstride + pv);
         // the parents' kept entries of the thread's positions, in the same round trip
 #pragma unroll
@@ -1819,11 +1831,11 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
         if (tid < G) s_hc[tid] = mine;
         __syncthreads();
         // every head's cut read from LDS at once, then the masks without branches
-        HeadCut hcs[ZHA_MAX_GROUP];
+        HeadCut hcs[MG];
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) hcs[hh] = s_hc[hh < G ? hh : 0];
+        for (int hh = 0; hh < MG; ++hh) hcs[hh] = s_hc[hh < G ? hh : 0];
 #pragma unroll
-        for (int hh = 0; hh < ZHA_MAX_GROUP; ++hh) {
+        for (int hh = 0; hh < MG; ++hh) {
             const HeadCut& hc = hcs[hh];
             const float v[4] = {x[hh].x, x[hh].y, x[hh].z, x[hh].w};
 #pragma unroll
@@ -2000,6 +2012,7 @@ hipError_t zha_launch_apply(const ZhaLevelArgs& a, int H_kv, int G, int c, hipSt
     const bool bits = a.glist == nullptr;
     if (apply_threads(a.cap) == 1024) {
         if (bits) hipLaunchKernelGGL((zha_apply_kernel<1024, true>), grid, dim3(1024), 0, stream, a, G, c);
+        else if (G <= 8) hipLaunchKernelGGL((zha_apply_kernel<1024, false, 8>), grid, dim3(1024), 0, stream, a, G, c);
         else hipLaunchKernelGGL((zha_apply_kernel<1024, false>), grid, dim3(1024), 0, stream, a, G, c);
     } else {
         if (bits) hipLaunchKernelGGL((zha_apply_kernel<256, true>), grid, dim3(256), 0, stream, a, G, c);

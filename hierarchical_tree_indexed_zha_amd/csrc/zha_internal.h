@@ -137,7 +137,7 @@ int zha_score_blocks(int64_t max_cand, int R);
 // The chain: the first routed levels while each has at most ZHA_CHAIN_SLOTS node
 // slots and together at most ZHA_CHAIN_PLANES planes per group; every node scored
 // by one launch, then each query head's workgroup selects them one after the other.
-#define ZHA_CHAIN_SLOTS 4096
+#define ZHA_CHAIN_SLOTS 8192
 #define ZHA_MAX_CHAIN 8
 #define ZHA_CHAIN_PLANES 32768
 struct ZhaChainArgs {                 // scoring every node of the chained levels

@@ -515,9 +515,9 @@ constexpr int kKeyRegs = kLdsKeys / kBT;       // positions per thread of a stag
 constexpr int kSlice = 4 * kBT;                 // positions a slice workgroup histograms (four per thread)
 constexpr int kSliceW = 8;                      // slice workgroups per head
 constexpr int kChainSlots = ZHA_CHAIN_SLOTS;
-constexpr int kChainStage = 16384;              // chained scores of one head staged in LDS (floats)
+constexpr int kChainStage = 8192;               // chained scores of one head staged in LDS (floats)
 constexpr int kChainPer = kChainSlots / kBT;  // candidate positions per thread in the chain
-static_assert(kChainPer * kBT == kChainSlots && kChainPer * kBW <= 64, "chain rows: one scan lane per (row, wave)");
+static_assert(kChainPer * kBT == kChainSlots && kChainPer * kBW <= 128, "chain rows: at most two scan entries per lane");
 // Small-path histogram bins pack a key count above a mass sum: at most kSmallN
 // keys of mass <= 2^40 sum below 2^52, so the fields never carry into each other
 // and one 64-bit LDS atomic per key updates both.
@@ -1101,6 +1101,32 @@ __device__ __forceinline__ float block_max(float x, float* red) {
     return m;
 }
 
+// Exclusive prefix sums of s[0, kRows) in place by one wave, kRows <= 128 (entries
+// lane * kPer .. lane * kPer + kPer - 1 per lane, so the order is kept); returns the
+// total.
+template <int kRows>
+__device__ __forceinline__ uint32_t wave_scan_rows(uint32_t* s) {
+    const int lane = threadIdx.x & 63;
+    constexpr int kPer = (kRows + 63) / 64;
+    uint32_t v[kPer];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = lane * kPer + j;
+        v[j] = i < kRows ? s[i] : 0u;
+        loc += v[j];
+    }
+    uint64_t tot;
+    uint32_t ex = (uint32_t)wave_excl_scan_u64(loc, &tot);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = lane * kPer + j;
+        if (i < kRows) s[i] = ex;
+        ex += v[j];
+    }
+    return (uint32_t)tot;
+}
+
 // ---- the chain: the first routed levels, each at most kChainSlots complete nodes,
 // every node of them scored beforehand (node-indexed scores).  One workgroup per
 // query head walks them top-down with its own kept set in LDS: its candidates at a
@@ -1162,19 +1188,23 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
         const int n = li == 0 ? L.n_nodes : nk * c + (L.orph_hi - L.orph_lo);
         const float* sg = L.sig + ((size_t)g * G + hl) * (size_t)L.sstride;
         const float* ss = s_sig + soff[li];
+        // (rows of 1024 positions wholly past n are skipped: a uniform branch)
         float x[kChainPer];
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) {
-            const int p = tid + k * kBT;
-            int32_t nd = p;
-            if (li > 0) {
-                const int pc = p < nk * c ? p : 0;
-                const int pi = pc / c;
-                nd = p < nk * c ? s_kept[pi] * c + (pc - pi * c) : L.orph_lo + (p - nk * c);
+            x[k] = zha_neg_inf();
+            if (k * kBT < n) {
+                const int p = tid + k * kBT;
+                int32_t nd = p;
+                if (li > 0) {
+                    const int pc = p < nk * c ? p : 0;
+                    const int pi = pc / c;
+                    nd = p < nk * c ? s_kept[pi] * c + (pc - pi * c) : L.orph_lo + (p - nk * c);
+                }
+                nd = p < n ? nd : 0;
+                s_node[p] = nd;
+                if (p < n) x[k] = staged ? ss[nd] : sg[nd];
             }
-            nd = p < n ? nd : 0;
-            s_node[p] = nd;
-            x[k] = p < n ? (staged ? ss[nd] : sg[nd]) : zha_neg_inf();
         }
         float mx = zha_neg_inf();
 #pragma unroll
@@ -1183,7 +1213,7 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) {
             const int p = tid + k * kBT;
-            s_keys[p] = p < n ? key_of(x[k], M) : kNotCand;
+            if (k * kBT < n) s_keys[p] = p < n ? key_of(x[k], M) : kNotCand;
         }
         for (int i = tid; i < kChainSlots / 64; i += kBT) s_bm[i] = 0ull;
         __syncthreads();
@@ -1198,20 +1228,21 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
         uint32_t ncand = 0;
 #pragma unroll
         for (int k = 0; k < kChainPer; ++k) {
-            const uint32_t p = (uint32_t)(tid + k * kBT);
-            const uint32_t key = s_keys[p];
-            kept[k] = kept_by(key, p, none, keep_all, ustar, plim);
-            bal[k] = __ballot(kept[k]);
-            ncand += (uint32_t)__popcll(__ballot(key != kNotCand));
+            kept[k] = false;
+            bal[k] = 0ull;
+            if (k * kBT < n) {
+                const uint32_t p = (uint32_t)(tid + k * kBT);
+                const uint32_t key = s_keys[p];
+                kept[k] = kept_by(key, p, none, keep_all, ustar, plim);
+                bal[k] = __ballot(kept[k]);
+                ncand += (uint32_t)__popcll(__ballot(key != kNotCand));
+            }
             if (lane == 0) s_pre[k * kBW + wave] = (uint32_t)__popcll(bal[k]);
         }
         __syncthreads();
         if (wave == 0) {
-            const uint32_t v = lane < kChainPer * kBW ? s_pre[lane] : 0u;
-            uint64_t tot;
-            const uint32_t ex = (uint32_t)wave_excl_scan_u64(v, &tot);
-            if (lane < kChainPer * kBW) s_pre[lane] = ex;
-            if (lane == 0) s_tot[0] = (uint32_t)tot;
+            const uint32_t tot = wave_scan_rows<kChainPer * kBW>(s_pre);
+            if (lane == 0) s_tot[0] = tot;
         }
         if (tid == 0) s_tot[1] = 0;
         __syncthreads();
@@ -1268,10 +1299,8 @@ __global__ __launch_bounds__(kBT) void zha_merge_ids_kernel(ZhaLevelArgs a, int 
     }
     __syncthreads();
     if (wave == 0) {
-        const uint32_t v = s_wc[lane];
-        uint64_t tot;
-        s_wc[lane] = (uint32_t)wave_excl_scan_u64(v, &tot);
-        if (lane == 0) s_tot = (uint32_t)tot;
+        const uint32_t tot = wave_scan_rows<kChainPer * kBW>(s_wc);
+        if (lane == 0) s_tot = tot;
     }
     __syncthreads();
     int32_t* kl = a.klist + (size_t)g * a.cap;

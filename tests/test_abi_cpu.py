@@ -173,16 +173,17 @@ def test_config_struct_layout_matches_header():
 
 
 def test_chained_levels_follow_the_slot_and_plane_bounds():
-    """The first routed levels form the chain while each has at most 4,096 node slots and
+    """The first routed levels form the chain while each has at most 8,192 node slots and
     together at most 32,768 planes per group; the rest are routed over group candidates."""
     def chained(name, n=None):
         w = W.get(name)
-        cfg = B.config_of(w)
         n = w.n_tokens if n is None else n
+        cfg = B.config_of(w, capacity=max(w.capacity, n))
         return [lv for lv in range(1, w.levels + 1) if B.zha_route_level_offsets(cfg, n, lv)["chained"]]
     assert chained("light") == [2, 3, 4]          # 4096 + 512 + 64 planes; level 1 has 32,768 slots
+    assert chained("light", 262144 + 272) == [2, 3, 4]   # after the bench's appends: 4,100 level-2 nodes
     assert chained("tiny") == [2, 3, 4, 5, 6]     # R = 16: 21,824 planes; level 1 would add 65,536
-    assert chained("deep") == [4, 5, 6]           # 1,344 nodes * 16 planes; level 3 has 4,096 slots but 65,536 planes
+    assert chained("deep") == [4, 5, 6]           # 1,344 nodes * 16 planes; level 3's 4,096 nodes would add 65,536 planes
     assert chained("wide") == [1]                 # 1,024 nodes * 16 planes
     assert chained("ultra") == [4, 5, 6, 7]       # 2,560 + 320 + 40 + 5 nodes
     assert chained("light", 100) == [1, 2]        # 12 level-1 nodes, one level-2 node

@@ -217,12 +217,30 @@ constexpr int kLmMinR = 4;         // fewer reference queries leave most MFMA ro
 constexpr int kLmStride = 144;     // LDS row of a staged key tile (floats): the B reads of
                                    // a half-wave (rows q4 and q4 + 1) fall 16 banks apart
 
+// Butterfly steps within a row of 16 lanes as DPP moves (no LDS traffic): lane
+// pairs at distance 1 and 2 (quad permutations), then 4 and 8 (mirrors within 8
+// and 16 lanes, which pair the already uniform quads and halves).  Every lane of a
+// segment ends with the same value, bit for bit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __uint_as_float(zha_dpp<CTRL, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+}
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
 __device__ __forceinline__ float seg_max(float x, int c) {
-    for (int o = 1; o < c && o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+    x = fmaxf(x, dpp_row<kDppXor1>(x));
+    if (c > 2) x = fmaxf(x, dpp_row<kDppXor2>(x));
+    if (c > 4) x = fmaxf(x, dpp_row<kDppHalfMirror>(x));
+    if (c > 8) x = fmaxf(x, dpp_row<kDppMirror>(x));
     return x;
 }
 __device__ __forceinline__ float seg_sum(float x, int c) {
-    for (int o = 1; o < c && o < 16; o <<= 1) x += __shfl_xor(x, o);
+    x += dpp_row<kDppXor1>(x);
+    if (c > 2) x += dpp_row<kDppXor2>(x);
+    if (c > 4) x += dpp_row<kDppHalfMirror>(x);
+    if (c > 8) x += dpp_row<kDppMirror>(x);
     return x;
 }
 
@@ -233,25 +251,24 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
     int64_t cap_tok, int64_t cap1, int c, int R, int64_t first_leaf, int64_t n_leaves, float tau) {
     __shared__ __align__(16) float s_k[4][16 * kLmStride];
     __shared__ float s_w[4][16 * 17];
+    __shared__ __align__(16) float s_q[16 * kLmStride];
     const int g = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, q4 = lane >> 4;
     float* sk = s_k[wave];
     float* sw = s_w[wave];
 
-    // the reference queries as the A operand of Z: row j (zero past R), d = 32 q4 + m
-    float qa[32];
-    {
-        const float* qr = Qref + ((size_t)g * R + (j < R ? j : 0)) * ZHA_D + 32 * q4;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const float4 x = reinterpret_cast<const float4*>(qr)[v];
-            qa[4 * v + 0] = j < R ? x.x : 0.f;
-            qa[4 * v + 1] = j < R ? x.y : 0.f;
-            qa[4 * v + 2] = j < R ? x.z : 0.f;
-            qa[4 * v + 3] = j < R ? x.w : 0.f;
-        }
+    // the reference queries, the A operand of Z (row j, zero past R; d = 32 q4 + m),
+    // staged in LDS once and read per product: held in registers they cost the
+    // second resident wave per SIMD
+    for (int i = threadIdx.x; i < 16 * (ZHA_D / 4); i += 256) {
+        const int r = i / (ZHA_D / 4), v = i - r * (ZHA_D / 4);
+        const float4 x = r < R ? reinterpret_cast<const float4*>(Qref + ((size_t)g * R + r) * ZHA_D)[v]
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(s_q + r * kLmStride + 4 * v) = x;
     }
+    __syncthreads();
+    const float* qrow = s_q + j * kLmStride + 32 * q4;
     const bool big = c > 16;                            // a leaf spans several tiles
     const int lpu = big ? 1 : 16 / c;                   // leaves per unit
     const int tpu = big ? c / 16 : 1;                   // tiles per unit
@@ -311,10 +328,16 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
             for (int v = 0; v < 8; ++v)
                 *reinterpret_cast<float4*>(sk + j * kLmStride + 32 * q4 + 4 * v) =
                     make_float4(kb[4 * v], kb[4 * v + 1], kb[4 * v + 2], kb[4 * v + 3]);
-            // Z: lane holds refs 4 q4 + i against token j
-            zha_f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            // Z: lane holds refs 4 q4 + i against token j; four independent chains of
+            // eight products (a single chain of 32 waits on every product in turn)
+            zha_f32x4 zc[4];
 #pragma unroll
-            for (int m = 0; m < 32; ++m) z4 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[m], kb[m], z4, 0, 0, 0);
+            for (int e = 0; e < 4; ++e) zc[e] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 32; ++m) zc[m & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(qrow[m], kb[m], zc[m & 3], 0, 0, 0);
+            zha_f32x4 z4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z4[i] = (zc[0][i] + zc[1][i]) + (zc[2][i] + zc[3][i]);
             const bool tv = j < ntok;
             float w[4];
             if (c <= 16) {
@@ -341,18 +364,11 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float z = tau * z4[i];
-                    float mt = z;
-#pragma unroll
-                    for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+                    const float mt = seg_max(z, 16);
                     const float mn = fmaxf(m_run[i], mt);
                     const float alpha = expf(m_run[i] - mn);   // 0 on the first tile
                     const float e = expf(z - mn);
-                    float es = e, ezs = e * z;
-#pragma unroll
-                    for (int o = 1; o < 16; o <<= 1) {
-                        es += __shfl_xor(es, o);
-                        ezs += __shfl_xor(ezs, o);
-                    }
+                    const float es = seg_sum(e, 16), ezs = seg_sum(e * z, 16);
                     l_run[i] = l_run[i] * alpha + es;
                     ez_run[i] = ez_run[i] * alpha + ezs;
                     m_run[i] = mn;

@@ -438,6 +438,180 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
     }
 }
 
+// ---- long leaves (c a multiple of 32, R <= 16, bfloat16 keys) on bfloat16 products.
+//
+// The reference queries and the softmax weights enter as three bfloat16 parts each
+// (hi + mid + lo is a float32 value exactly: each part is the remainder rounded to
+// 8 significant bits, and what is left after two has at most 8), the keys as they
+// are; the float32 sums of the parts' products are those of the float32 products,
+// at an eighth of the matrix work.  One wave per leaf, tiles of 32 tokens.  Per tile:
+//   Z = tau Q K^T    per 16-token half h and 32-dim block kb, one
+//                    v_mfma_f32_16x16x32_bf16 per query part (A: Q part row j, dims
+//                    32 kb + 8 q .. + 7, from LDS; B: key row 16 h + j, the same dims,
+//                    straight from the lane's 16-byte loads);
+//   online softmax of the lane's refs 4 q + i over the tile's 32 tokens;
+//   S += W K         the contraction over the tile's tokens is permuted (index 8 q + e
+//                    is token 4 e + q) so that each lane's B operand comes from its own
+//                    16-byte loads of rows 4 e + q, dims 8 j .. 8 j + 7, and output
+//                    column j of block c8 is dim 8 j + c8 (as in the gather's PV).
+// Outputs as the other leaf kernels: S[leaf][r][d], B, LSE (rows r < R).
+constexpr int kB3QRow = 68;        // LDS row of a query part (u32, two bf16 each): 16-byte aligned
+
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+    h = zha_f32_to_bf16_rne(x);
+    const float r1 = x - __uint_as_float(h << 16);
+    m = zha_f32_to_bf16_rne(r1);
+    const float r2 = r1 - __uint_as_float(m << 16);
+    l = zha_f32_to_bf16_rne(r2);
+}
+__device__ __forceinline__ uint32_t b3_word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
+    const uint16_t* __restrict__ K, const float* __restrict__ Qref,
+    float* __restrict__ S, float* __restrict__ B, float* __restrict__ LSE,
+    int64_t cap_tok, int64_t cap1, int c, int R, int64_t first_leaf, int64_t n_leaves, float tau) {
+    __shared__ __align__(16) uint32_t s_q[3][16 * kB3QRow];
+    __shared__ float s_w[4][16 * 33];
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, q = lane >> 4;
+    float* sw = s_w[wave];
+    // the reference queries' three parts, rows past R zero
+    for (int i = threadIdx.x; i < 16 * (ZHA_D / 2); i += 256) {
+        const int r = i / (ZHA_D / 2), dp = i - r * (ZHA_D / 2);
+        float2 v = make_float2(0.f, 0.f);
+        if (r < R) v = reinterpret_cast<const float2*>(Qref + ((size_t)g * R + r) * ZHA_D)[dp];
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3_bf16(v.x, h0, m0, l0);
+        split3_bf16(v.y, h1, m1, l1);
+        s_q[0][r * kB3QRow + dp] = h0 | (h1 << 16);
+        s_q[1][r * kB3QRow + dp] = m0 | (m1 << 16);
+        s_q[2][r * kB3QRow + dp] = l0 | (l1 << 16);
+    }
+    __syncthreads();
+    const int tpl = c / 32;
+    for (int64_t lf = (int64_t)blockIdx.x * 4 + wave; lf < n_leaves; lf += (int64_t)gridDim.x * 4) {
+        const int64_t leaf = first_leaf + lf;
+        const size_t row0 = (size_t)g * cap_tok + (size_t)leaf * c;
+        float m_run[4], l_run[4], ez_run[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { m_run[i] = zha_neg_inf(); l_run[i] = 0.f; ez_run[i] = 0.f; }
+        zha_f32x4 acc[8];
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) acc[c8] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
+        // key rows 16 h + j of a tile, dims 32 kb + 8 q .. + 7: the next tile's are
+        // requested before the current one is computed
+        uint4 kz[2][4];
+        auto fetch_z = [&](int tt, uint4 (&dst)[2][4]) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    dst[h][kb] = *reinterpret_cast<const uint4*>(K + (row0 + (size_t)(32 * tt + 16 * h + j)) * ZHA_D +
+                                                                 32 * kb + 8 * q);
+        };
+        fetch_z(0, kz);
+        for (int tt = 0; tt < tpl; ++tt) {
+            // rows 4 e + q of the tile, dims 8 j .. 8 j + 7 (the B operand of W K)
+            uint4 kv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                kv[e] = *reinterpret_cast<const uint4*>(K + (row0 + (size_t)(32 * tt + 4 * e + q)) * ZHA_D + 8 * j);
+            uint4 kzn[2][4];
+            if (tt + 1 < tpl) fetch_z(tt + 1, kzn);
+            // Z: four independent accumulator chains (half h, parts alternating)
+            zha_f32x4 zz[2][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int a2 = 0; a2 < 2; ++a2) zz[h][a2] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                for (int pt = 0; pt < 3; ++pt) {
+                    const zha_bf16x8 qa = zha_as_bf16x8(*reinterpret_cast<const uint4*>(&s_q[pt][j * kB3QRow + 16 * kb + 4 * q]));
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        zz[h][(kb * 3 + pt) & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, zha_as_bf16x8(kz[h][kb]),
+                                                                                           zz[h][(kb * 3 + pt) & 1], 0, 0, 0);
+                }
+            }
+            // online softmax of refs 4 q + i over tokens j and 16 + j
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float z0 = tau * (zz[0][0][i] + zz[0][1][i]);
+                const float z1 = tau * (zz[1][0][i] + zz[1][1][i]);
+                const float mt = seg_max(fmaxf(z0, z1), 16);
+                const float mn = fmaxf(m_run[i], mt);
+                const float alpha = expf(m_run[i] - mn);   // 0 on the first tile
+                const float e0 = expf(z0 - mn), e1 = expf(z1 - mn);
+                const float es = seg_sum(e0 + e1, 16), ezs = seg_sum(e0 * z0 + e1 * z1, 16);
+                l_run[i] = l_run[i] * alpha + es;
+                ez_run[i] = ez_run[i] * alpha + ezs;
+                m_run[i] = mn;
+#pragma unroll
+                for (int c8 = 0; c8 < 8; ++c8) acc[c8][i] *= alpha;
+                sw[(4 * q + i) * 33 + j] = e0;
+                sw[(4 * q + i) * 33 + 16 + j] = e1;
+            }
+            zha_wave_lds_sync();
+            // W (row j, tokens 4 e + q) in three parts; B from the rows' 16-byte loads
+            uint32_t wp[3][4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                uint32_t ha, ma, la, hb, mb, lb;
+                split3_bf16(sw[j * 33 + 4 * (2 * e2) + q], ha, ma, la);
+                split3_bf16(sw[j * 33 + 4 * (2 * e2 + 1) + q], hb, mb, lb);
+                wp[0][e2] = ha | (hb << 16);
+                wp[1][e2] = ma | (mb << 16);
+                wp[2][e2] = la | (lb << 16);
+            }
+            const zha_bf16x8 wa0 = zha_as_bf16x8(make_uint4(wp[0][0], wp[0][1], wp[0][2], wp[0][3]));
+            const zha_bf16x8 wa1 = zha_as_bf16x8(make_uint4(wp[1][0], wp[1][1], wp[1][2], wp[1][3]));
+            const zha_bf16x8 wa2 = zha_as_bf16x8(make_uint4(wp[2][0], wp[2][1], wp[2][2], wp[2][3]));
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) {
+                const int wsel = c8 >> 1;
+                const uint32_t sel = (c8 & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+                uint32_t bw[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2)
+                    bw[e2] = __builtin_amdgcn_perm(b3_word(kv[2 * e2 + 1], wsel), b3_word(kv[2 * e2], wsel), sel);
+                const zha_bf16x8 bv = zha_as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
+                acc[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa0, bv, acc[c8], 0, 0, 0);
+                acc[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa1, bv, acc[c8], 0, 0, 0);
+                acc[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa2, bv, acc[c8], 0, 0, 0);
+            }
+            zha_wave_lds_sync();                        // the next tile rewrites sw
+            if (tt + 1 < tpl) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) kz[h][kb] = kzn[h][kb];
+            }
+        }
+        // S[leaf][r][8 j .. 8 j + 7] = acc / l; B and LSE from the running sums
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q + i;
+            if (r < R) {
+                const float inv = 1.f / l_run[i];
+                float4* so = reinterpret_cast<float4*>(S + (((size_t)g * cap1 + (size_t)leaf) * R + r) * ZHA_D + 8 * j);
+                so[0] = make_float4(acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv);
+                so[1] = make_float4(acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv);
+                if (j == 0) {
+                    const size_t o = ((size_t)g * cap1 + (size_t)leaf) * R + r;
+                    const float lse = m_run[i] + logf(l_run[i]);
+                    LSE[o] = lse;
+                    B[o] = lse - ez_run[i] * inv;
+                }
+            }
+        }
+    }
+}
+
 // grid (ceil(n_parents / parents_per_block), H_kv), 256 threads.
 __global__ __launch_bounds__(256) void zha_merge_kernel(
     const float* __restrict__ Sc, const float* __restrict__ Bc, const float* __restrict__ Lc,
@@ -580,6 +754,16 @@ hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qre
                                    float* LSE, int H_kv, int64_t cap_tok, int64_t cap1, int c, int R,
                                    int64_t first_leaf, int64_t n_leaves, float tau, hipStream_t stream) {
     if (n_leaves <= 0) return hipSuccess;
+    if (kv_dtype == 0 && R >= kLmMinR && R <= 16 && c % 32 == 0) {
+        // long leaves, bfloat16 keys: bfloat16 products in three parts, four leaves
+        // per workgroup
+        int64_t blocks = (n_leaves + 3) / 4;
+        if (blocks > 2048) blocks = 2048;
+        hipLaunchKernelGGL(zha_leaf_b3_kernel, dim3((unsigned)blocks, (unsigned)H_kv), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(K), Qref, S, B, LSE, cap_tok, cap1, c, R, first_leaf, n_leaves,
+                           tau);
+        return hipGetLastError();
+    }
     if (R >= kLmMinR && R <= 16 && (c & (c - 1)) == 0) {
         // matrix-core kernel: units of 16 tokens (c <= 16) or whole leaves, four per workgroup
         const int64_t lpu = c <= 16 ? 16 / c : 1;

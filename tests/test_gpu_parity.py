@@ -39,6 +39,9 @@ CASES = [
     ("light@600000", _w("light", 600000, levels=4)),             # level 1 (75,000 slots): scores re-read per pass
     ("light@131072-L2", _w("light", 131072, levels=2)),          # a large top level (2,048 nodes) left unmerged
     ("light-f32@65536", _w("light", 65536, kv_dtype="f32")),     # fp32 cache: the two-per-CU gather at many tiles
+    # long leaves on the bfloat16-parts leaf kernel (c a multiple of 32), R below 16
+    ("wide-c64-R4@20000", _w("wide", 20000, levels=2, chunk=64, n_ref=4)),
+    ("wide-c32-R8@9001", _w("wide", 9001, levels=2, chunk=32, n_ref=8)),
 ]
 
 

@@ -438,6 +438,105 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
     }
 }
 
+// ---- one reference query, short leaves (R = 1, c <= 16, bfloat16 keys): a streaming
+// kernel.  Lane l of a wave takes leaf l / 8 of the wave's eight and dims 16 (l % 8) ..
+// 16 (l % 8) + 15: it loads those 16 dims of each of the leaf's c key rows (the eight
+// lanes of a leaf read each row's 256 bytes together), forms its part of every logit,
+// and the leaf's eight lanes add the parts with a DPP butterfly (the same sum in each
+// lane); each lane then forms the softmax of the c logits and the weighted mean of
+// its own 16 dims.  No LDS staging and no barrier: the kernel streams the keys once.
+constexpr int kR1MaxC = 16;
+template <int CMAX>
+__global__ __launch_bounds__(256) void zha_leaf_r1_kernel(
+    const uint16_t* __restrict__ K, const float* __restrict__ Qref,
+    float* __restrict__ S, float* __restrict__ B, float* __restrict__ LSE,
+    int64_t cap_tok, int64_t cap1, int c, int64_t first_leaf, int64_t n_leaves, float tau) {
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sl = lane & 7;                             // dims 16 sl .. 16 sl + 15
+    float qv[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float4 x = reinterpret_cast<const float4*>(Qref + (size_t)g * ZHA_D + 16 * sl)[v];
+        qv[4 * v] = x.x; qv[4 * v + 1] = x.y; qv[4 * v + 2] = x.z; qv[4 * v + 3] = x.w;
+    }
+    for (int64_t lb = ((int64_t)blockIdx.x * 4 + wave) * 8; lb < n_leaves; lb += (int64_t)gridDim.x * 32) {
+        const int64_t lf = lb + (lane >> 3);
+        const bool ok = lf < n_leaves;
+        const int64_t leaf = first_leaf + (ok ? lf : n_leaves - 1);
+        const uint16_t* row = K + ((size_t)g * cap_tok + (size_t)leaf * c) * ZHA_D + 16 * sl;
+        uint4 kr[CMAX][2];
+#pragma unroll
+        for (int t = 0; t < CMAX; ++t) {
+            if (t < c) {
+                kr[t][0] = reinterpret_cast<const uint4*>(row + (size_t)t * ZHA_D)[0];
+                kr[t][1] = reinterpret_cast<const uint4*>(row + (size_t)t * ZHA_D)[1];
+            }
+        }
+        // logits: this lane's 16-dim parts, then the leaf's eight lanes summed
+        float z[CMAX];
+        float m = zha_neg_inf();
+#pragma unroll
+        for (int t = 0; t < CMAX; ++t) {
+            if (t < c) {
+                float acc = 0.f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t w4[4] = {kr[t][h].x, kr[t][h].y, kr[t][h].z, kr[t][h].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc = fmaf(qv[8 * h + 2 * e], __uint_as_float(w4[e] << 16), acc);
+                        acc = fmaf(qv[8 * h + 2 * e + 1], __uint_as_float(w4[e] & 0xFFFF0000u), acc);
+                    }
+                }
+                z[t] = tau * seg_sum(acc, 8);
+                m = fmaxf(m, z[t]);
+            }
+        }
+        float l = 0.f;
+#pragma unroll
+        for (int t = 0; t < CMAX; ++t)
+            if (t < c) l += expf(z[t] - m);
+        const float lse = m + logf(l);
+        // the keys are decoded again below rather than held as floats across the softmax
+#pragma unroll
+        for (int t = 0; t < CMAX; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                asm volatile("" : "+v"(kr[t][h].x), "+v"(kr[t][h].y), "+v"(kr[t][h].z), "+v"(kr[t][h].w));
+        float ez = 0.f;
+        float sv[16];
+#pragma unroll
+        for (int d = 0; d < 16; ++d) sv[d] = 0.f;
+#pragma unroll
+        for (int t = 0; t < CMAX; ++t) {
+            if (t < c) {
+                const float w = expf(z[t] - lse);
+                ez = fmaf(w, z[t], ez);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t w4[4] = {kr[t][h].x, kr[t][h].y, kr[t][h].z, kr[t][h].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sv[8 * h + 2 * e] = fmaf(w, __uint_as_float(w4[e] << 16), sv[8 * h + 2 * e]);
+                        sv[8 * h + 2 * e + 1] = fmaf(w, __uint_as_float(w4[e] & 0xFFFF0000u), sv[8 * h + 2 * e + 1]);
+                    }
+                }
+            }
+        }
+        if (ok) {
+            float4* so = reinterpret_cast<float4*>(S + ((size_t)g * cap1 + (size_t)leaf) * ZHA_D + 16 * sl);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) so[v] = make_float4(sv[4 * v], sv[4 * v + 1], sv[4 * v + 2], sv[4 * v + 3]);
+            if (sl == 0) {
+                const size_t o = (size_t)g * cap1 + (size_t)leaf;
+                LSE[o] = lse;
+                B[o] = lse - ez;
+            }
+        }
+    }
+}
+
 // ---- long leaves (c a multiple of 32, R <= 16, bfloat16 keys) on bfloat16 products.
 //
 // The reference queries and the softmax weights enter as three bfloat16 parts each
@@ -613,10 +712,14 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
 }
 
 // grid (ceil(n_parents / parents_per_block), H_kv), 256 threads.
+template <int CMAX>
 __global__ __launch_bounds__(256) void zha_merge_kernel(
     const float* __restrict__ Sc, const float* __restrict__ Bc, const float* __restrict__ Lc,
     float* __restrict__ Sp, float* __restrict__ Bp, float* __restrict__ Lp,
     int64_t cap_c, int64_t cap_p, int c, int R, int64_t first_parent, int64_t n_parents) {
+    // CMAX > 0: c <= CMAX, and each thread loads all of its c children before it
+    // combines them (the loads overlap); CMAX == 0: any c, one child at a time.  The
+    // arithmetic and its order are the same in both forms.
     extern __shared__ float a_s[];                       // [ppb][R][c]
     const int g = blockIdx.y;
     const int tid = threadIdx.x;
@@ -629,22 +732,46 @@ __global__ __launch_bounds__(256) void zha_merge_kernel(
     for (int pr = tid; pr < np * R; pr += blockDim.x) {
         int pl = pr / R, r = pr - pl * R;
         int64_t child0 = (p0 + pl) * c;
-        float m = zha_neg_inf();
-        for (int j = 0; j < c; ++j) m = fmaxf(m, Lc[((size_t)g * cap_c + (size_t)(child0 + j)) * R + r]);
-        float sum = 0.f;
-        for (int j = 0; j < c; ++j) sum += expf(Lc[((size_t)g * cap_c + (size_t)(child0 + j)) * R + r] - m);
-        float lse = m + logf(sum);
-        float bp = 0.f;
+        const size_t o0 = ((size_t)g * cap_c + (size_t)child0) * R + r;
+        float m = zha_neg_inf(), sum = 0.f, bp = 0.f;
         float* a = a_s + (pl * R + r) * c;
-        for (int j = 0; j < c; ++j) {
-            size_t o = ((size_t)g * cap_c + (size_t)(child0 + j)) * R + r;
-            float la = Lc[o] - lse;                          // log a_j
-            float aj = expf(la);
-            a[j] = aj;
-            bp = fmaf(aj, Bc[o] - la, bp);
+        if constexpr (CMAX > 0) {
+            float lv[CMAX], bv[CMAX];
+#pragma unroll
+            for (int j = 0; j < CMAX; ++j)
+                if (j < c) { lv[j] = Lc[o0 + (size_t)j * R]; bv[j] = Bc[o0 + (size_t)j * R]; }
+#pragma unroll
+            for (int j = 0; j < CMAX; ++j)
+                if (j < c) m = fmaxf(m, lv[j]);
+#pragma unroll
+            for (int j = 0; j < CMAX; ++j)
+                if (j < c) sum += expf(lv[j] - m);
+            const float lse = m + logf(sum);
+#pragma unroll
+            for (int j = 0; j < CMAX; ++j) {
+                if (j < c) {
+                    const float la = lv[j] - lse;                // log a_j
+                    const float aj = expf(la);
+                    a[j] = aj;
+                    bp = fmaf(aj, bv[j] - la, bp);
+                }
+            }
+            m = lse;
+        } else {
+            for (int j = 0; j < c; ++j) m = fmaxf(m, Lc[o0 + (size_t)j * R]);
+            for (int j = 0; j < c; ++j) sum += expf(Lc[o0 + (size_t)j * R] - m);
+            const float lse = m + logf(sum);
+            for (int j = 0; j < c; ++j) {
+                const size_t o = o0 + (size_t)j * R;
+                const float la = Lc[o] - lse;                    // log a_j
+                const float aj = expf(la);
+                a[j] = aj;
+                bp = fmaf(aj, Bc[o] - la, bp);
+            }
+            m = lse;
         }
         size_t op = ((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r;
-        Lp[op] = lse;
+        Lp[op] = m;
         Bp[op] = bp;
     }
     __syncthreads();
@@ -653,13 +780,31 @@ __global__ __launch_bounds__(256) void zha_merge_kernel(
         int r = rem / (ZHA_D / 4), d4 = rem - r * (ZHA_D / 4);
         int64_t child0 = (p0 + pl) * c;
         const float* a = a_s + (pl * R + r) * c;
+        const float4* sc = reinterpret_cast<const float4*>(Sc + (((size_t)g * cap_c + (size_t)child0) * R + r) * ZHA_D) + d4;
+        const size_t step = (size_t)R * (ZHA_D / 4);         // float4s from one child to the next
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < c; ++j) {
-            float4 s = reinterpret_cast<const float4*>(Sc + (((size_t)g * cap_c + (size_t)(child0 + j)) * R + r) * ZHA_D)[d4];
-            acc.x = fmaf(a[j], s.x, acc.x);
-            acc.y = fmaf(a[j], s.y, acc.y);
-            acc.z = fmaf(a[j], s.z, acc.z);
-            acc.w = fmaf(a[j], s.w, acc.w);
+        if constexpr (CMAX > 0) {
+            float4 sv[CMAX];
+#pragma unroll
+            for (int j = 0; j < CMAX; ++j)
+                if (j < c) sv[j] = sc[(size_t)j * step];
+#pragma unroll
+            for (int j = 0; j < CMAX; ++j) {
+                if (j < c) {
+                    acc.x = fmaf(a[j], sv[j].x, acc.x);
+                    acc.y = fmaf(a[j], sv[j].y, acc.y);
+                    acc.z = fmaf(a[j], sv[j].z, acc.z);
+                    acc.w = fmaf(a[j], sv[j].w, acc.w);
+                }
+            }
+        } else {
+            for (int j = 0; j < c; ++j) {
+                const float4 s = sc[(size_t)j * step];
+                acc.x = fmaf(a[j], s.x, acc.x);
+                acc.y = fmaf(a[j], s.y, acc.y);
+                acc.z = fmaf(a[j], s.z, acc.z);
+                acc.w = fmaf(a[j], s.w, acc.w);
+            }
         }
         reinterpret_cast<float4*>(Sp + (((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r) * ZHA_D)[d4] = acc;
     }
@@ -754,6 +899,20 @@ hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qre
                                    float* LSE, int H_kv, int64_t cap_tok, int64_t cap1, int c, int R,
                                    int64_t first_leaf, int64_t n_leaves, float tau, hipStream_t stream) {
     if (n_leaves <= 0) return hipSuccess;
+    if (kv_dtype == 0 && R == 1 && c <= kR1MaxC) {
+        // one reference query, short leaves: the streaming kernel, 32 leaves per workgroup
+        int64_t blocks = (n_leaves + 31) / 32;
+        if (blocks > 4096) blocks = 4096;
+        const dim3 grid((unsigned)blocks, (unsigned)H_kv);
+        const uint16_t* K16 = static_cast<const uint16_t*>(K);
+        if (c <= 8)
+            hipLaunchKernelGGL(zha_leaf_r1_kernel<8>, grid, dim3(256), 0, stream, K16, Qref, S, B, LSE, cap_tok, cap1,
+                               c, first_leaf, n_leaves, tau);
+        else
+            hipLaunchKernelGGL(zha_leaf_r1_kernel<16>, grid, dim3(256), 0, stream, K16, Qref, S, B, LSE, cap_tok, cap1,
+                               c, first_leaf, n_leaves, tau);
+        return hipGetLastError();
+    }
     if (kv_dtype == 0 && R >= kLmMinR && R <= 16 && c % 32 == 0) {
         // long leaves, bfloat16 keys: bfloat16 products in three parts, four leaves
         // per workgroup
@@ -804,8 +963,16 @@ hipError_t zha_launch_merge(const float* Sc, const float* Bc, const float* Lc, f
     const int per_parent = R * (ZHA_D / 4);
     const int64_t ppb = per_parent >= 256 ? 1 : 256 / per_parent;
     dim3 grid((unsigned)((n_parents + ppb - 1) / ppb), (unsigned)H_kv);
-    hipLaunchKernelGGL(zha_merge_kernel, grid, dim3(256), zha_merge_lds_bytes(c, R), stream, Sc, Bc, Lc, Sp,
-                       Bp, Lp, cap_c, cap_p, c, R, first_parent, n_parents);
+    const size_t lds = zha_merge_lds_bytes(c, R);
+    if (c <= 8)
+        hipLaunchKernelGGL(zha_merge_kernel<8>, grid, dim3(256), lds, stream, Sc, Bc, Lc, Sp, Bp, Lp, cap_c, cap_p,
+                           c, R, first_parent, n_parents);
+    else if (c <= 16)
+        hipLaunchKernelGGL(zha_merge_kernel<16>, grid, dim3(256), lds, stream, Sc, Bc, Lc, Sp, Bp, Lp, cap_c, cap_p,
+                           c, R, first_parent, n_parents);
+    else
+        hipLaunchKernelGGL(zha_merge_kernel<0>, grid, dim3(256), lds, stream, Sc, Bc, Lc, Sp, Bp, Lp, cap_c, cap_p,
+                           c, R, first_parent, n_parents);
     return hipGetLastError();
 }
 

@@ -36,6 +36,8 @@ CASES = [
     ("light-c6@20001", _w("light", 20001, levels=4, chunk=6)),   # small frontiers only
     ("deep-c3@9000", _w("deep", 9000, levels=5, chunk=3)),       # R=16, orphans at several levels
     ("light-c5@50000", _w("light", 50000, levels=4, chunk=5)),   # level 1 takes the large select + merge
+    ("light-c16@40000", _w("light", 40000, levels=3, chunk=16)),  # R=1 leaves of 16 tokens
+    ("light-c12@30001", _w("light", 30001, levels=3, chunk=12)),  # R=1 leaves of 12 tokens, ragged tail
     ("light@600000", _w("light", 600000, levels=4)),             # level 1 (75,000 slots): scores re-read per pass
     ("light@131072-L2", _w("light", 131072, levels=2)),          # a large top level (2,048 nodes) left unmerged
     ("light-f32@65536", _w("light", 65536, kv_dtype="f32")),     # fp32 cache: the two-per-CU gather at many tiles

@@ -1947,12 +1947,15 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
 
 }  // namespace
 
+#ifndef ZHA_SCORE_CAP
+#define ZHA_SCORE_CAP 128
+#endif
 int zha_score_blocks(int64_t max_cand, int R) {
     const int64_t U = R <= 16 ? 16 / R : 1;
     const int64_t items = (max_cand + U - 1) / U;
     int64_t blocks = (items + 3) / 4;        // one item per wave
     if (blocks < 1) blocks = 1;
-    if (blocks > ZHA_SCORE_MAXB) blocks = ZHA_SCORE_MAXB;
+    if (blocks > ZHA_SCORE_CAP) blocks = ZHA_SCORE_CAP;
     return (int)blocks;
 }
 

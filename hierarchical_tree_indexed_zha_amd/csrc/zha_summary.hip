@@ -540,8 +540,10 @@ __global__ __launch_bounds__(256) void zha_leaf_r1_kernel(
 // ---- long leaves (c a multiple of 32, R <= 16, bfloat16 keys) on bfloat16 products.
 //
 // The reference queries and the softmax weights enter as three bfloat16 parts each
-// (hi + mid + lo is a float32 value exactly: each part is the remainder rounded to
-// 8 significant bits, and what is left after two has at most 8), the keys as they
+// (hi + mid + lo is a float32 value exactly: each part is the remainder cut to its
+// leading 8 significant bits, each remainder is exact (the part and what it is cut
+// from share sign and exponent, so their difference is exact by Sterbenz's lemma),
+// and what is left after two parts has at most 8 significant bits), the keys as they
 // are; the float32 sums of the parts' products are those of the float32 products,
 // at an eighth of the matrix work.  One wave per leaf, tiles of 32 tokens.  Per tile:
 //   Z = tau Q K^T    per 16-token half h and 32-dim block kb, one
@@ -554,14 +556,20 @@ __global__ __launch_bounds__(256) void zha_leaf_r1_kernel(
 //                    16-byte loads of rows 4 e + q, dims 8 j .. 8 j + 7, and output
 //                    column j of block c8 is dim 8 j + c8 (as in the gather's PV).
 // Outputs as the other leaf kernels: S[leaf][r][d], B, LSE (rows r < R).
+typedef unsigned int zha_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kB3QRow = 68;        // LDS row of a query part (u32, two bf16 each): 16-byte aligned
 
+// x = h + m + l exactly, as float32 bit patterns whose low 16 bits are zero (the
+// bfloat16 values in their high halves).
 __device__ __forceinline__ void split3_bf16(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
-    h = zha_f32_to_bf16_rne(x);
-    const float r1 = x - __uint_as_float(h << 16);
-    m = zha_f32_to_bf16_rne(r1);
-    const float r2 = r1 - __uint_as_float(m << 16);
-    l = zha_f32_to_bf16_rne(r2);
+    h = __float_as_uint(x) & 0xFFFF0000u;
+    const float r1 = x - __uint_as_float(h);
+    m = __float_as_uint(r1) & 0xFFFF0000u;
+    l = __float_as_uint(r1 - __uint_as_float(m));
+}
+// The bfloat16 pair {a, b} (a in the low half) from two such patterns.
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 __device__ __forceinline__ uint32_t b3_word(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -573,10 +581,12 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
     int64_t cap_tok, int64_t cap1, int c, int R, int64_t first_leaf, int64_t n_leaves, float tau) {
     __shared__ __align__(16) uint32_t s_q[3][16 * kB3QRow];
     __shared__ float s_w[4][16 * 33];
+    __shared__ __align__(16) uint32_t s_k[4][32 * kB3QRow];   // a wave's key tile: 32 rows of 64 words (+4)
     const int g = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, q = lane >> 4;
     float* sw = s_w[wave];
+    uint32_t* sk = s_k[wave];
     // the reference queries' three parts, rows past R zero
     for (int i = threadIdx.x; i < 16 * (ZHA_D / 2); i += 256) {
         const int r = i / (ZHA_D / 2), dp = i - r * (ZHA_D / 2);
@@ -585,9 +595,9 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
         uint32_t h0, m0, l0, h1, m1, l1;
         split3_bf16(v.x, h0, m0, l0);
         split3_bf16(v.y, h1, m1, l1);
-        s_q[0][r * kB3QRow + dp] = h0 | (h1 << 16);
-        s_q[1][r * kB3QRow + dp] = m0 | (m1 << 16);
-        s_q[2][r * kB3QRow + dp] = l0 | (l1 << 16);
+        s_q[0][r * kB3QRow + dp] = bf16_pair(h0, h1);
+        s_q[1][r * kB3QRow + dp] = bf16_pair(m0, m1);
+        s_q[2][r * kB3QRow + dp] = bf16_pair(l0, l1);
     }
     __syncthreads();
     const int tpl = c / 32;
@@ -600,26 +610,31 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
         zha_f32x4 acc[8];
 #pragma unroll
         for (int c8 = 0; c8 < 8; ++c8) acc[c8] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
-        // key rows 16 h + j of a tile, dims 32 kb + 8 q .. + 7: the next tile's are
-        // requested before the current one is computed
-        uint4 kz[2][4];
-        auto fetch_z = [&](int tt, uint4 (&dst)[2][4]) {
+        // a tile's 32 key rows, loaded once and whole (lane l: 16-byte pieces l + 64 m,
+        // rows 4 m + l / 16), staged in the wave's LDS tile and read back in the two
+        // operand layouts; the next tile's pieces are requested before the current one
+        // is computed
+        // (the last tile requests itself again: every load stays in the leaf)
+        const uint16_t* kt = K + (row0 + (size_t)(lane >> 4)) * ZHA_D + 8 * (lane & 15);
+        zha_u32x4 raw[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) raw[m] = *reinterpret_cast<const zha_u32x4*>(kt + (size_t)(4 * m) * ZHA_D);
+        for (int tt = 0; tt < tpl; ++tt) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                *reinterpret_cast<zha_u32x4*>(sk + (4 * m + (lane >> 4)) * kB3QRow + 4 * (lane & 15)) = raw[m];
+            zha_wave_lds_sync();
+            const int tn = tt + 1 < tpl ? tt + 1 : tt;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                raw[m] = *reinterpret_cast<const zha_u32x4*>(kt + (size_t)(32 * tn + 4 * m) * ZHA_D);
+            // key rows 16 h + j, dims 32 kb + 8 q .. + 7 (the B operand of Q K^T)
+            uint4 kz[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
-                    dst[h][kb] = *reinterpret_cast<const uint4*>(K + (row0 + (size_t)(32 * tt + 16 * h + j)) * ZHA_D +
-                                                                 32 * kb + 8 * q);
-        };
-        fetch_z(0, kz);
-        for (int tt = 0; tt < tpl; ++tt) {
-            // rows 4 e + q of the tile, dims 8 j .. 8 j + 7 (the B operand of W K)
-            uint4 kv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                kv[e] = *reinterpret_cast<const uint4*>(K + (row0 + (size_t)(32 * tt + 4 * e + q)) * ZHA_D + 8 * j);
-            uint4 kzn[2][4];
-            if (tt + 1 < tpl) fetch_z(tt + 1, kzn);
+                    kz[h][kb] = *reinterpret_cast<const uint4*>(sk + (16 * h + j) * kB3QRow + 4 * (4 * kb + q));
             // Z: four independent accumulator chains (half h, parts alternating)
             zha_f32x4 zz[2][2];
 #pragma unroll
@@ -637,7 +652,10 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
                                                                                            zz[h][(kb * 3 + pt) & 1], 0, 0, 0);
                 }
             }
-            // online softmax of refs 4 q + i over tokens j and 16 + j
+            // online softmax of refs 4 q + i over tokens j and 16 + j; the sums are
+            // rescaled only on tiles that raise some lane's running maximum
+            float alph[4];
+            bool grew = false;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float z0 = tau * (zz[0][0][i] + zz[0][1][i]);
@@ -650,22 +668,32 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
                 l_run[i] = l_run[i] * alpha + es;
                 ez_run[i] = ez_run[i] * alpha + ezs;
                 m_run[i] = mn;
-#pragma unroll
-                for (int c8 = 0; c8 < 8; ++c8) acc[c8][i] *= alpha;
+                alph[i] = alpha;
+                grew |= alpha != 1.0f;
                 sw[(4 * q + i) * 33 + j] = e0;
                 sw[(4 * q + i) * 33 + 16 + j] = e1;
             }
+            if (__ballot(grew) != 0ull) {
+#pragma unroll
+                for (int c8 = 0; c8 < 8; ++c8)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[c8][i] *= alph[i];
+            }
             zha_wave_lds_sync();
-            // W (row j, tokens 4 e + q) in three parts; B from the rows' 16-byte loads
+            // rows 4 e + q of the tile, dims 8 j .. 8 j + 7 (the B operand of W K)
+            uint4 kv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kv[e] = *reinterpret_cast<const uint4*>(sk + (4 * e + q) * kB3QRow + 4 * j);
+            // W (row j, tokens 4 e + q) in three parts; B from the tile's rows
             uint32_t wp[3][4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 uint32_t ha, ma, la, hb, mb, lb;
                 split3_bf16(sw[j * 33 + 4 * (2 * e2) + q], ha, ma, la);
                 split3_bf16(sw[j * 33 + 4 * (2 * e2 + 1) + q], hb, mb, lb);
-                wp[0][e2] = ha | (hb << 16);
-                wp[1][e2] = ma | (mb << 16);
-                wp[2][e2] = la | (lb << 16);
+                wp[0][e2] = bf16_pair(ha, hb);
+                wp[1][e2] = bf16_pair(ma, mb);
+                wp[2][e2] = bf16_pair(la, lb);
             }
             const zha_bf16x8 wa0 = zha_as_bf16x8(make_uint4(wp[0][0], wp[0][1], wp[0][2], wp[0][3]));
             const zha_bf16x8 wa1 = zha_as_bf16x8(make_uint4(wp[1][0], wp[1][1], wp[1][2], wp[1][3]));
@@ -683,13 +711,7 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
                 acc[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa1, bv, acc[c8], 0, 0, 0);
                 acc[c8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa2, bv, acc[c8], 0, 0, 0);
             }
-            zha_wave_lds_sync();                        // the next tile rewrites sw
-            if (tt + 1 < tpl) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) kz[h][kb] = kzn[h][kb];
-            }
+            zha_wave_lds_sync();                        // the next tile rewrites sw and sk
         }
         // S[leaf][r][8 j .. 8 j + 7] = acc / l; B and LSE from the running sums
 #pragma unroll

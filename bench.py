@@ -286,7 +286,8 @@ def bench_workload(args, torch, W, B, ZhaLayer):
 def build_device(layer, N, w, torch, reps=3):
     """The tree build's device time (HIP events around zha_build_tree, best of reps) and its
     algorithmic bytes: the keys read once, every level's planes (s, b, lse) written, and
-    the child planes each merge reads."""
+    the child planes each merge launch reads (none at level 2 where the leaf kernel
+    writes the level-2 nodes itself: 4 <= R <= 16 with c in {2, 4})."""
     ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -300,10 +301,11 @@ def build_device(layer, N, w, torch, reps=3):
     e_kv = 2 if w.kv_dtype == "bf16" else 4
     node = R * (d + 2) * 4
     byts = H * N * d * e_kv
+    fused = 4 <= R <= 16 and c in (2, 4)
     for lv in range(1, w.levels + 1):
         n = N // c ** lv
         byts += H * n * node                      # written
-        if lv > 1:
+        if lv > 2 or (lv == 2 and not fused):
             byts += H * n * c * node              # children read by the merge
     return {"us": round(us, 2), "alg_bytes": int(byts), "gbs": round(byts / (us * 1e-6) / 1e9, 1)}
 

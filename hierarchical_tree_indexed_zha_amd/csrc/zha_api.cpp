@@ -322,18 +322,25 @@ int zha_build_tree(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tok
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int c = cfg->chunk, R = cfg->n_ref;
     float* T = static_cast<float*>(bufs->tree);
+    // the leaf kernels that hold whole level-2 nodes write those as well (fused = 1)
+    const bool two = y.L >= 2 && n_nodes(cfg, n_tokens, 2) > 0;
+    int fused = 0;
     hipError_t e = zha_launch_leaf_summary(
         cfg->kv_dtype, bufs->k, bufs->ref_q, (float*)at(T, y.t_s[1]), (float*)at(T, y.t_b[1]), (float*)at(T, y.t_l[1]),
-        y.H, cfg->capacity, y.cap[1], c, R, 0, n_nodes(cfg, n_tokens, 1), tau_of(cfg), s);
+        y.H, cfg->capacity, y.cap[1], c, R, 0, n_nodes(cfg, n_tokens, 1), tau_of(cfg),
+        two ? (float*)at(T, y.t_s[2]) : nullptr, two ? (float*)at(T, y.t_b[2]) : nullptr,
+        two ? (float*)at(T, y.t_l[2]) : nullptr, two ? y.cap[2] : 0, &fused, s);
     if (e != hipSuccess) return hip_fail(e, "leaf summary launch");
     if ((rc = planes16(cfg, y, T, 1, 0, n_nodes(cfg, n_tokens, 1), s))) return rc;
     for (int l = 2; l <= y.L; ++l) {
         const int64_t n = n_nodes(cfg, n_tokens, l);
         if (n == 0) break;
-        e = zha_launch_merge((float*)at(T, y.t_s[l - 1]), (float*)at(T, y.t_b[l - 1]), (float*)at(T, y.t_l[l - 1]),
-                             (float*)at(T, y.t_s[l]), (float*)at(T, y.t_b[l]), (float*)at(T, y.t_l[l]), y.H,
-                             y.cap[l - 1], y.cap[l], c, R, 0, n, s);
-        if (e != hipSuccess) return hip_fail(e, "merge launch");
+        if (!(l == 2 && fused)) {
+            e = zha_launch_merge((float*)at(T, y.t_s[l - 1]), (float*)at(T, y.t_b[l - 1]),
+                                 (float*)at(T, y.t_l[l - 1]), (float*)at(T, y.t_s[l]), (float*)at(T, y.t_b[l]),
+                                 (float*)at(T, y.t_l[l]), y.H, y.cap[l - 1], y.cap[l], c, R, 0, n, s);
+            if (e != hipSuccess) return hip_fail(e, "merge launch");
+        }
         if ((rc = planes16(cfg, y, T, l, 0, n, s))) return rc;
     }
     return ok();
@@ -359,7 +366,7 @@ int zha_append_token(const zha_config* cfg, const zha_buffers* bufs, int64_t n_b
     float* T = static_cast<float*>(bufs->tree);
     e = zha_launch_leaf_summary(cfg->kv_dtype, bufs->k, bufs->ref_q, (float*)at(T, y.t_s[1]), (float*)at(T, y.t_b[1]),
                                 (float*)at(T, y.t_l[1]), y.H, cfg->capacity, y.cap[1], c, R, n / c - 1, 1,
-                                tau_of(cfg), s);
+                                tau_of(cfg), nullptr, nullptr, nullptr, 0, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "leaf summary launch");
     if ((rc = planes16(cfg, y, T, 1, n / c - 1, 1, s))) return rc;
     for (int l = 2; l <= y.L; ++l) {

@@ -8,9 +8,15 @@
 // ---- summary tree (zha_summary.hip)
 size_t zha_leaf_summary_lds_bytes(int R);
 size_t zha_merge_lds_bytes(int c, int R);
+// Leaves [first_leaf, first_leaf + n_leaves).  With Sp non-null and first_leaf a
+// multiple of c, a kernel that holds whole level-2 nodes (the matrix-core kernel at
+// 4 <= R <= 16 with c in {2, 4}) also writes the summaries of the
+// level-2 nodes made wholly of these leaves into Sp, Bp, Lp (capacity cap2) and sets
+// *fused to 1; otherwise *fused is 0 and the caller merges them.
 hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qref, float* S, float* B,
                                    float* LSE, int H_kv, int64_t cap_tok, int64_t cap1, int c, int R,
-                                   int64_t first_leaf, int64_t n_leaves, float tau, hipStream_t stream);
+                                   int64_t first_leaf, int64_t n_leaves, float tau, float* Sp, float* Bp, float* Lp,
+                                   int64_t cap2, int* fused, hipStream_t stream);
 hipError_t zha_launch_merge(const float* Sc, const float* Bc, const float* Lc, float* Sp, float* Bp, float* Lp,
                             int H_kv, int64_t cap_c, int64_t cap_p, int c, int R, int64_t first_parent,
                             int64_t n_parents, hipStream_t stream);

@@ -211,7 +211,13 @@ __global__ __launch_bounds__(256) void zha_leaf_summary_kernel(
 //   S += W K           per 16-column slice, the tile's tokens in groups of four:
 //                      W from LDS as the A operand (row r, token 4 kk + q4), K from
 //                      LDS as the B operand (token 4 kk + q4, column 16 s + j).
-// Outputs as the scalar kernel's: S[leaf][r][d], B, LSE (rows r < R).
+// Outputs as the scalar kernel's: S[leaf][r][d], B, LSE (rows r < R).  With `fuse`
+// (c in {2, 4}: a unit holds 16 / c^2 whole level-2 nodes; first_leaf a multiple of
+// c) the unit's level-2 nodes are written too, merged as the merge kernel does: per
+// ref, the node's LSE is the log-sum-exp of its leaves' (one lane per leaf segment
+// over the node's c^2 lanes), a = exp(LSE_leaf - LSE_node), b = sum a (b_leaf - log a),
+// and s = sum over the node's tokens of (a w) k, one more pass of the products with
+// each token's weight scaled by its leaf's a (which the token's own lane holds).
 constexpr int kLmMinR = 4;         // fewer reference queries leave most MFMA rows empty:
                                    // the scalar kernel is faster there (measured at R = 1)
 constexpr int kLmStride = 144;     // LDS row of a staged key tile (floats): the B reads of
@@ -248,7 +254,8 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
     const void* __restrict__ Kv, const float* __restrict__ Qref,
     float* __restrict__ S, float* __restrict__ B, float* __restrict__ LSE,
-    int64_t cap_tok, int64_t cap1, int c, int R, int64_t first_leaf, int64_t n_leaves, float tau) {
+    int64_t cap_tok, int64_t cap1, int c, int R, int64_t first_leaf, int64_t n_leaves, float tau,
+    float* __restrict__ Sp, float* __restrict__ Bp, float* __restrict__ Lp, int64_t cap2, int fuse) {
     __shared__ __align__(16) float s_k[4][16 * kLmStride];
     __shared__ float s_w[4][16 * 17];
     __shared__ __align__(16) float s_q[16 * kLmStride];
@@ -340,6 +347,7 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
             for (int i = 0; i < 4; ++i) z4[i] = (zc[0][i] + zc[1][i]) + (zc[2][i] + zc[3][i]);
             const bool tv = j < ntok;
             float w[4];
+            float ap[4];                                // this token's leaf's weight in its level-2 node
             if (c <= 16) {
                 // one leaf per c lanes: its log-sum-exp, weights and offset
 #pragma unroll
@@ -357,6 +365,25 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
                         const size_t o = ((size_t)g * cap1 + (size_t)(leaf0 + j / c)) * R + r;
                         LSE[o] = lse;
                         B[o] = lse - wz;
+                    }
+                    ap[i] = 0.f;
+                    if (fuse) {
+                        // the node of c leaves over lanes j / c^2: one lane per leaf segment
+                        const int cc = c * c;
+                        const bool head = (j & (c - 1)) == 0;
+                        const float mp = seg_max(lse, cc);
+                        const float sp = seg_sum(head ? expf(lse - mp) : 0.f, cc);
+                        const float lp = mp + logf(sp);
+                        const float la = lse - lp;              // log a of this lane's leaf
+                        const float a = expf(la);
+                        const float bp = seg_sum(head ? a * ((lse - wz) - la) : 0.f, cc);
+                        ap[i] = a;
+                        const int np = j / cc;                  // the node within the unit
+                        if ((j & (cc - 1)) == 0 && (np + 1) * cc <= ntok && r < R) {
+                            const size_t o = ((size_t)g * cap2 + (size_t)((leaf0 + np * c) / c)) * R + r;
+                            Lp[o] = lp;
+                            Bp[o] = bp;
+                        }
                     }
                 }
             } else {
@@ -411,6 +438,35 @@ __global__ __launch_bounds__(256) void zha_leaf_mfma_kernel(
                         if (r < R)
 #pragma unroll
                             for (int sl = 0; sl < 8; ++sl) so[r * ZHA_D + 16 * sl + j] = o[sl][i];
+                    }
+                }
+                if (fuse) {
+                    // the unit's whole level-2 nodes: tokens weighted by a w
+                    const int cc = c * c;
+                    zha_wave_lds_sync();                // every read of sw above is done
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sw[(4 * q4 + i) * 17 + j] = w[i] * ap[i];
+                    zha_wave_lds_sync();
+                    // (acc, the running sums of leaves longer than a tile, is free here)
+                    for (int np = 0; (np + 1) * cc <= ntok; ++np) {
+#pragma unroll
+                        for (int sl = 0; sl < 8; ++sl) acc[sl] = zha_f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int kk = (np * cc) >> 2; kk <= ((np + 1) * cc - 1) >> 2; ++kk) {
+                            const int tok = 4 * kk + q4;
+                            const float a = (tok >= np * cc && tok < (np + 1) * cc) ? sw[j * 17 + tok] : 0.f;
+#pragma unroll
+                            for (int sl = 0; sl < 8; ++sl)
+                                acc[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sk[tok * kLmStride + 16 * sl + j],
+                                                                               acc[sl], 0, 0, 0);
+                        }
+                        float* po = Sp + ((size_t)g * cap2 + (size_t)((leaf0 + np * c) / c)) * R * ZHA_D;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 4 * q4 + i;
+                            if (r < R)
+#pragma unroll
+                                for (int sl = 0; sl < 8; ++sl) po[r * ZHA_D + 16 * sl + j] = acc[sl][i];
+                        }
                     }
                 }
             }
@@ -919,8 +975,11 @@ size_t zha_leaf_summary_lds_bytes(int R) {
 
 hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qref, float* S, float* B,
                                    float* LSE, int H_kv, int64_t cap_tok, int64_t cap1, int c, int R,
-                                   int64_t first_leaf, int64_t n_leaves, float tau, hipStream_t stream) {
+                                   int64_t first_leaf, int64_t n_leaves, float tau, float* Sp, float* Bp, float* Lp,
+                                   int64_t cap2, int* fused, hipStream_t stream) {
+    if (fused) *fused = 0;
     if (n_leaves <= 0) return hipSuccess;
+    const bool aligned = Sp != nullptr && fused != nullptr && first_leaf % c == 0;
     if (kv_dtype == 0 && R == 1 && c <= kR1MaxC) {
         // one reference query, short leaves: the streaming kernel, 32 leaves per workgroup
         int64_t blocks = (n_leaves + 31) / 32;
@@ -952,12 +1011,14 @@ hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qre
         int64_t blocks = (units + 3) / 4;
         if (blocks > 2048) blocks = 2048;
         dim3 grid((unsigned)blocks, (unsigned)H_kv);
+        const int fuse = aligned && (c == 2 || c == 4) ? 1 : 0;
         if (kv_dtype == 0)
             hipLaunchKernelGGL(zha_leaf_mfma_kernel<true>, grid, dim3(256), 0, stream, K, Qref, S, B, LSE, cap_tok,
-                               cap1, c, R, first_leaf, n_leaves, tau);
+                               cap1, c, R, first_leaf, n_leaves, tau, Sp, Bp, Lp, cap2, fuse);
         else
             hipLaunchKernelGGL(zha_leaf_mfma_kernel<false>, grid, dim3(256), 0, stream, K, Qref, S, B, LSE, cap_tok,
-                               cap1, c, R, first_leaf, n_leaves, tau);
+                               cap1, c, R, first_leaf, n_leaves, tau, Sp, Bp, Lp, cap2, fuse);
+        if (fuse) *fused = 1;
         return hipGetLastError();
     }
     const int64_t lpb = c <= kTile ? kTile / c : 1;

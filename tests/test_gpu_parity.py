@@ -35,6 +35,9 @@ CASES = [
     # chunk sizes that are not powers of two (parent index and child offset by division)
     ("light-c6@20001", _w("light", 20001, levels=4, chunk=6)),   # small frontiers only
     ("deep-c3@9000", _w("deep", 9000, levels=5, chunk=3)),       # R=16, orphans at several levels
+    # level-2 nodes written by the matrix-core leaf kernel (c in {2, 4})
+    ("deep-c2@9001", _w("deep", 9001, levels=5, chunk=2)),       # four nodes per 16-token unit, odd tail
+    ("deep@20011", _w("deep", 20011, levels=5)),                 # last unit: two leaves, no whole node
     ("light-c5@50000", _w("light", 50000, levels=4, chunk=5)),   # level 1 takes the large select + merge
     ("light-c16@40000", _w("light", 40000, levels=3, chunk=16)),  # R=1 leaves of 16 tokens
     ("light-c12@30001", _w("light", 30001, levels=3, chunk=12)),  # R=1 leaves of 12 tokens, ragged tail

@@ -47,6 +47,7 @@
 // its parent's kept-list entry (or, below an unmerged level, from that level's
 // bitmaps staged in LDS).
 #include <algorithm>
+#include <type_traits>
 
 #include "zha_common.h"
 #include "zha_internal.h"
@@ -882,20 +883,30 @@ __device__ __forceinline__ void rank_entries(CutShared* st, int ne, uint64_t nee
 // kSweepB per thread whose keys are all read before any is used: the visitors'
 // LDS atomics and stores would otherwise order each later key read after them.
 constexpr int kSweepB = 8;
-template <class KF, class F>
+template <class KF, class F, int NB = kSweepB>
 __device__ __forceinline__ void sweep_keys(const KF& key_at, int n, F&& f) {
 #pragma unroll 1
-    for (int base = threadIdx.x; base < n; base += kSweepB * kBT) {
-        uint32_t kk[kSweepB];
+    for (int base = threadIdx.x; base < n; base += NB * kBT) {
+        uint32_t kk[NB];
 #pragma unroll
-        for (int j = 0; j < kSweepB; ++j) {
+        for (int j = 0; j < NB; ++j) {
             const int p = base + j * kBT;
             kk[j] = kNotCand;
             if (p < n) kk[j] = key_at(p);
         }
 #pragma unroll
-        for (int j = 0; j < kSweepB; ++j) f(kk[j], base + j * kBT);
+        for (int j = 0; j < NB; ++j) f(kk[j], base + j * kBT);
     }
+}
+
+// Calls f with the batch size of a sweep over n positions: one key per thread
+// up to kBT positions, four up to 4 kBT, else kSweepB (no batch slot that lies
+// past n for every thread).
+template <class F>
+__device__ __forceinline__ void with_batch(int n, F&& f) {
+    if (n <= kBT) f(std::integral_constant<int, 1>{});
+    else if (n <= 4 * kBT) f(std::integral_constant<int, 4>{});
+    else f(std::integral_constant<int, kSweepB>{});
 }
 
 // The cut of one head: kept iff key < ustar, or key == ustar and p <= plim.  With
@@ -949,9 +960,10 @@ __device__ bool block_cut(const KF& key_at, const PF& pos_at, int n, float top_p
         hist[2 * tid] = 0ull;
         hist[2 * tid + 1] = 0ull;
         __syncthreads();
-        sweep_keys(key_at, n, [&](uint32_t k, int) {
+        const auto add = [&](uint32_t k, int) {
             if (k < kNoMass) atomicAdd((unsigned long long*)&hist[k >> 21], (unsigned long long)mass_of(k));
-        });
+        };
+        with_batch(n, [&](auto nbc) { sweep_keys<KF, decltype(add) const&, decltype(nbc)::value>(key_at, n, add); });
         __syncthreads();
     }
     int nl = -1;                               // >= 0: the crossing keys of an earlier pass are gl[0, nl)
@@ -977,13 +989,14 @@ __device__ bool block_cut(const KF& key_at, const PF& pos_at, int n, float top_p
         // rank table, the first kGather to the list while none is kept yet; each adds
         // its mass to the next digit's histogram
         const bool listing = nl < 0;
-        const auto append = [&](const uint32_t* kk, const int* pp, int nb) {
-            bool in[kSweepB];
-            uint64_t bal[kSweepB];
+        const auto append = [&](const uint32_t* kk, const int* pp, auto nbc) {
+            constexpr int NB = decltype(nbc)::value;
+            bool in[NB];
+            uint64_t bal[NB];
             uint32_t tot = 0;
 #pragma unroll
-            for (int j = 0; j < kSweepB; ++j) {
-                in[j] = j < nb && (kk[j] < kNoMass) & ((kk[j] >> shift) == pref);
+            for (int j = 0; j < NB; ++j) {
+                in[j] = (kk[j] < kNoMass) & ((kk[j] >> shift) == pref);
                 bal[j] = __ballot(in[j]);
                 tot += (uint32_t)__popcll(bal[j]);
             }
@@ -992,7 +1005,7 @@ __device__ bool block_cut(const KF& key_at, const PF& pos_at, int n, float top_p
             if (lane == 0) e0 = atomicAdd(&st->nent, tot);
             e0 = (uint32_t)__shfl((int)e0, 0);
 #pragma unroll
-            for (int j = 0; j < kSweepB; ++j) {
+            for (int j = 0; j < NB; ++j) {
                 if (in[j]) {
                     const uint32_t k = kk[j];
                     const uint32_t e = e0 + bits_below_lane(bal[j]);
@@ -1005,29 +1018,32 @@ __device__ bool block_cut(const KF& key_at, const PF& pos_at, int n, float top_p
             }
         };
         if (!listing) {
-            uint32_t kk[kSweepB];
-            int pp[kSweepB];
+            uint32_t kk[1];
+            int pp[1];
             const uint2 le = tid < nl ? gl[tid] : make_uint2(kNotCand, 0u);
             kk[0] = le.x;
             pp[0] = (int)le.y;
-            append(kk, pp, 1);
+            append(kk, pp, std::integral_constant<int, 1>{});
         } else {
+            with_batch(n, [&](auto nbc) {
+                constexpr int NB = decltype(nbc)::value;
 #pragma unroll 1
-            for (int base = tid; base - tid < n; base += kSweepB * kBT) {   // uniform
-                uint32_t kk[kSweepB];
-                int pp[kSweepB];
+                for (int base = tid; base - tid < n; base += NB * kBT) {   // uniform
+                    uint32_t kk[NB];
+                    int pp[NB];
 #pragma unroll
-                for (int j = 0; j < kSweepB; ++j) {
-                    const int i = base + j * kBT;
-                    kk[j] = kNotCand;
-                    pp[j] = 0;
-                    if (i < n) {
-                        kk[j] = key_at(i);
-                        pp[j] = (int)pos_at(i);
+                    for (int j = 0; j < NB; ++j) {
+                        const int i = base + j * kBT;
+                        kk[j] = kNotCand;
+                        pp[j] = 0;
+                        if (i < n) {
+                            kk[j] = key_at(i);
+                            pp[j] = (int)pos_at(i);
+                        }
                     }
+                    append(kk, pp, nbc);
                 }
-                append(kk, pp, kSweepB);
-            }
+            });
         }
         __syncthreads();
         const uint32_t ne = st->nent;

@@ -1198,12 +1198,14 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
         __syncthreads();
     }
     int nk = 0;
+    int so = 0;                                // soff[li], kept as a running sum
 #pragma unroll 1
     for (int li = 0; li < m.n; ++li) {
         const ZhaChainLevel& L = m.lv[li];
         const int n = li == 0 ? L.n_nodes : nk * c + (L.orph_hi - L.orph_lo);
         const float* sg = L.sig + ((size_t)g * G + hl) * (size_t)L.sstride;
-        const float* ss = s_sig + soff[li];
+        const float* ss = s_sig + so;
+        so += (L.n_nodes + 3) / 4 * 4;
         // (rows of 1024 positions wholly past n are skipped: a uniform branch)
         float x[kChainPer];
 #pragma unroll
@@ -1964,7 +1966,7 @@ __global__ __launch_bounds__(kApplyThreads) void zha_apply_kernel(ZhaLevelArgs a
 }  // namespace
 
 #ifndef ZHA_SCORE_CAP
-#define ZHA_SCORE_CAP 128
+#define ZHA_SCORE_CAP 192
 #endif
 int zha_score_blocks(int64_t max_cand, int R) {
     const int64_t U = R <= 16 ? 16 / R : 1;

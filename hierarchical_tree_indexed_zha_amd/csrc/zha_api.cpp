@@ -197,9 +197,11 @@ int planes16(const zha_config* cfg, const Layout& y, void* T, int l, int64_t fir
     return e == hipSuccess ? ZHA_OK : hip_fail(e, "plane copy launch");
 }
 
-// Attention workgroups per KV group: about 8 tiles of 32 slots each, at most one
-// resident round of the whole device (768 workgroups: 256 CUs x 3 resident) so
-// that no partial second round trails the launch.
+// Attention workgroups per KV group: one per 8 tiles of 32 slots over every
+// cached token, at most one resident round of the whole device (768 workgroups:
+// 256 CUs x 3 resident) so that no partial second round trails the launch.  The
+// kernel then activates one of them per 4 tiles of the slots it actually reads
+// (kMinTilesPerBlock), up to this grid.
 int attn_blocks(int64_t n_slots, int H, int kv_dtype) {
     const int64_t tiles = (n_slots + 31) / 32;
     int64_t b = (tiles + 7) / 8;

@@ -36,7 +36,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileSlots = 32;
-constexpr int kMinTilesPerBlock = 8;
+#ifndef ZHA_ATTN_MIN_TILES
+#define ZHA_ATTN_MIN_TILES 4
+#endif
+constexpr int kMinTilesPerBlock = ZHA_ATTN_MIN_TILES;   // fewest 32-slot tiles a split block takes
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Byte permute: bytes of (hi_src:lo_src) picked by `sel` (v_perm_b32).

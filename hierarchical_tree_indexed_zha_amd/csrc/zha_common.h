@@ -10,8 +10,12 @@
 #define ZHA_ATTN_MAXB 512    // max attention split blocks per KV group
 // gather workgroups resident per compute unit: three for bf16 K/V; two for fp32,
 // whose wider rows need the registers of the lower occupancy
+#ifndef ZHA_ATTN_BLOCKS_BF16
 #define ZHA_ATTN_BLOCKS_BF16 3
+#endif
+#ifndef ZHA_ATTN_BLOCKS_F32
 #define ZHA_ATTN_BLOCKS_F32 2
+#endif
 
 typedef __attribute__((ext_vector_type(8))) __bf16 zha_bf16x8;
 typedef __attribute__((ext_vector_type(4))) float zha_f32x4;

@@ -423,6 +423,13 @@ def trace_kernels(args, layer, x, w, torch, B):
             scored = [lv for k, lv in kinds_l if k == "score"]
             low = (max(scored) + 1) if scored else 1
             chain_lv = list(range(low, top + 1))
+        # the first level below the chain, when the chain launch scored its every node
+        # (its streamed bytes then exceed its candidates' bytes)
+        spec_lv = None
+        if chain_lv and min(chain_lv) > 1:
+            lb = min(chain_lv) - 1
+            if st["bytes_streamed"][lb - 1] != st["bytes_read"][lb - 1]:
+                spec_lv = lb
         for i in range(1, len(kinds_l)):
             name, lv = kinds_l[i]
             us = evs[i - 1].elapsed_time(evs[i]) * 1e3
@@ -430,6 +437,10 @@ def trace_kernels(args, layer, x, w, torch, B):
                 byts = sum(st["bytes_streamed"][l - 1] + (N // c ** l) * w.n_q_heads * 4 for l in chain_lv)
             elif name == "chain":
                 byts = sum((N // c ** l) * w.n_q_heads * 4 for l in chain_lv)
+                if spec_lv:
+                    byts += st["bytes_streamed"][spec_lv - 1] + (N // c ** spec_lv) * w.n_q_heads * 4
+            elif name == "score" and lv == spec_lv:
+                byts = 2 * st["group_cand"][lv - 1] * G * 4     # node-indexed scores copied to the candidates
             elif name == "score":
                 byts = st["bytes_read"][lv - 1] + st["group_cand"][lv - 1] * G * 4
             elif name == "select":

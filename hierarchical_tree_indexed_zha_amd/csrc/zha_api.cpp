@@ -98,6 +98,7 @@ struct Layout {
     std::vector<size_t> sig, kbm, klist, kmask, ncand, nkept, stats;
     std::vector<size_t> hblk, ghist, hdone, hcut, tick, desc;   // selection state of a level below the chain
     std::vector<size_t> pub, gcnt, gpart, glist;  // frontiers beyond ZHA_LDS_KEYS (glist 0: the level never has one)
+    std::vector<size_t> sign;             // node-indexed scores of a level scored during the chain (0: none)
     std::vector<int64_t> wcap;            // bitmap words per head per level
     std::vector<int64_t> sstr;            // score row stride per level (slots rounded up to 4)
     size_t pm = 0, pl = 0, po = 0, nact = 0;
@@ -112,6 +113,15 @@ void attn_partials(const zha_config* cfg, size_t& off, size_t& pm, size_t& pl, s
     pl = off; off = align_up(off + sizeof(float) * H * ZHA_ATTN_MAXB * G);
     po = off; off = align_up(off + sizeof(float) * H * ZHA_ATTN_MAXB * G * ZHA_D);
     nact = off; off = align_up(off + sizeof(int32_t) * H);
+}
+
+// A level of n nodes per KV group may be scored whole while the chain above it
+// selects: its float32 planes over every group within kSpecBytes, and compute
+// units left over by the chain's H x G selecting workgroups.
+constexpr size_t kSpecBytes = 96ull << 20;
+constexpr int kSpecCUs = 256;
+bool spec_fits(size_t n, size_t R, size_t H, size_t G) {
+    return n * R * (sizeof(float) * ZHA_D + sizeof(float)) * H <= kSpecBytes && H * G + H <= (size_t)kSpecCUs;
 }
 
 Layout make_layout(const zha_config* cfg) {
@@ -143,7 +153,7 @@ Layout make_layout(const zha_config* cfg) {
 
     off = 0;
     for (auto* v : {&y.sig, &y.kbm, &y.klist, &y.kmask, &y.ncand, &y.nkept, &y.stats, &y.hblk, &y.ghist, &y.hdone, &y.hcut,
-                    &y.tick, &y.desc, &y.pub, &y.gcnt, &y.gpart, &y.glist})
+                    &y.tick, &y.desc, &y.pub, &y.gcnt, &y.gpart, &y.glist, &y.sign})
         v->assign(y.L + 1, 0);
     y.wcap.assign(y.L + 1, 0);
     y.sstr.assign(y.L + 1, 0);
@@ -164,6 +174,9 @@ Layout make_layout(const zha_config* cfg) {
         y.hcut[l] = off;  off = align_up(off + 16 * H * G);
         y.tick[l] = off;  off = align_up(off + sizeof(uint32_t) * H);
         y.desc[l] = off;  off = align_up(off + sizeof(uint32_t) * H * (size_t)zha_apply_chunks((int64_t)n));
+        if (spec_fits(n, R, H, G)) {
+            y.sign[l] = off; off = align_up(off + sizeof(float) * H * G * (size_t)y.sstr[l]);
+        }
         if (n > (size_t)ZHA_LDS_KEYS) {
             y.pub[l] = off;   off = align_up(off + 16 * H * G);
             y.gcnt[l] = off;  off = align_up(off + 16 * H * G);
@@ -487,6 +500,9 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
     // query head's workgroup selects them top-down.
     const int nchain = chain_levels(cfg, n_tokens, top);
     const int below = top - nchain;            // the next level to route (0: none)
+    // the level below the chain, scored whole during the chain when it fits
+    const int spec = (nchain > 0 && below >= 1 && y.sign[below] &&
+                      spec_fits((size_t)n_nodes(cfg, n_tokens, below), R, y.H, y.G)) ? below : 0;
     if (nchain > 0) {
         ZhaChainArgs sa{};
         ZhaChainSel cs{};
@@ -506,11 +522,35 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             cl.wcap = (int32_t)y.wcap[l];
             cl.sstride = (int32_t)y.sstr[l];
         }
+        cs.nsel = y.H * y.G;
+        cs.q = q;
+        cs.R = R;
+        cs.tau = tau;
+        if (spec >= 1) {
+            // the level below scored whole by the chain launch's other workgroups
+            ZhaLevelArgs& sp = cs.spec;
+            sp = level_args(spec);
+            sp.top = 1;
+            sp.n_top = n_nodes(cfg, n_tokens, spec);
+            sp.pklist = (const int32_t*)(X + y.noparent);
+            sp.pkmask = (const uint32_t*)(X + y.noparent);
+            sp.pnkept = (const int32_t*)(X + y.noparent);
+            sp.pcap = 1;
+            sp.orph_lo = sp.orph_hi = 0;
+            sp.sig = (float*)(X + y.sign[spec]);
+            // (its count as a first routed level, rewritten by the level's score kernel)
+            sp.ncand = (int32_t*)(X + y.ncand[spec]);
+            // workgroups of 16 waves (one item of 16 / R nodes per wave and round), at
+            // most the compute units the selecting workgroups leave
+            const int64_t U = R <= 16 ? 16 / R : 1;
+            const int64_t items = (sp.n_top + U - 1) / U;
+            cs.spec_blocks = (int)std::min<int64_t>((kSpecCUs - y.H * y.G) / y.H, (items + 15) / 16);
+        }
         if ((rc = TR.mark(0, top, s))) return rc;
         hipError_t e = zha_launch_score_all(cfg->kv_dtype, q, sa, y.H, y.G, c, R, tau, s);
         if (e != hipSuccess) return hip_fail(e, "score launch (chain)");
         if ((rc = TR.mark(ZHA_TRACE_SCORE_ALL, top, s))) return rc;
-        e = zha_launch_chain(cs, y.H, y.G, c, cfg->top_p, s);
+        e = zha_launch_chain(cfg->kv_dtype, cs, y.H, y.G, c, cfg->top_p, s);
         if (e != hipSuccess) return hip_fail(e, "chain launch");
         if ((rc = TR.mark(ZHA_TRACE_CHAIN, top, s))) return rc;
         if (below == 0) {
@@ -547,6 +587,10 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
         a.score_blocks = blocks;
         ZhaLevelArgs pa{};
         const bool defer = nchain > 0 && l == below;
+        if (l == spec) {
+            a.sigN = (const float*)(X + y.sign[l]);
+            a.nstride = y.sstr[l];
+        }
         if (defer) {
             // the chain's last level: positions are node ids, per-head bitmaps over them
             pa = level_args(l + 1);
@@ -619,6 +663,7 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             r.hstats[l - 1] = (const int32_t*)(X + y.stats[l]);
             r.routed[l - 1] = n_nodes(cfg, n_tokens, l) > 0 ? 1 : 0;
             r.all_nodes[l - 1] = (l <= top && top - l < nchain) ? n_nodes(cfg, n_tokens, l) : 0;
+            r.spec_nodes[l - 1] = l == spec ? n_nodes(cfg, n_tokens, l) : 0;
             r.kbm[l - 1] = (const uint64_t*)(X + y.kbm[l]);
             r.wcap[l - 1] = (int32_t)y.wcap[l];
             r.n_nodes[l - 1] = n_nodes(cfg, n_tokens, l);

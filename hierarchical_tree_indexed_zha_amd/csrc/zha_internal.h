@@ -106,13 +106,17 @@ struct ZhaLevelArgs {
     uint32_t* tick;            // [H_kv] apply chunks started
     uint32_t* desc;            // [H_kv][ndesc] look-back descriptors of the apply chunks
     int ndesc;                 // apply chunks per group at this level's capacity
+    // the level's every node already scored (node-indexed [H_kv][G][nstride], or
+    // null): the score kernel then copies its candidates' scores from there
+    const float* sigN;
+    int64_t nstride;
 };
 // One field in each 64-byte line of a level's arguments, and the arguments that
 // follow them, demanded at kernel entry: the argument loads then go out in one
 // batch (the compiler otherwise fetches them in dependent rounds behind uniform
 // branches, each a memory round trip on a cold argument line).
 #define ZHA_LEVEL_ARGS_READY(a, ...) \
-    asm volatile("" ::"s"((a).S), "s"((a).pcap), "s"((a).wcap), "s"((a).hblk), "s"((a).ndesc), __VA_ARGS__)
+    asm volatile("" ::"s"((a).S), "s"((a).pcap), "s"((a).wcap), "s"((a).hblk), "s"((a).nstride), __VA_ARGS__)
 #define ZHA_LDS_KEYS 32768     // a head's keys staged in LDS by the workgroup that cuts it
 #define ZHA_GLIST 16384        // a large frontier's crossing-bin keys listed per head
 #define ZHA_CROSS_MAXW 32      // cross workgroups per head
@@ -160,10 +164,21 @@ struct ZhaChainLevel {                // selecting one chained level
 struct ZhaChainSel {
     ZhaChainLevel lv[ZHA_MAX_CHAIN];
     int n;
+    // spec_blocks > 0: workgroups past the H_kv x G selecting ones score every
+    // node of the level below the chain (spec: its arguments as a first routed
+    // level, sig = the node-indexed scores), spec_blocks per KV group, on the
+    // compute units the selection leaves idle
+    int nsel;                          // selecting workgroups: (virtual) KV groups x G
+    int spec_blocks;
+    ZhaLevelArgs spec;
+    const void* q;
+    int R;
+    float tau;
 };
 hipError_t zha_launch_score_all(int kv_dtype, const void* q, const ZhaChainArgs& m, int H_kv, int G, int c, int R,
                                 float tau, hipStream_t stream);
-hipError_t zha_launch_chain(const ZhaChainSel& m, int H_kv, int G, int c, float top_p, hipStream_t stream);
+hipError_t zha_launch_chain(int kv_dtype, const ZhaChainSel& m, int H_kv, int G, int c, float top_p,
+                            hipStream_t stream);
 // the group kept list of a chained level 1 (bitmaps over node ids; a.top = 1)
 hipError_t zha_launch_merge_ids(const ZhaLevelArgs& a, int H_kv, int G, int c, hipStream_t stream);
 
@@ -213,6 +228,7 @@ struct ZhaReportArgs {
     const int32_t* nkept[32];    // [H_kv] nodes kept by some head
     const int32_t* hstats[32];   // [H_q][2] per head: candidates, kept
     int64_t all_nodes[32];       // > 0: a chained level, its every node scored (its count per head)
+    int64_t spec_nodes[32];      // > 0: the level below the chain, its every node scored during the chain
     int64_t n_nodes[32];         // complete nodes per head
     const uint64_t* kbm[32];     // chained levels: per-head kept bitmaps over node ids [H_kv][G][wcap]
     int32_t wcap[32];

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(256) void zha_stats_kernel(ZhaReportArgs r, zha_sta
                     gc += r.ncand[l][g];
                     gk += r.nkept[l][g];
                 }
-                streamed = gc * r.plane_bytes;
+                // (a level scored whole during the chain streamed every node's planes)
+                streamed = r.spec_nodes[l] > 0 ? r.spec_nodes[l] * r.H * r.plane_bytes : gc * r.plane_bytes;
             }
         }
         out->cand[l] = cand;

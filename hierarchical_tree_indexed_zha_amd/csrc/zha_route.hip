@@ -39,7 +39,12 @@
 //     then an apply launch forms every candidate's mask of the heads that keep
 //     it and writes the group's kept list in order (decoupled look-back).  Below
 //     the chain, the first score kernel derives the chain's last level's group
-//     kept list from the per-head bitmaps.
+//     kept list from the per-head bitmaps.  When that first level's planes are
+//     small enough, the chain launch carries more workgroups, dispatched after
+//     the selecting ones onto the compute units they leave idle, which score
+//     every node of it while the chain selects; its score kernel then only
+//     copies its candidates' scores (the same values: the same products over the
+//     same operands).
 //
 // The candidates of a level are never written out: they are the children of the
 // level above's kept nodes (kept list and head masks, ascending) followed by the
@@ -158,9 +163,12 @@ __device__ __forceinline__ float4 e4m3x4_to_f32(uint32_t w) {
 // level above kept.  hm gets the largest score of the lane's heads 4 kq + i.
 // DEF: the level above (pa) was selected but not merged; its kept list is
 // derived here from its bitmaps (dynamic LDS), and this workgroup writes its
-// share of it (all of it together with the other workgroups).
+// share of it (all of it together with the other workgroups).  NW: waves per
+// workgroup.  NODE: the level's every node was scored already (a.sigN, node
+// indexed, by this same arithmetic), and the candidates' scores are copied from
+// there instead of computed.
 // Candidate positions and node ids fit in 32 bits (capacity < 2^31).
-template <bool BF16, bool ALL, bool DEF = false, int PF = 0>
+template <bool BF16, bool ALL, bool DEF = false, int PF = 0, int NW = 4, bool NODE = false>
 __device__ __forceinline__ void score_level(const void* __restrict__ q, const ZhaLevelArgs& a, int G, int c, int R,
                                             float tau, int g, int blk, int nblk, float (&hm)[4],
                                             const ZhaLevelArgs* pa = nullptr) {
@@ -170,6 +178,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
                  "s"(a.pkmask), "s"(a.pnkept), "s"(a.pcap), "s"(a.orph_lo), "s"(a.orph_hi), "s"(a.dc.m),
                  "s"(a.dc.s1), "s"(a.dc.s2), "s"(a.ncand), "s"(a.sig), "s"(a.hblk), "s"(G), "s"(c), "s"(R),
                  "s"(tau));
+    static_assert(!DEF || NW == 4, "the deferred merge stages its words over four waves");
     const bool top = ALL || a.top;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, kq = lane >> 4;
@@ -180,14 +189,14 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     const uint32_t allg = all_heads(G);
     const size_t lrow = (size_t)(g % a.hkv) * a.cap;   // the tree's group (a batch routes virtual groups)
     const size_t prow = (size_t)g * a.pcap;
-    const int stride = nblk * 4;
+    const int stride = nblk * NW;
     const int pcap = (int)a.pcap;
 
     // One round trip before any work: the parent count, the first item's parent
     // entry (its index clamped to the parent level's capacity, not bounded by the
     // count) and the query rows are all in flight together.  At the first routed
     // level the parent arrays point at readable memory whose values go unused.
-    int it = blk * 4 + wave;
+    int it = blk * NW + wave;
     int32_t pk = 0;
     uint32_t pm = 0;
     int pn_raw = 0;
@@ -215,7 +224,10 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
     // d = 16m + 4kq + e.
     float qa[32];
     const int jq = j < G ? j : 0;
-    if (BF16) {
+    if (NODE) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) qa[k] = 0.f;
+    } else if (BF16) {
         const uint16_t* qr = static_cast<const uint16_t*>(q) + ((size_t)g * G + jq) * ZHA_D + 4 * kq;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -311,7 +323,15 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
             }
         }
         float best[4] = {zha_neg_inf(), zha_neg_inf(), zha_neg_inf(), zha_neg_inf()};
-        for (int cb = 0; cb < CB; ++cb) {
+        if (NODE) {
+            // the candidate's scores for the lane's heads 4 kq + i, already maxed over its planes
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 4 * kq + i;
+                if (valid && h < G) best[i] = a.sigN[((size_t)g * G + h) * (size_t)a.nstride + (size_t)node];
+            }
+        }
+        for (int cb = 0; cb < (NODE ? 0 : CB); ++cb) {
             const int r = R <= 16 ? (j % R) : (cb * 16 + j);
             const size_t prw = (lrow + (size_t)node) * R + r;
             float4 sv[8];
@@ -388,9 +408,9 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
         if (blk == 0 && (int)threadIdx.x == 0) a.tick[g] = 0u;
         if (blk == 0 && (int)threadIdx.x < G) a.hdone[g * G + threadIdx.x] = 0u;
         uint32_t* desc = a.desc + (size_t)g * a.ndesc;
-        for (int i = blk * kScoreThreads + (int)threadIdx.x; i < a.ndesc; i += nblk * kScoreThreads) desc[i] = 0u;
+        for (int i = blk * NW * 64 + (int)threadIdx.x; i < a.ndesc; i += nblk * NW * 64) desc[i] = 0u;
         uint64_t* gm = a.ghist + (size_t)g * G * kHistBins;
-        for (int i = blk * kScoreThreads + (int)threadIdx.x; i < G * kHistBins; i += nblk * kScoreThreads) gm[i] = 0ull;
+        for (int i = blk * NW * 64 + (int)threadIdx.x; i < G * kHistBins; i += nblk * NW * 64) gm[i] = 0ull;
     }
     if constexpr (DEF) {
         // this workgroup's share of the chain's last level's kept list: words 4 blk +
@@ -398,7 +418,7 @@ __device__ __forceinline__ void score_level(const void* __restrict__ q, const Zh
         int32_t* kl = pa->klist + (size_t)g * pa->cap;
         uint32_t* km = pa->kmask + (size_t)g * pa->cap;
 #pragma unroll 1
-        for (int w = blk * 4 + wave; w < dv.wc; w += 4 * nblk) {
+        for (int w = blk * NW + wave; w < dv.wc; w += NW * nblk) {
             const uint64_t x = dv.u[w];
             if (lane_bit(x, lane)) {
                 const int node = w * 64 + lane;
@@ -443,14 +463,14 @@ __global__ __launch_bounds__(kScoreThreads) void zha_route_score_kernel(const vo
 // As zha_route_score_kernel, for a level whose parent level (pa) was selected but
 // not merged: the workgroups derive and write that level's kept list themselves
 // (dynamic LDS: zha_defer_lds_bytes).
-template <bool BF16, int PF>
+template <bool BF16, int PF, bool NODE = false>
 __global__ __launch_bounds__(kScoreThreads) void zha_route_score_defer_kernel(const void* __restrict__ q,
                                                                               ZhaLevelArgs a, ZhaLevelArgs pa,
                                                                               int G, int c, int R, float tau) {
     ZHA_LEVEL_ARGS_READY(pa, "s"(G));
     const int g = blockIdx.y;
     float hm[4];
-    score_level<BF16, false, true, PF>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm, &pa);
+    score_level<BF16, false, true, PF, 4, NODE>(q, a, G, c, R, tau, g, blockIdx.x, gridDim.x, hm, &pa);
     if (a.hblk) block_head_max(a, g, G, hm);
 }
 
@@ -1149,6 +1169,7 @@ __device__ __forceinline__ uint32_t wave_scan_rows(uint32_t* s) {
 // level are the children of its kept nodes of the level above, in ascending node
 // order, then the level's orphans.  Per level it writes its kept bitmap over node
 // ids and its candidate and kept counts.
+template <bool BF16, int PF>
 __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, int c, float top_p) {
     __shared__ __align__(16) uint32_t s_keys[kChainSlots];
     __shared__ int32_t s_kept[kChainSlots];
@@ -1161,6 +1182,16 @@ __global__ __launch_bounds__(kBT) void zha_chain_kernel(ZhaChainSel m, int G, in
     __shared__ float s_red[kBW];
     __shared__ CutShared st;
     __shared__ __align__(16) float s_sig[kChainStage];
+    if ((int)blockIdx.x >= m.nsel) {
+        // dispatched after the selecting workgroups: score every node of the level
+        // below the chain for every head (node-indexed), by the score kernels' own
+        // arithmetic, while the selection runs (groups interleaved)
+        const int sb = (int)blockIdx.x - m.nsel, ng = m.nsel / G;
+        float hm[4];
+        score_level<BF16, true, false, PF, kBT / 64>(m.q, m.spec, G, c, m.R, m.tau, sb % ng, sb / ng, m.spec_blocks,
+                                                     hm);
+        return;
+    }
     const int h = blockIdx.x, g = h / G, hl = h - g * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // the head's scores of every chained level, staged in LDS together (one round
@@ -2012,6 +2043,16 @@ hipError_t zha_launch_route_score(int kv_dtype, const void* q, const ZhaLevelArg
     if (defer) {
         if (a.top || !defer->top || defer->n_top > ZHA_CHAIN_SLOTS) return hipErrorInvalidValue;
         const size_t lds = zha_defer_lds_bytes(G, defer->n_top);
+        if (a.sigN) {
+            // the candidates' scores copied from the node-indexed ones (planes unread)
+            if (kv_dtype == 0)
+                hipLaunchKernelGGL((zha_route_score_defer_kernel<true, 0, true>), grid, dim3(kScoreThreads), lds,
+                                   stream, q, a, *defer, G, c, R, tau);
+            else
+                hipLaunchKernelGGL((zha_route_score_defer_kernel<false, 0, true>), grid, dim3(kScoreThreads), lds,
+                                   stream, q, a, *defer, G, c, R, tau);
+            return hipGetLastError();
+        }
         ZHA_SCORE_LAUNCH(zha_route_score_defer_kernel, grid, lds, stream, pf, q, a, *defer, G, c, R, tau);
         return hipGetLastError();
     }
@@ -2029,10 +2070,22 @@ hipError_t zha_launch_score_all(int kv_dtype, const void* q, const ZhaChainArgs&
     return hipGetLastError();
 }
 
-hipError_t zha_launch_chain(const ZhaChainSel& m, int H_kv, int G, int c, float top_p, hipStream_t stream) {
+hipError_t zha_launch_chain(int kv_dtype, const ZhaChainSel& m, int H_kv, int G, int c, float top_p,
+                            hipStream_t stream) {
     for (int i = 0; i < m.n; ++i)
         if (m.lv[i].n_nodes > kChainSlots) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(zha_chain_kernel, dim3((unsigned)(H_kv * G)), dim3(kBT), 0, stream, m, G, c, top_p);
+    if (m.nsel != H_kv * G || m.spec_blocks < 0 || (m.spec_blocks > 0 && (!m.spec.sig || !m.q))) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(H_kv * G + H_kv * m.spec_blocks));
+    const int pf = m.spec_blocks > 0 ? plane_format_of(m.spec) : 0;
+#define ZHA_CHAIN_LAUNCH(BQ)                                                                                  \
+    do {                                                                                                     \
+        if (pf == 2) hipLaunchKernelGGL((zha_chain_kernel<BQ, 2>), grid, dim3(kBT), 0, stream, m, G, c, top_p); \
+        else if (pf == 1) hipLaunchKernelGGL((zha_chain_kernel<BQ, 1>), grid, dim3(kBT), 0, stream, m, G, c, top_p); \
+        else hipLaunchKernelGGL((zha_chain_kernel<BQ, 0>), grid, dim3(kBT), 0, stream, m, G, c, top_p);      \
+    } while (0)
+    if (kv_dtype == 0) ZHA_CHAIN_LAUNCH(true);
+    else ZHA_CHAIN_LAUNCH(false);
+#undef ZHA_CHAIN_LAUNCH
     return hipGetLastError();
 }
 

@@ -208,8 +208,9 @@ typedef struct zha_stats {
     int64_t bytes_streamed[ZHA_STATS_MAX_LEVELS];    /* summary bytes the kernels streamed for the level:
                                                         equal to bytes_read, except at the small top levels
                                                         whose every complete node is scored ahead of their
-                                                        selection (then n_nodes * n_kv_heads times the
-                                                        same bytes per node) */
+                                                        selection, and at the level below them when its
+                                                        every node is scored while they are selected (then
+                                                        n_nodes * n_kv_heads times the same bytes per node) */
     int64_t gather_tokens;                           /* distinct tokens attended, summed over KV groups */
     int64_t gather_bytes;                            /* K and V bytes those tokens occupy */
 } zha_stats;

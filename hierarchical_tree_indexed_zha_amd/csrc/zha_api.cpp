@@ -118,7 +118,10 @@ void attn_partials(const zha_config* cfg, size_t& off, size_t& pm, size_t& pl, s
 // A level of n nodes per KV group may be scored whole while the chain above it
 // selects: its float32 planes over every group within kSpecBytes, and compute
 // units left over by the chain's H x G selecting workgroups.
-constexpr size_t kSpecBytes = 96ull << 20;
+#ifndef ZHA_SPEC_MIB
+#define ZHA_SPEC_MIB 96
+#endif
+constexpr size_t kSpecBytes = (size_t)ZHA_SPEC_MIB << 20;
 constexpr int kSpecCUs = 256;
 bool spec_fits(size_t n, size_t R, size_t H, size_t G) {
     return n * R * (sizeof(float) * ZHA_D + sizeof(float)) * H <= kSpecBytes && H * G + H <= (size_t)kSpecCUs;

@@ -118,6 +118,9 @@ void attn_partials(const zha_config* cfg, size_t& off, size_t& pm, size_t& pl, s
 // A level of n nodes per KV group may be scored whole while the chain above it
 // selects: its float32 planes over every group within kSpecBytes, and compute
 // units left over by the chain's H x G selecting workgroups.
+#ifndef ZHA_COPY_CAP
+#define ZHA_COPY_CAP 192
+#endif
 #ifndef ZHA_SPEC_MIB
 #define ZHA_SPEC_MIB 96
 #endif
@@ -586,7 +589,8 @@ int decode_impl(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tokens
             a.glist = (uint2*)(X + y.glist[l]);
         }
         a.ndesc = zha_apply_chunks(y.cap[l]);
-        const int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);
+        int blocks = zha_score_blocks(n_nodes(cfg, n_tokens, l), R);
+        if (l == spec) blocks = std::min(blocks, ZHA_COPY_CAP);   // copying scores: fewer workgroups
         a.score_blocks = blocks;
         ZhaLevelArgs pa{};
         const bool defer = nchain > 0 && l == below;

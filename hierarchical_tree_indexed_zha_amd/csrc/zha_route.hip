@@ -1421,7 +1421,10 @@ __device__ __forceinline__ uint64_t head_words(const KF& key_at, int n, bool non
 // device-scope atomics read with device-scope loads.
 // Apply workgroups take four positions per thread: 256 threads at levels of at most
 // kApplyWideCap slots, else 1024 (fewer chunks, fewer tickets drawn on one word).
-constexpr int kApplyWideCap = 131072;
+#ifndef ZHA_APPLY_WIDE_CAP
+#define ZHA_APPLY_WIDE_CAP 131072
+#endif
+constexpr int kApplyWideCap = ZHA_APPLY_WIDE_CAP;
 constexpr int kApplyEarly = 64;                   // apply workgroups per group drawing their ticket at once
 __host__ __device__ constexpr int apply_threads(int64_t cap) { return cap > kApplyWideCap ? 1024 : 256; }
 constexpr uint32_t kDescAgg = 1u << 30;           // descriptor: the chunk's kept count is published

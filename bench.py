@@ -333,6 +333,21 @@ def append_device(layer, x, steps, torch, dense_us):
     return {"mean_us": round(sum(us) / len(us), 3), "max_us": round(max(us), 3), "steps": steps}
 
 
+EXEMPT_MARGIN = 1e-4    # cumulative-mass margin below which a cut has several correct answers
+
+
+def cpu_model():
+    """The host CPU's model name (first processor of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(args, layer, x, w, torch):
     """The fp64 oracle on a bounded sample of the same workload: append + decode steps
     over a tree precomputed outside the timed region (as the GPU's build is)."""
@@ -356,15 +371,20 @@ def cpu_baseline(args, layer, x, w, torch):
     _log(f"[cpu] oracle tree precompute {t_pre:.1f} s")
     n = N
     done, elapsed = 0, 0.0
+    exempt, pairs = 0, 0
     while done < 64 and (elapsed < args.cpu_seconds or done < 1):
         i = done % x["q"].shape[0]
         qh = conv(x["q"][i])
         t0 = time.perf_counter()
         if w.append:
             n, _ = O.append_token(kh, vh, tree, n, conv(x["k_app"][i]), conv(x["v_app"][i]))
-        O.decode_step(qh, kh, vh, tree, w.top_p)
+        _, routes = O.decode_step(qh, kh, vh, tree, w.top_p)
         elapsed += time.perf_counter() - t0
         done += 1
+        # (head, step) pairs with a cut margin below the tie bar: either side of that
+        # cut is a correct answer, so their leaf sets are exempt from identity
+        exempt += sum(1 for r in routes if r.min_margin < EXEMPT_MARGIN)
+        pairs += len(routes)
     us = elapsed / done * 1e6
     _log(f"[cpu] oracle {done} steps, {us / 1e3:.1f} ms/step, threads {threads}")
     # the same steps again on one core (BLAS limited to one thread), a third of the budget
@@ -384,7 +404,8 @@ def cpu_baseline(args, layer, x, w, torch):
     except Exception as e:
         _log(f"[cpu] one-core timing skipped: {e}")
     return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
-            "value_one_core": None if us1 is None else round(us1, 1),
+            "value_one_core": None if us1 is None else round(us1, 1), "cpu_model": cpu_model(),
+            "exempt_heads": {"count": exempt, "of": pairs, "margin": EXEMPT_MARGIN},
             "sample": f"{done} append+decode steps of {w.name} (N={N}) after an untimed fp64 tree "
                       f"precompute of {t_pre:.1f} s; host cores available {os.cpu_count()}; "
                       f"value_one_core: {done1} decode steps with BLAS on one thread"}

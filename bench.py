@@ -348,6 +348,56 @@ def cpu_model():
     return None
 
 
+_PROC = {}    # the forked workers' view of the oracle state (inherited, never sent)
+
+
+def _group_decode(job):
+    """Oracle decode of one KV group's query heads in a worker process: (group, output rows)."""
+    import numpy as np
+    import oracle as O
+    g, qh = job
+    st = _PROC
+    q = O.widen(qh)
+    G = q.shape[0] // st["n_kv"]
+    rows = []
+    for h in range(g * G, (g + 1) * G):
+        r = O.route_head(q[h], st["tree"], g, st["p"])
+        rows.append(O.attend(q[h], st["kh"][g], st["vh"][g], r.tokens, st["tree"].tau))
+    return g, np.stack(rows)
+
+
+def cpu_procs(args, x, w, conv, kh, vh, tree):
+    """The oracle's decode on every host core: one forked worker process per KV group (the
+    oracle state inherited copy-on-write), each with its share of the BLAS threads; a
+    bounded sample of decode steps at the sample's final context.  None if it fails."""
+    import multiprocessing as mp
+    ncpu = os.cpu_count() or 1
+    nproc = max(1, min(w.n_kv_heads, ncpu))
+    _PROC.update(tree=tree, kh=kh, vh=vh, p=w.top_p, n_kv=w.n_kv_heads)
+    pool = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=max(1, ncpu // nproc)):
+            pool = mp.get_context("fork").Pool(nproc)
+        done, elapsed = 0, 0.0
+        while done < 16 and (elapsed < args.cpu_seconds / 3 or done < 1):
+            qh = conv(x["q"][done % x["q"].shape[0]])
+            t0 = time.perf_counter()
+            pool.map_async(_group_decode, [(g, qh) for g in range(w.n_kv_heads)]).get(timeout=120)
+            elapsed += time.perf_counter() - t0
+            done += 1
+        return {"value": round(elapsed / done * 1e6, 1), "processes": nproc,
+                "threads_per_process": max(1, ncpu // nproc), "steps": done}
+    except Exception as e:
+        _log(f"[cpu] per-group processes skipped: {e!r}")
+        return None
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
+        _PROC.clear()
+
+
 def cpu_baseline(args, layer, x, w, torch):
     """The fp64 oracle on a bounded sample of the same workload: append + decode steps
     over a tree precomputed outside the timed region (as the GPU's build is)."""
@@ -403,8 +453,12 @@ def cpu_baseline(args, layer, x, w, torch):
         _log(f"[cpu] oracle on one core: {done1} decode steps, {us1 / 1e3:.1f} ms/step")
     except Exception as e:
         _log(f"[cpu] one-core timing skipped: {e}")
+    procs = cpu_procs(args, x, w, conv, kh, vh, tree)
+    if procs:
+        _log(f"[cpu] oracle decode, one process per KV group: {procs['value'] / 1e3:.1f} ms/step")
     return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
             "value_one_core": None if us1 is None else round(us1, 1), "cpu_model": cpu_model(),
+            "decode_processes": procs,
             "exempt_heads": {"count": exempt, "of": pairs, "margin": EXEMPT_MARGIN},
             "sample": f"{done} append+decode steps of {w.name} (N={N}) after an untimed fp64 tree "
                       f"precompute of {t_pre:.1f} s; host cores available {os.cpu_count()}; "

@@ -353,16 +353,39 @@ int zha_build_tree(const zha_config* cfg, const zha_buffers* bufs, int64_t n_tok
         two ? (float*)at(T, y.t_l[2]) : nullptr, two ? y.cap[2] : 0, &fused, s);
     if (e != hipSuccess) return hip_fail(e, "leaf summary launch");
     if ((rc = planes16(cfg, y, T, 1, 0, n_nodes(cfg, n_tokens, 1), s))) return rc;
-    for (int l = 2; l <= y.L; ++l) {
+    auto merge = [&](int l, int64_t first, int64_t n) {
+        return zha_launch_merge((float*)at(T, y.t_s[l - 1]), (float*)at(T, y.t_b[l - 1]), (float*)at(T, y.t_l[l - 1]),
+                                (float*)at(T, y.t_s[l]), (float*)at(T, y.t_b[l]), (float*)at(T, y.t_l[l]), y.H,
+                                y.cap[l - 1], y.cap[l], c, R, first, n, s);
+    };
+    for (int l = 2; l <= y.L;) {
         const int64_t n = n_nodes(cfg, n_tokens, l);
         if (n == 0) break;
-        if (!(l == 2 && fused)) {
-            e = zha_launch_merge((float*)at(T, y.t_s[l - 1]), (float*)at(T, y.t_b[l - 1]),
-                                 (float*)at(T, y.t_l[l - 1]), (float*)at(T, y.t_s[l]), (float*)at(T, y.t_b[l]),
-                                 (float*)at(T, y.t_l[l]), y.H, y.cap[l - 1], y.cap[l], c, R, 0, n, s);
-            if (e != hipSuccess) return hip_fail(e, "merge launch");
+        if (l == 2 && fused) {                 // written by the leaf kernel
+            if ((rc = planes16(cfg, y, T, l, 0, n, s))) return rc;
+            ++l;
+            continue;
         }
+        const int64_t ng = l < y.L ? n_nodes(cfg, n_tokens, l + 1) : 0;
+        if (ng > 0 && zha_merge2_lds_bytes(c, R) <= 64 * 1024) {
+            // levels l and l + 1 in one launch for the nodes under complete level-(l + 1)
+            // nodes, then level l's right-edge nodes (orphans one level up) alone
+            e = zha_launch_merge2((float*)at(T, y.t_s[l - 1]), (float*)at(T, y.t_b[l - 1]),
+                                  (float*)at(T, y.t_l[l - 1]), (float*)at(T, y.t_s[l]), (float*)at(T, y.t_b[l]),
+                                  (float*)at(T, y.t_l[l]), (float*)at(T, y.t_s[l + 1]), (float*)at(T, y.t_b[l + 1]),
+                                  (float*)at(T, y.t_l[l + 1]), y.H, y.cap[l - 1], y.cap[l], y.cap[l + 1], c, R, 0, ng,
+                                  s);
+            if (e != hipSuccess) return hip_fail(e, "merge launch (two levels)");
+            if (n > (int64_t)c * ng && (e = merge(l, (int64_t)c * ng, n - (int64_t)c * ng)) != hipSuccess)
+                return hip_fail(e, "merge launch");
+            if ((rc = planes16(cfg, y, T, l, 0, n, s))) return rc;
+            if ((rc = planes16(cfg, y, T, l + 1, 0, ng, s))) return rc;
+            l += 2;
+            continue;
+        }
+        if ((e = merge(l, 0, n)) != hipSuccess) return hip_fail(e, "merge launch");
         if ((rc = planes16(cfg, y, T, l, 0, n, s))) return rc;
+        ++l;
     }
     return ok();
 }

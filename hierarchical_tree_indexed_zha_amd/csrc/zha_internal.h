@@ -20,6 +20,13 @@ hipError_t zha_launch_leaf_summary(int kv_dtype, const void* K, const float* Qre
 hipError_t zha_launch_merge(const float* Sc, const float* Bc, const float* Lc, float* Sp, float* Bp, float* Lp,
                             int H_kv, int64_t cap_c, int64_t cap_p, int c, int R, int64_t first_parent,
                             int64_t n_parents, hipStream_t stream);
+// Two levels at once: the middle level's nodes c * first_grand .. c * (first_grand
+// + n_grand) - 1 (written to Sp/Bp/Lp) and their parents first_grand .. + n_grand
+// (Sg/Bg/Lg), the same values as two zha_launch_merge calls.
+size_t zha_merge2_lds_bytes(int c, int R);
+hipError_t zha_launch_merge2(const float* Sc, const float* Bc, const float* Lc, float* Sp, float* Bp, float* Lp,
+                             float* Sg, float* Bg, float* Lg, int H_kv, int64_t cap_c, int64_t cap_p, int64_t cap_g,
+                             int c, int R, int64_t first_grand, int64_t n_grand, hipStream_t stream);
 // the router's bfloat16 copy (round-to-nearest-even) of planes s of nodes
 // [first, first + n) of one level, every KV head
 hipError_t zha_launch_planes16(const float* S, uint16_t* S16, int H_kv, int64_t cap, int R, int64_t first, int64_t n,

@@ -789,35 +789,31 @@ __global__ __launch_bounds__(256) void zha_leaf_b3_kernel(
     }
 }
 
-// grid (ceil(n_parents / parents_per_block), H_kv), 256 threads.
-template <int CMAX>
-__global__ __launch_bounds__(256) void zha_merge_kernel(
-    const float* __restrict__ Sc, const float* __restrict__ Bc, const float* __restrict__ Lc,
-    float* __restrict__ Sp, float* __restrict__ Bp, float* __restrict__ Lp,
-    int64_t cap_c, int64_t cap_p, int c, int R, int64_t first_parent, int64_t n_parents) {
-    // CMAX > 0: c <= CMAX, and each thread loads all of its c children before it
-    // combines them (the loads overlap); CMAX == 0: any c, one child at a time.  The
-    // arithmetic and its order are the same in both forms.
-    extern __shared__ float a_s[];                       // [ppb][R][c]
-    const int g = blockIdx.y;
+// Merges np parents (local index pl) from their c children each, as the whole
+// workgroup: per (parent, plane) its LSE and b, with the children's weights a_j
+// kept in a_s [np][R][c], then its weighted mean s.  A child's (L, B) comes from
+// cl(pl, r, j) and its s from cs(pl, r, j, d4) (float4 d4 of the plane); results go
+// to wl(pl, r, L, B) and ws(pl, r, d4, s).  CMAX > 0: c <= CMAX, and each thread
+// loads all of its c children before it combines them (the loads overlap); CMAX ==
+// 0: any c, one child at a time.  The arithmetic and its order are the same in
+// both forms and for every caller.  Ends with a barrier.
+template <int CMAX, class CL, class CS, class WL, class WS>
+__device__ __forceinline__ void merge_block(int np, int c, int R, float* a_s, CL&& cl, CS&& cs, WL&& wl, WS&& ws) {
     const int tid = threadIdx.x;
     const int per_parent = R * (ZHA_D / 4);              // float4 outputs per parent
-    const int ppb = per_parent >= 256 ? 1 : 256 / per_parent;
-    const int64_t p0 = first_parent + (int64_t)blockIdx.x * ppb;
-    const int64_t end = first_parent + n_parents;
-    if (p0 >= end) return;
-    const int np = (int)min((int64_t)ppb, end - p0);
     for (int pr = tid; pr < np * R; pr += blockDim.x) {
-        int pl = pr / R, r = pr - pl * R;
-        int64_t child0 = (p0 + pl) * c;
-        const size_t o0 = ((size_t)g * cap_c + (size_t)child0) * R + r;
+        const int pl = pr / R, r = pr - pl * R;
         float m = zha_neg_inf(), sum = 0.f, bp = 0.f;
         float* a = a_s + (pl * R + r) * c;
         if constexpr (CMAX > 0) {
             float lv[CMAX], bv[CMAX];
 #pragma unroll
             for (int j = 0; j < CMAX; ++j)
-                if (j < c) { lv[j] = Lc[o0 + (size_t)j * R]; bv[j] = Bc[o0 + (size_t)j * R]; }
+                if (j < c) {
+                    const float2 t = cl(pl, r, j);
+                    lv[j] = t.x;
+                    bv[j] = t.y;
+                }
 #pragma unroll
             for (int j = 0; j < CMAX; ++j)
                 if (j < c) m = fmaxf(m, lv[j]);
@@ -836,36 +832,31 @@ __global__ __launch_bounds__(256) void zha_merge_kernel(
             }
             m = lse;
         } else {
-            for (int j = 0; j < c; ++j) m = fmaxf(m, Lc[o0 + (size_t)j * R]);
-            for (int j = 0; j < c; ++j) sum += expf(Lc[o0 + (size_t)j * R] - m);
+            for (int j = 0; j < c; ++j) m = fmaxf(m, cl(pl, r, j).x);
+            for (int j = 0; j < c; ++j) sum += expf(cl(pl, r, j).x - m);
             const float lse = m + logf(sum);
             for (int j = 0; j < c; ++j) {
-                const size_t o = o0 + (size_t)j * R;
-                const float la = Lc[o] - lse;                    // log a_j
+                const float2 t = cl(pl, r, j);
+                const float la = t.x - lse;                      // log a_j
                 const float aj = expf(la);
                 a[j] = aj;
-                bp = fmaf(aj, Bc[o] - la, bp);
+                bp = fmaf(aj, t.y - la, bp);
             }
             m = lse;
         }
-        size_t op = ((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r;
-        Lp[op] = m;
-        Bp[op] = bp;
+        wl(pl, r, m, bp);
     }
     __syncthreads();
     for (int o = tid; o < np * per_parent; o += blockDim.x) {
-        int pl = o / per_parent, rem = o - pl * per_parent;
-        int r = rem / (ZHA_D / 4), d4 = rem - r * (ZHA_D / 4);
-        int64_t child0 = (p0 + pl) * c;
+        const int pl = o / per_parent, rem = o - pl * per_parent;
+        const int r = rem / (ZHA_D / 4), d4 = rem - r * (ZHA_D / 4);
         const float* a = a_s + (pl * R + r) * c;
-        const float4* sc = reinterpret_cast<const float4*>(Sc + (((size_t)g * cap_c + (size_t)child0) * R + r) * ZHA_D) + d4;
-        const size_t step = (size_t)R * (ZHA_D / 4);         // float4s from one child to the next
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         if constexpr (CMAX > 0) {
             float4 sv[CMAX];
 #pragma unroll
             for (int j = 0; j < CMAX; ++j)
-                if (j < c) sv[j] = sc[(size_t)j * step];
+                if (j < c) sv[j] = cs(pl, r, j, d4);
 #pragma unroll
             for (int j = 0; j < CMAX; ++j) {
                 if (j < c) {
@@ -877,15 +868,109 @@ __global__ __launch_bounds__(256) void zha_merge_kernel(
             }
         } else {
             for (int j = 0; j < c; ++j) {
-                const float4 s = sc[(size_t)j * step];
-                acc.x = fmaf(a[j], s.x, acc.x);
-                acc.y = fmaf(a[j], s.y, acc.y);
-                acc.z = fmaf(a[j], s.z, acc.z);
-                acc.w = fmaf(a[j], s.w, acc.w);
+                const float4 t = cs(pl, r, j, d4);
+                acc.x = fmaf(a[j], t.x, acc.x);
+                acc.y = fmaf(a[j], t.y, acc.y);
+                acc.z = fmaf(a[j], t.z, acc.z);
+                acc.w = fmaf(a[j], t.w, acc.w);
             }
         }
-        reinterpret_cast<float4*>(Sp + (((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r) * ZHA_D)[d4] = acc;
+        ws(pl, r, d4, acc);
     }
+    __syncthreads();
+}
+
+// grid (ceil(n_parents / parents_per_block), H_kv), 256 threads: parents
+// first_parent .. + n_parents of one level from their children one level down.
+template <int CMAX>
+__global__ __launch_bounds__(256) void zha_merge_kernel(
+    const float* __restrict__ Sc, const float* __restrict__ Bc, const float* __restrict__ Lc,
+    float* __restrict__ Sp, float* __restrict__ Bp, float* __restrict__ Lp,
+    int64_t cap_c, int64_t cap_p, int c, int R, int64_t first_parent, int64_t n_parents) {
+    extern __shared__ float a_s[];                       // [ppb][R][c]
+    const int g = blockIdx.y;
+    const int per_parent = R * (ZHA_D / 4);
+    const int ppb = per_parent >= 256 ? 1 : 256 / per_parent;
+    const int64_t p0 = first_parent + (int64_t)blockIdx.x * ppb;
+    const int64_t end = first_parent + n_parents;
+    if (p0 >= end) return;
+    const int np = (int)min((int64_t)ppb, end - p0);
+    const size_t step = (size_t)R * (ZHA_D / 4);         // float4s from one child to the next
+    merge_block<CMAX>(
+        np, c, R, a_s,
+        [&](int pl, int r, int j) {
+            const size_t o = ((size_t)g * cap_c + (size_t)((p0 + pl) * c)) * R + r + (size_t)j * R;
+            return make_float2(Lc[o], Bc[o]);
+        },
+        [&](int pl, int r, int j, int d4) {
+            const float4* sc = reinterpret_cast<const float4*>(
+                Sc + (((size_t)g * cap_c + (size_t)((p0 + pl) * c)) * R + r) * ZHA_D) + d4;
+            return sc[(size_t)j * step];
+        },
+        [&](int pl, int r, float lse, float b) {
+            const size_t op = ((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r;
+            Lp[op] = lse;
+            Bp[op] = b;
+        },
+        [&](int pl, int r, int d4, float4 v) {
+            reinterpret_cast<float4*>(Sp + (((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r) * ZHA_D)[d4] = v;
+        });
+}
+
+// grid (n_grand, H_kv), 256 threads: two levels at once.  Workgroup k merges the
+// c children of grandparent first_grand + k (level l, written out and kept in
+// LDS) from their own children (level l - 1), then the grandparent (level l + 1)
+// from those: the same merge, so the same values as two merge launches, in one.
+// LDS: [c][R] L and B, [c][R][128] s of the middle level, and the weights.
+template <int CMAX>
+__global__ __launch_bounds__(256) void zha_merge2_kernel(
+    const float* __restrict__ Sc, const float* __restrict__ Bc, const float* __restrict__ Lc,
+    float* __restrict__ Sp, float* __restrict__ Bp, float* __restrict__ Lp,
+    float* __restrict__ Sg, float* __restrict__ Bg, float* __restrict__ Lg,
+    int64_t cap_c, int64_t cap_p, int64_t cap_g, int c, int R, int64_t first_grand) {
+    extern __shared__ float m_s[];
+    float* sL = m_s;                                     // [c][R]
+    float* sB = sL + c * R;                              // [c][R]
+    float4* sS = reinterpret_cast<float4*>(sB + c * R + ((4 - (2 * c * R) % 4) % 4));   // [c][R][32]
+    float* a_s = reinterpret_cast<float*>(sS + (size_t)c * R * (ZHA_D / 4));            // [c][R][c]
+    const int g = blockIdx.y;
+    const int64_t gp = first_grand + blockIdx.x;
+    const int64_t p0 = gp * c;                           // its first child (middle level)
+    const size_t step = (size_t)R * (ZHA_D / 4);
+    merge_block<CMAX>(
+        c, c, R, a_s,
+        [&](int pl, int r, int j) {
+            const size_t o = ((size_t)g * cap_c + (size_t)((p0 + pl) * c)) * R + r + (size_t)j * R;
+            return make_float2(Lc[o], Bc[o]);
+        },
+        [&](int pl, int r, int j, int d4) {
+            const float4* sc = reinterpret_cast<const float4*>(
+                Sc + (((size_t)g * cap_c + (size_t)((p0 + pl) * c)) * R + r) * ZHA_D) + d4;
+            return sc[(size_t)j * step];
+        },
+        [&](int pl, int r, float lse, float b) {
+            const size_t op = ((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r;
+            Lp[op] = lse;
+            Bp[op] = b;
+            sL[pl * R + r] = lse;
+            sB[pl * R + r] = b;
+        },
+        [&](int pl, int r, int d4, float4 v) {
+            reinterpret_cast<float4*>(Sp + (((size_t)g * cap_p + (size_t)(p0 + pl)) * R + r) * ZHA_D)[d4] = v;
+            sS[((size_t)pl * R + r) * (ZHA_D / 4) + d4] = v;
+        });
+    merge_block<CMAX>(
+        1, c, R, a_s,
+        [&](int, int r, int j) { return make_float2(sL[j * R + r], sB[j * R + r]); },
+        [&](int, int r, int j, int d4) { return sS[((size_t)j * R + r) * (ZHA_D / 4) + d4]; },
+        [&](int, int r, float lse, float b) {
+            const size_t og = ((size_t)g * cap_g + (size_t)gp) * R + r;
+            Lg[og] = lse;
+            Bg[og] = b;
+        },
+        [&](int, int r, int d4, float4 v) {
+            reinterpret_cast<float4*>(Sg + (((size_t)g * cap_g + (size_t)gp) * R + r) * ZHA_D)[d4] = v;
+        });
 }
 
 // grid (blocks, H_kv), 256 threads: S16 <- bfloat16(S), round to nearest, ties to
@@ -1056,6 +1141,29 @@ hipError_t zha_launch_merge(const float* Sc, const float* Bc, const float* Lc, f
     else
         hipLaunchKernelGGL(zha_merge_kernel<0>, grid, dim3(256), lds, stream, Sc, Bc, Lc, Sp, Bp, Lp, cap_c, cap_p,
                            c, R, first_parent, n_parents);
+    return hipGetLastError();
+}
+
+size_t zha_merge2_lds_bytes(int c, int R) {
+    return sizeof(float) * (size_t)(2 * c * R + 4 + c * R * ZHA_D + c * R * c);
+}
+
+hipError_t zha_launch_merge2(const float* Sc, const float* Bc, const float* Lc, float* Sp, float* Bp, float* Lp,
+                             float* Sg, float* Bg, float* Lg, int H_kv, int64_t cap_c, int64_t cap_p, int64_t cap_g,
+                             int c, int R, int64_t first_grand, int64_t n_grand, hipStream_t stream) {
+    if (n_grand <= 0) return hipSuccess;
+    const size_t lds = zha_merge2_lds_bytes(c, R);
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    dim3 grid((unsigned)n_grand, (unsigned)H_kv);
+    if (c <= 8)
+        hipLaunchKernelGGL(zha_merge2_kernel<8>, grid, dim3(256), lds, stream, Sc, Bc, Lc, Sp, Bp, Lp, Sg, Bg, Lg,
+                           cap_c, cap_p, cap_g, c, R, first_grand);
+    else if (c <= 16)
+        hipLaunchKernelGGL(zha_merge2_kernel<16>, grid, dim3(256), lds, stream, Sc, Bc, Lc, Sp, Bp, Lp, Sg, Bg, Lg,
+                           cap_c, cap_p, cap_g, c, R, first_grand);
+    else
+        hipLaunchKernelGGL(zha_merge2_kernel<0>, grid, dim3(256), lds, stream, Sc, Bc, Lc, Sp, Bp, Lp, Sg, Bg, Lg,
+                           cap_c, cap_p, cap_g, c, R, first_grand);
     return hipGetLastError();
 }
 
